@@ -1,0 +1,879 @@
+/*
+ * CPU oracle for the Angle-Domain Attention (ADA) decode path.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the tests, the smoke check and the CPU
+ * baseline leg of the benchmark load this file's library.  The product path
+ * (the HIP library under compressed_kv_attention_amd/) never calls it, and
+ * the two share no code: no header, helper, table or constant.
+ *
+ * Plain, slow and single-threaded inside every unit of work.  Floating point
+ * is carried in double except where an operation is defined at a stated
+ * storage precision (fp16 radius, fp16 scale, fp32 division of the int8 value
+ * quantiser); those spots say so.
+ *
+ * Sources (two web pages on one paper, arXiv 2605.18856):
+ *   [TS]  gist.science, "SPHERICAL KV: Angle-Domain Attention and
+ *         Rate-Distortion Retention ...", section "Technical Summary".
+ *   [ABS] fugumt.com, the same paper's arXiv abstract.
+ * The pages fix the shape of the method (a key becomes a scalar radius and
+ * compact angle codes; logits come straight from the codes; tokens get a
+ * keep/drop decision and a precision tier per token and head; retained tokens
+ * sit in pages that hold one tier each).  They fix no encoding, bit width,
+ * page layout or tie rule.  Each such choice below is stated where it is
+ * made, as "Reading:".
+ *
+ * Parity pins: every exported function is pinned by a CPU test against a
+ * closed form, an invariant or brute force (tests/test_oracle_*.py).
+ */
+#include <math.h>
+#include <pthread.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+/* ------------------------------------------------------------------------ */
+/* Number formats.                                                           */
+/* ------------------------------------------------------------------------ */
+
+/* IEEE binary16 -> double (exact). */
+static double f16_to_double(uint16_t h)
+{
+    int sign = (h >> 15) & 1;
+    int exp = (h >> 10) & 0x1f;
+    int man = h & 0x3ff;
+    double v;
+    if (exp == 0)
+        v = ldexp((double)man, -24); /* zero or subnormal */
+    else if (exp == 31)
+        v = man ? NAN : INFINITY;
+    else
+        v = ldexp((double)(man + 1024), exp - 25);
+    return sign ? -v : v;
+}
+
+/* bfloat16 -> double (exact): the upper half of an IEEE binary32. */
+static double bf16_to_double(uint16_t b)
+{
+    uint32_t u = (uint32_t)b << 16;
+    float f;
+    memcpy(&f, &u, 4);
+    return (double)f;
+}
+
+/* double -> binary16, round to nearest, ties to even.  Magnitudes that would
+ * round to infinity saturate to the largest finite value 65504 (Reading: a
+ * stored radius or scale is always finite).  NaN maps to the quiet NaN. */
+static uint16_t double_to_f16_sat(double x)
+{
+    uint16_t sign = 0;
+    if (isnan(x))
+        return 0x7e00;
+    if (x < 0 || (x == 0 && signbit(x))) {
+        sign = 0x8000;
+        x = -x;
+    }
+    if (x == 0)
+        return sign;
+    if (x >= 65520.0) /* rounds past 65504 */
+        return sign | 0x7bff;
+    if (x < ldexp(1.0, -14)) {
+        /* subnormal range: units of 2^-24; 1024 units is the smallest normal */
+        double m = nearbyint(ldexp(x, 24)); /* default rounding: ties to even */
+        return sign | (uint16_t)m;
+    }
+    int e;
+    frexp(x, &e); /* x = f * 2^e, f in [0.5, 1) */
+    e -= 1;       /* x in [2^e, 2^(e+1)) */
+    double m = nearbyint(ldexp(x, 10 - e)); /* in [1024, 2048] */
+    if (m == 2048.0) {
+        m = 1024.0;
+        e += 1;
+    }
+    if (e > 15)
+        return sign | 0x7bff;
+    return sign | (uint16_t)(((e + 15) << 10) | ((int)m - 1024));
+}
+
+/* double -> bfloat16, round to nearest, ties to even (finite inputs). */
+static uint16_t double_to_bf16(double x)
+{
+    float f = (float)x; /* exact for the values used (fp16 inputs) */
+    uint32_t u;
+    memcpy(&u, &f, 4);
+    uint32_t lsb = (u >> 16) & 1;
+    u += 0x7fff + lsb;
+    return (uint16_t)(u >> 16);
+}
+
+/* ------------------------------------------------------------------------ */
+/* Page format.                                                              */
+/*                                                                           */
+/* Reading: [TS] 2.2 asks for pages whose items share one precision tier so */
+/* that the decoder can stream them guided by a small header; [ABS] adds    */
+/* that the metadata is small and the reads coalesced.  Nothing more is     */
+/* given.  The format used here (the HIP library implements the same format */
+/* from this description, in code of its own):                              */
+/*                                                                           */
+/* A page holds P = 16 slots of one (sequence, kv-head) row.  D is the head  */
+/* dimension (64 or 128), G = D/8 code groups, L = D/4.  Sizes are padded    */
+/* to 128 bytes, the page-table unit.                                        */
+/*   tier 0 (fp16 keys):   K fp16 "wide" section | V bf16 "wide" section      */
+/*   tier 1 (8-bit codes): V bf16 wide | codes u8 [16][G] | radius fp16 [16] */
+/*   tier 2 (4-bit codes): V int8 "narrow" | codes u8 [16][G/2] |            */
+/*                         radius fp16 [16] | value scale fp16 [16]          */
+/*   tier 3 (dense bf16, comparison path): K bf16 wide | V bf16 wide         */
+/* A "wide" section stores a 16 x D matrix of 2-byte elements in 16-byte     */
+/* chunks of 8 elements: element (t, d) is at byte                          */
+/*     ((d % L) / 8) * 1024 + ((d / L) * 16 + t) * 16 + (d % 8) * 2.         */
+/* A "narrow" section stores 16 x D bytes in 16-byte chunks of 16 elements:  */
+/*     ((d % L) / 16) * 1024 + ((d / L) * 16 + t) * 16 + (d % 16).           */
+/* 4-bit codes: byte b of a slot holds group 2b in its low nibble and group  */
+/* 2b+1 in its high nibble.  Slots past the page's valid count, and all      */
+/* padding, are zero.  The page's metadata byte is tier | (n_valid-1) << 2.  */
+/* ------------------------------------------------------------------------ */
+
+enum { SLOTS = 16, UNIT = 128 };
+
+static size_t wide_off(int D, int t, int d)
+{
+    int L = D / 4;
+    return (size_t)((d % L) / 8) * 1024 + (size_t)((d / L) * 16 + t) * 16 + (size_t)(d % 8) * 2;
+}
+
+static size_t narrow_off(int D, int t, int d)
+{
+    int L = D / 4;
+    return (size_t)((d % L) / 16) * 1024 + (size_t)((d / L) * 16 + t) * 16 + (size_t)(d % 16);
+}
+
+static size_t pad_unit(size_t b) { return (b + UNIT - 1) / UNIT * UNIT; }
+
+/* Byte size of one page of a tier. */
+size_t oracle_page_bytes(int D, int tier)
+{
+    int G = D / 8;
+    switch (tier) {
+    case 0: return pad_unit((size_t)64 * D);
+    case 1: return pad_unit((size_t)32 * D + (size_t)16 * G + 32);
+    case 2: return pad_unit((size_t)16 * D + (size_t)8 * G + 64);
+    case 3: return pad_unit((size_t)64 * D);
+    default: return 0;
+    }
+}
+
+/* Section offsets inside a page. */
+static size_t off_codes(int D, int tier) { return tier == 1 ? (size_t)32 * D : (size_t)16 * D; }
+static size_t off_radius(int D, int tier)
+{
+    int G = D / 8;
+    return tier == 1 ? (size_t)32 * D + 16 * G : (size_t)16 * D + 8 * G;
+}
+static size_t off_vscale(int D) { return off_radius(D, 2) + 32; }
+static size_t off_v(int D, int tier) { return (tier == 0 || tier == 3) ? (size_t)32 * D : 0; }
+
+/* ------------------------------------------------------------------------ */
+/* Encode.                                                                   */
+/*                                                                           */
+/* [TS] 2.1 "Spherical Parameterization": a key k becomes a scalar radius    */
+/* r = ||k|| and a direction; "Compressed-Domain Similarity": the cache keeps */
+/* a quantized radius and packed angular codes.  Reading of the codes: the   */
+/* unit direction u = k / r is cut into G groups of 8 coordinates and each   */
+/* group is replaced by the index of its nearest codeword (squared Euclidean */
+/* distance, lowest index on ties) in a per-head codebook of 256 entries     */
+/* (8-bit tier) and of 16 entries (4-bit tier).  Reading of the radius: the  */
+/* norm of the fp16 key rounded once to fp16; u uses the unrounded norm;     */
+/* a zero key has u = 0.                                                     */
+/* ------------------------------------------------------------------------ */
+
+typedef struct {
+    int D, Hkv;
+    const uint16_t *keys; /* [N][Hkv][D] fp16 */
+    const float *cb8;     /* [Hkv][G][256][8] */
+    const float *cb4;     /* [Hkv][G][16][8] */
+    uint16_t *radius;     /* [N][Hkv] fp16 */
+    uint8_t *codes8;      /* [N][Hkv][G] */
+    uint8_t *codes4;      /* [N][Hkv][G/2] */
+    double *dist8;        /* optional [N][Hkv][G][256] */
+    double *dist4;        /* optional [N][Hkv][G][16] */
+} encode_args;
+
+static int nearest(const double *u8, const float *cb, int K, double *dist_out)
+{
+    int best = 0;
+    double bestd = INFINITY;
+    for (int c = 0; c < K; c++) {
+        double d = 0;
+        for (int j = 0; j < 8; j++) {
+            double diff = u8[j] - (double)cb[c * 8 + j];
+            d += diff * diff;
+        }
+        if (dist_out)
+            dist_out[c] = d;
+        if (d < bestd) {
+            bestd = d;
+            best = c;
+        }
+    }
+    return best;
+}
+
+static void encode_one(const encode_args *a, int64_t i /* token*Hkv + head */)
+{
+    int D = a->D, G = D / 8, h = (int)(i % a->Hkv);
+    const uint16_t *k = a->keys + i * D;
+    double x[128], u[128];
+    double ss = 0;
+    for (int j = 0; j < D; j++) {
+        x[j] = f16_to_double(k[j]);
+        ss += x[j] * x[j];
+    }
+    double r = sqrt(ss);
+    a->radius[i] = double_to_f16_sat(r);
+    for (int j = 0; j < D; j++)
+        u[j] = r > 0 ? x[j] / r : 0.0;
+    for (int g = 0; g < G; g++) {
+        const float *c8 = a->cb8 + ((size_t)h * G + g) * 256 * 8;
+        const float *c4 = a->cb4 + ((size_t)h * G + g) * 16 * 8;
+        double *d8 = a->dist8 ? a->dist8 + ((size_t)i * G + g) * 256 : NULL;
+        double *d4 = a->dist4 ? a->dist4 + ((size_t)i * G + g) * 16 : NULL;
+        a->codes8[i * G + g] = (uint8_t)nearest(u + 8 * g, c8, 256, d8);
+        int c = nearest(u + 8 * g, c4, 16, d4);
+        uint8_t *b = a->codes4 + i * (G / 2) + g / 2;
+        if (g % 2 == 0)
+            *b = (uint8_t)c;
+        else
+            *b = (uint8_t)(*b | (c << 4));
+    }
+}
+
+typedef struct {
+    const encode_args *a;
+    int64_t begin, end;
+} encode_job;
+
+static void *encode_worker(void *p)
+{
+    encode_job *j = (encode_job *)p;
+    for (int64_t i = j->begin; i < j->end; i++)
+        encode_one(j->a, i);
+    return NULL;
+}
+
+/* Encode n_tokens x Hkv keys.  dist8/dist4, when non-NULL, receive every
+ * candidate's squared distance (for tests of the argmin).  nthreads > 1
+ * splits independent (token, head) items across threads. */
+int oracle_encode(int D, int Hkv, int64_t n_tokens, const uint16_t *keys, const float *cb8,
+                  const float *cb4, uint16_t *radius, uint8_t *codes8, uint8_t *codes4,
+                  double *dist8, double *dist4, int nthreads)
+{
+    if ((D != 64 && D != 128) || Hkv <= 0 || n_tokens < 0)
+        return 1;
+    encode_args a = {D, Hkv, keys, cb8, cb4, radius, codes8, codes4, dist8, dist4};
+    int64_t n = n_tokens * Hkv;
+    if (nthreads < 1)
+        nthreads = 1;
+    if (nthreads > 256)
+        nthreads = 256;
+    pthread_t th[256];
+    encode_job jobs[256];
+    for (int t = 0; t < nthreads; t++) {
+        jobs[t].a = &a;
+        jobs[t].begin = n * t / nthreads;
+        jobs[t].end = n * (t + 1) / nthreads;
+        if (nthreads == 1)
+            encode_worker(&jobs[t]);
+        else
+            pthread_create(&th[t], NULL, encode_worker, &jobs[t]);
+    }
+    if (nthreads > 1)
+        for (int t = 0; t < nthreads; t++)
+            pthread_join(th[t], NULL);
+    return 0;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Pack (RDR tiering into tier-homogeneous pages).                           */
+/*                                                                           */
+/* [TS] 2.2 "Joint Optimization": every token/head state gets a residency    */
+/* bit z and a tier b; "Protection Constraints": a protected state is kept   */
+/* at the top tier; "Tier-Homogeneous Pages": retained states are grouped    */
+/* into pages that hold one tier each.  [ABS]: decisions are per token and   */
+/* head.  The pages give no solver.  Reading used here: each sequence comes   */
+/* with cumulative tier shares in basis points (fp16, +8-bit, +4-bit); the    */
+/* token counts are n_cum = floor((bp * T + 5000) / 10000); in every         */
+/* (sequence, kv-head) row the tokens are ranked by (protected first, higher  */
+/* utility score first, lower index first); the first n_cum[0] go to fp16,   */
+/* the next to 8-bit, then 4-bit, the rest are dropped.  Inside a tier the   */
+/* tokens keep index order and fill 16-slot pages; each row gains its fp16   */
+/* pages, then 8-bit, then 4-bit, after any pages it already had.  Pages of  */
+/* one call are numbered (sequence, head, tier, page) and take arena space   */
+/* by bump allocation in the order given by place_perm (identity if NULL).   */
+/* ------------------------------------------------------------------------ */
+
+typedef struct {
+    const float *score;
+    const uint8_t *prot;
+    int64_t stride; /* Hkv */
+} rank_ctx;
+
+static rank_ctx g_rank; /* qsort has no context argument; pack is serial */
+
+static int rank_cmp(const void *pa, const void *pb)
+{
+    int32_t a = *(const int32_t *)pa, b = *(const int32_t *)pb;
+    int pa_ = g_rank.prot ? g_rank.prot[a * g_rank.stride] : 0;
+    int pb_ = g_rank.prot ? g_rank.prot[b * g_rank.stride] : 0;
+    if (pa_ != pb_)
+        return pa_ > pb_ ? -1 : 1;
+    float sa = g_rank.score[a * g_rank.stride], sb = g_rank.score[b * g_rank.stride];
+    if (sa != sb)
+        return sa > sb ? -1 : 1;
+    return a < b ? -1 : (a > b ? 1 : 0);
+}
+
+static int idx_cmp(const void *pa, const void *pb)
+{
+    int32_t a = *(const int32_t *)pa, b = *(const int32_t *)pb;
+    return a < b ? -1 : (a > b ? 1 : 0);
+}
+
+/* int8 value quantiser for the 4-bit tier.  Reading: one scale per (token,
+ * head): amax = max |v|; scale = fp16(fp32(amax / 127)), saturating;
+ * q = clamp(rint_even(fp32(v / scale)), -127, 127); a zero scale gives q = 0.
+ * Carried out in binary32 as written (fp32 division, correctly rounded). */
+static void quant_v(int D, const uint16_t *v, int8_t *q, uint16_t *scale_out)
+{
+    float amax = 0.0f;
+    for (int d = 0; d < D; d++) {
+        float x = (float)bf16_to_double(v[d]);
+        float ax = fabsf(x);
+        if (ax > amax)
+            amax = ax;
+    }
+    float s32 = amax / 127.0f;
+    uint16_t sh = double_to_f16_sat((double)s32);
+    float s = (float)f16_to_double(sh);
+    *scale_out = sh;
+    for (int d = 0; d < D; d++) {
+        if (s == 0.0f) {
+            q[d] = 0;
+            continue;
+        }
+        float x = (float)bf16_to_double(v[d]);
+        float y = rintf(x / s);
+        if (y > 127.0f)
+            y = 127.0f;
+        if (y < -127.0f)
+            y = -127.0f;
+        q[d] = (int8_t)y;
+    }
+}
+
+/* Tier token counts for one sequence of T tokens: n_cum[0..2] cumulative. */
+void oracle_tier_counts(int64_t T, const int32_t *bp, int64_t *n_cum)
+{
+    for (int i = 0; i < 3; i++)
+        n_cum[i] = (bp[i] * T + 5000) / 10000;
+}
+
+/* Write one token's fields into slot t of a page. */
+static void put_slot(int D, int tier, uint8_t *page, int t, const uint16_t *k, const uint16_t *v,
+                     uint16_t r, const uint8_t *c8, const uint8_t *c4)
+{
+    int G = D / 8;
+    if (tier == 0 || tier == 3) {
+        for (int d = 0; d < D; d++) {
+            uint16_t kv = k[d];
+            if (tier == 3)
+                kv = double_to_bf16(f16_to_double(k[d]));
+            memcpy(page + wide_off(D, t, d), &kv, 2);
+        }
+    }
+    if (tier == 0 || tier == 1 || tier == 3) {
+        size_t base = off_v(D, tier);
+        for (int d = 0; d < D; d++)
+            memcpy(page + base + wide_off(D, t, d), &v[d], 2);
+    }
+    if (tier == 1) {
+        memcpy(page + off_codes(D, 1) + (size_t)t * G, c8, (size_t)G);
+        memcpy(page + off_radius(D, 1) + (size_t)t * 2, &r, 2);
+    }
+    if (tier == 2) {
+        int8_t q[128];
+        uint16_t sc;
+        quant_v(D, v, q, &sc);
+        for (int d = 0; d < D; d++)
+            page[narrow_off(D, t, d)] = (uint8_t)q[d];
+        memcpy(page + off_codes(D, 2) + (size_t)t * (G / 2), c4, (size_t)(G / 2));
+        memcpy(page + off_radius(D, 2) + (size_t)t * 2, &r, 2);
+        memcpy(page + off_vscale(D) + (size_t)t * 2, &sc, 2);
+    }
+}
+
+/* Return codes shared by pack and dense_pack. */
+enum { OR_OK = 0, OR_EINVAL = 1, OR_ENOSPACE = 3 };
+
+/*
+ * Pack one call's tokens into the cache.
+ *   cu_tokens[S+1]    token ranges of each sequence in the flat arrays
+ *   tier_cum_bp[S][3] cumulative basis points (fp16, +8-bit, +4-bit)
+ *   keys/values [N][Hkv][D] (fp16 / bf16), radius [N][Hkv], codes8 [N][Hkv][G],
+ *   codes4 [N][Hkv][G/2], scores [N][Hkv] (f32), protect [N][Hkv] or NULL,
+ *   place_perm [pages of this call] or NULL, pos_base [S] or NULL.
+ *   arena / arena_units / cursor (in/out, 128-byte units); page_table and
+ *   page_meta [S*Hkv][maxp]; num_pages [S*Hkv]; tier_tokens [S*Hkv][3];
+ *   slot_token [S*Hkv][maxp][16] or NULL.
+ * dense != 0 packs every token of the call into tier-3 pages instead.
+ */
+static int pack_impl(int D, int Hkv, int S, const int32_t *cu_tokens, const int32_t *tier_cum_bp,
+                     const uint16_t *keys, const uint16_t *values, const uint16_t *radius,
+                     const uint8_t *codes8, const uint8_t *codes4, const float *scores,
+                     const uint8_t *protect, const uint32_t *place_perm, const int64_t *pos_base,
+                     uint8_t *arena, uint64_t arena_units, uint64_t *cursor, uint32_t *page_table,
+                     uint8_t *page_meta, int32_t *num_pages, int32_t *tier_tokens,
+                     int32_t *slot_token, int maxp, int dense)
+{
+    int G = D / 8;
+    if ((D != 64 && D != 128) || Hkv <= 0 || S < 0 || maxp < 0)
+        return OR_EINVAL;
+    /* Per (sequence, head, tier): the token list of the tier in index order. */
+    int64_t rows = (int64_t)S * Hkv;
+    int64_t n_logical = 0;
+    int32_t **lists = calloc((size_t)rows * 3 + 1, sizeof(int32_t *));
+    int64_t *counts = calloc((size_t)rows * 3 + 1, sizeof(int64_t));
+    int rc = OR_OK;
+    for (int s = 0; s < S && rc == OR_OK; s++) {
+        int64_t b = cu_tokens[s], T = cu_tokens[s + 1] - cu_tokens[s];
+        if (T < 0) {
+            rc = OR_EINVAL;
+            break;
+        }
+        int64_t n_cum[3];
+        if (dense) { /* every token, index order, one list */
+            n_cum[0] = n_cum[1] = n_cum[2] = T;
+        } else {
+            const int32_t *bp = tier_cum_bp + 3 * s;
+            if (bp[0] < 0 || bp[0] > bp[1] || bp[1] > bp[2] || bp[2] > 10000) {
+                rc = OR_EINVAL;
+                break;
+            }
+            oracle_tier_counts(T, bp, n_cum);
+        }
+        for (int h = 0; h < Hkv; h++) {
+            int32_t *order = malloc((size_t)(T > 0 ? T : 1) * sizeof(int32_t));
+            for (int64_t i = 0; i < T; i++)
+                order[i] = (int32_t)i;
+            if (!dense) {
+                g_rank.score = scores + b * Hkv + h;
+                g_rank.prot = protect ? protect + b * Hkv + h : NULL;
+                g_rank.stride = Hkv;
+                qsort(order, (size_t)T, sizeof(int32_t), rank_cmp);
+                if (protect) {
+                    int64_t np = 0;
+                    for (int64_t i = 0; i < T; i++)
+                        np += protect[(b + i) * Hkv + h] != 0;
+                    if (np > n_cum[0])
+                        rc = OR_EINVAL;
+                }
+            }
+            int64_t lo = 0;
+            for (int tier = 0; tier < 3; tier++) {
+                int64_t hi = n_cum[tier];
+                int64_t n = hi - lo;
+                int32_t *lst = malloc((size_t)(n > 0 ? n : 1) * sizeof(int32_t));
+                memcpy(lst, order + lo, (size_t)n * sizeof(int32_t));
+                qsort(lst, (size_t)n, sizeof(int32_t), idx_cmp);
+                int64_t r = (int64_t)s * Hkv + h;
+                lists[r * 3 + tier] = lst;
+                counts[r * 3 + tier] = n;
+                n_logical += (n + SLOTS - 1) / SLOTS;
+                lo = hi;
+            }
+            free(order);
+        }
+    }
+    /* Logical page descriptors in (s, h, tier, page) order. */
+    int64_t *lp_row = malloc((size_t)(n_logical + 1) * sizeof(int64_t));
+    int *lp_tier = malloc((size_t)(n_logical + 1) * sizeof(int));
+    int64_t *lp_first = malloc((size_t)(n_logical + 1) * sizeof(int64_t)); /* first slot in tier list */
+    int64_t *lp_index = malloc((size_t)(n_logical + 1) * sizeof(int64_t)); /* page index in row */
+    int *lp_list = malloc((size_t)(n_logical + 1) * sizeof(int)); /* which tier list feeds it */
+    uint64_t *lp_off = malloc((size_t)(n_logical + 1) * sizeof(uint64_t));
+    if (rc == OR_OK) {
+        int64_t k = 0;
+        for (int64_t r = 0; r < rows && rc == OR_OK; r++) {
+            int64_t pi = num_pages[r];
+            for (int tier = 0; tier < 3; tier++) {
+                int64_t n = counts[r * 3 + tier];
+                for (int64_t f = 0; f < n; f += SLOTS) {
+                    lp_row[k] = r;
+                    lp_tier[k] = dense ? 3 : tier;
+                    lp_list[k] = tier;
+                    lp_first[k] = f;
+                    lp_index[k] = pi++;
+                    k++;
+                }
+            }
+            if (pi > maxp)
+                rc = OR_EINVAL;
+        }
+    }
+    /* Bump allocation in placement order. */
+    if (rc == OR_OK) {
+        uint64_t cur = *cursor;
+        char *seen = calloc((size_t)(n_logical + 1), 1);
+        for (int64_t k = 0; k < n_logical; k++) {
+            int64_t p = place_perm ? (int64_t)place_perm[k] : k;
+            if (p < 0 || p >= n_logical || seen[p]) {
+                rc = OR_EINVAL;
+                break;
+            }
+            seen[p] = 1;
+            lp_off[p] = cur;
+            cur += oracle_page_bytes(D, lp_tier[p]) / UNIT;
+        }
+        free(seen);
+        if (rc == OR_OK && cur > arena_units)
+            rc = OR_ENOSPACE;
+        if (rc == OR_OK && cur > 0xffffffffull)
+            rc = OR_ENOSPACE;
+        if (rc == OR_OK)
+            *cursor = cur;
+    }
+    /* Fill pages and tables. */
+    if (rc == OR_OK) {
+        for (int64_t k = 0; k < n_logical; k++) {
+            int64_t r = lp_row[k];
+            int s = (int)(r / Hkv), h = (int)(r % Hkv), tier = lp_tier[k];
+            int64_t b = cu_tokens[s];
+            const int32_t *lst = lists[r * 3 + lp_list[k]];
+            int64_t n = counts[r * 3 + lp_list[k]];
+            size_t bytes = oracle_page_bytes(D, tier);
+            uint8_t *page = arena + lp_off[k] * UNIT;
+            memset(page, 0, bytes);
+            int nv = (int)((n - lp_first[k]) < SLOTS ? (n - lp_first[k]) : SLOTS);
+            for (int t = 0; t < nv; t++) {
+                int64_t idx = lst[lp_first[k] + t];
+                int64_t e = (b + idx) * Hkv + h;
+                put_slot(D, tier, page, t, keys + e * D, values + e * D, radius ? radius[e] : 0,
+                         codes8 ? codes8 + e * G : NULL, codes4 ? codes4 + e * (G / 2) : NULL);
+            }
+            int64_t pi = lp_index[k];
+            page_table[r * maxp + pi] = (uint32_t)lp_off[k];
+            page_meta[r * maxp + pi] = (uint8_t)(tier | ((nv - 1) << 2));
+            if (slot_token) {
+                int64_t pb = pos_base ? pos_base[s] : 0;
+                for (int t = 0; t < SLOTS; t++)
+                    slot_token[(r * maxp + pi) * SLOTS + t] =
+                        t < nv ? (int32_t)(pb + lst[lp_first[k] + t]) : -1;
+            }
+        }
+        for (int64_t r = 0; r < rows; r++) {
+            for (int tier = 0; tier < 3; tier++) {
+                int64_t n = counts[r * 3 + tier];
+                num_pages[r] += (int32_t)((n + SLOTS - 1) / SLOTS);
+                if (!dense && tier_tokens)
+                    tier_tokens[r * 3 + tier] += (int32_t)n;
+            }
+        }
+    }
+    for (int64_t r = 0; r < rows * 3; r++)
+        free(lists[r]);
+    free(lists);
+    free(counts);
+    free(lp_row);
+    free(lp_tier);
+    free(lp_first);
+    free(lp_index);
+    free(lp_list);
+    free(lp_off);
+    return rc;
+}
+
+int oracle_pack(int D, int Hkv, int S, const int32_t *cu_tokens, const int32_t *tier_cum_bp,
+                const uint16_t *keys, const uint16_t *values, const uint16_t *radius,
+                const uint8_t *codes8, const uint8_t *codes4, const float *scores,
+                const uint8_t *protect, const uint32_t *place_perm, const int64_t *pos_base,
+                uint8_t *arena, uint64_t arena_units, uint64_t *cursor, uint32_t *page_table,
+                uint8_t *page_meta, int32_t *num_pages, int32_t *tier_tokens, int32_t *slot_token,
+                int maxp)
+{
+    return pack_impl(D, Hkv, S, cu_tokens, tier_cum_bp, keys, values, radius, codes8, codes4,
+                     scores, protect, place_perm, pos_base, arena, arena_units, cursor, page_table,
+                     page_meta, num_pages, tier_tokens, slot_token, maxp, 0);
+}
+
+/* Dense comparison cache: every token of the call, in index order, in tier-3
+ * pages (K converted fp16 -> bf16 with round-to-nearest-even, V bf16). */
+int oracle_dense_pack(int D, int Hkv, int S, const int32_t *cu_tokens, const uint16_t *keys,
+                      const uint16_t *values, const uint32_t *place_perm, uint8_t *arena,
+                      uint64_t arena_units, uint64_t *cursor, uint32_t *page_table,
+                      uint8_t *page_meta, int32_t *num_pages, int maxp)
+{
+    return pack_impl(D, Hkv, S, cu_tokens, NULL, keys, values, NULL, NULL, NULL, NULL, NULL,
+                     place_perm, NULL, arena, arena_units, cursor, page_table, page_meta,
+                     num_pages, NULL, NULL, maxp, 1);
+}
+
+/* ------------------------------------------------------------------------ */
+/* Decode.                                                                   */
+/*                                                                           */
+/* [TS] 2.1 "Compressed-Domain Similarity": the logit is computed from the   */
+/* codes as |q| * r~ * f_b(codes), f_b a cosine computed from the codes.     */
+/* With the encoding above that is                                          */
+/*     l(t) = sigma * r~_t * sum_g  q_g . C_g[code_{t,g}]                     */
+/*          = sigma * |q| * r~_t * (q/|q|) . u^(t),                           */
+/* u^ the concatenation of the chosen codewords, sigma the softmax scale.    */
+/* It is evaluated here through a per-(head, group) table                   */
+/* LUT_g[c] = q_g . C_g[c] as the formula groups it, and, separately, with   */
+/* the key direction rebuilt in full (logits_explicit) so tests can hold the */
+/* two against each other.  fp16-tier (and dense bf16) slots use the plain   */
+/* dot product sigma * q . k.  Attention over the retained slots is the      */
+/* ordinary softmax: out = sum_t e^(l_t - m) v^_t / sum_t e^(l_t - m),       */
+/* lse = m + ln sum_t e^(l_t - m), m = max_t l_t.  Dropped tokens are absent */
+/* from both sums.  A row with no retained slot gives out = 0, lse = -inf.   */
+/* v^ is the stored bf16 value, or int8 * scale in the 4-bit tier.           */
+/* Reading: no causal mask (decode attends to every cached token);          */
+/* q-head hq reads kv-head hq / (Hq / Hkv).                                 */
+/* ------------------------------------------------------------------------ */
+
+typedef struct {
+    int D, Hq, Hkv, S, maxp;
+    const uint8_t *arena;
+    const uint32_t *page_table;
+    const uint8_t *page_meta;
+    const int32_t *num_pages;
+    const float *cb8, *cb4;
+    const uint16_t *q; /* [S][Hq][D] bf16 */
+    double sigma;
+    double *out;             /* [S][Hq][D] */
+    double *lse;             /* [S][Hq] */
+    double *logits;          /* [S][Hq][maxp*16] or NULL */
+    double *logits_explicit; /* same, or NULL */
+} decode_args;
+
+static void decode_unit(const decode_args *a, int64_t unit)
+{
+    int D = a->D, G = D / 8, s = (int)(unit / a->Hq), hq = (int)(unit % a->Hq);
+    int hkv = hq / (a->Hq / a->Hkv);
+    int64_t row = (int64_t)s * a->Hkv + hkv;
+    double q[128];
+    for (int j = 0; j < D; j++)
+        q[j] = bf16_to_double(a->q[((int64_t)s * a->Hq + hq) * D + j]);
+    /* Per-group tables LUT_g[c] = q_g . C_g[c]: 256 entries (8-bit), 16 (4-bit). */
+    double *lut8 = malloc(sizeof(double) * (size_t)G * 256);
+    double *lut4 = malloc(sizeof(double) * (size_t)G * 16);
+    for (int g = 0; g < G; g++) {
+        for (int c = 0; c < 256; c++) {
+            const float *w = a->cb8 + (((size_t)hkv * G + g) * 256 + c) * 8;
+            double acc = 0;
+            for (int j = 0; j < 8; j++)
+                acc += q[8 * g + j] * (double)w[j];
+            lut8[g * 256 + c] = acc;
+        }
+        for (int c = 0; c < 16; c++) {
+            const float *w = a->cb4 + (((size_t)hkv * G + g) * 16 + c) * 8;
+            double acc = 0;
+            for (int j = 0; j < 8; j++)
+                acc += q[8 * g + j] * (double)w[j];
+            lut4[g * 16 + c] = acc;
+        }
+    }
+    int np = a->num_pages[row];
+    int64_t nslots = (int64_t)np * SLOTS;
+    double *lg = malloc(sizeof(double) * (size_t)(nslots > 0 ? nslots : 1));
+    double *vv = malloc(sizeof(double) * (size_t)(nslots > 0 ? nslots : 1) * D);
+    char *valid = calloc((size_t)(nslots > 0 ? nslots : 1), 1);
+    for (int p = 0; p < np; p++) {
+        const uint8_t *page = a->arena + (size_t)a->page_table[row * a->maxp + p] * UNIT;
+        uint8_t meta = a->page_meta[row * a->maxp + p];
+        int tier = meta & 3, nv = ((meta >> 2) & 15) + 1;
+        for (int t = 0; t < nv; t++) {
+            int64_t slot = (int64_t)p * SLOTS + t;
+            double l = 0, lx = 0;
+            if (tier == 0 || tier == 3) {
+                for (int d = 0; d < D; d++) {
+                    uint16_t kb;
+                    memcpy(&kb, page + wide_off(D, t, d), 2);
+                    l += q[d] * (tier == 0 ? f16_to_double(kb) : bf16_to_double(kb));
+                }
+                l *= a->sigma;
+                lx = l;
+            } else {
+                uint16_t rb;
+                memcpy(&rb, page + off_radius(D, tier) + (size_t)t * 2, 2);
+                double r = f16_to_double(rb);
+                const uint8_t *cd = page + off_codes(D, tier);
+                double sum = 0, dot = 0;
+                for (int g = 0; g < G; g++) {
+                    int c;
+                    const float *w;
+                    if (tier == 1) {
+                        c = cd[t * G + g];
+                        sum += lut8[g * 256 + c];
+                        w = a->cb8 + (((size_t)hkv * G + g) * 256 + c) * 8;
+                    } else {
+                        uint8_t byte = cd[t * (G / 2) + g / 2];
+                        c = g % 2 == 0 ? (byte & 15) : (byte >> 4);
+                        sum += lut4[g * 16 + c];
+                        w = a->cb4 + (((size_t)hkv * G + g) * 16 + c) * 8;
+                    }
+                    /* explicit form: rebuild the coded direction, then dot */
+                    for (int j = 0; j < 8; j++)
+                        dot += q[8 * g + j] * (double)w[j];
+                }
+                l = a->sigma * r * sum;
+                lx = a->sigma * r * dot;
+            }
+            lg[slot] = l;
+            valid[slot] = 1;
+            if (a->logits)
+                a->logits[((int64_t)s * a->Hq + hq) * a->maxp * SLOTS + slot] = l;
+            if (a->logits_explicit)
+                a->logits_explicit[((int64_t)s * a->Hq + hq) * a->maxp * SLOTS + slot] = lx;
+            double *v = vv + slot * D;
+            if (tier == 2) {
+                uint16_t sb;
+                memcpy(&sb, page + off_vscale(D) + (size_t)t * 2, 2);
+                double sc = f16_to_double(sb);
+                for (int d = 0; d < D; d++)
+                    v[d] = (double)(int8_t)page[narrow_off(D, t, d)] * sc;
+            } else {
+                for (int d = 0; d < D; d++) {
+                    uint16_t vb;
+                    memcpy(&vb, page + off_v(D, tier) + wide_off(D, t, d), 2);
+                    v[d] = bf16_to_double(vb);
+                }
+            }
+        }
+    }
+    double m = -INFINITY;
+    for (int64_t i = 0; i < nslots; i++)
+        if (valid[i] && lg[i] > m)
+            m = lg[i];
+    double *o = a->out + ((int64_t)s * a->Hq + hq) * D;
+    for (int d = 0; d < D; d++)
+        o[d] = 0;
+    if (m == -INFINITY) {
+        a->lse[(int64_t)s * a->Hq + hq] = -INFINITY;
+    } else {
+        double l = 0;
+        for (int64_t i = 0; i < nslots; i++) {
+            if (!valid[i])
+                continue;
+            double w = exp(lg[i] - m);
+            l += w;
+            for (int d = 0; d < D; d++)
+                o[d] += w * vv[i * D + d];
+        }
+        for (int d = 0; d < D; d++)
+            o[d] /= l;
+        a->lse[(int64_t)s * a->Hq + hq] = m + log(l);
+    }
+    free(lg);
+    free(vv);
+    free(valid);
+    free(lut8);
+    free(lut4);
+}
+
+typedef struct {
+    const decode_args *a;
+    int64_t begin, end;
+} decode_job;
+
+static void *decode_worker(void *p)
+{
+    decode_job *j = (decode_job *)p;
+    for (int64_t u = j->begin; u < j->end; u++)
+        decode_unit(j->a, u);
+    return NULL;
+}
+
+/* One decode step over a cache view.  units_begin/units_end select a range
+ * of (sequence, q-head) units, s * Hq + hq (for bounded samples); the rest
+ * of out/lse is left untouched.  nthreads > 1 runs independent units on
+ * separate threads.  Returns 0, or 1 on bad geometry. */
+int oracle_decode(int D, int Hq, int Hkv, int S, int maxp, const uint8_t *arena,
+                  const uint32_t *page_table, const uint8_t *page_meta, const int32_t *num_pages,
+                  const float *cb8, const float *cb4, const uint16_t *q, double sigma, double *out,
+                  double *lse, double *logits, double *logits_explicit, int64_t units_begin,
+                  int64_t units_end, int nthreads)
+{
+    if ((D != 64 && D != 128) || Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0 || S < 0)
+        return 1;
+    decode_args a = {D, Hq, Hkv, S, maxp, arena, page_table, page_meta, num_pages, cb8, cb4,
+                     q, sigma, out, lse, logits, logits_explicit};
+    int64_t n = units_end - units_begin;
+    if (n <= 0)
+        return 0;
+    if (nthreads < 1)
+        nthreads = 1;
+    if (nthreads > 256)
+        nthreads = 256;
+    if (nthreads > n)
+        nthreads = (int)n;
+    pthread_t th[256];
+    decode_job jobs[256];
+    for (int t = 0; t < nthreads; t++) {
+        jobs[t].a = &a;
+        jobs[t].begin = units_begin + n * t / nthreads;
+        jobs[t].end = units_begin + n * (t + 1) / nthreads;
+        if (nthreads == 1)
+            decode_worker(&jobs[t]);
+        else
+            pthread_create(&th[t], NULL, decode_worker, &jobs[t]);
+    }
+    if (nthreads > 1)
+        for (int t = 0; t < nthreads; t++)
+            pthread_join(th[t], NULL);
+    return 0;
+}
+
+/* Textbook attention of one query over an explicit token set:
+ * out = softmax(sigma * q K^T) V, lse = log-sum-exp of the logits.
+ * q[D], K[n][D], V[n][D] in double.  n = 0 gives out = 0, lse = -inf. */
+void oracle_dense_attention(int D, int64_t n, const double *q, const double *K, const double *V,
+                            double sigma, double *out, double *lse)
+{
+    double m = -INFINITY;
+    double *l = malloc(sizeof(double) * (size_t)(n > 0 ? n : 1));
+    for (int64_t i = 0; i < n; i++) {
+        double acc = 0;
+        for (int d = 0; d < D; d++)
+            acc += q[d] * K[i * D + d];
+        l[i] = sigma * acc;
+        if (l[i] > m)
+            m = l[i];
+    }
+    for (int d = 0; d < D; d++)
+        out[d] = 0;
+    if (n == 0) {
+        *lse = -INFINITY;
+        free(l);
+        return;
+    }
+    double z = 0;
+    for (int64_t i = 0; i < n; i++) {
+        double w = exp(l[i] - m);
+        z += w;
+        for (int d = 0; d < D; d++)
+            out[d] += w * V[i * D + d];
+    }
+    for (int d = 0; d < D; d++)
+        out[d] /= z;
+    *lse = m + log(z);
+    free(l);
+}
+
+/* Exposed number-format helpers, for the tests that pin them. */
+double oracle_f16_to_double(uint16_t h) { return f16_to_double(h); }
+uint16_t oracle_double_to_f16(double x) { return double_to_f16_sat(x); }
+double oracle_bf16_to_double(uint16_t b) { return bf16_to_double(b); }
+uint16_t oracle_double_to_bf16(double x) { return double_to_bf16(x); }
+void oracle_quant_v(int D, const uint16_t *v, int8_t *q, uint16_t *scale)
+{
+    quant_v(D, v, q, scale);
+}
+size_t oracle_wide_off(int D, int t, int d) { return wide_off(D, t, d); }
+size_t oracle_narrow_off(int D, int t, int d) { return narrow_off(D, t, d); }
