@@ -115,18 +115,19 @@ static uint16_t double_to_bf16(double x)
 /* from this description, in code of its own):                              */
 /*                                                                           */
 /* A page holds P = 16 slots of one (sequence, kv-head) row.  D is the head  */
-/* dimension (64 or 128), G = D/8 code groups, L = D/4.  Sizes are padded    */
-/* to 128 bytes, the page-table unit.                                        */
+/* dimension (64 or 128), G = D/8 code groups, B = D/8 dims per block.      */
+/* Sizes are padded to 128 bytes, the page-table unit.                       */
 /*   tier 0 (fp16 keys):   K fp16 "wide" section | V bf16 "wide" section      */
 /*   tier 1 (8-bit codes): V bf16 wide | codes u8 [16][G] | radius fp16 [16] */
 /*   tier 2 (4-bit codes): V int8 "narrow" | codes u8 [16][G/2] |            */
 /*                         radius fp16 [16] | value scale fp16 [16]          */
 /*   tier 3 (dense bf16, comparison path): K bf16 wide | V bf16 wide         */
-/* A "wide" section stores a 16 x D matrix of 2-byte elements in 16-byte     */
-/* chunks of 8 elements: element (t, d) is at byte                          */
-/*     ((d % L) / 8) * 1024 + ((d / L) * 16 + t) * 16 + (d % 8) * 2.         */
-/* A "narrow" section stores 16 x D bytes in 16-byte chunks of 16 elements:  */
-/*     ((d % L) / 16) * 1024 + ((d / L) * 16 + t) * 16 + (d % 16).           */
+/* A wide or narrow section stores a 16 x D matrix in 64 "lanes" of         */
+/* 16-byte chunks.  Element (t, d) belongs to lane (t % 8) * 8 + d / B and   */
+/* is element w = (t / 8) * B + d % B of that lane; the lane's elements are   */
+/* stored in chunks, chunk c of every lane together (1 KiB per c):           */
+/*   wide (2-byte elements):   byte (w / 8) * 1024 + lane * 16 + (w % 8) * 2  */
+/*   narrow (1-byte elements): byte (w / 16) * 1024 + lane * 16 + w % 16.     */
 /* 4-bit codes: byte b of a slot holds group 2b in its low nibble and group  */
 /* 2b+1 in its high nibble.  Slots past the page's valid count, and all      */
 /* padding, are zero.  The page's metadata byte is tier | (n_valid-1) << 2.  */
@@ -136,14 +137,18 @@ enum { SLOTS = 16, UNIT = 128 };
 
 static size_t wide_off(int D, int t, int d)
 {
-    int L = D / 4;
-    return (size_t)((d % L) / 8) * 1024 + (size_t)((d / L) * 16 + t) * 16 + (size_t)(d % 8) * 2;
+    int B = D / 8;
+    size_t lane = (size_t)(t % 8) * 8 + (size_t)(d / B);
+    size_t w = (size_t)(t / 8) * B + (size_t)(d % B);
+    return (w / 8) * 1024 + lane * 16 + (w % 8) * 2;
 }
 
 static size_t narrow_off(int D, int t, int d)
 {
-    int L = D / 4;
-    return (size_t)((d % L) / 16) * 1024 + (size_t)((d / L) * 16 + t) * 16 + (size_t)(d % 16);
+    int B = D / 8;
+    size_t lane = (size_t)(t % 8) * 8 + (size_t)(d / B);
+    size_t w = (size_t)(t / 8) * B + (size_t)(d % B);
+    return (w / 16) * 1024 + lane * 16 + (w % 16);
 }
 
 static size_t pad_unit(size_t b) { return (b + UNIT - 1) / UNIT * UNIT; }

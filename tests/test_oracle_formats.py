@@ -54,23 +54,22 @@ def test_bf16_round_trip_matches_torch():
 
 
 @pytest.mark.parametrize("D", [64, 128])
-def test_wide_and_narrow_sections_are_bijections_of_16_byte_rows(D):
-    L = D // 4
+def test_wide_and_narrow_sections_are_lane_chunked_bijections(D):
+    B = D // 8
     wide = np.array([[oracle.wide_off(D, t, d) for d in range(D)] for t in range(16)])
     narrow = np.array([[oracle.narrow_off(D, t, d) for d in range(D)] for t in range(16)])
     assert sorted(wide.ravel()) == list(range(0, 32 * D, 2))
     assert sorted(narrow.ravel()) == list(range(16 * D))
-    # every 16-byte chunk holds consecutive dims of one token, inside one
-    # quarter of the head dimension
-    for sec, per in ((wide, 8), (narrow, 16)):
-        chunk = sec // 16
-        for c in np.unique(chunk):
-            t, d = np.nonzero(chunk == c)
-            assert len(set(t)) == 1 and len(d) == per
-            assert np.array_equal(np.sort(d), np.arange(d.min(), d.min() + per))
-            assert d.min() // L == d.max() // L
-    # chunk index = i * 64 + (quarter * 16 + token): one 1 KiB block per i
-    assert wide[3, L + 8] == 1024 * 1 + (16 + 3) * 16
+    t, d = np.meshgrid(np.arange(16), np.arange(D), indexing="ij")
+    lane = (t % 8) * 8 + d // B
+    for sec, esz in ((wide, 2), (narrow, 1)):
+        # every element sits in its lane's 16-byte column of a 1 KiB block
+        assert np.array_equal((sec % 1024) // 16, lane)
+        # inside a lane: slot t % 8 first (t < 8), then t + 8; dims ascending
+        w = (sec // 1024) * (16 // esz) + (sec % 16) // esz
+        assert np.array_equal(w, (t // 8) * B + d % B)
+    # spot value: slot 9, dim B + 3 -> lane 9, element B + 3
+    assert wide[9, B + 3] == ((B + 3) // 8) * 1024 + 9 * 16 + ((B + 3) % 8) * 2
 
 
 def test_page_sizes():
