@@ -1,0 +1,276 @@
+"""Benchmark of the ADA decode step on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--workload 2|3] [--splits S]
+
+A step is one ada_decode call: code-table build, page stream, online softmax
+and split merge for every (sequence, query head) of the workload, one launch.
+The cache is built on the GPU (encode + pack) before timing; the timed region
+replays a HIP graph of decode steps over rotated copies of the page arena, so
+that repeated steps read HBM and not the 256 MiB Infinity Cache.  Prints one
+JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import compressed_kv_attention_amd as ada  # noqa: E402
+import synth  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0
+ROTATE_BYTES = 512 << 20  # at least this much distinct cache data per replay cycle
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def build_layer(cfg, layer, dev, dense=False):
+    """Generates one layer's inputs and builds its caches on the GPU."""
+    lens = synth.seq_lens(cfg)
+    cu = synth.cu_tokens(lens)
+    N = int(cu[-1])
+    H, D = cfg.num_kv_heads, cfg.head_dim
+    geom = ada.Geom(D, cfg.num_q_heads, H)
+    gen_dev = "cpu" if cfg.number <= 2 else dev
+    keys = synth.keys(cfg, layer, N, gen_dev).to(dev)
+    vals = synth.values(cfg, layer, N, gen_dev).to(dev)
+    scores = synth.scores(cfg, layer, N).to(dev)
+    q = synth.queries(cfg, layer, gen_dev).to(dev)
+    cb8, cb4 = (t.to(dev) for t in synth.codebooks(cfg, layer))
+    bp = synth.tier_mix(cfg)
+    r = torch.empty((N, H), dtype=torch.float16, device=dev)
+    c8 = torch.empty((N, H, D // 8), dtype=torch.uint8, device=dev)
+    c4 = torch.empty((N, H, D // 16), dtype=torch.uint8, device=dev)
+    ada.encode(geom, keys, cb8, cb4, r, c8, c4)
+    n_pages = ada.pack_num_pages(geom, cu, bp)
+    maxp = int(max(lens)) // 16 + 4
+    stored = 0
+    for s in range(cfg.num_seqs):
+        T = int(lens[s])
+        n = [(int(bp[s][k]) * T + 5000) // 10000 for k in range(3)]
+        cnt = [n[0], n[1] - n[0], n[2] - n[1]]
+        stored += H * sum((c + 15) // 16 * ada.page_bytes(D, k) for k, c in enumerate(cnt))
+    cache = ada.Cache(geom, cfg.num_seqs, maxp, stored)
+    ada.rdr_pack(geom, cache, cu, bp, keys, vals, r, c8, c4, scores,
+                 place_perm=synth.place_perm(cfg, layer, n_pages))
+    out = dict(geom=geom, cache=cache, cb8=cb8, cb4=cb4, q=q, lens=lens, cu=cu, N=N)
+    if dense:
+        dpages = H * sum((int(T) + 15) // 16 for T in lens)
+        dcache = ada.Cache(geom, cfg.num_seqs, maxp, dpages * ada.page_bytes(D, 3))
+        ada.dense_pack(geom, dcache, cu, keys, vals)
+        out["dense"] = dcache
+    torch.cuda.synchronize()
+    del keys, vals, scores, r, c8, c4
+    return out
+
+
+def time_graph(step_fns, steps, warmup):
+    """Captures one call of every fn in step_fns into a graph, replays it
+    enough times for `steps` steps; returns (steps run, seconds, per-step ms
+    from events)."""
+    for f in step_fns:  # eager warm-up (also sets kernel attributes)
+        f()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            for f in step_fns:
+                f()
+    torch.cuda.synchronize()
+    reps = max(1, math.ceil(steps / len(step_fns)))
+    wreps = max(1, math.ceil(warmup / len(step_fns)))
+    for _ in range(wreps):
+        g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    e0.record()
+    for _ in range(reps):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    n = reps * len(step_fns)
+    return n, wall, e0.elapsed_time(e1) / n
+
+
+def kernel_event_ms(step_fns, n):
+    """Average duration of single decode launches, each bracketed by events
+    on the launch stream (eager launches; the GPU timestamps the events)."""
+    st = torch.cuda.current_stream()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+    for i in range(n):
+        evs[i][0].record(st)
+        step_fns[i % len(step_fns)]()
+        evs[i][1].record(st)
+    torch.cuda.synchronize()
+    ts = sorted(a.elapsed_time(b) for a, b in evs)
+    return float(np.median(ts)), float(np.mean(ts))
+
+
+def cpu_baseline(cfg, layer, seconds_target=10.0):
+    """The CPU oracle (test infrastructure) timed on this host on a bounded
+    sample: whole decode steps of the same workload on oracle-built pages."""
+    sys.path.insert(0, os.path.join(ROOT, "tests"))
+    import oracle
+    lens = synth.seq_lens(cfg)
+    if cfg.number > 2:
+        return None
+    cu = synth.cu_tokens(lens)
+    N = int(cu[-1])
+    keys = synth.keys(cfg, layer, N)
+    vals = synth.values(cfg, layer, N)
+    scores = synth.scores(cfg, layer, N)
+    q = synth.queries(cfg, layer)
+    cb8, cb4 = synth.codebooks(cfg, layer)
+    threads = min(os.cpu_count() or 1, 16)
+    r, c8, c4 = oracle.encode(keys, cb8, cb4, nthreads=threads)
+    hc = oracle.HostCache(cfg.head_dim, cfg.num_kv_heads, cfg.num_seqs, int(max(lens)) // 16 + 4,
+                          N * cfg.num_kv_heads * 512 + (1 << 20), slot_tokens=False)
+    assert oracle.pack(hc, cu, synth.tier_mix(cfg), keys, vals, r, c8, c4, scores) == 0
+    units = cfg.num_seqs * cfg.num_q_heads
+    threads = min(threads, units)
+    reps, t = 0, 0.0
+    res = None
+    while t < seconds_target and reps < 50:
+        t0 = time.perf_counter()
+        res = oracle.decode(hc, cb8, cb4, q, cfg.sigma, nthreads=threads)
+        t += time.perf_counter() - t0
+        reps += 1
+    tokens = int(lens.sum())
+    return dict(value=tokens * reps / t, unit="KV tokens/s", cores=threads, kind="oracle",
+                sample=f"{reps} whole decode steps of the workload (all {units} query heads, "
+                       f"T={tokens}), double precision, {threads} threads"), res
+
+
+def algorithmic_bytes(L, cfg):
+    """Bytes one decode step must move: stored pages, codebooks, page table
+    and metadata, queries, outputs."""
+    cache = L["cache"]
+    pages = int(cache.num_pages_host.sum())
+    G = cfg.head_dim // 8
+    cb = cfg.num_kv_heads * G * (256 + 16) * 8 * 4
+    qb = cfg.num_seqs * cfg.num_q_heads * cfg.head_dim * 2
+    ob = cfg.num_seqs * cfg.num_q_heads * (cfg.head_dim + 1) * 4
+    return cache.used_bytes() + cb + pages * 5 + qb + ob
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", type=int, default=2)
+    ap.add_argument("--splits", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-dense", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: the ADA decode path has no multi-GPU mode "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    ada.load()
+    cfg = synth.WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    log(f"workload {cfg.number} {cfg.name}: building cache on the GPU")
+    L = build_layer(cfg, 0, dev, dense=not args.no_dense)
+    geom, cache = L["geom"], L["cache"]
+    used = cache.used_bytes()
+    n_copies = max(2, math.ceil(ROTATE_BYTES / max(used, 1)) + 1)
+    arenas = [cache.arena] + [cache.arena.clone() for _ in range(n_copies - 1)]
+    views = [cache.view(a) for a in arenas]
+    S, Hq, D = cfg.num_seqs, cfg.num_q_heads, cfg.head_dim
+    out = torch.empty((S, Hq, D), device=dev)
+    lse = torch.empty((S, Hq), device=dev)
+    ws = torch.zeros(ada.decode_workspace_size(geom, S, cache.maxp, args.splits), dtype=torch.uint8,
+                     device=dev)
+    splits = args.splits or ada.decode_default_splits(geom, S, cache.maxp)
+
+    def make_step(v):
+        return lambda: ada.decode(geom, cache, L["cb8"], L["cb4"], L["q"], cfg.sigma, out, lse,
+                                  num_splits=args.splits, ws=ws, view=v)
+
+    fns = [make_step(v) for v in views]
+    log(f"stored {used / 1e6:.2f} MB in {int(cache.num_pages_host.sum())} pages; "
+        f"{n_copies} arena copies; {splits} splits per row")
+    steps, wall, ms_graph = time_graph(fns, args.steps, args.warmup)
+    k_med, k_mean = kernel_event_ms(fns, max(50, 2 * n_copies))
+    tokens = int(L["lens"].sum())
+    value = tokens / (ms_graph / 1e3)
+    alg = algorithmic_bytes(L, cfg)
+    achieved = alg / (k_mean / 1e3) / 1e9
+    log(f"step {ms_graph * 1e3:.2f} us (graph), kernel {k_mean * 1e3:.2f} us mean / "
+        f"{k_med * 1e3:.2f} us median (events), {achieved:.0f} GB/s")
+
+    result = {
+        "metric": "ADA decode KV tokens/s per step",
+        "value": value,
+        "unit": "KV tokens/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_graph,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp32",
+        "data": "synthetic",
+        "config": {"workload": cfg.name, "num_seqs": S, "seq_len": int(L["lens"].max()),
+                   "tokens_per_step": tokens, "num_q_heads": Hq, "num_kv_heads": cfg.num_kv_heads,
+                   "head_dim": D, "tier_cum_bp": list(map(int, synth.tier_mix(cfg)[0])),
+                   "splits": splits, "arena_copies": n_copies},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "kernel": "decode_main<128,4,false>", "kernel_us_mean": k_mean * 1e3,
+                     "bytes_per_launch": alg},
+        "stored_bytes": used,
+        "stored_fraction_of_dense": used / (tokens * cfg.num_kv_heads * 512),
+    }
+    if "dense" in L:
+        dc = L["dense"]
+        dused = dc.used_bytes()
+        dcop = max(2, math.ceil(ROTATE_BYTES / dused) + 1)
+        darenas = [dc.arena] + [dc.arena.clone() for _ in range(dcop - 1)]
+        dws = torch.zeros(ada.decode_workspace_size(geom, S, dc.maxp, args.splits), dtype=torch.uint8,
+                          device=dev)
+        dfns = [(lambda v=dc.view(a): ada.dense_decode(geom, dc, L["q"], cfg.sigma, out, lse,
+                                                      num_splits=args.splits, ws=dws, view=v))
+                for a in darenas]
+        _, _, dms = time_graph(dfns, args.steps, args.warmup)
+        result["dense_bf16_baseline"] = {"ms_per_step": dms, "value": tokens / (dms / 1e3),
+                                         "stored_bytes": dused,
+                                         "achieved_GBs": dused / (dms / 1e3) / 1e9,
+                                         "ada_speedup": dms / ms_graph}
+        del darenas
+    torch.cuda.synchronize()
+    # numerics check of the timed outputs against the oracle (CPU baseline leg)
+    if not args.no_cpu_baseline:
+        cb = cpu_baseline(cfg, 0)
+        if cb is not None:
+            base, res = cb
+            result["cpu_baseline"] = base
+            ada.decode(geom, cache, L["cb8"], L["cb4"], L["q"], cfg.sigma, out, lse,
+                       num_splits=args.splits, ws=ws)
+            torch.cuda.synchronize()
+            result["parity_out_max_abs"] = float(np.abs(out.cpu().double().numpy() - res["out"]).max())
+    print(json.dumps(result))
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,300 @@
+"""ADA (Angle-Domain Attention) decode path for MI355X -- Python binding.
+
+This module only marshals arguments into libada (include/ada.h): every step
+of encode, pack and decode runs in the library's gfx950 kernels.  PyTorch
+provides device memory and the current stream.  There is no fallback: if
+libada.so is missing or fails to load, every call raises.
+
+Method: SPHERICAL KV (arXiv 2605.18856) -- gist.science technical summary,
+sections 2.1 (keys as radius + angle codes; logits from the codes without
+rebuilding keys) and 2.2 (per-state keep/drop and tier; tier-homogeneous
+pages).
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+
+import numpy as np
+import torch
+
+__all__ = [
+    "AdaError", "Geom", "Cache", "load", "lib_path", "page_bytes", "encode", "pack_num_pages",
+    "pack_workspace_size", "rdr_pack", "dense_pack", "decode_default_splits",
+    "decode_workspace_size", "decode", "dense_decode",
+]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libada.so")
+_lib = None
+
+OK, EINVAL, EUNSUPPORTED, ENOSPACE, EWORKSPACE, EHIP = range(6)
+
+
+class AdaError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what}: {load().ada_status_str(status).decode()} (status {status})")
+
+
+class Geom(C.Structure):
+    _fields_ = [("head_dim", C.c_int32), ("num_q_heads", C.c_int32),
+                ("num_kv_heads", C.c_int32), ("page_size", C.c_int32)]
+
+    def __init__(self, head_dim, num_q_heads, num_kv_heads, page_size=16):
+        super().__init__(head_dim, num_q_heads, num_kv_heads, page_size)
+
+
+class _CacheView(C.Structure):
+    _fields_ = [("arena", C.c_void_p), ("arena_units", C.c_uint64),
+                ("page_table", C.c_void_p), ("page_meta", C.c_void_p),
+                ("num_pages", C.c_void_p), ("tier_tokens", C.c_void_p),
+                ("slot_token", C.c_void_p), ("num_seqs", C.c_int32),
+                ("max_pages_per_head", C.c_int32)]
+
+
+def lib_path() -> str:
+    return _LIB_PATH
+
+
+def load():
+    """Loads libada.so once; raises if it is not built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            raise ImportError(f"{_LIB_PATH} is missing: build it with "
+                              "`python -m compressed_kv_attention_amd.build`")
+        L = C.CDLL(_LIB_PATH)
+        P, I32, I64, U64, SZ, F = C.c_void_p, C.c_int32, C.c_int64, C.c_uint64, C.c_size_t, C.c_float
+        G = C.POINTER(Geom)
+        CV = C.POINTER(_CacheView)
+        L.ada_status_str.argtypes = [C.c_int]
+        L.ada_status_str.restype = C.c_char_p
+        L.ada_version.restype = C.c_int
+        L.ada_page_bytes.argtypes = [I32, I32]
+        L.ada_page_bytes.restype = SZ
+        L.ada_encode.argtypes = [G, I64, P, P, P, P, P, P, P]
+        L.ada_encode.restype = C.c_int
+        L.rdr_pack_num_pages.argtypes = [G, I32, P, P, P]
+        L.rdr_pack_num_pages.restype = C.c_int
+        L.rdr_pack_workspace_size.argtypes = [G, I64, I32]
+        L.rdr_pack_workspace_size.restype = SZ
+        L.rdr_pack.argtypes = [G, CV, I32, P, P, P, P, P, P, P, P, P, P, P, P, P, P, SZ, P]
+        L.rdr_pack.restype = C.c_int
+        L.dense_pack.argtypes = [G, CV, I32, P, P, P, P, P, P, P, SZ, P]
+        L.dense_pack.restype = C.c_int
+        L.ada_decode_default_splits.argtypes = [G, I32, I32]
+        L.ada_decode_default_splits.restype = I32
+        L.ada_decode_workspace_size.argtypes = [G, I32, I32, I32]
+        L.ada_decode_workspace_size.restype = SZ
+        L.ada_decode.argtypes = [G, CV, P, P, P, F, P, P, P, I32, P, SZ, P]
+        L.ada_decode.restype = C.c_int
+        L.dense_decode.argtypes = [G, CV, P, F, P, P, P, I32, P, SZ, P]
+        L.dense_decode.restype = C.c_int
+        _lib = L
+    return _lib
+
+
+def _check(status: int, what: str):
+    if status != OK:
+        raise AdaError(status, what)
+
+
+def _dev(t: torch.Tensor | None, name: str, dtypes=None, device=None):
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor) or t.device.type != "cuda":
+        raise TypeError(f"{name} must be a CUDA (HIP) tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtypes is not None and t.dtype not in dtypes:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected one of {dtypes}")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    return C.c_void_p(t.data_ptr())
+
+
+def _host(a, dtype, name: str):
+    if a is None:
+        return None, None
+    arr = np.ascontiguousarray(a, dtype=dtype)
+    return arr, arr.ctypes.data_as(C.c_void_p)
+
+
+def _stream(stream) -> C.c_void_p:
+    s = torch.cuda.current_stream() if stream is None else stream
+    return C.c_void_p(s.cuda_stream)
+
+
+def page_bytes(head_dim: int, tier: int) -> int:
+    return int(load().ada_page_bytes(head_dim, tier))
+
+
+class Cache:
+    """One layer's paged cache on a device, allocated with torch, plus the
+    host-side allocator state (arena cursor, per-row page counts) that pack
+    calls advance.  `view()` gives the C struct the library reads."""
+
+    def __init__(self, geom: Geom, num_seqs: int, max_pages_per_head: int, arena_bytes: int,
+                 device="cuda", slot_tokens: bool = False):
+        self.geom = geom
+        self.num_seqs = num_seqs
+        self.maxp = max_pages_per_head
+        rows = num_seqs * geom.num_kv_heads
+        arena_bytes = (arena_bytes + 127) // 128 * 128
+        dev = torch.device(device)
+        self.arena = torch.zeros(arena_bytes, dtype=torch.uint8, device=dev)
+        self.page_table = torch.zeros((rows, max(1, max_pages_per_head)), dtype=torch.int32, device=dev)
+        self.page_meta = torch.zeros((rows, max(1, max_pages_per_head)), dtype=torch.uint8, device=dev)
+        self.num_pages = torch.zeros(max(1, rows), dtype=torch.int32, device=dev)
+        self.tier_tokens = torch.zeros((max(1, rows), 3), dtype=torch.int32, device=dev)
+        self.slot_token = (torch.full((rows, max(1, max_pages_per_head), 16), -1, dtype=torch.int32,
+                                      device=dev) if slot_tokens else None)
+        self.cursor = np.zeros(1, dtype=np.uint64)
+        self.num_pages_host = np.zeros(max(1, rows), dtype=np.int32)
+
+    @property
+    def arena_units(self) -> int:
+        return self.arena.numel() // 128
+
+    def used_bytes(self) -> int:
+        return int(self.cursor[0]) * 128
+
+    def view(self, arena: torch.Tensor | None = None) -> _CacheView:
+        """C view; `arena` may substitute a same-size copy of the arena
+        (same page table), e.g. to rotate copies in a benchmark."""
+        ar = self.arena if arena is None else arena
+        if ar.numel() != self.arena.numel():
+            raise ValueError("substitute arena must have the same size")
+        return _CacheView(ar.data_ptr(), ar.numel() // 128, self.page_table.data_ptr(),
+                          self.page_meta.data_ptr(), self.num_pages.data_ptr(),
+                          self.tier_tokens.data_ptr(),
+                          self.slot_token.data_ptr() if self.slot_token is not None else None,
+                          self.num_seqs, self.maxp)
+
+
+def encode(geom: Geom, keys, cb8, cb4, radius, codes8, codes4, stream=None):
+    """keys [N][Hkv][D] fp16 -> radius [N][Hkv] fp16 bits, codes8 [N][Hkv][G]
+    u8, codes4 [N][Hkv][G/2] u8 (outputs preallocated)."""
+    n = keys.shape[0]
+    H, D = geom.num_kv_heads, geom.head_dim
+    if tuple(keys.shape) != (n, H, D):
+        raise ValueError(f"keys shape {tuple(keys.shape)} != {(n, H, D)}")
+    for t, shape, name in ((radius, (n, H), "radius"), (codes8, (n, H, D // 8), "codes8"),
+                           (codes4, (n, H, D // 16), "codes4"),
+                           (cb8, (H, D // 8, 256, 8), "cb8"), (cb4, (H, D // 8, 16, 8), "cb4")):
+        if tuple(t.shape) != shape:
+            raise ValueError(f"{name} shape {tuple(t.shape)} != {shape}")
+    st = load().ada_encode(C.byref(geom), n, _dev(keys, "keys", (torch.float16,)),
+                           _dev(cb8, "cb8", (torch.float32,)), _dev(cb4, "cb4", (torch.float32,)),
+                           _dev(radius, "radius", (torch.float16, torch.int16)),
+                           _dev(codes8, "codes8", (torch.uint8,)), _dev(codes4, "codes4", (torch.uint8,)),
+                           _stream(stream))
+    _check(st, "ada_encode")
+
+
+def pack_num_pages(geom: Geom, cu_tokens, tier_cum_bp) -> int:
+    cu, cup = _host(cu_tokens, np.int32, "cu_tokens")
+    bp, bpp = _host(tier_cum_bp, np.int32, "tier_cum_bp")
+    out = C.c_int64(0)
+    _check(load().rdr_pack_num_pages(C.byref(geom), len(cu) - 1, cup, bpp, C.byref(out)),
+           "rdr_pack_num_pages")
+    return out.value
+
+
+def pack_workspace_size(geom: Geom, n_tokens: int, num_seqs: int) -> int:
+    return int(load().rdr_pack_workspace_size(C.byref(geom), n_tokens, num_seqs))
+
+
+def _workspace(nbytes: int, device) -> torch.Tensor:
+    # zero-filled: the decode workspace starts with split counters that must
+    # read zero before its first use
+    return torch.zeros(max(256, nbytes), dtype=torch.uint8, device=device)
+
+
+def rdr_pack(geom: Geom, cache: Cache, cu_tokens, tier_cum_bp, keys, values, radius, codes8, codes4,
+             scores, protect=None, place_perm=None, pos_base=None, ws=None, stream=None):
+    """Appends one call's tokens to `cache` (see rdr_pack in include/ada.h).
+    cu_tokens / tier_cum_bp / protect / place_perm / pos_base are host arrays."""
+    cu, cup = _host(cu_tokens, np.int32, "cu_tokens")
+    bp, bpp = _host(tier_cum_bp, np.int32, "tier_cum_bp")
+    n = int(cu[-1])
+    pr, prp = _host(protect, np.uint8, "protect")
+    pp, ppp = _host(place_perm, np.uint32, "place_perm")
+    pb, pbp = _host(pos_base, np.int64, "pos_base")
+    if ws is None:
+        ws = _workspace(pack_workspace_size(geom, n, len(cu) - 1), cache.arena.device)
+    view = cache.view()
+    st = load().rdr_pack(
+        C.byref(geom), C.byref(view), len(cu) - 1, cup, bpp,
+        _dev(keys, "keys", (torch.float16,)), _dev(values, "values", (torch.bfloat16,)),
+        _dev(radius, "radius", (torch.float16, torch.int16)), _dev(codes8, "codes8", (torch.uint8,)),
+        _dev(codes4, "codes4", (torch.uint8,)), _dev(scores, "scores", (torch.float32,)),
+        prp, ppp, pbp, cache.cursor.ctypes.data_as(C.c_void_p),
+        cache.num_pages_host.ctypes.data_as(C.c_void_p), _dev(ws, "ws"), ws.numel(), _stream(stream))
+    _check(st, "rdr_pack")
+    return ws
+
+
+def dense_pack(geom: Geom, cache: Cache, cu_tokens, keys, values, place_perm=None, ws=None, stream=None):
+    cu, cup = _host(cu_tokens, np.int32, "cu_tokens")
+    n = int(cu[-1])
+    pp, ppp = _host(place_perm, np.uint32, "place_perm")
+    if ws is None:
+        ws = _workspace(pack_workspace_size(geom, n, len(cu) - 1), cache.arena.device)
+    view = cache.view()
+    st = load().dense_pack(C.byref(geom), C.byref(view), len(cu) - 1, cup,
+                           _dev(keys, "keys", (torch.float16,)), _dev(values, "values", (torch.bfloat16,)),
+                           ppp, cache.cursor.ctypes.data_as(C.c_void_p),
+                           cache.num_pages_host.ctypes.data_as(C.c_void_p), _dev(ws, "ws"), ws.numel(),
+                           _stream(stream))
+    _check(st, "dense_pack")
+    return ws
+
+
+def decode_default_splits(geom: Geom, num_seqs: int, max_pages_per_head: int) -> int:
+    return int(load().ada_decode_default_splits(C.byref(geom), num_seqs, max_pages_per_head))
+
+
+def decode_workspace_size(geom: Geom, num_seqs: int, max_pages_per_head: int, num_splits: int = 0) -> int:
+    return int(load().ada_decode_workspace_size(C.byref(geom), num_seqs, max_pages_per_head, num_splits))
+
+
+def _decode_args(geom, cache, q, out, lse, logits, ws, num_splits):
+    S, Hq, D = cache.num_seqs, geom.num_q_heads, geom.head_dim
+    if tuple(q.shape) != (S, Hq, D) or tuple(out.shape) != (S, Hq, D):
+        raise ValueError("q and out must be [S][Hq][D]")
+    if lse is not None and tuple(lse.shape) != (S, Hq):
+        raise ValueError("lse must be [S][Hq]")
+    if logits is not None and tuple(logits.shape) != (S, Hq, cache.maxp * 16):
+        raise ValueError("logits must be [S][Hq][max_pages_per_head*16]")
+    if ws is None:
+        ws = _workspace(decode_workspace_size(geom, S, cache.maxp, num_splits), q.device)
+    return ws
+
+
+def decode(geom: Geom, cache: Cache, cb8, cb4, q, softmax_scale: float, out, lse=None, logits=None,
+           num_splits: int = 0, ws=None, stream=None, view=None):
+    """One ADA decode step (ada_decode).  `view` may pass a prebuilt
+    cache.view(...) (e.g. with a rotated arena)."""
+    ws = _decode_args(geom, cache, q, out, lse, logits, ws, num_splits)
+    v = cache.view() if view is None else view
+    st = load().ada_decode(C.byref(geom), C.byref(v), _dev(cb8, "cb8", (torch.float32,)),
+                           _dev(cb4, "cb4", (torch.float32,)), _dev(q, "q", (torch.bfloat16,)),
+                           float(softmax_scale), _dev(out, "out", (torch.float32,)),
+                           _dev(lse, "lse", (torch.float32,)), _dev(logits, "logits", (torch.float32,)),
+                           num_splits, _dev(ws, "ws"), ws.numel(), _stream(stream))
+    _check(st, "ada_decode")
+    return ws
+
+
+def dense_decode(geom: Geom, cache: Cache, q, softmax_scale: float, out, lse=None, logits=None,
+                 num_splits: int = 0, ws=None, stream=None, view=None):
+    ws = _decode_args(geom, cache, q, out, lse, logits, ws, num_splits)
+    v = cache.view() if view is None else view
+    st = load().dense_decode(C.byref(geom), C.byref(v), _dev(q, "q", (torch.bfloat16,)),
+                             float(softmax_scale), _dev(out, "out", (torch.float32,)),
+                             _dev(lse, "lse", (torch.float32,)), _dev(logits, "logits", (torch.float32,)),
+                             num_splits, _dev(ws, "ws"), ws.numel(), _stream(stream))
+    _check(st, "dense_decode")
+    return ws

@@ -1,0 +1,441 @@
+// Host side of libada: argument checks, pack planning, launches.
+// Declarations and the contract of every entry point are in include/ada.h.
+#include "ada.h"
+#include "ada_internal.h"
+
+#include <algorithm>
+#include <cstring>
+#include <vector>
+
+namespace {
+
+using namespace ada;
+
+constexpr int kVersion = 100; // 0.1.0
+
+hipStream_t as_stream(void *s) { return reinterpret_cast<hipStream_t>(s); }
+
+bool geom_ok(const ada_geom *g)
+{
+    return g != nullptr && (g->head_dim == 64 || g->head_dim == 128) && g->num_kv_heads > 0 &&
+           g->num_q_heads > 0 && g->num_q_heads % g->num_kv_heads == 0 && g->page_size == kSlots;
+}
+
+bool gqa_supported(const ada_geom *g)
+{
+    const int r = g->num_q_heads / g->num_kv_heads;
+    return r == 1 || r == 2 || r == 4;
+}
+
+bool cache_ok(const ada_cache *c)
+{
+    return c != nullptr && c->arena != nullptr && c->page_table != nullptr &&
+           c->page_meta != nullptr && c->num_pages != nullptr && c->num_seqs >= 0 &&
+           c->max_pages_per_head >= 0 && c->arena_units <= (1ull << 32);
+}
+
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+int64_t tier_count(int64_t T, int32_t bp) { return (bp * T + 5000) / 10000; }
+
+// Upper bound on the pages one pack call can create.
+int64_t max_pack_pages(int Hkv, int64_t n_tokens, int32_t num_seqs)
+{
+    return (int64_t)Hkv * (n_tokens / kSlots + 3 * (int64_t)num_seqs + 1);
+}
+
+struct PlanBuf {
+    std::vector<uint8_t> blob; // [seqs][rows][pages] (each 256-byte aligned)
+    size_t seq_off = 0, row_off = 0, page_off = 0;
+    int n_pages = 0;
+    uint64_t cursor_after = 0;
+    std::vector<int32_t> new_pages_per_row;
+};
+
+size_t pack_workspace(int Hkv, int64_t n_tokens, int32_t num_seqs)
+{
+    const int64_t rows = (int64_t)num_seqs * Hkv;
+    size_t b = align256(sizeof(PackSeq) * (size_t)std::max<int32_t>(num_seqs, 1));
+    b += align256(sizeof(PackRow) * (size_t)std::max<int64_t>(rows, 1));
+    b += align256(sizeof(PackPage) * (size_t)max_pack_pages(Hkv, n_tokens, num_seqs));
+    b += align256((size_t)n_tokens * Hkv);                   // protect copy
+    b += align256((size_t)n_tokens * Hkv * sizeof(int32_t)); // dest
+    return b;
+}
+
+// Plans one pack call on the host: counts, page numbering, placement.
+// counts[s][3] per-tier token counts; returns ADA_OK or the error.
+ada_status plan_pack(const ada_geom *g, const ada_cache *c, int32_t S, const int32_t *cu,
+                     const std::vector<int64_t> &counts, bool dense, const uint32_t *perm,
+                     const int64_t *pos_base, uint64_t cursor, const int32_t *num_pages_host,
+                     PlanBuf &pb)
+{
+    const int H = g->num_kv_heads, D = g->head_dim;
+    const int64_t rows = (int64_t)S * H;
+    std::vector<PackSeq> seqs(S);
+    std::vector<PackRow> rowv(rows);
+    std::vector<PackPage> pages;
+    pb.new_pages_per_row.assign(rows, 0);
+    for (int s = 0; s < S; s++) {
+        seqs[s].begin = cu[s];
+        seqs[s].len = cu[s + 1] - cu[s];
+        int64_t acc = 0;
+        for (int k = 0; k < 3; k++) {
+            acc += counts[s * 3 + k];
+            seqs[s].n_cum[k] = (int32_t)acc;
+        }
+        seqs[s].pad = 0;
+        seqs[s].pos_base = pos_base ? pos_base[s] : 0;
+        for (int h = 0; h < H; h++) {
+            const int64_t r = (int64_t)s * H + h;
+            int32_t pi = num_pages_host[r];
+            for (int k = 0; k < 3; k++) {
+                const int64_t n = counts[s * 3 + k];
+                rowv[r].lp_first[k] = (int32_t)pages.size();
+                rowv[r].count[k] = (int32_t)n;
+                for (int64_t f = 0; f < n; f += kSlots) {
+                    PackPage p;
+                    p.off = 0;
+                    p.row = (int32_t)r;
+                    p.pi = pi++;
+                    const int nv = (int)std::min<int64_t>(kSlots, n - f);
+                    p.meta = (dense ? 3 : k) | ((nv - 1) << 2);
+                    pages.push_back(p);
+                }
+            }
+            if (pi > c->max_pages_per_head)
+                return ADA_EINVAL;
+            pb.new_pages_per_row[r] = pi - num_pages_host[r];
+        }
+    }
+    const int64_t n = (int64_t)pages.size();
+    if (n > INT32_MAX)
+        return ADA_EINVAL;
+    // placement in the given order
+    uint64_t cur = cursor;
+    if (perm != nullptr) {
+        std::vector<char> seen(n, 0);
+        for (int64_t k = 0; k < n; k++)
+            if (perm[k] >= (uint64_t)n || seen[perm[k]]++)
+                return ADA_EINVAL;
+    }
+    for (int64_t k = 0; k < n; k++) {
+        PackPage &p = pages[perm ? perm[k] : k];
+        p.off = (uint32_t)cur;
+        cur += (uint64_t)page_bytes(D, p.meta & 3) / kUnit;
+        if (cur > c->arena_units)
+            return ADA_ENOSPACE;
+    }
+    pb.n_pages = (int)n;
+    pb.cursor_after = cur;
+    pb.seq_off = 0;
+    pb.row_off = align256(sizeof(PackSeq) * (size_t)std::max(S, 1));
+    pb.page_off = pb.row_off + align256(sizeof(PackRow) * (size_t)std::max<int64_t>(rows, 1));
+    pb.blob.assign(pb.page_off + sizeof(PackPage) * (size_t)std::max<int64_t>(n, 1), 0);
+    std::memcpy(pb.blob.data() + pb.seq_off, seqs.data(), sizeof(PackSeq) * seqs.size());
+    std::memcpy(pb.blob.data() + pb.row_off, rowv.data(), sizeof(PackRow) * rowv.size());
+    std::memcpy(pb.blob.data() + pb.page_off, pages.data(), sizeof(PackPage) * pages.size());
+    return ADA_OK;
+}
+
+ada_status run_pack(const ada_geom *g, const ada_cache *c, int32_t S, const int32_t *cu,
+                    const std::vector<int64_t> &counts, bool dense, const uint16_t *keys,
+                    const uint16_t *values, const uint16_t *radius, const uint8_t *codes8,
+                    const uint8_t *codes4, const float *scores, const uint8_t *protect_host,
+                    const uint32_t *perm, const int64_t *pos_base, uint64_t *cursor,
+                    int32_t *num_pages_host, void *ws, size_t ws_bytes, void *stream)
+{
+    const int H = g->num_kv_heads;
+    const int64_t N = cu[S];
+    if (ws == nullptr || ws_bytes < pack_workspace(H, N, S) || (reinterpret_cast<uintptr_t>(ws) & 255))
+        return ADA_EWORKSPACE;
+    PlanBuf pb;
+    if (ada_status st = plan_pack(g, c, S, cu, counts, dense, perm, pos_base, *cursor,
+                                  num_pages_host, pb);
+        st != ADA_OK)
+        return st;
+    if (pb.n_pages > max_pack_pages(H, N, S))
+        return ADA_EWORKSPACE;
+    // workspace: [plan blob][protect][dest]
+    uint8_t *wsb = static_cast<uint8_t *>(ws);
+    const size_t blob_cap = align256(sizeof(PackSeq) * (size_t)std::max(S, 1)) +
+                            align256(sizeof(PackRow) * (size_t)std::max<int64_t>((int64_t)S * H, 1)) +
+                            align256(sizeof(PackPage) * (size_t)max_pack_pages(H, N, S));
+    uint8_t *prot_dev = wsb + blob_cap;
+    int32_t *dest = reinterpret_cast<int32_t *>(prot_dev + align256((size_t)N * H));
+    hipStream_t st = as_stream(stream);
+    // pageable host source: the runtime copies it before returning
+    if (hipMemcpyAsync(wsb, pb.blob.data(), pb.blob.size(), hipMemcpyHostToDevice, st) != hipSuccess)
+        return ADA_EHIP;
+    if (protect_host != nullptr && N > 0 &&
+        hipMemcpyAsync(prot_dev, protect_host, (size_t)N * H, hipMemcpyHostToDevice, st) != hipSuccess)
+        return ADA_EHIP;
+    PackPlan plan;
+    plan.seqs = reinterpret_cast<const PackSeq *>(wsb + pb.seq_off);
+    plan.rows = reinterpret_cast<const PackRow *>(wsb + pb.row_off);
+    plan.pages = reinterpret_cast<const PackPage *>(wsb + pb.page_off);
+    plan.protect = protect_host != nullptr ? prot_dev : nullptr;
+    plan.dest = dest;
+    plan.S = S;
+    plan.Hkv = H;
+    plan.D = g->head_dim;
+    plan.maxp = c->max_pages_per_head;
+    plan.n_pages = pb.n_pages;
+    plan.dense = dense ? 1 : 0;
+    plan.n_tokens = N;
+    PackData data{keys, values, radius, codes8, codes4, scores};
+    PackCache cache{c->arena, c->page_table, c->page_meta, c->num_pages, c->tier_tokens, c->slot_token};
+    if (launch_pack(plan, data, cache, st) != hipSuccess)
+        return ADA_EHIP;
+    *cursor = pb.cursor_after;
+    for (size_t r = 0; r < pb.new_pages_per_row.size(); r++)
+        num_pages_host[r] += pb.new_pages_per_row[r];
+    return ADA_OK;
+}
+
+bool cu_ok(int32_t S, const int32_t *cu)
+{
+    if (cu == nullptr || cu[0] != 0)
+        return false;
+    for (int s = 0; s < S; s++)
+        if (cu[s + 1] < cu[s])
+            return false;
+    return true;
+}
+
+bool counts_from_bp(int32_t S, const int32_t *cu, const int32_t *bp, std::vector<int64_t> &counts)
+{
+    counts.assign((size_t)S * 3, 0);
+    for (int s = 0; s < S; s++) {
+        const int32_t *b = bp + 3 * s;
+        if (b[0] < 0 || b[0] > b[1] || b[1] > b[2] || b[2] > 10000)
+            return false;
+        const int64_t T = cu[s + 1] - cu[s];
+        int64_t prev = 0;
+        for (int k = 0; k < 3; k++) {
+            const int64_t n = tier_count(T, b[k]);
+            counts[s * 3 + k] = n - prev;
+            prev = n;
+        }
+    }
+    return true;
+}
+
+int32_t default_splits(const ada_geom *g, int32_t S, int32_t maxp)
+{
+    const int64_t rows = (int64_t)S * g->num_kv_heads;
+    if (rows <= 0)
+        return 1;
+    int64_t n = (512 + rows - 1) / rows;
+    n = std::min<int64_t>(n, std::max<int64_t>(1, maxp / 8));
+    return (int32_t)std::max<int64_t>(1, std::min<int64_t>(n, 4096));
+}
+
+ada_status decode_common(const ada_geom *g, const ada_cache *c, const float *cb8, const float *cb4,
+                         const uint16_t *q, float scale, float *out, float *lse, float *logits,
+                         int32_t num_splits, void *ws, size_t ws_bytes, void *stream, bool dense)
+{
+    if (!geom_ok(g) || !cache_ok(c) || q == nullptr || out == nullptr || num_splits < 0)
+        return ADA_EINVAL;
+    if (!dense && (cb8 == nullptr || cb4 == nullptr))
+        return ADA_EINVAL;
+    if (!gqa_supported(g))
+        return ADA_EUNSUPPORTED;
+    const int32_t ns = num_splits > 0 ? num_splits : default_splits(g, c->num_seqs, c->max_pages_per_head);
+    const size_t need = ada_decode_workspace_size(g, c->num_seqs, c->max_pages_per_head, ns);
+    if (ws == nullptr || ws_bytes < need || (reinterpret_cast<uintptr_t>(ws) & 255))
+        return ADA_EWORKSPACE;
+    const int NH = g->num_q_heads / g->num_kv_heads;
+    const int64_t rows = (int64_t)c->num_seqs * g->num_kv_heads;
+    if (rows * ns > INT32_MAX)
+        return ADA_EINVAL;
+    DecodeArgs a;
+    a.arena = c->arena;
+    a.page_table = c->page_table;
+    a.page_meta = c->page_meta;
+    a.num_pages = c->num_pages;
+    a.cb8 = cb8;
+    a.cb4 = cb4;
+    a.q = q;
+    a.out = out;
+    a.lse = lse;
+    a.logits = logits;
+    // workspace: [counters][partial (m, l)][partial acc]
+    uint8_t *w = static_cast<uint8_t *>(ws);
+    a.counters = reinterpret_cast<unsigned *>(w);
+    w += align256((size_t)rows * sizeof(unsigned));
+    a.part_ml = reinterpret_cast<float *>(w);
+    w += align256((size_t)rows * ns * NH * 2 * sizeof(float));
+    a.part_acc = reinterpret_cast<float *>(w);
+    a.sigma = scale;
+    a.S = c->num_seqs;
+    a.Hq = g->num_q_heads;
+    a.Hkv = g->num_kv_heads;
+    a.maxp = c->max_pages_per_head;
+    a.nsplit = ns;
+    if (launch_decode(g->head_dim, NH, dense, a, as_stream(stream)) != hipSuccess)
+        return ADA_EHIP;
+    return ADA_OK;
+}
+
+} // namespace
+
+extern "C" {
+
+const char *ada_status_str(int status)
+{
+    switch (status) {
+    case ADA_OK: return "ok";
+    case ADA_EINVAL: return "invalid argument";
+    case ADA_EUNSUPPORTED: return "unsupported geometry";
+    case ADA_ENOSPACE: return "arena full";
+    case ADA_EWORKSPACE: return "workspace missing, misaligned or too small";
+    case ADA_EHIP: return "HIP launch or copy failed";
+    default: return "unknown status";
+    }
+}
+
+int ada_version(void) { return kVersion; }
+
+size_t ada_page_bytes(int32_t head_dim, int32_t tier)
+{
+    if ((head_dim != 64 && head_dim != 128) || tier < 0 || tier > 3)
+        return 0;
+    return (size_t)page_bytes(head_dim, tier);
+}
+
+ada_status ada_encode(const ada_geom *geom, int64_t n_tokens, const uint16_t *keys, const float *cb8,
+                      const float *cb4, uint16_t *radius, uint8_t *codes8, uint8_t *codes4,
+                      void *stream)
+{
+    if (!geom_ok(geom) || n_tokens < 0 || n_tokens > ((int64_t)1 << 40))
+        return ADA_EINVAL;
+    if (n_tokens == 0)
+        return ADA_OK;
+    if (!keys || !cb8 || !cb4 || !radius || !codes8 || !codes4)
+        return ADA_EINVAL;
+    if ((reinterpret_cast<uintptr_t>(keys) & 15) || (reinterpret_cast<uintptr_t>(codes8) & 1))
+        return ADA_EINVAL;
+    if ((n_tokens + 255) / 256 > INT32_MAX)
+        return ADA_EINVAL;
+    return launch_encode(geom->head_dim, geom->num_kv_heads, n_tokens, keys, cb8, cb4, radius, codes8,
+                         codes4, as_stream(stream)) == hipSuccess
+               ? ADA_OK
+               : ADA_EHIP;
+}
+
+ada_status rdr_pack_num_pages(const ada_geom *geom, int32_t num_seqs, const int32_t *cu_tokens_host,
+                              const int32_t *tier_cum_bp_host, int64_t *n_pages_out)
+{
+    if (!geom_ok(geom) || num_seqs < 0 || !cu_ok(num_seqs, cu_tokens_host) || !tier_cum_bp_host ||
+        !n_pages_out)
+        return ADA_EINVAL;
+    std::vector<int64_t> counts;
+    if (!counts_from_bp(num_seqs, cu_tokens_host, tier_cum_bp_host, counts))
+        return ADA_EINVAL;
+    int64_t n = 0;
+    for (int s = 0; s < num_seqs; s++)
+        for (int k = 0; k < 3; k++)
+            n += (counts[s * 3 + k] + kSlots - 1) / kSlots;
+    *n_pages_out = n * geom->num_kv_heads;
+    return ADA_OK;
+}
+
+size_t rdr_pack_workspace_size(const ada_geom *geom, int64_t n_tokens, int32_t num_seqs)
+{
+    if (!geom_ok(geom) || n_tokens < 0 || num_seqs < 0)
+        return 0;
+    return pack_workspace(geom->num_kv_heads, n_tokens, num_seqs);
+}
+
+ada_status rdr_pack(const ada_geom *geom, const ada_cache *cache, int32_t num_seqs,
+                    const int32_t *cu_tokens_host, const int32_t *tier_cum_bp_host,
+                    const uint16_t *keys, const uint16_t *values, const uint16_t *radius,
+                    const uint8_t *codes8, const uint8_t *codes4, const float *scores,
+                    const uint8_t *protect_host, const uint32_t *place_perm_host,
+                    const int64_t *pos_base_host, uint64_t *arena_cursor_host,
+                    int32_t *num_pages_host, void *ws, size_t ws_bytes, void *stream)
+{
+    if (!geom_ok(geom) || !cache_ok(cache) || num_seqs != cache->num_seqs || num_seqs < 0 ||
+        !cu_ok(num_seqs, cu_tokens_host) || !tier_cum_bp_host || !arena_cursor_host ||
+        !num_pages_host || cache->tier_tokens == nullptr)
+        return ADA_EINVAL;
+    const int64_t N = cu_tokens_host[num_seqs];
+    if (N > 0 && (!keys || !values || !radius || !codes8 || !codes4 || !scores))
+        return ADA_EINVAL;
+    if (N > 0 && (reinterpret_cast<uintptr_t>(cache->arena) & 255))
+        return ADA_EINVAL;
+    std::vector<int64_t> counts;
+    if (!counts_from_bp(num_seqs, cu_tokens_host, tier_cum_bp_host, counts))
+        return ADA_EINVAL;
+    if (protect_host != nullptr) {
+        const int H = geom->num_kv_heads;
+        for (int s = 0; s < num_seqs; s++)
+            for (int h = 0; h < H; h++) {
+                int64_t np = 0;
+                for (int64_t i = cu_tokens_host[s]; i < cu_tokens_host[s + 1]; i++)
+                    np += protect_host[i * H + h] != 0;
+                if (np > counts[s * 3])
+                    return ADA_EINVAL;
+            }
+    }
+    return run_pack(geom, cache, num_seqs, cu_tokens_host, counts, false, keys, values, radius, codes8,
+                    codes4, scores, protect_host, place_perm_host, pos_base_host, arena_cursor_host,
+                    num_pages_host, ws, ws_bytes, stream);
+}
+
+ada_status dense_pack(const ada_geom *geom, const ada_cache *cache, int32_t num_seqs,
+                      const int32_t *cu_tokens_host, const uint16_t *keys, const uint16_t *values,
+                      const uint32_t *place_perm_host, uint64_t *arena_cursor_host,
+                      int32_t *num_pages_host, void *ws, size_t ws_bytes, void *stream)
+{
+    if (!geom_ok(geom) || !cache_ok(cache) || num_seqs != cache->num_seqs || num_seqs < 0 ||
+        !cu_ok(num_seqs, cu_tokens_host) || !arena_cursor_host || !num_pages_host)
+        return ADA_EINVAL;
+    const int64_t N = cu_tokens_host[num_seqs];
+    if (N > 0 && (!keys || !values))
+        return ADA_EINVAL;
+    std::vector<int64_t> counts((size_t)num_seqs * 3, 0);
+    for (int s = 0; s < num_seqs; s++)
+        counts[s * 3] = cu_tokens_host[s + 1] - cu_tokens_host[s];
+    return run_pack(geom, cache, num_seqs, cu_tokens_host, counts, true, keys, values, nullptr,
+                    nullptr, nullptr, nullptr, nullptr, place_perm_host, nullptr, arena_cursor_host,
+                    num_pages_host, ws, ws_bytes, stream);
+}
+
+int32_t ada_decode_default_splits(const ada_geom *geom, int32_t num_seqs, int32_t max_pages_per_head)
+{
+    if (!geom_ok(geom) || num_seqs < 0 || max_pages_per_head < 0)
+        return 0;
+    return default_splits(geom, num_seqs, max_pages_per_head);
+}
+
+size_t ada_decode_workspace_size(const ada_geom *geom, int32_t num_seqs, int32_t max_pages_per_head,
+                                 int32_t num_splits)
+{
+    if (!geom_ok(geom) || num_seqs < 0 || max_pages_per_head < 0 || num_splits < 0)
+        return 0;
+    const int32_t ns = num_splits > 0 ? num_splits : default_splits(geom, num_seqs, max_pages_per_head);
+    const size_t rows = (size_t)num_seqs * geom->num_kv_heads;
+    const size_t NH = (size_t)(geom->num_q_heads / geom->num_kv_heads);
+    return align256(rows * sizeof(unsigned)) + align256(rows * ns * NH * 2 * sizeof(float)) +
+           align256(rows * ns * NH * geom->head_dim * sizeof(float));
+}
+
+ada_status ada_decode(const ada_geom *geom, const ada_cache *cache, const float *cb8, const float *cb4,
+                      const uint16_t *q, float softmax_scale, float *out, float *lse,
+                      float *logits_dbg, int32_t num_splits, void *ws, size_t ws_bytes, void *stream)
+{
+    return decode_common(geom, cache, cb8, cb4, q, softmax_scale, out, lse, logits_dbg, num_splits, ws,
+                         ws_bytes, stream, false);
+}
+
+ada_status dense_decode(const ada_geom *geom, const ada_cache *cache, const uint16_t *q,
+                        float softmax_scale, float *out, float *lse, float *logits_dbg,
+                        int32_t num_splits, void *ws, size_t ws_bytes, void *stream)
+{
+    return decode_common(geom, cache, nullptr, nullptr, q, softmax_scale, out, lse, logits_dbg,
+                         num_splits, ws, ws_bytes, stream, true);
+}
+
+} // extern "C"

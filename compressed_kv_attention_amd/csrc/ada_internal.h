@@ -1,0 +1,111 @@
+// Internal interface between the host entry points (ada_abi.cpp) and the
+// gfx950 kernels (decode.hip, encode.hip, pack.hip).  Not installed.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace ada {
+
+constexpr int kSlots = 16;      // slots per page
+constexpr int kUnit = 128;      // page-table unit, bytes
+constexpr int kCodes8 = 256;    // codewords per group, 8-bit tier
+constexpr int kCodes4 = 16;     // codewords per group, 4-bit tier
+constexpr int kLutCodes = kCodes8 + kCodes4;
+
+// Byte layout of one page (see include/ada.h for the format).
+struct PageLayout {
+    int bytes[4];
+    int codes_off[3];   // per tier; -1 where absent
+    int radius_off[3];
+    int vscale_off;     // tier 2
+    int v_off[4];       // V section per tier
+};
+
+__host__ __device__ constexpr int pad_unit(int b) { return (b + kUnit - 1) / kUnit * kUnit; }
+__host__ __device__ constexpr int page_bytes(int D, int tier)
+{
+    return tier == 0 || tier == 3 ? pad_unit(64 * D)
+         : tier == 1              ? pad_unit(32 * D + 2 * D + 32)
+         : tier == 2              ? pad_unit(16 * D + D + 64)
+                                  : 0;
+}
+__host__ __device__ constexpr int codes_off(int D, int tier) { return tier == 1 ? 32 * D : 16 * D; }
+__host__ __device__ constexpr int radius_off(int D, int tier)
+{
+    return tier == 1 ? 32 * D + 2 * D : 16 * D + D;
+}
+__host__ __device__ constexpr int vscale_off(int D) { return 16 * D + D + 32; }
+__host__ __device__ constexpr int v_off(int D, int tier) { return tier == 0 || tier == 3 ? 32 * D : 0; }
+
+struct DecodeArgs {
+    const uint8_t *arena;
+    const uint32_t *page_table;
+    const uint8_t *page_meta;
+    const int32_t *num_pages;
+    const float *cb8;
+    const float *cb4;
+    const uint16_t *q;
+    float *out;
+    float *lse;
+    float *logits;
+    float *part_ml;  // [rows][nsplit][NH][2]  (running max in log2 units, sum)
+    float *part_acc; // [rows][nsplit][NH][D]  (unnormalised output)
+    unsigned *counters; // [rows] splits finished; zero between calls
+    float sigma;
+    int S, Hq, Hkv, maxp, nsplit;
+};
+
+hipError_t launch_decode(int D, int NH, bool dense, const DecodeArgs &a, hipStream_t st);
+
+hipError_t launch_encode(int D, int Hkv, int64_t n_tokens, const uint16_t *keys, const float *cb8,
+                         const float *cb4, uint16_t *radius, uint8_t *codes8, uint8_t *codes4,
+                         hipStream_t st);
+
+// ---- pack ----------------------------------------------------------------
+// Host-built plan of one pack call, copied into the workspace.
+struct PackSeq {
+    int32_t begin;     // first flat token of the sequence in this call
+    int32_t len;       // T_s
+    int32_t n_cum[3];  // cumulative tier counts
+    int32_t pad;
+    int64_t pos_base;  // position recorded in slot_token for index 0
+};
+struct PackRow {
+    int32_t lp_first[3]; // logical index of the row's first page of each tier
+    int32_t count[3];    // tokens per tier
+};
+struct PackPage {
+    uint32_t off;        // arena offset, 128-byte units
+    int32_t row;
+    int32_t pi;          // page index inside the row
+    int32_t meta;        // tier | (valid - 1) << 2
+};
+struct PackPlan {
+    const PackSeq *seqs;
+    const PackRow *rows;
+    const PackPage *pages;
+    const uint8_t *protect; // [N][Hkv] or null
+    int32_t *dest;          // [N][Hkv]: logical page * 16 + slot, or -1
+    int S, Hkv, D, maxp, n_pages, dense;
+    int64_t n_tokens;
+};
+struct PackData {
+    const uint16_t *keys, *values, *radius;
+    const uint8_t *codes8, *codes4;
+    const float *scores;
+};
+struct PackCache {
+    uint8_t *arena;
+    uint32_t *page_table;
+    uint8_t *page_meta;
+    int32_t *num_pages;
+    int32_t *tier_tokens;
+    int32_t *slot_token;
+};
+
+hipError_t launch_pack(const PackPlan &plan, const PackData &data, const PackCache &cache,
+                       hipStream_t st);
+
+} // namespace ada

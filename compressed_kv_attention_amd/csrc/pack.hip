@@ -1,0 +1,296 @@
+// RDR pack for gfx950: per-row tiering and tier-homogeneous pages.
+//
+// SPHERICAL KV (arXiv 2605.18856), gist.science technical summary, section
+// 2.2: each (token, head) state gets a residency bit and a precision tier;
+// protected states are kept at the top tier; retained states are grouped into
+// pages of a single tier.  The abstract adds that the choice is made per token
+// and head under a fixed budget.  The pages give no solver: a row's tokens are
+// ranked by (protected, utility score, -index) and cut at the tier counts the
+// host computed from the sequence's cumulative basis points.
+//
+// Kernels, in stream order:
+//   pack_pages   one block per new page: zero its bytes, write its page-table
+//                entry and metadata byte, mark its slot_token entries empty;
+//   pack_rows    one thread per row: advance num_pages and tier_tokens;
+//   pack_rank    one 1024-thread block per row: radix-select the keys at the
+//                three tier boundaries (8 passes of 8 bits over 64-bit keys,
+//                exact because keys are unique), then walk the row in index
+//                order with a block-wide scan to give every token its tier
+//                page and slot (dest = logical page * 16 + slot, -1 = dropped);
+//   pack_scatter one wave per (token, head): copy or quantize its fields into
+//                its slot.
+#include "ada_internal.h"
+#include "numfmt.h"
+
+namespace ada {
+namespace {
+
+#pragma clang fp contract(off)
+
+__global__ __launch_bounds__(256) void pack_pages(PackPlan plan, PackCache cache)
+{
+    const PackPage pg = plan.pages[blockIdx.x];
+    const int tier = pg.meta & 3;
+    uint4 *base = reinterpret_cast<uint4 *>(cache.arena + (size_t)pg.off * kUnit);
+    const int n16 = page_bytes(plan.D, tier) / 16;
+    for (int i = threadIdx.x; i < n16; i += 256)
+        base[i] = make_uint4(0, 0, 0, 0);
+    const size_t slot = (size_t)pg.row * plan.maxp + pg.pi;
+    if (threadIdx.x == 0) {
+        cache.page_table[slot] = pg.off;
+        cache.page_meta[slot] = (uint8_t)pg.meta;
+    }
+    if (cache.slot_token != nullptr && threadIdx.x < kSlots)
+        cache.slot_token[slot * kSlots + threadIdx.x] = -1;
+}
+
+__global__ __launch_bounds__(256) void pack_rows(PackPlan plan, PackCache cache)
+{
+    const int row = blockIdx.x * 256 + threadIdx.x;
+    if (row >= plan.S * plan.Hkv)
+        return;
+    const PackRow rw = plan.rows[row];
+    int pages = 0;
+    for (int k = 0; k < 3; k++)
+        pages += (rw.count[k] + kSlots - 1) / kSlots;
+    cache.num_pages[row] += pages;
+    if (!plan.dense && cache.tier_tokens != nullptr)
+        for (int k = 0; k < 3; k++)
+            cache.tier_tokens[row * 3 + k] += rw.count[k];
+}
+
+// Order-preserving map of a finite float (with -0 == +0) to uint32.
+__device__ __forceinline__ uint32_t ord_score(float f)
+{
+    const uint32_t u = __float_as_uint(f + 0.0f);
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__device__ __forceinline__ uint64_t rank_key(const PackPlan &plan, const PackData &data,
+                                             size_t e, int i)
+{
+    const uint64_t prot = plan.protect != nullptr && plan.protect[e] != 0 ? 1ull : 0ull;
+    return (prot << 63) | ((uint64_t)ord_score(data.scores[e]) << 31) |
+           (uint64_t)(0x7fffffffu - (uint32_t)i);
+}
+
+__global__ __launch_bounds__(1024) void pack_rank(PackPlan plan, PackData data)
+{
+    __shared__ uint32_t hist[3][256];
+    __shared__ uint64_t prefix[3], mask[3], thr[3];
+    __shared__ int64_t krem[3];
+    __shared__ int has[3];
+    __shared__ int wave_tot[16][3];
+    __shared__ int running[3];
+
+    const int row = blockIdx.x;
+    const int s = row / plan.Hkv, h = row % plan.Hkv;
+    const PackSeq sq = plan.seqs[s];
+    const PackRow rw = plan.rows[row];
+    const int T = sq.len;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+
+    if (!plan.dense) {
+        if (tid < 3) {
+            has[tid] = sq.n_cum[tid] > 0;
+            krem[tid] = (int64_t)sq.n_cum[tid] - 1;
+            prefix[tid] = 0;
+            mask[tid] = 0;
+        }
+        __syncthreads();
+        for (int pass = 0; pass < 8; pass++) {
+            const int shift = 56 - 8 * pass;
+            for (int i = tid; i < 3 * 256; i += 1024)
+                (&hist[0][0])[i] = 0;
+            __syncthreads();
+            const uint64_t p0 = prefix[0], p1 = prefix[1], p2 = prefix[2];
+            const uint64_t m0 = mask[0], m1 = mask[1], m2 = mask[2];
+            for (int i = tid; i < T; i += 1024) {
+                const uint64_t K = rank_key(plan, data, ((size_t)sq.begin + i) * plan.Hkv + h, i);
+                const uint32_t dg = (uint32_t)(K >> shift) & 255u;
+                if (has[0] && (K & m0) == p0)
+                    atomicAdd(&hist[0][dg], 1u);
+                if (has[1] && (K & m1) == p1)
+                    atomicAdd(&hist[1][dg], 1u);
+                if (has[2] && (K & m2) == p2)
+                    atomicAdd(&hist[2][dg], 1u);
+            }
+            __syncthreads();
+            if (tid < 3 && has[tid]) {
+                int64_t cum = 0;
+                for (int dg = 255; dg >= 0; dg--) {
+                    const int64_t c = hist[tid][dg];
+                    if (cum + c > krem[tid]) {
+                        prefix[tid] |= (uint64_t)dg << shift;
+                        mask[tid] |= 255ull << shift;
+                        krem[tid] -= cum;
+                        break;
+                    }
+                    cum += c;
+                }
+            }
+            __syncthreads();
+        }
+        if (tid < 3)
+            thr[tid] = prefix[tid];
+    }
+    if (tid < 3)
+        running[tid] = 0;
+    __syncthreads();
+
+    for (int base = 0; base < T; base += 1024) {
+        const int i = base + tid;
+        const size_t e = ((size_t)sq.begin + i) * plan.Hkv + h;
+        int tier = 3;
+        if (i < T) {
+            if (plan.dense) {
+                tier = 0;
+            } else {
+                const uint64_t K = rank_key(plan, data, e, i);
+                tier = has[0] && K >= thr[0] ? 0 : has[1] && K >= thr[1] ? 1 : has[2] && K >= thr[2] ? 2 : 3;
+            }
+        }
+        const uint64_t below = (1ull << lane) - 1ull;
+        int lane_pre = 0;
+#pragma unroll
+        for (int k = 0; k < 3; k++) {
+            const uint64_t b = __ballot(tier == k);
+            if (lane == 0)
+                wave_tot[wave][k] = __popcll(b);
+            if (tier == k)
+                lane_pre = __popcll(b & below);
+        }
+        __syncthreads();
+        if (i < T) {
+            if (tier < 3) {
+                int pos = running[tier] + lane_pre;
+                for (int w = 0; w < wave; w++)
+                    pos += wave_tot[w][tier];
+                // a position past the tier's count cannot happen with exact
+                // thresholds; it is dropped rather than written out of range
+                plan.dest[e] = pos < rw.count[tier]
+                                   ? (rw.lp_first[tier] + pos / kSlots) * kSlots + pos % kSlots
+                                   : -1;
+            } else {
+                plan.dest[e] = -1;
+            }
+        }
+        __syncthreads();
+        if (tid < 3) {
+            int tot = 0;
+            for (int w = 0; w < 16; w++)
+                tot += wave_tot[w][tid];
+            running[tid] += tot;
+        }
+        __syncthreads();
+    }
+}
+
+__global__ __launch_bounds__(256) void pack_scatter(PackPlan plan, PackData data, PackCache cache)
+{
+    const int64_t e = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int k = threadIdx.x & 63;
+    if (e >= plan.n_tokens * plan.Hkv)
+        return;
+    const int dest = plan.dest[e];
+    if (dest < 0 || dest / kSlots >= plan.n_pages)
+        return;
+    const int D = plan.D, G = D / 8;
+    const PackPage pg = plan.pages[dest / kSlots];
+    const int slot = dest % kSlots;
+    const int tier = pg.meta & 3;
+    uint8_t *base = cache.arena + (size_t)pg.off * kUnit;
+    const uint16_t *kk = data.keys + (size_t)e * D;
+    const uint16_t *vv = data.values + (size_t)e * D;
+
+    if (tier == 0 || tier == 3) {
+        for (int d = k; d < D; d += 64) {
+            uint16_t kb = kk[d];
+            if (tier == 3)
+                kb = f32_to_bf16(f16_bits_to_f32(kb));
+            *reinterpret_cast<uint16_t *>(base + wide_off(D, slot, d)) = kb;
+            *reinterpret_cast<uint16_t *>(base + 32 * D + wide_off(D, slot, d)) = vv[d];
+        }
+    } else if (tier == 1) {
+        for (int d = k; d < D; d += 64)
+            *reinterpret_cast<uint16_t *>(base + wide_off(D, slot, d)) = vv[d];
+        if (k < G)
+            base[codes_off(D, 1) + slot * G + k] = data.codes8[(size_t)e * G + k];
+        if (k == 0)
+            *reinterpret_cast<uint16_t *>(base + radius_off(D, 1) + slot * 2) = data.radius[e];
+    } else {
+        // int8 values with one fp16 scale: scale = fp16(fp32(max|v| / 127)),
+        // q = clamp(rint(fp32(v / scale)), -127, 127), zero scale -> q = 0.
+        float amax = 0.f;
+        for (int d = k; d < D; d += 64)
+            amax = fmaxf(amax, fabsf(bf16_bits_to_f32(vv[d])));
+#pragma unroll
+        for (int o = 32; o >= 1; o >>= 1)
+            amax = fmaxf(amax, __shfl_xor(amax, o, 64));
+        const float s32 = amax / 127.0f;
+        const uint16_t sh = f64_to_f16_sat((double)s32);
+        const float sc = f16_bits_to_f32(sh);
+        for (int d = k; d < D; d += 64) {
+            int q = 0;
+            if (sc != 0.f) {
+                float y = rintf(bf16_bits_to_f32(vv[d]) / sc);
+                y = fminf(fmaxf(y, -127.f), 127.f);
+                q = (int)y;
+            }
+            base[narrow_off(D, slot, d)] = (uint8_t)(int8_t)q;
+        }
+        if (k < G / 2)
+            base[codes_off(D, 2) + slot * (G / 2) + k] = data.codes4[(size_t)e * (G / 2) + k];
+        if (k == 0) {
+            *reinterpret_cast<uint16_t *>(base + radius_off(D, 2) + slot * 2) = data.radius[e];
+            *reinterpret_cast<uint16_t *>(base + vscale_off(D) + slot * 2) = sh;
+        }
+    }
+    if (cache.slot_token != nullptr && k == 0) {
+        // sequence of this token: last s with seqs[s].begin <= n
+        const int n = (int)(e / plan.Hkv);
+        int lo = 0, hi = plan.S - 1;
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) / 2;
+            if (plan.seqs[mid].begin <= n)
+                lo = mid;
+            else
+                hi = mid - 1;
+        }
+        // (an empty sequence is never the last one with begin <= n)
+        const PackSeq sq = plan.seqs[lo];
+        cache.slot_token[((size_t)pg.row * plan.maxp + pg.pi) * kSlots + slot] =
+            (int32_t)(sq.pos_base + (n - sq.begin));
+    }
+}
+
+} // namespace
+
+hipError_t launch_pack(const PackPlan &plan, const PackData &data, const PackCache &cache,
+                       hipStream_t st)
+{
+    const int rows = plan.S * plan.Hkv;
+    if (plan.n_pages > 0) {
+        hipLaunchKernelGGL(pack_pages, dim3(plan.n_pages), dim3(256), 0, st, plan, cache);
+        if (hipError_t e = hipGetLastError(); e != hipSuccess)
+            return e;
+    }
+    if (rows > 0) {
+        hipLaunchKernelGGL(pack_rows, dim3((rows + 255) / 256), dim3(256), 0, st, plan, cache);
+        if (hipError_t e = hipGetLastError(); e != hipSuccess)
+            return e;
+    }
+    if (plan.n_tokens > 0 && rows > 0) {
+        hipLaunchKernelGGL(pack_rank, dim3(rows), dim3(1024), 0, st, plan, data);
+        if (hipError_t e = hipGetLastError(); e != hipSuccess)
+            return e;
+        const int64_t items = plan.n_tokens * plan.Hkv;
+        hipLaunchKernelGGL(pack_scatter, dim3((unsigned)((items + 3) / 4)), dim3(256), 0, st, plan,
+                           data, cache);
+        if (hipError_t e = hipGetLastError(); e != hipSuccess)
+            return e;
+    }
+    return hipSuccess;
+}
+
+} // namespace ada

@@ -1,0 +1,240 @@
+/*
+ * libada -- C ABI of the Angle-Domain Attention (ADA) decode path for
+ * MI355X (gfx950).
+ *
+ * Method sources (arXiv 2605.18856, "SPHERICAL KV: Angle-Domain Attention and
+ * Rate-Distortion Retention for Efficient Long-Context Inference"):
+ *   [TS]  the gist.science technical summary of the paper, sections 2.1-2.3;
+ *   [ABS] the paper's abstract as shown on fugumt.com.
+ *
+ * Conventions for every entry point:
+ *   - Pointers named *_host are host memory.  All other data pointers are
+ *     device memory (HIP device allocations or views into them).
+ *   - The caller owns every buffer.  The library allocates nothing, frees
+ *     nothing and keeps no pointer after a call returns.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).
+ *     Device work is enqueued on it and the call returns; results are ready
+ *     once the caller synchronises that stream.  The library never
+ *     synchronises the device.
+ *   - Argument, shape and capacity errors are found on the host before any
+ *     device work is enqueued and leave every buffer and every *_host
+ *     in/out value unchanged.  A failed launch returns ADA_EHIP.  A device
+ *     fault surfaces at the caller's next synchronisation.
+ *   - Nothing throws across the ABI.  Calls keep no hidden state and may be
+ *     made from several host threads (on different data).
+ *   - fp16 is IEEE binary16, bf16 is bfloat16; both are passed as uint16_t.
+ *
+ * Page format (a reading: [TS] 2.2 asks for tier-homogeneous pages read in
+ * one pass guided by a small header, [ABS] for small metadata and coalesced
+ * reads; nothing else is given).  A page holds 16 slots of one
+ * (sequence, kv-head) row, all of one tier.  D = head_dim, G = D / 8 code
+ * groups, B = D / 8 dims per block.  Page sizes are multiples of 128 bytes,
+ * the unit of the page table.
+ *   tier 0  fp16 keys:    K fp16 wide | V bf16 wide               64*D bytes
+ *   tier 1  8-bit codes:  V bf16 wide | codes u8 [16][G] | radius fp16 [16]
+ *   tier 2  4-bit codes:  V int8 narrow | codes u8 [16][G/2] | radius fp16 [16]
+ *                         | value scale fp16 [16]
+ *   tier 3  dense bf16 (comparison cache): K bf16 wide | V bf16 wide
+ * Wide and narrow sections hold a 16 x D matrix as 64 lanes of 16-byte
+ * chunks: element (t, d) belongs to lane (t % 8) * 8 + d / B and is element
+ * w = (t / 8) * B + d % B of that lane; chunk c of all 64 lanes forms the
+ * c-th KiB of the section:
+ *   wide (2-byte elements):   byte (w / 8) * 1024 + lane * 16 + (w % 8) * 2
+ *   narrow (1-byte elements): byte (w / 16) * 1024 + lane * 16 + w % 16.
+ * A 4-bit code byte holds group 2b in its low nibble, group 2b+1 in its
+ * high nibble.  Unused slots and padding are zero.  page_meta byte:
+ * tier | (valid_slots - 1) << 2.  For D = 128 the sizes are 8192 / 4480 /
+ * 2304 / 8192 bytes; for D = 64, 4096 / 2304 / 1152 / 4096.
+ */
+#ifndef ADA_H
+#define ADA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    ADA_OK = 0,
+    ADA_EINVAL = 1,       /* bad argument, shape or value */
+    ADA_EUNSUPPORTED = 2, /* valid but not built (head_dim, GQA ratio) */
+    ADA_ENOSPACE = 3,     /* arena too small for the pages of a pack call */
+    ADA_EWORKSPACE = 4,   /* workspace missing or smaller than required */
+    ADA_EHIP = 5          /* a HIP launch or copy failed */
+} ada_status;
+
+/* Static text for a status code (never NULL). */
+const char *ada_status_str(int status);
+
+/* Library version, major * 10000 + minor * 100 + patch. */
+int ada_version(void);
+
+typedef struct {
+    int32_t head_dim;     /* D: 64 or 128 */
+    int32_t num_q_heads;  /* Hq */
+    int32_t num_kv_heads; /* Hkv; Hq % Hkv == 0 and Hq / Hkv in {1, 2, 4} */
+    int32_t page_size;    /* must be 16 */
+} ada_geom;
+
+/* One layer's cache view.  Rows are (sequence, kv-head) pairs,
+ * row = s * Hkv + h.  All pointers are device memory owned by the caller. */
+typedef struct {
+    uint8_t *arena;          /* page bytes; 256-byte aligned */
+    uint64_t arena_units;    /* arena size in 128-byte units (<= 2^32) */
+    uint32_t *page_table;    /* [rows][max_pages_per_head]: page offset, 128-byte units */
+    uint8_t *page_meta;      /* [rows][max_pages_per_head]: tier | (valid-1) << 2 */
+    int32_t *num_pages;      /* [rows] pages in use per row */
+    int32_t *tier_tokens;    /* [rows][3] retained tokens per tier (may be NULL for dense caches) */
+    int32_t *slot_token;     /* [rows][max_pages_per_head][16] token position or -1; may be NULL */
+    int32_t num_seqs;        /* S */
+    int32_t max_pages_per_head;
+} ada_cache;
+
+/* Bytes of one page of `tier` (0..3) for head_dim D; 0 if unsupported. */
+size_t ada_page_bytes(int32_t head_dim, int32_t tier);
+
+/*
+ * ada_encode -- keys to radius + angle codes.
+ * [TS] 2.1 (spherical parameterization; quantized radius and packed angular
+ * codes).  Reading: r = ||k|| of the fp16 key (double precision), stored
+ * as fp16 (round to nearest even, saturating at 65504); the direction
+ * u = k / r (u = 0 for a zero key) is split into G groups of 8 and each
+ * group takes the index of its nearest codeword (squared Euclidean
+ * distance, evaluated in double; lowest index on ties) among the 256
+ * codewords of cb8 and, separately, the 16 codewords of cb4.
+ *   keys    [n_tokens][Hkv][D] fp16
+ *   cb8     [Hkv][G][256][8] f32,  cb4 [Hkv][G][16][8] f32 (one layer)
+ *   radius  [n_tokens][Hkv] fp16 out
+ *   codes8  [n_tokens][Hkv][G] u8 out
+ *   codes4  [n_tokens][Hkv][G/2] u8 out (two 4-bit codes per byte)
+ * n_tokens may be 0 (no work).
+ */
+ada_status ada_encode(const ada_geom *geom, int64_t n_tokens, const uint16_t *keys,
+                      const float *cb8, const float *cb4, uint16_t *radius, uint8_t *codes8,
+                      uint8_t *codes4, void *stream);
+
+/*
+ * rdr_pack_num_pages -- number of pages one rdr_pack call with these
+ * sequences and mixes creates (the length of its place_perm_host).
+ */
+ada_status rdr_pack_num_pages(const ada_geom *geom, int32_t num_seqs,
+                              const int32_t *cu_tokens_host, const int32_t *tier_cum_bp_host,
+                              int64_t *n_pages_out);
+
+/* Workspace bytes rdr_pack and dense_pack need for a call of n_tokens tokens
+ * over num_seqs sequences. */
+size_t rdr_pack_workspace_size(const ada_geom *geom, int64_t n_tokens, int32_t num_seqs);
+
+/*
+ * rdr_pack -- keep/drop + tier per (token, head), then tier-homogeneous pages.
+ * [TS] 2.2 (joint residency/tier choice per state; protection forces the top
+ * tier; pages hold one tier) and [ABS] (per token and head, under a fixed
+ * budget).  The pages give no solver.  Reading: sequence s of this call owns
+ * tokens cu_tokens_host[s] .. cu_tokens_host[s+1]-1 of the flat arrays
+ * (T_s of them); tier_cum_bp_host[s][0..2] are cumulative basis points
+ * (fp16, +8-bit, +4-bit; 0 <= b0 <= b1 <= b2 <= 10000) and give token
+ * counts n_cum = floor((b * T_s + 5000) / 10000).  In each row the tokens
+ * are ranked by (protected first, higher score first, lower index first):
+ * the first n_cum[0] take tier 0, the next take tier 1 up to n_cum[1],
+ * then tier 2 up to n_cum[2]; the rest are dropped (stored nowhere).  Inside
+ * a tier, tokens keep index order and fill 16-slot pages.  Each row gains
+ * its tier-0 pages, then tier-1, then tier-2, after the pages it had.  The
+ * call's pages, numbered (s, h, tier, page), are placed in the arena by bump
+ * allocation from *arena_cursor_host in the order place_perm_host[0..n)
+ * (identity when NULL).  The 4-bit tier stores values as int8 with one fp16
+ * scale per (token, head): scale = fp16(fp32(max|v| / 127)),
+ * q = clamp(rint(fp32(v / scale)), -127, 127), q = 0 when scale = 0.
+ *   num_seqs must equal cache->num_seqs (a sequence may bring 0 tokens).
+ *   keys fp16 / values bf16 [N][Hkv][D]; radius [N][Hkv]; codes8 [N][Hkv][G];
+ *   codes4 [N][Hkv][G/2] (from ada_encode); scores f32 [N][Hkv] (finite).
+ *   protect_host [N][Hkv] u8 (nonzero = protected) or NULL; more protected
+ *     tokens in a row than its tier-0 count is ADA_EINVAL.
+ *   place_perm_host: permutation of [0, n_pages) or NULL.
+ *   pos_base_host [S]: position of each sequence's first token of this call,
+ *     recorded in slot_token (NULL = 0).
+ *   arena_cursor_host (in/out): next free 128-byte unit of the arena.
+ *   num_pages_host [S*Hkv] (in/out): host copy of cache->num_pages; the call
+ *     checks row capacity against it and advances it.
+ *   ws: device workspace of rdr_pack_workspace_size bytes.
+ * Errors: ADA_ENOSPACE when the pages do not fit in the arena, ADA_EINVAL
+ * when a row would exceed max_pages_per_head -- both before any device work.
+ */
+ada_status rdr_pack(const ada_geom *geom, const ada_cache *cache, int32_t num_seqs,
+                    const int32_t *cu_tokens_host, const int32_t *tier_cum_bp_host,
+                    const uint16_t *keys, const uint16_t *values, const uint16_t *radius,
+                    const uint8_t *codes8, const uint8_t *codes4, const float *scores,
+                    const uint8_t *protect_host, const uint32_t *place_perm_host,
+                    const int64_t *pos_base_host, uint64_t *arena_cursor_host,
+                    int32_t *num_pages_host, void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * dense_pack -- the comparison cache: every token of the call, in index
+ * order, in tier-3 pages (keys rounded fp16 -> bf16, values bf16).  Not part
+ * of the method; it feeds dense_decode, the dense bf16 paged-attention
+ * baseline the pages compare against ([TS] section 4).  Arguments as in
+ * rdr_pack; place_perm_host has one entry per page of the call
+ * (rows * ceil(T_s / 16) summed over sequences).
+ */
+ada_status dense_pack(const ada_geom *geom, const ada_cache *cache, int32_t num_seqs,
+                      const int32_t *cu_tokens_host, const uint16_t *keys,
+                      const uint16_t *values, const uint32_t *place_perm_host,
+                      uint64_t *arena_cursor_host, int32_t *num_pages_host, void *ws,
+                      size_t ws_bytes, void *stream);
+
+/* Split count ada_decode / dense_decode use for num_splits == 0. */
+int32_t ada_decode_default_splits(const ada_geom *geom, int32_t num_seqs,
+                                  int32_t max_pages_per_head);
+
+/* Workspace bytes of ada_decode / dense_decode with this many splits
+ * (0 = the default).  The workspace holds per-split partial results. */
+size_t ada_decode_workspace_size(const ada_geom *geom, int32_t num_seqs,
+                                 int32_t max_pages_per_head, int32_t num_splits);
+
+/*
+ * ada_decode -- one decode step over a cache view.
+ * [TS] 2.1: logits straight from the stored codes, with no dense key rebuilt
+ * in device memory; the pages give l ~ |q| * r~ * f_b(codes), f_b a cosine
+ * from the codes.  With the encoding above this is
+ *   l_t = softmax_scale * r~_t * sum_g LUT_g[code_{t,g}],
+ *   LUT_g[c] = q_g . C_g[c]      (tiers 1 and 2),
+ *   l_t = softmax_scale * q . k_t (tier 0),
+ * then softmax attention over the row's retained slots:
+ *   out = sum_t e^(l_t - m) v_t / sum_t e^(l_t - m),  lse = m + ln sum_t e^(l_t - m),
+ * v_t the stored bf16 value, or int8 * scale in tier 2.  Query head hq reads
+ * kv-head hq / (Hq / Hkv).  No causal mask.  A row with no pages gives
+ * out = 0, lse = -inf.
+ *   cb8 / cb4 as in ada_encode (the layer's codebooks).
+ *   q        [S][Hq][D] bf16
+ *   out      [S][Hq][D] f32;  lse [S][Hq] f32 or NULL
+ *   logits_dbg [S][Hq][max_pages_per_head * 16] f32 or NULL: for parity
+ *     tests, receives l_t of every valid slot (page p, slot t at p*16+t);
+ *     other entries are left untouched.
+ *   num_splits: page-range splits per row (0 = ada_decode_default_splits).
+ *   ws: ada_decode_workspace_size(geom, S, max_pages_per_head, num_splits)
+ *     bytes, 256-byte aligned.  Its first S*Hkv 32-bit words are per-row
+ *     split counters: they must be zero before the first call that uses the
+ *     workspace (allocate it zero-filled), and every completed call leaves
+ *     them zero.  Calls that overlap in time must not share a workspace.
+ * Cache pages must be tiers 0-2.  Queries must be finite with |q| < 2^64.
+ */
+ada_status ada_decode(const ada_geom *geom, const ada_cache *cache, const float *cb8,
+                      const float *cb4, const uint16_t *q, float softmax_scale, float *out,
+                      float *lse, float *logits_dbg, int32_t num_splits, void *ws,
+                      size_t ws_bytes, void *stream);
+
+/*
+ * dense_decode -- the dense bf16 paged-decode baseline over tier-3 pages
+ * (l_t = softmax_scale * q . k_t with bf16 keys), same split/merge scheme
+ * and arguments as ada_decode without codebooks.
+ */
+ada_status dense_decode(const ada_geom *geom, const ada_cache *cache, const uint16_t *q,
+                        float softmax_scale, float *out, float *lse, float *logits_dbg,
+                        int32_t num_splits, void *ws, size_t ws_bytes, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ADA_H */

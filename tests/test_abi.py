@@ -1,0 +1,115 @@
+"""The C-ABI library loads, exports every declared entry point, and rejects
+bad arguments on the host before touching a device (CPU only: no call here
+launches work)."""
+import ctypes as C
+import os
+import re
+
+import numpy as np
+import pytest
+
+import compressed_kv_attention_amd as ada
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    src = open(os.path.join(ROOT, "include", "ada.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b([a-z_][a-z0-9_]*)\s*\(", src)) - {"if", "sizeof"})
+
+
+def test_library_exports_every_declared_symbol():
+    names = _declared()
+    assert {"ada_encode", "rdr_pack", "ada_decode", "dense_decode", "dense_pack"} <= set(names)
+    lib = C.CDLL(ada.lib_path())
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings_and_version():
+    L = ada.load()
+    for st in range(6):
+        assert L.ada_status_str(st)
+    assert L.ada_status_str(99) == b"unknown status"
+    assert L.ada_version() >= 100
+
+
+def test_page_bytes_match_the_format():
+    assert [ada.page_bytes(128, t) for t in range(4)] == [8192, 4480, 2304, 8192]
+    assert [ada.page_bytes(64, t) for t in range(4)] == [4096, 2304, 1152, 4096]
+    assert ada.page_bytes(96, 0) == 0 and ada.page_bytes(128, 4) == 0
+
+
+def test_pack_page_count_and_workspace():
+    g = ada.Geom(128, 32, 8)
+    # config-2 mix at T=32768: 308 + 922 + 512 pages per kv-head
+    assert ada.pack_num_pages(g, [0, 32768], [[1500, 6000, 8500]]) == 8 * 1742
+    assert ada.pack_num_pages(g, [0, 0, 5], [[0, 0, 0], [10000, 10000, 10000]]) == 8
+    assert ada.pack_workspace_size(g, 32768, 1) > 32768 * 8 * 4
+    assert ada.decode_workspace_size(g, 1, 2000) >= 8 * ada.decode_default_splits(g, 1, 2000) * 4 * 130 * 4
+
+
+def _bad(call):
+    with pytest.raises(ada.AdaError) as e:
+        call()
+    return e.value.status
+
+
+def test_host_argument_errors():
+    L = ada.load()
+    for bad in (ada.Geom(96, 32, 8), ada.Geom(128, 30, 8), ada.Geom(128, 32, 8, 32), ada.Geom(128, 0, 8)):
+        assert L.rdr_pack_num_pages(C.byref(bad), 1, np.array([0, 16], np.int32).ctypes.data_as(C.c_void_p),
+                                    np.array([5000, 5000, 5000], np.int32).ctypes.data_as(C.c_void_p),
+                                    C.byref(C.c_int64())) == ada.EINVAL
+    g = ada.Geom(128, 32, 8)
+    # decreasing cumulative basis points / non-zero start / decreasing cu
+    assert _bad(lambda: ada.pack_num_pages(g, [0, 16], [[5000, 4000, 9000]])) == ada.EINVAL
+    assert _bad(lambda: ada.pack_num_pages(g, [1, 16], [[0, 0, 0]])) == ada.EINVAL
+    assert _bad(lambda: ada.pack_num_pages(g, [0, 16, 8], [[0, 0, 0], [0, 0, 0]])) == ada.EINVAL
+    # decode: null pointers and unsupported GQA ratios are refused before any launch
+    view = ada._CacheView(0, 0, 0, 0, 0, 0, 0, 1, 4)
+    assert L.ada_decode(C.byref(g), C.byref(view), None, None, None, 1.0, None, None, None, 0, None, 0,
+                        None) == ada.EINVAL
+    g8 = ada.Geom(128, 64, 8)
+    view = ada._CacheView(16, 1, 16, 16, 16, 16, 0, 1, 4)
+    assert L.ada_decode(C.byref(g8), C.byref(view), C.c_void_p(16), C.c_void_p(16), C.c_void_p(16), 1.0,
+                        C.c_void_p(16), None, None, 0, C.c_void_p(256), 1 << 20, None) == ada.EUNSUPPORTED
+    # too small a workspace
+    view = ada._CacheView(16, 1, 16, 16, 16, 16, 0, 1, 4)
+    assert L.ada_decode(C.byref(g), C.byref(view), C.c_void_p(16), C.c_void_p(16), C.c_void_p(16), 1.0,
+                        C.c_void_p(16), None, None, 0, C.c_void_p(256), 8, None) == ada.EWORKSPACE
+    # encode with no tokens is a no-op; negative counts are refused
+    assert L.ada_encode(C.byref(g), 0, None, None, None, None, None, None, None) == ada.OK
+    assert L.ada_encode(C.byref(g), -1, None, None, None, None, None, None, None) == ada.EINVAL
+
+
+def test_pack_host_errors_leave_host_state_untouched():
+    """Arena overflow and row-capacity errors come back before any device
+    work, with the cursor and page counts unchanged (no device needed: the
+    device pointers are never dereferenced on these paths)."""
+    L = ada.load()
+    g = ada.Geom(64, 4, 2)
+    cu = np.array([0, 64], np.int32)
+    bp = np.array([2500, 7500, 10000], np.int32)
+    cursor = np.zeros(1, np.uint64)
+    npages = np.zeros(2, np.int32)
+    fake = C.c_void_p(256)
+
+    def call(arena_units, maxp, protect=None, perm=None):
+        view = ada._CacheView(256, arena_units, 256, 256, 256, 256, 0, 1, maxp)
+        return L.rdr_pack(C.byref(g), C.byref(view), 1, cu.ctypes.data_as(C.c_void_p),
+                          bp.ctypes.data_as(C.c_void_p), fake, fake, fake, fake, fake, fake,
+                          None if protect is None else protect.ctypes.data_as(C.c_void_p),
+                          None if perm is None else perm.ctypes.data_as(C.c_void_p), None,
+                          cursor.ctypes.data_as(C.c_void_p), npages.ctypes.data_as(C.c_void_p),
+                          C.c_void_p(1 << 20), 1 << 30, None)
+
+    assert call(arena_units=10, maxp=64) == ada.ENOSPACE          # needs 2 * 36 units + more
+    assert call(arena_units=1 << 20, maxp=3) == ada.EINVAL        # 4 pages per row needed
+    prot = np.zeros((64, 2), np.uint8)
+    prot[:17, 1] = 1                                              # 16 fp16 slots only
+    assert call(arena_units=1 << 20, maxp=64, protect=prot) == ada.EINVAL
+    bad_perm = np.zeros(8, np.uint32)
+    assert call(arena_units=1 << 20, maxp=64, perm=bad_perm) == ada.EINVAL
+    assert cursor[0] == 0 and not npages.any()

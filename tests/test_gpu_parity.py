@@ -1,0 +1,293 @@
+"""GPU parity: the HIP library through its C ABI against the CPU oracle on the
+same seeded inputs.
+
+Bars (written here, from the method's targets): encode codes and radii
+bit-exact (both sides take the argmin in double; any disagreement must be a
+near-tie, |d_gpu - d_ref| < 1e-6); pages, page tables, metadata and tier
+counts bit-exact when both packs get the same encode outputs; logits within
+|d| <= 1e-3 * max(|l|, 1e-2); outputs max-abs <= 1e-2 (fp32 accumulation);
+lse within 1e-3 * max(|lse|, 1)."""
+import numpy as np
+import pytest
+import torch
+
+import compressed_kv_attention_amd as ada
+import oracle
+import synth
+from gpu_util import (decode_outputs, flush, geom_of, gpu_encode, logit_tol_ok, to_dev, u16,
+                      upload_cache)
+from helpers import make_case, oracle_cache, small_workload
+
+pytestmark = pytest.mark.gpu
+
+OUT_TOL = 1e-2
+
+
+def _dev_case(case):
+    return {k: to_dev(case[k]) for k in ("keys", "values", "scores", "q", "cb8", "cb4")}
+
+
+def _check_decode(geom, hc, case, num_splits=0, label=""):
+    flush(f"[decode] {label} splits={num_splits}")
+    cfg = case["cfg"]
+    ref = oracle.decode(hc, case["cb8"], case["cb4"], case["q"], cfg.sigma, logits=True, nthreads=8)
+    dc = upload_cache(hc, geom)
+    d = _dev_case(case)
+    out, lse, lg = decode_outputs(geom, dc, d["q"])
+    ada.decode(geom, dc, d["cb8"], d["cb4"], d["q"], cfg.sigma, out, lse, lg, num_splits=num_splits)
+    torch.cuda.synchronize()
+    ok, worst = logit_tol_ok(lg.cpu().double().numpy(), ref["logits"])
+    assert ok, f"logits off by {worst:.3g} (relative)"
+    o = out.cpu().double().numpy()
+    err = np.abs(o - ref["out"]).max(initial=0.0)
+    assert err <= OUT_TOL, f"out max-abs {err:.3g}"
+    l = lse.cpu().double().numpy()
+    fin = np.isfinite(ref["lse"])
+    assert np.array_equal(np.isfinite(l), fin)
+    assert (np.abs(l[fin] - ref["lse"][fin]) <= 1e-3 * np.maximum(np.abs(ref["lse"][fin]), 1.0)).all()
+    assert (l[~fin] == -np.inf).all() and not o[~fin].any()
+    flush(f"[decode] {label} ok: out max-abs {err:.2e}, logits rel {worst:.2e}")
+    return err
+
+
+@pytest.mark.parametrize("splits", [0, 1, 3])
+def test_decode_tiny_workload(splits):
+    cfg = synth.WORKLOADS[1]
+    case = make_case(cfg)
+    hc, _ = oracle_cache(case)
+    _check_decode(geom_of(cfg), hc, case, splits, "tiny D=64 MHA T=512")
+
+
+@pytest.mark.parametrize("D,Hq,Hkv", [(128, 4, 2), (64, 8, 2), (128, 4, 4), (64, 2, 2)])
+def test_decode_ragged_mixed_tiers(D, Hq, Hkv):
+    cfg = small_workload(D=D, Hq=Hq, Hkv=Hkv, S=4, T=300, seed=40 + D + Hq)
+    mixes = [(1500, 6000, 8500), (0, 0, 0), (10000, 10000, 10000), (0, 3000, 9000)]
+    case = make_case(cfg, lens=[300, 40, 17, 0], mixes=mixes)
+    hc, _ = oracle_cache(case)
+    for sp in (0, 1, 5):
+        _check_decode(geom_of(cfg), hc, case, sp, f"ragged D={D} Hq={Hq} Hkv={Hkv}")
+
+
+@pytest.mark.parametrize("mix", [(10000, 10000, 10000), (0, 10000, 10000), (0, 0, 10000)])
+def test_decode_single_token_rows(mix):
+    cfg = small_workload(D=128, Hq=4, Hkv=1, S=3, T=1, mix=mix, seed=50)
+    case = make_case(cfg, lens=[1, 1, 1])
+    hc, _ = oracle_cache(case)
+    _check_decode(geom_of(cfg), hc, case, 0, f"single token {mix}")
+
+
+def test_decode_permuted_pool_and_appends():
+    cfg = small_workload(D=128, Hq=8, Hkv=2, S=2, T=200, seed=51)
+    case = make_case(cfg, lens=[200, 150, 64, 33], mixes=[(1000, 5000, 8000)] * 4)
+    r, c8, c4 = oracle.encode(case["keys"], case["cb8"], case["cb4"])
+    hc = oracle.HostCache(128, 2, 2, 64, 4 << 20)
+    cu1, cu2 = np.array([0, 200, 350], np.int32), np.array([0, 64, 97], np.int32)
+    bp = np.array([(1000, 5000, 8000)] * 2, np.int32)
+    n1 = oracle.num_pages_of_call(128, 2, cu1, bp)
+    perm = np.random.default_rng(3).permutation(n1).astype(np.uint32)
+    assert oracle.pack(hc, cu1, bp, case["keys"][:350], case["values"][:350], r[:350], c8[:350],
+                       c4[:350], case["scores"][:350], place_perm=perm) == 0
+    assert oracle.pack(hc, cu2, bp, case["keys"][350:], case["values"][350:], r[350:], c8[350:],
+                       c4[350:], case["scores"][350:], pos_base=[200, 150]) == 0
+    _check_decode(geom_of(cfg), hc, case, 0, "permuted pool + append")
+    _check_decode(geom_of(cfg), hc, case, 2, "permuted pool + append")
+
+
+def test_decode_llama_shape_t32k_full():
+    cfg = synth.WORKLOADS[2]
+    case = make_case(cfg)
+    hc, _ = oracle_cache(case, maxp=1760)
+    for sp in (0, 7):
+        _check_decode(geom_of(cfg), hc, case, sp, "Llama-3-8B shape T=32768")
+
+
+# ---- encode ---------------------------------------------------------------
+
+def _check_encode(cfg, case, label):
+    flush(f"[encode] {label}")
+    geom = geom_of(cfg)
+    d = _dev_case(case)
+    r, c8, c4 = gpu_encode(geom, d["keys"], d["cb8"], d["cb4"])
+    torch.cuda.synchronize()
+    rr, rc8, rc4 = oracle.encode(case["keys"], case["cb8"], case["cb4"], nthreads=8)
+    assert np.array_equal(u16(r), rr), "radius differs"
+    g8, g4 = c8.cpu().numpy(), c4.cpu().numpy()
+    agree8 = (g8 == rc8).mean()
+    agree4 = (g4 == rc4).mean()
+    flush(f"[encode] {label}: codes8 agree {agree8:.6f}, codes4 agree {agree4:.6f}")
+    if agree8 < 1.0 or agree4 < 1.0:
+        # every disagreement must be a near-tie under the oracle's distances
+        lo4, hi4 = g4 & 15, g4 >> 4
+        rlo4, rhi4 = rc4 & 15, rc4 >> 4
+        gg4 = np.stack([lo4, hi4], -1).reshape(g8.shape)
+        rr4 = np.stack([rlo4, rhi4], -1).reshape(g8.shape)
+        toks = np.unique(np.concatenate([np.nonzero((g8 != rc8).any((1, 2)))[0],
+                                         np.nonzero((gg4 != rr4).any((1, 2)))[0]]))
+        _, _, _, d8, d4 = oracle.encode(case["keys"][toks], case["cb8"], case["cb4"], with_dist=True)
+        for i, t in enumerate(toks):
+            for h, g in zip(*np.nonzero(g8[t] != rc8[t])):
+                gap = abs(d8[i, h, g, g8[t, h, g]] - d8[i, h, g, rc8[t, h, g]])
+                assert gap < 1e-6, f"8-bit code of token {t} head {h} group {g}: gap {gap}"
+            for h, g in zip(*np.nonzero(gg4[t] != rr4[t])):
+                gap = abs(d4[i, h, g, gg4[t, h, g]] - d4[i, h, g, rr4[t, h, g]])
+                assert gap < 1e-6, f"4-bit code of token {t} head {h} group {g}: gap {gap}"
+    assert agree8 >= 0.999 and agree4 >= 0.999
+    return r, c8, c4
+
+
+def test_encode_tiny_and_small():
+    _check_encode(synth.WORKLOADS[1], make_case(synth.WORKLOADS[1]), "tiny")
+    cfg = small_workload(D=128, Hq=4, Hkv=2, S=2, T=333, seed=60)
+    case = make_case(cfg)
+    # a zero key and a key of one huge channel
+    case["keys"][5, 0] = 0
+    case["keys"][7, 1] = 0
+    case["keys"][7, 1, 3] = 60000.0
+    _check_encode(cfg, case, "D=128 with zero and extreme keys")
+
+
+def test_encode_llama_shape_t32k_full():
+    cfg = synth.WORKLOADS[2]
+    _check_encode(cfg, make_case(cfg), "Llama-3-8B shape T=32768")
+
+
+# ---- pack -----------------------------------------------------------------
+
+def _gpu_pack_like(hc_ref, geom, calls, slot_tokens=True):
+    """Replays oracle pack calls on the GPU; returns the device cache."""
+    dc = ada.Cache(geom, hc_ref.S, hc_ref.maxp, len(hc_ref.arena), slot_tokens=slot_tokens)
+    for c in calls:
+        ada.rdr_pack(geom, dc, c["cu"], c["bp"], to_dev(c["keys"]), to_dev(c["values"]),
+                     to_dev(c["radius"]), to_dev(c["codes8"]), to_dev(c["codes4"]),
+                     to_dev(c["scores"]), protect=c.get("protect"), place_perm=c.get("perm"),
+                     pos_base=c.get("pos_base"))
+    torch.cuda.synchronize()
+    return dc
+
+
+def _compare_caches(dc, hc, label):
+    used = int(hc.cursor[0]) * 128
+    assert int(dc.cursor[0]) == int(hc.cursor[0]), label
+    assert np.array_equal(dc.num_pages_host[: len(hc.num_pages)], hc.num_pages)
+    a = dc.arena[:used].cpu().numpy()
+    diff = np.nonzero(a != hc.arena[:used])[0]
+    assert len(diff) == 0, f"{label}: {len(diff)} arena bytes differ, first at {diff[:5]}"
+    rows = len(hc.num_pages)
+    assert np.array_equal(dc.num_pages[:rows].cpu().numpy(), hc.num_pages)
+    assert np.array_equal(dc.tier_tokens[:rows].cpu().numpy(), hc.tier_tokens)
+    for r in range(rows):
+        n = hc.num_pages[r]
+        assert np.array_equal(dc.page_table[r, :n].cpu().numpy().view(np.uint32), hc.page_table[r, :n])
+        assert np.array_equal(dc.page_meta[r, :n].cpu().numpy(), hc.page_meta[r, :n])
+        if dc.slot_token is not None:
+            assert np.array_equal(dc.slot_token[r, :n].cpu().numpy(), hc.slot_token[r, :n])
+
+
+def test_pack_tiny_bit_exact():
+    cfg = synth.WORKLOADS[1]
+    case = make_case(cfg)
+    flush("[pack] tiny")
+    hc, (r, c8, c4) = oracle_cache(case)
+    dc = _gpu_pack_like(hc, geom_of(cfg), [dict(cu=case["cu"], bp=case["bp"], keys=case["keys"],
+                                                values=case["values"], radius=r, codes8=c8, codes4=c4,
+                                                scores=case["scores"])])
+    _compare_caches(dc, hc, "tiny")
+
+
+@pytest.mark.parametrize("D", [64, 128])
+def test_pack_ragged_protect_permuted_two_calls(D):
+    cfg = small_workload(D=D, Hq=4, Hkv=2, S=3, T=100, seed=70 + D)
+    lens = np.array([500, 37, 0, 20, 0, 45])
+    case = make_case(cfg, lens=lens, mixes=[(2500, 7500, 9000)] * 6)
+    flush(f"[pack] ragged D={D}")
+    r, c8, c4 = oracle.encode(case["keys"], case["cb8"], case["cb4"])
+    rng = np.random.default_rng(D)
+    scores = torch.from_numpy(rng.integers(1, 5, (case["N"], 2)).astype(np.float32))
+    scores[3, 0] = -0.0  # signed zero ties with +0
+    scores[4, 0] = 0.0
+    N1 = 537
+    cu1, cu2 = np.array([0, 500, 537, 537], np.int32), np.array([0, 20, 20, 65], np.int32)
+    bp1 = np.array([(2500, 7500, 9000), (0, 5000, 10000), (3000, 3000, 3000)], np.int32)
+    bp2 = np.array([(10000, 10000, 10000), (5000, 5000, 5000), (0, 2000, 6000)], np.int32)
+    protect = np.zeros((case["N"], 2), np.uint8)
+    protect[[1, 9, 77, 300], 0] = 1
+    protect[[2, 499], 1] = 1
+    protect[500, 1] = 1
+    hc = oracle.HostCache(D, 2, 3, 64, 2 << 20)
+    n1 = oracle.num_pages_of_call(D, 2, cu1, bp1)
+    perm1 = rng.permutation(n1).astype(np.uint32)
+    calls = [dict(cu=cu1, bp=bp1, keys=case["keys"][:N1], values=case["values"][:N1], radius=r[:N1],
+                  codes8=c8[:N1], codes4=c4[:N1], scores=scores[:N1], protect=protect[:N1], perm=perm1),
+             dict(cu=cu2, bp=bp2, keys=case["keys"][N1:], values=case["values"][N1:], radius=r[N1:],
+                  codes8=c8[N1:], codes4=c4[N1:], scores=scores[N1:],
+                  pos_base=np.array([500, 37, 0], np.int64))]
+    for c in calls:
+        rc = oracle.pack(hc, c["cu"], c["bp"], c["keys"], c["values"], c["radius"], c["codes8"],
+                         c["codes4"], c["scores"], protect=c.get("protect"), place_perm=c.get("perm"),
+                         pos_base=c.get("pos_base"))
+        assert rc == 0
+    dc = _gpu_pack_like(hc, geom_of(cfg), calls)
+    _compare_caches(dc, hc, f"ragged D={D}")
+
+
+def test_pack_llama_shape_t32k_full():
+    cfg = synth.WORKLOADS[2]
+    case = make_case(cfg)
+    flush("[pack] Llama-3-8B shape T=32768")
+    hc, (r, c8, c4) = oracle_cache(case, maxp=1760)
+    dc = _gpu_pack_like(hc, geom_of(cfg), [dict(cu=case["cu"], bp=case["bp"], keys=case["keys"],
+                                                values=case["values"], radius=r, codes8=c8, codes4=c4,
+                                                scores=case["scores"])])
+    _compare_caches(dc, hc, "T=32768")
+
+
+# ---- whole path and the dense baseline -------------------------------------
+
+@pytest.mark.parametrize("number", [1, 2])
+def test_pipeline_encode_pack_decode(number):
+    """GPU encode -> GPU pack -> GPU decode against oracle encode -> pack -> decode."""
+    cfg = synth.WORKLOADS[number]
+    case = make_case(cfg)
+    flush(f"[pipeline] workload {number}")
+    geom = geom_of(cfg)
+    hc, _ = oracle_cache(case, maxp=1760 if number == 2 else None)
+    ref = oracle.decode(hc, case["cb8"], case["cb4"], case["q"], cfg.sigma, nthreads=8)
+    d = _dev_case(case)
+    r, c8, c4 = gpu_encode(geom, d["keys"], d["cb8"], d["cb4"])
+    dc = ada.Cache(geom, hc.S, hc.maxp, len(hc.arena))
+    ada.rdr_pack(geom, dc, case["cu"], case["bp"], d["keys"], d["values"], r, c8, c4, d["scores"])
+    out, lse, _ = decode_outputs(geom, dc, d["q"], with_logits=False)
+    ada.decode(geom, dc, d["cb8"], d["cb4"], d["q"], cfg.sigma, out, lse)
+    torch.cuda.synchronize()
+    assert int(dc.cursor[0]) == int(hc.cursor[0])
+    err = np.abs(out.cpu().double().numpy() - ref["out"]).max()
+    flush(f"[pipeline] workload {number}: out max-abs {err:.2e}")
+    assert err <= OUT_TOL
+
+
+@pytest.mark.parametrize("D,Hq,Hkv", [(128, 32, 8), (64, 4, 4)])
+def test_dense_pack_and_decode(D, Hq, Hkv):
+    cfg = small_workload(D=D, Hq=Hq, Hkv=Hkv, S=3, T=500, seed=80 + D)
+    case = make_case(cfg, lens=[500, 1, 77])
+    flush(f"[dense] D={D} Hq={Hq} Hkv={Hkv}")
+    geom = geom_of(cfg)
+    hc = oracle.HostCache(D, Hkv, 3, 40, 8 << 20, slot_tokens=False)
+    n = sum((int(x) + 15) // 16 for x in case["lens"]) * Hkv
+    perm = np.random.default_rng(1).permutation(n).astype(np.uint32)
+    assert oracle.dense_pack(hc, case["cu"], case["keys"], case["values"], place_perm=perm) == 0
+    dc = ada.Cache(geom, 3, 40, 8 << 20)
+    d = _dev_case(case)
+    ada.dense_pack(geom, dc, case["cu"], d["keys"], d["values"], place_perm=perm)
+    torch.cuda.synchronize()
+    used = int(hc.cursor[0]) * 128
+    assert int(dc.cursor[0]) == int(hc.cursor[0])
+    assert np.array_equal(dc.arena[:used].cpu().numpy(), hc.arena[:used])
+    ref = oracle.decode(hc, None, None, case["q"], cfg.sigma, logits=True)
+    out, lse, lg = decode_outputs(geom, dc, d["q"])
+    ada.dense_decode(geom, dc, d["q"], cfg.sigma, out, lse, lg)
+    torch.cuda.synchronize()
+    ok, worst = logit_tol_ok(lg.cpu().double().numpy(), ref["logits"])
+    assert ok, worst
+    err = np.abs(out.cpu().double().numpy() - ref["out"]).max()
+    flush(f"[dense] out max-abs {err:.2e}")
+    assert err <= OUT_TOL
