@@ -12,6 +12,7 @@ namespace {
 using namespace ada;
 
 constexpr int kVersion = 100; // 0.1.0
+constexpr int kMaxSplits = 1024;
 
 hipStream_t as_stream(void *s) { return reinterpret_cast<hipStream_t>(s); }
 
@@ -226,9 +227,12 @@ int32_t default_splits(const ada_geom *g, int32_t S, int32_t maxp)
     const int64_t rows = (int64_t)S * g->num_kv_heads;
     if (rows <= 0)
         return 1;
-    int64_t n = (512 + rows - 1) / rows;
-    n = std::min<int64_t>(n, std::max<int64_t>(1, maxp / 8));
-    return (int32_t)std::max<int64_t>(1, std::min<int64_t>(n, 4096));
+    // about one workgroup per compute unit, at least 16 pages per split, and
+    // at most 8192 pages per split (their table entries are staged in LDS)
+    int64_t n = (256 + rows - 1) / rows;
+    n = std::min<int64_t>(n, std::max<int64_t>(1, maxp / 16));
+    n = std::max<int64_t>(n, (maxp + 8191) / 8192);
+    return (int32_t)std::max<int64_t>(1, std::min<int64_t>(n, kMaxSplits));
 }
 
 ada_status decode_common(const ada_geom *g, const ada_cache *c, const float *cb8, const float *cb4,
@@ -241,6 +245,8 @@ ada_status decode_common(const ada_geom *g, const ada_cache *c, const float *cb8
         return ADA_EINVAL;
     if (!gqa_supported(g))
         return ADA_EUNSUPPORTED;
+    if (num_splits > kMaxSplits)
+        return ADA_EINVAL;
     const int32_t ns = num_splits > 0 ? num_splits : default_splits(g, c->num_seqs, c->max_pages_per_head);
     const size_t need = ada_decode_workspace_size(g, c->num_seqs, c->max_pages_per_head, ns);
     if (ws == nullptr || ws_bytes < need || (reinterpret_cast<uintptr_t>(ws) & 255))
@@ -249,6 +255,8 @@ ada_status decode_common(const ada_geom *g, const ada_cache *c, const float *cb8
     const int64_t rows = (int64_t)c->num_seqs * g->num_kv_heads;
     if (rows * ns > INT32_MAX)
         return ADA_EINVAL;
+    if (decode_shmem_bytes(g->head_dim, NH, dense, ns, c->max_pages_per_head) > kMaxLds)
+        return ADA_EINVAL; // too many pages per split: use more splits
     DecodeArgs a;
     a.arena = c->arena;
     a.page_table = c->page_table;

@@ -59,6 +59,10 @@ struct DecodeArgs {
 
 hipError_t launch_decode(int D, int NH, bool dense, const DecodeArgs &a, hipStream_t st);
 
+// LDS bytes one decode workgroup needs; the device offers 160 KiB.
+size_t decode_shmem_bytes(int D, int NH, bool dense, int nsplit, int maxp);
+constexpr size_t kMaxLds = 160 * 1024;
+
 hipError_t launch_encode(int D, int Hkv, int64_t n_tokens, const uint16_t *keys, const float *cb8,
                          const float *cb4, uint16_t *radius, uint8_t *codes8, uint8_t *codes4,
                          hipStream_t st);

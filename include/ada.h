@@ -211,7 +211,7 @@ size_t ada_decode_workspace_size(const ada_geom *geom, int32_t num_seqs,
  *   logits_dbg [S][Hq][max_pages_per_head * 16] f32 or NULL: for parity
  *     tests, receives l_t of every valid slot (page p, slot t at p*16+t);
  *     other entries are left untouched.
- *   num_splits: page-range splits per row (0 = ada_decode_default_splits).
+ *   num_splits: page subsets per row, 1..1024 (0 = ada_decode_default_splits).
  *   ws: ada_decode_workspace_size(geom, S, max_pages_per_head, num_splits)
  *     bytes, 256-byte aligned.  Its first S*Hkv 32-bit words are per-row
  *     split counters: they must be zero before the first call that uses the

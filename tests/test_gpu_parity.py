@@ -207,7 +207,7 @@ def test_pack_ragged_protect_permuted_two_calls(D):
     scores[4, 0] = 0.0
     N1 = 537
     cu1, cu2 = np.array([0, 500, 537, 537], np.int32), np.array([0, 20, 20, 65], np.int32)
-    bp1 = np.array([(2500, 7500, 9000), (0, 5000, 10000), (3000, 3000, 3000)], np.int32)
+    bp1 = np.array([(2500, 7500, 9000), (1000, 5000, 10000), (3000, 3000, 3000)], np.int32)
     bp2 = np.array([(10000, 10000, 10000), (5000, 5000, 5000), (0, 2000, 6000)], np.int32)
     protect = np.zeros((case["N"], 2), np.uint8)
     protect[[1, 9, 77, 300], 0] = 1
