@@ -12,25 +12,36 @@
 // Work decomposition.  One workgroup (8 wave64s, one per CU at D = 128)
 // serves one (sequence, kv-head) row and one of `nsplit` interleaved page
 // subsets of it, for all NH query heads of the GQA group, so every page is
-// read from HBM once.  Wave w of split s takes pages s + (w + 8i) * nsplit.
-// A wave holds a page in 64 lanes: lane (tl, db) = tl * 8 + db keeps slots tl
-// and tl + 8 for the dims of block db ([db * D/8, (db + 1) * D/8)), and the
-// codes of the groups inside that block.  The page format stores exactly
-// these values as the lane's own 16-byte chunks, so every load is one
-// coalesced dwordx4 per lane.  Each wave keeps the next page's loads in
-// flight while it computes the current one (a register double buffer), and
-// its page-table entries sit in lane registers, 64 pages at a time.
-// Logits are summed over the 8 dim blocks of a slot with three DPP steps
-// inside a row; each lane then weights its own value chunks, so the PV
-// product needs no lane exchange.  Running maxima are wave-wide (DPP row
-// max + two row broadcasts per head and page); accumulators are rescaled
-// only when the maximum grows by more than 2^8, which keeps every weight
-// <= 2^8.  At the end the 8 slot pairs are summed with lane exchanges, the
-// 8 waves are merged through LDS, and the split's partial (m, l, acc) is
-// written; the last split of each row to finish (an atomic counter per row)
-// merges the row's partials into the outputs, so one decode step is one
-// kernel launch.
+// read from HBM once.  Wave w of split s takes pages s + (w + 8i) * nsplit,
+// one page (16 slots) at a time, with the next page's eight dwordx4 loads in
+// flight while the current one is computed.
+//
+// Per page the wave forms a 16 x 16 tile of logits, rows = query heads
+// (NH used, the rest zero), columns = slots, held the way a 16x16x16 MFMA
+// takes its A operand: lane h + 16 r holds slots 4r .. 4r+3 of head h.
+//   - fp16 / bf16 key pages: one MFMA chain, keys (stored in the B^T order,
+//     so each lane's 8-byte half chunk is its operand) times the query
+//     block held in registers; the result lands in the tile layout.
+//   - coded pages: lane j + 16 r sums the LUT entries of slot 4r + j/4 over
+//     a quarter of the groups, a quad reduction completes each slot, and
+//     three DPP row rotations move head h's values of the row's four slots
+//     into lane h + 16 r; the radii scale them there.
+// The softmax runs on that tile (running maxima per head, rescaled only
+// when a page's maximum exceeds the running one by 2^8, so every weight is
+// at most 2^8), and the weights are split into bf16 hi + lo parts (about
+// 16 significant bits) for two MFMAs per 16-dim value block.  Value
+// sections are stored as the B operand (lane n + 16 r: slots 4r .. 4r+3 of
+// dim n); int8 values become bf16 exactly, and their per-slot scales are
+// folded into the weights.  The output accumulators are the MFMA C tiles
+// (rows = heads, so lanes 0-15 hold the outputs of one dim each).
+//
+// At the end the 8 waves are merged through LDS and the split's partial
+// (m, l, acc) is written; the last split of each row to finish (an atomic
+// counter per row) merges the row's partials into the outputs, so one
+// decode step is one kernel launch.
 #include "ada_internal.h"
+
+#include <type_traits>
 
 namespace ada {
 namespace {
@@ -41,35 +52,49 @@ constexpr float kRescale = 8.0f; // log2 of the largest weight kept between resc
 constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
 
-typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
-typedef __bf16 bf162_t __attribute__((ext_vector_type(2)));
-
-__device__ __forceinline__ float bf16_lo(uint32_t u) { return __uint_as_float(u << 16); }
-__device__ __forceinline__ float bf16_hi(uint32_t u) { return __uint_as_float(u & 0xffff0000u); }
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef const u32x4 __attribute__((address_space(1))) *gchunk;
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ float f16_to_f32(uint32_t h)
 {
     return (float)__builtin_bit_cast(_Float16, (uint16_t)h);
 }
 
-// Sum over the 8 dim-block lanes of a slot pair (lanes 8k..8k+7); every lane
-// of the group receives the total.
-__device__ __forceinline__ float block_sum8(float x)
+// Two floats -> packed bf16 pair (round to nearest even).
+__device__ __forceinline__ uint32_t pack_bf16(float a, float b)
 {
-    x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0xb1, 0xf, 0xf, false)); // xor 1
-    x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x4e, 0xf, 0xf, false)); // xor 2
-    x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x141, 0xf, 0xf, false)); // half-row mirror
-    return x;
+    const f32x2 v = {a, b};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
+}
+__device__ __forceinline__ float bf16_lo(uint32_t u) { return __uint_as_float(u << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t u) { return __uint_as_float(u & 0xffff0000u); }
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x)
+{
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xf, 0xf, false));
 }
 
-// Max over the whole wave, returned as a wave-uniform value.  Lanes of one
-// slot pair hold equal values, so the row step only needs the 8-lane rotate.
-__device__ __forceinline__ float wave_max(float x)
+// Max / sum over the four lanes h, h+16, h+32, h+48 (every lane receives it).
+__device__ __forceinline__ float rows_max(float x)
 {
-    x = fmaxf(x, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x128, 0xf, 0xf, false))); // row_ror 8
-    x = fmaxf(x, __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(x), __float_as_int(x), 0x142, 0xa, 0xf, false))); // row_bcast 15
-    x = fmaxf(x, __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(x), __float_as_int(x), 0x143, 0xc, 0xf, false))); // row_bcast 31
-    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 63));
+    auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+    auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float rows_sum(float x)
+{
+    auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+    auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
 // Device-coherent (agent-scope) accesses to the split partials.
@@ -80,15 +105,6 @@ __device__ __forceinline__ void coherent_store(float *p, float v)
 __device__ __forceinline__ float coherent_load(const float *p)
 {
     return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-// Sum over the 8 slot pairs (lanes db, db+8, ..., db+56).
-__device__ __forceinline__ float pair_sum8(float x)
-{
-    x += __shfl_xor(x, 8, 64);
-    x += __shfl_xor(x, 16, 64);
-    x += __shfl_xor(x, 32, 64);
-    return x;
 }
 
 template <int NH>
@@ -105,61 +121,9 @@ __device__ __forceinline__ void lut_add(const float *lut, int idx, float (&sum)[
     }
 }
 
-// Raw bytes of one page as this lane sees them: eight 16-byte loads.
-//   tiers 0/3: c[0..D/32) K chunks, then D/32 V chunks
-//   tier 1:    c[0..D/32) V chunks; c[4], c[5] the 16-byte blocks holding
-//              slot t0's / t1's codes; c[6], c[7] radius[0..8) / [8..16)
-//   tier 2:    c[0..D/64) V chunks; c[2], c[3] value scale[0..8) / [8..16);
-//              c[4..7] as in tier 1
-// Unused slots repeat the page's first chunk (same cache lines, no extra
-// HBM traffic).  Every tier issues the same eight loads with no branch, so
-// the next page's loads stay in flight while the current page is computed.
-typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-typedef const u32x4 __attribute__((address_space(1))) *gchunk;
-
-struct PageRegs {
-    u32x4 c[8];
-    int tier, nvalid;
-};
-
-template <int D, bool DENSE>
-__device__ __forceinline__ void fetch_page(PageRegs &pr, const uint8_t *page, int tier, int nvalid,
-                                           int lane, int t0)
-{
-    constexpr int G = D / 8;
-    const int t1 = t0 + 8;
-    pr.tier = tier;
-    pr.nvalid = nvalid;
-    // byte offsets inside the page (the page address is wave-uniform)
-    uint32_t o[8];
-    const uint32_t lo = lane * 16;
-    if (DENSE || tier == 0) {
-#pragma unroll
-        for (int c = 0; c < 8; c++)
-            o[c] = c < D / 16 ? lo + c * 1024 : lo;
-    } else {
-        const int rb = tier == 1 ? G : G / 2; // code bytes per slot
-        const uint32_t codes = codes_off(D, tier), rad = radius_off(D, tier);
-        const int nv = tier == 1 ? D / 32 : D / 64;
-#pragma unroll
-        for (int c = 0; c < 4; c++)
-            o[c] = c < nv ? lo + c * 1024 : lo;
-        if (tier == 2) {
-            o[2] = vscale_off(D);
-            o[3] = vscale_off(D) + 16;
-        }
-        o[4] = codes + ((t0 * rb) & ~15);
-        o[5] = codes + ((t1 * rb) & ~15);
-        o[6] = rad;
-        o[7] = rad + 16;
-    }
-#pragma unroll
-    for (int c = 0; c < 8; c++)
-        pr.c[c] = *(gchunk)(page + o[c]);
-}
-
-// Bytes at a per-lane offset o (0..15) of a 16-byte chunk, picked with
-// masks and a 64-bit shift so the chunk stays in registers.
+// The bytes from offset o (0..15) of a 16-byte chunk up to the end of its
+// 8-byte half, picked with masks and a 64-bit shift so the chunk stays in
+// registers.  A lane's code bytes never straddle an 8-byte boundary.
 __device__ __forceinline__ uint32_t bits_at(const u32x4 &v, int o)
 {
     const uint64_t lo = ((uint64_t)v.y << 32) | v.x;
@@ -167,172 +131,283 @@ __device__ __forceinline__ uint32_t bits_at(const u32x4 &v, int o)
     const uint64_t m = 0ull - (uint64_t)((o >> 3) & 1);
     return (uint32_t)(((lo & ~m) | (hi & m)) >> (8 * (o & 7)));
 }
-__device__ __forceinline__ uint32_t u8_at(const u32x4 &v, int o) { return bits_at(v, o) & 255u; }
-__device__ __forceinline__ uint32_t u16_at(const u32x4 &v, int o) { return bits_at(v, o) & 0xffffu; }
+
+// Per-lane constants of the page walk.
+struct Lane {
+    int lane, hl, r;      // lane = hl + 16 r
+    int gq, g0;           // coded logits: group quarter, first group
+    uint32_t cblk1, cblk2; // code block of the lane's slot, tiers 1 and 2
+    int co1, co2;         // byte of the lane's codes inside that block
+    uint32_t rblk1, rblk2, sblk2; // radius blocks (tiers 1, 2), scale block (tier 2)
+    int nv_off;           // 4 r, or a large value for lanes of unused heads
+};
+
+template <int D, int NH>
+__device__ __forceinline__ Lane make_lane(int lane)
+{
+    constexpr int G = D / 8, GPL = G / 4;
+    Lane L;
+    L.lane = lane;
+    L.hl = lane & 15;
+    L.r = lane >> 4;
+    const int t = 4 * L.r + (L.hl >> 2); // slot whose codes this lane reads
+    L.gq = L.hl & 3;
+    L.g0 = L.gq * GPL;
+    const int b1 = t * G + L.g0, b2 = t * (G / 2) + L.g0 / 2;
+    L.cblk1 = codes_off(D, 1) + (b1 & ~15);
+    L.co1 = b1 & 15;
+    L.cblk2 = codes_off(D, 2) + (b2 & ~15);
+    L.co2 = b2 & 15;
+    L.rblk1 = radius_off(D, 1) + 16 * (L.r >> 1);
+    L.rblk2 = radius_off(D, 2) + 16 * (L.r >> 1);
+    L.sblk2 = vscale_off(D) + 16 * (L.r >> 1);
+    L.nv_off = L.hl < NH ? 4 * L.r : 64;
+    return L;
+}
+
+// Raw bytes of one page as this lane sees them: NL 16-byte loads.
+//   tiers 0/3: c[0 .. D/32) key chunks, c[D/32 .. D/16) value chunks
+//   tier 1:    c[0 .. D/32) value chunks; c[4] the lane's code block;
+//              c[5] the 16-byte block of radii holding slots 4r .. 4r+3
+//   tier 2:    c[0 .. D/64) value chunks; c[2] the scale block (as c[5]);
+//              c[4], c[5] as in tier 1
+// Unused loads repeat chunk 0 (same cache lines, no extra HBM traffic).
+// Every tier issues the same loads with no branch, so the next page's loads
+// stay in flight while the current page is computed.
+template <int D>
+struct PageRegs {
+    static constexpr int NL = D == 128 ? 8 : 6;
+    u32x4 c[NL];
+    int tier, nvalid;
+};
+
+template <int D, bool DENSE>
+__device__ __forceinline__ void fetch_page(PageRegs<D> &pr, const uint8_t *page, int tier, int nvalid,
+                                           const Lane &L)
+{
+    constexpr int NL = PageRegs<D>::NL;
+    pr.tier = tier;
+    pr.nvalid = nvalid;
+    const uint32_t lo = L.lane * 16;
+    uint32_t o[NL];
+#pragma unroll
+    for (int c = 0; c < NL; c++) {
+        const uint32_t dense = c < D / 16 ? lo + c * 1024 : lo;
+        uint32_t t1 = c < D / 32 ? lo + c * 1024 : lo;
+        uint32_t t2 = c < D / 64 ? lo + c * 1024 : lo;
+        if (c == 2)
+            t2 = L.sblk2;
+        if (c == 4) {
+            t1 = L.cblk1;
+            t2 = L.cblk2;
+        }
+        if (c == 5) {
+            t1 = L.rblk1;
+            t2 = L.rblk2;
+        }
+        o[c] = (DENSE || tier == 0) ? dense : tier == 1 ? t1 : t2;
+    }
+#pragma unroll
+    for (int c = 0; c < NL; c++)
+        pr.c[c] = *(gchunk)(page + o[c]);
+}
+
+// The four fp16 values of slots 4r .. 4r+3 from a 16-byte block holding
+// slots 8 (r/2) .. 8 (r/2) + 7.
+__device__ __forceinline__ void quad_f16(const u32x4 &blk, int r, float (&v)[4])
+{
+    const uint32_t a = (r & 1) ? blk.z : blk.x;
+    const uint32_t b = (r & 1) ? blk.w : blk.y;
+    v[0] = f16_to_f32(a & 0xffffu);
+    v[1] = f16_to_f32(a >> 16);
+    v[2] = f16_to_f32(b & 0xffffu);
+    v[3] = f16_to_f32(b >> 16);
+}
 
 template <int D, int NH>
 struct WaveState {
-    float m_run[NH], l_run[NH], corr[NH], acc[NH][D / 8];
+    f32x4 acc[D / 16]; // C tiles: lane n (< 16) element h = output dim 16 b + n of head h
+    float m[NH];       // running max per head, log2 units (wave-uniform)
+    float mlane;       // running max of this lane's head (0 for unused heads)
+    float l;           // softmax denominator: this lane's head, its slots
 };
+
+// Query operand of the key MFMA: lane h + 16 q holds dims 16 b + 4 q .. +3
+// of head h for each 16-dim block b (zero for h >= NH).
+template <int D, bool DENSE>
+struct QOperand {
+    typedef typename std::conditional<DENSE, s16x4, f16x4>::type T;
+    T blk[D / 16];
+};
+
+// Logits of a key page (fp16 keys, or bf16 keys in the dense cache) in the
+// tile layout, in log2 units.
+template <int D, bool DENSE>
+__device__ __forceinline__ void key_logits(const PageRegs<D> &cur, const QOperand<D, DENSE> &qo,
+                                           float lsc, float (&x)[4])
+{
+    f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = s0;
+#pragma unroll
+    for (int b = 0; b < D / 16; b++) {
+        const u32x4 &ch = cur.c[b / 2];
+        const u32x2 k2 = (b & 1) ? u32x2{ch.z, ch.w} : u32x2{ch.x, ch.y};
+        f32x4 &s = (b & 1) ? s1 : s0;
+        if constexpr (DENSE)
+            s = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, k2), qo.blk[b], s, 0, 0, 0);
+        else
+            s = __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4, k2), qo.blk[b], s, 0, 0, 0);
+    }
+#pragma unroll
+    for (int e = 0; e < 4; e++)
+        x[e] = (s0[e] + s1[e]) * lsc;
+}
+
+// Logits of a coded page in the tile layout, in log2 units.
+template <int D, int NH>
+__device__ __forceinline__ void coded_logits(const PageRegs<D> &cur, const float *lut, const Lane &L,
+                                             float sig2, float (&x)[4])
+{
+    constexpr int G = D / 8, GPL = G / 4;
+    const bool t8 = cur.tier == 1;
+    const uint32_t bits = bits_at(cur.c[4], t8 ? L.co1 : L.co2);
+    float s[NH];
+#pragma unroll
+    for (int h = 0; h < NH; h++)
+        s[h] = 0.f;
+#pragma unroll
+    for (int k = 0; k < GPL; k++) {
+        const int code = t8 ? (int)((bits >> (8 * k)) & 255u) : kCodes8 + (int)((bits >> (4 * k)) & 15u);
+        lut_add<NH>(lut, (L.g0 + k) * kLutCodes + code, s);
+    }
+    // complete each slot's sum over its four lanes (a quad)
+#pragma unroll
+    for (int h = 0; h < NH; h++) {
+        s[h] += dpp<0xb1>(s[h]); // quad_perm [1,0,3,2]
+        s[h] += dpp<0x4e>(s[h]); // quad_perm [2,3,0,1]
+    }
+    // lane j of a row offers head (j % 4) of its slot; lane h (< 4) of the
+    // row then collects head h of slots 4r + e from lanes 4e + h
+    float sel = s[0];
+    if constexpr (NH >= 2)
+        sel = (L.gq & 1) ? s[1] : sel;
+    if constexpr (NH == 4) {
+        sel = L.gq == 2 ? s[2] : sel;
+        sel = L.gq == 3 ? s[3] : sel;
+    }
+    float v[4];
+    v[0] = sel;
+    v[1] = dpp<0x12c>(sel); // row_ror:12 -> lane + 4
+    v[2] = dpp<0x128>(sel); // row_ror:8  -> lane + 8
+    v[3] = dpp<0x124>(sel); // row_ror:4  -> lane + 12
+    float rad[4];
+    quad_f16(cur.c[5], L.r, rad);
+#pragma unroll
+    for (int e = 0; e < 4; e++)
+        x[e] = v[e] * (rad[e] * sig2);
+}
 
 // Logits, online-softmax update and PV product of one page (page index p in
 // its row) for the wave's NH query heads.
 template <int D, int NH, bool DENSE>
-__device__ __forceinline__ void process_page(const PageRegs &cur, int p, WaveState<D, NH> &st,
-                                             const float *lut, const uint32_t *qh,
-                                             const float (&lscale)[NH], float sigma, float *lgout,
-                                             int maxp, int t0, int db)
+__device__ __forceinline__ void process_page(const PageRegs<D> &cur, int p, WaveState<D, NH> &st,
+                                             const float *lut, const QOperand<D, DENSE> &qo, float lsc,
+                                             float sig2, float *lgout, int maxp, const Lane &L)
 {
-    constexpr int G = D / 8, B = D / 8, GPL = B / 8, NWC = D / 32, NNC = D / 64;
-    const int t1 = t0 + 8;
     const int tier = cur.tier;
-    const bool v0 = t0 < cur.nvalid, v1 = t1 < cur.nvalid;
+    float x[4];
+    if (DENSE || tier == 0)
+        key_logits<D, DENSE>(cur, qo, lsc, x);
+    else
+        coded_logits<D, NH>(cur, lut, L, sig2, x);
 
-    float lg0[NH], lg1[NH];
-    if (DENSE || tier == 0) {
-        // dot-product tier: the lane's K chunks (slot t0 first), then the
-        // sum over the 8 dim blocks
-        float p0[NH], p1[NH];
+    // mask slots past the page's valid count, and unused heads
+    const int nv = cur.nvalid - L.nv_off;
 #pragma unroll
-        for (int h = 0; h < NH; h++)
-            p0[h] = p1[h] = 0.f;
+    for (int e = 0; e < 4; e++)
+        x[e] = e < nv ? x[e] : -INFINITY;
+
+    if (lgout != nullptr && L.hl < NH) {
+        float *lo = lgout + (size_t)L.hl * maxp * kSlots + (size_t)p * kSlots + 4 * L.r;
 #pragma unroll
-        for (int c = 0; c < NWC; c++) {
-            const uint32_t kw[4] = {cur.c[c].x, cur.c[c].y, cur.c[c].z, cur.c[c].w};
-            const int qo = db * (B / 2) + ((8 * c) % B) / 2; // first q pair of this chunk
-            const bool second = (8 * c) >= B;
-#pragma unroll
-            for (int h = 0; h < NH; h++) {
-                const u32x4 qv = *reinterpret_cast<const u32x4 *>(qh + h * (D / 2) + qo);
-                const uint32_t qw[4] = {qv.x, qv.y, qv.z, qv.w};
-#pragma unroll
-                for (int w = 0; w < 4; w++) {
-                    float &pp = second ? p1[h] : p0[h];
-                    if constexpr (DENSE)
-                        pp = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf162_t, qw[w]),
-                                                             __builtin_bit_cast(bf162_t, kw[w]), pp, false);
-                    else
-                        pp = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, qw[w]),
-                                                    __builtin_bit_cast(half2_t, kw[w]), pp, false);
-                }
-            }
-        }
-#pragma unroll
-        for (int h = 0; h < NH; h++) {
-            lg0[h] = block_sum8(p0[h]) * lscale[h];
-            lg1[h] = block_sum8(p1[h]) * lscale[h];
-        }
-    } else {
-        float s0[NH], s1[NH];
-#pragma unroll
-        for (int h = 0; h < NH; h++)
-            s0[h] = s1[h] = 0.f;
-        // the lane's code byte(s) inside its two 16-byte code blocks
-        const int rb = tier == 1 ? G : G / 2;
-        const int ob = tier == 1 ? GPL * db : (GPL * db) / 2;
-        const int o0 = ((t0 * rb) & 15) + ob, o1 = ((t1 * rb) & 15) + ob;
-        if (tier == 1) {
-            const uint32_t code0 = GPL == 2 ? u16_at(cur.c[4], o0) : u8_at(cur.c[4], o0);
-            const uint32_t code1 = GPL == 2 ? u16_at(cur.c[5], o1) : u8_at(cur.c[5], o1);
-#pragma unroll
-            for (int k = 0; k < GPL; k++) {
-                lut_add<NH>(lut, (GPL * db + k) * kLutCodes + ((code0 >> (8 * k)) & 255), s0);
-                lut_add<NH>(lut, (GPL * db + k) * kLutCodes + ((code1 >> (8 * k)) & 255), s1);
-            }
-        } else {
-            const int sh = GPL == 2 ? 0 : 4 * (db & 1);
-            const uint32_t code0 = u8_at(cur.c[4], o0), code1 = u8_at(cur.c[5], o1);
-#pragma unroll
-            for (int k = 0; k < GPL; k++) {
-                lut_add<NH>(lut, (GPL * db + k) * kLutCodes + kCodes8 + ((code0 >> (sh + 4 * k)) & 15), s0);
-                lut_add<NH>(lut, (GPL * db + k) * kLutCodes + kCodes8 + ((code1 >> (sh + 4 * k)) & 15), s1);
-            }
-        }
-        const float r0 = sigma * f16_to_f32(u16_at(cur.c[6], 2 * t0));
-        const float r1 = sigma * f16_to_f32(u16_at(cur.c[7], 2 * t0));
-#pragma unroll
-        for (int h = 0; h < NH; h++) {
-            lg0[h] = block_sum8(s0[h]) * r0;
-            lg1[h] = block_sum8(s1[h]) * r1;
-        }
+        for (int e = 0; e < 4; e++)
+            if (e < nv)
+                lo[e] = x[e] * kLn2;
     }
 
-    if (lgout != nullptr && db == 0) {
-#pragma unroll
-        for (int h = 0; h < NH; h++) {
-            float *lo = lgout + (size_t)h * maxp * kSlots + (size_t)p * kSlots;
-            if (v0)
-                lo[t0] = lg0[h];
-            if (v1)
-                lo[t1] = lg1[h];
-        }
-    }
-
-    // online softmax, log2 domain
-    float w0[NH], w1[NH];
+    // online softmax: per-head page maxima, rescale when they run ahead
+    const float pm = rows_max(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])));
 #pragma unroll
     for (int h = 0; h < NH; h++) {
-        const float x0 = v0 ? lg0[h] * kLog2e : -INFINITY;
-        const float x1 = v1 ? lg1[h] * kLog2e : -INFINITY;
-        const float pmax = wave_max(fmaxf(x0, x1));
-        if (pmax > st.m_run[h] + kRescale) {
-            const float f = __builtin_amdgcn_exp2f(st.m_run[h] - pmax);
-            st.l_run[h] *= f;
-            st.corr[h] *= f;
+        const float pmh = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(pm), h));
+        if (pmh > st.m[h] + kRescale) {
+            const float f = __builtin_amdgcn_exp2f(st.m[h] - pmh);
+            st.m[h] = pmh;
 #pragma unroll
-            for (int e = 0; e < B; e++)
-                st.acc[h][e] *= f;
-            st.m_run[h] = pmax;
+            for (int b = 0; b < D / 16; b++)
+                st.acc[b][h] *= f;
+            const bool mine = L.hl == h;
+            st.l = mine ? st.l * f : st.l;
+            st.mlane = mine ? pmh : st.mlane;
         }
-        w0[h] = __builtin_amdgcn_exp2f(x0 - st.m_run[h]);
-        w1[h] = __builtin_amdgcn_exp2f(x1 - st.m_run[h]);
-        st.l_run[h] += w0[h] + w1[h];
     }
+    float w[4];
+#pragma unroll
+    for (int e = 0; e < 4; e++)
+        w[e] = __builtin_amdgcn_exp2f(x[e] - st.mlane);
+    st.l += (w[0] + w[1]) + (w[2] + w[3]);
 
-    if (DENSE || tier != 2) {
-        const bool kfirst = DENSE || tier == 0; // V chunks follow K in tiers 0 and 3
+    const bool int8v = !DENSE && tier == 2;
+    if (int8v) {
+        float sc[4];
+        quad_f16(cur.c[2], L.r, sc);
 #pragma unroll
-        for (int c = 0; c < NWC; c++) {
-            const u32x4 v = kfirst ? cur.c[NWC + c] : cur.c[c];
-            const float vf[8] = {bf16_lo(v.x), bf16_hi(v.x), bf16_lo(v.y), bf16_hi(v.y),
-                                 bf16_lo(v.z), bf16_hi(v.z), bf16_lo(v.w), bf16_hi(v.w)};
-            const int eo = (8 * c) % B;
-            const bool second = (8 * c) >= B;
+        for (int e = 0; e < 4; e++)
+            w[e] *= sc[e];
+    }
+    // weights as bf16 hi + lo (A operands)
+    const uint32_t h01 = pack_bf16(w[0], w[1]), h23 = pack_bf16(w[2], w[3]);
+    const uint32_t l01 = pack_bf16(w[0] - bf16_lo(h01), w[1] - bf16_hi(h01));
+    const uint32_t l23 = pack_bf16(w[2] - bf16_lo(h23), w[3] - bf16_hi(h23));
+    const s16x4 ahi = __builtin_bit_cast(s16x4, u32x2{h01, h23});
+    const s16x4 alo = __builtin_bit_cast(s16x4, u32x2{l01, l23});
+
+    if (int8v) {
+        // value block b: dword b % 4 of chunk b / 4, one int8 per slot
 #pragma unroll
-            for (int h = 0; h < NH; h++) {
-                const float wt = second ? w1[h] : w0[h];
+        for (int b = 0; b < D / 16; b++) {
+            const u32x4 &ch = cur.c[b / 4];
+            const uint32_t q = (b % 4 == 0) ? ch.x : (b % 4 == 1) ? ch.y : (b % 4 == 2) ? ch.z : ch.w;
+            const uint32_t v01 = pack_bf16((float)(signed char)(q & 255u), (float)(signed char)((q >> 8) & 255u));
+            const uint32_t v23 = pack_bf16((float)(signed char)((q >> 16) & 255u), (float)(signed char)(q >> 24));
+            const s16x4 bv = __builtin_bit_cast(s16x4, u32x2{v01, v23});
+            st.acc[b] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ahi, bv, st.acc[b], 0, 0, 0);
+            st.acc[b] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(alo, bv, st.acc[b], 0, 0, 0);
+        }
+    } else if (DENSE || tier == 0) {
 #pragma unroll
-                for (int e = 0; e < 8; e++)
-                    st.acc[h][eo + e] = fmaf(wt, vf[e], st.acc[h][eo + e]);
-            }
+        for (int b = 0; b < D / 16; b++) {
+            const u32x4 &ch = cur.c[D / 32 + b / 2];
+            const s16x4 bv = __builtin_bit_cast(s16x4, (b & 1) ? u32x2{ch.z, ch.w} : u32x2{ch.x, ch.y});
+            st.acc[b] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ahi, bv, st.acc[b], 0, 0, 0);
+        }
+#pragma unroll
+        for (int b = 0; b < D / 16; b++) {
+            const u32x4 &ch = cur.c[D / 32 + b / 2];
+            const s16x4 bv = __builtin_bit_cast(s16x4, (b & 1) ? u32x2{ch.z, ch.w} : u32x2{ch.x, ch.y});
+            st.acc[b] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(alo, bv, st.acc[b], 0, 0, 0);
         }
     } else {
-        // int8 values: weight * scale applied to the biased bytes
-        // (byte ^ 0x80 = v + 128); the bias is removed once at the end.
-        const float sc0 = f16_to_f32(u16_at(cur.c[2], 2 * t0));
-        const float sc1 = f16_to_f32(u16_at(cur.c[3], 2 * t0));
-        float pv0[NH], pv1[NH];
 #pragma unroll
-        for (int h = 0; h < NH; h++) {
-            pv0[h] = w0[h] * sc0;
-            pv1[h] = w1[h] * sc1;
-            st.corr[h] += pv0[h] + pv1[h];
+        for (int b = 0; b < D / 16; b++) {
+            const u32x4 &ch = cur.c[b / 2];
+            const s16x4 bv = __builtin_bit_cast(s16x4, (b & 1) ? u32x2{ch.z, ch.w} : u32x2{ch.x, ch.y});
+            st.acc[b] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ahi, bv, st.acc[b], 0, 0, 0);
         }
 #pragma unroll
-        for (int c = 0; c < NNC; c++) {
-            const u32x4 v = cur.c[c];
-            const uint32_t vw[4] = {v.x ^ 0x80808080u, v.y ^ 0x80808080u, v.z ^ 0x80808080u,
-                                    v.w ^ 0x80808080u};
-#pragma unroll
-            for (int e = 0; e < 16; e++) {
-                const int w = 16 * c + e; // lane element
-                const float b = (float)((vw[e / 4] >> (8 * (e % 4))) & 255u);
-#pragma unroll
-                for (int h = 0; h < NH; h++) {
-                    const float wt = w >= B ? pv1[h] : pv0[h];
-                    st.acc[h][w % B] = fmaf(wt, b, st.acc[h][w % B]);
-                }
-            }
+        for (int b = 0; b < D / 16; b++) {
+            const u32x4 &ch = cur.c[b / 2];
+            const s16x4 bv = __builtin_bit_cast(s16x4, (b & 1) ? u32x2{ch.z, ch.w} : u32x2{ch.x, ch.y});
+            st.acc[b] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(alo, bv, st.acc[b], 0, 0, 0);
         }
     }
 }
@@ -340,25 +415,23 @@ __device__ __forceinline__ void process_page(const PageRegs &cur, int p, WaveSta
 // Issues the loads of the page whose table entry is e = (offset in 128-byte
 // units, metadata byte); e is the same in every lane.
 template <int D, bool DENSE>
-__device__ __forceinline__ void fetch_entry(PageRegs &pr, uint2 e, const uint8_t *arena, int lane, int t0)
+__device__ __forceinline__ void fetch_entry(PageRegs<D> &pr, uint2 e, const uint8_t *arena, const Lane &L)
 {
     const uint32_t off = __builtin_amdgcn_readfirstlane(e.x);
     const uint32_t meta = __builtin_amdgcn_readfirstlane(e.y);
-    fetch_page<D, DENSE>(pr, arena + (size_t)off * kUnit, meta & 3, ((meta >> 2) & 15) + 1, lane, t0);
+    fetch_page<D, DENSE>(pr, arena + (size_t)off * kUnit, meta & 3, ((meta >> 2) & 15) + 1, L);
 }
 
 template <int D, int NH, bool DENSE>
 __global__ __launch_bounds__(kThreads) void decode_main(DecodeArgs a)
 {
-    constexpr int G = D / 8;      // code groups
-    constexpr int B = D / 8;      // dims per lane block
+    constexpr int G = D / 8; // code groups
     constexpr int LUT_FLOATS = DENSE ? 0 : G * kLutCodes * NH;
 
     extern __shared__ float smem[];
     float *lut = smem;
-    float *qs = smem + LUT_FLOATS;                                  // [NH][D] fp32 queries
-    uint32_t *qh = reinterpret_cast<uint32_t *>(qs + NH * D);        // [NH][D/2] query pairs
-    uint2 *tbl = reinterpret_cast<uint2 *>(qh + NH * D / 2);        // [n_wg] page-table entries
+    float *qs = smem + LUT_FLOATS;                           // [NH][D] fp32 queries
+    uint2 *tbl = reinterpret_cast<uint2 *>(qs + NH * D);     // [n_wg] page-table entries
 
     // Consecutive logical blocks share an XCD (blocks are dealt round-robin
     // over the 8 XCDs), so one row's splits hit one L2.
@@ -369,8 +442,7 @@ __global__ __launch_bounds__(kThreads) void decode_main(DecodeArgs a)
     const int row = logical / a.nsplit, split = logical % a.nsplit;
     const int s = row / a.Hkv, hkv = row % a.Hkv;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-    const int tl = lane >> 3, db = lane & 7;
-    const int t0 = tl; // the lane's slots are t0 and t0 + 8
+    const Lane L = make_lane<D, NH>(lane);
 
     // This workgroup's pages are p_k = split + k * nsplit, k < n_wg; wave w
     // takes k = w + kWaves * i, i < n_mine.  Their table entries are staged
@@ -392,133 +464,156 @@ __global__ __launch_bounds__(kThreads) void decode_main(DecodeArgs a)
     __syncthreads();
 
     // the first page's loads overlap the code-table build
-    PageRegs bufA, bufB;
+    PageRegs<D> bufA, bufB;
     if (n_mine > 0)
-        fetch_entry<D, DENSE>(bufA, tbl[wave], a.arena, lane, t0);
+        fetch_entry<D, DENSE>(bufA, tbl[wave], a.arena, L);
 
     if constexpr (!DENSE) {
-        // LUT[g][c][h] = q_h[8g..8g+8) . C[g][c]; c < 256 from cb8, else cb4.
-        // All of a thread's codeword loads are issued before any is used.
-        constexpr int CW = G * kLutCodes;
-        constexpr int PER = (CW + kThreads - 1) / kThreads;
-        const float *cb8 = a.cb8 + (size_t)hkv * G * kCodes8 * 8;
-        const float *cb4 = a.cb4 + (size_t)hkv * G * kCodes4 * 8;
-        float4 w0[PER], w1[PER];
+        // LUT[g][c][h] = q_h[8g .. 8g+8) . C[g][c]; c < 256 from cb8, else
+        // cb4.  TPG threads share group g (its query slices in registers);
+        // consecutive threads take consecutive codewords, and all of a
+        // thread's codeword loads are issued before any is used.
+        constexpr int TPG = kThreads / G;
+        constexpr int NC = (kLutCodes + TPG - 1) / TPG;
+        const int g = tid / TPG, c0 = tid % TPG;
+        const float *cb8 = a.cb8 + ((size_t)hkv * G + g) * kCodes8 * 8;
+        const float *cb4 = a.cb4 + ((size_t)hkv * G + g) * kCodes4 * 8;
+        float4 w0[NC], w1[NC];
 #pragma unroll
-        for (int k = 0; k < PER; k++) {
-            const int i = min(tid + k * kThreads, CW - 1);
-            const int g = i / kLutCodes, c = i - g * kLutCodes;
-            const float *w = c < kCodes8 ? cb8 + ((size_t)g * kCodes8 + c) * 8
-                                         : cb4 + ((size_t)g * kCodes4 + (c - kCodes8)) * 8;
+        for (int k = 0; k < NC; k++) {
+            const int c = min(c0 + k * TPG, kLutCodes - 1);
+            const float *w = c < kCodes8 ? cb8 + c * 8 : cb4 + (c - kCodes8) * 8;
             w0[k] = *reinterpret_cast<const float4 *>(w);
             w1[k] = *reinterpret_cast<const float4 *>(w + 4);
         }
+        float qq[NH][8];
 #pragma unroll
-        for (int k = 0; k < PER; k++) {
-            const int i = tid + k * kThreads;
-            if (i < CW) {
-                const int g = i / kLutCodes;
+        for (int h = 0; h < NH; h++) {
+            const float4 a0 = *reinterpret_cast<const float4 *>(qs + h * D + 8 * g);
+            const float4 a1 = *reinterpret_cast<const float4 *>(qs + h * D + 8 * g + 4);
+            qq[h][0] = a0.x; qq[h][1] = a0.y; qq[h][2] = a0.z; qq[h][3] = a0.w;
+            qq[h][4] = a1.x; qq[h][5] = a1.y; qq[h][6] = a1.z; qq[h][7] = a1.w;
+        }
+#pragma unroll
+        for (int k = 0; k < NC; k++) {
+            const int c = c0 + k * TPG;
+            if (c < kLutCodes) {
+                float o[NH];
 #pragma unroll
                 for (int h = 0; h < NH; h++) {
-                    const float *qq = qs + h * D + 8 * g;
-                    float acc = qq[0] * w0[k].x;
-                    acc = fmaf(qq[1], w0[k].y, acc);
-                    acc = fmaf(qq[2], w0[k].z, acc);
-                    acc = fmaf(qq[3], w0[k].w, acc);
-                    acc = fmaf(qq[4], w1[k].x, acc);
-                    acc = fmaf(qq[5], w1[k].y, acc);
-                    acc = fmaf(qq[6], w1[k].z, acc);
-                    acc = fmaf(qq[7], w1[k].w, acc);
-                    lut[i * NH + h] = acc;
+                    float acc = qq[h][0] * w0[k].x;
+                    acc = fmaf(qq[h][1], w0[k].y, acc);
+                    acc = fmaf(qq[h][2], w0[k].z, acc);
+                    acc = fmaf(qq[h][3], w0[k].w, acc);
+                    acc = fmaf(qq[h][4], w1[k].x, acc);
+                    acc = fmaf(qq[h][5], w1[k].y, acc);
+                    acc = fmaf(qq[h][6], w1[k].z, acc);
+                    acc = fmaf(qq[h][7], w1[k].w, acc);
+                    o[h] = acc;
                 }
+                float *dst = lut + (g * kLutCodes + c) * NH;
+                if constexpr (NH == 4)
+                    *reinterpret_cast<float4 *>(dst) = make_float4(o[0], o[1], o[2], o[3]);
+                else if constexpr (NH == 2)
+                    *reinterpret_cast<float2 *>(dst) = make_float2(o[0], o[1]);
+                else
+                    dst[0] = o[0];
             }
         }
     }
 
-    // Query pairs for the dot-product tiers, in LDS.  Tier 0 (fp16 keys): q
-    // as fp16 pairs, each head scaled by 2^-e_h so its largest |q| lies in
-    // [2^14, 2^15) (exact for bf16 values within 2^-28 of that maximum);
-    // tier 3 (bf16 keys): q as bf16 pairs, exact.
-    float lscale[NH]; // softmax scale (times 2^e_h for tier 0)
+    // Query operand of the key MFMA.  fp16 keys: each head's q scaled by
+    // 2^-e_h so its largest |q| lies in [2^14, 2^15) (exact for bf16 values
+    // within 2^-28 of that maximum); bf16 keys: q as is (exact).
+    QOperand<D, DENSE> qo;
+    float lsc; // softmax scale (times 2^e_h for fp16 keys) in log2 units, this lane's head
+    {
+        int eh = 0;
+        if constexpr (!DENSE) {
 #pragma unroll
-    for (int h = 0; h < NH; h++) {
-        float mx = 0.f;
-        for (int d = lane; d < D; d += 64)
-            mx = fmaxf(mx, fabsf(qs[h * D + d]));
+            for (int h = 0; h < NH; h++) {
+                float mx = 0.f;
+                for (int d = lane; d < D; d += 64)
+                    mx = fmaxf(mx, fabsf(qs[h * D + d]));
 #pragma unroll
-        for (int o = 32; o >= 1; o >>= 1)
-            mx = fmaxf(mx, __shfl_xor(mx, o, 64));
-        int e = 0;
-        if (!DENSE && mx > 0.f) {
-            int ex;
-            frexpf(mx, &ex);
-            e = ex - 15;
-        }
-        lscale[h] = ldexpf(a.sigma, e);
-        if (wave == 0) {
-            for (int k = lane; k < D / 2; k += 64) {
-                const float x0 = qs[h * D + 2 * k], x1 = qs[h * D + 2 * k + 1];
-                if constexpr (DENSE) {
-                    qh[h * (D / 2) + k] = (__float_as_uint(x0) >> 16) | (__float_as_uint(x1) & 0xffff0000u);
-                } else {
-                    half2_t v;
-                    v.x = (_Float16)ldexpf(x0, -e);
-                    v.y = (_Float16)ldexpf(x1, -e);
-                    qh[h * (D / 2) + k] = __builtin_bit_cast(uint32_t, v);
+                for (int o = 32; o >= 1; o >>= 1)
+                    mx = fmaxf(mx, __shfl_xor(mx, o, 64));
+                int ex = 0;
+                if (mx > 0.f) {
+                    frexpf(mx, &ex);
+                    ex -= 15;
                 }
+                eh = L.hl == h ? ex : eh;
+            }
+        }
+        lsc = ldexpf(a.sigma, eh) * kLog2e;
+        const int qq = L.r; // dims 4 q .. 4 q + 3 of each block
+#pragma unroll
+        for (int b = 0; b < D / 16; b++) {
+            float v[4] = {0.f, 0.f, 0.f, 0.f};
+            if (L.hl < NH) {
+                const float4 t = *reinterpret_cast<const float4 *>(qs + L.hl * D + 16 * b + 4 * qq);
+                v[0] = t.x; v[1] = t.y; v[2] = t.z; v[3] = t.w;
+            }
+            if constexpr (DENSE) {
+                s16x4 o;
+#pragma unroll
+                for (int e = 0; e < 4; e++)
+                    o[e] = (short)(__float_as_uint(v[e]) >> 16);
+                qo.blk[b] = o;
+            } else {
+                f16x4 o;
+#pragma unroll
+                for (int e = 0; e < 4; e++)
+                    o[e] = (_Float16)ldexpf(v[e], -eh);
+                qo.blk[b] = o;
             }
         }
     }
+    const float sig2 = a.sigma * kLog2e;
     __syncthreads();
 
     WaveState<D, NH> st;
 #pragma unroll
-    for (int h = 0; h < NH; h++) {
-        st.m_run[h] = -INFINITY;
-        st.l_run[h] = 0.f;
-        st.corr[h] = 0.f;
+    for (int b = 0; b < D / 16; b++)
+        st.acc[b] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int e = 0; e < B; e++)
-            st.acc[h][e] = 0.f;
-    }
+    for (int h = 0; h < NH; h++)
+        st.m[h] = -INFINITY;
+    st.mlane = L.hl < NH ? -INFINITY : 0.f;
+    st.l = 0.f;
     float *lgout = a.logits ? a.logits + ((size_t)s * a.Hq + (size_t)hkv * NH) * a.maxp * kSlots
                             : nullptr;
 
     // Two register buffers in turn: page i+1's loads are in flight while
-    // page i is computed.  Every half-step issues its eight loads (past the
-    // end it reloads the last page), so the wait counts are fixed.
+    // page i is computed.  Every half-step issues its loads (past the end it
+    // reloads the last page), so the wait counts are fixed.
     const int last = n_mine - 1;
     for (int i = 0; i < n_mine; i += 2) {
-        fetch_entry<D, DENSE>(bufB, tbl[wave + kWaves * min(i + 1, last)], a.arena, lane, t0);
-        process_page<D, NH, DENSE>(bufA, split + (wave + kWaves * i) * a.nsplit, st, lut, qh, lscale,
-                                   a.sigma, lgout, a.maxp, t0, db);
+        fetch_entry<D, DENSE>(bufB, tbl[wave + kWaves * min(i + 1, last)], a.arena, L);
+        process_page<D, NH, DENSE>(bufA, split + (wave + kWaves * i) * a.nsplit, st, lut, qo, lsc, sig2,
+                                   lgout, a.maxp, L);
         if (i + 1 >= n_mine)
             break;
-        fetch_entry<D, DENSE>(bufA, tbl[wave + kWaves * min(i + 2, last)], a.arena, lane, t0);
-        process_page<D, NH, DENSE>(bufB, split + (wave + kWaves * (i + 1)) * a.nsplit, st, lut, qh,
-                                   lscale, a.sigma, lgout, a.maxp, t0, db);
+        fetch_entry<D, DENSE>(bufA, tbl[wave + kWaves * min(i + 2, last)], a.arena, L);
+        process_page<D, NH, DENSE>(bufB, split + (wave + kWaves * (i + 1)) * a.nsplit, st, lut, qo, lsc,
+                                   sig2, lgout, a.maxp, L);
     }
 
-    // Sum the 8 slot pairs of each dim block in registers, then the waves
-    // through LDS (the LUT space is free now): [wave][h][D] accumulators and
-    // [wave][h] (m, l).
+    // Waves -> LDS (the LUT space is free now): [wave][D][4] accumulators
+    // (element h = head h) and [wave][h] (m, l).
     float *red = smem;
-    float *redml = smem + kWaves * NH * D;
+    float *redml = smem + kWaves * D * 4;
+    const float lsum = rows_sum(st.l);
     __syncthreads();
+    if (lane < 16) {
 #pragma unroll
-    for (int h = 0; h < NH; h++) {
-        float *dst = red + ((size_t)wave * NH + h) * D + db * B;
-#pragma unroll
-        for (int e = 0; e < B; e++) {
-            const float v = pair_sum8(st.acc[h][e] - 128.f * st.corr[h]);
-            if (tl == 0)
-                dst[e] = v;
-        }
-        const float lsum = pair_sum8(st.l_run[h]);
-        if (lane == 0) {
-            redml[(wave * NH + h) * 2] = st.m_run[h];
-            redml[(wave * NH + h) * 2 + 1] = lsum;
-        }
+        for (int b = 0; b < D / 16; b++)
+            *reinterpret_cast<f32x4 *>(red + ((size_t)wave * D + 16 * b + lane) * 4) = st.acc[b];
+    }
+    if (lane < NH) {
+        redml[(wave * NH + lane) * 2] = st.mlane;
+        redml[(wave * NH + lane) * 2 + 1] = lsum;
     }
     __syncthreads();
 
@@ -535,7 +630,7 @@ __global__ __launch_bounds__(kThreads) void decode_main(DecodeArgs a)
         for (int w = 0; w < kWaves; w++) {
             const float mw = redml[(w * NH + h) * 2];
             const float f = mw > -INFINITY ? __builtin_amdgcn_exp2f(mw - mx) : 0.f;
-            o = fmaf(red[((size_t)w * NH + h) * D + d], f, o);
+            o = fmaf(red[((size_t)w * D + d) * 4 + h], f, o);
             l = fmaf(redml[(w * NH + h) * 2 + 1], f, l);
         }
         const size_t sh = (size_t)s * a.Hq + (size_t)hkv * NH + h;
@@ -667,9 +762,8 @@ template <int D, int NH, bool DENSE>
 size_t shmem_bytes(int nsplit, int max_wg_pages)
 {
     const size_t lut = DENSE ? 0 : (size_t)(D / 8) * kLutCodes * NH * sizeof(float);
-    size_t b = lut + (size_t)NH * D * sizeof(float) + (size_t)NH * D / 2 * sizeof(uint32_t) +
-               (size_t)max_wg_pages * sizeof(uint2);
-    const size_t red = ((size_t)kWaves * NH * D + (size_t)kWaves * NH * 2) * sizeof(float);
+    size_t b = lut + (size_t)NH * D * sizeof(float) + (size_t)max_wg_pages * sizeof(uint2);
+    const size_t red = ((size_t)kWaves * D * 4 + (size_t)kWaves * NH * 2) * sizeof(float);
     constexpr int KS = kThreads / (NH * D / 4);
     const size_t merge = ((size_t)3 * nsplit * NH + 2 * NH + (size_t)KS * NH * D) * sizeof(float);
     b = b > red ? b : red;

@@ -53,20 +53,25 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f)
     return (uint16_t)(u >> 16);
 }
 
-// Byte offset of element (t, d) in a wide (2-byte) / narrow (1-byte)
-// section: lane (t % 8) * 8 + d / B holds slots t % 8 and t % 8 + 8 over
-// dims [d / B * B, +B), B = D / 8; chunk c of every lane is the c-th KiB.
-__device__ __forceinline__ int wide_off(int D, int t, int d)
+// Byte offsets of element (slot t, dim d) in a page section: 64 lanes of
+// 16-byte chunks, chunk c of every lane forming the c-th KiB, dims in blocks
+// b = d / 16.  Row sections (keys) give lane t + 16 q dims 4q..4q+3 of each
+// block; column sections (values) give lane n + 16 r slots 4r..4r+3 of dim n
+// of each block -- the B-operand layouts of a 16x16x16 MFMA.
+__device__ __forceinline__ int row_off(int t, int d)
 {
-    const int B = D / 8;
-    const int lane = (t % 8) * 8 + d / B, w = (t / 8) * B + d % B;
-    return (w / 8) * 1024 + lane * 16 + (w % 8) * 2;
+    const int b = d / 16;
+    return (b / 2) * 1024 + (t + 16 * ((d % 16) / 4)) * 16 + (b % 2) * 8 + (d % 4) * 2;
 }
-__device__ __forceinline__ int narrow_off(int D, int t, int d)
+__device__ __forceinline__ int col_off(int t, int d)
 {
-    const int B = D / 8;
-    const int lane = (t % 8) * 8 + d / B, w = (t / 8) * B + d % B;
-    return (w / 16) * 1024 + lane * 16 + (w % 16);
+    const int b = d / 16;
+    return (b / 2) * 1024 + (d % 16 + 16 * (t / 4)) * 16 + (b % 2) * 8 + (t % 4) * 2;
+}
+__device__ __forceinline__ int col8_off(int t, int d)
+{
+    const int b = d / 16;
+    return (b / 4) * 1024 + (d % 16 + 16 * (t / 4)) * 16 + (b % 4) * 4 + t % 4;
 }
 
 } // namespace ada

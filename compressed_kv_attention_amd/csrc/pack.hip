@@ -208,12 +208,12 @@ __global__ __launch_bounds__(256) void pack_scatter(PackPlan plan, PackData data
             uint16_t kb = kk[d];
             if (tier == 3)
                 kb = f32_to_bf16(f16_bits_to_f32(kb));
-            *reinterpret_cast<uint16_t *>(base + wide_off(D, slot, d)) = kb;
-            *reinterpret_cast<uint16_t *>(base + 32 * D + wide_off(D, slot, d)) = vv[d];
+            *reinterpret_cast<uint16_t *>(base + row_off(slot, d)) = kb;
+            *reinterpret_cast<uint16_t *>(base + 32 * D + col_off(slot, d)) = vv[d];
         }
     } else if (tier == 1) {
         for (int d = k; d < D; d += 64)
-            *reinterpret_cast<uint16_t *>(base + wide_off(D, slot, d)) = vv[d];
+            *reinterpret_cast<uint16_t *>(base + col_off(slot, d)) = vv[d];
         if (k < G)
             base[codes_off(D, 1) + slot * G + k] = data.codes8[(size_t)e * G + k];
         if (k == 0)
@@ -237,7 +237,7 @@ __global__ __launch_bounds__(256) void pack_scatter(PackPlan plan, PackData data
                 y = fminf(fmaxf(y, -127.f), 127.f);
                 q = (int)y;
             }
-            base[narrow_off(D, slot, d)] = (uint8_t)(int8_t)q;
+            base[col8_off(slot, d)] = (uint8_t)(int8_t)q;
         }
         if (k < G / 2)
             base[codes_off(D, 2) + slot * (G / 2) + k] = data.codes4[(size_t)e * (G / 2) + k];

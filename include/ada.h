@@ -28,19 +28,19 @@
  * one pass guided by a small header, [ABS] for small metadata and coalesced
  * reads; nothing else is given).  A page holds 16 slots of one
  * (sequence, kv-head) row, all of one tier.  D = head_dim, G = D / 8 code
- * groups, B = D / 8 dims per block.  Page sizes are multiples of 128 bytes,
- * the unit of the page table.
- *   tier 0  fp16 keys:    K fp16 wide | V bf16 wide               64*D bytes
- *   tier 1  8-bit codes:  V bf16 wide | codes u8 [16][G] | radius fp16 [16]
- *   tier 2  4-bit codes:  V int8 narrow | codes u8 [16][G/2] | radius fp16 [16]
+ * groups.  Page sizes are multiples of 128 bytes, the unit of the page table.
+ *   tier 0  fp16 keys:    K fp16 row | V bf16 column              64*D bytes
+ *   tier 1  8-bit codes:  V bf16 column | codes u8 [16][G] | radius fp16 [16]
+ *   tier 2  4-bit codes:  V int8 column | codes u8 [16][G/2] | radius fp16 [16]
  *                         | value scale fp16 [16]
- *   tier 3  dense bf16 (comparison cache): K bf16 wide | V bf16 wide
- * Wide and narrow sections hold a 16 x D matrix as 64 lanes of 16-byte
- * chunks: element (t, d) belongs to lane (t % 8) * 8 + d / B and is element
- * w = (t / 8) * B + d % B of that lane; chunk c of all 64 lanes forms the
- * c-th KiB of the section:
- *   wide (2-byte elements):   byte (w / 8) * 1024 + lane * 16 + (w % 8) * 2
- *   narrow (1-byte elements): byte (w / 16) * 1024 + lane * 16 + w % 16.
+ *   tier 3  dense bf16 (comparison cache): K bf16 row | V bf16 column
+ * A section holds a 16 x D matrix (slot t, dim d) as 64 lanes of 16-byte
+ * chunks, chunk c of all 64 lanes forming the c-th KiB of the section; the
+ * dims split into blocks b = d / 16 of 16.  These are the operand layouts of
+ * a 16x16x16 matrix-core product:
+ *   row (2-byte):     byte (b/2)*1024 + (t + 16*((d%16)/4))*16 + (b%2)*8 + (d%4)*2
+ *   column (2-byte):  byte (b/2)*1024 + (d%16 + 16*(t/4))*16 + (b%2)*8 + (t%4)*2
+ *   column (int8):    byte (b/4)*1024 + (d%16 + 16*(t/4))*16 + (b%4)*4 + t%4
  * A 4-bit code byte holds group 2b in its low nibble, group 2b+1 in its
  * high nibble.  Unused slots and padding are zero.  page_meta byte:
  * tier | (valid_slots - 1) << 2.  For D = 128 the sizes are 8192 / 4480 /

@@ -63,10 +63,9 @@ def lib():
         L.oracle_double_to_bf16.argtypes = [D_]
         L.oracle_double_to_bf16.restype = C.c_uint16
         L.oracle_quant_v.argtypes = [I, P, P, P]
-        L.oracle_wide_off.argtypes = [I, I, I]
-        L.oracle_wide_off.restype = SZ
-        L.oracle_narrow_off.argtypes = [I, I, I]
-        L.oracle_narrow_off.restype = SZ
+        for f in (L.oracle_row_off, L.oracle_col_off, L.oracle_col8_off):
+            f.argtypes = [I, I]
+            f.restype = SZ
         _lib = L
     return _lib
 
@@ -115,12 +114,16 @@ def double_to_bf16(x: float) -> int:
     return lib().oracle_double_to_bf16(x)
 
 
-def wide_off(D, t, d) -> int:
-    return int(lib().oracle_wide_off(D, t, d))
+def row_off(t, d) -> int:
+    return int(lib().oracle_row_off(t, d))
 
 
-def narrow_off(D, t, d) -> int:
-    return int(lib().oracle_narrow_off(D, t, d))
+def col_off(t, d) -> int:
+    return int(lib().oracle_col_off(t, d))
+
+
+def col8_off(t, d) -> int:
+    return int(lib().oracle_col8_off(t, d))
 
 
 def quant_v(v_bf16) -> tuple[np.ndarray, int]:

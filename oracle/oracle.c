@@ -115,19 +115,24 @@ static uint16_t double_to_bf16(double x)
 /* from this description, in code of its own):                              */
 /*                                                                           */
 /* A page holds P = 16 slots of one (sequence, kv-head) row.  D is the head  */
-/* dimension (64 or 128), G = D/8 code groups, B = D/8 dims per block.      */
-/* Sizes are padded to 128 bytes, the page-table unit.                       */
-/*   tier 0 (fp16 keys):   K fp16 "wide" section | V bf16 "wide" section      */
-/*   tier 1 (8-bit codes): V bf16 wide | codes u8 [16][G] | radius fp16 [16] */
-/*   tier 2 (4-bit codes): V int8 "narrow" | codes u8 [16][G/2] |            */
+/* dimension (64 or 128), G = D/8 code groups.  Sizes are padded to 128     */
+/* bytes, the page-table unit.                                               */
+/*   tier 0 (fp16 keys):   K fp16 "row" section | V bf16 "column" section    */
+/*   tier 1 (8-bit codes): V bf16 column | codes u8 [16][G] | radius fp16 [16]*/
+/*   tier 2 (4-bit codes): V int8 "column" | codes u8 [16][G/2] |            */
 /*                         radius fp16 [16] | value scale fp16 [16]          */
-/*   tier 3 (dense bf16, comparison path): K bf16 wide | V bf16 wide         */
-/* A wide or narrow section stores a 16 x D matrix in 64 "lanes" of         */
-/* 16-byte chunks.  Element (t, d) belongs to lane (t % 8) * 8 + d / B and   */
-/* is element w = (t / 8) * B + d % B of that lane; the lane's elements are   */
-/* stored in chunks, chunk c of every lane together (1 KiB per c):           */
-/*   wide (2-byte elements):   byte (w / 8) * 1024 + lane * 16 + (w % 8) * 2  */
-/*   narrow (1-byte elements): byte (w / 16) * 1024 + lane * 16 + w % 16.     */
+/*   tier 3 (dense bf16, comparison path): K bf16 row | V bf16 column        */
+/* Each section stores a 16 x D matrix (slot t, dim d) as 64 "lanes" of     */
+/* 16-byte chunks, chunk c of all lanes forming the c-th KiB; the D dims   */
+/* split into blocks b = d / 16 of 16 dims.                                 */
+/*   row section (2-byte elements): slot t, dims 4q..4q+3 of a block are    */
+/*     lane t + 16 q, 8 bytes per block: byte                                */
+/*     (b/2)*1024 + (t + 16*((d%16)/4))*16 + (b%2)*8 + (d%4)*2               */
+/*   column section (2-byte elements): dim n of a block, slots 4r..4r+3 are */
+/*     lane n + 16 r, 8 bytes per block: byte                                */
+/*     (b/2)*1024 + (d%16 + 16*(t/4))*16 + (b%2)*8 + (t%4)*2                 */
+/*   int8 column section: the same lanes, 4 bytes per block: byte           */
+/*     (b/4)*1024 + (d%16 + 16*(t/4))*16 + (b%4)*4 + t%4                     */
 /* 4-bit codes: byte b of a slot holds group 2b in its low nibble and group  */
 /* 2b+1 in its high nibble.  Slots past the page's valid count, and all      */
 /* padding, are zero.  The page's metadata byte is tier | (n_valid-1) << 2.  */
@@ -135,20 +140,25 @@ static uint16_t double_to_bf16(double x)
 
 enum { SLOTS = 16, UNIT = 128 };
 
-static size_t wide_off(int D, int t, int d)
+static size_t row_off(int t, int d)
 {
-    int B = D / 8;
-    size_t lane = (size_t)(t % 8) * 8 + (size_t)(d / B);
-    size_t w = (size_t)(t / 8) * B + (size_t)(d % B);
-    return (w / 8) * 1024 + lane * 16 + (w % 8) * 2;
+    int b = d / 16;
+    return (size_t)(b / 2) * 1024 + (size_t)(t + 16 * ((d % 16) / 4)) * 16 + (size_t)(b % 2) * 8 +
+           (size_t)(d % 4) * 2;
 }
 
-static size_t narrow_off(int D, int t, int d)
+static size_t col_off(int t, int d)
 {
-    int B = D / 8;
-    size_t lane = (size_t)(t % 8) * 8 + (size_t)(d / B);
-    size_t w = (size_t)(t / 8) * B + (size_t)(d % B);
-    return (w / 16) * 1024 + lane * 16 + (w % 16);
+    int b = d / 16;
+    return (size_t)(b / 2) * 1024 + (size_t)(d % 16 + 16 * (t / 4)) * 16 + (size_t)(b % 2) * 8 +
+           (size_t)(t % 4) * 2;
+}
+
+static size_t col8_off(int t, int d)
+{
+    int b = d / 16;
+    return (size_t)(b / 4) * 1024 + (size_t)(d % 16 + 16 * (t / 4)) * 16 + (size_t)(b % 4) * 4 +
+           (size_t)(t % 4);
 }
 
 static size_t pad_unit(size_t b) { return (b + UNIT - 1) / UNIT * UNIT; }
@@ -391,13 +401,13 @@ static void put_slot(int D, int tier, uint8_t *page, int t, const uint16_t *k, c
             uint16_t kv = k[d];
             if (tier == 3)
                 kv = double_to_bf16(f16_to_double(k[d]));
-            memcpy(page + wide_off(D, t, d), &kv, 2);
+            memcpy(page + row_off(t, d), &kv, 2);
         }
     }
     if (tier == 0 || tier == 1 || tier == 3) {
         size_t base = off_v(D, tier);
         for (int d = 0; d < D; d++)
-            memcpy(page + base + wide_off(D, t, d), &v[d], 2);
+            memcpy(page + base + col_off(t, d), &v[d], 2);
     }
     if (tier == 1) {
         memcpy(page + off_codes(D, 1) + (size_t)t * G, c8, (size_t)G);
@@ -408,7 +418,7 @@ static void put_slot(int D, int tier, uint8_t *page, int t, const uint16_t *k, c
         uint16_t sc;
         quant_v(D, v, q, &sc);
         for (int d = 0; d < D; d++)
-            page[narrow_off(D, t, d)] = (uint8_t)q[d];
+            page[col8_off(t, d)] = (uint8_t)q[d];
         memcpy(page + off_codes(D, 2) + (size_t)t * (G / 2), c4, (size_t)(G / 2));
         memcpy(page + off_radius(D, 2) + (size_t)t * 2, &r, 2);
         memcpy(page + off_vscale(D) + (size_t)t * 2, &sc, 2);
@@ -699,7 +709,7 @@ static void decode_unit(const decode_args *a, int64_t unit)
             if (tier == 0 || tier == 3) {
                 for (int d = 0; d < D; d++) {
                     uint16_t kb;
-                    memcpy(&kb, page + wide_off(D, t, d), 2);
+                    memcpy(&kb, page + row_off(t, d), 2);
                     l += q[d] * (tier == 0 ? f16_to_double(kb) : bf16_to_double(kb));
                 }
                 l *= a->sigma;
@@ -742,11 +752,11 @@ static void decode_unit(const decode_args *a, int64_t unit)
                 memcpy(&sb, page + off_vscale(D) + (size_t)t * 2, 2);
                 double sc = f16_to_double(sb);
                 for (int d = 0; d < D; d++)
-                    v[d] = (double)(int8_t)page[narrow_off(D, t, d)] * sc;
+                    v[d] = (double)(int8_t)page[col8_off(t, d)] * sc;
             } else {
                 for (int d = 0; d < D; d++) {
                     uint16_t vb;
-                    memcpy(&vb, page + off_v(D, tier) + wide_off(D, t, d), 2);
+                    memcpy(&vb, page + off_v(D, tier) + col_off(t, d), 2);
                     v[d] = bf16_to_double(vb);
                 }
             }
@@ -880,5 +890,6 @@ void oracle_quant_v(int D, const uint16_t *v, int8_t *q, uint16_t *scale)
 {
     quant_v(D, v, q, scale);
 }
-size_t oracle_wide_off(int D, int t, int d) { return wide_off(D, t, d); }
-size_t oracle_narrow_off(int D, int t, int d) { return narrow_off(D, t, d); }
+size_t oracle_row_off(int t, int d) { return row_off(t, d); }
+size_t oracle_col_off(int t, int d) { return col_off(t, d); }
+size_t oracle_col8_off(int t, int d) { return col8_off(t, d); }

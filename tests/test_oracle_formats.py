@@ -54,22 +54,28 @@ def test_bf16_round_trip_matches_torch():
 
 
 @pytest.mark.parametrize("D", [64, 128])
-def test_wide_and_narrow_sections_are_lane_chunked_bijections(D):
-    B = D // 8
-    wide = np.array([[oracle.wide_off(D, t, d) for d in range(D)] for t in range(16)])
-    narrow = np.array([[oracle.narrow_off(D, t, d) for d in range(D)] for t in range(16)])
-    assert sorted(wide.ravel()) == list(range(0, 32 * D, 2))
-    assert sorted(narrow.ravel()) == list(range(16 * D))
+def test_row_and_column_sections_are_lane_chunked_bijections(D):
     t, d = np.meshgrid(np.arange(16), np.arange(D), indexing="ij")
-    lane = (t % 8) * 8 + d // B
-    for sec, esz in ((wide, 2), (narrow, 1)):
-        # every element sits in its lane's 16-byte column of a 1 KiB block
-        assert np.array_equal((sec % 1024) // 16, lane)
-        # inside a lane: slot t % 8 first (t < 8), then t + 8; dims ascending
-        w = (sec // 1024) * (16 // esz) + (sec % 16) // esz
-        assert np.array_equal(w, (t // 8) * B + d % B)
-    # spot value: slot 9, dim B + 3 -> lane 9, element B + 3
-    assert wide[9, B + 3] == ((B + 3) // 8) * 1024 + 9 * 16 + ((B + 3) % 8) * 2
+    rows = np.array([[oracle.row_off(a, b) for b in range(D)] for a in range(16)])
+    cols = np.array([[oracle.col_off(a, b) for b in range(D)] for a in range(16)])
+    cols8 = np.array([[oracle.col8_off(a, b) for b in range(D)] for a in range(16)])
+    assert sorted(rows.ravel()) == list(range(0, 32 * D, 2))
+    assert sorted(cols.ravel()) == list(range(0, 32 * D, 2))
+    assert sorted(cols8.ravel()) == list(range(16 * D))
+    blk = d // 16
+    # the lane (16-byte column of a KiB) and the 8-byte half / 4-byte quarter
+    assert np.array_equal((rows % 1024) // 16, t + 16 * ((d % 16) // 4))
+    assert np.array_equal((cols % 1024) // 16, d % 16 + 16 * (t // 4))
+    assert np.array_equal((cols8 % 1024) // 16, d % 16 + 16 * (t // 4))
+    assert np.array_equal(rows // 1024, blk // 2) and np.array_equal(cols // 1024, blk // 2)
+    assert np.array_equal(cols8 // 1024, blk // 4)
+    assert np.array_equal((rows % 16) // 8, blk % 2) and np.array_equal((rows % 8) // 2, d % 4)
+    assert np.array_equal((cols % 16) // 8, blk % 2) and np.array_equal((cols % 8) // 2, t % 4)
+    assert np.array_equal((cols8 % 16) // 4, blk % 4) and np.array_equal(cols8 % 4, t % 4)
+    # spot values: slot 5, dim 22 (block 1)
+    assert oracle.row_off(5, 22) == 0 * 1024 + (5 + 16 * 1) * 16 + 8 + 2 * 2
+    assert oracle.col_off(5, 22) == 0 * 1024 + (6 + 16 * 1) * 16 + 8 + 1 * 2
+    assert oracle.col8_off(5, 22) == 0 * 1024 + (6 + 16 * 1) * 16 + 4 + 1
 
 
 def test_page_sizes():
