@@ -75,6 +75,21 @@ def build_layer(cfg, layer, dev, dense=False):
     return out
 
 
+def time_eager(step_fns, steps, warmup):
+    """Eager launches, events around the whole run."""
+    for i in range(warmup):
+        step_fns[i % len(step_fns)]()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record()
+    for i in range(steps):
+        step_fns[i % len(step_fns)]()
+    e1.record()
+    torch.cuda.synchronize()
+    return steps, time.perf_counter() - t0, e0.elapsed_time(e1) / steps
+
+
 def time_graph(step_fns, steps, warmup):
     """Captures one call of every fn in step_fns into a graph, replays it
     enough times for `steps` steps; returns (steps run, seconds, per-step ms
@@ -177,6 +192,10 @@ def main():
     ap.add_argument("--splits", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
+    ap.add_argument("--eager", action="store_true",
+                    help="time eager launches instead of graph replays (for profilers)")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="run one device-to-device copy of this size first (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: the ADA decode path has no multi-GPU mode "
@@ -188,6 +207,13 @@ def main():
     ada.load()
     cfg = synth.WORKLOADS[args.workload]
     dev = torch.device("cuda:0")
+    if args.copy_probe_mib:
+        src = torch.ones(args.copy_probe_mib << 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"copy probe: {args.copy_probe_mib} MiB device-to-device")
+        del src, dst
     log(f"workload {cfg.number} {cfg.name}: building cache on the GPU")
     L = build_layer(cfg, 0, dev, dense=not args.no_dense)
     geom, cache = L["geom"], L["cache"]
@@ -209,7 +235,8 @@ def main():
     fns = [make_step(v) for v in views]
     log(f"stored {used / 1e6:.2f} MB in {int(cache.num_pages_host.sum())} pages; "
         f"{n_copies} arena copies; {splits} splits per row")
-    steps, wall, ms_graph = time_graph(fns, args.steps, args.warmup)
+    timer = time_eager if args.eager else time_graph
+    steps, wall, ms_graph = timer(fns, args.steps, args.warmup)
     k_med, k_mean = kernel_event_ms(fns, max(50, 2 * n_copies))
     tokens = int(L["lens"].sum())
     value = tokens / (ms_graph / 1e3)
@@ -252,7 +279,7 @@ def main():
         dfns = [(lambda v=dc.view(a): ada.dense_decode(geom, dc, L["q"], cfg.sigma, out, lse,
                                                       num_splits=args.splits, ws=dws, view=v))
                 for a in darenas]
-        _, _, dms = time_graph(dfns, args.steps, args.warmup)
+        _, _, dms = timer(dfns, args.steps, args.warmup)
         result["dense_bf16_baseline"] = {"ms_per_step": dms, "value": tokens / (dms / 1e3),
                                          "stored_bytes": dused,
                                          "achieved_GBs": dused / (dms / 1e3) / 1e9,

@@ -50,16 +50,20 @@ struct DecodeArgs {
     float *out;
     float *lse;
     float *logits;
-    float *part_ml;  // [rows][nsplit][NH][2]  (running max in log2 units, sum)
-    float *part_acc; // [rows][nsplit][NH][D]  (unnormalised output)
-    unsigned *counters; // [rows] splits finished; zero between calls
+    float *lut;        // [rows][G * 272][NH] code tables (coded caches only)
+    uint16_t *qh;      // [rows][NH][D] fp16 queries, scaled per head (coded caches only)
+    float *lsc;        // [rows][NH] softmax scale * 2^e_h * log2(e) (coded caches only)
+    float *part_ml;    // [rows][nsplit][NH][2]  (running max in log2 units, sum)
+    float *part_acc;   // [rows][nsplit][NH][D]  (unnormalised output)
     float sigma;
     int S, Hq, Hkv, maxp, nsplit;
 };
 
+// Enqueues one decode step: the per-row preparation (coded caches), the
+// page stream and, with more than one split, the split merge.
 hipError_t launch_decode(int D, int NH, bool dense, const DecodeArgs &a, hipStream_t st);
 
-// LDS bytes one decode workgroup needs; the device offers 160 KiB.
+// LDS bytes the page-stream workgroup needs; the device offers 160 KiB.
 size_t decode_shmem_bytes(int D, int NH, bool dense, int nsplit, int maxp);
 constexpr size_t kMaxLds = 160 * 1024;
 

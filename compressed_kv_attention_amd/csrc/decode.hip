@@ -9,12 +9,15 @@
 // scale); the per-group dot products are tabulated once per query head
 // (the "LUT") and each coded key costs G table reads.
 //
-// Work decomposition.  One workgroup (8 wave64s, one per CU at D = 128)
-// serves one (sequence, kv-head) row and one of `nsplit` interleaved page
-// subsets of it, for all NH query heads of the GQA group, so every page is
-// read from HBM once.  Wave w of split s takes pages s + (w + 8i) * nsplit,
-// one page (16 slots) at a time, with the next page's eight dwordx4 loads in
-// flight while the current one is computed.
+// Work decomposition.  A step is three kernels.  The preparation kernel
+// tabulates each (sequence, kv-head) row's LUT once, with the query operand
+// of the fp16-key tier, into the workspace.  In the page stream one
+// workgroup (8 wave64s, one per CU at D = 128) serves one row and one of
+// `nsplit` interleaved page subsets of it, for all NH query heads of the
+// GQA group, so every page is read from HBM once; it copies the row's LUT
+// into LDS.  Wave w of split s takes pages s + (w + 8i) * nsplit, one page
+// (16 slots) at a time, with the next two pages' loads in flight while the
+// current one is computed.
 //
 // Per page the wave forms a 16 x 16 tile of logits, rows = query heads
 // (NH used, the rest zero), columns = slots, held the way a 16x16x16 MFMA
@@ -36,9 +39,8 @@
 // (rows = heads, so lanes 0-15 hold the outputs of one dim each).
 //
 // At the end the 8 waves are merged through LDS and the split's partial
-// (m, l, acc) is written; the last split of each row to finish (an atomic
-// counter per row) merges the row's partials into the outputs, so one
-// decode step is one kernel launch.
+// (m, l, acc) is written; the merge kernel combines a row's splits into the
+// outputs (with one split the stream writes them directly).
 #include "ada_internal.h"
 
 #include <type_traits>
@@ -97,15 +99,9 @@ __device__ __forceinline__ float rows_sum(float x)
     return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
-// Device-coherent (agent-scope) accesses to the split partials.
-__device__ __forceinline__ void coherent_store(float *p, float v)
-{
-    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ float coherent_load(const float *p)
-{
-    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
+// s_waitcnt immediate that waits until at most n vector-memory operations
+// are outstanding (expcnt and lgkmcnt left at their maxima).
+constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
 
 template <int NH>
 __device__ __forceinline__ void lut_add(const float *lut, int idx, float (&sum)[NH])
@@ -165,18 +161,21 @@ __device__ __forceinline__ Lane make_lane(int lane)
     return L;
 }
 
-// Raw bytes of one page as this lane sees them: NL 16-byte loads.
-//   tiers 0/3: c[0 .. D/32) key chunks, c[D/32 .. D/16) value chunks
-//   tier 1:    c[0 .. D/32) value chunks; c[4] the lane's code block;
-//              c[5] the 16-byte block of radii holding slots 4r .. 4r+3
-//   tier 2:    c[0 .. D/64) value chunks; c[2] the scale block (as c[5]);
-//              c[4], c[5] as in tier 1
+// Raw bytes of one page as this lane sees them: NL 16-byte loads.  With
+// NV = D / 32 (the chunks of a bf16 value section):
+//   tiers 0/3: c[0 .. NV) value chunks, c[NV .. 2 NV) key chunks
+//   tier 1:    c[0 .. NV) value chunks; c[NV] the lane's code block;
+//              c[NV+1] the 16-byte block of radii holding slots 4r .. 4r+3
+//   tier 2:    c[0 .. NV/2) int8 value chunks; c[NV], c[NV+1] as in tier 1;
+//              c[NV+2] the value-scale block (as the radii)
 // Unused loads repeat chunk 0 (same cache lines, no extra HBM traffic).
 // Every tier issues the same loads with no branch, so the next page's loads
-// stay in flight while the current page is computed.
+// stay in flight while the current page is computed.  The value chunks sit
+// in the same registers for every tier, so one MFMA sequence serves all.
 template <int D>
 struct PageRegs {
-    static constexpr int NL = D == 128 ? 8 : 6;
+    static constexpr int NV = D / 32;
+    static constexpr int NL = 2 * NV > NV + 3 ? 2 * NV : NV + 3;
     u32x4 c[NL];
     int tier, nvalid;
 };
@@ -185,26 +184,27 @@ template <int D, bool DENSE>
 __device__ __forceinline__ void fetch_page(PageRegs<D> &pr, const uint8_t *page, int tier, int nvalid,
                                            const Lane &L)
 {
-    constexpr int NL = PageRegs<D>::NL;
+    constexpr int NL = PageRegs<D>::NL, NV = PageRegs<D>::NV;
     pr.tier = tier;
     pr.nvalid = nvalid;
     const uint32_t lo = L.lane * 16;
     uint32_t o[NL];
 #pragma unroll
     for (int c = 0; c < NL; c++) {
-        const uint32_t dense = c < D / 16 ? lo + c * 1024 : lo;
-        uint32_t t1 = c < D / 32 ? lo + c * 1024 : lo;
-        uint32_t t2 = c < D / 64 ? lo + c * 1024 : lo;
-        if (c == 2)
-            t2 = L.sblk2;
-        if (c == 4) {
+        // tiers 0/3: the value section starts at 32 D, the key section at 0
+        const uint32_t dense = c < NV ? 32 * D + lo + c * 1024 : c < 2 * NV ? lo + (c - NV) * 1024 : lo;
+        uint32_t t1 = c < NV ? lo + c * 1024 : lo;
+        uint32_t t2 = c < NV / 2 ? lo + c * 1024 : lo;
+        if (c == NV) {
             t1 = L.cblk1;
             t2 = L.cblk2;
         }
-        if (c == 5) {
+        if (c == NV + 1) {
             t1 = L.rblk1;
             t2 = L.rblk2;
         }
+        if (c == NV + 2)
+            t2 = L.sblk2;
         o[c] = (DENSE || tier == 0) ? dense : tier == 1 ? t1 : t2;
     }
 #pragma unroll
@@ -249,7 +249,7 @@ __device__ __forceinline__ void key_logits(const PageRegs<D> &cur, const QOperan
     f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = s0;
 #pragma unroll
     for (int b = 0; b < D / 16; b++) {
-        const u32x4 &ch = cur.c[b / 2];
+        const u32x4 &ch = cur.c[PageRegs<D>::NV + b / 2];
         const u32x2 k2 = (b & 1) ? u32x2{ch.z, ch.w} : u32x2{ch.x, ch.y};
         f32x4 &s = (b & 1) ? s1 : s0;
         if constexpr (DENSE)
@@ -267,16 +267,20 @@ template <int D, int NH>
 __device__ __forceinline__ void coded_logits(const PageRegs<D> &cur, const float *lut, const Lane &L,
                                              float sig2, float (&x)[4])
 {
-    constexpr int G = D / 8, GPL = G / 4;
+    constexpr int GPL = D / 32; // groups per lane
+    constexpr int NV = PageRegs<D>::NV;
     const bool t8 = cur.tier == 1;
-    const uint32_t bits = bits_at(cur.c[4], t8 ? L.co1 : L.co2);
+    const uint32_t bits = bits_at(cur.c[NV], t8 ? L.co1 : L.co2);
+    // code field k: 8 bits (tier 1) or 4 bits (tier 2, LUT entries from 256)
+    const uint32_t width = t8 ? 8u : 4u;
+    const int base = t8 ? 0 : kCodes8;
     float s[NH];
 #pragma unroll
     for (int h = 0; h < NH; h++)
         s[h] = 0.f;
 #pragma unroll
     for (int k = 0; k < GPL; k++) {
-        const int code = t8 ? (int)((bits >> (8 * k)) & 255u) : kCodes8 + (int)((bits >> (4 * k)) & 15u);
+        const int code = base + (int)__builtin_amdgcn_ubfe(bits, k * width, width);
         lut_add<NH>(lut, (L.g0 + k) * kLutCodes + code, s);
     }
     // complete each slot's sum over its four lanes (a quad)
@@ -300,7 +304,7 @@ __device__ __forceinline__ void coded_logits(const PageRegs<D> &cur, const float
     v[2] = dpp<0x128>(sel); // row_ror:8  -> lane + 8
     v[3] = dpp<0x124>(sel); // row_ror:4  -> lane + 12
     float rad[4];
-    quad_f16(cur.c[5], L.r, rad);
+    quad_f16(cur.c[NV + 1], L.r, rad);
 #pragma unroll
     for (int e = 0; e < 4; e++)
         x[e] = v[e] * (rad[e] * sig2);
@@ -309,10 +313,16 @@ __device__ __forceinline__ void coded_logits(const PageRegs<D> &cur, const float
 // Logits, online-softmax update and PV product of one page (page index p in
 // its row) for the wave's NH query heads.
 template <int D, int NH, bool DENSE>
-__device__ __forceinline__ void process_page(const PageRegs<D> &cur, int p, WaveState<D, NH> &st,
+__device__ __forceinline__ void process_page(PageRegs<D> &cur, int p, WaveState<D, NH> &st,
                                              const float *lut, const QOperand<D, DENSE> &qo, float lsc,
                                              float sig2, float *lgout, int maxp, const Lane &L)
 {
+    // This page's loads were issued before the next two pages' loads: wait
+    // until at most those 2 NL are outstanding.  Every register of this page
+    // is then complete on every path, including chunks a tier never reads,
+    // so the wait-count pass needs no full drain where they are reused.
+    constexpr int NL = PageRegs<D>::NL;
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * NL));
     const int tier = cur.tier;
     float x[4];
     if (DENSE || tier == 0)
@@ -356,13 +366,35 @@ __device__ __forceinline__ void process_page(const PageRegs<D> &cur, int p, Wave
         w[e] = __builtin_amdgcn_exp2f(x[e] - st.mlane);
     st.l += (w[0] + w[1]) + (w[2] + w[3]);
 
+    constexpr int NV = PageRegs<D>::NV;
     const bool int8v = !DENSE && tier == 2;
     if (int8v) {
         float sc[4];
-        quad_f16(cur.c[2], L.r, sc);
+        quad_f16(cur.c[NV + 2], L.r, sc);
 #pragma unroll
         for (int e = 0; e < 4; e++)
             w[e] *= sc[e];
+        // int8 values -> bf16 (exact), into the registers the bf16 tiers
+        // use: block b is dword b % 4 of int8 chunk b / 4, and becomes
+        // half b % 2 of chunk b / 2
+        u32x4 cv[NV];
+#pragma unroll
+        for (int b = 0; b < D / 16; b++) {
+            const u32x4 &ch = cur.c[b / 4];
+            const uint32_t q = (b % 4 == 0) ? ch.x : (b % 4 == 1) ? ch.y : (b % 4 == 2) ? ch.z : ch.w;
+            const uint32_t v01 = pack_bf16((float)(signed char)(q & 255u), (float)(signed char)((q >> 8) & 255u));
+            const uint32_t v23 = pack_bf16((float)(signed char)((q >> 16) & 255u), (float)(signed char)(q >> 24));
+            if (b & 1) {
+                cv[b / 2].z = v01;
+                cv[b / 2].w = v23;
+            } else {
+                cv[b / 2].x = v01;
+                cv[b / 2].y = v23;
+            }
+        }
+#pragma unroll
+        for (int c = 0; c < NV; c++)
+            cur.c[c] = cv[c];
     }
     // weights as bf16 hi + lo (A operands)
     const uint32_t h01 = pack_bf16(w[0], w[1]), h23 = pack_bf16(w[2], w[3]);
@@ -370,45 +402,17 @@ __device__ __forceinline__ void process_page(const PageRegs<D> &cur, int p, Wave
     const uint32_t l23 = pack_bf16(w[2] - bf16_lo(h23), w[3] - bf16_hi(h23));
     const s16x4 ahi = __builtin_bit_cast(s16x4, u32x2{h01, h23});
     const s16x4 alo = __builtin_bit_cast(s16x4, u32x2{l01, l23});
-
-    if (int8v) {
-        // value block b: dword b % 4 of chunk b / 4, one int8 per slot
 #pragma unroll
-        for (int b = 0; b < D / 16; b++) {
-            const u32x4 &ch = cur.c[b / 4];
-            const uint32_t q = (b % 4 == 0) ? ch.x : (b % 4 == 1) ? ch.y : (b % 4 == 2) ? ch.z : ch.w;
-            const uint32_t v01 = pack_bf16((float)(signed char)(q & 255u), (float)(signed char)((q >> 8) & 255u));
-            const uint32_t v23 = pack_bf16((float)(signed char)((q >> 16) & 255u), (float)(signed char)(q >> 24));
-            const s16x4 bv = __builtin_bit_cast(s16x4, u32x2{v01, v23});
-            st.acc[b] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ahi, bv, st.acc[b], 0, 0, 0);
-            st.acc[b] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(alo, bv, st.acc[b], 0, 0, 0);
-        }
-    } else if (DENSE || tier == 0) {
+    for (int b = 0; b < D / 16; b++) {
+        const u32x4 &ch = cur.c[b / 2];
+        const s16x4 bv = __builtin_bit_cast(s16x4, (b & 1) ? u32x2{ch.z, ch.w} : u32x2{ch.x, ch.y});
+        st.acc[b] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ahi, bv, st.acc[b], 0, 0, 0);
+    }
 #pragma unroll
-        for (int b = 0; b < D / 16; b++) {
-            const u32x4 &ch = cur.c[D / 32 + b / 2];
-            const s16x4 bv = __builtin_bit_cast(s16x4, (b & 1) ? u32x2{ch.z, ch.w} : u32x2{ch.x, ch.y});
-            st.acc[b] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ahi, bv, st.acc[b], 0, 0, 0);
-        }
-#pragma unroll
-        for (int b = 0; b < D / 16; b++) {
-            const u32x4 &ch = cur.c[D / 32 + b / 2];
-            const s16x4 bv = __builtin_bit_cast(s16x4, (b & 1) ? u32x2{ch.z, ch.w} : u32x2{ch.x, ch.y});
-            st.acc[b] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(alo, bv, st.acc[b], 0, 0, 0);
-        }
-    } else {
-#pragma unroll
-        for (int b = 0; b < D / 16; b++) {
-            const u32x4 &ch = cur.c[b / 2];
-            const s16x4 bv = __builtin_bit_cast(s16x4, (b & 1) ? u32x2{ch.z, ch.w} : u32x2{ch.x, ch.y});
-            st.acc[b] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ahi, bv, st.acc[b], 0, 0, 0);
-        }
-#pragma unroll
-        for (int b = 0; b < D / 16; b++) {
-            const u32x4 &ch = cur.c[b / 2];
-            const s16x4 bv = __builtin_bit_cast(s16x4, (b & 1) ? u32x2{ch.z, ch.w} : u32x2{ch.x, ch.y});
-            st.acc[b] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(alo, bv, st.acc[b], 0, 0, 0);
-        }
+    for (int b = 0; b < D / 16; b++) {
+        const u32x4 &ch = cur.c[b / 2];
+        const s16x4 bv = __builtin_bit_cast(s16x4, (b & 1) ? u32x2{ch.z, ch.w} : u32x2{ch.x, ch.y});
+        st.acc[b] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(alo, bv, st.acc[b], 0, 0, 0);
     }
 }
 
@@ -422,6 +426,83 @@ __device__ __forceinline__ void fetch_entry(PageRegs<D> &pr, uint2 e, const uint
     fetch_page<D, DENSE>(pr, arena + (size_t)off * kUnit, meta & 3, ((meta >> 2) & 15) + 1, L);
 }
 
+// ---- per-row preparation (coded caches) ----------------------------------
+// Grid (rows, G + 1), 256 threads.  Block (row, g < G) tabulates
+// LUT[g][c][h] = q_h[8g .. 8g+8) . C[g][c] for the row's NH query heads
+// (c < 256 from cb8, else cb4); block (row, G) writes the fp16 key-tier
+// query operand: each head's q scaled by 2^-e_h so its largest |q| lies in
+// [2^14, 2^15) (exact for bf16 values within 2^-28 of that maximum), and
+// the matching logit scale softmax_scale * 2^e_h * log2(e).
+constexpr int kPrepThreads = 256;
+
+template <int D, int NH>
+__global__ __launch_bounds__(kPrepThreads) void decode_prep(DecodeArgs a)
+{
+    constexpr int G = D / 8;
+    const int row = blockIdx.x, g = blockIdx.y, tid = threadIdx.x;
+    const int s = row / a.Hkv, hkv = row % a.Hkv;
+    const uint16_t *qg = a.q + ((size_t)s * a.Hq + (size_t)hkv * NH) * D;
+    if (g < G) {
+        float qq[NH][8];
+#pragma unroll
+        for (int h = 0; h < NH; h++)
+#pragma unroll
+            for (int i = 0; i < 8; i++)
+                qq[h][i] = __uint_as_float((uint32_t)qg[h * D + 8 * g + i] << 16);
+        const float *cb8 = a.cb8 + ((size_t)hkv * G + g) * kCodes8 * 8;
+        const float *cb4 = a.cb4 + ((size_t)hkv * G + g) * kCodes4 * 8;
+        float *dst = a.lut + ((size_t)row * G + g) * kLutCodes * NH;
+        for (int c = tid; c < kLutCodes; c += kPrepThreads) {
+            const float *w = c < kCodes8 ? cb8 + c * 8 : cb4 + (c - kCodes8) * 8;
+            const float4 w0 = *reinterpret_cast<const float4 *>(w);
+            const float4 w1 = *reinterpret_cast<const float4 *>(w + 4);
+            float o[NH];
+#pragma unroll
+            for (int h = 0; h < NH; h++) {
+                float acc = qq[h][0] * w0.x;
+                acc = fmaf(qq[h][1], w0.y, acc);
+                acc = fmaf(qq[h][2], w0.z, acc);
+                acc = fmaf(qq[h][3], w0.w, acc);
+                acc = fmaf(qq[h][4], w1.x, acc);
+                acc = fmaf(qq[h][5], w1.y, acc);
+                acc = fmaf(qq[h][6], w1.z, acc);
+                acc = fmaf(qq[h][7], w1.w, acc);
+                o[h] = acc;
+            }
+            if constexpr (NH == 4)
+                *reinterpret_cast<float4 *>(dst + c * NH) = make_float4(o[0], o[1], o[2], o[3]);
+            else if constexpr (NH == 2)
+                *reinterpret_cast<float2 *>(dst + c * NH) = make_float2(o[0], o[1]);
+            else
+                dst[c] = o[0];
+        }
+        return;
+    }
+    __shared__ int smax[NH];
+    if (tid < NH)
+        smax[tid] = 0;
+    __syncthreads();
+    for (int i = tid; i < NH * D; i += kPrepThreads) {
+        const float v = fabsf(__uint_as_float((uint32_t)qg[i] << 16));
+        atomicMax(&smax[i / D], __float_as_int(v)); // non-negative floats order as integers
+    }
+    __syncthreads();
+    for (int i = tid; i < NH * D; i += kPrepThreads) {
+        const int h = i / D;
+        const float mx = __int_as_float(smax[h]);
+        int e = 0;
+        if (mx > 0.f) {
+            frexpf(mx, &e);
+            e -= 15;
+        }
+        const float v = __uint_as_float((uint32_t)qg[i] << 16);
+        a.qh[(size_t)row * NH * D + i] = __builtin_bit_cast(uint16_t, (_Float16)ldexpf(v, -e));
+        if (i % D == 0)
+            a.lsc[(size_t)row * NH + h] = ldexpf(a.sigma, e) * kLog2e;
+    }
+}
+
+// ---- page stream ------------------------------------------------------------
 template <int D, int NH, bool DENSE>
 __global__ __launch_bounds__(kThreads) void decode_main(DecodeArgs a)
 {
@@ -430,8 +511,7 @@ __global__ __launch_bounds__(kThreads) void decode_main(DecodeArgs a)
 
     extern __shared__ float smem[];
     float *lut = smem;
-    float *qs = smem + LUT_FLOATS;                           // [NH][D] fp32 queries
-    uint2 *tbl = reinterpret_cast<uint2 *>(qs + NH * D);     // [n_wg] page-table entries
+    uint2 *tbl = reinterpret_cast<uint2 *>(smem + LUT_FLOATS); // [n_wg] page-table entries
 
     // Consecutive logical blocks share an XCD (blocks are dealt round-robin
     // over the 8 XCDs), so one row's splits hit one L2.
@@ -441,7 +521,9 @@ __global__ __launch_bounds__(kThreads) void decode_main(DecodeArgs a)
         logical = (blockIdx.x % 8) * (nblk / 8) + blockIdx.x / 8;
     const int row = logical / a.nsplit, split = logical % a.nsplit;
     const int s = row / a.Hkv, hkv = row % a.Hkv;
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    // the wave index is wave-uniform; say so, so the page loop is scalar
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const Lane L = make_lane<D, NH>(lane);
 
     // This workgroup's pages are p_k = split + k * nsplit, k < n_wg; wave w
@@ -450,127 +532,56 @@ __global__ __launch_bounds__(kThreads) void decode_main(DecodeArgs a)
     const int np = a.num_pages[row];
     const int n_wg = split < np ? (np - split + a.nsplit - 1) / a.nsplit : 0;
     const int n_mine = wave < n_wg ? (n_wg - wave + kWaves - 1) / kWaves : 0;
+    const int last = n_mine - 1;
+    const uint32_t *pt = a.page_table + (size_t)row * a.maxp;
+    const uint8_t *pm = a.page_meta + (size_t)row * a.maxp;
+    // the wave's first two pages, straight from the table: their loads
+    // overlap the table staging and the LUT copy
+    PageRegs<D> bufA, bufB, bufC;
+    if (n_mine > 0) {
+        const int p0 = split + wave * a.nsplit, p1 = split + (wave + kWaves * min(1, last)) * a.nsplit;
+        fetch_entry<D, DENSE>(bufA, make_uint2(pt[p0], pm[p0]), a.arena, L);
+        fetch_entry<D, DENSE>(bufB, make_uint2(pt[p1], pm[p1]), a.arena, L);
+    }
     {
-        const uint32_t *pt = a.page_table + (size_t)row * a.maxp;
-        const uint8_t *pm = a.page_meta + (size_t)row * a.maxp;
         for (int k = tid; k < n_wg; k += kThreads) {
             const int p = split + k * a.nsplit;
             tbl[k] = make_uint2(pt[p], pm[p]);
         }
     }
-    const uint16_t *qg = a.q + ((size_t)s * a.Hq + (size_t)hkv * NH) * D;
-    for (int i = tid; i < NH * D; i += kThreads)
-        qs[i] = __uint_as_float((uint32_t)qg[i] << 16);
-    __syncthreads();
-
-    // the first page's loads overlap the code-table build
-    PageRegs<D> bufA, bufB;
-    if (n_mine > 0)
-        fetch_entry<D, DENSE>(bufA, tbl[wave], a.arena, L);
-
+    // the row's code tables, all loads in flight at once
     if constexpr (!DENSE) {
-        // LUT[g][c][h] = q_h[8g .. 8g+8) . C[g][c]; c < 256 from cb8, else
-        // cb4.  TPG threads share group g (its query slices in registers);
-        // consecutive threads take consecutive codewords, and all of a
-        // thread's codeword loads are issued before any is used.
-        constexpr int TPG = kThreads / G;
-        constexpr int NC = (kLutCodes + TPG - 1) / TPG;
-        const int g = tid / TPG, c0 = tid % TPG;
-        const float *cb8 = a.cb8 + ((size_t)hkv * G + g) * kCodes8 * 8;
-        const float *cb4 = a.cb4 + ((size_t)hkv * G + g) * kCodes4 * 8;
-        float4 w0[NC], w1[NC];
+        constexpr int N4 = LUT_FLOATS / 4;
+        constexpr int PER = (N4 + kThreads - 1) / kThreads;
+        const float4 *src = reinterpret_cast<const float4 *>(a.lut + (size_t)row * LUT_FLOATS);
+        float4 t[PER];
 #pragma unroll
-        for (int k = 0; k < NC; k++) {
-            const int c = min(c0 + k * TPG, kLutCodes - 1);
-            const float *w = c < kCodes8 ? cb8 + c * 8 : cb4 + (c - kCodes8) * 8;
-            w0[k] = *reinterpret_cast<const float4 *>(w);
-            w1[k] = *reinterpret_cast<const float4 *>(w + 4);
-        }
-        float qq[NH][8];
+        for (int k = 0; k < PER; k++)
+            t[k] = src[min(tid + k * kThreads, N4 - 1)];
 #pragma unroll
-        for (int h = 0; h < NH; h++) {
-            const float4 a0 = *reinterpret_cast<const float4 *>(qs + h * D + 8 * g);
-            const float4 a1 = *reinterpret_cast<const float4 *>(qs + h * D + 8 * g + 4);
-            qq[h][0] = a0.x; qq[h][1] = a0.y; qq[h][2] = a0.z; qq[h][3] = a0.w;
-            qq[h][4] = a1.x; qq[h][5] = a1.y; qq[h][6] = a1.z; qq[h][7] = a1.w;
-        }
-#pragma unroll
-        for (int k = 0; k < NC; k++) {
-            const int c = c0 + k * TPG;
-            if (c < kLutCodes) {
-                float o[NH];
-#pragma unroll
-                for (int h = 0; h < NH; h++) {
-                    float acc = qq[h][0] * w0[k].x;
-                    acc = fmaf(qq[h][1], w0[k].y, acc);
-                    acc = fmaf(qq[h][2], w0[k].z, acc);
-                    acc = fmaf(qq[h][3], w0[k].w, acc);
-                    acc = fmaf(qq[h][4], w1[k].x, acc);
-                    acc = fmaf(qq[h][5], w1[k].y, acc);
-                    acc = fmaf(qq[h][6], w1[k].z, acc);
-                    acc = fmaf(qq[h][7], w1[k].w, acc);
-                    o[h] = acc;
-                }
-                float *dst = lut + (g * kLutCodes + c) * NH;
-                if constexpr (NH == 4)
-                    *reinterpret_cast<float4 *>(dst) = make_float4(o[0], o[1], o[2], o[3]);
-                else if constexpr (NH == 2)
-                    *reinterpret_cast<float2 *>(dst) = make_float2(o[0], o[1]);
-                else
-                    dst[0] = o[0];
-            }
-        }
+        for (int k = 0; k < PER; k++)
+            if (tid + k * kThreads < N4)
+                reinterpret_cast<float4 *>(lut)[tid + k * kThreads] = t[k];
     }
-
-    // Query operand of the key MFMA.  fp16 keys: each head's q scaled by
-    // 2^-e_h so its largest |q| lies in [2^14, 2^15) (exact for bf16 values
-    // within 2^-28 of that maximum); bf16 keys: q as is (exact).
+    // Query operand of the key MFMA: lane h + 16 r takes dims 16 b + 4 r ..
+    // +3 of head h (zero for h >= NH): the scaled fp16 query of the
+    // preparation kernel, or the bf16 query itself for bf16 keys.
     QOperand<D, DENSE> qo;
-    float lsc; // softmax scale (times 2^e_h for fp16 keys) in log2 units, this lane's head
-    {
-        int eh = 0;
-        if constexpr (!DENSE) {
+    float lsc = a.sigma * kLog2e;
 #pragma unroll
-            for (int h = 0; h < NH; h++) {
-                float mx = 0.f;
-                for (int d = lane; d < D; d += 64)
-                    mx = fmaxf(mx, fabsf(qs[h * D + d]));
-#pragma unroll
-                for (int o = 32; o >= 1; o >>= 1)
-                    mx = fmaxf(mx, __shfl_xor(mx, o, 64));
-                int ex = 0;
-                if (mx > 0.f) {
-                    frexpf(mx, &ex);
-                    ex -= 15;
-                }
-                eh = L.hl == h ? ex : eh;
-            }
+    for (int b = 0; b < D / 16; b++) {
+        u32x2 v = {0u, 0u};
+        if (L.hl < NH) {
+            const uint16_t *src = DENSE ? a.q + ((size_t)s * a.Hq + (size_t)hkv * NH + L.hl) * D
+                                        : a.qh + ((size_t)row * NH + L.hl) * D;
+            v = *reinterpret_cast<const u32x2 *>(src + 16 * b + 4 * L.r);
         }
-        lsc = ldexpf(a.sigma, eh) * kLog2e;
-        const int qq = L.r; // dims 4 q .. 4 q + 3 of each block
-#pragma unroll
-        for (int b = 0; b < D / 16; b++) {
-            float v[4] = {0.f, 0.f, 0.f, 0.f};
-            if (L.hl < NH) {
-                const float4 t = *reinterpret_cast<const float4 *>(qs + L.hl * D + 16 * b + 4 * qq);
-                v[0] = t.x; v[1] = t.y; v[2] = t.z; v[3] = t.w;
-            }
-            if constexpr (DENSE) {
-                s16x4 o;
-#pragma unroll
-                for (int e = 0; e < 4; e++)
-                    o[e] = (short)(__float_as_uint(v[e]) >> 16);
-                qo.blk[b] = o;
-            } else {
-                f16x4 o;
-#pragma unroll
-                for (int e = 0; e < 4; e++)
-                    o[e] = (_Float16)ldexpf(v[e], -eh);
-                qo.blk[b] = o;
-            }
-        }
+        qo.blk[b] = __builtin_bit_cast(typename QOperand<D, DENSE>::T, v);
     }
+    if (!DENSE && L.hl < NH)
+        lsc = a.lsc[(size_t)row * NH + L.hl];
     const float sig2 = a.sigma * kLog2e;
+
     __syncthreads();
 
     WaveState<D, NH> st;
@@ -585,17 +596,30 @@ __global__ __launch_bounds__(kThreads) void decode_main(DecodeArgs a)
     float *lgout = a.logits ? a.logits + ((size_t)s * a.Hq + (size_t)hkv * NH) * a.maxp * kSlots
                             : nullptr;
 
-    // Two register buffers in turn: page i+1's loads are in flight while
-    // page i is computed.  Every half-step issues its loads (past the end it
-    // reloads the last page), so the wait counts are fixed.
-    const int last = n_mine - 1;
-    for (int i = 0; i < n_mine; i += 2) {
-        fetch_entry<D, DENSE>(bufB, tbl[wave + kWaves * min(i + 1, last)], a.arena, L);
+    // Three register buffers in turn: pages i+1 and i+2 are in flight while
+    // page i is computed.  Pages go in threes through a loop with one exit;
+    // every step issues one page's loads (past the end it reloads the last
+    // page), so the wait counts are fixed.  On exit bufA holds page i and
+    // bufB page i+1.
+    int i = 0;
+    for (; i + 2 < n_mine; i += 3) {
+        fetch_entry<D, DENSE>(bufC, tbl[wave + kWaves * (i + 2)], a.arena, L);
         process_page<D, NH, DENSE>(bufA, split + (wave + kWaves * i) * a.nsplit, st, lut, qo, lsc, sig2,
                                    lgout, a.maxp, L);
-        if (i + 1 >= n_mine)
-            break;
-        fetch_entry<D, DENSE>(bufA, tbl[wave + kWaves * min(i + 2, last)], a.arena, L);
+        fetch_entry<D, DENSE>(bufA, tbl[wave + kWaves * min(i + 3, last)], a.arena, L);
+        process_page<D, NH, DENSE>(bufB, split + (wave + kWaves * (i + 1)) * a.nsplit, st, lut, qo, lsc,
+                                   sig2, lgout, a.maxp, L);
+        fetch_entry<D, DENSE>(bufB, tbl[wave + kWaves * min(i + 4, last)], a.arena, L);
+        process_page<D, NH, DENSE>(bufC, split + (wave + kWaves * (i + 2)) * a.nsplit, st, lut, qo, lsc,
+                                   sig2, lgout, a.maxp, L);
+    }
+    if (i < n_mine) {
+        fetch_entry<D, DENSE>(bufC, tbl[wave + kWaves * last], a.arena, L); // keeps the wait count
+        process_page<D, NH, DENSE>(bufA, split + (wave + kWaves * i) * a.nsplit, st, lut, qo, lsc, sig2,
+                                   lgout, a.maxp, L);
+    }
+    if (i + 1 < n_mine) {
+        fetch_entry<D, DENSE>(bufA, tbl[wave + kWaves * last], a.arena, L);
         process_page<D, NH, DENSE>(bufB, split + (wave + kWaves * (i + 1)) * a.nsplit, st, lut, qo, lsc,
                                    sig2, lgout, a.maxp, L);
     }
@@ -617,10 +641,11 @@ __global__ __launch_bounds__(kThreads) void decode_main(DecodeArgs a)
     }
     __syncthreads();
 
-    // Merge the waves into this split's (m, l, acc).
+    // Merge the waves into this split's (m, l, acc), or into the outputs
+    // when the row has one split.
     const size_t part = (size_t)row * a.nsplit + split;
-    for (int i = tid; i < NH * D; i += kThreads) {
-        const int h = i / D, d = i - h * D;
+    for (int i2 = tid; i2 < NH * D; i2 += kThreads) {
+        const int h = i2 / D, d = i2 - h * D;
         float mx = -INFINITY;
 #pragma unroll
         for (int w = 0; w < kWaves; w++)
@@ -633,56 +658,49 @@ __global__ __launch_bounds__(kThreads) void decode_main(DecodeArgs a)
             o = fmaf(red[((size_t)w * D + d) * 4 + h], f, o);
             l = fmaf(redml[(w * NH + h) * 2 + 1], f, l);
         }
-        const size_t sh = (size_t)s * a.Hq + (size_t)hkv * NH + h;
         if (a.nsplit == 1) {
+            const size_t sh = (size_t)s * a.Hq + (size_t)hkv * NH + h;
             a.out[sh * D + d] = mx > -INFINITY ? o / l : 0.f;
             if (a.lse != nullptr && d == 0)
                 a.lse[sh] = mx > -INFINITY ? (mx + __log2f(l)) * kLn2 : -INFINITY;
             continue;
         }
-        coherent_store(a.part_acc + (part * NH + h) * D + d, o);
+        a.part_acc[(part * NH + h) * D + d] = o;
         if (d == 0) {
-            coherent_store(a.part_ml + (part * NH + h) * 2, mx);
-            coherent_store(a.part_ml + (part * NH + h) * 2 + 1, l);
+            a.part_ml[(part * NH + h) * 2] = mx;
+            a.part_ml[(part * NH + h) * 2 + 1] = l;
         }
     }
-    if (a.nsplit == 1)
-        return;
+}
 
-    // The last split of a row to finish merges all of them:
-    // out = sum_i acc_i 2^(m_i - m) / sum_i l_i 2^(m_i - m), lse in nats.
-    // Partials move through device-coherent accesses (agent-scope atomic
-    // stores and loads, which bypass the per-XCD L2), so the hand-off needs
-    // only the stores to have completed before the counter moves -- no L2
-    // write-back or invalidate.  The counter is reset for the next call.
-    __shared__ int is_last;
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    if (tid == 0) {
-        const unsigned prev = __hip_atomic_fetch_add(a.counters + row, 1u, __ATOMIC_RELAXED,
-                                                     __HIP_MEMORY_SCOPE_AGENT);
-        is_last = prev == (unsigned)a.nsplit - 1;
-    }
-    __syncthreads();
-    if (!is_last)
-        return;
+// ---- split merge --------------------------------------------------------------
+// One workgroup per row: out = sum_i acc_i 2^(m_i - m) / sum_i l_i 2^(m_i - m)
+// over the row's splits, lse = (m + log2 of the denominator) in nats.  The
+// partials come from the page-stream kernel before it in the stream.
+constexpr int kMergeThreads = 256;
 
-    // LDS: per (split, head) m, l and the weight f = 2^(m - m*); per head
-    // m*, l*; then [KS][NH][D] partial column sums.
+template <int D, int NH>
+__global__ __launch_bounds__(kMergeThreads) void decode_merge(DecodeArgs a)
+{
+    extern __shared__ float smem[];
+    const int row = blockIdx.x, tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int s = row / a.Hkv, hkv = row % a.Hkv;
     const int ns = a.nsplit;
+    constexpr int ITEMS = NH * D / 4;            // (head, 4 dims) items
+    constexpr int KS = kMergeThreads / ITEMS;    // threads per item
     float *sm = smem;           // [ns][NH]
-    float *sf = sm + ns * NH;   // [ns][NH]
+    float *sf = sm + ns * NH;   // [ns][NH] weights 2^(m_i - m*)
     float *sl = sf + ns * NH;   // [ns][NH]
     float *smax = sl + ns * NH; // [NH]
     float *ssum = smax + NH;    // [NH]
     float *scol = ssum + NH;    // [KS][NH][D]
     const size_t base = (size_t)row * ns * NH;
-    for (int i = tid; i < ns * NH; i += kThreads) {
-        sm[i] = coherent_load(a.part_ml + (base + i) * 2);
-        sl[i] = coherent_load(a.part_ml + (base + i) * 2 + 1);
+    for (int i = tid; i < ns * NH; i += kMergeThreads) {
+        const float2 ml = *reinterpret_cast<const float2 *>(a.part_ml + (base + i) * 2);
+        sm[i] = ml.x;
+        sl[i] = ml.y;
     }
     __syncthreads();
-    // wave h < NH: m* and l* of head h
     if (wave < NH) {
         const int h = wave;
         float mx = -INFINITY;
@@ -707,42 +725,32 @@ __global__ __launch_bounds__(kThreads) void decode_main(DecodeArgs a)
         }
     }
     __syncthreads();
-    // columns: item = (h, 4 dims); KS threads share an item, each summing
-    // every KS-th split, with many loads in flight
-    constexpr int ITEMS = NH * D / 4;
-    constexpr int KS = kThreads / ITEMS;
     {
+        // KS threads share an item, each summing every KS-th split, 8 splits
+        // per batch with all loads in flight
         const int item = tid % ITEMS, part_i = tid / ITEMS;
         const int h = item / (D / 4), d4 = item % (D / 4);
         float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
-        if (part_i < KS) {
-            const float *src = a.part_acc + (base + h) * D + 4 * d4;
-            // batches of 16 splits: all loads of a batch are in flight at once
-            for (int k0 = part_i; k0 < ns; k0 += 16 * KS) {
-                float v[16][4];
+        const float *src = a.part_acc + (base + h) * D + 4 * d4;
+        for (int k0 = part_i; k0 < ns; k0 += 8 * KS) {
+            float4 v[8];
 #pragma unroll
-                for (int j = 0; j < 16; j++) {
-                    const int k = min(k0 + j * KS, ns - 1);
-                    const float *pv = src + (size_t)k * NH * D;
+            for (int j = 0; j < 8; j++)
+                v[j] = *reinterpret_cast<const float4 *>(src + (size_t)min(k0 + j * KS, ns - 1) * NH * D);
 #pragma unroll
-                    for (int e = 0; e < 4; e++)
-                        v[j][e] = coherent_load(pv + e);
-                }
-#pragma unroll
-                for (int j = 0; j < 16; j++) {
-                    const int k = k0 + j * KS;
-                    const float f = k < ns ? sf[k * NH + h] : 0.f;
-                    o.x = fmaf(v[j][0], f, o.x);
-                    o.y = fmaf(v[j][1], f, o.y);
-                    o.z = fmaf(v[j][2], f, o.z);
-                    o.w = fmaf(v[j][3], f, o.w);
-                }
+            for (int j = 0; j < 8; j++) {
+                const int k = k0 + j * KS;
+                const float f = k < ns ? sf[k * NH + h] : 0.f;
+                o.x = fmaf(v[j].x, f, o.x);
+                o.y = fmaf(v[j].y, f, o.y);
+                o.z = fmaf(v[j].z, f, o.z);
+                o.w = fmaf(v[j].w, f, o.w);
             }
-            *reinterpret_cast<float4 *>(scol + ((size_t)part_i * NH + h) * D + 4 * d4) = o;
         }
+        *reinterpret_cast<float4 *>(scol + ((size_t)part_i * NH + h) * D + 4 * d4) = o;
     }
     __syncthreads();
-    for (int i = tid; i < NH * D; i += kThreads) {
+    for (int i = tid; i < NH * D; i += kMergeThreads) {
         const int h = i / D, d = i - h * D;
         float o = 0.f;
 #pragma unroll
@@ -754,27 +762,31 @@ __global__ __launch_bounds__(kThreads) void decode_main(DecodeArgs a)
         if (a.lse != nullptr && d == 0)
             a.lse[sh] = mx > -INFINITY ? (mx + __log2f(l)) * kLn2 : -INFINITY;
     }
-    if (tid == 0)
-        __hip_atomic_store(a.counters + row, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 template <int D, int NH, bool DENSE>
-size_t shmem_bytes(int nsplit, int max_wg_pages)
+size_t shmem_bytes(int max_wg_pages)
 {
     const size_t lut = DENSE ? 0 : (size_t)(D / 8) * kLutCodes * NH * sizeof(float);
-    size_t b = lut + (size_t)NH * D * sizeof(float) + (size_t)max_wg_pages * sizeof(uint2);
+    const size_t b = lut + (size_t)max_wg_pages * sizeof(uint2);
     const size_t red = ((size_t)kWaves * D * 4 + (size_t)kWaves * NH * 2) * sizeof(float);
-    constexpr int KS = kThreads / (NH * D / 4);
-    const size_t merge = ((size_t)3 * nsplit * NH + 2 * NH + (size_t)KS * NH * D) * sizeof(float);
-    b = b > red ? b : red;
-    return b > merge ? b : merge;
+    return b > red ? b : red;
+}
+
+template <int D, int NH>
+size_t merge_shmem_bytes(int nsplit)
+{
+    constexpr int KS = kMergeThreads / (NH * D / 4);
+    return ((size_t)3 * nsplit * NH + 2 * NH + (size_t)KS * NH * D) * sizeof(float);
 }
 
 template <int D, int NH, bool DENSE>
 hipError_t launch_t(const DecodeArgs &a, hipStream_t st)
 {
     const int rows = a.S * a.Hkv;
-    const size_t shmem = shmem_bytes<D, NH, DENSE>(a.nsplit, (a.maxp + a.nsplit - 1) / a.nsplit);
+    if (rows <= 0 || a.nsplit <= 0)
+        return hipSuccess;
+    const size_t shmem = shmem_bytes<D, NH, DENSE>((a.maxp + a.nsplit - 1) / a.nsplit);
     static size_t attr_set = 0;
     if (shmem > attr_set) {
         hipError_t e = hipFuncSetAttribute((const void *)decode_main<D, NH, DENSE>,
@@ -783,11 +795,27 @@ hipError_t launch_t(const DecodeArgs &a, hipStream_t st)
             return e;
         attr_set = shmem;
     }
-    if (rows > 0 && a.nsplit > 0) {
-        hipLaunchKernelGGL((decode_main<D, NH, DENSE>), dim3(rows * a.nsplit), dim3(kThreads), shmem, st, a);
-        return hipGetLastError();
+    if constexpr (!DENSE) {
+        hipLaunchKernelGGL((decode_prep<D, NH>), dim3(rows, D / 8 + 1), dim3(kPrepThreads), 0, st, a);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess)
+            return e;
     }
-    return hipSuccess;
+    hipLaunchKernelGGL((decode_main<D, NH, DENSE>), dim3(rows * a.nsplit), dim3(kThreads), shmem, st, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || a.nsplit == 1)
+        return e;
+    const size_t mshmem = merge_shmem_bytes<D, NH>(a.nsplit);
+    static size_t mattr_set = 0;
+    if (mshmem > mattr_set) {
+        e = hipFuncSetAttribute((const void *)decode_merge<D, NH>,
+                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)mshmem);
+        if (e != hipSuccess)
+            return e;
+        mattr_set = mshmem;
+    }
+    hipLaunchKernelGGL((decode_merge<D, NH>), dim3(rows), dim3(kMergeThreads), mshmem, st, a);
+    return hipGetLastError();
 }
 
 } // namespace
@@ -796,8 +824,11 @@ size_t decode_shmem_bytes(int D, int NH, bool dense, int nsplit, int maxp)
 {
     const int wg = (maxp + nsplit - 1) / nsplit;
 #define ADA_CASE(DD, NN)                                                                          \
-    if (D == DD && NH == NN)                                                                      \
-        return dense ? shmem_bytes<DD, NN, true>(nsplit, wg) : shmem_bytes<DD, NN, false>(nsplit, wg);
+    if (D == DD && NH == NN) {                                                                    \
+        const size_t m = merge_shmem_bytes<DD, NN>(nsplit);                                       \
+        const size_t k = dense ? shmem_bytes<DD, NN, true>(wg) : shmem_bytes<DD, NN, false>(wg);  \
+        return k > m ? k : m;                                                                     \
+    }
     ADA_CASE(64, 1)
     ADA_CASE(64, 2)
     ADA_CASE(64, 4)

@@ -188,7 +188,8 @@ int32_t ada_decode_default_splits(const ada_geom *geom, int32_t num_seqs,
                                   int32_t max_pages_per_head);
 
 /* Workspace bytes of ada_decode / dense_decode with this many splits
- * (0 = the default).  The workspace holds per-split partial results. */
+ * (0 = the default).  The workspace holds each row's code tables and scaled
+ * query, and the per-split partial results. */
 size_t ada_decode_workspace_size(const ada_geom *geom, int32_t num_seqs,
                                  int32_t max_pages_per_head, int32_t num_splits);
 
@@ -213,10 +214,11 @@ size_t ada_decode_workspace_size(const ada_geom *geom, int32_t num_seqs,
  *     other entries are left untouched.
  *   num_splits: page subsets per row, 1..1024 (0 = ada_decode_default_splits).
  *   ws: ada_decode_workspace_size(geom, S, max_pages_per_head, num_splits)
- *     bytes, 256-byte aligned.  Its first S*Hkv 32-bit words are per-row
- *     split counters: they must be zero before the first call that uses the
- *     workspace (allocate it zero-filled), and every completed call leaves
- *     them zero.  Calls that overlap in time must not share a workspace.
+ *     bytes, 256-byte aligned, any content: every call writes what it
+ *     reads.  Calls that overlap in time must not share a workspace.
+ * The step is up to three kernels on `stream`: a per-row preparation
+ * (code tables, scaled query; ada_decode only), the page stream, and a
+ * split merge when num_splits > 1.
  * Cache pages must be tiers 0-2.  Queries must be finite with |q| < 2^64.
  */
 ada_status ada_decode(const ada_geom *geom, const ada_cache *cache, const float *cb8,
