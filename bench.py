@@ -2,12 +2,14 @@
 
     python bench.py [--steps K] [--warmup W] [--workload 2|3] [--splits S]
 
-A step is one ada_decode call: code-table build, page stream, online softmax
-and split merge for every (sequence, query head) of the workload, one launch.
-The cache is built on the GPU (encode + pack) before timing; the timed region
-replays a HIP graph of decode steps over rotated copies of the page arena, so
-that repeated steps read HBM and not the 256 MiB Infinity Cache.  Prints one
-JSON line.
+A step is one ada_decode call over the workload: the per-row code-table
+preparation, the page stream (logits, online softmax, PV) and the split
+merge, for every (sequence, query head).  The cache is built on the GPU
+(encode + pack) before timing; the timed region replays a HIP graph of
+steps over rotated copies of the page arena, so repeated steps read HBM and
+not the 256 MiB Infinity Cache.  `value` is context tokens per second of
+whole steps.  The roofline entry is for the dominant kernel, the page
+stream, timed alone with events on its stream.  Prints one JSON line.
 """
 from __future__ import annotations
 
@@ -122,6 +124,23 @@ def time_graph(step_fns, steps, warmup):
     return n, wall, e0.elapsed_time(e1) / n
 
 
+def batch_event_ms(step_fns, n):
+    """Mean duration of n back-to-back launches (the GPU stays busy: each
+    launch is queued well before the previous one ends), from two events on
+    the launch stream around the batch."""
+    st = torch.cuda.current_stream()
+    for f in step_fns:
+        f()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(st)
+    for i in range(n):
+        step_fns[i % len(step_fns)]()
+    e1.record(st)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / n
+
+
 def kernel_event_ms(step_fns, n):
     """Average duration of single decode launches, each bracketed by events
     on the launch stream (eager launches; the GPU timestamps the events)."""
@@ -165,10 +184,39 @@ def cpu_baseline(cfg, layer, seconds_target=10.0):
         res = oracle.decode(hc, cb8, cb4, q, cfg.sigma, nthreads=threads)
         t += time.perf_counter() - t0
         reps += 1
+    # one thread, on the first query head's share of the step
+    t0 = time.perf_counter()
+    oracle.decode(hc, cb8, cb4, q, cfg.sigma, units=(0, 1), nthreads=1)
+    t1 = time.perf_counter() - t0
     tokens = int(lens.sum())
     return dict(value=tokens * reps / t, unit="KV tokens/s", cores=threads, kind="oracle",
                 sample=f"{reps} whole decode steps of the workload (all {units} query heads, "
-                       f"T={tokens}), double precision, {threads} threads"), res
+                       f"T={tokens}), double precision, {threads} threads",
+                single_thread_value=tokens / (t1 * units)), res
+
+
+def stream_bytes(L):
+    """Bytes the page-stream kernel must read from HBM per launch: the stored
+    pages and their page-table entries (4 B offset + 1 B metadata)."""
+    cache = L["cache"]
+    return cache.used_bytes() + int(cache.num_pages_host.sum()) * 5
+
+
+def profiled_traffic(kernel, workload):
+    """HBM bytes per launch of `kernel` on `workload` from the committed
+    rocprofv3 counter summary, if that summary was taken on the current
+    kernel source; else None."""
+    import glob
+    import hashlib
+    src = os.path.join(ROOT, "compressed_kv_attention_amd", "csrc", "decode.hip")
+    sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    for f in sorted(glob.glob(os.path.join(ROOT, "profiles", "*.md"))):
+        for line in open(f):
+            if line.startswith("traffic: "):
+                rec = json.loads(line[len("traffic: "):])
+                if rec.get("kernel") == kernel and rec.get("workload") == workload:
+                    return rec["bytes_per_launch"] if rec.get("source_sha256") == sha else None
+    return None
 
 
 def algorithmic_bytes(L, cfg):
@@ -237,13 +285,28 @@ def main():
         f"{n_copies} arena copies; {splits} splits per row")
     timer = time_eager if args.eager else time_graph
     steps, wall, ms_graph = timer(fns, args.steps, args.warmup)
-    k_med, k_mean = kernel_event_ms(fns, max(50, 2 * n_copies))
     tokens = int(L["lens"].sum())
     value = tokens / (ms_graph / 1e3)
     alg = algorithmic_bytes(L, cfg)
-    achieved = alg / (k_mean / 1e3) / 1e9
-    log(f"step {ms_graph * 1e3:.2f} us (graph), kernel {k_mean * 1e3:.2f} us mean / "
-        f"{k_med * 1e3:.2f} us median (events), {achieved:.0f} GB/s")
+
+    # dominant kernel: the page stream alone, events around each launch on
+    # the stream it is launched on (the preparation it reads is done once)
+    ada.decode_stage("prepare", geom, cache, L["cb8"], L["cb4"], L["q"], cfg.sigma, out,
+                     num_splits=args.splits, ws=ws)
+
+    def make_stream(v):
+        return lambda: ada.decode_stage("stream", geom, cache, L["cb8"], L["cb4"], L["q"], cfg.sigma,
+                                        out, lse, num_splits=args.splits, ws=ws, view=v)
+
+    sfns = [make_stream(v) for v in views]
+    k_mean = batch_event_ms(sfns, max(200, 4 * n_copies))
+    k_med, _ = kernel_event_ms(sfns, max(50, 2 * n_copies))
+    sbytes = stream_bytes(L)
+    achieved = sbytes / (k_mean / 1e3) / 1e9
+    kernel_name = f"decode_main<{D},{Hq // cfg.num_kv_heads},false>"
+    traffic = profiled_traffic(kernel_name, cfg.name)
+    log(f"step {ms_graph * 1e3:.2f} us (graph); page stream {k_mean * 1e3:.2f} us mean of back-to-back "
+        f"launches, {k_med * 1e3:.2f} us median single launch (events), {achieved:.0f} GB/s")
 
     result = {
         "metric": "ADA decode KV tokens/s per step",
@@ -263,9 +326,11 @@ def main():
                    "head_dim": D, "tier_cum_bp": list(map(int, synth.tier_mix(cfg)[0])),
                    "splits": splits, "arena_copies": n_copies},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
-                     "kernel": "decode_main<128,4,false>", "kernel_us_mean": k_mean * 1e3,
-                     "bytes_per_launch": alg},
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
+                     "kernel": kernel_name, "kernel_us_mean": k_mean * 1e3,
+                     "kernel_us_median_single_launch": k_med * 1e3, "bytes_per_launch": sbytes},
+        "step_roofline": {"bytes_per_step": alg, "achieved_GBs": alg / (ms_graph / 1e3) / 1e9,
+                          "frac": alg / (ms_graph / 1e3) / 1e9 / HBM_PEAK_GBS},
         "stored_bytes": used,
         "stored_fraction_of_dense": used / (tokens * cfg.num_kv_heads * 512),
     }

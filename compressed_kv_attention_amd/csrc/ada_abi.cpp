@@ -267,7 +267,8 @@ int32_t default_splits(const ada_geom *g, int32_t S, int32_t maxp)
 
 ada_status decode_common(const ada_geom *g, const ada_cache *c, const float *cb8, const float *cb4,
                          const uint16_t *q, float scale, float *out, float *lse, float *logits,
-                         int32_t num_splits, void *ws, size_t ws_bytes, void *stream, bool dense)
+                         int32_t num_splits, void *ws, size_t ws_bytes, void *stream, bool dense,
+                         unsigned stages = kStageAll)
 {
     if (!geom_ok(g) || !cache_ok(c) || q == nullptr || out == nullptr || num_splits < 0)
         return ADA_EINVAL;
@@ -312,7 +313,7 @@ ada_status decode_common(const ada_geom *g, const ada_cache *c, const float *cb8
     a.Hkv = g->num_kv_heads;
     a.maxp = c->max_pages_per_head;
     a.nsplit = ns;
-    if (launch_decode(g->head_dim, NH, dense, a, as_stream(stream)) != hipSuccess)
+    if (launch_decode(g->head_dim, NH, dense, a, as_stream(stream), stages) != hipSuccess)
         return ADA_EHIP;
     return ADA_OK;
 }
@@ -465,6 +466,31 @@ ada_status ada_decode(const ada_geom *geom, const ada_cache *cache, const float 
 {
     return decode_common(geom, cache, cb8, cb4, q, softmax_scale, out, lse, logits_dbg, num_splits, ws,
                          ws_bytes, stream, false);
+}
+
+ada_status ada_decode_prepare(const ada_geom *geom, const ada_cache *cache, const float *cb8,
+                              const float *cb4, const uint16_t *q, float softmax_scale, float *out,
+                              int32_t num_splits, void *ws, size_t ws_bytes, void *stream)
+{
+    return decode_common(geom, cache, cb8, cb4, q, softmax_scale, out, nullptr, nullptr, num_splits, ws,
+                         ws_bytes, stream, false, kStagePrep);
+}
+
+ada_status ada_decode_stream(const ada_geom *geom, const ada_cache *cache, const float *cb8,
+                             const float *cb4, const uint16_t *q, float softmax_scale, float *out,
+                             float *lse, float *logits_dbg, int32_t num_splits, void *ws,
+                             size_t ws_bytes, void *stream)
+{
+    return decode_common(geom, cache, cb8, cb4, q, softmax_scale, out, lse, logits_dbg, num_splits, ws,
+                         ws_bytes, stream, false, kStageStream);
+}
+
+ada_status ada_decode_merge(const ada_geom *geom, const ada_cache *cache, const float *cb8,
+                            const float *cb4, const uint16_t *q, float softmax_scale, float *out,
+                            float *lse, int32_t num_splits, void *ws, size_t ws_bytes, void *stream)
+{
+    return decode_common(geom, cache, cb8, cb4, q, softmax_scale, out, lse, nullptr, num_splits, ws,
+                         ws_bytes, stream, false, kStageMerge);
 }
 
 ada_status dense_decode(const ada_geom *geom, const ada_cache *cache, const uint16_t *q,

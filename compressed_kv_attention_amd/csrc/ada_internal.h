@@ -59,9 +59,11 @@ struct DecodeArgs {
     int S, Hq, Hkv, maxp, nsplit;
 };
 
-// Enqueues one decode step: the per-row preparation (coded caches), the
-// page stream and, with more than one split, the split merge.
-hipError_t launch_decode(int D, int NH, bool dense, const DecodeArgs &a, hipStream_t st);
+// Decode stages: the per-row preparation (coded caches only), the page
+// stream, and the split merge (only with more than one split).
+enum : unsigned { kStagePrep = 1, kStageStream = 2, kStageMerge = 4, kStageAll = 7 };
+hipError_t launch_decode(int D, int NH, bool dense, const DecodeArgs &a, hipStream_t st,
+                         unsigned stages = kStageAll);
 
 // LDS bytes the page-stream workgroup needs; the device offers 160 KiB.
 size_t decode_shmem_bytes(int D, int NH, bool dense, int nsplit, int maxp);

@@ -781,7 +781,7 @@ size_t merge_shmem_bytes(int nsplit)
 }
 
 template <int D, int NH, bool DENSE>
-hipError_t launch_t(const DecodeArgs &a, hipStream_t st)
+hipError_t launch_t(const DecodeArgs &a, hipStream_t st, unsigned stages)
 {
     const int rows = a.S * a.Hkv;
     if (rows <= 0 || a.nsplit <= 0)
@@ -795,15 +795,18 @@ hipError_t launch_t(const DecodeArgs &a, hipStream_t st)
             return e;
         attr_set = shmem;
     }
-    if constexpr (!DENSE) {
+    if (!DENSE && (stages & kStagePrep)) {
         hipLaunchKernelGGL((decode_prep<D, NH>), dim3(rows, D / 8 + 1), dim3(kPrepThreads), 0, st, a);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess)
             return e;
     }
-    hipLaunchKernelGGL((decode_main<D, NH, DENSE>), dim3(rows * a.nsplit), dim3(kThreads), shmem, st, a);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess || a.nsplit == 1)
+    hipError_t e = hipSuccess;
+    if (stages & kStageStream) {
+        hipLaunchKernelGGL((decode_main<D, NH, DENSE>), dim3(rows * a.nsplit), dim3(kThreads), shmem, st, a);
+        e = hipGetLastError();
+    }
+    if (e != hipSuccess || a.nsplit == 1 || !(stages & kStageMerge))
         return e;
     const size_t mshmem = merge_shmem_bytes<D, NH>(a.nsplit);
     static size_t mattr_set = 0;
@@ -839,11 +842,11 @@ size_t decode_shmem_bytes(int D, int NH, bool dense, int nsplit, int maxp)
     return 0;
 }
 
-hipError_t launch_decode(int D, int NH, bool dense, const DecodeArgs &a, hipStream_t st)
+hipError_t launch_decode(int D, int NH, bool dense, const DecodeArgs &a, hipStream_t st, unsigned stages)
 {
 #define ADA_CASE(DD, NN)                                                                          \
     if (D == DD && NH == NN)                                                                      \
-        return dense ? launch_t<DD, NN, true>(a, st) : launch_t<DD, NN, false>(a, st);
+        return dense ? launch_t<DD, NN, true>(a, st, stages) : launch_t<DD, NN, false>(a, st, stages);
     ADA_CASE(64, 1)
     ADA_CASE(64, 2)
     ADA_CASE(64, 4)

@@ -227,6 +227,28 @@ ada_status ada_decode(const ada_geom *geom, const ada_cache *cache, const float 
                       size_t ws_bytes, void *stream);
 
 /*
+ * The three stages of ada_decode, for callers that time or schedule them
+ * apart.  Each takes the arguments of ada_decode (unused ones may be NULL);
+ * called in this order on one stream with the same arguments and workspace
+ * they do exactly what one ada_decode call does.
+ *   ada_decode_prepare: the row code tables and scaled queries, into ws.
+ *   ada_decode_stream:  the page stream; writes the split partials into ws
+ *     (or out / lse / logits_dbg directly when num_splits resolves to 1).
+ *   ada_decode_merge:   combines the partials into out / lse; enqueues
+ *     nothing when num_splits resolves to 1.
+ */
+ada_status ada_decode_prepare(const ada_geom *geom, const ada_cache *cache, const float *cb8,
+                              const float *cb4, const uint16_t *q, float softmax_scale, float *out,
+                              int32_t num_splits, void *ws, size_t ws_bytes, void *stream);
+ada_status ada_decode_stream(const ada_geom *geom, const ada_cache *cache, const float *cb8,
+                             const float *cb4, const uint16_t *q, float softmax_scale, float *out,
+                             float *lse, float *logits_dbg, int32_t num_splits, void *ws,
+                             size_t ws_bytes, void *stream);
+ada_status ada_decode_merge(const ada_geom *geom, const ada_cache *cache, const float *cb8,
+                            const float *cb4, const uint16_t *q, float softmax_scale, float *out,
+                            float *lse, int32_t num_splits, void *ws, size_t ws_bytes, void *stream);
+
+/*
  * dense_decode -- the dense bf16 paged-decode baseline over tier-3 pages
  * (l_t = softmax_scale * q . k_t with bf16 keys), same split/merge scheme
  * and arguments as ada_decode without codebooks.

@@ -58,6 +58,31 @@ def test_decode_tiny_workload(splits):
     _check_decode(geom_of(cfg), hc, case, splits, "tiny D=64 MHA T=512")
 
 
+@pytest.mark.parametrize("splits", [1, 4])
+def test_decode_stages_equal_one_call(splits):
+    """ada_decode_prepare + _stream + _merge on one stream give exactly the
+    outputs of one ada_decode call (same kernels, same order)."""
+    cfg = small_workload(D=128, Hq=8, Hkv=2, S=3, T=700, seed=61)
+    case = make_case(cfg, lens=[700, 333, 90], mixes=[(1500, 6000, 8500)] * 3)
+    hc, _ = oracle_cache(case)
+    geom = geom_of(cfg)
+    dc = upload_cache(hc, geom)
+    d = _dev_case(case)
+    flush(f"[stages] splits={splits}")
+    out1, lse1, lg1 = decode_outputs(geom, dc, d["q"])
+    ada.decode(geom, dc, d["cb8"], d["cb4"], d["q"], cfg.sigma, out1, lse1, lg1, num_splits=splits)
+    out2, lse2, lg2 = decode_outputs(geom, dc, d["q"])
+    ws = None
+    for st in ("prepare", "stream", "merge"):
+        ws = ada.decode_stage(st, geom, dc, d["cb8"], d["cb4"], d["q"], cfg.sigma, out2, lse2, lg2,
+                              num_splits=splits, ws=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(out1, out2) and torch.equal(lse1, lse2)
+    assert torch.equal(torch.nan_to_num(lg1, nan=7.0), torch.nan_to_num(lg2, nan=7.0))
+    ref = oracle.decode(hc, case["cb8"], case["cb4"], case["q"], cfg.sigma, nthreads=8)
+    assert np.abs(out2.cpu().double().numpy() - ref["out"]).max() <= OUT_TOL
+
+
 @pytest.mark.parametrize("D,Hq,Hkv", [(128, 4, 2), (64, 8, 2), (128, 4, 4), (64, 2, 2)])
 def test_decode_ragged_mixed_tiers(D, Hq, Hkv):
     cfg = small_workload(D=D, Hq=Hq, Hkv=Hkv, S=4, T=300, seed=40 + D + Hq)
