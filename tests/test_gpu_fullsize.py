@@ -1,0 +1,215 @@
+"""Full-size parity for the large workloads (GPU).
+
+The whole workload runs on the GPU exactly as the benchmark runs it: encode,
+pack into a (permuted) pool, decode with the default split count.  The
+oracle then builds its own cache from the same synthetic inputs for a sample
+of sequences -- a sequence's pages, and so its outputs, depend on no other
+sequence -- and the two are compared:
+  * radii bit-exact and codes bit-exact (a disagreement must be a near-tie,
+    distance gap < 1e-6 in the oracle's double arithmetic);
+  * every page of every sampled row bit-exact, with its metadata, page count
+    and tier counts (pages are found through each side's own page table);
+  * outputs max-abs <= 1e-2 and lse within 1e-3 * max(|lse|, 1).
+The GPU pool itself must be exactly tiled by the pages of every row.
+"""
+from __future__ import annotations
+
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import compressed_kv_attention_amd as ada
+import oracle
+import synth
+from gpu_util import flush, u16
+
+pytestmark = pytest.mark.gpu
+
+OUT_TOL = 1e-2
+NTHREADS = max(1, min(os.cpu_count() or 1, 16))
+
+
+def _stored_bytes(cfg, lens, bp, extra_tokens=0):
+    H, D = cfg.num_kv_heads, cfg.head_dim
+    total = 0
+    for s, T in enumerate(lens):
+        for T_call in ([int(T)] + ([extra_tokens] if extra_tokens else [])):
+            n = [(int(bp[s][k]) * T_call + 5000) // 10000 for k in range(3)]
+            cnt = [n[0], n[1] - n[0], n[2] - n[1]]
+            total += H * sum((c + 15) // 16 * ada.page_bytes(D, k) for k, c in enumerate(cnt))
+    return total
+
+
+def _gpu_encode(geom, keys, cb8, cb4):
+    n, H, D = keys.shape
+    r = torch.empty((n, H), dtype=torch.float16, device="cuda")
+    c8 = torch.empty((n, H, D // 8), dtype=torch.uint8, device="cuda")
+    c4 = torch.empty((n, H, D // 16), dtype=torch.uint8, device="cuda")
+    ada.encode(geom, keys, cb8, cb4, r, c8, c4)
+    return r, c8, c4
+
+
+def _check_codes(label, g_r, g_c8, g_c4, keys_cpu, cb8, cb4):
+    """GPU encode outputs of a token sample against the oracle's."""
+    rr, rc8, rc4 = oracle.encode(keys_cpu, cb8, cb4, nthreads=NTHREADS)
+    assert np.array_equal(u16(g_r), rr), f"{label}: radius differs"
+    g8, g4 = g_c8.cpu().numpy(), g_c4.cpu().numpy()
+    bad = np.nonzero((g8 != rc8).any((1, 2)) | (g4 != rc4).any((1, 2)))[0]
+    if len(bad):
+        _, _, _, d8, d4 = oracle.encode(keys_cpu[bad], cb8, cb4, with_dist=True)
+        for i, t in enumerate(bad):
+            for h, g in zip(*np.nonzero(g8[t] != rc8[t])):
+                assert abs(d8[i, h, g, g8[t, h, g]] - d8[i, h, g, rc8[t, h, g]]) < 1e-6
+            lo, hi = g4[t] & 15, g4[t] >> 4
+            rlo, rhi = rc4[t] & 15, rc4[t] >> 4
+            for h, b in zip(*np.nonzero((lo != rlo) | (hi != rhi))):
+                for gg, a, c in ((2 * b, lo[h, b], rlo[h, b]), (2 * b + 1, hi[h, b], rhi[h, b])):
+                    if a != c:
+                        assert abs(d4[i, h, gg, a] - d4[i, h, gg, c]) < 1e-6
+    agree = 1.0 - len(bad) / max(1, len(g8))
+    assert agree >= 0.999
+    flush(f"[{label}] codes of {len(g8)} tokens: {len(bad)} tokens with near-tie differences")
+    return rr, rc8, rc4
+
+
+def _check_pool_tiling(label, dc, geom):
+    """The GPU pool is exactly tiled by the pages of all rows: no gap, no
+    overlap, ending at the arena cursor."""
+    npg = dc.num_pages.cpu().numpy()
+    pt = dc.page_table.cpu().numpy().view(np.uint32)
+    pm = dc.page_meta.cpu().numpy()
+    offs, sizes = [], []
+    for r in range(len(npg)):
+        n = int(npg[r])
+        offs.append(pt[r, :n].astype(np.int64) * 128)
+        sizes.append(np.array([ada.page_bytes(geom.head_dim, int(m) & 3) for m in pm[r, :n]], np.int64))
+    offs, sizes = np.concatenate(offs), np.concatenate(sizes)
+    order = np.argsort(offs)
+    o, z = offs[order], sizes[order]
+    assert o[0] == 0 and np.array_equal(o[1:], (o + z)[:-1]), f"{label}: pool not tiled"
+    assert int(o[-1] + z[-1]) == int(dc.cursor[0]) * 128
+    flush(f"[{label}] pool of {len(o)} pages exactly tiled")
+
+
+def _compare_rows(label, dc, arena_gpu, hc, seqs, H, D):
+    """Pages, metadata and counts of the sampled rows, bit-exact."""
+    npg = dc.num_pages.cpu().numpy()
+    pt = dc.page_table.cpu().numpy().view(np.uint32)
+    pm = dc.page_meta.cpu().numpy()
+    tt = dc.tier_tokens.cpu().numpy()
+    for i, s in enumerate(seqs):
+        for h in range(H):
+            rg, ro = s * H + h, i * H + h
+            n = int(hc.num_pages[ro])
+            assert int(npg[rg]) == n, f"{label}: row ({s},{h}) page count"
+            assert np.array_equal(pm[rg, :n], hc.page_meta[ro, :n]), f"{label}: row ({s},{h}) metadata"
+            assert np.array_equal(tt[rg], hc.tier_tokens[ro]), f"{label}: row ({s},{h}) tier counts"
+            if n == 0:
+                continue
+            sizes = [ada.page_bytes(D, int(m) & 3) for m in pm[rg, :n]]
+            g = torch.cat([arena_gpu[int(pt[rg, p]) * 128: int(pt[rg, p]) * 128 + sizes[p]]
+                           for p in range(n)]).cpu().numpy()
+            o = np.concatenate([hc.arena[int(hc.page_table[ro, p]) * 128: int(hc.page_table[ro, p]) * 128 + sizes[p]]
+                                for p in range(n)])
+            if not np.array_equal(g, o):
+                first = int(np.nonzero(g != o)[0][0])
+                page = int(np.searchsorted(np.cumsum(sizes), first, side="right"))
+                raise AssertionError(f"{label}: row ({s},{h}) page {page} bytes differ")
+    flush(f"[{label}] pages of {len(seqs) * H} sampled rows bit-exact")
+
+
+def _check_outputs(label, out, lse, ref, seqs):
+    o = out[seqs].cpu().double().numpy()
+    err = np.abs(o - ref["out"]).max()
+    assert err <= OUT_TOL, f"{label}: out max-abs {err:.3g}"
+    l = lse[seqs].cpu().double().numpy()
+    assert (np.abs(l - ref["lse"]) <= 1e-3 * np.maximum(np.abs(ref["lse"]), 1.0)).all(), f"{label}: lse"
+    flush(f"[{label}] outputs of {len(seqs)} sampled sequences: max-abs {err:.2e}")
+
+
+def _run(number, layer, seqs, append=0):
+    cfg = synth.WORKLOADS[number]
+    label = f"workload {number} layer {layer}"
+    flush(f"[{label}] building inputs on the GPU")
+    H, D, S = cfg.num_kv_heads, cfg.head_dim, cfg.num_seqs
+    geom = ada.Geom(D, cfg.num_q_heads, H)
+    lens = synth.seq_lens(cfg)
+    cu = synth.cu_tokens(lens)
+    N = int(cu[-1])
+    bp = synth.tier_mix(cfg)
+    keys = synth.keys(cfg, layer, N, "cuda")
+    vals = synth.values(cfg, layer, N, "cuda")
+    scores = synth.scores(cfg, layer, N)
+    q = synth.queries(cfg, layer, "cuda")
+    cb8, cb4 = synth.codebooks(cfg, layer)
+    cb8d, cb4d = cb8.cuda(), cb4.cuda()
+
+    # --- the GPU path at full size ------------------------------------------
+    flush(f"[{label}] GPU encode + pack of {N} tokens x {H} heads")
+    r, c8, c4 = _gpu_encode(geom, keys, cb8d, cb4d)
+    maxp = int(max(lens)) // 16 + 4 + (append // 16 + 4 if append else 0)
+    dc = ada.Cache(geom, S, maxp, _stored_bytes(cfg, lens, bp, append))
+    n_pages = ada.pack_num_pages(geom, cu, bp)
+    ada.rdr_pack(geom, dc, cu, bp, keys, vals, r, c8, c4, scores.cuda(),
+                 place_perm=synth.place_perm(cfg, layer, n_pages))
+    if append:
+        acu = synth.cu_tokens(np.full(S, append, np.int64))
+        ak = synth.keys(cfg, layer, S * append, "cuda", stream="k-append")
+        av = synth.values(cfg, layer, S * append, "cuda", stream="v-append")
+        asc = synth.scores(cfg, layer, S * append, stream="score-append")
+        ar, ac8, ac4 = _gpu_encode(geom, ak, cb8d, cb4d)
+        an = ada.pack_num_pages(geom, acu, bp)
+        ada.rdr_pack(geom, dc, acu, bp, ak, av, ar, ac8, ac4, asc.cuda(),
+                     place_perm=synth.place_perm(cfg, layer, an, stream="place-append"),
+                     pos_base=lens.astype(np.int64))
+    out = torch.full((S, cfg.num_q_heads, D), float("nan"), device="cuda")
+    lse = torch.full((S, cfg.num_q_heads), float("nan"), device="cuda")
+    ada.decode(geom, dc, cb8d, cb4d, q, cfg.sigma, out, lse)
+    torch.cuda.synchronize()
+    _check_pool_tiling(label, dc, geom)
+
+    # --- the oracle on the sampled sequences ----------------------------------
+    sl = [slice(int(cu[s]), int(cu[s + 1])) for s in seqs]
+    k_s = torch.cat([keys[x] for x in sl]).cpu()
+    v_s = torch.cat([vals[x] for x in sl]).cpu()
+    sc_s = torch.cat([scores[x] for x in sl])
+    flush(f"[{label}] oracle encode of {len(k_s)} tokens x {H} heads ({NTHREADS} threads)")
+    rr, rc8, rc4 = _check_codes(label, torch.cat([r[x] for x in sl]), torch.cat([c8[x] for x in sl]),
+                                torch.cat([c4[x] for x in sl]), k_s, cb8, cb4)
+    lens_s = lens[seqs]
+    cu_s = synth.cu_tokens(lens_s)
+    bp_s = bp[seqs]
+    hc = oracle.HostCache(D, H, len(seqs), maxp, _stored_bytes(cfg, lens_s, bp_s, append) + 4096,
+                          slot_tokens=False)
+    assert oracle.pack(hc, cu_s, bp_s, k_s, v_s, rr, rc8, rc4, sc_s) == 0
+    if append:
+        ak_s = torch.cat([ak[s * append:(s + 1) * append] for s in seqs]).cpu()
+        av_s = torch.cat([av[s * append:(s + 1) * append] for s in seqs]).cpu()
+        asc_s = torch.cat([asc[s * append:(s + 1) * append] for s in seqs])
+        arr, arc8, arc4 = _check_codes(label + " append", torch.cat([ar[s * append:(s + 1) * append] for s in seqs]),
+                                       torch.cat([ac8[s * append:(s + 1) * append] for s in seqs]),
+                                       torch.cat([ac4[s * append:(s + 1) * append] for s in seqs]),
+                                       ak_s, cb8, cb4)
+        acu_s = synth.cu_tokens(np.full(len(seqs), append, np.int64))
+        assert oracle.pack(hc, acu_s, bp_s, ak_s, av_s, arr, arc8, arc4, asc_s,
+                           pos_base=lens_s.astype(np.int64)) == 0
+    _compare_rows(label, dc, dc.arena, hc, seqs, H, D)
+    flush(f"[{label}] oracle decode of {len(seqs)} sequences")
+    ref = oracle.decode(hc, cb8, cb4, q[seqs].cpu(), cfg.sigma, nthreads=NTHREADS)
+    _check_outputs(label, out, lse, ref, seqs)
+
+
+def test_workload3_batch4_t128k_permuted_pool():
+    _run(3, 0, [0, 3])
+
+
+def test_workload4_ragged64_budgets():
+    lens = synth.seq_lens(synth.WORKLOADS[4])
+    seqs = sorted({int(np.argmin(lens)), int(np.argmax(lens)), 17})
+    _run(4, 0, seqs)
+
+
+def test_workload5_one_layer_t128k_with_append():
+    _run(5, 7, [2, 5], append=synth.WORKLOADS[5].append_tokens)
