@@ -12,11 +12,11 @@
 // Work decomposition.  A step is three kernels.  The preparation kernel
 // tabulates each (sequence, kv-head) row's LUT once, with the query operand
 // of the fp16-key tier, into the workspace.  In the page stream one
-// workgroup (8 wave64s, one per CU at D = 128) serves one row and one of
+// workgroup (12 wave64s, one per CU at D = 128) serves one row and one of
 // `nsplit` interleaved page subsets of it, for all NH query heads of the
 // GQA group, so every page is read from HBM once; it copies the row's LUT
-// into LDS.  Wave w of split s takes pages s + (w + 8i) * nsplit, one page
-// (16 slots) at a time, with the next two pages' loads in flight while the
+// into LDS.  Wave w of split s takes pages s + (w + 12i) * nsplit, one page
+// (16 slots) at a time, with the next page's loads in flight while the
 // current one is computed.
 //
 // Per page the wave forms a 16 x 16 tile of logits, rows = query heads
@@ -38,7 +38,7 @@
 // folded into the weights.  The output accumulators are the MFMA C tiles
 // (rows = heads, so lanes 0-15 hold the outputs of one dim each).
 //
-// At the end the 8 waves are merged through LDS and the split's partial
+// At the end the 12 waves are merged through LDS and the split's partial
 // (m, l, acc) is written; the merge kernel combines a row's splits into the
 // outputs (with one split the stream writes them directly).
 #include "ada_internal.h"
@@ -51,7 +51,7 @@ namespace {
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kRescale = 8.0f; // log2 of the largest weight kept between rescales
-constexpr int kWaves = 8;
+constexpr int kWaves = 12;
 constexpr int kThreads = 64 * kWaves;
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
@@ -317,12 +317,12 @@ __device__ __forceinline__ void process_page(PageRegs<D> &cur, int p, WaveState<
                                              const float *lut, const QOperand<D, DENSE> &qo, float lsc,
                                              float sig2, float *lgout, int maxp, const Lane &L)
 {
-    // This page's loads were issued before the next two pages' loads: wait
-    // until at most those 2 NL are outstanding.  Every register of this page
+    // This page's loads were issued before the next page's NL loads: wait
+    // until at most those NL are outstanding.  Every register of this page
     // is then complete on every path, including chunks a tier never reads,
     // so the wait-count pass needs no full drain where they are reused.
     constexpr int NL = PageRegs<D>::NL;
-    __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * NL));
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(NL));
     const int tier = cur.tier;
     float x[4];
     if (DENSE || tier == 0)
@@ -344,20 +344,24 @@ __device__ __forceinline__ void process_page(PageRegs<D> &cur, int p, WaveState<
                 lo[e] = x[e] * kLn2;
     }
 
-    // online softmax: per-head page maxima, rescale when they run ahead
+    // online softmax: per-head page maxima; one wave-wide test whether any
+    // of them runs ahead of its running maximum (lanes of unused heads have
+    // pm = -inf and never do), the per-head rescale only then
     const float pm = rows_max(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])));
+    if (__builtin_amdgcn_ballot_w64(pm > st.mlane + kRescale) != 0) {
 #pragma unroll
-    for (int h = 0; h < NH; h++) {
-        const float pmh = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(pm), h));
-        if (pmh > st.m[h] + kRescale) {
-            const float f = __builtin_amdgcn_exp2f(st.m[h] - pmh);
-            st.m[h] = pmh;
+        for (int h = 0; h < NH; h++) {
+            const float pmh = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(pm), h));
+            if (pmh > st.m[h] + kRescale) {
+                const float f = __builtin_amdgcn_exp2f(st.m[h] - pmh);
+                st.m[h] = pmh;
 #pragma unroll
-            for (int b = 0; b < D / 16; b++)
-                st.acc[b][h] *= f;
-            const bool mine = L.hl == h;
-            st.l = mine ? st.l * f : st.l;
-            st.mlane = mine ? pmh : st.mlane;
+                for (int b = 0; b < D / 16; b++)
+                    st.acc[b][h] *= f;
+                const bool mine = L.hl == h;
+                st.l = mine ? st.l * f : st.l;
+                st.mlane = mine ? pmh : st.mlane;
+            }
         }
     }
     float w[4];
@@ -535,13 +539,12 @@ __global__ __launch_bounds__(kThreads) void decode_main(DecodeArgs a)
     const int last = n_mine - 1;
     const uint32_t *pt = a.page_table + (size_t)row * a.maxp;
     const uint8_t *pm = a.page_meta + (size_t)row * a.maxp;
-    // the wave's first two pages, straight from the table: their loads
-    // overlap the table staging and the LUT copy
-    PageRegs<D> bufA, bufB, bufC;
+    // the wave's first page, straight from the table: its loads overlap the
+    // table staging and the LUT copy
+    PageRegs<D> bufA, bufB;
     if (n_mine > 0) {
-        const int p0 = split + wave * a.nsplit, p1 = split + (wave + kWaves * min(1, last)) * a.nsplit;
+        const int p0 = split + wave * a.nsplit;
         fetch_entry<D, DENSE>(bufA, make_uint2(pt[p0], pm[p0]), a.arena, L);
-        fetch_entry<D, DENSE>(bufB, make_uint2(pt[p1], pm[p1]), a.arena, L);
     }
     {
         for (int k = tid; k < n_wg; k += kThreads) {
@@ -596,32 +599,28 @@ __global__ __launch_bounds__(kThreads) void decode_main(DecodeArgs a)
     float *lgout = a.logits ? a.logits + ((size_t)s * a.Hq + (size_t)hkv * NH) * a.maxp * kSlots
                             : nullptr;
 
-    // Three register buffers in turn: pages i+1 and i+2 are in flight while
-    // page i is computed.  Pages go in threes through a loop with one exit;
-    // every step issues one page's loads (past the end it reloads the last
-    // page), so the wait counts are fixed.  On exit bufA holds page i and
-    // bufB page i+1.
+    // Two register buffers in turn: page i+1's loads are in flight while
+    // page i is computed.  Pages go in pairs through a loop with one exit;
+    // every half-step issues one page's loads (past the end it reloads the
+    // last page), so the wait counts are fixed.  The table entry of the
+    // page after next is read from LDS a half-step ahead.  An odd last page
+    // is in bufA.
+    uint2 next = n_mine > 0 ? tbl[wave + kWaves * min(1, last)] : make_uint2(0u, 0u);
     int i = 0;
-    for (; i + 2 < n_mine; i += 3) {
-        fetch_entry<D, DENSE>(bufC, tbl[wave + kWaves * (i + 2)], a.arena, L);
+    for (; i + 1 < n_mine; i += 2) {
+        fetch_entry<D, DENSE>(bufB, next, a.arena, L);
+        next = tbl[wave + kWaves * min(i + 2, last)];
         process_page<D, NH, DENSE>(bufA, split + (wave + kWaves * i) * a.nsplit, st, lut, qo, lsc, sig2,
                                    lgout, a.maxp, L);
-        fetch_entry<D, DENSE>(bufA, tbl[wave + kWaves * min(i + 3, last)], a.arena, L);
+        fetch_entry<D, DENSE>(bufA, next, a.arena, L);
+        next = tbl[wave + kWaves * min(i + 3, last)];
         process_page<D, NH, DENSE>(bufB, split + (wave + kWaves * (i + 1)) * a.nsplit, st, lut, qo, lsc,
-                                   sig2, lgout, a.maxp, L);
-        fetch_entry<D, DENSE>(bufB, tbl[wave + kWaves * min(i + 4, last)], a.arena, L);
-        process_page<D, NH, DENSE>(bufC, split + (wave + kWaves * (i + 2)) * a.nsplit, st, lut, qo, lsc,
                                    sig2, lgout, a.maxp, L);
     }
     if (i < n_mine) {
-        fetch_entry<D, DENSE>(bufC, tbl[wave + kWaves * last], a.arena, L); // keeps the wait count
+        fetch_entry<D, DENSE>(bufB, next, a.arena, L); // keeps the wait count
         process_page<D, NH, DENSE>(bufA, split + (wave + kWaves * i) * a.nsplit, st, lut, qo, lsc, sig2,
                                    lgout, a.maxp, L);
-    }
-    if (i + 1 < n_mine) {
-        fetch_entry<D, DENSE>(bufA, tbl[wave + kWaves * last], a.arena, L);
-        process_page<D, NH, DENSE>(bufB, split + (wave + kWaves * (i + 1)) * a.nsplit, st, lut, qo, lsc,
-                                   sig2, lgout, a.maxp, L);
     }
 
     // Waves -> LDS (the LUT space is free now): [wave][D][4] accumulators
