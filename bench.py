@@ -2,9 +2,9 @@
 
     python bench.py [--steps K] [--warmup W] [--workload 2|3] [--splits S]
 
-A step is one ada_decode call over the workload: the per-row code-table
-preparation, the page stream (logits, online softmax, PV) and the split
-merge, for every (sequence, query head).  The cache is built on the GPU
+A step is one ada_decode call over the workload: the page stream (code
+tables, logits, online softmax, PV) and the split merge, for every
+(sequence, query head).  The cache is built on the GPU
 (encode + pack) before timing; the timed region replays a HIP graph of
 steps over rotated copies of the page arena, so repeated steps read HBM and
 not the 256 MiB Infinity Cache.  `value` is context tokens per second of
@@ -289,11 +289,8 @@ def main():
     value = tokens / (ms_graph / 1e3)
     alg = algorithmic_bytes(L, cfg)
 
-    # dominant kernel: the page stream alone, events around each launch on
-    # the stream it is launched on (the preparation it reads is done once)
-    ada.decode_stage("prepare", geom, cache, L["cb8"], L["cb4"], L["q"], cfg.sigma, out,
-                     num_splits=args.splits, ws=ws)
-
+    # dominant kernel: the page stream alone, events around back-to-back
+    # launches on the stream it is launched on
     def make_stream(v):
         return lambda: ada.decode_stage("stream", geom, cache, L["cb8"], L["cb4"], L["q"], cfg.sigma,
                                         out, lse, num_splits=args.splits, ws=ws, view=v)

@@ -91,8 +91,6 @@ def load():
         L.ada_decode.restype = C.c_int
         L.dense_decode.argtypes = [G, CV, P, F, P, P, P, I32, P, SZ, P]
         L.dense_decode.restype = C.c_int
-        L.ada_decode_prepare.argtypes = [G, CV, P, P, P, F, P, I32, P, SZ, P]
-        L.ada_decode_prepare.restype = C.c_int
         L.ada_decode_stream.argtypes = [G, CV, P, P, P, F, P, P, P, I32, P, SZ, P]
         L.ada_decode_stream.restype = C.c_int
         L.ada_decode_merge.argtypes = [G, CV, P, P, P, F, P, P, I32, P, SZ, P]
@@ -296,8 +294,8 @@ def decode(geom: Geom, cache: Cache, cb8, cb4, q, softmax_scale: float, out, lse
 
 def decode_stage(stage: str, geom: Geom, cache: Cache, cb8, cb4, q, softmax_scale: float, out,
                  lse=None, logits=None, num_splits: int = 0, ws=None, stream=None, view=None):
-    """One stage of ada_decode: "prepare", "stream" or "merge"
-    (ada_decode_prepare / _stream / _merge).  The stages share `ws`."""
+    """One stage of ada_decode: "stream" or "merge" (ada_decode_stream /
+    ada_decode_merge).  The stages share `ws`."""
     ws = _decode_args(geom, cache, q, out, lse, logits, ws, num_splits)
     v = cache.view() if view is None else view
     L = load()
@@ -305,10 +303,7 @@ def decode_stage(stage: str, geom: Geom, cache: Cache, cb8, cb4, q, softmax_scal
     c8, c4 = _dev(cb8, "cb8", (torch.float32,)), _dev(cb4, "cb4", (torch.float32,))
     qq, oo = _dev(q, "q", (torch.bfloat16,)), _dev(out, "out", (torch.float32,))
     ll = _dev(lse, "lse", (torch.float32,))
-    if stage == "prepare":
-        st = L.ada_decode_prepare(g, cv, c8, c4, qq, float(softmax_scale), oo, num_splits, _dev(ws, "ws"),
-                                  ws.numel(), _stream(stream))
-    elif stage == "stream":
+    if stage == "stream":
         st = L.ada_decode_stream(g, cv, c8, c4, qq, float(softmax_scale), oo, ll,
                                  _dev(logits, "logits", (torch.float32,)), num_splits, _dev(ws, "ws"),
                                  ws.numel(), _stream(stream))

@@ -222,33 +222,21 @@ bool counts_from_bp(int32_t S, const int32_t *cu, const int32_t *bp, std::vector
     return true;
 }
 
-// Byte offsets of the decode workspace parts (all 256-byte aligned).
+// Byte offsets of the decode workspace parts (all 256-byte aligned): the
+// split partials (m, l) and acc.
 struct WsLayout {
-    bool lut;
-    size_t lut_off, qh_off, lsc_off, ml_off, acc_off, total;
+    size_t ml_off, acc_off, total;
 };
 
-WsLayout ws_layout(const ada_geom *g, int32_t S, int32_t ns, bool dense)
+WsLayout ws_layout(const ada_geom *g, int32_t S, int32_t ns)
 {
     const size_t rows = (size_t)S * g->num_kv_heads;
     const size_t NH = (size_t)(g->num_q_heads / g->num_kv_heads);
     const size_t D = (size_t)g->head_dim;
     WsLayout l{};
-    l.lut = !dense;
-    size_t off = 0;
-    l.lut_off = off;
-    if (!dense) {
-        off += align256(rows * (D / 8) * 272 * NH * sizeof(float));
-        l.qh_off = off;
-        off += align256(rows * NH * D * sizeof(uint16_t));
-        l.lsc_off = off;
-        off += align256(rows * NH * sizeof(float));
-    }
-    l.ml_off = off;
-    off += align256(rows * ns * NH * 2 * sizeof(float));
-    l.acc_off = off;
-    off += align256(rows * ns * NH * D * sizeof(float));
-    l.total = off;
+    l.ml_off = 0;
+    l.acc_off = align256(rows * ns * NH * 2 * sizeof(float));
+    l.total = l.acc_off + align256(rows * ns * NH * D * sizeof(float));
     return l;
 }
 
@@ -299,12 +287,9 @@ ada_status decode_common(const ada_geom *g, const ada_cache *c, const float *cb8
     a.out = out;
     a.lse = lse;
     a.logits = logits;
-    // workspace: [code tables][scaled queries][logit scales][partial (m, l)][partial acc]
+    // workspace: [partial (m, l)][partial acc]
     uint8_t *w = static_cast<uint8_t *>(ws);
-    const WsLayout lay = ws_layout(g, c->num_seqs, ns, dense);
-    a.lut = lay.lut ? reinterpret_cast<float *>(w + lay.lut_off) : nullptr;
-    a.qh = lay.lut ? reinterpret_cast<uint16_t *>(w + lay.qh_off) : nullptr;
-    a.lsc = lay.lut ? reinterpret_cast<float *>(w + lay.lsc_off) : nullptr;
+    const WsLayout lay = ws_layout(g, c->num_seqs, ns);
     a.part_ml = reinterpret_cast<float *>(w + lay.ml_off);
     a.part_acc = reinterpret_cast<float *>(w + lay.acc_off);
     a.sigma = scale;
@@ -456,8 +441,7 @@ size_t ada_decode_workspace_size(const ada_geom *geom, int32_t num_seqs, int32_t
     if (!geom_ok(geom) || num_seqs < 0 || max_pages_per_head < 0 || num_splits < 0)
         return 0;
     const int32_t ns = num_splits > 0 ? num_splits : default_splits(geom, num_seqs, max_pages_per_head);
-    // sized for ada_decode (the dense path needs less)
-    return ws_layout(geom, num_seqs, ns, false).total;
+    return ws_layout(geom, num_seqs, ns).total;
 }
 
 ada_status ada_decode(const ada_geom *geom, const ada_cache *cache, const float *cb8, const float *cb4,
@@ -466,14 +450,6 @@ ada_status ada_decode(const ada_geom *geom, const ada_cache *cache, const float 
 {
     return decode_common(geom, cache, cb8, cb4, q, softmax_scale, out, lse, logits_dbg, num_splits, ws,
                          ws_bytes, stream, false);
-}
-
-ada_status ada_decode_prepare(const ada_geom *geom, const ada_cache *cache, const float *cb8,
-                              const float *cb4, const uint16_t *q, float softmax_scale, float *out,
-                              int32_t num_splits, void *ws, size_t ws_bytes, void *stream)
-{
-    return decode_common(geom, cache, cb8, cb4, q, softmax_scale, out, nullptr, nullptr, num_splits, ws,
-                         ws_bytes, stream, false, kStagePrep);
 }
 
 ada_status ada_decode_stream(const ada_geom *geom, const ada_cache *cache, const float *cb8,

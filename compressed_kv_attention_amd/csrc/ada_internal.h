@@ -50,18 +50,15 @@ struct DecodeArgs {
     float *out;
     float *lse;
     float *logits;
-    float *lut;        // [rows][G * 272][NH] code tables (coded caches only)
-    uint16_t *qh;      // [rows][NH][D] fp16 queries, scaled per head (coded caches only)
-    float *lsc;        // [rows][NH] softmax scale * 2^e_h * log2(e) (coded caches only)
     float *part_ml;    // [rows][nsplit][NH][2]  (running max in log2 units, sum)
     float *part_acc;   // [rows][nsplit][NH][D]  (unnormalised output)
     float sigma;
     int S, Hq, Hkv, maxp, nsplit;
 };
 
-// Decode stages: the per-row preparation (coded caches only), the page
-// stream, and the split merge (only with more than one split).
-enum : unsigned { kStagePrep = 1, kStageStream = 2, kStageMerge = 4, kStageAll = 7 };
+// Decode stages: the page stream, and the split merge (only with more than
+// one split).
+enum : unsigned { kStageStream = 2, kStageMerge = 4, kStageAll = 6 };
 hipError_t launch_decode(int D, int NH, bool dense, const DecodeArgs &a, hipStream_t st,
                          unsigned stages = kStageAll);
 

@@ -9,15 +9,15 @@
 // scale); the per-group dot products are tabulated once per query head
 // (the "LUT") and each coded key costs G table reads.
 //
-// Work decomposition.  A step is three kernels.  The preparation kernel
-// tabulates each (sequence, kv-head) row's LUT once, with the query operand
-// of the fp16-key tier, into the workspace.  In the page stream one
-// workgroup (12 wave64s, one per CU at D = 128) serves one row and one of
-// `nsplit` interleaved page subsets of it, for all NH query heads of the
-// GQA group, so every page is read from HBM once; it copies the row's LUT
-// into LDS.  Wave w of split s takes pages s + (w + 12i) * nsplit, one page
-// (16 slots) at a time, with the next page's loads in flight while the
-// current one is computed.
+// Work decomposition.  A step is two kernels: the page stream and, with
+// more than one split per row, the split merge.  In the page stream one
+// workgroup (12 wave64s, one per CU at D = 128) serves one (sequence,
+// kv-head) row and one of `nsplit` interleaved page subsets of it, for all
+// NH query heads of the GQA group, so every page is read from HBM once.  It
+// tabulates the row's LUT into LDS while its first pages are in flight.
+// Wave w of split s takes pages s + (w + 12i) * nsplit, one page (16 slots)
+// at a time, with the next page's loads in flight while the current one is
+// computed.
 //
 // Per page the wave forms a 16 x 16 tile of logits, rows = query heads
 // (NH used, the rest zero), columns = slots, held the way a 16x16x16 MFMA
@@ -53,6 +53,7 @@ constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kRescale = 8.0f; // log2 of the largest weight kept between rescales
 constexpr int kWaves = 12;
 constexpr int kThreads = 64 * kWaves;
+constexpr int kMaxSplitsDev = 1024; // the ABI's split limit
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef const u32x4 __attribute__((address_space(1))) *gchunk;
@@ -430,82 +431,6 @@ __device__ __forceinline__ void fetch_entry(PageRegs<D> &pr, uint2 e, const uint
     fetch_page<D, DENSE>(pr, arena + (size_t)off * kUnit, meta & 3, ((meta >> 2) & 15) + 1, L);
 }
 
-// ---- per-row preparation (coded caches) ----------------------------------
-// Grid (rows, G + 1), 256 threads.  Block (row, g < G) tabulates
-// LUT[g][c][h] = q_h[8g .. 8g+8) . C[g][c] for the row's NH query heads
-// (c < 256 from cb8, else cb4); block (row, G) writes the fp16 key-tier
-// query operand: each head's q scaled by 2^-e_h so its largest |q| lies in
-// [2^14, 2^15) (exact for bf16 values within 2^-28 of that maximum), and
-// the matching logit scale softmax_scale * 2^e_h * log2(e).
-constexpr int kPrepThreads = 256;
-
-template <int D, int NH>
-__global__ __launch_bounds__(kPrepThreads) void decode_prep(DecodeArgs a)
-{
-    constexpr int G = D / 8;
-    const int row = blockIdx.x, g = blockIdx.y, tid = threadIdx.x;
-    const int s = row / a.Hkv, hkv = row % a.Hkv;
-    const uint16_t *qg = a.q + ((size_t)s * a.Hq + (size_t)hkv * NH) * D;
-    if (g < G) {
-        float qq[NH][8];
-#pragma unroll
-        for (int h = 0; h < NH; h++)
-#pragma unroll
-            for (int i = 0; i < 8; i++)
-                qq[h][i] = __uint_as_float((uint32_t)qg[h * D + 8 * g + i] << 16);
-        const float *cb8 = a.cb8 + ((size_t)hkv * G + g) * kCodes8 * 8;
-        const float *cb4 = a.cb4 + ((size_t)hkv * G + g) * kCodes4 * 8;
-        float *dst = a.lut + ((size_t)row * G + g) * kLutCodes * NH;
-        for (int c = tid; c < kLutCodes; c += kPrepThreads) {
-            const float *w = c < kCodes8 ? cb8 + c * 8 : cb4 + (c - kCodes8) * 8;
-            const float4 w0 = *reinterpret_cast<const float4 *>(w);
-            const float4 w1 = *reinterpret_cast<const float4 *>(w + 4);
-            float o[NH];
-#pragma unroll
-            for (int h = 0; h < NH; h++) {
-                float acc = qq[h][0] * w0.x;
-                acc = fmaf(qq[h][1], w0.y, acc);
-                acc = fmaf(qq[h][2], w0.z, acc);
-                acc = fmaf(qq[h][3], w0.w, acc);
-                acc = fmaf(qq[h][4], w1.x, acc);
-                acc = fmaf(qq[h][5], w1.y, acc);
-                acc = fmaf(qq[h][6], w1.z, acc);
-                acc = fmaf(qq[h][7], w1.w, acc);
-                o[h] = acc;
-            }
-            if constexpr (NH == 4)
-                *reinterpret_cast<float4 *>(dst + c * NH) = make_float4(o[0], o[1], o[2], o[3]);
-            else if constexpr (NH == 2)
-                *reinterpret_cast<float2 *>(dst + c * NH) = make_float2(o[0], o[1]);
-            else
-                dst[c] = o[0];
-        }
-        return;
-    }
-    __shared__ int smax[NH];
-    if (tid < NH)
-        smax[tid] = 0;
-    __syncthreads();
-    for (int i = tid; i < NH * D; i += kPrepThreads) {
-        const float v = fabsf(__uint_as_float((uint32_t)qg[i] << 16));
-        atomicMax(&smax[i / D], __float_as_int(v)); // non-negative floats order as integers
-    }
-    __syncthreads();
-    for (int i = tid; i < NH * D; i += kPrepThreads) {
-        const int h = i / D;
-        const float mx = __int_as_float(smax[h]);
-        int e = 0;
-        if (mx > 0.f) {
-            frexpf(mx, &e);
-            e -= 15;
-        }
-        const float v = __uint_as_float((uint32_t)qg[i] << 16);
-        a.qh[(size_t)row * NH * D + i] = __builtin_bit_cast(uint16_t, (_Float16)ldexpf(v, -e));
-        if (i % D == 0)
-            a.lsc[(size_t)row * NH + h] = ldexpf(a.sigma, e) * kLog2e;
-    }
-}
-
 // ---- page stream ------------------------------------------------------------
 template <int D, int NH, bool DENSE>
 __global__ __launch_bounds__(kThreads) void decode_main(DecodeArgs a)
@@ -539,50 +464,149 @@ __global__ __launch_bounds__(kThreads) void decode_main(DecodeArgs a)
     const int last = n_mine - 1;
     const uint32_t *pt = a.page_table + (size_t)row * a.maxp;
     const uint8_t *pm = a.page_meta + (size_t)row * a.maxp;
-    // the wave's first page, straight from the table: its loads overlap the
-    // table staging and the LUT copy
+    // Prologue: every load is issued before any is waited for -- the wave's
+    // first page (straight from the table), the workgroup's table entries,
+    // the codewords and query slices of the LUT, the query operand -- so
+    // the prologue costs about one memory latency.  Then the entries go to
+    // LDS and the LUT is tabulated into LDS.
     PageRegs<D> bufA, bufB;
     if (n_mine > 0) {
         const int p0 = split + wave * a.nsplit;
         fetch_entry<D, DENSE>(bufA, make_uint2(pt[p0], pm[p0]), a.arena, L);
     }
-    {
-        for (int k = tid; k < n_wg; k += kThreads) {
+    constexpr int TE = 2; // table entries per thread held in registers
+    uint32_t te_off[TE], te_meta[TE];
+#pragma unroll
+    for (int j = 0; j < TE; j++) {
+        const int k = tid + j * kThreads;
+        te_off[j] = 0u;
+        te_meta[j] = 0u;
+        if (k < n_wg) {
             const int p = split + k * a.nsplit;
-            tbl[k] = make_uint2(pt[p], pm[p]);
+            te_off[j] = pt[p];
+            te_meta[j] = pm[p];
         }
     }
-    // the row's code tables, all loads in flight at once
+    // Code tables: thread t serves group g = t / TPG and codes t % TPG +
+    // TPG k; its codewords and the group's query slices load with the rest.
+    constexpr int TPG = kThreads / G;
+    constexpr int NC = (kLutCodes + TPG - 1) / TPG;
+    const int g = tid / TPG, c0 = tid % TPG;
+    const uint16_t *qrow = a.q + ((size_t)s * a.Hq + (size_t)hkv * NH) * D;
+    float4 w0[DENSE ? 1 : NC], w1[DENSE ? 1 : NC];
+    uint4 qv[NH];
     if constexpr (!DENSE) {
-        constexpr int N4 = LUT_FLOATS / 4;
-        constexpr int PER = (N4 + kThreads - 1) / kThreads;
-        const float4 *src = reinterpret_cast<const float4 *>(a.lut + (size_t)row * LUT_FLOATS);
-        float4 t[PER];
+        const float *cb8 = a.cb8 + ((size_t)hkv * G + g) * kCodes8 * 8;
+        const float *cb4 = a.cb4 + ((size_t)hkv * G + g) * kCodes4 * 8;
 #pragma unroll
-        for (int k = 0; k < PER; k++)
-            t[k] = src[min(tid + k * kThreads, N4 - 1)];
+        for (int k = 0; k < NC; k++) {
+            const int c = min(c0 + k * TPG, kLutCodes - 1);
+            const float *w = c < kCodes8 ? cb8 + c * 8 : cb4 + (c - kCodes8) * 8;
+            w0[k] = *reinterpret_cast<const float4 *>(w);
+            w1[k] = *reinterpret_cast<const float4 *>(w + 4);
+        }
 #pragma unroll
-        for (int k = 0; k < PER; k++)
-            if (tid + k * kThreads < N4)
-                reinterpret_cast<float4 *>(lut)[tid + k * kThreads] = t[k];
+        for (int h = 0; h < NH; h++)
+            qv[h] = *reinterpret_cast<const uint4 *>(qrow + h * D + 8 * g);
     }
     // Query operand of the key MFMA: lane h + 16 r takes dims 16 b + 4 r ..
-    // +3 of head h (zero for h >= NH): the scaled fp16 query of the
-    // preparation kernel, or the bf16 query itself for bf16 keys.
-    QOperand<D, DENSE> qo;
-    float lsc = a.sigma * kLog2e;
+    // +3 of head h (zero for h >= NH), as bf16 (bf16 keys) or as fp16
+    // scaled by 2^-e_h with the head's largest |q| in [2^14, 2^15).
+    u32x2 qraw[D / 16];
 #pragma unroll
     for (int b = 0; b < D / 16; b++) {
-        u32x2 v = {0u, 0u};
-        if (L.hl < NH) {
-            const uint16_t *src = DENSE ? a.q + ((size_t)s * a.Hq + (size_t)hkv * NH + L.hl) * D
-                                        : a.qh + ((size_t)row * NH + L.hl) * D;
-            v = *reinterpret_cast<const u32x2 *>(src + 16 * b + 4 * L.r);
-        }
-        qo.blk[b] = __builtin_bit_cast(typename QOperand<D, DENSE>::T, v);
+        qraw[b] = u32x2{0u, 0u};
+        if (L.hl < NH)
+            qraw[b] = *reinterpret_cast<const u32x2 *>(qrow + (size_t)L.hl * D + 16 * b + 4 * L.r);
     }
-    if (!DENSE && L.hl < NH)
-        lsc = a.lsc[(size_t)row * NH + L.hl];
+    // per-head max |q| (each wave on its own: lane j holds 8 dims of head j / (D/8))
+    int eh = 0;
+    if constexpr (!DENSE) {
+        constexpr int LPH = D / 8; // lanes per head
+        float mx = 0.f;
+        if (lane < NH * LPH) {
+            const uint4 v = *reinterpret_cast<const uint4 *>(qrow + 8 * lane);
+            const uint32_t u[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+            for (int e = 0; e < 4; e++)
+                mx = fmaxf(mx, fmaxf(fabsf(bf16_lo(u[e])), fabsf(bf16_hi(u[e]))));
+        }
+#pragma unroll
+        for (int o = 1; o < LPH; o <<= 1)
+            mx = fmaxf(mx, __shfl_xor(mx, o, 64));
+#pragma unroll
+        for (int h = 0; h < NH; h++) {
+            const float m = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(mx), h * LPH));
+            int ex = 0;
+            if (m > 0.f) {
+                frexpf(m, &ex);
+                ex -= 15;
+            }
+            eh = L.hl == h ? ex : eh;
+        }
+    }
+    QOperand<D, DENSE> qo;
+#pragma unroll
+    for (int b = 0; b < D / 16; b++) {
+        if constexpr (DENSE) {
+            qo.blk[b] = __builtin_bit_cast(s16x4, qraw[b]);
+        } else {
+            f16x4 o;
+            o[0] = (_Float16)ldexpf(bf16_lo(qraw[b].x), -eh);
+            o[1] = (_Float16)ldexpf(bf16_hi(qraw[b].x), -eh);
+            o[2] = (_Float16)ldexpf(bf16_lo(qraw[b].y), -eh);
+            o[3] = (_Float16)ldexpf(bf16_hi(qraw[b].y), -eh);
+            qo.blk[b] = o;
+        }
+    }
+    const float lsc = ldexpf(a.sigma, eh) * kLog2e;
+#pragma unroll
+    for (int j = 0; j < TE; j++)
+        if (tid + j * kThreads < n_wg)
+            tbl[tid + j * kThreads] = make_uint2(te_off[j], te_meta[j]);
+    for (int k = tid + TE * kThreads; k < n_wg; k += kThreads) {
+        const int p = split + k * a.nsplit;
+        tbl[k] = make_uint2(pt[p], pm[p]);
+    }
+    if constexpr (!DENSE) {
+        // LUT[g][c][h] = q_h[8g .. 8g+8) . C[g][c] (c < 256 from cb8, else cb4)
+        float qq[NH][8];
+#pragma unroll
+        for (int h = 0; h < NH; h++) {
+            const uint32_t u[4] = {qv[h].x, qv[h].y, qv[h].z, qv[h].w};
+#pragma unroll
+            for (int e = 0; e < 4; e++) {
+                qq[h][2 * e] = bf16_lo(u[e]);
+                qq[h][2 * e + 1] = bf16_hi(u[e]);
+            }
+        }
+#pragma unroll
+        for (int k = 0; k < NC; k++) {
+            const int c = c0 + k * TPG;
+            if (c < kLutCodes) {
+                float o[NH];
+#pragma unroll
+                for (int h = 0; h < NH; h++) {
+                    float acc = qq[h][0] * w0[k].x;
+                    acc = fmaf(qq[h][1], w0[k].y, acc);
+                    acc = fmaf(qq[h][2], w0[k].z, acc);
+                    acc = fmaf(qq[h][3], w0[k].w, acc);
+                    acc = fmaf(qq[h][4], w1[k].x, acc);
+                    acc = fmaf(qq[h][5], w1[k].y, acc);
+                    acc = fmaf(qq[h][6], w1[k].z, acc);
+                    acc = fmaf(qq[h][7], w1[k].w, acc);
+                    o[h] = acc;
+                }
+                float *dst = lut + (g * kLutCodes + c) * NH;
+                if constexpr (NH == 4)
+                    *reinterpret_cast<float4 *>(dst) = make_float4(o[0], o[1], o[2], o[3]);
+                else if constexpr (NH == 2)
+                    *reinterpret_cast<float2 *>(dst) = make_float2(o[0], o[1]);
+                else
+                    dst[0] = o[0];
+            }
+        }
+    }
     const float sig2 = a.sigma * kLog2e;
 
     __syncthreads();
@@ -673,93 +697,106 @@ __global__ __launch_bounds__(kThreads) void decode_main(DecodeArgs a)
 }
 
 // ---- split merge --------------------------------------------------------------
-// One workgroup per row: out = sum_i acc_i 2^(m_i - m) / sum_i l_i 2^(m_i - m)
-// over the row's splits, lse = (m + log2 of the denominator) in nats.  The
-// partials come from the page-stream kernel before it in the stream.
+// One workgroup per (row, query head): out = sum_i acc_i 2^(m_i - m) /
+// sum_i l_i 2^(m_i - m) over the row's splits (m = max m_i, empty splits
+// with m_i = -inf skipped), lse = (m + log2 of the denominator) in nats.
+// The partials come from the page-stream kernel before it in the stream.
+// The first batch of partial columns is loaded together with the (m, l)
+// pairs, so the merge costs about one memory latency.
 constexpr int kMergeThreads = 256;
+constexpr int kMergeBatch = 8;
 
 template <int D, int NH>
 __global__ __launch_bounds__(kMergeThreads) void decode_merge(DecodeArgs a)
 {
-    extern __shared__ float smem[];
-    const int row = blockIdx.x, tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    constexpr int ITEMS = D / 4;                 // 4-float columns of one head
+    constexpr int KS = kMergeThreads / ITEMS;    // threads per column
+    __shared__ float sm[kMaxSplitsDev], sl[kMaxSplitsDev];
+    __shared__ float swave[kMergeThreads / 64][2];
+    __shared__ float4 scol[KS][ITEMS];
+    const int row = blockIdx.x, h = blockIdx.y, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int s = row / a.Hkv, hkv = row % a.Hkv;
     const int ns = a.nsplit;
-    constexpr int ITEMS = NH * D / 4;            // (head, 4 dims) items
-    constexpr int KS = kMergeThreads / ITEMS;    // threads per item
-    float *sm = smem;           // [ns][NH]
-    float *sf = sm + ns * NH;   // [ns][NH] weights 2^(m_i - m*)
-    float *sl = sf + ns * NH;   // [ns][NH]
-    float *smax = sl + ns * NH; // [NH]
-    float *ssum = smax + NH;    // [NH]
-    float *scol = ssum + NH;    // [KS][NH][D]
-    const size_t base = (size_t)row * ns * NH;
-    for (int i = tid; i < ns * NH; i += kMergeThreads) {
-        const float2 ml = *reinterpret_cast<const float2 *>(a.part_ml + (base + i) * 2);
-        sm[i] = ml.x;
-        sl[i] = ml.y;
+    const int item = tid % ITEMS, part_i = tid / ITEMS;
+    const size_t base = (size_t)row * ns * NH + h;  // split k of this head: base + k * NH
+    const float *acc = a.part_acc + base * D + 4 * item;
+
+    float4 v[kMergeBatch];
+#pragma unroll
+    for (int j = 0; j < kMergeBatch; j++)
+        v[j] = *reinterpret_cast<const float4 *>(acc + (size_t)min(part_i + j * KS, ns - 1) * NH * D);
+    float mx = -INFINITY;
+    for (int k = tid; k < ns; k += kMergeThreads) {
+        const float2 ml = *reinterpret_cast<const float2 *>(a.part_ml + (base + (size_t)k * NH) * 2);
+        sm[k] = ml.x;
+        sl[k] = ml.y;
+        mx = fmaxf(mx, ml.x);
     }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1)
+        mx = fmaxf(mx, __shfl_xor(mx, o, 64));
+    if (lane == 0)
+        swave[wave][0] = mx;
     __syncthreads();
-    if (wave < NH) {
-        const int h = wave;
-        float mx = -INFINITY;
-        for (int k = lane; k < ns; k += 64)
-            mx = fmaxf(mx, sm[k * NH + h]);
+    mx = swave[0][0];
 #pragma unroll
-        for (int o = 32; o >= 1; o >>= 1)
-            mx = fmaxf(mx, __shfl_xor(mx, o, 64));
-        float l = 0.f;
-        for (int k = lane; k < ns; k += 64) {
-            const float m = sm[k * NH + h];
-            const float f = m > -INFINITY ? __builtin_amdgcn_exp2f(m - mx) : 0.f;
-            sf[k * NH + h] = f;
-            l = fmaf(sl[k * NH + h], f, l);
-        }
-#pragma unroll
-        for (int o = 32; o >= 1; o >>= 1)
-            l += __shfl_xor(l, o, 64);
-        if (lane == 0) {
-            smax[h] = mx;
-            ssum[h] = l;
-        }
+    for (int w = 1; w < kMergeThreads / 64; w++)
+        mx = fmaxf(mx, swave[w][0]);
+    // weights 2^(m_i - m) in place of m_i, and the denominator
+    float l = 0.f;
+    for (int k = tid; k < ns; k += kMergeThreads) {
+        const float m = sm[k];
+        const float f = m > -INFINITY ? __builtin_amdgcn_exp2f(m - mx) : 0.f;
+        sm[k] = f;
+        l = fmaf(sl[k], f, l);
     }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1)
+        l += __shfl_xor(l, o, 64);
+    if (lane == 0)
+        swave[wave][1] = l;
     __syncthreads();
-    {
-        // KS threads share an item, each summing every KS-th split, 8 splits
-        // per batch with all loads in flight
-        const int item = tid % ITEMS, part_i = tid / ITEMS;
-        const int h = item / (D / 4), d4 = item % (D / 4);
-        float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
-        const float *src = a.part_acc + (base + h) * D + 4 * d4;
-        for (int k0 = part_i; k0 < ns; k0 += 8 * KS) {
-            float4 v[8];
+    l = 0.f;
 #pragma unroll
-            for (int j = 0; j < 8; j++)
-                v[j] = *reinterpret_cast<const float4 *>(src + (size_t)min(k0 + j * KS, ns - 1) * NH * D);
+    for (int w = 0; w < kMergeThreads / 64; w++)
+        l += swave[w][1];
+
+    float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int k0 = part_i;; ) {
 #pragma unroll
-            for (int j = 0; j < 8; j++) {
-                const int k = k0 + j * KS;
-                const float f = k < ns ? sf[k * NH + h] : 0.f;
-                o.x = fmaf(v[j].x, f, o.x);
-                o.y = fmaf(v[j].y, f, o.y);
-                o.z = fmaf(v[j].z, f, o.z);
-                o.w = fmaf(v[j].w, f, o.w);
-            }
+        for (int j = 0; j < kMergeBatch; j++) {
+            const int k = k0 + j * KS;
+            const float f = k < ns ? sm[k] : 0.f;
+            o.x = fmaf(v[j].x, f, o.x);
+            o.y = fmaf(v[j].y, f, o.y);
+            o.z = fmaf(v[j].z, f, o.z);
+            o.w = fmaf(v[j].w, f, o.w);
         }
-        *reinterpret_cast<float4 *>(scol + ((size_t)part_i * NH + h) * D + 4 * d4) = o;
-    }
-    __syncthreads();
-    for (int i = tid; i < NH * D; i += kMergeThreads) {
-        const int h = i / D, d = i - h * D;
-        float o = 0.f;
+        k0 += kMergeBatch * KS;
+        if (k0 >= ns)
+            break;
 #pragma unroll
-        for (int k = 0; k < KS; k++)
-            o += scol[((size_t)k * NH + h) * D + d];
-        const float mx = smax[h], l = ssum[h];
+        for (int j = 0; j < kMergeBatch; j++)
+            v[j] = *reinterpret_cast<const float4 *>(acc + (size_t)min(k0 + j * KS, ns - 1) * NH * D);
+    }
+    scol[part_i][item] = o;
+    __syncthreads();
+    if (tid < ITEMS) {
+        float4 t = scol[0][tid];
+#pragma unroll
+        for (int k = 1; k < KS; k++) {
+            t.x += scol[k][tid].x;
+            t.y += scol[k][tid].y;
+            t.z += scol[k][tid].z;
+            t.w += scol[k][tid].w;
+        }
+        const bool any = mx > -INFINITY;
+        const float inv = any ? 1.f / l : 0.f;
         const size_t sh = (size_t)s * a.Hq + (size_t)hkv * NH + h;
-        a.out[sh * D + d] = mx > -INFINITY ? o / l : 0.f;
-        if (a.lse != nullptr && d == 0)
-            a.lse[sh] = mx > -INFINITY ? (mx + __log2f(l)) * kLn2 : -INFINITY;
+        *reinterpret_cast<float4 *>(a.out + sh * D + 4 * tid) =
+            make_float4(t.x * inv, t.y * inv, t.z * inv, t.w * inv);
+        if (a.lse != nullptr && tid == 0)
+            a.lse[sh] = any ? (mx + __log2f(l)) * kLn2 : -INFINITY;
     }
 }
 
@@ -770,13 +807,6 @@ size_t shmem_bytes(int max_wg_pages)
     const size_t b = lut + (size_t)max_wg_pages * sizeof(uint2);
     const size_t red = ((size_t)kWaves * D * 4 + (size_t)kWaves * NH * 2) * sizeof(float);
     return b > red ? b : red;
-}
-
-template <int D, int NH>
-size_t merge_shmem_bytes(int nsplit)
-{
-    constexpr int KS = kMergeThreads / (NH * D / 4);
-    return ((size_t)3 * nsplit * NH + 2 * NH + (size_t)KS * NH * D) * sizeof(float);
 }
 
 template <int D, int NH, bool DENSE>
@@ -794,12 +824,6 @@ hipError_t launch_t(const DecodeArgs &a, hipStream_t st, unsigned stages)
             return e;
         attr_set = shmem;
     }
-    if (!DENSE && (stages & kStagePrep)) {
-        hipLaunchKernelGGL((decode_prep<D, NH>), dim3(rows, D / 8 + 1), dim3(kPrepThreads), 0, st, a);
-        hipError_t e = hipGetLastError();
-        if (e != hipSuccess)
-            return e;
-    }
     hipError_t e = hipSuccess;
     if (stages & kStageStream) {
         hipLaunchKernelGGL((decode_main<D, NH, DENSE>), dim3(rows * a.nsplit), dim3(kThreads), shmem, st, a);
@@ -807,16 +831,7 @@ hipError_t launch_t(const DecodeArgs &a, hipStream_t st, unsigned stages)
     }
     if (e != hipSuccess || a.nsplit == 1 || !(stages & kStageMerge))
         return e;
-    const size_t mshmem = merge_shmem_bytes<D, NH>(a.nsplit);
-    static size_t mattr_set = 0;
-    if (mshmem > mattr_set) {
-        e = hipFuncSetAttribute((const void *)decode_merge<D, NH>,
-                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)mshmem);
-        if (e != hipSuccess)
-            return e;
-        mattr_set = mshmem;
-    }
-    hipLaunchKernelGGL((decode_merge<D, NH>), dim3(rows), dim3(kMergeThreads), mshmem, st, a);
+    hipLaunchKernelGGL((decode_merge<D, NH>), dim3(rows, NH), dim3(kMergeThreads), 0, st, a);
     return hipGetLastError();
 }
 
@@ -826,11 +841,8 @@ size_t decode_shmem_bytes(int D, int NH, bool dense, int nsplit, int maxp)
 {
     const int wg = (maxp + nsplit - 1) / nsplit;
 #define ADA_CASE(DD, NN)                                                                          \
-    if (D == DD && NH == NN) {                                                                    \
-        const size_t m = merge_shmem_bytes<DD, NN>(nsplit);                                       \
-        const size_t k = dense ? shmem_bytes<DD, NN, true>(wg) : shmem_bytes<DD, NN, false>(wg);  \
-        return k > m ? k : m;                                                                     \
-    }
+    if (D == DD && NH == NN)                                                                      \
+        return dense ? shmem_bytes<DD, NN, true>(wg) : shmem_bytes<DD, NN, false>(wg);
     ADA_CASE(64, 1)
     ADA_CASE(64, 2)
     ADA_CASE(64, 4)

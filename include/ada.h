@@ -188,8 +188,7 @@ int32_t ada_decode_default_splits(const ada_geom *geom, int32_t num_seqs,
                                   int32_t max_pages_per_head);
 
 /* Workspace bytes of ada_decode / dense_decode with this many splits
- * (0 = the default).  The workspace holds each row's code tables and scaled
- * query, and the per-split partial results. */
+ * (0 = the default).  The workspace holds the per-split partial results. */
 size_t ada_decode_workspace_size(const ada_geom *geom, int32_t num_seqs,
                                  int32_t max_pages_per_head, int32_t num_splits);
 
@@ -216,9 +215,9 @@ size_t ada_decode_workspace_size(const ada_geom *geom, int32_t num_seqs,
  *   ws: ada_decode_workspace_size(geom, S, max_pages_per_head, num_splits)
  *     bytes, 256-byte aligned, any content: every call writes what it
  *     reads.  Calls that overlap in time must not share a workspace.
- * The step is up to three kernels on `stream`: a per-row preparation
- * (code tables, scaled query; ada_decode only), the page stream, and a
- * split merge when num_splits > 1.
+ * The step is up to two kernels on `stream`: the page stream (which also
+ * tabulates each row's code tables in LDS) and a split merge when
+ * num_splits > 1.
  * Cache pages must be tiers 0-2.  Queries must be finite with |q| < 2^64.
  */
 ada_status ada_decode(const ada_geom *geom, const ada_cache *cache, const float *cb8,
@@ -227,19 +226,15 @@ ada_status ada_decode(const ada_geom *geom, const ada_cache *cache, const float 
                       size_t ws_bytes, void *stream);
 
 /*
- * The three stages of ada_decode, for callers that time or schedule them
+ * The two stages of ada_decode, for callers that time or schedule them
  * apart.  Each takes the arguments of ada_decode (unused ones may be NULL);
  * called in this order on one stream with the same arguments and workspace
  * they do exactly what one ada_decode call does.
- *   ada_decode_prepare: the row code tables and scaled queries, into ws.
- *   ada_decode_stream:  the page stream; writes the split partials into ws
+ *   ada_decode_stream: the page stream; writes the split partials into ws
  *     (or out / lse / logits_dbg directly when num_splits resolves to 1).
- *   ada_decode_merge:   combines the partials into out / lse; enqueues
+ *   ada_decode_merge:  combines the partials into out / lse; enqueues
  *     nothing when num_splits resolves to 1.
  */
-ada_status ada_decode_prepare(const ada_geom *geom, const ada_cache *cache, const float *cb8,
-                              const float *cb4, const uint16_t *q, float softmax_scale, float *out,
-                              int32_t num_splits, void *ws, size_t ws_bytes, void *stream);
 ada_status ada_decode_stream(const ada_geom *geom, const ada_cache *cache, const float *cb8,
                              const float *cb4, const uint16_t *q, float softmax_scale, float *out,
                              float *lse, float *logits_dbg, int32_t num_splits, void *ws,

@@ -60,7 +60,7 @@ def test_decode_tiny_workload(splits):
 
 @pytest.mark.parametrize("splits", [1, 4])
 def test_decode_stages_equal_one_call(splits):
-    """ada_decode_prepare + _stream + _merge on one stream give exactly the
+    """ada_decode_stream + ada_decode_merge on one stream give exactly the
     outputs of one ada_decode call (same kernels, same order)."""
     cfg = small_workload(D=128, Hq=8, Hkv=2, S=3, T=700, seed=61)
     case = make_case(cfg, lens=[700, 333, 90], mixes=[(1500, 6000, 8500)] * 3)
@@ -73,7 +73,7 @@ def test_decode_stages_equal_one_call(splits):
     ada.decode(geom, dc, d["cb8"], d["cb4"], d["q"], cfg.sigma, out1, lse1, lg1, num_splits=splits)
     out2, lse2, lg2 = decode_outputs(geom, dc, d["q"])
     ws = None
-    for st in ("prepare", "stream", "merge"):
+    for st in ("stream", "merge"):
         ws = ada.decode_stage(st, geom, dc, d["cb8"], d["cb4"], d["q"], cfg.sigma, out2, lse2, lg2,
                               num_splits=splits, ws=ws)
     torch.cuda.synchronize()
