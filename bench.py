@@ -195,6 +195,48 @@ def cpu_baseline(cfg, layer, seconds_target=10.0):
                 single_thread_value=tokens / (t1 * units)), res
 
 
+def append_path(dev, reps=20):
+    """Times the append path on the 32-layer workload's shape: ada_encode and
+    rdr_pack of 512 new tokens for each of 8 sequences (one layer), into a
+    cache that already holds a first chunk of those sequences."""
+    cfg = synth.WORKLOADS[5]
+    S, H, D, n = cfg.num_seqs, cfg.num_kv_heads, cfg.head_dim, cfg.append_tokens
+    geom = ada.Geom(D, cfg.num_q_heads, H)
+    cb8, cb4 = (t.to(dev) for t in synth.codebooks(cfg, 0))
+    bp = synth.tier_mix(cfg)
+    cu = synth.cu_tokens(np.full(S, n, np.int64))
+    keys = synth.keys(cfg, 0, S * n, dev, stream="k-append")
+    vals = synth.values(cfg, 0, S * n, dev, stream="v-append")
+    scores = synth.scores(cfg, 0, S * n, stream="score-append").to(dev)
+    r = torch.empty((S * n, H), dtype=torch.float16, device=dev)
+    c8 = torch.empty((S * n, H, D // 8), dtype=torch.uint8, device=dev)
+    c4 = torch.empty((S * n, H, D // 16), dtype=torch.uint8, device=dev)
+    per_call = S * H * (n // 16 + 3) * ada.page_bytes(D, 0)  # a bound: every page at the largest size
+    cache = ada.Cache(geom, S, (reps + 2) * (n // 16 + 3), per_call * (reps + 2))
+    ws = torch.zeros(ada.pack_workspace_size(geom, S * n, S), dtype=torch.uint8, device=dev)
+    pos = np.zeros(S, np.int64)
+    ada.encode(geom, keys, cb8, cb4, r, c8, c4)
+    ada.rdr_pack(geom, cache, cu, bp, keys, vals, r, c8, c4, scores, pos_base=pos, ws=ws)
+    torch.cuda.synchronize()
+    e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+    enc, pack = 0.0, 0.0
+    for i in range(reps):
+        pos += n
+        e[0].record()
+        ada.encode(geom, keys, cb8, cb4, r, c8, c4)
+        e[1].record()
+        ada.rdr_pack(geom, cache, cu, bp, keys, vals, r, c8, c4, scores, pos_base=pos, ws=ws)
+        e[2].record()
+        torch.cuda.synchronize()
+        enc += e[0].elapsed_time(e[1])
+        pack += e[1].elapsed_time(e[2])
+    th = S * n * H
+    return {"workload": f"{cfg.name} append, one layer", "tokens": S * n, "token_heads": th,
+            "encode_us": enc / reps * 1e3, "pack_us": pack / reps * 1e3,
+            "token_heads_per_s": th / ((enc + pack) / reps / 1e3),
+            "note": "pack includes its host plan and the plan's host-to-device copy"}
+
+
 def stream_bytes(L):
     """Bytes the page-stream kernel must read from HBM per launch: the stored
     pages and their page-table entries (4 B offset + 1 B metadata)."""
@@ -240,6 +282,7 @@ def main():
     ap.add_argument("--splits", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
+    ap.add_argument("--no-append", action="store_true", help="skip the append-path timing")
     ap.add_argument("--eager", action="store_true",
                     help="time eager launches instead of graph replays (for profilers)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
@@ -348,6 +391,10 @@ def main():
                                          "ada_speedup": dms / ms_graph}
         del darenas
     torch.cuda.synchronize()
+    if not args.no_append:
+        result["append_path"] = append_path(dev)
+        log(f"append path: encode {result['append_path']['encode_us']:.1f} us, "
+            f"pack {result['append_path']['pack_us']:.1f} us per layer")
     # numerics check of the timed outputs against the oracle (CPU baseline leg)
     if not args.no_cpu_baseline:
         cb = cpu_baseline(cfg, 0)
