@@ -25,7 +25,7 @@ bool geom_ok(const ada_geom *g)
 bool gqa_supported(const ada_geom *g)
 {
     const int r = g->num_q_heads / g->num_kv_heads;
-    return r == 1 || r == 2 || r == 4;
+    return r == 1 || r == 2 || r == 4 || r == 5 || r == 8;
 }
 
 bool cache_ok(const ada_cache *c)
@@ -245,12 +245,16 @@ int32_t default_splits(const ada_geom *g, int32_t S, int32_t maxp)
     const int64_t rows = (int64_t)S * g->num_kv_heads;
     if (rows <= 0)
         return 1;
-    // about one workgroup per compute unit, at least 16 pages per split, and
-    // at most 8192 pages per split (their table entries are staged in LDS)
+    // about one workgroup per compute unit and at least 16 pages per split,
+    // with few enough pages per split that their table entries fit in LDS
+    // beside the group's LUT
     int64_t n = (256 + rows - 1) / rows;
     n = std::min<int64_t>(n, std::max<int64_t>(1, maxp / 16));
-    n = std::max<int64_t>(n, (maxp + 8191) / 8192);
-    return (int32_t)std::max<int64_t>(1, std::min<int64_t>(n, kMaxSplits));
+    n = std::max<int64_t>(n, 1);
+    const int NH = g->num_q_heads / g->num_kv_heads;
+    while (n < kMaxSplits && decode_shmem_bytes(g->head_dim, NH, false, (int)n, maxp) > kMaxLds)
+        n++;
+    return (int32_t)std::min<int64_t>(n, kMaxSplits);
 }
 
 ada_status decode_common(const ada_geom *g, const ada_cache *c, const float *cb8, const float *cb4,

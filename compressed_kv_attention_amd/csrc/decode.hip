@@ -27,8 +27,8 @@
 //     block held in registers; the result lands in the tile layout.
 //   - coded pages: lane j + 16 r sums the LUT entries of slot 4r + j/4 over
 //     a quarter of the groups, a quad reduction completes each slot, and
-//     three DPP row rotations move head h's values of the row's four slots
-//     into lane h + 16 r; the radii scale them there.
+//     DPP row rotations (three per quad of heads) move head h's values of
+//     the row's four slots into lane h + 16 r; the radii scale them there.
 // The softmax runs on that tile (running maxima per head, rescaled only
 // when a page's maximum exceeds the running one by 2^8, so every weight is
 // at most 2^8), and the weights are split into bf16 hi + lo parts (about
@@ -36,7 +36,7 @@
 // sections are stored as the B operand (lane n + 16 r: slots 4r .. 4r+3 of
 // dim n); int8 values become bf16 exactly, and their per-slot scales are
 // folded into the weights.  The output accumulators are the MFMA C tiles
-// (rows = heads, so lanes 0-15 hold the outputs of one dim each).
+// (rows = heads: element h % 4 of lane 16 (h / 4) + n holds dim n of head h).
 //
 // At the end the 12 waves are merged through LDS and the split's partial
 // (m, l, acc) is written; the merge kernel combines a row's splits into the
@@ -104,18 +104,48 @@ __device__ __forceinline__ float rows_sum(float x)
 // are outstanding (expcnt and lgkmcnt left at their maxima).
 constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
 
+// Heads of a GQA group: NH = 4 NQF + REM.  The LUT holds NQF regions of
+// [G][kLutCodes] float4 entries (heads 4 j .. 4 j + 3), then one region of
+// [G][kLutCodes][REM] floats for the remaining heads, so every lookup is
+// one aligned LDS read per region.
 template <int NH>
+struct Heads {
+    static_assert(NH >= 1 && NH <= 8 && NH % 4 != 3, "GQA group of 1, 2, 4, 5, 6 or 8 query heads");
+    static constexpr int NQF = NH / 4, REM = NH % 4;
+    static constexpr int NQ = (NH + 3) / 4; // head quads of the output tile
+};
+
+template <int NH, int G>
 __device__ __forceinline__ void lut_add(const float *lut, int idx, float (&sum)[NH])
 {
-    if constexpr (NH == 4) {
-        float4 v = *reinterpret_cast<const float4 *>(lut + idx * 4);
-        sum[0] += v.x; sum[1] += v.y; sum[2] += v.z; sum[3] += v.w;
-    } else if constexpr (NH == 2) {
-        float2 v = *reinterpret_cast<const float2 *>(lut + idx * 2);
-        sum[0] += v.x; sum[1] += v.y;
-    } else {
-        sum[0] += lut[idx];
+    constexpr int NQF = Heads<NH>::NQF, REM = Heads<NH>::REM;
+    constexpr int REGION = G * kLutCodes * 4; // floats of one head-quad region
+#pragma unroll
+    for (int j = 0; j < NQF; j++) {
+        const float4 v = *reinterpret_cast<const float4 *>(lut + j * REGION + idx * 4);
+        sum[4 * j] += v.x; sum[4 * j + 1] += v.y; sum[4 * j + 2] += v.z; sum[4 * j + 3] += v.w;
     }
+    if constexpr (REM == 2) {
+        const float2 v = *reinterpret_cast<const float2 *>(lut + NQF * REGION + idx * 2);
+        sum[4 * NQF] += v.x; sum[4 * NQF + 1] += v.y;
+    } else if constexpr (REM == 1) {
+        sum[4 * NQF] += lut[NQF * REGION + idx];
+    }
+}
+
+template <int NH, int G>
+__device__ __forceinline__ void lut_store(float *lut, int idx, const float (&o)[NH])
+{
+    constexpr int NQF = Heads<NH>::NQF, REM = Heads<NH>::REM;
+    constexpr int REGION = G * kLutCodes * 4;
+#pragma unroll
+    for (int j = 0; j < NQF; j++)
+        *reinterpret_cast<float4 *>(lut + j * REGION + idx * 4) =
+            make_float4(o[4 * j], o[4 * j + 1], o[4 * j + 2], o[4 * j + 3]);
+    if constexpr (REM == 2)
+        *reinterpret_cast<float2 *>(lut + NQF * REGION + idx * 2) = make_float2(o[4 * NQF], o[4 * NQF + 1]);
+    else if constexpr (REM == 1)
+        lut[NQF * REGION + idx] = o[4 * NQF];
 }
 
 // The bytes from offset o (0..15) of a 16-byte chunk up to the end of its
@@ -282,7 +312,7 @@ __device__ __forceinline__ void coded_logits(const PageRegs<D> &cur, const float
 #pragma unroll
     for (int k = 0; k < GPL; k++) {
         const int code = base + (int)__builtin_amdgcn_ubfe(bits, k * width, width);
-        lut_add<NH>(lut, (L.g0 + k) * kLutCodes + code, s);
+        lut_add<NH, D / 8>(lut, (L.g0 + k) * kLutCodes + code, s);
     }
     // complete each slot's sum over its four lanes (a quad)
 #pragma unroll
@@ -290,20 +320,28 @@ __device__ __forceinline__ void coded_logits(const PageRegs<D> &cur, const float
         s[h] += dpp<0xb1>(s[h]); // quad_perm [1,0,3,2]
         s[h] += dpp<0x4e>(s[h]); // quad_perm [2,3,0,1]
     }
-    // lane j of a row offers head (j % 4) of its slot; lane h (< 4) of the
-    // row then collects head h of slots 4r + e from lanes 4e + h
-    float sel = s[0];
-    if constexpr (NH >= 2)
-        sel = (L.gq & 1) ? s[1] : sel;
-    if constexpr (NH == 4) {
-        sel = L.gq == 2 ? s[2] : sel;
-        sel = L.gq == 3 ? s[3] : sel;
-    }
+    // For head quad q, lane j of a row offers head 4 q + j % 4 of its slot;
+    // lane 4 q + i of the row then collects head 4 q + i of slots 4 r + e
+    // from lane 4 e + i, a rotation of the row by 4 (q - e) lanes.
+    constexpr int NQ = Heads<NH>::NQ;
     float v[4];
-    v[0] = sel;
-    v[1] = dpp<0x12c>(sel); // row_ror:12 -> lane + 4
-    v[2] = dpp<0x128>(sel); // row_ror:8  -> lane + 8
-    v[3] = dpp<0x124>(sel); // row_ror:4  -> lane + 12
+#pragma unroll
+    for (int q = 0; q < NQ; q++) {
+        // (the loop is unrolled, so the head bounds fold away)
+        float sel = s[4 * q];
+        if (4 * q + 1 < NH)
+            sel = (L.gq & 1) ? s[min(4 * q + 1, NH - 1)] : sel;
+        if (4 * q + 2 < NH)
+            sel = L.gq == 2 ? s[min(4 * q + 2, NH - 1)] : sel;
+        if (4 * q + 3 < NH)
+            sel = L.gq == 3 ? s[min(4 * q + 3, NH - 1)] : sel;
+        // row_ror:n moves lane i - n to lane i
+        const float r0 = sel, r4 = dpp<0x124>(sel), r8 = dpp<0x128>(sel), r12 = dpp<0x12c>(sel);
+        const float vq[4] = {q == 0 ? r0 : r4, q == 0 ? r12 : r0, q == 0 ? r8 : r12, q == 0 ? r4 : r8};
+#pragma unroll
+        for (int e = 0; e < 4; e++)
+            v[e] = (q == 0 || (L.hl >> 2) == q) ? vq[e] : v[e];
+    }
     float rad[4];
     quad_f16(cur.c[NV + 1], L.r, rad);
 #pragma unroll
@@ -350,19 +388,34 @@ __device__ __forceinline__ void process_page(PageRegs<D> &cur, int p, WaveState<
     // pm = -inf and never do), the per-head rescale only then
     const float pm = rows_max(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])));
     if (__builtin_amdgcn_ballot_w64(pm > st.mlane + kRescale) != 0) {
+        // head h's outputs are element h % 4 of the C tiles in lanes
+        // 16 (h / 4) .. 16 (h / 4) + 15
+        constexpr int NQ = Heads<NH>::NQ;
+        float fe[4] = {1.f, 1.f, 1.f, 1.f};
 #pragma unroll
         for (int h = 0; h < NH; h++) {
             const float pmh = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(pm), h));
             if (pmh > st.m[h] + kRescale) {
                 const float f = __builtin_amdgcn_exp2f(st.m[h] - pmh);
                 st.m[h] = pmh;
+                if constexpr (NQ == 1) {
 #pragma unroll
-                for (int b = 0; b < D / 16; b++)
-                    st.acc[b][h] *= f;
+                    for (int b = 0; b < D / 16; b++)
+                        st.acc[b][h] *= f;
+                } else {
+                    fe[h % 4] = L.r == h / 4 ? f : fe[h % 4];
+                }
                 const bool mine = L.hl == h;
                 st.l = mine ? st.l * f : st.l;
                 st.mlane = mine ? pmh : st.mlane;
             }
+        }
+        if constexpr (NQ > 1) {
+#pragma unroll
+            for (int b = 0; b < D / 16; b++)
+#pragma unroll
+                for (int e = 0; e < 4; e++)
+                    st.acc[b][e] *= fe[e];
         }
     }
     float w[4];
@@ -519,30 +572,35 @@ __global__ __launch_bounds__(kThreads) void decode_main(DecodeArgs a)
         if (L.hl < NH)
             qraw[b] = *reinterpret_cast<const u32x2 *>(qrow + (size_t)L.hl * D + 16 * b + 4 * L.r);
     }
-    // per-head max |q| (each wave on its own: lane j holds 8 dims of head j / (D/8))
+    // per-head max |q| (each wave on its own: in pass p lane j holds 8 dims
+    // of head p HPP + j / (D/8))
     int eh = 0;
     if constexpr (!DENSE) {
-        constexpr int LPH = D / 8; // lanes per head
-        float mx = 0.f;
-        if (lane < NH * LPH) {
-            const uint4 v = *reinterpret_cast<const uint4 *>(qrow + 8 * lane);
-            const uint32_t u[4] = {v.x, v.y, v.z, v.w};
+        constexpr int LPH = D / 8;   // lanes per head
+        constexpr int HPP = 64 / LPH; // heads per pass
 #pragma unroll
-            for (int e = 0; e < 4; e++)
-                mx = fmaxf(mx, fmaxf(fabsf(bf16_lo(u[e])), fabsf(bf16_hi(u[e]))));
-        }
+        for (int h0 = 0; h0 < NH; h0 += HPP) {
+            float mx = 0.f;
+            if (lane < (NH - h0 < HPP ? NH - h0 : HPP) * LPH) {
+                const uint4 v = *reinterpret_cast<const uint4 *>(qrow + (size_t)h0 * D + 8 * lane);
+                const uint32_t u[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
-        for (int o = 1; o < LPH; o <<= 1)
-            mx = fmaxf(mx, __shfl_xor(mx, o, 64));
-#pragma unroll
-        for (int h = 0; h < NH; h++) {
-            const float m = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(mx), h * LPH));
-            int ex = 0;
-            if (m > 0.f) {
-                frexpf(m, &ex);
-                ex -= 15;
+                for (int e = 0; e < 4; e++)
+                    mx = fmaxf(mx, fmaxf(fabsf(bf16_lo(u[e])), fabsf(bf16_hi(u[e]))));
             }
-            eh = L.hl == h ? ex : eh;
+#pragma unroll
+            for (int o = 1; o < LPH; o <<= 1)
+                mx = fmaxf(mx, __shfl_xor(mx, o, 64));
+#pragma unroll
+            for (int h = h0; h < NH && h < h0 + HPP; h++) {
+                const float m = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(mx), (h - h0) * LPH));
+                int ex = 0;
+                if (m > 0.f) {
+                    frexpf(m, &ex);
+                    ex -= 15;
+                }
+                eh = L.hl == h ? ex : eh;
+            }
         }
     }
     QOperand<D, DENSE> qo;
@@ -597,13 +655,7 @@ __global__ __launch_bounds__(kThreads) void decode_main(DecodeArgs a)
                     acc = fmaf(qq[h][7], w1[k].w, acc);
                     o[h] = acc;
                 }
-                float *dst = lut + (g * kLutCodes + c) * NH;
-                if constexpr (NH == 4)
-                    *reinterpret_cast<float4 *>(dst) = make_float4(o[0], o[1], o[2], o[3]);
-                else if constexpr (NH == 2)
-                    *reinterpret_cast<float2 *>(dst) = make_float2(o[0], o[1]);
-                else
-                    dst[0] = o[0];
+                lut_store<NH, G>(lut, g * kLutCodes + c, o);
             }
         }
     }
@@ -647,16 +699,17 @@ __global__ __launch_bounds__(kThreads) void decode_main(DecodeArgs a)
                                    lgout, a.maxp, L);
     }
 
-    // Waves -> LDS (the LUT space is free now): [wave][D][4] accumulators
+    // Waves -> LDS (the LUT space is free now): [wave][D][NHP] accumulators
     // (element h = head h) and [wave][h] (m, l).
+    constexpr int NHP = 4 * Heads<NH>::NQ;
     float *red = smem;
-    float *redml = smem + kWaves * D * 4;
+    float *redml = smem + kWaves * D * NHP;
     const float lsum = rows_sum(st.l);
     __syncthreads();
-    if (lane < 16) {
+    if (lane < 16 * Heads<NH>::NQ) {
 #pragma unroll
         for (int b = 0; b < D / 16; b++)
-            *reinterpret_cast<f32x4 *>(red + ((size_t)wave * D + 16 * b + lane) * 4) = st.acc[b];
+            *reinterpret_cast<f32x4 *>(red + ((size_t)wave * D + 16 * b + L.hl) * NHP + 4 * L.r) = st.acc[b];
     }
     if (lane < NH) {
         redml[(wave * NH + lane) * 2] = st.mlane;
@@ -678,7 +731,7 @@ __global__ __launch_bounds__(kThreads) void decode_main(DecodeArgs a)
         for (int w = 0; w < kWaves; w++) {
             const float mw = redml[(w * NH + h) * 2];
             const float f = mw > -INFINITY ? __builtin_amdgcn_exp2f(mw - mx) : 0.f;
-            o = fmaf(red[((size_t)w * D + d) * 4 + h], f, o);
+            o = fmaf(red[((size_t)w * D + d) * NHP + h], f, o);
             l = fmaf(redml[(w * NH + h) * 2 + 1], f, l);
         }
         if (a.nsplit == 1) {
@@ -805,7 +858,7 @@ size_t shmem_bytes(int max_wg_pages)
 {
     const size_t lut = DENSE ? 0 : (size_t)(D / 8) * kLutCodes * NH * sizeof(float);
     const size_t b = lut + (size_t)max_wg_pages * sizeof(uint2);
-    const size_t red = ((size_t)kWaves * D * 4 + (size_t)kWaves * NH * 2) * sizeof(float);
+    const size_t red = ((size_t)kWaves * D * 4 * Heads<NH>::NQ + (size_t)kWaves * NH * 2) * sizeof(float);
     return b > red ? b : red;
 }
 
@@ -846,9 +899,13 @@ size_t decode_shmem_bytes(int D, int NH, bool dense, int nsplit, int maxp)
     ADA_CASE(64, 1)
     ADA_CASE(64, 2)
     ADA_CASE(64, 4)
+    ADA_CASE(64, 5)
+    ADA_CASE(64, 8)
     ADA_CASE(128, 1)
     ADA_CASE(128, 2)
     ADA_CASE(128, 4)
+    ADA_CASE(128, 5)
+    ADA_CASE(128, 8)
 #undef ADA_CASE
     return 0;
 }
@@ -861,9 +918,13 @@ hipError_t launch_decode(int D, int NH, bool dense, const DecodeArgs &a, hipStre
     ADA_CASE(64, 1)
     ADA_CASE(64, 2)
     ADA_CASE(64, 4)
+    ADA_CASE(64, 5)
+    ADA_CASE(64, 8)
     ADA_CASE(128, 1)
     ADA_CASE(128, 2)
     ADA_CASE(128, 4)
+    ADA_CASE(128, 5)
+    ADA_CASE(128, 8)
 #undef ADA_CASE
     return hipErrorInvalidValue;
 }

@@ -74,7 +74,7 @@ int ada_version(void);
 typedef struct {
     int32_t head_dim;     /* D: 64 or 128 */
     int32_t num_q_heads;  /* Hq */
-    int32_t num_kv_heads; /* Hkv; Hq % Hkv == 0 and Hq / Hkv in {1, 2, 4} */
+    int32_t num_kv_heads; /* Hkv; Hq % Hkv == 0 and Hq / Hkv in {1, 2, 4, 5, 8} */
     int32_t page_size;    /* must be 16 */
 } ada_geom;
 
@@ -212,6 +212,9 @@ size_t ada_decode_workspace_size(const ada_geom *geom, int32_t num_seqs,
  *     tests, receives l_t of every valid slot (page p, slot t at p*16+t);
  *     other entries are left untouched.
  *   num_splits: page subsets per row, 1..1024 (0 = ada_decode_default_splits).
+ *     A count so small that a split's page-table entries and the row's code
+ *     tables overflow the 160 KiB of LDS gives ADA_EINVAL (the default
+ *     never does).
  *   ws: ada_decode_workspace_size(geom, S, max_pages_per_head, num_splits)
  *     bytes, 256-byte aligned, any content: every call writes what it
  *     reads.  Calls that overlap in time must not share a workspace.

@@ -1,10 +1,14 @@
 """Workload table for the ADA decode path, and the byte-budget -> tier-mix rule.
 
-Five seeded synthetic workloads stand in for the pages' evaluation (three
+Seven seeded synthetic workloads stand in for the pages' evaluation (three
 instruction-tuned LLMs at 8K/32K/128K contexts on long-document, multi-hop QA
 and agent-trajectory suites; gist.science technical summary of SPHERICAL KV,
 section 4).  No dataset or model weight is used: only shapes, lengths and the
-value distributions below.  Tier mixes are cumulative basis points
+value distributions below.  Workloads 1-5 use the Llama-3-8B attention shape;
+6 and 7 take the attention shapes of the other two models the pages name
+(Qwen2.5-14B: 40 query / 8 KV heads of 128 dims; gpt-oss-20b: 64 query / 8
+KV heads of 64 dims).  Those shapes come from the models' public
+configurations, not from the pages.  Tier mixes are cumulative basis points
 (fp16, fp16 + 8-bit, fp16 + 8-bit + 4-bit); the rest is dropped.
 """
 from __future__ import annotations
@@ -62,6 +66,10 @@ WORKLOADS = {
                 len_range=(4096, 65536), budget_range_bp=(4000, 8000), permuted_pool=True),
     5: Workload(5, "32layer-batch8-t128k", 8, 32, 32, 8, 128, 131072,
                 tier_cum_bp=(1500, 6000, 8500), append_tokens=512),
+    6: Workload(6, "qwen2.5-14b-shape-t32k", 1, 1, 40, 8, 128, 32768,
+                tier_cum_bp=(1500, 6000, 8500)),
+    7: Workload(7, "gpt-oss-20b-shape-t32k", 1, 1, 64, 8, 64, 32768,
+                tier_cum_bp=(1500, 6000, 8500)),
 }
 
 # Endpoints of the budget rule: cumulative bp of two mixes whose stored bytes

@@ -72,9 +72,9 @@ def test_host_argument_errors():
     view = ada._CacheView(0, 0, 0, 0, 0, 0, 0, 1, 4)
     assert L.ada_decode(C.byref(g), C.byref(view), None, None, None, 1.0, None, None, None, 0, None, 0,
                         None) == ada.EINVAL
-    g8 = ada.Geom(128, 64, 8)
+    g3 = ada.Geom(128, 24, 8)  # GQA ratio 3 is not built
     view = ada._CacheView(16, 1, 16, 16, 16, 16, 0, 1, 4)
-    assert L.ada_decode(C.byref(g8), C.byref(view), C.c_void_p(16), C.c_void_p(16), C.c_void_p(16), 1.0,
+    assert L.ada_decode(C.byref(g3), C.byref(view), C.c_void_p(16), C.c_void_p(16), C.c_void_p(16), 1.0,
                         C.c_void_p(16), None, None, 0, C.c_void_p(256), 1 << 20, None) == ada.EUNSUPPORTED
     # too small a workspace
     view = ada._CacheView(16, 1, 16, 16, 16, 16, 0, 1, 4)

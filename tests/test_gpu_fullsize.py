@@ -213,3 +213,11 @@ def test_workload4_ragged64_budgets():
 
 def test_workload5_one_layer_t128k_with_append():
     _run(5, 7, [2, 5], append=synth.WORKLOADS[5].append_tokens)
+
+
+def test_workload6_qwen_shape_gqa5_t32k():
+    _run(6, 0, [0])
+
+
+def test_workload7_gpt_oss_shape_gqa8_d64_t32k():
+    _run(7, 0, [0])

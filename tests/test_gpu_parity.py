@@ -83,7 +83,8 @@ def test_decode_stages_equal_one_call(splits):
     assert np.abs(out2.cpu().double().numpy() - ref["out"]).max() <= OUT_TOL
 
 
-@pytest.mark.parametrize("D,Hq,Hkv", [(128, 4, 2), (64, 8, 2), (128, 4, 4), (64, 2, 2)])
+@pytest.mark.parametrize("D,Hq,Hkv", [(128, 4, 2), (64, 8, 2), (128, 4, 4), (64, 2, 2),
+                                     (128, 10, 2), (64, 5, 1), (128, 16, 2), (64, 16, 2)])
 def test_decode_ragged_mixed_tiers(D, Hq, Hkv):
     cfg = small_workload(D=D, Hq=Hq, Hkv=Hkv, S=4, T=300, seed=40 + D + Hq)
     mixes = [(1500, 6000, 8500), (0, 0, 0), (10000, 10000, 10000), (0, 3000, 9000)]
@@ -91,6 +92,23 @@ def test_decode_ragged_mixed_tiers(D, Hq, Hkv):
     hc, _ = oracle_cache(case)
     for sp in (0, 1, 5):
         _check_decode(geom_of(cfg), hc, case, sp, f"ragged D={D} Hq={Hq} Hkv={Hkv}")
+
+
+@pytest.mark.parametrize("D,ratio", [(128, 5), (128, 8), (64, 8), (128, 4)])
+def test_decode_growing_logits_rescale_per_head(D, ratio):
+    """Keys grow along the sequence and each query head has its own scale,
+    so the running maxima of the heads of one group jump on different pages
+    (the rescale of one head must leave the others' accumulators alone)."""
+    cfg = small_workload(D=D, Hq=2 * ratio, Hkv=2, S=2, T=900, seed=70 + D + ratio)
+    case = make_case(cfg, lens=[900, 411], mixes=[(2000, 6000, 9000)] * 2)
+    N = case["N"]
+    grow = (1.0 + torch.arange(N, dtype=torch.float32) / 60.0).view(N, 1, 1)
+    case["keys"] = (case["keys"].float() * grow).to(torch.float16)
+    hs = (1.0 + 0.7 * torch.arange(cfg.num_q_heads, dtype=torch.float32)).view(1, -1, 1)
+    case["q"] = (case["q"].float() * hs).to(torch.bfloat16)
+    hc, _ = oracle_cache(case)
+    for sp in (1, 3):
+        _check_decode(geom_of(cfg), hc, case, sp, f"growing logits D={D} GQA {ratio}")
 
 
 @pytest.mark.parametrize("mix", [(10000, 10000, 10000), (0, 10000, 10000), (0, 0, 10000)])
