@@ -372,7 +372,7 @@ def main():
         "step_roofline": {"bytes_per_step": alg, "achieved_GBs": alg / (ms_graph / 1e3) / 1e9,
                           "frac": alg / (ms_graph / 1e3) / 1e9 / HBM_PEAK_GBS},
         "stored_bytes": used,
-        "stored_fraction_of_dense": used / (tokens * cfg.num_kv_heads * 512),
+        "stored_fraction_of_dense": used / (tokens * cfg.num_kv_heads * 4 * cfg.head_dim),
     }
     if "dense" in L:
         dc = L["dense"]

@@ -11,11 +11,12 @@
 //
 // Work decomposition.  A step is two kernels: the page stream and, with
 // more than one split per row, the split merge.  In the page stream one
-// workgroup (12 wave64s, one per CU at D = 128) serves one (sequence,
+// workgroup (12 wave64s, or 8 for groups of more than 4 heads at D = 128;
+// one workgroup per CU at D = 128) serves one (sequence,
 // kv-head) row and one of `nsplit` interleaved page subsets of it, for all
 // NH query heads of the GQA group, so every page is read from HBM once.  It
 // tabulates the row's LUT into LDS while its first pages are in flight.
-// Wave w of split s takes pages s + (w + 12i) * nsplit, one page (16 slots)
+// Wave w of split s takes pages s + (w + W i) * nsplit (W waves), one page (16 slots)
 // at a time, with the next page's loads in flight while the current one is
 // computed.
 //
@@ -38,7 +39,7 @@
 // folded into the weights.  The output accumulators are the MFMA C tiles
 // (rows = heads: element h % 4 of lane 16 (h / 4) + n holds dim n of head h).
 //
-// At the end the 12 waves are merged through LDS and the split's partial
+// At the end the waves are merged through LDS and the split's partial
 // (m, l, acc) is written; the merge kernel combines a row's splits into the
 // outputs (with one split the stream writes them directly).
 #include "ada_internal.h"
@@ -51,8 +52,14 @@ namespace {
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kRescale = 8.0f; // log2 of the largest weight kept between rescales
-constexpr int kWaves = 12;
-constexpr int kThreads = 64 * kWaves;
+// Waves per page-stream workgroup: 12 (three per SIMD, up to 168 VGPRs
+// each).  Groups of more than four heads at D = 128 need more registers
+// than that in the page loop and run 8 waves of up to 256.
+template <int D, int NH>
+struct Waves {
+    static constexpr int W = (D == 128 && NH > 4) ? 8 : 12;
+    static constexpr int THREADS = 64 * W;
+};
 constexpr int kMaxSplitsDev = 1024; // the ABI's split limit
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
@@ -486,8 +493,9 @@ __device__ __forceinline__ void fetch_entry(PageRegs<D> &pr, uint2 e, const uint
 
 // ---- page stream ------------------------------------------------------------
 template <int D, int NH, bool DENSE>
-__global__ __launch_bounds__(kThreads) void decode_main(DecodeArgs a)
+__global__ __launch_bounds__((Waves<D, NH>::THREADS)) void decode_main(DecodeArgs a)
 {
+    constexpr int kWaves = Waves<D, NH>::W, kThreads = Waves<D, NH>::THREADS;
     constexpr int G = D / 8; // code groups
     constexpr int LUT_FLOATS = DENSE ? 0 : G * kLutCodes * NH;
 
@@ -858,7 +866,8 @@ size_t shmem_bytes(int max_wg_pages)
 {
     const size_t lut = DENSE ? 0 : (size_t)(D / 8) * kLutCodes * NH * sizeof(float);
     const size_t b = lut + (size_t)max_wg_pages * sizeof(uint2);
-    const size_t red = ((size_t)kWaves * D * 4 * Heads<NH>::NQ + (size_t)kWaves * NH * 2) * sizeof(float);
+    constexpr size_t W = Waves<D, NH>::W;
+    const size_t red = (W * D * 4 * Heads<NH>::NQ + W * NH * 2) * sizeof(float);
     return b > red ? b : red;
 }
 
@@ -879,7 +888,8 @@ hipError_t launch_t(const DecodeArgs &a, hipStream_t st, unsigned stages)
     }
     hipError_t e = hipSuccess;
     if (stages & kStageStream) {
-        hipLaunchKernelGGL((decode_main<D, NH, DENSE>), dim3(rows * a.nsplit), dim3(kThreads), shmem, st, a);
+        hipLaunchKernelGGL((decode_main<D, NH, DENSE>), dim3(rows * a.nsplit), dim3(Waves<D, NH>::THREADS), shmem,
+                           st, a);
         e = hipGetLastError();
     }
     if (e != hipSuccess || a.nsplit == 1 || !(stages & kStageMerge))
