@@ -49,6 +49,13 @@ def lib():
         L.oracle_pack.argtypes = [I, I, I, P, P, P, P, P, P, P, P, P, P, P, P, U64, P, P, P, P,
                                   P, P, I]
         L.oracle_pack.restype = I
+        L.oracle_code_error.argtypes = [I, I, I64, P, P, P, P, P, P, P]
+        L.oracle_code_error.restype = I
+        L.oracle_rdr_solve.argtypes = [I, I, I, P, P, P, P, P, P, P, P]
+        L.oracle_rdr_solve.restype = I
+        L.oracle_pack_tiers.argtypes = [I, I, I, P, P, P, P, P, P, P, P, P, P, U64, P, P, P, P, P,
+                                        P, I]
+        L.oracle_pack_tiers.restype = I
         L.oracle_dense_pack.argtypes = [I, I, I, P, P, P, P, P, U64, P, P, P, P, I]
         L.oracle_dense_pack.restype = I
         L.oracle_decode.argtypes = [I, I, I, I, I, P, P, P, P, P, P, P, D_, P, P, P, P, I64, I64, I]
@@ -201,6 +208,69 @@ def pack(cache: HostCache, cu_tokens, tier_cum_bp, keys, values, radius, codes8,
                              cache.arena_units, _p(cache.cursor), _p(cache.page_table),
                              _p(cache.page_meta), _p(cache.num_pages), _p(cache.tier_tokens),
                              _p(cache.slot_token), cache.maxp)
+
+
+def code_error(keys, cb8, cb4, codes8, codes4):
+    """Squared chord error of each (token, head)'s 8-bit and 4-bit code
+    reconstruction: (err8, err4) f32 [N][Hkv]."""
+    k = _u16(keys)
+    N, H, D = k.shape
+    c8, c4 = _np(cb8, np.float32), _np(cb4, np.float32)
+    k8, k4 = _np(codes8, np.uint8), _np(codes4, np.uint8)
+    e8 = np.zeros((N, H), dtype=np.float32)
+    e4 = np.zeros((N, H), dtype=np.float32)
+    rc = lib().oracle_code_error(D, H, N, _p(k), _p(c8), _p(c4), _p(k8), _p(k4), _p(e8), _p(e4))
+    assert rc == 0
+    return e8, e4
+
+
+def rdr_solve(D, cu_tokens, budget_bytes, radius, err8, err4, scores, protect=None):
+    """Tier of every (token, head) under a per-sequence byte budget:
+    u8 [N][Hkv], 0-2 kept tier, 3 dropped."""
+    cu = _np(cu_tokens, np.int32)
+    bud = _np(budget_bytes, np.int64)
+    r = _u16(radius)
+    N, H = r.shape
+    e8, e4 = _np(err8, np.float32), _np(err4, np.float32)
+    sc = _np(scores, np.float32)
+    pr = None if protect is None else _np(protect, np.uint8)
+    t = np.zeros((N, H), dtype=np.uint8)
+    rc = lib().oracle_rdr_solve(D, H, len(cu) - 1, _p(cu), _p(bud), _p(r), _p(e8), _p(e4), _p(sc),
+                                _p(pr), _p(t))
+    assert rc == 0, rc
+    return t
+
+
+def pack_tiers(cache: HostCache, cu_tokens, tiers, keys, values, radius, codes8, codes4,
+               place_perm=None, pos_base=None) -> int:
+    """pack() with the tier of every (token, head) given (0-2 kept, 3 dropped)."""
+    cu = _np(cu_tokens, np.int32)
+    t = _np(tiers, np.uint8)
+    k, v = _u16(keys), _u16(values)
+    r = _u16(radius)
+    c8, c4 = _np(codes8, np.uint8), _np(codes4, np.uint8)
+    pp = None if place_perm is None else _np(place_perm, np.uint32)
+    pb = None if pos_base is None else _np(pos_base, np.int64)
+    S = len(cu) - 1
+    assert S == cache.S
+    return lib().oracle_pack_tiers(cache.D, cache.Hkv, S, _p(cu), _p(t), _p(k), _p(v), _p(r),
+                                   _p(c8), _p(c4), _p(pp), _p(pb), _p(cache.arena),
+                                   cache.arena_units, _p(cache.cursor), _p(cache.page_table),
+                                   _p(cache.page_meta), _p(cache.num_pages),
+                                   _p(cache.tier_tokens), _p(cache.slot_token), cache.maxp)
+
+
+def row_tier_counts(cu_tokens, tiers) -> np.ndarray:
+    """Tokens of each kept tier per (sequence, head) row: int32 [S*Hkv][3]."""
+    cu = np.asarray(cu_tokens)
+    t = np.asarray(tiers)
+    H = t.shape[1]
+    out = np.zeros((len(cu) - 1, H, 3), dtype=np.int32)
+    for s in range(len(cu) - 1):
+        seg = t[cu[s]:cu[s + 1]]
+        for k in range(3):
+            out[s, :, k] = (seg == k).sum(axis=0)
+    return out.reshape(-1, 3)
 
 
 def dense_pack(cache: HostCache, cu_tokens, keys, values, place_perm=None) -> int:

@@ -307,6 +307,212 @@ int oracle_encode(int D, int Hkv, int64_t n_tokens, const uint16_t *keys, const 
 }
 
 /* ------------------------------------------------------------------------ */
+/* Angular error of the stored codes (input of the RDR distortion surrogate). */
+/*                                                                           */
+/* [TS] 2.2 "Distortion Surrogate": the controller's proxy says the logit    */
+/* error is dominated by the angular approximation error, scaled by the      */
+/* query and key magnitudes.  Reading of the angular error of a tier: the   */
+/* squared Euclidean distance between the unit direction u and its code      */
+/* reconstruction (the chosen codeword of every group, concatenated),        */
+/*     err = sum_g || u_g - C_g[code_g] ||^2,                                */
+/* whose square root bounds |q . (u - u~)| / |q|.  u is formed exactly as in */
+/* encode (double, sequential norm); each group's distance is summed over    */
+/* its 8 coordinates in order and added to the total in group order, in      */
+/* double; the total is rounded once to binary32.                            */
+/* ------------------------------------------------------------------------ */
+
+int oracle_code_error(int D, int Hkv, int64_t n_tokens, const uint16_t *keys, const float *cb8,
+                      const float *cb4, const uint8_t *codes8, const uint8_t *codes4, float *err8,
+                      float *err4)
+{
+    if ((D != 64 && D != 128) || Hkv <= 0 || n_tokens < 0)
+        return 1;
+    int G = D / 8;
+    for (int64_t i = 0; i < n_tokens * Hkv; i++) {
+        int h = (int)(i % Hkv);
+        const uint16_t *k = keys + i * D;
+        double x[128], u[128], ss = 0;
+        for (int j = 0; j < D; j++) {
+            x[j] = f16_to_double(k[j]);
+            ss += x[j] * x[j];
+        }
+        double r = sqrt(ss);
+        for (int j = 0; j < D; j++)
+            u[j] = r > 0 ? x[j] / r : 0.0;
+        double e8 = 0, e4 = 0;
+        for (int g = 0; g < G; g++) {
+            int c8 = codes8[i * G + g];
+            int c4 = (codes4[i * (G / 2) + g / 2] >> (4 * (g % 2))) & 15;
+            const float *w8 = cb8 + (((size_t)h * G + g) * 256 + c8) * 8;
+            const float *w4 = cb4 + (((size_t)h * G + g) * 16 + c4) * 8;
+            double d8 = 0, d4 = 0;
+            for (int j = 0; j < 8; j++) {
+                double a = u[8 * g + j] - (double)w8[j];
+                double b = u[8 * g + j] - (double)w4[j];
+                d8 += a * a;
+                d4 += b * b;
+            }
+            e8 += d8;
+            e4 += d4;
+        }
+        err8[i] = (float)e8;
+        err4[i] = (float)e4;
+    }
+    return 0;
+}
+
+/* ------------------------------------------------------------------------ */
+/* RDR budget solver.                                                        */
+/*                                                                           */
+/* [TS] 2.2 "Joint Optimization": for every token/head state i the          */
+/* controller picks a residency bit z_i and a tier b_i by solving a discrete */
+/* rate-distortion allocation under a fixed memory budget; "Distortion       */
+/* Surrogate": the error proxy is the angular error scaled by the query and  */
+/* key magnitudes; "Protection Constraints": protected states are kept at    */
+/* the top tier.  [ABS]: retention and precision follow estimated future     */
+/* utility, per token and head, under a fixed budget.  The pages give no     */
+/* solver.  Readings used here:                                              */
+/*   options of a state: tier 0 (fp16 key), 1 (8-bit codes), 2 (4-bit       */
+/*     codes), 3 (dropped);                                                  */
+/*   rate R_b: bytes one state takes in a full page of its tier (page bytes  */
+/*     / 16), R_3 = 0;                                                       */
+/*   distortion D_b = w * r~ * e_b with w the state's utility score, r~ its  */
+/*     stored radius, e_0 = 0, e_1 = sqrt(err8), e_2 = sqrt(err4) (the chord */
+/*     error of the code reconstruction, see above) and e_3 = 1 (a dropped   */
+/*     key keeps none of its direction, as if u~ = 0).  The query magnitude */
+/*     is the same unknown factor for every state and is left out;          */
+/*   the budget is a cap per sequence on the bytes of all its rows' pages,   */
+/*     so the solver keeps 15 slots of every tier per row in reserve for the */
+/*     partial last pages: cap = budget - Hkv * 15 * (R_0 + R_1 + R_2);      */
+/*   the allocation is the Lagrangian (convex-hull) solution of the          */
+/*     multiple-choice knapsack: every state starts at tier 0, its lower     */
+/*     convex hull in the (rate, distortion) plane gives a chain of          */
+/*     demotions with increasing slopes (distortion added per byte saved),   */
+/*     and demotions are taken in order of slope, all of the sequence's      */
+/*     states together, until the rows fit under the cap.  Exactly: with     */
+/*     need = (bytes at tier 0) - cap, s* is the smallest slope such that    */
+/*     the demotions of slope <= s* save at least `need` bytes (+inf if none */
+/*     does); every state takes the longest prefix of its chain whose        */
+/*     slopes are <= s*.  need <= 0 keeps everything at tier 0.  Protected   */
+/*     states have no demotions.                                             */
+/* Arithmetic is binary32, in the order written (it decides integers, so     */
+/* the HIP solver uses the same): wr = w * r~; D_1 = wr * sqrtf(err8);       */
+/* D_2 = wr * sqrtf(err4); D_3 = wr; slope = (D_j - D_c) / (R_c - R_j) + 0;  */
+/* the hull walk from the current point c takes the candidate j > c of least */
+/* slope (the largest j on ties); a slope below its predecessor in the chain */
+/* is raised to it, so chains are non-decreasing.                            */
+/* ------------------------------------------------------------------------ */
+
+enum { OR_EINVAL_SOLVE = 1 };
+
+typedef struct {
+    float slope;
+    int32_t dr;
+} rdr_step;
+
+static int step_cmp(const void *pa, const void *pb)
+{
+    float a = ((const rdr_step *)pa)->slope, b = ((const rdr_step *)pb)->slope;
+    return a < b ? -1 : (a > b ? 1 : 0);
+}
+
+/* Demotion chain of one state: up to 3 steps; returns their number and the
+ * tier each one ends at. */
+static int rdr_chain(const int32_t R[4], float w, uint16_t r_f16, float e8, float e4,
+                     float slope[3], int32_t dr[3], int to[3])
+{
+    float wr = w * (float)f16_to_double(r_f16);
+    float Dv[4] = {0.0f, wr * sqrtf(e8), wr * sqrtf(e4), wr};
+    int c = 0, n = 0;
+    float prev = -INFINITY;
+    while (c < 3) {
+        int best = -1;
+        float bs = 0.0f;
+        for (int j = c + 1; j < 4; j++) {
+            float sl = (Dv[j] - Dv[c]) / (float)(R[c] - R[j]) + 0.0f;
+            if (best < 0 || sl <= bs) {
+                best = j;
+                bs = sl;
+            }
+        }
+        if (bs < prev)
+            bs = prev;
+        slope[n] = bs;
+        dr[n] = R[c] - R[best];
+        to[n] = best;
+        prev = bs;
+        n++;
+        c = best;
+    }
+    return n;
+}
+
+int oracle_rdr_solve(int D, int Hkv, int S, const int32_t *cu_tokens, const int64_t *budget_bytes,
+                     const uint16_t *radius, const float *err8, const float *err4,
+                     const float *scores, const uint8_t *protect, uint8_t *tiers)
+{
+    if ((D != 64 && D != 128) || Hkv <= 0 || S < 0)
+        return OR_EINVAL_SOLVE;
+    int32_t R[4] = {(int32_t)(oracle_page_bytes(D, 0) / SLOTS), (int32_t)(oracle_page_bytes(D, 1) / SLOTS),
+                    (int32_t)(oracle_page_bytes(D, 2) / SLOTS), 0};
+    for (int s = 0; s < S; s++)
+        if (cu_tokens[s + 1] < cu_tokens[s] || budget_bytes[s] < 0)
+            return OR_EINVAL_SOLVE;
+    for (int s = 0; s < S; s++) {
+        int64_t b = cu_tokens[s], T = cu_tokens[s + 1] - cu_tokens[s];
+        int64_t items = T * Hkv;
+        int64_t cap = budget_bytes[s] - (int64_t)Hkv * 15 * (R[0] + R[1] + R[2]);
+        int64_t need = items * R[0] - cap;
+        for (int64_t i = 0; i < items; i++)
+            tiers[b * Hkv + i] = 0;
+        if (need <= 0)
+            continue;
+        /* every demotion of the sequence, sorted by slope */
+        rdr_step *all = malloc((size_t)(3 * items + 1) * sizeof(rdr_step));
+        int64_t n_all = 0;
+        for (int64_t i = 0; i < items; i++) {
+            int64_t e = b * Hkv + i;
+            if (protect && protect[e])
+                continue;
+            float sl[3];
+            int32_t dr[3];
+            int to[3];
+            int n = rdr_chain(R, scores[e], radius[e], err8[e], err4[e], sl, dr, to);
+            for (int k = 0; k < n; k++) {
+                all[n_all].slope = sl[k];
+                all[n_all].dr = dr[k];
+                n_all++;
+            }
+        }
+        qsort(all, (size_t)n_all, sizeof(rdr_step), step_cmp);
+        float sstar = INFINITY;
+        int64_t cum = 0;
+        for (int64_t k = 0; k < n_all; k++) {
+            cum += all[k].dr;
+            if (cum >= need) {
+                sstar = all[k].slope;
+                break;
+            }
+        }
+        free(all);
+        for (int64_t i = 0; i < items; i++) {
+            int64_t e = b * Hkv + i;
+            if (protect && protect[e])
+                continue;
+            float sl[3];
+            int32_t dr[3];
+            int to[3];
+            int n = rdr_chain(R, scores[e], radius[e], err8[e], err4[e], sl, dr, to);
+            int t = 0;
+            for (int k = 0; k < n && sl[k] <= sstar; k++)
+                t = to[k];
+            tiers[e] = (uint8_t)t;
+        }
+    }
+    return 0;
+}
+
+/* ------------------------------------------------------------------------ */
 /* Pack (RDR tiering into tier-homogeneous pages).                           */
 /*                                                                           */
 /* [TS] 2.2 "Joint Optimization": every token/head state gets a residency    */
@@ -438,10 +644,13 @@ enum { OR_OK = 0, OR_EINVAL = 1, OR_ENOSPACE = 3 };
  *   arena / arena_units / cursor (in/out, 128-byte units); page_table and
  *   page_meta [S*Hkv][maxp]; num_pages [S*Hkv]; tier_tokens [S*Hkv][3];
  *   slot_token [S*Hkv][maxp][16] or NULL.
+ * tiers [N][Hkv] (0-2 kept tier, 3 dropped), when non-NULL, replaces the
+ * ranking: each row's tokens of a tier keep index order (tier_cum_bp, scores
+ * and protect are then unused).
  * dense != 0 packs every token of the call into tier-3 pages instead.
  */
 static int pack_impl(int D, int Hkv, int S, const int32_t *cu_tokens, const int32_t *tier_cum_bp,
-                     const uint16_t *keys, const uint16_t *values, const uint16_t *radius,
+                     const uint8_t *tiers, const uint16_t *keys, const uint16_t *values, const uint16_t *radius,
                      const uint8_t *codes8, const uint8_t *codes4, const float *scores,
                      const uint8_t *protect, const uint32_t *place_perm, const int64_t *pos_base,
                      uint8_t *arena, uint64_t arena_units, uint64_t *cursor, uint32_t *page_table,
@@ -466,6 +675,8 @@ static int pack_impl(int D, int Hkv, int S, const int32_t *cu_tokens, const int3
         int64_t n_cum[3];
         if (dense) { /* every token, index order, one list */
             n_cum[0] = n_cum[1] = n_cum[2] = T;
+        } else if (tiers) { /* given tiers: sort tokens by (tier, index) */
+            n_cum[0] = n_cum[1] = n_cum[2] = 0;
         } else {
             const int32_t *bp = tier_cum_bp + 3 * s;
             if (bp[0] < 0 || bp[0] > bp[1] || bp[1] > bp[2] || bp[2] > 10000) {
@@ -478,7 +689,24 @@ static int pack_impl(int D, int Hkv, int S, const int32_t *cu_tokens, const int3
             int32_t *order = malloc((size_t)(T > 0 ? T : 1) * sizeof(int32_t));
             for (int64_t i = 0; i < T; i++)
                 order[i] = (int32_t)i;
-            if (!dense) {
+            if (!dense && tiers) {
+                int64_t at = 0, cnt[4] = {0, 0, 0, 0};
+                for (int64_t i = 0; i < T; i++) {
+                    int t = tiers[(b + i) * Hkv + h];
+                    if (t > 3) {
+                        rc = OR_EINVAL;
+                        t = 3;
+                    }
+                    cnt[t]++;
+                }
+                for (int tier = 0; tier < 4; tier++)
+                    for (int64_t i = 0; i < T; i++)
+                        if (tiers[(b + i) * Hkv + h] == tier)
+                            order[at++] = (int32_t)i;
+                n_cum[0] = cnt[0];
+                n_cum[1] = cnt[0] + cnt[1];
+                n_cum[2] = cnt[0] + cnt[1] + cnt[2];
+            } else if (!dense) {
                 g_rank.score = scores + b * Hkv + h;
                 g_rank.prot = protect ? protect + b * Hkv + h : NULL;
                 g_rank.stride = Hkv;
@@ -613,9 +841,24 @@ int oracle_pack(int D, int Hkv, int S, const int32_t *cu_tokens, const int32_t *
                 uint8_t *page_meta, int32_t *num_pages, int32_t *tier_tokens, int32_t *slot_token,
                 int maxp)
 {
-    return pack_impl(D, Hkv, S, cu_tokens, tier_cum_bp, keys, values, radius, codes8, codes4,
+    return pack_impl(D, Hkv, S, cu_tokens, tier_cum_bp, NULL, keys, values, radius, codes8, codes4,
                      scores, protect, place_perm, pos_base, arena, arena_units, cursor, page_table,
                      page_meta, num_pages, tier_tokens, slot_token, maxp, 0);
+}
+
+/* Pack with the tier of every (token, head) given (e.g. by the solver). */
+int oracle_pack_tiers(int D, int Hkv, int S, const int32_t *cu_tokens, const uint8_t *tiers,
+                      const uint16_t *keys, const uint16_t *values, const uint16_t *radius,
+                      const uint8_t *codes8, const uint8_t *codes4, const uint32_t *place_perm,
+                      const int64_t *pos_base, uint8_t *arena, uint64_t arena_units,
+                      uint64_t *cursor, uint32_t *page_table, uint8_t *page_meta,
+                      int32_t *num_pages, int32_t *tier_tokens, int32_t *slot_token, int maxp)
+{
+    if (tiers == NULL)
+        return OR_EINVAL;
+    return pack_impl(D, Hkv, S, cu_tokens, NULL, tiers, keys, values, radius, codes8, codes4, NULL,
+                     NULL, place_perm, pos_base, arena, arena_units, cursor, page_table, page_meta,
+                     num_pages, tier_tokens, slot_token, maxp, 0);
 }
 
 /* Dense comparison cache: every token of the call, in index order, in tier-3
@@ -625,7 +868,7 @@ int oracle_dense_pack(int D, int Hkv, int S, const int32_t *cu_tokens, const uin
                       uint64_t arena_units, uint64_t *cursor, uint32_t *page_table,
                       uint8_t *page_meta, int32_t *num_pages, int maxp)
 {
-    return pack_impl(D, Hkv, S, cu_tokens, NULL, keys, values, NULL, NULL, NULL, NULL, NULL,
+    return pack_impl(D, Hkv, S, cu_tokens, NULL, NULL, keys, values, NULL, NULL, NULL, NULL, NULL,
                      place_perm, NULL, arena, arena_units, cursor, page_table, page_meta,
                      num_pages, NULL, NULL, maxp, 1);
 }
