@@ -83,6 +83,20 @@ def load():
         L.rdr_pack.restype = C.c_int
         L.dense_pack.argtypes = [G, CV, I32, P, P, P, P, P, P, P, SZ, P]
         L.dense_pack.restype = C.c_int
+        L.ada_code_error.argtypes = [G, I64, P, P, P, P, P, P, P, P]
+        L.ada_code_error.restype = C.c_int
+        L.rdr_solve_workspace_size.argtypes = [G, I32, I64]
+        L.rdr_solve_workspace_size.restype = SZ
+        L.rdr_solve.argtypes = [G, I32, P, P, P, P, P, P, P, P, P, SZ, P]
+        L.rdr_solve.restype = C.c_int
+        L.rdr_tier_counts_workspace_size.argtypes = [G, I32]
+        L.rdr_tier_counts_workspace_size.restype = SZ
+        L.rdr_tier_counts.argtypes = [G, I32, P, P, P, P, SZ, P]
+        L.rdr_tier_counts.restype = C.c_int
+        L.rdr_pack_tiers_num_pages.argtypes = [G, I32, P, P]
+        L.rdr_pack_tiers_num_pages.restype = C.c_int
+        L.rdr_pack_tiers.argtypes = [G, CV, I32, P, P, P, P, P, P, P, P, P, P, P, P, P, SZ, P]
+        L.rdr_pack_tiers.restype = C.c_int
         L.ada_decode_default_splits.argtypes = [G, I32, I32]
         L.ada_decode_default_splits.restype = I32
         L.ada_decode_workspace_size.argtypes = [G, I32, I32, I32]
@@ -211,8 +225,8 @@ def pack_workspace_size(geom: Geom, n_tokens: int, num_seqs: int) -> int:
 
 
 def _workspace(nbytes: int, device) -> torch.Tensor:
-    # zero-filled: the decode workspace starts with split counters that must
-    # read zero before its first use
+    # (every entry point writes what it reads; zero-filled only so that a
+    # workspace never holds stale data from elsewhere)
     return torch.zeros(max(256, nbytes), dtype=torch.uint8, device=device)
 
 
@@ -237,6 +251,101 @@ def rdr_pack(geom: Geom, cache: Cache, cu_tokens, tier_cum_bp, keys, values, rad
         prp, ppp, pbp, cache.cursor.ctypes.data_as(C.c_void_p),
         cache.num_pages_host.ctypes.data_as(C.c_void_p), _dev(ws, "ws"), ws.numel(), _stream(stream))
     _check(st, "rdr_pack")
+    return ws
+
+
+def code_error(geom: Geom, keys, cb8, cb4, codes8, codes4, err8, err4, stream=None):
+    """Squared chord error of each (token, head)'s 8-bit and 4-bit codes:
+    err8 / err4 [N][Hkv] f32 (preallocated).  See ada_code_error."""
+    n = keys.shape[0]
+    H, D = geom.num_kv_heads, geom.head_dim
+    for t, shape, name in ((keys, (n, H, D), "keys"), (codes8, (n, H, D // 8), "codes8"),
+                           (codes4, (n, H, D // 16), "codes4"), (err8, (n, H), "err8"),
+                           (err4, (n, H), "err4"), (cb8, (H, D // 8, 256, 8), "cb8"),
+                           (cb4, (H, D // 8, 16, 8), "cb4")):
+        if tuple(t.shape) != shape:
+            raise ValueError(f"{name} shape {tuple(t.shape)} != {shape}")
+    st = load().ada_code_error(C.byref(geom), n, _dev(keys, "keys", (torch.float16,)),
+                               _dev(cb8, "cb8", (torch.float32,)), _dev(cb4, "cb4", (torch.float32,)),
+                               _dev(codes8, "codes8", (torch.uint8,)), _dev(codes4, "codes4", (torch.uint8,)),
+                               _dev(err8, "err8", (torch.float32,)), _dev(err4, "err4", (torch.float32,)),
+                               _stream(stream))
+    _check(st, "ada_code_error")
+
+
+def solve_workspace_size(geom: Geom, num_seqs: int, n_tokens: int) -> int:
+    return int(load().rdr_solve_workspace_size(C.byref(geom), num_seqs, n_tokens))
+
+
+def rdr_solve(geom: Geom, cu_tokens, budget_bytes, radius, err8, err4, scores, tiers, protect=None,
+              ws=None, stream=None):
+    """Tier of every (token, head) under a byte budget per sequence (see
+    rdr_solve in include/ada.h).  cu_tokens / budget_bytes are host arrays;
+    radius, err8, err4, scores, protect (u8 or None) and tiers (u8 out,
+    [N][Hkv]) are device tensors."""
+    cu, cup = _host(cu_tokens, np.int32, "cu_tokens")
+    bud, budp = _host(budget_bytes, np.int64, "budget_bytes")
+    if len(bud) != len(cu) - 1:
+        raise ValueError("one budget per sequence")
+    n = int(cu[-1])
+    H = geom.num_kv_heads
+    for t, name in ((radius, "radius"), (err8, "err8"), (err4, "err4"), (scores, "scores"),
+                    (tiers, "tiers")) + (((protect, "protect"),) if protect is not None else ()):
+        if tuple(t.shape) != (n, H):
+            raise ValueError(f"{name} shape {tuple(t.shape)} != {(n, H)}")
+    if ws is None:
+        ws = _workspace(solve_workspace_size(geom, len(cu) - 1, n), tiers.device)
+    st = load().rdr_solve(C.byref(geom), len(cu) - 1, cup, budp,
+                          _dev(radius, "radius", (torch.float16, torch.int16)),
+                          _dev(err8, "err8", (torch.float32,)), _dev(err4, "err4", (torch.float32,)),
+                          _dev(scores, "scores", (torch.float32,)), _dev(protect, "protect", (torch.uint8,)),
+                          _dev(tiers, "tiers", (torch.uint8,)), _dev(ws, "ws"), ws.numel(), _stream(stream))
+    _check(st, "rdr_solve")
+    return ws
+
+
+def tier_counts(geom: Geom, cu_tokens, tiers, stream=None) -> np.ndarray:
+    """Tokens of tier 0, 1, 2 per row: int32 [S*Hkv][3] on the host
+    (synchronizes the stream)."""
+    cu, cup = _host(cu_tokens, np.int32, "cu_tokens")
+    S = len(cu) - 1
+    out = np.zeros((max(1, S * geom.num_kv_heads), 3), dtype=np.int32)
+    ws = _workspace(int(load().rdr_tier_counts_workspace_size(C.byref(geom), S)), tiers.device)
+    st = load().rdr_tier_counts(C.byref(geom), S, cup, _dev(tiers, "tiers", (torch.uint8,)),
+                                out.ctypes.data_as(C.c_void_p), _dev(ws, "ws"), ws.numel(), _stream(stream))
+    _check(st, "rdr_tier_counts")
+    return out[: S * geom.num_kv_heads]
+
+
+def pack_tiers_num_pages(geom: Geom, row_counts) -> int:
+    rc, rcp = _host(row_counts, np.int32, "row_counts")
+    out = C.c_int64(0)
+    _check(load().rdr_pack_tiers_num_pages(C.byref(geom), rc.shape[0] // max(1, geom.num_kv_heads), rcp,
+                                           C.byref(out)), "rdr_pack_tiers_num_pages")
+    return out.value
+
+
+def rdr_pack_tiers(geom: Geom, cache: Cache, cu_tokens, row_counts, tiers, keys, values, radius, codes8,
+                   codes4, place_perm=None, pos_base=None, ws=None, stream=None):
+    """rdr_pack with the tier of every (token, head) given (see rdr_pack_tiers
+    in include/ada.h).  row_counts = tier_counts(geom, cu_tokens, tiers)."""
+    cu, cup = _host(cu_tokens, np.int32, "cu_tokens")
+    rc, rcp = _host(row_counts, np.int32, "row_counts")
+    n = int(cu[-1])
+    if rc.shape != ((len(cu) - 1) * geom.num_kv_heads, 3):
+        raise ValueError("row_counts must be [S*Hkv][3]")
+    pp, ppp = _host(place_perm, np.uint32, "place_perm")
+    pb, pbp = _host(pos_base, np.int64, "pos_base")
+    if ws is None:
+        ws = _workspace(pack_workspace_size(geom, n, len(cu) - 1), cache.arena.device)
+    view = cache.view()
+    st = load().rdr_pack_tiers(
+        C.byref(geom), C.byref(view), len(cu) - 1, cup, rcp, _dev(tiers, "tiers", (torch.uint8,)),
+        _dev(keys, "keys", (torch.float16,)), _dev(values, "values", (torch.bfloat16,)),
+        _dev(radius, "radius", (torch.float16, torch.int16)), _dev(codes8, "codes8", (torch.uint8,)),
+        _dev(codes4, "codes4", (torch.uint8,)), ppp, pbp, cache.cursor.ctypes.data_as(C.c_void_p),
+        cache.num_pages_host.ctypes.data_as(C.c_void_p), _dev(ws, "ws"), ws.numel(), _stream(stream))
+    _check(st, "rdr_pack_tiers")
     return ws
 
 

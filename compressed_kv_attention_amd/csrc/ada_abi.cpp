@@ -65,9 +65,11 @@ size_t pack_workspace(int Hkv, int64_t n_tokens, int32_t num_seqs)
 }
 
 // Plans one pack call on the host: counts, page numbering, placement.
-// counts[s][3] per-tier token counts; returns ADA_OK or the error.
+// counts[s][3] per-tier token counts of each sequence (the ranked path), and
+// row_counts[s * Hkv + h][3] those of each row; returns ADA_OK or the error.
 ada_status plan_pack(const ada_geom *g, const ada_cache *c, int32_t S, const int32_t *cu,
-                     const std::vector<int64_t> &counts, bool dense, const uint32_t *perm,
+                     const std::vector<int64_t> &counts, const std::vector<int64_t> &row_counts,
+                     bool dense, const uint32_t *perm,
                      const int64_t *pos_base, uint64_t cursor, const int32_t *num_pages_host,
                      PlanBuf &pb)
 {
@@ -91,7 +93,7 @@ ada_status plan_pack(const ada_geom *g, const ada_cache *c, int32_t S, const int
             const int64_t r = (int64_t)s * H + h;
             int32_t pi = num_pages_host[r];
             for (int k = 0; k < 3; k++) {
-                const int64_t n = counts[s * 3 + k];
+                const int64_t n = row_counts[r * 3 + k];
                 rowv[r].lp_first[k] = (int32_t)pages.size();
                 rowv[r].count[k] = (int32_t)n;
                 for (int64_t f = 0; f < n; f += kSlots) {
@@ -140,7 +142,8 @@ ada_status plan_pack(const ada_geom *g, const ada_cache *c, int32_t S, const int
 }
 
 ada_status run_pack(const ada_geom *g, const ada_cache *c, int32_t S, const int32_t *cu,
-                    const std::vector<int64_t> &counts, bool dense, const uint16_t *keys,
+                    const std::vector<int64_t> &counts, const std::vector<int64_t> &row_counts,
+                    const uint8_t *tiers, bool dense, const uint16_t *keys,
                     const uint16_t *values, const uint16_t *radius, const uint8_t *codes8,
                     const uint8_t *codes4, const float *scores, const uint8_t *protect_host,
                     const uint32_t *perm, const int64_t *pos_base, uint64_t *cursor,
@@ -151,7 +154,7 @@ ada_status run_pack(const ada_geom *g, const ada_cache *c, int32_t S, const int3
     if (ws == nullptr || ws_bytes < pack_workspace(H, N, S) || (reinterpret_cast<uintptr_t>(ws) & 255))
         return ADA_EWORKSPACE;
     PlanBuf pb;
-    if (ada_status st = plan_pack(g, c, S, cu, counts, dense, perm, pos_base, *cursor,
+    if (ada_status st = plan_pack(g, c, S, cu, counts, row_counts, dense, perm, pos_base, *cursor,
                                   num_pages_host, pb);
         st != ADA_OK)
         return st;
@@ -176,6 +179,7 @@ ada_status run_pack(const ada_geom *g, const ada_cache *c, int32_t S, const int3
     plan.rows = reinterpret_cast<const PackRow *>(wsb + pb.row_off);
     plan.pages = reinterpret_cast<const PackPage *>(wsb + pb.page_off);
     plan.protect = protect_host != nullptr ? prot_dev : nullptr;
+    plan.tiers = tiers;
     plan.dest = dest;
     plan.S = S;
     plan.Hkv = H;
@@ -202,6 +206,17 @@ bool cu_ok(int32_t S, const int32_t *cu)
         if (cu[s + 1] < cu[s])
             return false;
     return true;
+}
+
+// Per-row counts when every row of a sequence has the sequence's counts.
+std::vector<int64_t> rows_of(int32_t S, int H, const std::vector<int64_t> &counts)
+{
+    std::vector<int64_t> rc((size_t)S * H * 3);
+    for (int s = 0; s < S; s++)
+        for (int h = 0; h < H; h++)
+            for (int k = 0; k < 3; k++)
+                rc[((size_t)s * H + h) * 3 + k] = counts[(size_t)s * 3 + k];
+    return rc;
 }
 
 bool counts_from_bp(int32_t S, const int32_t *cu, const int32_t *bp, std::vector<int64_t> &counts)
@@ -408,8 +423,9 @@ ada_status rdr_pack(const ada_geom *geom, const ada_cache *cache, int32_t num_se
                     return ADA_EINVAL;
             }
     }
-    return run_pack(geom, cache, num_seqs, cu_tokens_host, counts, false, keys, values, radius, codes8,
-                    codes4, scores, protect_host, place_perm_host, pos_base_host, arena_cursor_host,
+    return run_pack(geom, cache, num_seqs, cu_tokens_host, counts,
+                    rows_of(num_seqs, geom->num_kv_heads, counts), nullptr, false, keys, values,
+                    radius, codes8, codes4, scores, protect_host, place_perm_host, pos_base_host, arena_cursor_host,
                     num_pages_host, ws, ws_bytes, stream);
 }
 
@@ -427,8 +443,193 @@ ada_status dense_pack(const ada_geom *geom, const ada_cache *cache, int32_t num_
     std::vector<int64_t> counts((size_t)num_seqs * 3, 0);
     for (int s = 0; s < num_seqs; s++)
         counts[s * 3] = cu_tokens_host[s + 1] - cu_tokens_host[s];
-    return run_pack(geom, cache, num_seqs, cu_tokens_host, counts, true, keys, values, nullptr,
-                    nullptr, nullptr, nullptr, nullptr, place_perm_host, nullptr, arena_cursor_host,
+    return run_pack(geom, cache, num_seqs, cu_tokens_host, counts,
+                    rows_of(num_seqs, geom->num_kv_heads, counts), nullptr, true, keys, values,
+                    nullptr, nullptr, nullptr, nullptr, nullptr, place_perm_host, nullptr, arena_cursor_host,
+                    num_pages_host, ws, ws_bytes, stream);
+}
+
+ada_status ada_code_error(const ada_geom *geom, int64_t n_tokens, const uint16_t *keys, const float *cb8,
+                          const float *cb4, const uint8_t *codes8, const uint8_t *codes4, float *err8,
+                          float *err4, void *stream)
+{
+    if (!geom_ok(geom) || n_tokens < 0 || n_tokens > ((int64_t)1 << 40))
+        return ADA_EINVAL;
+    if (n_tokens == 0)
+        return ADA_OK;
+    if (!keys || !cb8 || !cb4 || !codes8 || !codes4 || !err8 || !err4)
+        return ADA_EINVAL;
+    if ((reinterpret_cast<uintptr_t>(keys) & 15) || (reinterpret_cast<uintptr_t>(cb8) & 15) ||
+        (reinterpret_cast<uintptr_t>(cb4) & 15))
+        return ADA_EINVAL;
+    if ((n_tokens * geom->num_kv_heads + 255) / 256 > INT32_MAX)
+        return ADA_EINVAL;
+    return launch_code_error(geom->head_dim, geom->num_kv_heads, n_tokens, keys, cb8, cb4, codes8, codes4,
+                             err8, err4, as_stream(stream)) == hipSuccess
+               ? ADA_OK
+               : ADA_EHIP;
+}
+
+size_t rdr_solve_workspace_size(const ada_geom *geom, int32_t num_seqs, int64_t n_tokens)
+{
+    if (!geom_ok(geom) || num_seqs < 0 || n_tokens < 0)
+        return 0;
+    const int64_t blocks = n_tokens * geom->num_kv_heads / kSolveItems + num_seqs + 1;
+    return align256(sizeof(SolveSeq) * (size_t)std::max(num_seqs, 1)) +
+           align256(sizeof(SolveBlock) * (size_t)blocks) +
+           align256(sizeof(unsigned long long) * kSolvePasses * 256 * (size_t)std::max(num_seqs, 1));
+}
+
+ada_status rdr_solve(const ada_geom *geom, int32_t num_seqs, const int32_t *cu_tokens_host,
+                     const int64_t *budget_bytes_host, const uint16_t *radius, const float *err8,
+                     const float *err4, const float *scores, const uint8_t *protect, uint8_t *tiers,
+                     void *ws, size_t ws_bytes, void *stream)
+{
+    if (!geom_ok(geom) || num_seqs < 0 || !cu_ok(num_seqs, cu_tokens_host) || budget_bytes_host == nullptr)
+        return ADA_EINVAL;
+    const int H = geom->num_kv_heads, D = geom->head_dim;
+    const int64_t N = cu_tokens_host[num_seqs];
+    if (N > 0 && (!radius || !err8 || !err4 || !scores || !tiers))
+        return ADA_EINVAL;
+    for (int s = 0; s < num_seqs; s++)
+        if (budget_bytes_host[s] < 0)
+            return ADA_EINVAL;
+    const size_t need_ws = rdr_solve_workspace_size(geom, num_seqs, N);
+    if (ws == nullptr || ws_bytes < need_ws || (reinterpret_cast<uintptr_t>(ws) & 255))
+        return ADA_EWORKSPACE;
+    const int64_t R0 = page_bytes(D, 0) / kSlots, R1 = page_bytes(D, 1) / kSlots,
+                  R2 = page_bytes(D, 2) / kSlots;
+    const int64_t reserve = (int64_t)H * 15 * (R0 + R1 + R2);
+    std::vector<SolveSeq> seqs(std::max(num_seqs, 1));
+    std::vector<SolveBlock> blocks;
+    for (int s = 0; s < num_seqs; s++) {
+        const int64_t items = (int64_t)(cu_tokens_host[s + 1] - cu_tokens_host[s]) * H;
+        seqs[s].begin = (int64_t)cu_tokens_host[s] * H;
+        seqs[s].n_items = items;
+        seqs[s].need = items * R0 - (budget_bytes_host[s] - reserve);
+        for (int64_t f = 0; f < items; f += kSolveItems)
+            blocks.push_back(SolveBlock{s, 0, seqs[s].begin + f});
+    }
+    if (blocks.size() > (size_t)INT32_MAX)
+        return ADA_EINVAL;
+    // workspace: [sequences][blocks][digit histograms]
+    uint8_t *w = static_cast<uint8_t *>(ws);
+    const size_t seq_bytes = align256(sizeof(SolveSeq) * seqs.size());
+    const size_t blk_bytes = align256(sizeof(SolveBlock) * std::max<size_t>(blocks.size(), 1));
+    std::vector<uint8_t> blob(seq_bytes + sizeof(SolveBlock) * blocks.size(), 0);
+    std::memcpy(blob.data(), seqs.data(), sizeof(SolveSeq) * seqs.size());
+    if (!blocks.empty())
+        std::memcpy(blob.data() + seq_bytes, blocks.data(), sizeof(SolveBlock) * blocks.size());
+    hipStream_t st = as_stream(stream);
+    // pageable host source: the runtime copies it before returning
+    if (hipMemcpyAsync(w, blob.data(), blob.size(), hipMemcpyHostToDevice, st) != hipSuccess)
+        return ADA_EHIP;
+    SolveArgs a;
+    a.seqs = reinterpret_cast<const SolveSeq *>(w);
+    a.blocks = reinterpret_cast<const SolveBlock *>(w + seq_bytes);
+    a.hist = reinterpret_cast<unsigned long long *>(w + seq_bytes + blk_bytes);
+    a.radius = radius;
+    a.err8 = err8;
+    a.err4 = err4;
+    a.scores = scores;
+    a.protect = protect;
+    a.tiers = tiers;
+    a.S = num_seqs;
+    a.D = D;
+    a.n_blocks = (int)blocks.size();
+    return launch_solve(a, st) == hipSuccess ? ADA_OK : ADA_EHIP;
+}
+
+size_t rdr_tier_counts_workspace_size(const ada_geom *geom, int32_t num_seqs)
+{
+    if (!geom_ok(geom) || num_seqs < 0)
+        return 0;
+    return align256(sizeof(int32_t) * ((size_t)num_seqs + 1)) +
+           align256(sizeof(int32_t) * 3 * (size_t)std::max<int64_t>((int64_t)num_seqs * geom->num_kv_heads, 1));
+}
+
+ada_status rdr_tier_counts(const ada_geom *geom, int32_t num_seqs, const int32_t *cu_tokens_host,
+                           const uint8_t *tiers, int32_t *row_counts_host, void *ws, size_t ws_bytes,
+                           void *stream)
+{
+    if (!geom_ok(geom) || num_seqs < 0 || !cu_ok(num_seqs, cu_tokens_host) || !row_counts_host)
+        return ADA_EINVAL;
+    const int H = geom->num_kv_heads;
+    const int64_t rows = (int64_t)num_seqs * H;
+    if (rows == 0)
+        return ADA_OK;
+    if (cu_tokens_host[num_seqs] > 0 && tiers == nullptr)
+        return ADA_EINVAL;
+    if (rows > INT32_MAX)
+        return ADA_EINVAL;
+    if (ws == nullptr || ws_bytes < rdr_tier_counts_workspace_size(geom, num_seqs) ||
+        (reinterpret_cast<uintptr_t>(ws) & 255))
+        return ADA_EWORKSPACE;
+    uint8_t *w = static_cast<uint8_t *>(ws);
+    int32_t *cu_dev = reinterpret_cast<int32_t *>(w);
+    int32_t *counts = reinterpret_cast<int32_t *>(w + align256(sizeof(int32_t) * ((size_t)num_seqs + 1)));
+    hipStream_t st = as_stream(stream);
+    if (hipMemcpyAsync(cu_dev, cu_tokens_host, sizeof(int32_t) * ((size_t)num_seqs + 1),
+                       hipMemcpyHostToDevice, st) != hipSuccess)
+        return ADA_EHIP;
+    if (launch_tier_counts(H, num_seqs, cu_dev, tiers, counts, st) != hipSuccess)
+        return ADA_EHIP;
+    if (hipMemcpyAsync(row_counts_host, counts, sizeof(int32_t) * 3 * (size_t)rows, hipMemcpyDeviceToHost,
+                       st) != hipSuccess ||
+        hipStreamSynchronize(st) != hipSuccess)
+        return ADA_EHIP;
+    return ADA_OK;
+}
+
+ada_status rdr_pack_tiers_num_pages(const ada_geom *geom, int32_t num_seqs, const int32_t *row_counts_host,
+                                    int64_t *n_pages_out)
+{
+    if (!geom_ok(geom) || num_seqs < 0 || !row_counts_host || !n_pages_out)
+        return ADA_EINVAL;
+    int64_t n = 0;
+    for (int64_t i = 0; i < (int64_t)num_seqs * geom->num_kv_heads * 3; i++) {
+        if (row_counts_host[i] < 0)
+            return ADA_EINVAL;
+        n += (row_counts_host[i] + kSlots - 1) / kSlots;
+    }
+    *n_pages_out = n;
+    return ADA_OK;
+}
+
+ada_status rdr_pack_tiers(const ada_geom *geom, const ada_cache *cache, int32_t num_seqs,
+                          const int32_t *cu_tokens_host, const int32_t *row_counts_host, const uint8_t *tiers,
+                          const uint16_t *keys, const uint16_t *values, const uint16_t *radius,
+                          const uint8_t *codes8, const uint8_t *codes4, const uint32_t *place_perm_host,
+                          const int64_t *pos_base_host, uint64_t *arena_cursor_host, int32_t *num_pages_host,
+                          void *ws, size_t ws_bytes, void *stream)
+{
+    if (!geom_ok(geom) || !cache_ok(cache) || num_seqs != cache->num_seqs || num_seqs < 0 ||
+        !cu_ok(num_seqs, cu_tokens_host) || !row_counts_host || !arena_cursor_host || !num_pages_host ||
+        cache->tier_tokens == nullptr)
+        return ADA_EINVAL;
+    const int H = geom->num_kv_heads;
+    const int64_t N = cu_tokens_host[num_seqs];
+    if (N > 0 && (!tiers || !keys || !values || !radius || !codes8 || !codes4))
+        return ADA_EINVAL;
+    std::vector<int64_t> rc((size_t)num_seqs * H * 3);
+    for (int s = 0; s < num_seqs; s++) {
+        const int64_t T = cu_tokens_host[s + 1] - cu_tokens_host[s];
+        for (int h = 0; h < H; h++) {
+            int64_t tot = 0;
+            for (int k = 0; k < 3; k++) {
+                const int64_t n = row_counts_host[((int64_t)s * H + h) * 3 + k];
+                if (n < 0)
+                    return ADA_EINVAL;
+                rc[((size_t)s * H + h) * 3 + k] = n;
+                tot += n;
+            }
+            if (tot > T)
+                return ADA_EINVAL;
+        }
+    }
+    std::vector<int64_t> counts((size_t)num_seqs * 3, 0); // (the ranked path's; unused here)
+    return run_pack(geom, cache, num_seqs, cu_tokens_host, counts, rc, tiers, false, keys, values, radius,
+                    codes8, codes4, nullptr, nullptr, place_perm_host, pos_base_host, arena_cursor_host,
                     num_pages_host, ws, ws_bytes, stream);
 }
 

@@ -1,5 +1,5 @@
 // Internal interface between the host entry points (ada_abi.cpp) and the
-// gfx950 kernels (decode.hip, encode.hip, pack.hip).  Not installed.
+// gfx950 kernels (decode.hip, encode.hip, pack.hip, rdr.hip).  Not installed.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -70,6 +70,38 @@ hipError_t launch_encode(int D, int Hkv, int64_t n_tokens, const uint16_t *keys,
                          const float *cb4, uint16_t *radius, uint8_t *codes8, uint8_t *codes4,
                          hipStream_t st);
 
+// ---- RDR: code error and budget solver ------------------------------------
+hipError_t launch_code_error(int D, int Hkv, int64_t n_tokens, const uint16_t *keys, const float *cb8,
+                             const float *cb4, const uint8_t *codes8, const uint8_t *codes4,
+                             float *err8, float *err4, hipStream_t st);
+
+struct SolveSeq {
+    int64_t begin;   // first flat item (token * Hkv + head) of the sequence
+    int64_t n_items; // tokens * Hkv
+    int64_t need;    // bytes the demotions must save; <= 0: every state stays at tier 0
+};
+struct SolveBlock {
+    int32_t seq;
+    int32_t pad;
+    int64_t first;   // first flat item of the block (kSolveItems items, cut at the sequence's end)
+};
+constexpr int kSolveThreads = 256;
+constexpr int kSolveItems = 4 * kSolveThreads;
+constexpr int kSolvePasses = 4; // 8-bit digits of the 32-bit slope key
+struct SolveArgs {
+    const SolveSeq *seqs;
+    const SolveBlock *blocks;
+    unsigned long long *hist; // [kSolvePasses][S][256]: bytes saved per key digit
+    const uint16_t *radius;
+    const float *err8, *err4, *scores;
+    const uint8_t *protect;   // or null
+    uint8_t *tiers;
+    int S, D, n_blocks;
+};
+hipError_t launch_solve(const SolveArgs &a, hipStream_t st);
+hipError_t launch_tier_counts(int Hkv, int S, const int32_t *cu_dev, const uint8_t *tiers,
+                              int32_t *counts, hipStream_t st);
+
 // ---- pack ----------------------------------------------------------------
 // Host-built plan of one pack call, copied into the workspace.
 struct PackSeq {
@@ -94,6 +126,7 @@ struct PackPlan {
     const PackRow *rows;
     const PackPage *pages;
     const uint8_t *protect; // [N][Hkv] or null
+    const uint8_t *tiers;   // [N][Hkv] given tiers (0-2 kept, other values dropped) or null
     int32_t *dest;          // [N][Hkv]: logical page * 16 + slot, or -1
     int S, Hkv, D, maxp, n_pages, dense;
     int64_t n_tokens;

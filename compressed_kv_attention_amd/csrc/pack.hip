@@ -4,9 +4,10 @@
 // 2.2: each (token, head) state gets a residency bit and a precision tier;
 // protected states are kept at the top tier; retained states are grouped into
 // pages of a single tier.  The abstract adds that the choice is made per token
-// and head under a fixed budget.  The pages give no solver: a row's tokens are
-// ranked by (protected, utility score, -index) and cut at the tier counts the
-// host computed from the sequence's cumulative basis points.
+// and head under a fixed budget.  Either a row's tokens are ranked by
+// (protected, utility score, -index) and cut at the tier counts the host
+// computed from the sequence's cumulative basis points, or every token's tier
+// is given (by the budget solver in rdr.hip).
 //
 // Kernels, in stream order:
 //   pack_pages   one block per new page: zero its bytes, write its page-table
@@ -14,7 +15,8 @@
 //   pack_rows    one thread per row: advance num_pages and tier_tokens;
 //   pack_rank    one 1024-thread block per row: radix-select the keys at the
 //                three tier boundaries (8 passes of 8 bits over 64-bit keys,
-//                exact because keys are unique), then walk the row in index
+//                exact because keys are unique; skipped when the tiers are
+//                given), then walk the row in index
 //                order with a block-wide scan to give every token its tier
 //                page and slot (dest = logical page * 16 + slot, -1 = dropped);
 //   pack_scatter one wave per (token, head): copy or quantize its fields into
@@ -90,7 +92,7 @@ __global__ __launch_bounds__(1024) void pack_rank(PackPlan plan, PackData data)
     const int T = sq.len;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
 
-    if (!plan.dense) {
+    if (!plan.dense && plan.tiers == nullptr) {
         if (tid < 3) {
             has[tid] = sq.n_cum[tid] > 0;
             krem[tid] = (int64_t)sq.n_cum[tid] - 1;
@@ -145,6 +147,9 @@ __global__ __launch_bounds__(1024) void pack_rank(PackPlan plan, PackData data)
         if (i < T) {
             if (plan.dense) {
                 tier = 0;
+            } else if (plan.tiers != nullptr) {
+                const int t = plan.tiers[e];
+                tier = t < 3 ? t : 3;
             } else {
                 const uint64_t K = rank_key(plan, data, e, i);
                 tier = has[0] && K >= thr[0] ? 0 : has[1] && K >= thr[1] ? 1 : has[2] && K >= thr[2] ? 2 : 3;

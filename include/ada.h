@@ -183,6 +183,107 @@ ada_status dense_pack(const ada_geom *geom, const ada_cache *cache, int32_t num_
                       uint64_t *arena_cursor_host, int32_t *num_pages_host, void *ws,
                       size_t ws_bytes, void *stream);
 
+/*
+ * ada_code_error -- angular error of the stored codes of each (token, head),
+ * the input of the RDR distortion surrogate.  [TS] 2.2 (the logit error is
+ * dominated by the angular approximation error, scaled by the query and key
+ * magnitudes).  Reading: the chord error of the code reconstruction,
+ *   err = sum_g || u_g - C_g[code_g] ||^2,  u = k / ||k|| (u = 0 for k = 0),
+ * for the 8-bit codes (err8) and the 4-bit codes (err4); sqrt(err) bounds
+ * |q . (u - u~)| / |q|.  u is formed as in ada_encode; every sum runs in
+ * double (each group over its 8 coordinates, then the groups in order) and
+ * the total is rounded once to f32.
+ *   keys [n_tokens][Hkv][D] fp16 (16-byte aligned); cb8 / cb4 as in
+ *   ada_encode (16-byte aligned); codes8 / codes4 as ada_encode writes them
+ *   (any codes are accepted); err8, err4 [n_tokens][Hkv] f32 out.
+ */
+ada_status ada_code_error(const ada_geom *geom, int64_t n_tokens, const uint16_t *keys,
+                          const float *cb8, const float *cb4, const uint8_t *codes8,
+                          const uint8_t *codes4, float *err8, float *err4, void *stream);
+
+/* Workspace bytes of rdr_solve for num_seqs sequences of n_tokens tokens in
+ * total. */
+size_t rdr_solve_workspace_size(const ada_geom *geom, int32_t num_seqs, int64_t n_tokens);
+
+/*
+ * rdr_solve -- the tier of every (token, head) under a byte budget per
+ * sequence.  [TS] 2.2 (a residency bit and a tier per state from a discrete
+ * rate-distortion allocation under a strict memory budget; the distortion
+ * surrogate; protection keeps a state at the top tier) and [ABS] (retention
+ * and precision follow estimated utility, per token and head).  The pages
+ * give no solver.  Reading:
+ *   rate of a state in tier b: R_b = ada_page_bytes(D, b) / 16, R_3 = 0
+ *     (tier 3 = dropped);
+ *   distortion: D_b = w * r~ * e_b, w = scores (utility), r~ = radius,
+ *     e_0 = 0, e_1 = sqrt(err8), e_2 = sqrt(err4), e_3 = 1 (a dropped key
+ *     keeps none of its direction); the common query magnitude is left out;
+ *   cap = budget_bytes_host[s] - Hkv * 15 * (R_0 + R_1 + R_2): room for the
+ *     partial last page of each tier in every row, so the pages rdr_pack_tiers
+ *     writes for this call stay within the budget;
+ *   every state starts at tier 0; the lower convex hull of its four
+ *     (rate, distortion) points is a chain of demotions of non-decreasing
+ *     slope (distortion added per byte saved); with need = (bytes at tier 0)
+ *     - cap, s* is the least slope such that the demotions of slope <= s*
+ *     over all the sequence's states save at least `need` bytes (+inf when
+ *     none does: every unprotected state is dropped), and each state takes
+ *     the longest prefix of its chain with slopes <= s*.  need <= 0 leaves
+ *     every state at tier 0.  Protected states stay at tier 0.
+ *   The result is optimal, for its own byte count, among all assignments
+ *   (the Lagrangian property).  The chain arithmetic is binary32 in a fixed
+ *   order: wr = w * r~, D_1 = wr * sqrtf(err8), D_2 = wr * sqrtf(err4),
+ *   D_3 = wr, slope = (D_j - D_c) / (R_c - R_j) + 0 (IEEE division and
+ *   square root); the hull walk takes the least slope, the lower rate on
+ *   ties, and a slope below its predecessor is raised to it.
+ *   budget_bytes_host [S] (>= 0).  radius [N][Hkv] fp16, err8 / err4 [N][Hkv]
+ *   f32 (ada_code_error), scores [N][Hkv] f32: finite and >= 0 (device).
+ *   protect [N][Hkv] u8 on the DEVICE (nonzero = protected) or NULL.
+ *   tiers [N][Hkv] u8 out: 0, 1, 2 kept tier, 3 dropped.
+ *   ws: rdr_solve_workspace_size bytes, 256-byte aligned, any content.
+ * Seven kernels on `stream`; the small per-sequence table is copied from
+ * host memory first.
+ */
+ada_status rdr_solve(const ada_geom *geom, int32_t num_seqs, const int32_t *cu_tokens_host,
+                     const int64_t *budget_bytes_host, const uint16_t *radius, const float *err8,
+                     const float *err4, const float *scores, const uint8_t *protect,
+                     uint8_t *tiers, void *ws, size_t ws_bytes, void *stream);
+
+/* Workspace bytes of rdr_tier_counts. */
+size_t rdr_tier_counts_workspace_size(const ada_geom *geom, int32_t num_seqs);
+
+/*
+ * rdr_tier_counts -- tokens of tier 0, 1 and 2 in every row (s, h) of a
+ * tiers array (values other than 0-2 count as dropped), copied to
+ * row_counts_host [S*Hkv][3].  Synchronizes `stream`: the counts are on the
+ * host when the call returns.  They size the pages of rdr_pack_tiers.
+ */
+ada_status rdr_tier_counts(const ada_geom *geom, int32_t num_seqs, const int32_t *cu_tokens_host,
+                           const uint8_t *tiers, int32_t *row_counts_host, void *ws,
+                           size_t ws_bytes, void *stream);
+
+/* Number of pages rdr_pack_tiers creates for these row counts (the length of
+ * its place_perm_host). */
+ada_status rdr_pack_tiers_num_pages(const ada_geom *geom, int32_t num_seqs,
+                                    const int32_t *row_counts_host, int64_t *n_pages_out);
+
+/*
+ * rdr_pack_tiers -- rdr_pack with the tier of every (token, head) given
+ * (rdr_solve's output) instead of ranked from basis points.  [TS] 2.2
+ * (tier-homogeneous pages).  Each row's tokens of one tier keep index order
+ * and fill 16-slot pages; tier values other than 0-2 are dropped.
+ * row_counts_host [S*Hkv][3] must be rdr_tier_counts of the same tiers
+ * (the page plan is built from them on the host; a row's counts may not
+ * exceed its tokens).  Everything else -- page order, placement, value
+ * quantisation, workspace (rdr_pack_workspace_size), errors -- is as in
+ * rdr_pack.
+ */
+ada_status rdr_pack_tiers(const ada_geom *geom, const ada_cache *cache, int32_t num_seqs,
+                          const int32_t *cu_tokens_host, const int32_t *row_counts_host,
+                          const uint8_t *tiers, const uint16_t *keys, const uint16_t *values,
+                          const uint16_t *radius, const uint8_t *codes8, const uint8_t *codes4,
+                          const uint32_t *place_perm_host, const int64_t *pos_base_host,
+                          uint64_t *arena_cursor_host, int32_t *num_pages_host, void *ws,
+                          size_t ws_bytes, void *stream);
+
 /* Split count ada_decode / dense_decode use for num_splits == 0. */
 int32_t ada_decode_default_splits(const ada_geom *geom, int32_t num_seqs,
                                   int32_t max_pages_per_head);

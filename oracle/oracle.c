@@ -644,7 +644,7 @@ enum { OR_OK = 0, OR_EINVAL = 1, OR_ENOSPACE = 3 };
  *   arena / arena_units / cursor (in/out, 128-byte units); page_table and
  *   page_meta [S*Hkv][maxp]; num_pages [S*Hkv]; tier_tokens [S*Hkv][3];
  *   slot_token [S*Hkv][maxp][16] or NULL.
- * tiers [N][Hkv] (0-2 kept tier, 3 dropped), when non-NULL, replaces the
+ * tiers [N][Hkv] (0-2 kept tier, any other value dropped), when non-NULL, replaces the
  * ranking: each row's tokens of a tier keep index order (tier_cum_bp, scores
  * and protect are then unused).
  * dense != 0 packs every token of the call into tier-3 pages instead.
@@ -691,18 +691,17 @@ static int pack_impl(int D, int Hkv, int S, const int32_t *cu_tokens, const int3
                 order[i] = (int32_t)i;
             if (!dense && tiers) {
                 int64_t at = 0, cnt[4] = {0, 0, 0, 0};
+                /* a value above 3 counts as dropped */
                 for (int64_t i = 0; i < T; i++) {
                     int t = tiers[(b + i) * Hkv + h];
-                    if (t > 3) {
-                        rc = OR_EINVAL;
-                        t = 3;
-                    }
-                    cnt[t]++;
+                    cnt[t < 3 ? t : 3]++;
                 }
                 for (int tier = 0; tier < 4; tier++)
-                    for (int64_t i = 0; i < T; i++)
-                        if (tiers[(b + i) * Hkv + h] == tier)
+                    for (int64_t i = 0; i < T; i++) {
+                        int t = tiers[(b + i) * Hkv + h];
+                        if ((t < 3 ? t : 3) == tier)
                             order[at++] = (int32_t)i;
+                    }
                 n_cum[0] = cnt[0];
                 n_cum[1] = cnt[0] + cnt[1];
                 n_cum[2] = cnt[0] + cnt[1] + cnt[2];

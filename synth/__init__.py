@@ -63,13 +63,29 @@ def seq_lens(cfg: Workload) -> np.ndarray:
     return _rng(cfg.seed, "lens").integers(lo, hi + 1, size=cfg.num_seqs).astype(np.int64)
 
 
+def budgets_bp(cfg: Workload) -> np.ndarray:
+    """[S] int64 byte budget of each sequence, in basis points of its dense
+    bf16 cache: drawn per sequence where the workload gives a range, else the
+    workload's fixed budget."""
+    if cfg.budget_range_bp is None:
+        return np.full(cfg.num_seqs, cfg.budget_bp, dtype=np.int64)
+    lo, hi = cfg.budget_range_bp
+    return _rng(cfg.seed, "budgets").integers(lo, hi + 1, size=cfg.num_seqs).astype(np.int64)
+
+
+def budget_bytes(cfg: Workload, lens) -> np.ndarray:
+    """[S] int64 byte budget per sequence for the budget solver: the budget's
+    share of the dense bf16 cache (K and V, 2 bytes each per dim) of the
+    sequence's tokens, rounded down."""
+    dense = np.asarray(lens, dtype=np.int64) * cfg.num_kv_heads * 4 * cfg.head_dim
+    return dense * budgets_bp(cfg) // 10000
+
+
 def tier_mix(cfg: Workload) -> np.ndarray:
     """[S][3] int32 cumulative basis points per sequence."""
     if cfg.tier_cum_bp is not None:
         return np.tile(np.array(cfg.tier_cum_bp, dtype=np.int32), (cfg.num_seqs, 1))
-    lo, hi = cfg.budget_range_bp
-    budgets = _rng(cfg.seed, "budgets").integers(lo, hi + 1, size=cfg.num_seqs)
-    return np.array([mix_for_budget(int(b)) for b in budgets], dtype=np.int32)
+    return np.array([mix_for_budget(int(b)) for b in budgets_bp(cfg)], dtype=np.int32)
 
 
 def cu_tokens(lens) -> np.ndarray:

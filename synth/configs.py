@@ -34,6 +34,7 @@ class Workload:
     len_range: tuple[int, int] | None = None
     tier_cum_bp: tuple[int, int, int] | None = None  # fixed mix for every sequence
     budget_range_bp: tuple[int, int] | None = None   # drawn byte budget per sequence
+    budget_bp: int = 6000        # fixed byte budget (basis points of dense) for the budget solver
     key_outliers: bool = True    # 1% of channels at 8x
     value_scaled: bool = False   # values also get lognormal channel scales
     permuted_pool: bool = False  # pages placed in a seeded random order

@@ -114,3 +114,54 @@ def test_pack_host_errors_leave_host_state_untouched():
     bad_perm = np.zeros(8, np.uint32)
     assert call(arena_units=1 << 20, maxp=64, perm=bad_perm) == ada.EINVAL
     assert cursor[0] == 0 and not npages.any()
+
+
+def test_rdr_entry_points_host_errors():
+    """The budget solver, tier counts and tier-given pack refuse bad host
+    arguments before any launch (device pointers are never dereferenced)."""
+    L = ada.load()
+    g = ada.Geom(64, 4, 2)
+    names = _declared()
+    assert {"ada_code_error", "rdr_solve", "rdr_tier_counts", "rdr_pack_tiers",
+            "rdr_pack_tiers_num_pages"} <= set(names)
+    cu = np.array([0, 10, 30], np.int32)
+    fake = C.c_void_p(256)
+    cup = cu.ctypes.data_as(C.c_void_p)
+
+    def solve(budget, ws_bytes=1 << 20, ws=fake):
+        b = np.asarray(budget, np.int64)
+        return L.rdr_solve(C.byref(g), 2, cup, b.ctypes.data_as(C.c_void_p), fake, fake, fake, fake, None,
+                           fake, ws, ws_bytes, None)
+
+    assert solve([100, -1]) == ada.EINVAL
+    assert solve([100, 100], ws_bytes=16) == ada.EWORKSPACE
+    assert solve([100, 100], ws=C.c_void_p(257)) == ada.EWORKSPACE
+    assert L.rdr_solve(C.byref(g), 2, cup, None, fake, fake, fake, fake, None, fake, fake, 1 << 20,
+                       None) == ada.EINVAL
+    assert ada.solve_workspace_size(g, 2, 30) >= 4 * 256 * 8 * 2
+    # tier counts: null output, too small a workspace
+    assert L.rdr_tier_counts(C.byref(g), 2, cup, fake, None, fake, 1 << 20, None) == ada.EINVAL
+    out = np.zeros((4, 3), np.int32)
+    assert L.rdr_tier_counts(C.byref(g), 2, cup, fake, out.ctypes.data_as(C.c_void_p), fake, 8,
+                             None) == ada.EWORKSPACE
+    # page count from row counts (host arithmetic only)
+    rc = np.array([[3, 16, 17], [0, 0, 1], [16, 0, 0], [0, 0, 0]], np.int32)
+    assert ada.pack_tiers_num_pages(g, rc) == 1 + 1 + 2 + 1 + 1
+    # tier-given pack: a row whose counts exceed its tokens, negative counts
+    cursor = np.zeros(1, np.uint64)
+    npages = np.zeros(4, np.int32)
+    view = ada._CacheView(256, 1 << 20, 256, 256, 256, 256, 0, 2, 64)
+
+    def pack(counts):
+        c = np.asarray(counts, np.int32)
+        return L.rdr_pack_tiers(C.byref(g), C.byref(view), 2, cup, c.ctypes.data_as(C.c_void_p), fake,
+                                fake, fake, fake, fake, fake, None, None,
+                                cursor.ctypes.data_as(C.c_void_p), npages.ctypes.data_as(C.c_void_p),
+                                C.c_void_p(1 << 20), 1 << 30, None)
+
+    assert pack([[5, 5, 1], [0, 0, 0], [0, 0, 0], [0, 0, 0]]) == ada.EINVAL    # 11 > 10 tokens
+    assert pack([[-1, 0, 0], [0, 0, 0], [0, 0, 0], [0, 0, 0]]) == ada.EINVAL
+    assert cursor[0] == 0 and not npages.any()
+    # code error: nothing to do for no tokens; negative counts refused
+    assert L.ada_code_error(C.byref(g), 0, None, None, None, None, None, None, None, None) == ada.OK
+    assert L.ada_code_error(C.byref(g), -2, None, None, None, None, None, None, None, None) == ada.EINVAL

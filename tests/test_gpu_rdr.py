@@ -1,0 +1,182 @@
+"""GPU parity of the RDR pieces through the C ABI against the CPU oracle.
+
+Bars: code errors bit-exact (both sides sum the same doubles in the same
+order and round once); solver tiers bit-exact given the same inputs (the
+decisions are binary32 arithmetic in a fixed order on both sides); tier
+counts exact; pages, tables and metadata of rdr_pack_tiers bit-exact; the
+decode of a solver-built cache within the decode bars (outputs max-abs
+<= 1e-2, lse within 1e-3 * max(|lse|, 1))."""
+import json
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import compressed_kv_attention_amd as ada
+import oracle
+import synth
+from gpu_util import decode_outputs, flush, geom_of, gpu_encode, to_dev, u16
+from helpers import make_case, small_workload
+
+pytestmark = pytest.mark.gpu
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+OUT_TOL = 1e-2
+
+
+def _codes(case):
+    r, c8, c4 = oracle.encode(case["keys"], case["cb8"], case["cb4"], nthreads=8)
+    return r, c8, c4
+
+
+@pytest.mark.parametrize("D", [64, 128])
+def test_code_error_bit_exact(D):
+    cfg = small_workload(D=D, Hq=4, Hkv=2, S=2, T=700, seed=80 + D)
+    case = make_case(cfg, lens=[700, 333])
+    r, c8, c4 = _codes(case)
+    rng = np.random.default_rng(D)
+    rc8 = rng.integers(0, 256, c8.shape).astype(np.uint8)   # any codes, not only the nearest
+    rc4 = rng.integers(0, 256, c4.shape).astype(np.uint8)
+    geom = geom_of(cfg)
+    k = to_dev(case["keys"])
+    cb8, cb4 = to_dev(case["cb8"]), to_dev(case["cb4"])
+    for codes8, codes4, label in ((c8, c4, "nearest"), (rc8, rc4, "random")):
+        flush(f"[code_error] D={D} {label}")
+        e8 = torch.full(c8.shape[:2], float("nan"), device="cuda")
+        e4 = torch.full(c8.shape[:2], float("nan"), device="cuda")
+        ada.code_error(geom, k, cb8, cb4, to_dev(codes8), to_dev(codes4), e8, e4)
+        torch.cuda.synchronize()
+        r8, r4 = oracle.code_error(case["keys"], case["cb8"], case["cb4"], codes8, codes4)
+        assert np.array_equal(e8.cpu().numpy(), r8) and np.array_equal(e4.cpu().numpy(), r4)
+
+
+def _solve_both(geom, D, cu, budgets, r, e8, e4, sc, prot=None):
+    tiers = torch.full(r.shape, 77, dtype=torch.uint8, device="cuda")
+    ada.rdr_solve(geom, cu, budgets, to_dev(r), to_dev(e8), to_dev(e4), to_dev(sc), tiers,
+                  protect=None if prot is None else to_dev(prot))
+    torch.cuda.synchronize()
+    ref = oracle.rdr_solve(D, cu, budgets, r, e8, e4, sc, protect=prot)
+    return tiers.cpu().numpy(), ref
+
+
+def test_rdr_solve_golden_hand_cases():
+    with open(os.path.join(GOLDEN, "rdr_solve_hand.json")) as f:
+        g = json.load(f)
+    st = g["states"]
+    n = len(st)
+    geom = ada.Geom(g["D"], 1, 1)
+    r = np.array([[x["radius"]] for x in st], np.float16).view(np.uint16)
+    e8 = np.array([[x["err8"]] for x in st], np.float32)
+    e4 = np.array([[x["err4"]] for x in st], np.float32)
+    sc = np.array([[x["score"]] for x in st], np.float32)
+    reserve = 15 * (256 + 144 + 72)
+    for case in g["cases"]:
+        pr = None if "protect" not in case else np.array(case["protect"], np.uint8).reshape(n, 1)
+        got, ref = _solve_both(geom, g["D"], [0, n], [case["cap"] + reserve], r, e8, e4, sc, pr)
+        assert got.ravel().tolist() == case["tiers"] == ref.ravel().tolist(), case["note"]
+
+
+@pytest.mark.parametrize("D,H", [(128, 8), (64, 4), (128, 1)])
+def test_rdr_solve_bit_exact_ragged(D, H):
+    """Several sequences (one empty, one of a single token, others spanning
+    several 1024-state blocks with ragged ends), budgets from infeasible to
+    non-binding, with and without protection."""
+    rng = np.random.default_rng(D + H)
+    lens = [700, 0, 1, 2100, 333, 64]
+    cu = synth.cu_tokens(lens)
+    N = int(cu[-1])
+    r = (rng.lognormal(2.0, 0.6, (N, H)).astype(np.float16)).view(np.uint16)
+    e8 = rng.uniform(0.05, 0.5, (N, H)).astype(np.float32)
+    e4 = (e8 + rng.uniform(-0.05, 0.5, (N, H))).clip(0, 2).astype(np.float32)
+    sc = np.minimum(rng.zipf(1.1, (N, H)), 1 << 24).astype(np.float32)
+    sc[rng.random((N, H)) < 0.01] = 0.0           # zero utility: free to drop
+    prot = (rng.random((N, H)) < 0.02).astype(np.uint8)
+    R0 = ada.page_bytes(D, 0) // 16
+    dense = np.array(lens, np.int64) * H * R0
+    geom = ada.Geom(D, H, H)
+    for frac in (0.0, 0.1, 0.35, 0.6, 0.9, 1.2):
+        budgets = (dense * frac).astype(np.int64)
+        for pr in (None, prot):
+            flush(f"[solve] D={D} H={H} budget {frac} protect={pr is not None}")
+            got, ref = _solve_both(geom, D, cu, budgets, r, e8, e4, sc, pr)
+            assert np.array_equal(got, ref), int((got != ref).sum())
+
+
+def test_tier_counts_and_pack_tiers_bit_exact_then_decode():
+    cfg = small_workload(D=128, Hq=8, Hkv=2, S=3, T=900, seed=90)
+    lens = [900, 250, 17]
+    case = make_case(cfg, lens=lens)
+    geom = geom_of(cfg)
+    r, c8, c4 = _codes(case)
+    e8, e4 = oracle.code_error(case["keys"], case["cb8"], case["cb4"], c8, c4)
+    budgets = synth.budget_bytes(cfg, lens) * 5 // 6
+    tiers = oracle.rdr_solve(128, case["cu"], budgets, r, e8, e4, case["scores"].numpy())
+    counts = oracle.row_tier_counts(case["cu"], tiers)
+    flush("[tier_counts]")
+    got = ada.tier_counts(geom, case["cu"], to_dev(tiers))
+    assert np.array_equal(got, counts)
+    n_pages = ada.pack_tiers_num_pages(geom, counts)
+    perm = np.random.default_rng(5).permutation(n_pages).astype(np.uint32)
+    maxp = max(lens) // 16 + 4
+    arena = int(sum(lens) * 2 * 512 + 3 * 2 * 3 * 8192)
+    hc = oracle.HostCache(128, 2, 3, maxp, arena)
+    assert oracle.pack_tiers(hc, case["cu"], tiers, case["keys"], case["values"], r, c8, c4,
+                             place_perm=perm) == 0
+    flush("[pack_tiers]")
+    dc = ada.Cache(geom, 3, maxp, arena, slot_tokens=True)
+    ada.rdr_pack_tiers(geom, dc, case["cu"], got, to_dev(tiers), to_dev(case["keys"]),
+                       to_dev(case["values"]), to_dev(r), to_dev(c8), to_dev(c4), place_perm=perm)
+    torch.cuda.synchronize()
+    assert int(dc.cursor[0]) == int(hc.cursor[0])
+    used = int(hc.cursor[0]) * 128
+    assert np.array_equal(dc.arena[:used].cpu().numpy(), hc.arena[:used])
+    assert np.array_equal(dc.page_table.cpu().numpy().view(np.uint32), hc.page_table)
+    assert np.array_equal(dc.page_meta.cpu().numpy(), hc.page_meta)
+    assert np.array_equal(dc.num_pages.cpu().numpy(), hc.num_pages)
+    assert np.array_equal(dc.tier_tokens.cpu().numpy(), hc.tier_tokens)
+    assert np.array_equal(dc.slot_token.cpu().numpy(), hc.slot_token)
+    assert np.array_equal(dc.num_pages_host, hc.num_pages)
+    # the stored bytes stay within each sequence's budget
+    for s in range(3):
+        rows = slice(2 * s, 2 * s + 2)
+        b = sum(oracle.page_bytes(128, k) * -(-int(c) // 16) for row in counts[rows] for k, c in enumerate(row))
+        assert b <= budgets[s]
+    flush("[decode of the solver-built cache]")
+    ref = oracle.decode(hc, case["cb8"], case["cb4"], case["q"], cfg.sigma, nthreads=8)
+    out, lse, _ = decode_outputs(geom, dc, to_dev(case["q"]), with_logits=False)
+    ada.decode(geom, dc, to_dev(case["cb8"]), to_dev(case["cb4"]), to_dev(case["q"]), cfg.sigma, out, lse)
+    torch.cuda.synchronize()
+    assert np.abs(out.cpu().double().numpy() - ref["out"]).max() <= OUT_TOL
+    l = lse.cpu().double().numpy()
+    fin = np.isfinite(ref["lse"])  # a row left with no pages has lse = -inf
+    assert np.array_equal(np.isfinite(l), fin) and (l[~fin] == -np.inf).all()
+    assert (np.abs(l[fin] - ref["lse"][fin]) <= 1e-3 * np.maximum(np.abs(ref["lse"][fin]), 1.0)).all()
+
+
+def test_gpu_encode_error_solve_chain_matches_oracle():
+    """The append path on the GPU (encode -> code error -> solve -> counts)
+    equals the oracle's on the same keys and codes, bit for bit."""
+    cfg = small_workload(D=64, Hq=8, Hkv=4, S=2, T=1500, seed=91)
+    lens = [1500, 611]
+    case = make_case(cfg, lens=lens)
+    geom = geom_of(cfg)
+    k = to_dev(case["keys"])
+    cb8, cb4 = to_dev(case["cb8"]), to_dev(case["cb4"])
+    flush("[chain] encode + code error + solve on the GPU")
+    r, c8, c4 = gpu_encode(geom, k, cb8, cb4)
+    e8 = torch.empty(r.shape, device="cuda")
+    e4 = torch.empty(r.shape, device="cuda")
+    ada.code_error(geom, k, cb8, cb4, c8, c4, e8, e4)
+    budgets = synth.budget_bytes(cfg, lens) // 2
+    tiers = torch.empty(r.shape, dtype=torch.uint8, device="cuda")
+    ada.rdr_solve(geom, case["cu"], budgets, r, e8, e4, to_dev(case["scores"]), tiers)
+    counts = ada.tier_counts(geom, case["cu"], tiers)
+    # (the oracle takes the GPU's codes: encode parity, near-ties included,
+    # is tested on its own)
+    rr, rc8, rc4 = u16(r), c8.cpu().numpy(), c4.cpu().numpy()
+    re8, re4 = oracle.code_error(case["keys"], case["cb8"], case["cb4"], rc8, rc4)
+    assert np.array_equal(e8.cpu().numpy(), re8) and np.array_equal(e4.cpu().numpy(), re4)
+    rt = oracle.rdr_solve(64, case["cu"], budgets, rr, re8, re4, case["scores"].numpy())
+    assert np.array_equal(tiers.cpu().numpy(), rt)
+    assert np.array_equal(counts, oracle.row_tier_counts(case["cu"], rt))

@@ -280,7 +280,8 @@ def test_pack_tiers_places_every_kept_state_once():
                     assert tiers[case["cu"][s] + tok, h] == tier
                     seen[case["cu"][s] + tok, h] += 1
     assert np.array_equal(seen, (tiers < 3).astype(np.int32))
-    bad = tiers.copy()
-    bad[0, 0] = 9
+    # a value above 3 is a drop
+    odd = np.where(tiers == 3, 200, tiers).astype(np.uint8)
     hc3 = oracle.HostCache(64, 2, 2, 16, 1 << 20)
-    assert oracle.pack_tiers(hc3, case["cu"], bad, case["keys"], case["values"], r, c8, c4) == 1
+    assert oracle.pack_tiers(hc3, case["cu"], odd, case["keys"], case["values"], r, c8, c4) == 0
+    assert np.array_equal(hc3.arena, hc.arena) and np.array_equal(hc3.slot_token, hc.slot_token)
