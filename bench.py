@@ -212,7 +212,8 @@ def append_path(dev, reps=20):
     c8 = torch.empty((S * n, H, D // 8), dtype=torch.uint8, device=dev)
     c4 = torch.empty((S * n, H, D // 16), dtype=torch.uint8, device=dev)
     per_call = S * H * (n // 16 + 3) * ada.page_bytes(D, 0)  # a bound: every page at the largest size
-    cache = ada.Cache(geom, S, (reps + 2) * (n // 16 + 3), per_call * (reps + 2))
+    calls = 2 * reps + 2  # the ranked path, then the budget-solver path
+    cache = ada.Cache(geom, S, calls * (n // 16 + 3), per_call * calls)
     ws = torch.zeros(ada.pack_workspace_size(geom, S * n, S), dtype=torch.uint8, device=dev)
     pos = np.zeros(S, np.int64)
     ada.encode(geom, keys, cb8, cb4, r, c8, c4)
@@ -231,10 +232,95 @@ def append_path(dev, reps=20):
         enc += e[0].elapsed_time(e[1])
         pack += e[1].elapsed_time(e[2])
     th = S * n * H
-    return {"workload": f"{cfg.name} append, one layer", "tokens": S * n, "token_heads": th,
-            "encode_us": enc / reps * 1e3, "pack_us": pack / reps * 1e3,
-            "token_heads_per_s": th / ((enc + pack) / reps / 1e3),
-            "note": "pack includes its host plan and the plan's host-to-device copy"}
+    res = {"workload": f"{cfg.name} append, one layer", "tokens": S * n, "token_heads": th,
+           "encode_us": enc / reps * 1e3, "pack_us": pack / reps * 1e3,
+           "token_heads_per_s": th / ((enc + pack) / reps / 1e3),
+           "note": "pack includes its host plan and the plan's host-to-device copy"}
+    # the same append with the budget solver choosing the tiers (60% budget)
+    e8 = torch.empty((S * n, H), device=dev)
+    e4 = torch.empty((S * n, H), device=dev)
+    tiers = torch.empty((S * n, H), dtype=torch.uint8, device=dev)
+    budgets = synth.budget_bytes(cfg, np.full(S, n, np.int64))
+    sws = torch.zeros(ada.solve_workspace_size(geom, S, S * n), dtype=torch.uint8, device=dev)
+    e = [torch.cuda.Event(enable_timing=True) for _ in range(6)]
+    t = np.zeros(5)
+    for i in range(reps):
+        pos += n
+        e[0].record()
+        ada.encode(geom, keys, cb8, cb4, r, c8, c4)
+        e[1].record()
+        ada.code_error(geom, keys, cb8, cb4, c8, c4, e8, e4)
+        e[2].record()
+        ada.rdr_solve(geom, cu, budgets, r, e8, e4, scores, tiers, ws=sws)
+        e[3].record()
+        counts = ada.tier_counts(geom, cu, tiers)
+        e[4].record()
+        ada.rdr_pack_tiers(geom, cache, cu, counts, tiers, keys, vals, r, c8, c4, pos_base=pos, ws=ws)
+        e[5].record()
+        torch.cuda.synchronize()
+        t += [e[k].elapsed_time(e[k + 1]) for k in range(5)]
+    t = t / reps * 1e3
+    res["solver"] = {"budget_bp": int(synth.budgets_bp(cfg)[0]), "encode_us": t[0], "code_error_us": t[1],
+                     "solve_us": t[2], "tier_counts_us": t[3], "pack_tiers_us": t[4],
+                     "token_heads_per_s": th / (t.sum() / 1e6),
+                     "note": "tier_counts includes its device-to-host copy and stream synchronization"}
+    return res
+
+
+def solver_full(cfg, dev, reps=5):
+    """Times the budget solver over a whole workload (one layer): code error,
+    solve, tier counts and tier-given pack of every token."""
+    S, H, D = cfg.num_seqs, cfg.num_kv_heads, cfg.head_dim
+    geom = ada.Geom(D, cfg.num_q_heads, H)
+    lens = synth.seq_lens(cfg)
+    cu = synth.cu_tokens(lens)
+    N = int(cu[-1])
+    keys = synth.keys(cfg, 0, N, dev)
+    vals = synth.values(cfg, 0, N, dev)
+    scores = synth.scores(cfg, 0, N).to(dev)
+    cb8, cb4 = (t.to(dev) for t in synth.codebooks(cfg, 0))
+    r = torch.empty((N, H), dtype=torch.float16, device=dev)
+    c8 = torch.empty((N, H, D // 8), dtype=torch.uint8, device=dev)
+    c4 = torch.empty((N, H, D // 16), dtype=torch.uint8, device=dev)
+    ada.encode(geom, keys, cb8, cb4, r, c8, c4)
+    e8 = torch.empty((N, H), device=dev)
+    e4 = torch.empty((N, H), device=dev)
+    tiers = torch.empty((N, H), dtype=torch.uint8, device=dev)
+    budgets = synth.budget_bytes(cfg, lens)
+    sws = torch.zeros(ada.solve_workspace_size(geom, S, N), dtype=torch.uint8, device=dev)
+    pws = torch.zeros(ada.pack_workspace_size(geom, N, S), dtype=torch.uint8, device=dev)
+    e = [torch.cuda.Event(enable_timing=True) for _ in range(6)]
+    t = np.zeros(4)
+    stored = 0
+    for i in range(reps + 1):
+        e[0].record()
+        ada.code_error(geom, keys, cb8, cb4, c8, c4, e8, e4)
+        e[1].record()
+        ada.rdr_solve(geom, cu, budgets, r, e8, e4, scores, tiers, ws=sws)
+        e[2].record()
+        counts = ada.tier_counts(geom, cu, tiers)
+        e[3].record()
+        stored = sum(ada.page_bytes(D, k) * ((counts[:, k] + 15) // 16).sum() for k in range(3))
+        cache = ada.Cache(geom, S, int(max(lens)) // 16 + 4, int(stored))
+        torch.cuda.synchronize()
+        e[4].record()
+        ada.rdr_pack_tiers(geom, cache, cu, counts, tiers, keys, vals, r, c8, c4, ws=pws)
+        e[5].record()
+        torch.cuda.synchronize()
+        if i > 0:  # the first round warms up
+            t += [e[0].elapsed_time(e[1]), e[1].elapsed_time(e[2]), e[2].elapsed_time(e[3]),
+                  e[4].elapsed_time(e[5])]
+        del cache
+    t = t / reps * 1e3
+    th = N * H
+    mix = np.bincount(tiers.cpu().numpy().ravel(), minlength=4) / th
+    dense = int(np.asarray(lens, np.int64).sum()) * H * 4 * D
+    return {"workload": cfg.name, "token_heads": th, "budget_bp": [int(x) for x in np.unique(synth.budgets_bp(cfg))][:4],
+            "code_error_us": t[0], "solve_us": t[1], "tier_counts_us": t[2], "pack_tiers_us": t[3],
+            "solve_token_heads_per_s": th / (t[1] / 1e6), "tier_mix": [round(float(x), 4) for x in mix],
+            "stored_fraction_of_dense": stored / dense,
+            "note": "tier_counts includes its device-to-host copy and stream synchronization; "
+                    "pack_tiers its host plan and the plan's copy"}
 
 
 def stream_bytes(L):
@@ -283,6 +369,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--no-append", action="store_true", help="skip the append-path timing")
+    ap.add_argument("--solver-full", action="store_true",
+                    help="also time the budget solver over the whole workload")
     ap.add_argument("--eager", action="store_true",
                     help="time eager launches instead of graph replays (for profilers)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
@@ -393,8 +481,17 @@ def main():
     torch.cuda.synchronize()
     if not args.no_append:
         result["append_path"] = append_path(dev)
-        log(f"append path: encode {result['append_path']['encode_us']:.1f} us, "
-            f"pack {result['append_path']['pack_us']:.1f} us per layer")
+        ap = result["append_path"]
+        log(f"append path: encode {ap['encode_us']:.1f} us, pack {ap['pack_us']:.1f} us per layer; "
+            f"with the budget solver: code error {ap['solver']['code_error_us']:.1f} us, "
+            f"solve {ap['solver']['solve_us']:.1f} us, counts {ap['solver']['tier_counts_us']:.1f} us, "
+            f"pack {ap['solver']['pack_tiers_us']:.1f} us")
+    if args.solver_full:
+        result["solver_full"] = solver_full(cfg, dev)
+        sf = result["solver_full"]
+        log(f"budget solver over the workload: code error {sf['code_error_us']:.1f} us, "
+            f"solve {sf['solve_us']:.1f} us, counts {sf['tier_counts_us']:.1f} us, "
+            f"pack {sf['pack_tiers_us']:.1f} us; mix {sf['tier_mix']}")
     # numerics check of the timed outputs against the oracle (CPU baseline leg)
     if not args.no_cpu_baseline:
         cb = cpu_baseline(cfg, 0)

@@ -221,3 +221,84 @@ def test_workload6_qwen_shape_gqa5_t32k():
 
 def test_workload7_gpt_oss_shape_gqa8_d64_t32k():
     _run(7, 0, [0])
+
+
+def _run_solver(number, layer, seqs):
+    """The append path with the budget solver at full size: GPU encode, code
+    error, solve under each sequence's byte budget, tier counts, tier-given
+    pack into a permuted pool, decode; then the oracle on the sampled
+    sequences (each sequence's solve depends on no other)."""
+    cfg = synth.WORKLOADS[number]
+    label = f"workload {number} budget solver"
+    H, D, S = cfg.num_kv_heads, cfg.head_dim, cfg.num_seqs
+    geom = ada.Geom(D, cfg.num_q_heads, H)
+    lens = synth.seq_lens(cfg)
+    cu = synth.cu_tokens(lens)
+    N = int(cu[-1])
+    budgets = synth.budget_bytes(cfg, lens)
+    flush(f"[{label}] GPU encode, code error and solve of {N} tokens x {H} heads")
+    keys = synth.keys(cfg, layer, N, "cuda")
+    vals = synth.values(cfg, layer, N, "cuda")
+    scores = synth.scores(cfg, layer, N)
+    q = synth.queries(cfg, layer, "cuda")
+    cb8, cb4 = synth.codebooks(cfg, layer)
+    cb8d, cb4d = cb8.cuda(), cb4.cuda()
+    r, c8, c4 = _gpu_encode(geom, keys, cb8d, cb4d)
+    e8 = torch.empty((N, H), device="cuda")
+    e4 = torch.empty((N, H), device="cuda")
+    ada.code_error(geom, keys, cb8d, cb4d, c8, c4, e8, e4)
+    tiers = torch.empty((N, H), dtype=torch.uint8, device="cuda")
+    ada.rdr_solve(geom, cu, budgets, r, e8, e4, scores.cuda(), tiers)
+    counts = ada.tier_counts(geom, cu, tiers)
+    n_pages = ada.pack_tiers_num_pages(geom, counts)
+    per_seq = np.zeros(S, np.int64)
+    for s in range(S):
+        for row in counts[s * H:(s + 1) * H]:
+            per_seq[s] += sum(ada.page_bytes(D, k) * -(-int(c) // 16) for k, c in enumerate(row))
+    assert (per_seq <= budgets).all(), f"{label}: a sequence exceeds its budget"
+    maxp = int(max(lens)) // 16 + 4
+    dc = ada.Cache(geom, S, maxp, int(per_seq.sum()))
+    ada.rdr_pack_tiers(geom, dc, cu, counts, tiers, keys, vals, r, c8, c4,
+                       place_perm=synth.place_perm(cfg, layer, n_pages))
+    out = torch.full((S, cfg.num_q_heads, D), float("nan"), device="cuda")
+    lse = torch.full((S, cfg.num_q_heads), float("nan"), device="cuda")
+    ada.decode(geom, dc, cb8d, cb4d, q, cfg.sigma, out, lse)
+    torch.cuda.synchronize()
+    _check_pool_tiling(label, dc, geom)
+    mix = np.bincount(tiers.cpu().numpy().ravel(), minlength=4) / (N * H)
+    flush(f"[{label}] tier mix {np.round(mix, 3)}, stored {per_seq.sum() / 1e6:.1f} MB")
+
+    sl = [slice(int(cu[s]), int(cu[s + 1])) for s in seqs]
+    k_s = torch.cat([keys[x] for x in sl]).cpu()
+    v_s = torch.cat([vals[x] for x in sl]).cpu()
+    sc_s = torch.cat([scores[x] for x in sl]).numpy()
+    g_r = torch.cat([r[x] for x in sl])
+    g_c8 = torch.cat([c8[x] for x in sl])
+    g_c4 = torch.cat([c4[x] for x in sl])
+    flush(f"[{label}] oracle on {len(k_s)} tokens x {H} heads ({NTHREADS} threads)")
+    _check_codes(label, g_r, g_c8, g_c4, k_s, cb8, cb4)
+    # downstream of the codes the oracle takes the GPU's (near-ties included)
+    gr, gc8, gc4 = u16(g_r), g_c8.cpu().numpy(), g_c4.cpu().numpy()
+    re8, re4 = oracle.code_error(k_s, cb8, cb4, gc8, gc4)
+    assert np.array_equal(torch.cat([e8[x] for x in sl]).cpu().numpy(), re8), f"{label}: err8"
+    assert np.array_equal(torch.cat([e4[x] for x in sl]).cpu().numpy(), re4), f"{label}: err4"
+    lens_s = lens[seqs]
+    cu_s = synth.cu_tokens(lens_s)
+    rt = oracle.rdr_solve(D, cu_s, budgets[seqs], gr, re8, re4, sc_s)
+    assert np.array_equal(torch.cat([tiers[x] for x in sl]).cpu().numpy(), rt), f"{label}: tiers"
+    flush(f"[{label}] code errors and tiers of the sampled sequences bit-exact")
+    hc = oracle.HostCache(D, H, len(seqs), maxp, int(per_seq[seqs].sum()) + 4096, slot_tokens=False)
+    assert oracle.pack_tiers(hc, cu_s, rt, k_s, v_s, gr, gc8, gc4) == 0
+    _compare_rows(label, dc, dc.arena, hc, seqs, H, D)
+    ref = oracle.decode(hc, cb8, cb4, q[seqs].cpu(), cfg.sigma, nthreads=NTHREADS)
+    _check_outputs(label, out, lse, ref, seqs)
+
+
+def test_workload4_ragged64_with_budget_solver():
+    lens = synth.seq_lens(synth.WORKLOADS[4])
+    seqs = sorted({int(np.argmin(lens)), int(np.argmax(lens)), 17})
+    _run_solver(4, 0, seqs)
+
+
+def test_workload2_budget_solver_60pct():
+    _run_solver(2, 0, [0])
