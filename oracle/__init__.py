@@ -60,6 +60,10 @@ def lib():
         L.oracle_dense_pack.restype = I
         L.oracle_decode.argtypes = [I, I, I, I, I, P, P, P, P, P, P, P, D_, P, P, P, P, I64, I64, I]
         L.oracle_decode.restype = I
+        L.oracle_decode_sym.argtypes = L.oracle_decode.argtypes
+        L.oracle_decode_sym.restype = I
+        L.oracle_query_codes.argtypes = [I, I, I, I, P, P, P, P, P, P]
+        L.oracle_query_codes.restype = I
         L.oracle_dense_attention.argtypes = [I, I64, P, P, P, D_, P, P]
         L.oracle_f16_to_double.argtypes = [C.c_uint16]
         L.oracle_f16_to_double.restype = D_
@@ -283,10 +287,11 @@ def dense_pack(cache: HostCache, cu_tokens, keys, values, place_perm=None) -> in
                                    _p(cache.num_pages), cache.maxp)
 
 
-def decode(cache: HostCache, cb8, cb4, q, sigma, units=None, logits=False, nthreads=1):
+def decode(cache: HostCache, cb8, cb4, q, sigma, units=None, logits=False, nthreads=1, sym=False):
     """One decode step.  q [S][Hq][D] bf16.  Returns dict(out [S][Hq][D],
     lse [S][Hq]) (+ logits, logits_explicit [S][Hq][maxp*16], NaN where no
-    retained slot) in double.  `units` = (begin, end) range of s*Hq + hq."""
+    retained slot) in double.  `units` = (begin, end) range of s*Hq + hq.
+    sym: the symmetric variant (the query's direction quantized too)."""
     qq = _u16(q)
     S, Hq, D = qq.shape
     c8 = _np(cb8, np.float32) if cb8 is not None else np.zeros((cache.Hkv, D // 8, 256, 8), np.float32)
@@ -296,15 +301,29 @@ def decode(cache: HostCache, cb8, cb4, q, sigma, units=None, logits=False, nthre
     lg = np.full((S, Hq, cache.maxp * SLOTS), np.nan) if logits else None
     lx = np.full((S, Hq, cache.maxp * SLOTS), np.nan) if logits else None
     b, e = units if units is not None else (0, S * Hq)
-    rc = lib().oracle_decode(D, Hq, cache.Hkv, S, cache.maxp, _p(cache.arena),
-                             _p(cache.page_table), _p(cache.page_meta), _p(cache.num_pages),
-                             _p(c8), _p(c4), _p(qq), float(sigma), _p(out), _p(lse), _p(lg), _p(lx),
-                             b, e, nthreads)
+    fn = lib().oracle_decode_sym if sym else lib().oracle_decode
+    rc = fn(D, Hq, cache.Hkv, S, cache.maxp, _p(cache.arena), _p(cache.page_table),
+            _p(cache.page_meta), _p(cache.num_pages), _p(c8), _p(c4), _p(qq), float(sigma), _p(out),
+            _p(lse), _p(lg), _p(lx), b, e, nthreads)
     assert rc == 0
     res = {"out": out, "lse": lse}
     if logits:
         res["logits"], res["logits_explicit"] = lg, lx
     return res
+
+
+def query_codes(q, cb8, cb4):
+    """Symmetric variant: the query codes (qc8, qc4 int32 [S][Hq][G]) and
+    |q| [S][Hq] of every (sequence, q-head)."""
+    qq = _u16(q)
+    S, Hq, D = qq.shape
+    c8, c4 = _np(cb8, np.float32), _np(cb4, np.float32)
+    Hkv = c8.shape[0]
+    qc8 = np.zeros((S, Hq, D // 8), np.int32)
+    qc4 = np.zeros((S, Hq, D // 8), np.int32)
+    qn = np.zeros((S, Hq))
+    assert lib().oracle_query_codes(D, Hq, Hkv, S, _p(qq), _p(c8), _p(c4), _p(qc8), _p(qc4), _p(qn)) == 0
+    return qc8, qc4, qn
 
 
 def dense_attention(q, K, V, sigma):

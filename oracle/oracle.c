@@ -892,6 +892,16 @@ int oracle_dense_pack(int D, int Hkv, int S, const int32_t *cu_tokens, const uin
 /* v^ is the stored bf16 value, or int8 * scale in the 4-bit tier.           */
 /* Reading: no causal mask (decode attends to every cached token);          */
 /* q-head hq reads kv-head hq / (Hq / Hkv).                                 */
+/*                                                                           */
+/* Symmetric variant.  [TS] 2.1 writes f_b(c_q, c_k): a cosine computed from */
+/* the angular codes of both the query and the key.  Reading: the query's    */
+/* unit direction u_q = q / |q| (|q| summed sequentially over D, in double)  */
+/* takes, per group and per codebook, the index of its nearest codeword      */
+/* exactly as a key does in encode, and                                     */
+/*     l(t) = sigma * |q| * r~_t * sum_g C_g[cq_g] . C_g[code_{t,g}],         */
+/* with the 8-bit codebook for 8-bit keys and the 4-bit codebook for 4-bit   */
+/* keys.  As a table, LUT_g[c] = |q| C_g[cq_g] . C_g[c]: the asymmetric      */
+/* table with q_g replaced by |q| C_g[cq_g].  fp16-tier keys keep sigma q.k. */
 /* ------------------------------------------------------------------------ */
 
 typedef struct {
@@ -907,7 +917,26 @@ typedef struct {
     double *lse;             /* [S][Hq] */
     double *logits;          /* [S][Hq][maxp*16] or NULL */
     double *logits_explicit; /* same, or NULL */
+    int sym;                 /* symmetric (query codes) variant for coded keys */
 } decode_args;
+
+/* Query codes of the symmetric variant: per group, the nearest codeword of
+ * u_q = q / |q| in the 8-bit and the 4-bit codebook; returns |q|. */
+static double query_codes(int D, const double *q, const float *cb8, const float *cb4, int *cq8, int *cq4)
+{
+    int G = D / 8;
+    double ss = 0, u[128];
+    for (int j = 0; j < D; j++)
+        ss += q[j] * q[j];
+    double qn = sqrt(ss);
+    for (int j = 0; j < D; j++)
+        u[j] = qn > 0 ? q[j] / qn : 0.0;
+    for (int g = 0; g < G; g++) {
+        cq8[g] = nearest(u + 8 * g, cb8 + (size_t)g * 256 * 8, 256, NULL);
+        cq4[g] = nearest(u + 8 * g, cb4 + (size_t)g * 16 * 8, 16, NULL);
+    }
+    return qn;
+}
 
 static void decode_unit(const decode_args *a, int64_t unit)
 {
@@ -917,6 +946,22 @@ static void decode_unit(const decode_args *a, int64_t unit)
     double q[128];
     for (int j = 0; j < D; j++)
         q[j] = bf16_to_double(a->q[((int64_t)s * a->Hq + hq) * D + j]);
+    /* The query the coded tiers see: q itself, or in the symmetric variant
+     * |q| times the codeword reconstruction of its direction (one per
+     * codebook). */
+    double q8[128], q4[128];
+    for (int j = 0; j < D; j++)
+        q8[j] = q4[j] = q[j];
+    if (a->sym) {
+        int cq8[16], cq4[16];
+        const float *c8h = a->cb8 + (size_t)hkv * G * 256 * 8, *c4h = a->cb4 + (size_t)hkv * G * 16 * 8;
+        double qn = query_codes(D, q, c8h, c4h, cq8, cq4);
+        for (int g = 0; g < G; g++)
+            for (int j = 0; j < 8; j++) {
+                q8[8 * g + j] = qn * (double)c8h[((size_t)g * 256 + cq8[g]) * 8 + j];
+                q4[8 * g + j] = qn * (double)c4h[((size_t)g * 16 + cq4[g]) * 8 + j];
+            }
+    }
     /* Per-group tables LUT_g[c] = q_g . C_g[c]: 256 entries (8-bit), 16 (4-bit). */
     double *lut8 = malloc(sizeof(double) * (size_t)G * 256);
     double *lut4 = malloc(sizeof(double) * (size_t)G * 16);
@@ -925,14 +970,14 @@ static void decode_unit(const decode_args *a, int64_t unit)
             const float *w = a->cb8 + (((size_t)hkv * G + g) * 256 + c) * 8;
             double acc = 0;
             for (int j = 0; j < 8; j++)
-                acc += q[8 * g + j] * (double)w[j];
+                acc += q8[8 * g + j] * (double)w[j];
             lut8[g * 256 + c] = acc;
         }
         for (int c = 0; c < 16; c++) {
             const float *w = a->cb4 + (((size_t)hkv * G + g) * 16 + c) * 8;
             double acc = 0;
             for (int j = 0; j < 8; j++)
-                acc += q[8 * g + j] * (double)w[j];
+                acc += q4[8 * g + j] * (double)w[j];
             lut4[g * 16 + c] = acc;
         }
     }
@@ -976,8 +1021,9 @@ static void decode_unit(const decode_args *a, int64_t unit)
                         w = a->cb4 + (((size_t)hkv * G + g) * 16 + c) * 8;
                     }
                     /* explicit form: rebuild the coded direction, then dot */
+                    const double *qq = tier == 1 ? q8 : q4;
                     for (int j = 0; j < 8; j++)
-                        dot += q[8 * g + j] * (double)w[j];
+                        dot += qq[8 * g + j] * (double)w[j];
                 }
                 l = a->sigma * r * sum;
                 lx = a->sigma * r * dot;
@@ -1051,16 +1097,16 @@ static void *decode_worker(void *p)
  * of (sequence, q-head) units, s * Hq + hq (for bounded samples); the rest
  * of out/lse is left untouched.  nthreads > 1 runs independent units on
  * separate threads.  Returns 0, or 1 on bad geometry. */
-int oracle_decode(int D, int Hq, int Hkv, int S, int maxp, const uint8_t *arena,
-                  const uint32_t *page_table, const uint8_t *page_meta, const int32_t *num_pages,
-                  const float *cb8, const float *cb4, const uint16_t *q, double sigma, double *out,
-                  double *lse, double *logits, double *logits_explicit, int64_t units_begin,
-                  int64_t units_end, int nthreads)
+static int decode_impl(int D, int Hq, int Hkv, int S, int maxp, const uint8_t *arena,
+                       const uint32_t *page_table, const uint8_t *page_meta, const int32_t *num_pages,
+                       const float *cb8, const float *cb4, const uint16_t *q, double sigma, double *out,
+                       double *lse, double *logits, double *logits_explicit, int64_t units_begin,
+                       int64_t units_end, int nthreads, int sym)
 {
     if ((D != 64 && D != 128) || Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0 || S < 0)
         return 1;
     decode_args a = {D, Hq, Hkv, S, maxp, arena, page_table, page_meta, num_pages, cb8, cb4,
-                     q, sigma, out, lse, logits, logits_explicit};
+                     q, sigma, out, lse, logits, logits_explicit, sym};
     int64_t n = units_end - units_begin;
     if (n <= 0)
         return 0;
@@ -1084,6 +1130,50 @@ int oracle_decode(int D, int Hq, int Hkv, int S, int maxp, const uint8_t *arena,
     if (nthreads > 1)
         for (int t = 0; t < nthreads; t++)
             pthread_join(th[t], NULL);
+    return 0;
+}
+
+int oracle_decode(int D, int Hq, int Hkv, int S, int maxp, const uint8_t *arena,
+                  const uint32_t *page_table, const uint8_t *page_meta, const int32_t *num_pages,
+                  const float *cb8, const float *cb4, const uint16_t *q, double sigma, double *out,
+                  double *lse, double *logits, double *logits_explicit, int64_t units_begin,
+                  int64_t units_end, int nthreads)
+{
+    return decode_impl(D, Hq, Hkv, S, maxp, arena, page_table, page_meta, num_pages, cb8, cb4, q, sigma,
+                       out, lse, logits, logits_explicit, units_begin, units_end, nthreads, 0);
+}
+
+/* The symmetric variant (query codes); arguments as oracle_decode. */
+int oracle_decode_sym(int D, int Hq, int Hkv, int S, int maxp, const uint8_t *arena,
+                      const uint32_t *page_table, const uint8_t *page_meta, const int32_t *num_pages,
+                      const float *cb8, const float *cb4, const uint16_t *q, double sigma, double *out,
+                      double *lse, double *logits, double *logits_explicit, int64_t units_begin,
+                      int64_t units_end, int nthreads)
+{
+    return decode_impl(D, Hq, Hkv, S, maxp, arena, page_table, page_meta, num_pages, cb8, cb4, q, sigma,
+                       out, lse, logits, logits_explicit, units_begin, units_end, nthreads, 1);
+}
+
+/* Query codes of the symmetric variant for every (sequence, q-head):
+ * qc8, qc4 [S][Hq][G]; qnorm [S][Hq]. */
+int oracle_query_codes(int D, int Hq, int Hkv, int S, const uint16_t *qbits, const float *cb8,
+                       const float *cb4, int32_t *qc8, int32_t *qc4, double *qnorm)
+{
+    if ((D != 64 && D != 128) || Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0 || S < 0)
+        return 1;
+    int G = D / 8;
+    for (int64_t u = 0; u < (int64_t)S * Hq; u++) {
+        int hkv = (int)(u % Hq) / (Hq / Hkv);
+        double q[128];
+        int c8[16], c4[16];
+        for (int j = 0; j < D; j++)
+            q[j] = bf16_to_double(qbits[u * D + j]);
+        qnorm[u] = query_codes(D, q, cb8 + (size_t)hkv * G * 256 * 8, cb4 + (size_t)hkv * G * 16 * 8, c8, c4);
+        for (int g = 0; g < G; g++) {
+            qc8[u * G + g] = c8[g];
+            qc4[u * G + g] = c4[g];
+        }
+    }
     return 0;
 }
 
