@@ -107,6 +107,10 @@ def load():
         L.dense_decode.restype = C.c_int
         L.ada_decode_stream.argtypes = [G, CV, P, P, P, F, P, P, P, I32, P, SZ, P]
         L.ada_decode_stream.restype = C.c_int
+        L.ada_decode_sym.argtypes = [G, CV, P, P, P, F, P, P, P, I32, P, SZ, P]
+        L.ada_decode_sym.restype = C.c_int
+        L.ada_decode_sym_workspace_size.argtypes = [G, I32, I32, I32]
+        L.ada_decode_sym_workspace_size.restype = SZ
         L.ada_decode_merge.argtypes = [G, CV, P, P, P, F, P, P, I32, P, SZ, P]
         L.ada_decode_merge.restype = C.c_int
         _lib = L
@@ -398,6 +402,26 @@ def decode(geom: Geom, cache: Cache, cb8, cb4, q, softmax_scale: float, out, lse
                            _dev(lse, "lse", (torch.float32,)), _dev(logits, "logits", (torch.float32,)),
                            num_splits, _dev(ws, "ws"), ws.numel(), _stream(stream))
     _check(st, "ada_decode")
+    return ws
+
+
+def decode_sym_workspace_size(geom: Geom, num_seqs: int, max_pages_per_head: int, num_splits: int = 0) -> int:
+    return int(load().ada_decode_sym_workspace_size(C.byref(geom), num_seqs, max_pages_per_head, num_splits))
+
+
+def decode_sym(geom: Geom, cache: Cache, cb8, cb4, q, softmax_scale: float, out, lse=None, logits=None,
+               num_splits: int = 0, ws=None, stream=None, view=None):
+    """One decode step with the symmetric angle-code logit (ada_decode_sym)."""
+    if ws is None:
+        ws = _workspace(decode_sym_workspace_size(geom, cache.num_seqs, cache.maxp, num_splits), q.device)
+    ws = _decode_args(geom, cache, q, out, lse, logits, ws, num_splits)
+    v = cache.view() if view is None else view
+    st = load().ada_decode_sym(C.byref(geom), C.byref(v), _dev(cb8, "cb8", (torch.float32,)),
+                               _dev(cb4, "cb4", (torch.float32,)), _dev(q, "q", (torch.bfloat16,)),
+                               float(softmax_scale), _dev(out, "out", (torch.float32,)),
+                               _dev(lse, "lse", (torch.float32,)), _dev(logits, "logits", (torch.float32,)),
+                               num_splits, _dev(ws, "ws"), ws.numel(), _stream(stream))
+    _check(st, "ada_decode_sym")
     return ws
 
 

@@ -240,10 +240,11 @@ bool counts_from_bp(int32_t S, const int32_t *cu, const int32_t *bp, std::vector
 // Byte offsets of the decode workspace parts (all 256-byte aligned): the
 // split partials (m, l) and acc.
 struct WsLayout {
-    size_t ml_off, acc_off, total;
+    size_t ml_off, acc_off, lut_off, total;
 };
 
-WsLayout ws_layout(const ada_geom *g, int32_t S, int32_t ns)
+// sym: the symmetric variant adds every row's LUT after the partials.
+WsLayout ws_layout(const ada_geom *g, int32_t S, int32_t ns, bool sym = false)
 {
     const size_t rows = (size_t)S * g->num_kv_heads;
     const size_t NH = (size_t)(g->num_q_heads / g->num_kv_heads);
@@ -251,7 +252,10 @@ WsLayout ws_layout(const ada_geom *g, int32_t S, int32_t ns)
     WsLayout l{};
     l.ml_off = 0;
     l.acc_off = align256(rows * ns * NH * 2 * sizeof(float));
-    l.total = l.acc_off + align256(rows * ns * NH * D * sizeof(float));
+    l.lut_off = l.acc_off + align256(rows * ns * NH * D * sizeof(float));
+    l.total = l.lut_off;
+    if (sym)
+        l.total += align256(rows * decode_lut_floats(g->head_dim, (int)NH) * sizeof(float));
     return l;
 }
 
@@ -275,7 +279,7 @@ int32_t default_splits(const ada_geom *g, int32_t S, int32_t maxp)
 ada_status decode_common(const ada_geom *g, const ada_cache *c, const float *cb8, const float *cb4,
                          const uint16_t *q, float scale, float *out, float *lse, float *logits,
                          int32_t num_splits, void *ws, size_t ws_bytes, void *stream, bool dense,
-                         unsigned stages = kStageAll)
+                         unsigned stages = kStageAll, bool sym = false)
 {
     if (!geom_ok(g) || !cache_ok(c) || q == nullptr || out == nullptr || num_splits < 0)
         return ADA_EINVAL;
@@ -286,7 +290,7 @@ ada_status decode_common(const ada_geom *g, const ada_cache *c, const float *cb8
     if (num_splits > kMaxSplits)
         return ADA_EINVAL;
     const int32_t ns = num_splits > 0 ? num_splits : default_splits(g, c->num_seqs, c->max_pages_per_head);
-    const size_t need = ada_decode_workspace_size(g, c->num_seqs, c->max_pages_per_head, ns);
+    const size_t need = ws_layout(g, c->num_seqs, ns, sym).total;
     if (ws == nullptr || ws_bytes < need || (reinterpret_cast<uintptr_t>(ws) & 255))
         return ADA_EWORKSPACE;
     const int NH = g->num_q_heads / g->num_kv_heads;
@@ -308,16 +312,17 @@ ada_status decode_common(const ada_geom *g, const ada_cache *c, const float *cb8
     a.logits = logits;
     // workspace: [partial (m, l)][partial acc]
     uint8_t *w = static_cast<uint8_t *>(ws);
-    const WsLayout lay = ws_layout(g, c->num_seqs, ns);
+    const WsLayout lay = ws_layout(g, c->num_seqs, ns, sym);
     a.part_ml = reinterpret_cast<float *>(w + lay.ml_off);
     a.part_acc = reinterpret_cast<float *>(w + lay.acc_off);
+    a.glut = sym ? reinterpret_cast<float *>(w + lay.lut_off) : nullptr;
     a.sigma = scale;
     a.S = c->num_seqs;
     a.Hq = g->num_q_heads;
     a.Hkv = g->num_kv_heads;
     a.maxp = c->max_pages_per_head;
     a.nsplit = ns;
-    if (launch_decode(g->head_dim, NH, dense, a, as_stream(stream), stages) != hipSuccess)
+    if (launch_decode(g->head_dim, NH, dense, a, as_stream(stream), stages, sym) != hipSuccess)
         return ADA_EHIP;
     return ADA_OK;
 }
@@ -672,6 +677,23 @@ ada_status ada_decode_merge(const ada_geom *geom, const ada_cache *cache, const 
 {
     return decode_common(geom, cache, cb8, cb4, q, softmax_scale, out, lse, nullptr, num_splits, ws,
                          ws_bytes, stream, false, kStageMerge);
+}
+
+size_t ada_decode_sym_workspace_size(const ada_geom *geom, int32_t num_seqs, int32_t max_pages_per_head,
+                                     int32_t num_splits)
+{
+    if (!geom_ok(geom) || num_seqs < 0 || max_pages_per_head < 0 || num_splits < 0)
+        return 0;
+    const int32_t ns = num_splits > 0 ? num_splits : default_splits(geom, num_seqs, max_pages_per_head);
+    return ws_layout(geom, num_seqs, ns, true).total;
+}
+
+ada_status ada_decode_sym(const ada_geom *geom, const ada_cache *cache, const float *cb8, const float *cb4,
+                          const uint16_t *q, float softmax_scale, float *out, float *lse, float *logits_dbg,
+                          int32_t num_splits, void *ws, size_t ws_bytes, void *stream)
+{
+    return decode_common(geom, cache, cb8, cb4, q, softmax_scale, out, lse, logits_dbg, num_splits, ws,
+                         ws_bytes, stream, false, kStageAll, true);
 }
 
 ada_status dense_decode(const ada_geom *geom, const ada_cache *cache, const uint16_t *q,

@@ -52,6 +52,7 @@ struct DecodeArgs {
     float *logits;
     float *part_ml;    // [rows][nsplit][NH][2]  (running max in log2 units, sum)
     float *part_acc;   // [rows][nsplit][NH][D]  (unnormalised output)
+    float *glut;       // [rows][LUT floats]: symmetric variant's tabulated LUT, else null
     float sigma;
     int S, Hq, Hkv, maxp, nsplit;
 };
@@ -60,7 +61,10 @@ struct DecodeArgs {
 // one split).
 enum : unsigned { kStageStream = 2, kStageMerge = 4, kStageAll = 6 };
 hipError_t launch_decode(int D, int NH, bool dense, const DecodeArgs &a, hipStream_t st,
-                         unsigned stages = kStageAll);
+                         unsigned stages = kStageAll, bool sym = false);
+// Floats of one row's LUT (the symmetric variant keeps every row's in the
+// workspace).
+size_t decode_lut_floats(int D, int NH);
 
 // LDS bytes the page-stream workgroup needs; the device offers 160 KiB.
 size_t decode_shmem_bytes(int D, int NH, bool dense, int nsplit, int maxp);

@@ -492,7 +492,9 @@ __device__ __forceinline__ void fetch_entry(PageRegs<D> &pr, uint2 e, const uint
 }
 
 // ---- page stream ------------------------------------------------------------
-template <int D, int NH, bool DENSE>
+// SYM: the symmetric variant; the row's LUT was tabulated by sym_lut_kernel
+// and is copied into LDS instead of being built from the query.
+template <int D, int NH, bool DENSE, bool SYM>
 __global__ __launch_bounds__((Waves<D, NH>::THREADS)) void decode_main(DecodeArgs a)
 {
     constexpr int kWaves = Waves<D, NH>::W, kThreads = Waves<D, NH>::THREADS;
@@ -556,7 +558,7 @@ __global__ __launch_bounds__((Waves<D, NH>::THREADS)) void decode_main(DecodeArg
     const uint16_t *qrow = a.q + ((size_t)s * a.Hq + (size_t)hkv * NH) * D;
     float4 w0[DENSE ? 1 : NC], w1[DENSE ? 1 : NC];
     uint4 qv[NH];
-    if constexpr (!DENSE) {
+    if constexpr (!DENSE && !SYM) {
         const float *cb8 = a.cb8 + ((size_t)hkv * G + g) * kCodes8 * 8;
         const float *cb4 = a.cb4 + ((size_t)hkv * G + g) * kCodes4 * 8;
 #pragma unroll
@@ -634,7 +636,12 @@ __global__ __launch_bounds__((Waves<D, NH>::THREADS)) void decode_main(DecodeArg
         const int p = split + k * a.nsplit;
         tbl[k] = make_uint2(pt[p], pm[p]);
     }
-    if constexpr (!DENSE) {
+    if constexpr (SYM) {
+        // the row's tabulated LUT, already in the LDS layout
+        const float4 *src = reinterpret_cast<const float4 *>(a.glut + (size_t)row * LUT_FLOATS);
+        for (int i = tid; i < LUT_FLOATS / 4; i += kThreads)
+            reinterpret_cast<float4 *>(lut)[i] = src[i];
+    } else if constexpr (!DENSE) {
         // LUT[g][c][h] = q_h[8g .. 8g+8) . C[g][c] (c < 256 from cb8, else cb4)
         float qq[NH][8];
 #pragma unroll
@@ -861,6 +868,126 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge(DecodeArgs a)
     }
 }
 
+// ---- symmetric variant: the LUT from the query's codes -------------------------
+// One block per (row, group g).  The query direction u_q = q / |q| (|q|
+// summed sequentially over D, in double) takes in each codebook the index
+// of its nearest codeword (squared distance in double, lowest index on
+// ties), as a key does in encode; then LUT_g[c][h] = |q_h| C_g[cq_h] .
+// C_g[c] (fp32 dot product), written in the page stream's LDS layout.
+template <int D, int NH>
+__global__ __launch_bounds__(256) void sym_lut_kernel(DecodeArgs a)
+{
+    constexpr int G = D / 8, LUT_FLOATS = G * kLutCodes * NH;
+    __shared__ double qn[NH], u[NH][8];
+    __shared__ double bd[4][NH];
+    __shared__ int bc[4][NH];
+    __shared__ int cq8[NH], cq4[NH];
+    const int row = blockIdx.x, g = blockIdx.y, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int s = row / a.Hkv, hkv = row % a.Hkv;
+    const uint16_t *qrow = a.q + ((size_t)s * a.Hq + (size_t)hkv * NH) * D;
+    if (tid < NH) {
+        double ss = 0.0;
+        for (int j = 0; j < D; j++) {
+            const double x = (double)__uint_as_float((uint32_t)qrow[tid * D + j] << 16);
+            ss = ss + x * x;
+        }
+        qn[tid] = sqrt(ss);
+    }
+    __syncthreads();
+    if (tid < NH * 8) {
+        const int h = tid / 8, j = tid % 8;
+        const double x = (double)__uint_as_float((uint32_t)qrow[h * D + 8 * g + j] << 16);
+        u[h][j] = qn[h] > 0.0 ? x / qn[h] : 0.0;
+    }
+    __syncthreads();
+    const float *c8 = a.cb8 + ((size_t)hkv * G + g) * kCodes8 * 8;
+    const float *c4 = a.cb4 + ((size_t)hkv * G + g) * kCodes4 * 8;
+    // nearest 8-bit codeword per head: thread t scores codeword t
+    {
+        const float4 w0 = *reinterpret_cast<const float4 *>(c8 + tid * 8);
+        const float4 w1 = *reinterpret_cast<const float4 *>(c8 + tid * 8 + 4);
+        const float w[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+#pragma unroll
+        for (int h = 0; h < NH; h++) {
+            double d = 0.0;
+#pragma unroll
+            for (int j = 0; j < 8; j++) {
+                const double df = u[h][j] - (double)w[j];
+                d = d + df * df;
+            }
+            int c = tid;
+#pragma unroll
+            for (int o = 32; o >= 1; o >>= 1) {
+                const double d2 = __shfl_xor(d, o, 64);
+                const int c2 = __shfl_xor(c, o, 64);
+                if (d2 < d || (d2 == d && c2 < c)) {
+                    d = d2;
+                    c = c2;
+                }
+            }
+            if (lane == 0) {
+                bd[wave][h] = d;
+                bc[wave][h] = c;
+            }
+        }
+    }
+    // nearest 4-bit codeword per head: lanes 0..15 of wave 0
+    if (wave == 0) {
+        const int cc = lane & 15;
+        const float4 w0 = *reinterpret_cast<const float4 *>(c4 + cc * 8);
+        const float4 w1 = *reinterpret_cast<const float4 *>(c4 + cc * 8 + 4);
+        const float w[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+#pragma unroll
+        for (int h = 0; h < NH; h++) {
+            double d = 0.0;
+#pragma unroll
+            for (int j = 0; j < 8; j++) {
+                const double df = u[h][j] - (double)w[j];
+                d = d + df * df;
+            }
+            int c = cc;
+#pragma unroll
+            for (int o = 8; o >= 1; o >>= 1) {
+                const double d2 = __shfl_xor(d, o, 64);
+                const int c2 = __shfl_xor(c, o, 64);
+                if (d2 < d || (d2 == d && c2 < c)) {
+                    d = d2;
+                    c = c2;
+                }
+            }
+            if (lane == 0)
+                cq4[h] = c;
+        }
+    }
+    __syncthreads();
+    if (tid < NH) {
+        double d = bd[0][tid];
+        int c = bc[0][tid];
+        for (int w = 1; w < 4; w++)
+            if (bd[w][tid] < d || (bd[w][tid] == d && bc[w][tid] < c)) {
+                d = bd[w][tid];
+                c = bc[w][tid];
+            }
+        cq8[tid] = c;
+    }
+    __syncthreads();
+    float *lut = a.glut + (size_t)row * LUT_FLOATS;
+    for (int c = tid; c < kLutCodes; c += 256) {
+        const float *wc = c < kCodes8 ? c8 + c * 8 : c4 + (c - kCodes8) * 8;
+        float o[NH];
+#pragma unroll
+        for (int h = 0; h < NH; h++) {
+            const float *wq = c < kCodes8 ? c8 + cq8[h] * 8 : c4 + cq4[h] * 8;
+            float acc = wq[0] * wc[0];
+#pragma unroll
+            for (int j = 1; j < 8; j++)
+                acc = fmaf(wq[j], wc[j], acc);
+            o[h] = acc * (float)qn[h];
+        }
+        lut_store<NH, G>(lut, g * kLutCodes + c, o);
+    }
+}
+
 template <int D, int NH, bool DENSE>
 size_t shmem_bytes(int max_wg_pages)
 {
@@ -871,7 +998,7 @@ size_t shmem_bytes(int max_wg_pages)
     return b > red ? b : red;
 }
 
-template <int D, int NH, bool DENSE>
+template <int D, int NH, bool DENSE, bool SYM>
 hipError_t launch_t(const DecodeArgs &a, hipStream_t st, unsigned stages)
 {
     const int rows = a.S * a.Hkv;
@@ -880,16 +1007,24 @@ hipError_t launch_t(const DecodeArgs &a, hipStream_t st, unsigned stages)
     const size_t shmem = shmem_bytes<D, NH, DENSE>((a.maxp + a.nsplit - 1) / a.nsplit);
     static size_t attr_set = 0;
     if (shmem > attr_set) {
-        hipError_t e = hipFuncSetAttribute((const void *)decode_main<D, NH, DENSE>,
+        hipError_t e = hipFuncSetAttribute((const void *)decode_main<D, NH, DENSE, SYM>,
                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)shmem);
         if (e != hipSuccess)
             return e;
         attr_set = shmem;
     }
     hipError_t e = hipSuccess;
+    if constexpr (SYM) {
+        if (stages & kStageStream) {
+            hipLaunchKernelGGL((sym_lut_kernel<D, NH>), dim3(rows, D / 8), dim3(256), 0, st, a);
+            e = hipGetLastError();
+            if (e != hipSuccess)
+                return e;
+        }
+    }
     if (stages & kStageStream) {
-        hipLaunchKernelGGL((decode_main<D, NH, DENSE>), dim3(rows * a.nsplit), dim3(Waves<D, NH>::THREADS), shmem,
-                           st, a);
+        hipLaunchKernelGGL((decode_main<D, NH, DENSE, SYM>), dim3(rows * a.nsplit), dim3(Waves<D, NH>::THREADS),
+                           shmem, st, a);
         e = hipGetLastError();
     }
     if (e != hipSuccess || a.nsplit == 1 || !(stages & kStageMerge))
@@ -899,6 +1034,8 @@ hipError_t launch_t(const DecodeArgs &a, hipStream_t st, unsigned stages)
 }
 
 } // namespace
+
+size_t decode_lut_floats(int D, int NH) { return (size_t)(D / 8) * kLutCodes * NH; }
 
 size_t decode_shmem_bytes(int D, int NH, bool dense, int nsplit, int maxp)
 {
@@ -920,11 +1057,14 @@ size_t decode_shmem_bytes(int D, int NH, bool dense, int nsplit, int maxp)
     return 0;
 }
 
-hipError_t launch_decode(int D, int NH, bool dense, const DecodeArgs &a, hipStream_t st, unsigned stages)
+hipError_t launch_decode(int D, int NH, bool dense, const DecodeArgs &a, hipStream_t st, unsigned stages,
+                         bool sym)
 {
 #define ADA_CASE(DD, NN)                                                                          \
     if (D == DD && NH == NN)                                                                      \
-        return dense ? launch_t<DD, NN, true>(a, st, stages) : launch_t<DD, NN, false>(a, st, stages);
+        return dense ? launch_t<DD, NN, true, false>(a, st, stages)                               \
+                     : sym ? launch_t<DD, NN, false, true>(a, st, stages)                          \
+                           : launch_t<DD, NN, false, false>(a, st, stages);
     ADA_CASE(64, 1)
     ADA_CASE(64, 2)
     ADA_CASE(64, 4)

@@ -284,6 +284,31 @@ ada_status rdr_pack_tiers(const ada_geom *geom, const ada_cache *cache, int32_t 
                           uint64_t *arena_cursor_host, int32_t *num_pages_host, void *ws,
                           size_t ws_bytes, void *stream);
 
+/* Workspace bytes of ada_decode_sym: ada_decode's plus every row's table. */
+size_t ada_decode_sym_workspace_size(const ada_geom *geom, int32_t num_seqs,
+                                     int32_t max_pages_per_head, int32_t num_splits);
+
+/*
+ * ada_decode_sym -- ada_decode with the symmetric angle-code logit.  [TS]
+ * 2.1 writes the logit as |q| * r~ * f_b(c_q, c_k), a cosine computed from
+ * the angular codes of both query and key.  Reading: the query's unit
+ * direction u_q = q / |q| (|q| in double, summed sequentially over D) takes,
+ * in each group and each codebook, the index of its nearest codeword as a
+ * key does in ada_encode (squared distance in double, lowest index on
+ * ties), and a coded slot's logit is
+ *   l_t = softmax_scale * |q| * r~_t * sum_g C_g[cq_g] . C_g[code_{t,g}]
+ * (the 8-bit codebook for 8-bit keys, the 4-bit one for 4-bit keys): the
+ * table of ada_decode with q_g replaced by |q| C_g[cq_g], tabulated in fp32
+ * as |q| * (C_g[cq_g] . C_g[c]).  fp16-tier slots keep softmax_scale * q.k.
+ * Arguments and outputs as ada_decode; ws: ada_decode_sym_workspace_size
+ * bytes (any content).  Up to three kernels on `stream`: the table, the
+ * page stream (which copies its row's table into LDS) and the merge.
+ */
+ada_status ada_decode_sym(const ada_geom *geom, const ada_cache *cache, const float *cb8,
+                          const float *cb4, const uint16_t *q, float softmax_scale, float *out,
+                          float *lse, float *logits_dbg, int32_t num_splits, void *ws,
+                          size_t ws_bytes, void *stream);
+
 /* Split count ada_decode / dense_decode use for num_splits == 0. */
 int32_t ada_decode_default_splits(const ada_geom *geom, int32_t num_seqs,
                                   int32_t max_pages_per_head);

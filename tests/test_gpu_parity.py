@@ -111,6 +111,36 @@ def test_decode_growing_logits_rescale_per_head(D, ratio):
         _check_decode(geom_of(cfg), hc, case, sp, f"growing logits D={D} GQA {ratio}")
 
 
+@pytest.mark.parametrize("D,Hq,Hkv", [(128, 8, 2), (64, 4, 4), (128, 10, 2), (64, 16, 2)])
+def test_decode_sym_matches_oracle(D, Hq, Hkv):
+    """The symmetric angle-code variant (query codes) against the oracle's:
+    logits to the decode bar (so the query codes agree), outputs, lse."""
+    cfg = small_workload(D=D, Hq=Hq, Hkv=Hkv, S=3, T=400, seed=95 + D + Hq)
+    case = make_case(cfg, lens=[400, 77, 0], mixes=[(1500, 6000, 8500), (0, 5000, 10000), (0, 0, 0)])
+    hc, _ = oracle_cache(case)
+    geom = geom_of(cfg)
+    ref = oracle.decode(hc, case["cb8"], case["cb4"], case["q"], cfg.sigma, logits=True, nthreads=8, sym=True)
+    dc = upload_cache(hc, geom)
+    d = _dev_case(case)
+    for sp in (0, 1, 3):
+        flush(f"[decode_sym] D={D} Hq={Hq} Hkv={Hkv} splits={sp}")
+        out, lse, lg = decode_outputs(geom, dc, d["q"])
+        ada.decode_sym(geom, dc, d["cb8"], d["cb4"], d["q"], cfg.sigma, out, lse, lg, num_splits=sp)
+        torch.cuda.synchronize()
+        ok, worst = logit_tol_ok(lg.cpu().double().numpy(), ref["logits"])
+        assert ok, f"logits off by {worst:.3g} (relative)"
+        o = out.cpu().double().numpy()
+        assert np.abs(o - ref["out"]).max(initial=0.0) <= OUT_TOL
+        l = lse.cpu().double().numpy()
+        fin = np.isfinite(ref["lse"])
+        assert np.array_equal(np.isfinite(l), fin)
+        assert (np.abs(l[fin] - ref["lse"][fin]) <= 1e-3 * np.maximum(np.abs(ref["lse"][fin]), 1.0)).all()
+    # the variant really differs from the asymmetric decode on coded slots
+    asym = oracle.decode(hc, case["cb8"], case["cb4"], case["q"], cfg.sigma, logits=True)
+    m = ~np.isnan(ref["logits"])
+    assert np.abs(asym["logits"][m] - ref["logits"][m]).max() > 1e-2
+
+
 @pytest.mark.parametrize("mix", [(10000, 10000, 10000), (0, 10000, 10000), (0, 0, 10000)])
 def test_decode_single_token_rows(mix):
     cfg = small_workload(D=128, Hq=4, Hkv=1, S=3, T=1, mix=mix, seed=50)
