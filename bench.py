@@ -369,6 +369,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--no-append", action="store_true", help="skip the append-path timing")
+    ap.add_argument("--no-sym", action="store_true", help="skip the symmetric-variant timing")
     ap.add_argument("--solver-full", action="store_true",
                     help="also time the budget solver over the whole workload")
     ap.add_argument("--eager", action="store_true",
@@ -478,6 +479,16 @@ def main():
                                          "achieved_GBs": dused / (dms / 1e3) / 1e9,
                                          "ada_speedup": dms / ms_graph}
         del darenas
+    if not args.no_sym:
+        # the symmetric angle-code variant on the same cache
+        yws = torch.zeros(ada.decode_sym_workspace_size(geom, S, cache.maxp, args.splits), dtype=torch.uint8,
+                          device=dev)
+        yfns = [(lambda v=v: ada.decode_sym(geom, cache, L["cb8"], L["cb4"], L["q"], cfg.sigma, out, lse,
+                                            num_splits=args.splits, ws=yws, view=v)) for v in views]
+        _, _, yms = timer(yfns, args.steps, args.warmup)
+        result["symmetric_variant"] = {"ms_per_step": yms, "value": tokens / (yms / 1e3),
+                                       "note": "ada_decode_sym: query codes and table kernel, page stream, merge"}
+        log(f"symmetric variant: step {yms * 1e3:.2f} us")
     torch.cuda.synchronize()
     if not args.no_append:
         result["append_path"] = append_path(dev)
