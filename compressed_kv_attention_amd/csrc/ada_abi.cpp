@@ -60,7 +60,7 @@ size_t pack_workspace(int Hkv, int64_t n_tokens, int32_t num_seqs)
     b += align256(sizeof(PackRow) * (size_t)std::max<int64_t>(rows, 1));
     b += align256(sizeof(PackPage) * (size_t)max_pack_pages(Hkv, n_tokens, num_seqs));
     b += align256((size_t)n_tokens * Hkv);                   // protect copy
-    b += align256((size_t)n_tokens * Hkv * sizeof(int32_t)); // dest
+    b += align256((size_t)max_pack_pages(Hkv, n_tokens, num_seqs) * kSlots * sizeof(int32_t)); // src
     return b;
 }
 
@@ -160,13 +160,13 @@ ada_status run_pack(const ada_geom *g, const ada_cache *c, int32_t S, const int3
         return st;
     if (pb.n_pages > max_pack_pages(H, N, S))
         return ADA_EWORKSPACE;
-    // workspace: [plan blob][protect][dest]
+    // workspace: [plan blob][protect][src]
     uint8_t *wsb = static_cast<uint8_t *>(ws);
     const size_t blob_cap = align256(sizeof(PackSeq) * (size_t)std::max(S, 1)) +
                             align256(sizeof(PackRow) * (size_t)std::max<int64_t>((int64_t)S * H, 1)) +
                             align256(sizeof(PackPage) * (size_t)max_pack_pages(H, N, S));
     uint8_t *prot_dev = wsb + blob_cap;
-    int32_t *dest = reinterpret_cast<int32_t *>(prot_dev + align256((size_t)N * H));
+    int32_t *src = reinterpret_cast<int32_t *>(prot_dev + align256((size_t)N * H));
     hipStream_t st = as_stream(stream);
     // pageable host source: the runtime copies it before returning
     if (hipMemcpyAsync(wsb, pb.blob.data(), pb.blob.size(), hipMemcpyHostToDevice, st) != hipSuccess)
@@ -180,7 +180,7 @@ ada_status run_pack(const ada_geom *g, const ada_cache *c, int32_t S, const int3
     plan.pages = reinterpret_cast<const PackPage *>(wsb + pb.page_off);
     plan.protect = protect_host != nullptr ? prot_dev : nullptr;
     plan.tiers = tiers;
-    plan.dest = dest;
+    plan.src = src;
     plan.S = S;
     plan.Hkv = H;
     plan.D = g->head_dim;

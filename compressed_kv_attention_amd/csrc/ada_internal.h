@@ -131,7 +131,7 @@ struct PackPlan {
     const PackPage *pages;
     const uint8_t *protect; // [N][Hkv] or null
     const uint8_t *tiers;   // [N][Hkv] given tiers (0-2 kept, other values dropped) or null
-    int32_t *dest;          // [N][Hkv]: logical page * 16 + slot, or -1
+    int32_t *src;           // [n_pages][16]: flat (token, head) index a slot holds, or -1
     int S, Hkv, D, maxp, n_pages, dense;
     int64_t n_tokens;
 };

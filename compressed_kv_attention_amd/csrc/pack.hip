@@ -10,17 +10,18 @@
 // is given (by the budget solver in rdr.hip).
 //
 // Kernels, in stream order:
-//   pack_pages   one block per new page: zero its bytes, write its page-table
-//                entry and metadata byte, mark its slot_token entries empty;
 //   pack_rows    one thread per row: advance num_pages and tier_tokens;
 //   pack_rank    one 1024-thread block per row: radix-select the keys at the
 //                three tier boundaries (8 passes of 8 bits over 64-bit keys,
 //                exact because keys are unique; skipped when the tiers are
 //                given), then walk the row in index
 //                order with a block-wide scan to give every token its tier
-//                page and slot (dest = logical page * 16 + slot, -1 = dropped);
-//   pack_scatter one wave per (token, head): copy or quantize its fields into
-//                its slot.
+//                page and slot (src[page][slot] = the token-head it holds);
+//   pack_fill    one block per new page: assemble the page image in LDS in its
+//                final byte layout (fields copied, values of the 4-bit tier
+//                quantized, every other byte zero), write it with 16-byte
+//                stores, then its page-table entry, metadata byte and
+//                slot_token entries.
 #include "ada_internal.h"
 #include "numfmt.h"
 
@@ -28,23 +29,6 @@ namespace ada {
 namespace {
 
 #pragma clang fp contract(off)
-
-__global__ __launch_bounds__(256) void pack_pages(PackPlan plan, PackCache cache)
-{
-    const PackPage pg = plan.pages[blockIdx.x];
-    const int tier = pg.meta & 3;
-    uint4 *base = reinterpret_cast<uint4 *>(cache.arena + (size_t)pg.off * kUnit);
-    const int n16 = page_bytes(plan.D, tier) / 16;
-    for (int i = threadIdx.x; i < n16; i += 256)
-        base[i] = make_uint4(0, 0, 0, 0);
-    const size_t slot = (size_t)pg.row * plan.maxp + pg.pi;
-    if (threadIdx.x == 0) {
-        cache.page_table[slot] = pg.off;
-        cache.page_meta[slot] = (uint8_t)pg.meta;
-    }
-    if (cache.slot_token != nullptr && threadIdx.x < kSlots)
-        cache.slot_token[slot * kSlots + threadIdx.x] = -1;
-}
 
 __global__ __launch_bounds__(256) void pack_rows(PackPlan plan, PackCache cache)
 {
@@ -138,6 +122,13 @@ __global__ __launch_bounds__(1024) void pack_rank(PackPlan plan, PackData data)
     }
     if (tid < 3)
         running[tid] = 0;
+    // every slot of the row's new pages starts empty (the walk fills the
+    // first `count` of each tier)
+    for (int k = 0; k < 3; k++) {
+        const int n16 = (rw.count[k] + kSlots - 1) / kSlots * kSlots;
+        for (int i = tid; i < n16; i += 1024)
+            plan.src[(size_t)rw.lp_first[k] * kSlots + i] = -1;
+    }
     __syncthreads();
 
     for (int base = 0; base < T; base += 1024) {
@@ -173,11 +164,8 @@ __global__ __launch_bounds__(1024) void pack_rank(PackPlan plan, PackData data)
                     pos += wave_tot[w][tier];
                 // a position past the tier's count cannot happen with exact
                 // thresholds; it is dropped rather than written out of range
-                plan.dest[e] = pos < rw.count[tier]
-                                   ? (rw.lp_first[tier] + pos / kSlots) * kSlots + pos % kSlots
-                                   : -1;
-            } else {
-                plan.dest[e] = -1;
+                if (pos < rw.count[tier])
+                    plan.src[(size_t)(rw.lp_first[tier] + pos / kSlots) * kSlots + pos % kSlots] = (int32_t)e;
             }
         }
         __syncthreads();
@@ -191,81 +179,110 @@ __global__ __launch_bounds__(1024) void pack_rank(PackPlan plan, PackData data)
     }
 }
 
-__global__ __launch_bounds__(256) void pack_scatter(PackPlan plan, PackData data, PackCache cache)
+constexpr int kFillThreads = 256;
+constexpr int kMaxPageBytes = 8192; // the largest page (D = 128, tiers 0 and 3)
+
+__global__ __launch_bounds__(kFillThreads) void pack_fill(PackPlan plan, PackData data, PackCache cache)
 {
-    const int64_t e = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-    const int k = threadIdx.x & 63;
-    if (e >= plan.n_tokens * plan.Hkv)
-        return;
-    const int dest = plan.dest[e];
-    if (dest < 0 || dest / kSlots >= plan.n_pages)
-        return;
-    const int D = plan.D, G = D / 8;
-    const PackPage pg = plan.pages[dest / kSlots];
-    const int slot = dest % kSlots;
-    const int tier = pg.meta & 3;
-    uint8_t *base = cache.arena + (size_t)pg.off * kUnit;
-    const uint16_t *kk = data.keys + (size_t)e * D;
-    const uint16_t *vv = data.values + (size_t)e * D;
+    __shared__ uint4 img4[kMaxPageBytes / 16];
+    __shared__ int64_t src_s[kSlots];
+    const PackPage pg = plan.pages[blockIdx.x];
+    const int tier = pg.meta & 3, nv = ((pg.meta >> 2) & 15) + 1;
+    const int D = plan.D, G = D / 8, H = plan.Hkv;
+    const int n16 = page_bytes(D, tier) / 16;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    uint8_t *img = reinterpret_cast<uint8_t *>(img4);
+    for (int i = tid; i < n16; i += kFillThreads)
+        img4[i] = make_uint4(0, 0, 0, 0);
+    if (tid < kSlots)
+        src_s[tid] = tid < nv ? (int64_t)plan.src[(size_t)blockIdx.x * kSlots + tid] : -1;
+    __syncthreads();
 
     if (tier == 0 || tier == 3) {
-        for (int d = k; d < D; d += 64) {
-            uint16_t kb = kk[d];
+        // keys: dims d, d+1 of a slot are adjacent in the row section
+        for (int i = tid; i < kSlots * D / 2; i += kFillThreads) {
+            const int t = i / (D / 2), d = 2 * (i % (D / 2));
+            const int64_t e = src_s[t];
+            if (e < 0)
+                continue;
+            uint32_t kk = *reinterpret_cast<const uint32_t *>(data.keys + e * D + d);
             if (tier == 3)
-                kb = f32_to_bf16(f16_bits_to_f32(kb));
-            *reinterpret_cast<uint16_t *>(base + row_off(slot, d)) = kb;
-            *reinterpret_cast<uint16_t *>(base + 32 * D + col_off(slot, d)) = vv[d];
+                kk = (uint32_t)f32_to_bf16(f16_bits_to_f32((uint16_t)(kk & 0xffff))) |
+                     ((uint32_t)f32_to_bf16(f16_bits_to_f32((uint16_t)(kk >> 16))) << 16);
+            *reinterpret_cast<uint32_t *>(img + row_off(t, d)) = kk;
+            const uint32_t vv = *reinterpret_cast<const uint32_t *>(data.values + e * D + d);
+            *reinterpret_cast<uint16_t *>(img + 32 * D + col_off(t, d)) = (uint16_t)(vv & 0xffff);
+            *reinterpret_cast<uint16_t *>(img + 32 * D + col_off(t, d + 1)) = (uint16_t)(vv >> 16);
         }
     } else if (tier == 1) {
-        for (int d = k; d < D; d += 64)
-            *reinterpret_cast<uint16_t *>(base + col_off(slot, d)) = vv[d];
-        if (k < G)
-            base[codes_off(D, 1) + slot * G + k] = data.codes8[(size_t)e * G + k];
-        if (k == 0)
-            *reinterpret_cast<uint16_t *>(base + radius_off(D, 1) + slot * 2) = data.radius[e];
+        for (int i = tid; i < kSlots * D / 2; i += kFillThreads) {
+            const int t = i / (D / 2), d = 2 * (i % (D / 2));
+            const int64_t e = src_s[t];
+            if (e < 0)
+                continue;
+            const uint32_t vv = *reinterpret_cast<const uint32_t *>(data.values + e * D + d);
+            *reinterpret_cast<uint16_t *>(img + col_off(t, d)) = (uint16_t)(vv & 0xffff);
+            *reinterpret_cast<uint16_t *>(img + col_off(t, d + 1)) = (uint16_t)(vv >> 16);
+        }
+        for (int i = tid; i < kSlots * G; i += kFillThreads) {
+            const int t = i / G, g = i % G;
+            if (src_s[t] >= 0)
+                img[codes_off(D, 1) + i] = data.codes8[src_s[t] * G + g];
+        }
+        if (tid < kSlots && src_s[tid] >= 0)
+            *reinterpret_cast<uint16_t *>(img + radius_off(D, 1) + 2 * tid) = data.radius[src_s[tid]];
     } else {
         // int8 values with one fp16 scale: scale = fp16(fp32(max|v| / 127)),
-        // q = clamp(rint(fp32(v / scale)), -127, 127), zero scale -> q = 0.
-        float amax = 0.f;
-        for (int d = k; d < D; d += 64)
-            amax = fmaxf(amax, fabsf(bf16_bits_to_f32(vv[d])));
+        // q = clamp(rint(fp32(v / scale)), -127, 127), zero scale -> q = 0;
+        // wave w quantizes slots w, w + 4, w + 8, w + 12
+        for (int t = wave; t < kSlots; t += kFillThreads / 64) {
+            const int64_t e = src_s[t];
+            if (e < 0)
+                continue;
+            const uint16_t *vv = data.values + e * D;
+            float amax = 0.f;
+            for (int d = lane; d < D; d += 64)
+                amax = fmaxf(amax, fabsf(bf16_bits_to_f32(vv[d])));
 #pragma unroll
-        for (int o = 32; o >= 1; o >>= 1)
-            amax = fmaxf(amax, __shfl_xor(amax, o, 64));
-        const float s32 = amax / 127.0f;
-        const uint16_t sh = f64_to_f16_sat((double)s32);
-        const float sc = f16_bits_to_f32(sh);
-        for (int d = k; d < D; d += 64) {
-            int q = 0;
-            if (sc != 0.f) {
-                float y = rintf(bf16_bits_to_f32(vv[d]) / sc);
-                y = fminf(fmaxf(y, -127.f), 127.f);
-                q = (int)y;
+            for (int o = 32; o >= 1; o >>= 1)
+                amax = fmaxf(amax, __shfl_xor(amax, o, 64));
+            const float s32 = amax / 127.0f;
+            const uint16_t sh = f64_to_f16_sat((double)s32);
+            const float sc = f16_bits_to_f32(sh);
+            for (int d = lane; d < D; d += 64) {
+                int q = 0;
+                if (sc != 0.f) {
+                    float y = rintf(bf16_bits_to_f32(vv[d]) / sc);
+                    y = fminf(fmaxf(y, -127.f), 127.f);
+                    q = (int)y;
+                }
+                img[col8_off(t, d)] = (uint8_t)(int8_t)q;
             }
-            base[col8_off(slot, d)] = (uint8_t)(int8_t)q;
-        }
-        if (k < G / 2)
-            base[codes_off(D, 2) + slot * (G / 2) + k] = data.codes4[(size_t)e * (G / 2) + k];
-        if (k == 0) {
-            *reinterpret_cast<uint16_t *>(base + radius_off(D, 2) + slot * 2) = data.radius[e];
-            *reinterpret_cast<uint16_t *>(base + vscale_off(D) + slot * 2) = sh;
+            if (lane < G / 2)
+                img[codes_off(D, 2) + t * (G / 2) + lane] = data.codes4[e * (G / 2) + lane];
+            if (lane == 0) {
+                *reinterpret_cast<uint16_t *>(img + radius_off(D, 2) + 2 * t) = data.radius[e];
+                *reinterpret_cast<uint16_t *>(img + vscale_off(D) + 2 * t) = sh;
+            }
         }
     }
-    if (cache.slot_token != nullptr && k == 0) {
-        // sequence of this token: last s with seqs[s].begin <= n
-        const int n = (int)(e / plan.Hkv);
-        int lo = 0, hi = plan.S - 1;
-        while (lo < hi) {
-            const int mid = (lo + hi + 1) / 2;
-            if (plan.seqs[mid].begin <= n)
-                lo = mid;
-            else
-                hi = mid - 1;
+    __syncthreads();
+    uint4 *dst = reinterpret_cast<uint4 *>(cache.arena + (size_t)pg.off * kUnit);
+    for (int i = tid; i < n16; i += kFillThreads)
+        dst[i] = img4[i];
+    const size_t slot = (size_t)pg.row * plan.maxp + pg.pi;
+    if (tid == 0) {
+        cache.page_table[slot] = pg.off;
+        cache.page_meta[slot] = (uint8_t)pg.meta;
+    }
+    if (cache.slot_token != nullptr && tid < kSlots) {
+        const int64_t e = src_s[tid];
+        int32_t pos = -1;
+        if (e >= 0) {
+            const PackSeq sq = plan.seqs[pg.row / H];
+            pos = (int32_t)(sq.pos_base + (e / H - sq.begin));
         }
-        // (an empty sequence is never the last one with begin <= n)
-        const PackSeq sq = plan.seqs[lo];
-        cache.slot_token[((size_t)pg.row * plan.maxp + pg.pi) * kSlots + slot] =
-            (int32_t)(sq.pos_base + (n - sq.begin));
+        cache.slot_token[slot * kSlots + tid] = pos;
     }
 }
 
@@ -275,11 +292,6 @@ hipError_t launch_pack(const PackPlan &plan, const PackData &data, const PackCac
                        hipStream_t st)
 {
     const int rows = plan.S * plan.Hkv;
-    if (plan.n_pages > 0) {
-        hipLaunchKernelGGL(pack_pages, dim3(plan.n_pages), dim3(256), 0, st, plan, cache);
-        if (hipError_t e = hipGetLastError(); e != hipSuccess)
-            return e;
-    }
     if (rows > 0) {
         hipLaunchKernelGGL(pack_rows, dim3((rows + 255) / 256), dim3(256), 0, st, plan, cache);
         if (hipError_t e = hipGetLastError(); e != hipSuccess)
@@ -289,9 +301,9 @@ hipError_t launch_pack(const PackPlan &plan, const PackData &data, const PackCac
         hipLaunchKernelGGL(pack_rank, dim3(rows), dim3(1024), 0, st, plan, data);
         if (hipError_t e = hipGetLastError(); e != hipSuccess)
             return e;
-        const int64_t items = plan.n_tokens * plan.Hkv;
-        hipLaunchKernelGGL(pack_scatter, dim3((unsigned)((items + 3) / 4)), dim3(256), 0, st, plan,
-                           data, cache);
+    }
+    if (plan.n_pages > 0) {
+        hipLaunchKernelGGL(pack_fill, dim3(plan.n_pages), dim3(kFillThreads), 0, st, plan, data, cache);
         if (hipError_t e = hipGetLastError(); e != hipSuccess)
             return e;
     }
