@@ -51,11 +51,13 @@ def lib():
         L.oracle_pack.restype = I
         L.oracle_code_error.argtypes = [I, I, I64, P, P, P, P, P, P, P]
         L.oracle_code_error.restype = I
-        L.oracle_rdr_solve.argtypes = [I, I, I, P, P, P, P, P, P, P, P]
+        L.oracle_rdr_solve.argtypes = [I, I, I, P, P, P, P, P, P, P, P, P]
         L.oracle_rdr_solve.restype = I
         L.oracle_pack_tiers.argtypes = [I, I, I, P, P, P, P, P, P, P, P, P, P, U64, P, P, P, P, P,
                                         P, I]
         L.oracle_pack_tiers.restype = I
+        L.oracle_append.argtypes = [I, I, I, P, P, P, P, P, P, P, P, P, U64, P, P, P, P, P, P, I, P, P, P]
+        L.oracle_append.restype = I
         L.oracle_dense_pack.argtypes = [I, I, I, P, P, P, P, P, U64, P, P, P, P, I]
         L.oracle_dense_pack.restype = I
         L.oracle_decode.argtypes = [I, I, I, I, I, P, P, P, P, P, P, P, D_, P, P, P, P, I64, I64, I]
@@ -228,9 +230,10 @@ def code_error(keys, cb8, cb4, codes8, codes4):
     return e8, e4
 
 
-def rdr_solve(D, cu_tokens, budget_bytes, radius, err8, err4, scores, protect=None):
+def rdr_solve(D, cu_tokens, budget_bytes, radius, err8, err4, scores, protect=None, with_threshold=False):
     """Tier of every (token, head) under a per-sequence byte budget:
-    u8 [N][Hkv], 0-2 kept tier, 3 dropped."""
+    u8 [N][Hkv], 0-2 kept tier, 3 dropped (and each sequence's slope
+    threshold s*, f32 [S], when with_threshold)."""
     cu = _np(cu_tokens, np.int32)
     bud = _np(budget_bytes, np.int64)
     r = _u16(radius)
@@ -239,10 +242,11 @@ def rdr_solve(D, cu_tokens, budget_bytes, radius, err8, err4, scores, protect=No
     sc = _np(scores, np.float32)
     pr = None if protect is None else _np(protect, np.uint8)
     t = np.zeros((N, H), dtype=np.uint8)
+    th = np.zeros(len(cu) - 1, dtype=np.float32)
     rc = lib().oracle_rdr_solve(D, H, len(cu) - 1, _p(cu), _p(bud), _p(r), _p(e8), _p(e4), _p(sc),
-                                _p(pr), _p(t))
+                                _p(pr), _p(t), _p(th))
     assert rc == 0, rc
-    return t
+    return (t, th) if with_threshold else t
 
 
 def pack_tiers(cache: HostCache, cu_tokens, tiers, keys, values, radius, codes8, codes4,
@@ -262,6 +266,29 @@ def pack_tiers(cache: HostCache, cu_tokens, tiers, keys, values, radius, codes8,
                                    cache.arena_units, _p(cache.cursor), _p(cache.page_table),
                                    _p(cache.page_meta), _p(cache.num_pages),
                                    _p(cache.tier_tokens), _p(cache.slot_token), cache.maxp)
+
+
+def append(cache: HostCache, keys, values, scores, cb8, cb4, threshold, pos, open_page, protect=None):
+    """One decode-step append: one new token per sequence (keys fp16 /
+    values bf16 [S][Hkv][D], scores f32 [S][Hkv], threshold f32 [S], pos
+    int64 [S]); open_page int32 [S*Hkv][3] is updated in place.  Returns
+    (tiers u8 [S][Hkv], status bits)."""
+    k, v = _u16(keys), _u16(values)
+    S, H, D = k.shape
+    sc = _np(scores, np.float32)
+    c8, c4 = _np(cb8, np.float32), _np(cb4, np.float32)
+    th = _np(threshold, np.float32)
+    ps = _np(pos, np.int64)
+    pr = None if protect is None else _np(protect, np.uint8)
+    assert open_page.dtype == np.int32 and open_page.shape == (S * H, 3) and open_page.flags.c_contiguous
+    tiers = np.zeros((S, H), np.uint8)
+    status = np.zeros(1, np.int32)
+    rc = lib().oracle_append(D, H, S, _p(k), _p(v), _p(sc), _p(pr), _p(c8), _p(c4), _p(th), _p(ps),
+                             _p(cache.arena), cache.arena_units, _p(cache.cursor), _p(cache.page_table),
+                             _p(cache.page_meta), _p(cache.num_pages), _p(cache.tier_tokens),
+                             _p(cache.slot_token), cache.maxp, _p(open_page), _p(tiers), _p(status))
+    assert rc == 0
+    return tiers, int(status[0])
 
 
 def row_tier_counts(cu_tokens, tiers) -> np.ndarray:

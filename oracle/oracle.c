@@ -449,7 +449,7 @@ static int rdr_chain(const int32_t R[4], float w, uint16_t r_f16, float e8, floa
 
 int oracle_rdr_solve(int D, int Hkv, int S, const int32_t *cu_tokens, const int64_t *budget_bytes,
                      const uint16_t *radius, const float *err8, const float *err4,
-                     const float *scores, const uint8_t *protect, uint8_t *tiers)
+                     const float *scores, const uint8_t *protect, uint8_t *tiers, float *threshold)
 {
     if ((D != 64 && D != 128) || Hkv <= 0 || S < 0)
         return OR_EINVAL_SOLVE;
@@ -465,6 +465,8 @@ int oracle_rdr_solve(int D, int Hkv, int S, const int32_t *cu_tokens, const int6
         int64_t need = items * R[0] - cap;
         for (int64_t i = 0; i < items; i++)
             tiers[b * Hkv + i] = 0;
+        if (threshold)
+            threshold[s] = need <= 0 ? -INFINITY : INFINITY;
         if (need <= 0)
             continue;
         /* every demotion of the sequence, sorted by slope */
@@ -495,6 +497,8 @@ int oracle_rdr_solve(int D, int Hkv, int S, const int32_t *cu_tokens, const int6
             }
         }
         free(all);
+        if (threshold)
+            threshold[s] = sstar;
         for (int64_t i = 0; i < items; i++) {
             int64_t e = b * Hkv + i;
             if (protect && protect[e])
@@ -858,6 +862,132 @@ int oracle_pack_tiers(int D, int Hkv, int S, const int32_t *cu_tokens, const uin
     return pack_impl(D, Hkv, S, cu_tokens, NULL, tiers, keys, values, radius, codes8, codes4, NULL,
                      NULL, place_perm, pos_base, arena, arena_units, cursor, page_table, page_meta,
                      num_pages, tier_tokens, slot_token, maxp, 0);
+}
+
+/* ------------------------------------------------------------------------ */
+/* Decode-step append.                                                       */
+/*                                                                           */
+/* [TS] 2.3: the pipeline maps dense keys to spherical codes, applies RDR to */
+/* filter and tier them, and stores the result; [TS] 2.2: retained states    */
+/* sit in tier-homogeneous pages.  Reading for the decode loop, where each   */
+/* step brings one new token per sequence: its key is encoded as in encode  */
+/* (the code errors are the chosen codewords' distances, summed as in        */
+/* code_error), its tier follows from the solver's chain rule with the       */
+/* sequence's slope threshold s* of the last solve (the online continuation */
+/* of the same Lagrangian allocation; protected states take tier 0), and a  */
+/* kept state goes into the next free slot of its row's open page of that    */
+/* tier.  A row without an open page of the tier, or whose open page is      */
+/* full, takes a new page: the row's next page-table index, arena space by   */
+/* bump allocation, all bytes zero before the slot is written.  open_page    */
+/* [rows][3] holds each row's open page index + 1 (0: none).  Rows are       */
+/* visited in (sequence, head) order.  A row whose page table is full sets   */
+/* status bit 1 and one that finds no arena space sets bit 2; its token is   */
+/* not stored.                                                              */
+/* ------------------------------------------------------------------------ */
+
+static int nearest_dist(const double *u8, const float *cb, int K, double *bestd)
+{
+    int best = 0;
+    double bd = INFINITY;
+    for (int c = 0; c < K; c++) {
+        double d = 0;
+        for (int j = 0; j < 8; j++) {
+            double diff = u8[j] - (double)cb[c * 8 + j];
+            d += diff * diff;
+        }
+        if (d < bd) {
+            bd = d;
+            best = c;
+        }
+    }
+    *bestd = bd;
+    return best;
+}
+
+int oracle_append(int D, int Hkv, int S, const uint16_t *keys, const uint16_t *values, const float *scores,
+                  const uint8_t *protect, const float *cb8, const float *cb4, const float *threshold,
+                  const int64_t *pos, uint8_t *arena, uint64_t arena_units, uint64_t *cursor,
+                  uint32_t *page_table, uint8_t *page_meta, int32_t *num_pages, int32_t *tier_tokens,
+                  int32_t *slot_token, int maxp, int32_t *open_page, uint8_t *tiers_out, int32_t *status)
+{
+    if ((D != 64 && D != 128) || Hkv <= 0 || S < 0)
+        return OR_EINVAL;
+    int G = D / 8;
+    int32_t R[4] = {(int32_t)(oracle_page_bytes(D, 0) / SLOTS), (int32_t)(oracle_page_bytes(D, 1) / SLOTS),
+                    (int32_t)(oracle_page_bytes(D, 2) / SLOTS), 0};
+    for (int64_t row = 0; row < (int64_t)S * Hkv; row++) {
+        int s = (int)(row / Hkv), h = (int)(row % Hkv);
+        const uint16_t *k = keys + row * D;
+        const uint16_t *v = values + row * D;
+        /* encode */
+        double x[128], u[128], ss = 0;
+        for (int j = 0; j < D; j++) {
+            x[j] = f16_to_double(k[j]);
+            ss += x[j] * x[j];
+        }
+        double r = sqrt(ss);
+        uint16_t rb = double_to_f16_sat(r);
+        for (int j = 0; j < D; j++)
+            u[j] = r > 0 ? x[j] / r : 0.0;
+        uint8_t c8[16], c4[8];
+        double e8 = 0, e4 = 0;
+        for (int g = 0; g < G; g++) {
+            double d8, d4;
+            c8[g] = (uint8_t)nearest_dist(u + 8 * g, cb8 + ((size_t)h * G + g) * 256 * 8, 256, &d8);
+            int q4 = nearest_dist(u + 8 * g, cb4 + ((size_t)h * G + g) * 16 * 8, 16, &d4);
+            if (g % 2 == 0)
+                c4[g / 2] = (uint8_t)q4;
+            else
+                c4[g / 2] = (uint8_t)(c4[g / 2] | (q4 << 4));
+            e8 += d8;
+            e4 += d4;
+        }
+        /* tier */
+        int tier = 0;
+        if (!(protect && protect[row])) {
+            float sl[3];
+            int32_t dr[3];
+            int to[3];
+            int n = rdr_chain(R, scores[row], rb, (float)e8, (float)e4, sl, dr, to);
+            for (int q = 0; q < n && sl[q] <= threshold[s]; q++)
+                tier = to[q];
+        }
+        tiers_out[row] = (uint8_t)tier;
+        if (tier == 3)
+            continue;
+        /* place */
+        int32_t pi = open_page[row * 3 + tier] - 1, slot = SLOTS;
+        if (pi >= 0)
+            slot = ((page_meta[row * maxp + pi] >> 2) & 15) + 1;
+        if (slot == SLOTS) {
+            pi = num_pages[row];
+            uint64_t units = oracle_page_bytes(D, tier) / UNIT;
+            if (pi >= maxp) {
+                *status |= 1;
+                continue;
+            }
+            if (*cursor + units > arena_units) {
+                *status |= 2;
+                continue;
+            }
+            page_table[row * maxp + pi] = (uint32_t)*cursor;
+            memset(arena + *cursor * UNIT, 0, oracle_page_bytes(D, tier));
+            *cursor += units;
+            num_pages[row] = pi + 1;
+            open_page[row * 3 + tier] = pi + 1;
+            slot = 0;
+            if (slot_token)
+                for (int t = 0; t < SLOTS; t++)
+                    slot_token[((int64_t)row * maxp + pi) * SLOTS + t] = -1;
+        }
+        uint8_t *page = arena + (size_t)page_table[row * maxp + pi] * UNIT;
+        put_slot(D, tier, page, slot, k, v, rb, c8, c4);
+        page_meta[row * maxp + pi] = (uint8_t)(tier | (slot << 2));
+        tier_tokens[row * 3 + tier] += 1;
+        if (slot_token)
+            slot_token[((int64_t)row * maxp + pi) * SLOTS + slot] = (int32_t)pos[s];
+    }
+    return OR_OK;
 }
 
 /* Dense comparison cache: every token of the call, in index order, in tier-3
