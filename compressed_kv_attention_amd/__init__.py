@@ -87,7 +87,11 @@ def load():
         L.ada_code_error.restype = C.c_int
         L.rdr_solve_workspace_size.argtypes = [G, I32, I64]
         L.rdr_solve_workspace_size.restype = SZ
-        L.rdr_solve.argtypes = [G, I32, P, P, P, P, P, P, P, P, P, SZ, P]
+        L.rdr_solve.argtypes = [G, I32, P, P, P, P, P, P, P, P, P, P, SZ, P]
+        L.ada_append_state_bytes.argtypes = [G, I32]
+        L.ada_append_state_bytes.restype = SZ
+        L.ada_append.argtypes = [G, CV, P, P, P, P, P, P, P, P, P, P, P]
+        L.ada_append.restype = C.c_int
         L.rdr_solve.restype = C.c_int
         L.rdr_tier_counts_workspace_size.argtypes = [G, I32]
         L.rdr_tier_counts_workspace_size.restype = SZ
@@ -282,7 +286,7 @@ def solve_workspace_size(geom: Geom, num_seqs: int, n_tokens: int) -> int:
 
 
 def rdr_solve(geom: Geom, cu_tokens, budget_bytes, radius, err8, err4, scores, tiers, protect=None,
-              ws=None, stream=None):
+              threshold=None, ws=None, stream=None):
     """Tier of every (token, head) under a byte budget per sequence (see
     rdr_solve in include/ada.h).  cu_tokens / budget_bytes are host arrays;
     radius, err8, err4, scores, protect (u8 or None) and tiers (u8 out,
@@ -303,9 +307,53 @@ def rdr_solve(geom: Geom, cu_tokens, budget_bytes, radius, err8, err4, scores, t
                           _dev(radius, "radius", (torch.float16, torch.int16)),
                           _dev(err8, "err8", (torch.float32,)), _dev(err4, "err4", (torch.float32,)),
                           _dev(scores, "scores", (torch.float32,)), _dev(protect, "protect", (torch.uint8,)),
-                          _dev(tiers, "tiers", (torch.uint8,)), _dev(ws, "ws"), ws.numel(), _stream(stream))
+                          _dev(tiers, "tiers", (torch.uint8,)), _dev(threshold, "threshold", (torch.float32,)),
+                          _dev(ws, "ws"), ws.numel(), _stream(stream))
     _check(st, "rdr_solve")
     return ws
+
+
+class AppendState:
+    """Device state of the decode-step append (ada_append) for one cache:
+    the arena cursor, sticky status bits and each row's open pages."""
+
+    def __init__(self, geom: Geom, cache: "Cache"):
+        n = int(load().ada_append_state_bytes(C.byref(geom), cache.num_seqs))
+        self.buf = torch.zeros(n, dtype=torch.uint8, device=cache.arena.device)
+        self.cache = cache
+        self.push_cursor()
+
+    def push_cursor(self):
+        """Host cursor -> device (before appending after host-planned packs)."""
+        self.buf[:8].copy_(torch.from_numpy(self.cache.cursor.view(np.uint8).copy()))
+
+    def pull(self) -> int:
+        """Device cursor and page counts -> the cache's host copies (before a
+        host-planned pack); returns the status bits.  Synchronizes."""
+        c = self.buf[:16].cpu().numpy()
+        self.cache.cursor[:] = c[:8].view(np.uint64)
+        rows = self.cache.num_pages_host.shape[0]
+        self.cache.num_pages_host[:] = self.cache.num_pages[:rows].cpu().numpy()
+        return int(c[8:12].view(np.uint32)[0])
+
+
+def append(geom: Geom, cache: Cache, state: AppendState, cb8, cb4, keys, values, scores, threshold, pos,
+           protect=None, tiers=None, stream=None):
+    """One decode step's append (ada_append): keys / values [S][Hkv][D],
+    scores [S][Hkv], threshold f32 [S], pos int64 [S], all device tensors."""
+    S, H, D = cache.num_seqs, geom.num_kv_heads, geom.head_dim
+    for t, shape, name in ((keys, (S, H, D), "keys"), (values, (S, H, D), "values"), (scores, (S, H), "scores"),
+                           (threshold, (S,), "threshold"), (pos, (S,), "pos")):
+        if tuple(t.shape) != shape:
+            raise ValueError(f"{name} shape {tuple(t.shape)} != {shape}")
+    view = cache.view()
+    st = load().ada_append(C.byref(geom), C.byref(view), _dev(cb8, "cb8", (torch.float32,)),
+                           _dev(cb4, "cb4", (torch.float32,)), _dev(keys, "keys", (torch.float16,)),
+                           _dev(values, "values", (torch.bfloat16,)), _dev(scores, "scores", (torch.float32,)),
+                           _dev(protect, "protect", (torch.uint8,)), _dev(threshold, "threshold", (torch.float32,)),
+                           _dev(pos, "pos", (torch.int64,)), _dev(tiers, "tiers", (torch.uint8,)),
+                           _dev(state.buf, "state"), _stream(stream))
+    _check(st, "ada_append")
 
 
 def tier_counts(geom: Geom, cu_tokens, tiers, stream=None) -> np.ndarray:

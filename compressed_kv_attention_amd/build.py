@@ -15,7 +15,7 @@ CSRC = os.path.join(PKG, "csrc")
 OUT = os.path.join(PKG, "libada.so")
 BUILD = os.path.join(PKG, "_build")
 
-SOURCES = ["ada_abi.cpp", "decode.hip", "encode.hip", "pack.hip", "rdr.hip"]
+SOURCES = ["ada_abi.cpp", "decode.hip", "encode.hip", "pack.hip", "rdr.hip", "append.hip"]
 
 FLAGS = [
     "-O3", "-std=c++17", "--offload-arch=gfx950", "-fPIC",

@@ -488,7 +488,7 @@ size_t rdr_solve_workspace_size(const ada_geom *geom, int32_t num_seqs, int64_t 
 ada_status rdr_solve(const ada_geom *geom, int32_t num_seqs, const int32_t *cu_tokens_host,
                      const int64_t *budget_bytes_host, const uint16_t *radius, const float *err8,
                      const float *err4, const float *scores, const uint8_t *protect, uint8_t *tiers,
-                     void *ws, size_t ws_bytes, void *stream)
+                     float *threshold, void *ws, size_t ws_bytes, void *stream)
 {
     if (!geom_ok(geom) || num_seqs < 0 || !cu_ok(num_seqs, cu_tokens_host) || budget_bytes_host == nullptr)
         return ADA_EINVAL;
@@ -539,6 +539,7 @@ ada_status rdr_solve(const ada_geom *geom, int32_t num_seqs, const int32_t *cu_t
     a.scores = scores;
     a.protect = protect;
     a.tiers = tiers;
+    a.threshold = threshold;
     a.S = num_seqs;
     a.D = D;
     a.n_blocks = (int)blocks.size();
@@ -677,6 +678,53 @@ ada_status ada_decode_merge(const ada_geom *geom, const ada_cache *cache, const 
 {
     return decode_common(geom, cache, cb8, cb4, q, softmax_scale, out, lse, nullptr, num_splits, ws,
                          ws_bytes, stream, false, kStageMerge);
+}
+
+size_t ada_append_state_bytes(const ada_geom *geom, int32_t num_seqs)
+{
+    if (!geom_ok(geom) || num_seqs < 0)
+        return 0;
+    return 256 + align256(sizeof(int32_t) * 3 * (size_t)std::max<int64_t>((int64_t)num_seqs * geom->num_kv_heads, 1));
+}
+
+ada_status ada_append(const ada_geom *geom, const ada_cache *cache, const float *cb8, const float *cb4,
+                      const uint16_t *keys, const uint16_t *values, const float *scores, const uint8_t *protect,
+                      const float *threshold, const int64_t *pos, uint8_t *tiers_out, void *state, void *stream)
+{
+    if (!geom_ok(geom) || !cache_ok(cache) || cache->tier_tokens == nullptr || !cb8 || !cb4 || !keys ||
+        !values || !scores || !threshold || !pos || !state)
+        return ADA_EINVAL;
+    if ((reinterpret_cast<uintptr_t>(state) & 255) || (reinterpret_cast<uintptr_t>(keys) & 3) ||
+        (reinterpret_cast<uintptr_t>(values) & 3) || (reinterpret_cast<uintptr_t>(cb8) & 15) ||
+        (reinterpret_cast<uintptr_t>(cb4) & 15) || (reinterpret_cast<uintptr_t>(cache->arena) & 15))
+        return ADA_EINVAL;
+    const int64_t rows = (int64_t)cache->num_seqs * geom->num_kv_heads;
+    if (rows > INT32_MAX)
+        return ADA_EINVAL;
+    uint8_t *st8 = static_cast<uint8_t *>(state);
+    AppendArgs a;
+    a.arena = cache->arena;
+    a.page_table = cache->page_table;
+    a.page_meta = cache->page_meta;
+    a.num_pages = cache->num_pages;
+    a.tier_tokens = cache->tier_tokens;
+    a.slot_token = cache->slot_token;
+    a.cb8 = cb8;
+    a.cb4 = cb4;
+    a.keys = keys;
+    a.values = values;
+    a.scores = scores;
+    a.protect = protect;
+    a.threshold = threshold;
+    a.pos = pos;
+    a.tiers_out = tiers_out;
+    a.cursor = reinterpret_cast<unsigned long long *>(st8);
+    a.status = reinterpret_cast<unsigned int *>(st8 + 8);
+    a.open = reinterpret_cast<int32_t *>(st8 + 256);
+    a.capacity = cache->arena_units;
+    a.maxp = cache->max_pages_per_head;
+    a.Hkv = geom->num_kv_heads;
+    return launch_append(geom->head_dim, a, (int)rows, as_stream(stream)) == hipSuccess ? ADA_OK : ADA_EHIP;
 }
 
 size_t ada_decode_sym_workspace_size(const ada_geom *geom, int32_t num_seqs, int32_t max_pages_per_head,

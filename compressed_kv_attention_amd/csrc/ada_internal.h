@@ -1,5 +1,5 @@
 // Internal interface between the host entry points (ada_abi.cpp) and the
-// gfx950 kernels (decode.hip, encode.hip, pack.hip, rdr.hip).  Not installed.
+// gfx950 kernels (decode.hip, encode.hip, pack.hip, rdr.hip, append.hip).  Not installed.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -100,11 +100,35 @@ struct SolveArgs {
     const float *err8, *err4, *scores;
     const uint8_t *protect;   // or null
     uint8_t *tiers;
+    float *threshold;         // [S] slope threshold s* out, or null
     int S, D, n_blocks;
 };
 hipError_t launch_solve(const SolveArgs &a, hipStream_t st);
 hipError_t launch_tier_counts(int Hkv, int S, const int32_t *cu_dev, const uint8_t *tiers,
                               int32_t *counts, hipStream_t st);
+
+// ---- decode-step append ----------------------------------------------------
+struct AppendArgs {
+    uint8_t *arena;
+    uint32_t *page_table;
+    uint8_t *page_meta;
+    int32_t *num_pages;
+    int32_t *tier_tokens;
+    int32_t *slot_token;        // or null
+    const float *cb8, *cb4;
+    const uint16_t *keys, *values; // [S][Hkv][D]
+    const float *scores;        // [S][Hkv]
+    const uint8_t *protect;     // [S][Hkv] or null
+    const float *threshold;     // [S]
+    const int64_t *pos;         // [S]
+    uint8_t *tiers_out;         // [S][Hkv] or null
+    unsigned long long *cursor; // arena cursor, 128-byte units
+    unsigned int *status;       // sticky bits: 1 page table full, 2 arena full
+    int32_t *open;              // [rows][3] open page index + 1
+    unsigned long long capacity;
+    int maxp, Hkv;
+};
+hipError_t launch_append(int D, const AppendArgs &a, int rows, hipStream_t st);
 
 // ---- pack ----------------------------------------------------------------
 // Host-built plan of one pack call, copied into the workspace.

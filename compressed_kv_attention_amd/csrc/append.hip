@@ -1,0 +1,290 @@
+// Decode-step append for gfx950: encode, tier and place one new token per
+// (sequence, kv-head) row, in one kernel.
+//
+// SPHERICAL KV (arXiv 2605.18856), gist.science technical summary, section
+// 2.3 (dense keys are mapped to spherical codes, RDR filters and tiers them,
+// the result is stored compressed) and section 2.2 (tier-homogeneous pages;
+// tiers chosen under a budget).  Each new state is tiered by the solver's
+// chain rule with its sequence's slope threshold s* from the last solve --
+// the online continuation of the same Lagrangian allocation -- and goes into
+// the next free slot of its row's open page of that tier.  A row without a
+// usable open page takes a new one: the next page-table index and arena
+// space from a device-side bump cursor (a compare-and-swap loop that never
+// passes the arena's end), zeroed before the slot is written.  Nothing goes
+// through the host, so a decode loop can capture the step in a graph.
+//
+// One 256-thread block per row:
+//   - the key's norm (double, summed sequentially over D, as in encode) and
+//     its unit direction;
+//   - per group, the nearest 8-bit codeword (16 lanes, 16 codewords each,
+//     then a (distance, index) reduction over the 16 lanes) and the nearest
+//     4-bit codeword (one per lane); the chosen distances, summed in group
+//     order, are the code errors of ada_code_error;
+//   - the chain and the tier (binary32, as rdr_solve);
+//   - allocation if needed, then the slot's fields, metadata, counters.
+#include "ada_internal.h"
+#include "numfmt.h"
+
+namespace ada {
+namespace {
+
+#pragma clang fp contract(off)
+
+// The tier the chain rule gives a state for slope threshold th (binary32,
+// the same arithmetic as the budget solver).
+__device__ int chain_tier(int D, float w, uint16_t rbits, float e8, float e4, float th)
+{
+    const int R0 = page_bytes(D, 0) / kSlots, R1 = page_bytes(D, 1) / kSlots, R2 = page_bytes(D, 2) / kSlots;
+    const float wr = w * f16_bits_to_f32(rbits);
+    const float D1 = wr * sqrtf(e8), D2 = wr * sqrtf(e4), D3 = wr;
+    auto dist = [&](int i) { return i == 0 ? 0.0f : i == 1 ? D1 : i == 2 ? D2 : D3; };
+    auto rate = [&](int i) { return i == 0 ? R0 : i == 1 ? R1 : i == 2 ? R2 : 0; };
+    int c = 0, tier = 0;
+    bool go = true;
+    float prev = -INFINITY;
+    for (int it = 0; it < 3 && c < 3; it++) {
+        int best = -1;
+        float bs = 0.0f;
+        for (int j = c + 1; j < 4; j++) {
+            const float sl = (dist(j) - dist(c)) / (float)(rate(c) - rate(j)) + 0.0f;
+            if (best < 0 || sl <= bs) {
+                best = j;
+                bs = sl;
+            }
+        }
+        bs = bs < prev ? prev : bs;
+        go = go && bs <= th;
+        tier = go ? best : tier;
+        prev = bs;
+        c = best;
+    }
+    return tier;
+}
+
+template <int D>
+__global__ __launch_bounds__(256) void append_kernel(AppendArgs a)
+{
+    constexpr int G = D / 8;
+    __shared__ double u[D];
+    __shared__ double rn;
+    __shared__ double d8s[G], d4s[G];
+    __shared__ int c8s[G], c4s[G];
+    __shared__ int tier_s, pi_s, slot_s, fresh_s;
+    __shared__ uint32_t off_s;
+    __shared__ uint16_t rbits_s;
+    const int row = blockIdx.x, s = row / a.Hkv, h = row % a.Hkv;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const uint16_t *k = a.keys + (size_t)row * D;
+    const uint16_t *v = a.values + (size_t)row * D;
+
+    if (tid == 0) {
+        double ss = 0.0;
+        for (int j = 0; j < D; j++) {
+            const double x = (double)f16_bits_to_f32(k[j]);
+            ss = ss + x * x;
+        }
+        rn = sqrt(ss);
+    }
+    __syncthreads();
+    if (tid < D) {
+        const double x = (double)f16_bits_to_f32(k[tid]);
+        u[tid] = rn > 0.0 ? x / rn : 0.0;
+    }
+    __syncthreads();
+    if (tid < G * 16) {
+        const int g = tid / 16, j16 = tid % 16;
+        double uu[8];
+#pragma unroll
+        for (int j = 0; j < 8; j++)
+            uu[j] = u[8 * g + j];
+        const float *cb8 = a.cb8 + ((size_t)h * G + g) * kCodes8 * 8;
+        double bd = INFINITY;
+        int bc = 0;
+        for (int i = 0; i < kCodes8 / 16; i++) { // ascending codewords: strict < keeps the lowest
+            const int c = j16 + 16 * i;
+            const float4 w0 = *reinterpret_cast<const float4 *>(cb8 + c * 8);
+            const float4 w1 = *reinterpret_cast<const float4 *>(cb8 + c * 8 + 4);
+            const float w[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+            double d = 0.0;
+#pragma unroll
+            for (int j = 0; j < 8; j++) {
+                const double df = uu[j] - (double)w[j];
+                d = d + df * df;
+            }
+            if (d < bd) {
+                bd = d;
+                bc = c;
+            }
+        }
+        const float *cb4 = a.cb4 + (((size_t)h * G + g) * kCodes4 + j16) * 8;
+        const float4 w0 = *reinterpret_cast<const float4 *>(cb4);
+        const float4 w1 = *reinterpret_cast<const float4 *>(cb4 + 4);
+        const float w[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+        double b4 = 0.0;
+#pragma unroll
+        for (int j = 0; j < 8; j++) {
+            const double df = uu[j] - (double)w[j];
+            b4 = b4 + df * df;
+        }
+        int c4 = j16;
+        // (distance, index) minima over the group's 16 lanes
+#pragma unroll
+        for (int o = 8; o >= 1; o >>= 1) {
+            const double od = __shfl_xor(bd, o, 64);
+            const int oc = __shfl_xor(bc, o, 64);
+            if (od < bd || (od == bd && oc < bc)) {
+                bd = od;
+                bc = oc;
+            }
+            const double o4 = __shfl_xor(b4, o, 64);
+            const int oc4 = __shfl_xor(c4, o, 64);
+            if (o4 < b4 || (o4 == b4 && oc4 < c4)) {
+                b4 = o4;
+                c4 = oc4;
+            }
+        }
+        if (j16 == 0) {
+            c8s[g] = bc;
+            d8s[g] = bd;
+            c4s[g] = c4;
+            d4s[g] = b4;
+        }
+    }
+    __syncthreads();
+    if (tid == 0) {
+        double e8 = 0.0, e4 = 0.0;
+        for (int g = 0; g < G; g++) {
+            e8 = e8 + d8s[g];
+            e4 = e4 + d4s[g];
+        }
+        const uint16_t rb = f64_to_f16_sat(rn);
+        rbits_s = rb;
+        int tier = 0;
+        if (a.protect == nullptr || a.protect[row] == 0)
+            tier = chain_tier(D, a.scores[row], rb, (float)e8, (float)e4, a.threshold[s]);
+        if (a.tiers_out != nullptr)
+            a.tiers_out[row] = (uint8_t)tier;
+        int pi = -1, slot = kSlots, fresh = 0;
+        uint32_t off = 0;
+        if (tier < 3) {
+            pi = a.open[row * 3 + tier] - 1;
+            if (pi >= 0)
+                slot = ((a.page_meta[(size_t)row * a.maxp + pi] >> 2) & 15) + 1;
+            if (slot == kSlots) {
+                pi = a.num_pages[row];
+                const unsigned long long units = (unsigned long long)(page_bytes(D, tier) / kUnit);
+                if (pi >= a.maxp) {
+                    atomicOr(a.status, 1u);
+                    tier = 3;
+                } else {
+                    unsigned long long cur = atomicAdd(a.cursor, 0ull);
+                    bool ok = false;
+                    while (cur + units <= a.capacity) {
+                        const unsigned long long seen = atomicCAS(a.cursor, cur, cur + units);
+                        if (seen == cur) {
+                            ok = true;
+                            break;
+                        }
+                        cur = seen;
+                    }
+                    if (!ok) {
+                        atomicOr(a.status, 2u);
+                        tier = 3;
+                    } else {
+                        off = (uint32_t)cur;
+                        a.page_table[(size_t)row * a.maxp + pi] = off;
+                        a.num_pages[row] = pi + 1;
+                        a.open[row * 3 + tier] = pi + 1;
+                        slot = 0;
+                        fresh = 1;
+                    }
+                }
+            } else {
+                off = a.page_table[(size_t)row * a.maxp + pi];
+            }
+        }
+        tier_s = tier;
+        pi_s = pi;
+        slot_s = slot;
+        fresh_s = fresh;
+        off_s = off;
+    }
+    __syncthreads();
+    const int tier = tier_s;
+    if (tier == 3)
+        return;
+    const int pi = pi_s, slot = slot_s;
+    uint8_t *page = a.arena + (size_t)off_s * kUnit;
+    if (fresh_s) {
+        uint4 *p4 = reinterpret_cast<uint4 *>(page);
+        for (int i = tid; i < page_bytes(D, tier) / 16; i += 256)
+            p4[i] = make_uint4(0, 0, 0, 0);
+        if (a.slot_token != nullptr && tid < kSlots)
+            a.slot_token[((size_t)row * a.maxp + pi) * kSlots + tid] = -1;
+    }
+    __syncthreads();
+    if (tier == 0) {
+        for (int d = 2 * tid; d < D; d += 512) {
+            *reinterpret_cast<uint32_t *>(page + row_off(slot, d)) = *reinterpret_cast<const uint32_t *>(k + d);
+            const uint32_t vv = *reinterpret_cast<const uint32_t *>(v + d);
+            *reinterpret_cast<uint16_t *>(page + 32 * D + col_off(slot, d)) = (uint16_t)(vv & 0xffff);
+            *reinterpret_cast<uint16_t *>(page + 32 * D + col_off(slot, d + 1)) = (uint16_t)(vv >> 16);
+        }
+    } else if (tier == 1) {
+        for (int d = tid; d < D; d += 256)
+            *reinterpret_cast<uint16_t *>(page + col_off(slot, d)) = v[d];
+        if (tid < G)
+            page[codes_off(D, 1) + slot * G + tid] = (uint8_t)c8s[tid];
+        if (tid == 0)
+            *reinterpret_cast<uint16_t *>(page + radius_off(D, 1) + 2 * slot) = rbits_s;
+    } else if (tid < 64) {
+        // int8 values with one fp16 scale, as in the pack
+        float amax = 0.f;
+        for (int d = lane; d < D; d += 64)
+            amax = fmaxf(amax, fabsf(bf16_bits_to_f32(v[d])));
+#pragma unroll
+        for (int o = 32; o >= 1; o >>= 1)
+            amax = fmaxf(amax, __shfl_xor(amax, o, 64));
+        const float s32 = amax / 127.0f;
+        const uint16_t sh = f64_to_f16_sat((double)s32);
+        const float sc = f16_bits_to_f32(sh);
+        for (int d = lane; d < D; d += 64) {
+            int q = 0;
+            if (sc != 0.f) {
+                float y = rintf(bf16_bits_to_f32(v[d]) / sc);
+                y = fminf(fmaxf(y, -127.f), 127.f);
+                q = (int)y;
+            }
+            page[col8_off(slot, d)] = (uint8_t)(int8_t)q;
+        }
+        if (lane < G / 2)
+            page[codes_off(D, 2) + slot * (G / 2) + lane] = (uint8_t)(c4s[2 * lane] | (c4s[2 * lane + 1] << 4));
+        if (lane == 0) {
+            *reinterpret_cast<uint16_t *>(page + radius_off(D, 2) + 2 * slot) = rbits_s;
+            *reinterpret_cast<uint16_t *>(page + vscale_off(D) + 2 * slot) = sh;
+        }
+    }
+    if (tid == 0) {
+        a.page_meta[(size_t)row * a.maxp + pi] = (uint8_t)(tier | (slot << 2));
+        a.tier_tokens[row * 3 + tier] += 1;
+        if (a.slot_token != nullptr)
+            a.slot_token[((size_t)row * a.maxp + pi) * kSlots + slot] = (int32_t)a.pos[s];
+    }
+}
+
+} // namespace
+
+hipError_t launch_append(int D, const AppendArgs &a, int rows, hipStream_t st)
+{
+    if (rows == 0)
+        return hipSuccess;
+    if (D == 128)
+        hipLaunchKernelGGL(append_kernel<128>, dim3(rows), dim3(256), 0, st, a);
+    else if (D == 64)
+        hipLaunchKernelGGL(append_kernel<64>, dim3(rows), dim3(256), 0, st, a);
+    else
+        return hipErrorInvalidValue;
+    return hipGetLastError();
+}
+
+} // namespace ada

@@ -210,11 +210,16 @@ __device__ Sel select_prefix(const SolveArgs &a, int s, int passes)
     return r;
 }
 
-__global__ __launch_bounds__(256) void solve_zero(unsigned long long *hist, int64_t n)
+// Clears the digit histograms; gives every sequence's threshold its value
+// for the cases with no search (no demotion needed: -inf; every demotion:
+// +inf, the result for a sequence with no states and a negative cap).
+__global__ __launch_bounds__(256) void solve_zero(SolveArgs a, int64_t n)
 {
     const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (i < n)
-        hist[i] = 0ull;
+        a.hist[i] = 0ull;
+    if (a.threshold != nullptr && i < a.S)
+        a.threshold[i] = a.seqs[i].need <= 0 ? -INFINITY : INFINITY;
 }
 
 template <int P>
@@ -270,6 +275,11 @@ __global__ __launch_bounds__(kSolveThreads) void solve_assign(SolveArgs a)
     __syncthreads();
     const int state = sel.state;
     const uint32_t kstar = sel.prefix;
+    if (a.threshold != nullptr && tid == 0 && blk.first == sq.begin) {
+        // s* back from its order-preserving key
+        const uint32_t bits = (kstar & 0x80000000u) ? (kstar & 0x7fffffffu) : ~kstar;
+        a.threshold[blk.seq] = state == 1 ? -INFINITY : state == 2 ? INFINITY : __uint_as_float(bits);
+    }
     const int64_t end = sq.begin + sq.n_items;
 #pragma unroll
     for (int k = 0; k < 4; k++) {
@@ -340,10 +350,10 @@ hipError_t launch_code_error(int D, int Hkv, int64_t n_tokens, const uint16_t *k
 
 hipError_t launch_solve(const SolveArgs &a, hipStream_t st)
 {
-    if (a.n_blocks == 0)
+    if (a.S == 0)
         return hipSuccess;
     const int64_t nh = (int64_t)kSolvePasses * a.S * 256;
-    hipLaunchKernelGGL(solve_zero, dim3((unsigned)((nh + 255) / 256)), dim3(256), 0, st, a.hist, nh);
+    hipLaunchKernelGGL(solve_zero, dim3((unsigned)((nh + 255) / 256)), dim3(256), 0, st, a, nh);
     if (hipError_t e = hipGetLastError(); e != hipSuccess)
         return e;
     const dim3 grid((unsigned)a.n_blocks), blk(kSolveThreads);

@@ -238,6 +238,8 @@ size_t rdr_solve_workspace_size(const ada_geom *geom, int32_t num_seqs, int64_t 
  *   f32 (ada_code_error), scores [N][Hkv] f32: finite and >= 0 (device).
  *   protect [N][Hkv] u8 on the DEVICE (nonzero = protected) or NULL.
  *   tiers [N][Hkv] u8 out: 0, 1, 2 kept tier, 3 dropped.
+ *   threshold [S] f32 out (device) or NULL: each sequence's s*; -inf when
+ *     need <= 0, +inf when every demotion is taken (ada_append's input).
  *   ws: rdr_solve_workspace_size bytes, 256-byte aligned, any content.
  * Seven kernels on `stream`; the small per-sequence table is copied from
  * host memory first.
@@ -245,7 +247,7 @@ size_t rdr_solve_workspace_size(const ada_geom *geom, int32_t num_seqs, int64_t 
 ada_status rdr_solve(const ada_geom *geom, int32_t num_seqs, const int32_t *cu_tokens_host,
                      const int64_t *budget_bytes_host, const uint16_t *radius, const float *err8,
                      const float *err4, const float *scores, const uint8_t *protect,
-                     uint8_t *tiers, void *ws, size_t ws_bytes, void *stream);
+                     uint8_t *tiers, float *threshold, void *ws, size_t ws_bytes, void *stream);
 
 /* Workspace bytes of rdr_tier_counts. */
 size_t rdr_tier_counts_workspace_size(const ada_geom *geom, int32_t num_seqs);
@@ -283,6 +285,46 @@ ada_status rdr_pack_tiers(const ada_geom *geom, const ada_cache *cache, int32_t 
                           const uint32_t *place_perm_host, const int64_t *pos_base_host,
                           uint64_t *arena_cursor_host, int32_t *num_pages_host, void *ws,
                           size_t ws_bytes, void *stream);
+
+/* Bytes of the device state ada_append keeps between decode steps. */
+size_t ada_append_state_bytes(const ada_geom *geom, int32_t num_seqs);
+
+/*
+ * ada_append -- one decode step's new token per (sequence, kv-head) row:
+ * encode, tier and place it, in one kernel, with no host round trip.
+ * [TS] 2.3 (dense keys mapped to codes, filtered and tiered by RDR, stored
+ * compressed) and 2.2 (tier-homogeneous pages; tiers under a budget).
+ * Reading:
+ *   - the key is encoded exactly as ada_encode does, and its code errors
+ *     are those of ada_code_error;
+ *   - its tier follows the rdr_solve chain rule with its sequence's slope
+ *     threshold (threshold[s], e.g. rdr_solve's output): the online
+ *     continuation of the last solve's Lagrangian allocation. Protected
+ *     states take tier 0; tier 3 is a drop;
+ *   - a kept state fills the next free slot of its row's open page of that
+ *     tier. If the row has none, or it is full, the row takes a new page:
+ *     the next page-table index and arena space from a device-side bump
+ *     cursor that never passes arena_units. The page is zeroed first.
+ *   keys fp16 / values bf16 [S][Hkv][D]; scores f32 [S][Hkv]; protect u8
+ *   [S][Hkv] or NULL; threshold f32 [S]; pos int64 [S] (recorded in
+ *   slot_token); tiers_out u8 [S][Hkv] or NULL (the tier each state was
+ *   given). All device pointers.
+ *   state: ada_append_state_bytes, 256-byte aligned, device memory:
+ *     [0]   u64 arena cursor in 128-byte units. Set it from the host cursor
+ *           before the first append, and read it back (with num_pages)
+ *           before the next host-planned pack.
+ *     [8]   u32 status, sticky bits: 1 = a row's page table was full,
+ *           2 = the arena was full. That row's token is not stored.
+ *     [256] i32 [S*Hkv][3]: each row's open page index + 1 per tier
+ *           (0 = none). Zero-filled: no open page (pages from packs stay as
+ *           they are).
+ *   Rows race only for the cursor, so which page offset a row gets is not
+ *   fixed; what each row holds is.
+ */
+ada_status ada_append(const ada_geom *geom, const ada_cache *cache, const float *cb8,
+                      const float *cb4, const uint16_t *keys, const uint16_t *values,
+                      const float *scores, const uint8_t *protect, const float *threshold,
+                      const int64_t *pos, uint8_t *tiers_out, void *state, void *stream);
 
 /* Workspace bytes of ada_decode_sym: ada_decode's plus every row's table. */
 size_t ada_decode_sym_workspace_size(const ada_geom *geom, int32_t num_seqs,

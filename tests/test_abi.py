@@ -131,12 +131,12 @@ def test_rdr_entry_points_host_errors():
     def solve(budget, ws_bytes=1 << 20, ws=fake):
         b = np.asarray(budget, np.int64)
         return L.rdr_solve(C.byref(g), 2, cup, b.ctypes.data_as(C.c_void_p), fake, fake, fake, fake, None,
-                           fake, ws, ws_bytes, None)
+                           fake, None, ws, ws_bytes, None)
 
     assert solve([100, -1]) == ada.EINVAL
     assert solve([100, 100], ws_bytes=16) == ada.EWORKSPACE
     assert solve([100, 100], ws=C.c_void_p(257)) == ada.EWORKSPACE
-    assert L.rdr_solve(C.byref(g), 2, cup, None, fake, fake, fake, fake, None, fake, fake, 1 << 20,
+    assert L.rdr_solve(C.byref(g), 2, cup, None, fake, fake, fake, fake, None, fake, None, fake, 1 << 20,
                        None) == ada.EINVAL
     assert ada.solve_workspace_size(g, 2, 30) >= 4 * 256 * 8 * 2
     # tier counts: null output, too small a workspace
