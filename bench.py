@@ -267,6 +267,56 @@ def append_path(dev, reps=20):
     return res
 
 
+def append_steps(dev, steps=200):
+    """Times the decode-step append (ada_append) on the 32-layer workload's
+    shape: one new token for each of 8 sequences x 8 KV heads (one layer),
+    tiered by the slope thresholds of a budget solve over a 512-token
+    chunk, captured once in a graph and replayed."""
+    cfg = synth.WORKLOADS[5]
+    S, H, D, n = cfg.num_seqs, cfg.num_kv_heads, cfg.head_dim, cfg.append_tokens
+    geom = ada.Geom(D, cfg.num_q_heads, H)
+    cb8, cb4 = (t.to(dev) for t in synth.codebooks(cfg, 0))
+    cu = synth.cu_tokens(np.full(S, n, np.int64))
+    keys = synth.keys(cfg, 0, S * n, dev, stream="k-append")
+    scores = synth.scores(cfg, 0, S * n, stream="score-append").to(dev)
+    r = torch.empty((S * n, H), dtype=torch.float16, device=dev)
+    c8 = torch.empty((S * n, H, D // 8), dtype=torch.uint8, device=dev)
+    c4 = torch.empty((S * n, H, D // 16), dtype=torch.uint8, device=dev)
+    ada.encode(geom, keys, cb8, cb4, r, c8, c4)
+    e8 = torch.empty((S * n, H), device=dev)
+    e4 = torch.empty((S * n, H), device=dev)
+    ada.code_error(geom, keys, cb8, cb4, c8, c4, e8, e4)
+    tiers = torch.empty((S * n, H), dtype=torch.uint8, device=dev)
+    th = torch.empty(S, device=dev)
+    ada.rdr_solve(geom, cu, synth.budget_bytes(cfg, np.full(S, n, np.int64)), r, e8, e4, scores, tiers,
+                  threshold=th)
+    maxp = steps // 16 + 8
+    cache = ada.Cache(geom, S, maxp, S * H * maxp * ada.page_bytes(D, 0))
+    state = ada.AppendState(geom, cache)
+    kb = synth.keys(cfg, 0, S, dev, stream="k-step").contiguous()
+    vb = synth.values(cfg, 0, S, dev, stream="v-step").contiguous()
+    sb = synth.scores(cfg, 0, S, stream="s-step").to(dev)
+    pb = torch.zeros(S, dtype=torch.int64, device=dev)
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        ada.append(geom, cache, state, cb8, cb4, kb, vb, sb, th, pb)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    status = state.pull()
+    return {"workload": f"{cfg.name}: one token x {S} sequences x {H} heads per step, one layer",
+            "steps": steps, "us_per_step": e0.elapsed_time(e1) / steps * 1e3, "status": status,
+            "pages": int(cache.num_pages_host.sum()),
+            "note": "graph replays of ada_append back to back (the same token each step)"}
+
+
 def solver_full(cfg, dev, reps=5):
     """Times the budget solver over a whole workload (one layer): code error,
     solve, tier counts and tier-given pack of every token."""
@@ -497,6 +547,10 @@ def main():
             f"with the budget solver: code error {ap['solver']['code_error_us']:.1f} us, "
             f"solve {ap['solver']['solve_us']:.1f} us, counts {ap['solver']['tier_counts_us']:.1f} us, "
             f"pack {ap['solver']['pack_tiers_us']:.1f} us")
+    if not args.no_append:
+        result["append_step"] = append_steps(dev)
+        log(f"decode-step append: {result['append_step']['us_per_step']:.2f} us per step "
+            f"(64 token-heads, graph replay)")
     if args.solver_full:
         result["solver_full"] = solver_full(cfg, dev)
         sf = result["solver_full"]

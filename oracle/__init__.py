@@ -58,6 +58,10 @@ def lib():
         L.oracle_pack_tiers.restype = I
         L.oracle_append.argtypes = [I, I, I, P, P, P, P, P, P, P, P, P, U64, P, P, P, P, P, P, I, P, P, P]
         L.oracle_append.restype = I
+        L.oracle_retier.argtypes = [I, I, I, P, P, P, P, P, P, U64, P, P, P, P, P, P, I, P, P]
+        L.oracle_retier.restype = I
+        L.oracle_retier_plan.argtypes = [I, I, I, P, P, P, I, I, I, P, P, P]
+        L.oracle_retier_plan.restype = I
         L.oracle_dense_pack.argtypes = [I, I, I, P, P, P, P, P, U64, P, P, P, P, I]
         L.oracle_dense_pack.restype = I
         L.oracle_decode.argtypes = [I, I, I, I, I, P, P, P, P, P, P, P, D_, P, P, P, P, I64, I64, I]
@@ -289,6 +293,33 @@ def append(cache: HostCache, keys, values, scores, cb8, cb4, threshold, pos, ope
                              _p(cache.slot_token), cache.maxp, _p(open_page), _p(tiers), _p(status))
     assert rc == 0
     return tiers, int(status[0])
+
+
+def retier(cache: HostCache, cb8, cb4, rows, pages, target, open_page) -> int:
+    """Demote (target 1 / 2) or evict (3) the listed pages in place; returns
+    the status bits.  open_page int32 [S*Hkv][3] is updated in place."""
+    r = np.ascontiguousarray(rows, np.int32)
+    p = np.ascontiguousarray(pages, np.int32)
+    t = np.ascontiguousarray(target, np.uint8)
+    c8, c4 = _np(cb8, np.float32), _np(cb4, np.float32)
+    status = np.zeros(1, np.int32)
+    rc = lib().oracle_retier(cache.D, cache.Hkv, len(r), _p(r), _p(p), _p(t), _p(c8), _p(c4), _p(cache.arena),
+                             cache.arena_units, _p(cache.cursor), _p(cache.page_table), _p(cache.page_meta),
+                             _p(cache.num_pages), _p(cache.tier_tokens), _p(cache.slot_token), cache.maxp,
+                             _p(open_page), _p(status))
+    assert rc == 0
+    return int(status[0])
+
+
+def retier_plan(cache: HostCache, budget_bytes, demote_to=2, cap=1 << 20):
+    """The re-tiering policy: (rows, pages, target) arrays."""
+    bud = np.ascontiguousarray(budget_bytes, np.int64)
+    rows = np.zeros(cap, np.int32)
+    pages = np.zeros(cap, np.int32)
+    tgt = np.zeros(cap, np.uint8)
+    n = lib().oracle_retier_plan(cache.D, cache.Hkv, cache.S, _p(bud), _p(cache.num_pages), _p(cache.page_meta),
+                                 cache.maxp, demote_to, cap, _p(rows), _p(pages), _p(tgt))
+    return rows[:n], pages[:n], tgt[:n]
 
 
 def row_tier_counts(cu_tokens, tiers) -> np.ndarray:

@@ -990,6 +990,183 @@ int oracle_append(int D, int Hkv, int S, const uint16_t *keys, const uint16_t *v
     return OR_OK;
 }
 
+/* ------------------------------------------------------------------------ */
+/* Re-tiering as T grows.                                                    */
+/*                                                                           */
+/* [TS] 2.2: states are kept and tiered under a strict memory budget, in     */
+/* tier-homogeneous pages.  As decode steps append states, a sequence's      */
+/* pages outgrow its budget; re-tiering brings it back.  Readings:           */
+/*   mechanics -- a full or partial fp16 page can be demoted in place to an  */
+/*   8-bit or 4-bit page: its keys are encoded from the page's own fp16 keys  */
+/*   exactly as encode does, its values kept (8-bit) or quantised (4-bit),    */
+/*   the result written to new arena space and the page-table entry pointed  */
+/*   at it (same index, same slots, same slot positions); any page can be    */
+/*   evicted: per row, in descending page index, the row's last page moves   */
+/*   into the evicted page's place.  Demotions run before evictions.  A page */
+/*   that is not fp16 (demotion) or not in use sets status bit 4 and is       */
+/*   skipped; no arena space sets bit 2.                                      */
+/*   policy -- stored pages keep no utility scores, so age stands in for     */
+/*   utility: while a sequence's page bytes exceed its budget, its oldest    */
+/*   full fp16 page (lowest page index, then lowest head) is demoted to the  */
+/*   given tier; when none is left, its oldest coded page is evicted; then   */
+/*   its oldest remaining fp16 page.                                         */
+/* ------------------------------------------------------------------------ */
+
+static void read_key_value(int D, const uint8_t *page, int t, uint16_t *k, uint16_t *v)
+{
+    for (int d = 0; d < D; d++) {
+        memcpy(&k[d], page + row_off(t, d), 2);
+        memcpy(&v[d], page + off_v(D, 0) + col_off(t, d), 2);
+    }
+}
+
+int oracle_retier(int D, int Hkv, int n, const int32_t *rows, const int32_t *pages, const uint8_t *target,
+                  const float *cb8, const float *cb4, uint8_t *arena, uint64_t arena_units, uint64_t *cursor,
+                  uint32_t *page_table, uint8_t *page_meta, int32_t *num_pages, int32_t *tier_tokens,
+                  int32_t *slot_token, int maxp, int32_t *open_page, int32_t *status)
+{
+    if ((D != 64 && D != 128) || Hkv <= 0 || n < 0)
+        return OR_EINVAL;
+    int G = D / 8;
+    /* demotions, in list order */
+    for (int i = 0; i < n; i++) {
+        if (target[i] != 1 && target[i] != 2)
+            continue;
+        int32_t row = rows[i], p = pages[i];
+        int tier = target[i], h = row % Hkv;
+        if (p < 0 || p >= num_pages[row] || (page_meta[(int64_t)row * maxp + p] & 3) != 0) {
+            *status |= 4;
+            continue;
+        }
+        uint64_t units = oracle_page_bytes(D, tier) / UNIT;
+        if (*cursor + units > arena_units) {
+            *status |= 2;
+            continue;
+        }
+        int nv = ((page_meta[(int64_t)row * maxp + p] >> 2) & 15) + 1;
+        const uint8_t *old = arena + (size_t)page_table[(int64_t)row * maxp + p] * UNIT;
+        uint8_t *pg = arena + *cursor * UNIT;
+        memset(pg, 0, oracle_page_bytes(D, tier));
+        for (int t = 0; t < nv; t++) {
+            uint16_t k[128], v[128], r;
+            uint8_t c8[16], c4[8];
+            read_key_value(D, old, t, k, v);
+            encode_args a = {D, 1, k, cb8 + (size_t)h * G * 256 * 8, cb4 + (size_t)h * G * 16 * 8,
+                             &r, c8, c4, NULL, NULL};
+            encode_one(&a, 0);
+            put_slot(D, tier, pg, t, k, v, r, c8, c4);
+        }
+        page_table[(int64_t)row * maxp + p] = (uint32_t)*cursor;
+        *cursor += units;
+        page_meta[(int64_t)row * maxp + p] = (uint8_t)(tier | ((nv - 1) << 2));
+        tier_tokens[row * 3 + 0] -= nv;
+        tier_tokens[row * 3 + tier] += nv;
+        if (open_page[row * 3 + 0] == p + 1)
+            open_page[row * 3 + 0] = 0;
+    }
+    /* evictions: each row's, in descending page index */
+    int32_t *ev = malloc(sizeof(int32_t) * (size_t)(n > 0 ? n : 1));
+    for (int i = 0; i < n; i++) {
+        if (target[i] != 3)
+            continue;
+        int32_t row = rows[i];
+        int seen = 0;
+        for (int j = 0; j < i; j++)
+            seen |= target[j] == 3 && rows[j] == row;
+        if (seen)
+            continue; /* the row's evictions were done with its first entry */
+        int m = 0;
+        for (int j = i; j < n; j++)
+            if (target[j] == 3 && rows[j] == row)
+                ev[m++] = pages[j];
+        for (int a = 1; a < m; a++) /* descending */
+            for (int b = a; b > 0 && ev[b] > ev[b - 1]; b--) {
+                int32_t t = ev[b];
+                ev[b] = ev[b - 1];
+                ev[b - 1] = t;
+            }
+        for (int a = 0; a < m; a++) {
+            int32_t p = ev[a], last = num_pages[row] - 1;
+            if (p < 0 || p > last) {
+                *status |= 4;
+                continue;
+            }
+            uint8_t meta = page_meta[(int64_t)row * maxp + p];
+            tier_tokens[row * 3 + (meta & 3)] -= ((meta >> 2) & 15) + 1;
+            for (int t = 0; t < 3; t++)
+                if (open_page[row * 3 + t] == p + 1)
+                    open_page[row * 3 + t] = 0;
+            if (p != last) {
+                page_table[(int64_t)row * maxp + p] = page_table[(int64_t)row * maxp + last];
+                page_meta[(int64_t)row * maxp + p] = page_meta[(int64_t)row * maxp + last];
+                if (slot_token)
+                    for (int t = 0; t < SLOTS; t++)
+                        slot_token[((int64_t)row * maxp + p) * SLOTS + t] =
+                            slot_token[((int64_t)row * maxp + last) * SLOTS + t];
+                for (int t = 0; t < 3; t++)
+                    if (open_page[row * 3 + t] == last + 1)
+                        open_page[row * 3 + t] = p + 1;
+            }
+            num_pages[row] = last;
+        }
+    }
+    free(ev);
+    return OR_OK;
+}
+
+/* The re-tiering policy: the (row, page, target) list, at most cap entries;
+ * returns the number of entries. */
+int oracle_retier_plan(int D, int Hkv, int S, const int64_t *budget_bytes, const int32_t *num_pages,
+                       const uint8_t *page_meta, int maxp, int demote_to, int cap, int32_t *rows,
+                       int32_t *pages, uint8_t *target)
+{
+    int n = 0;
+    for (int s = 0; s < S; s++) {
+        int64_t bytes = 0;
+        int maxn = 0;
+        for (int h = 0; h < Hkv; h++) {
+            int row = s * Hkv + h;
+            for (int p = 0; p < num_pages[row]; p++)
+                bytes += (int64_t)oracle_page_bytes(D, page_meta[(int64_t)row * maxp + p] & 3);
+            if (num_pages[row] > maxn)
+                maxn = num_pages[row];
+        }
+        /* three sweeps over (page index, head): full fp16 pages demoted,
+         * coded pages evicted, remaining fp16 pages evicted */
+        for (int sweep = 0; sweep < 3; sweep++)
+            for (int p = 0; p < maxn && bytes > budget_bytes[s]; p++)
+                for (int h = 0; h < Hkv && bytes > budget_bytes[s]; h++) {
+                    int row = s * Hkv + h;
+                    if (p >= num_pages[row])
+                        continue;
+                    uint8_t meta = page_meta[(int64_t)row * maxp + p];
+                    int tier = meta & 3, full = ((meta >> 2) & 15) == 15;
+                    int32_t tgt = -1;
+                    if (sweep == 0 && tier == 0 && full)
+                        tgt = demote_to;
+                    if (sweep == 1 && (tier == 1 || tier == 2))
+                        tgt = 3;
+                    /* (pages demoted by this plan are not evicted by it; a
+                     * later call sees them as coded) */
+                    if (sweep == 2 && tier == 0 && !full)
+                        tgt = 3;
+                    if (tgt < 0)
+                        continue;
+                    if (n >= cap)
+                        return n;
+                    rows[n] = row;
+                    pages[n] = p;
+                    target[n] = (uint8_t)tgt;
+                    n++;
+                    if (tgt == 3)
+                        bytes -= (int64_t)oracle_page_bytes(D, tier);
+                    else
+                        bytes -= (int64_t)oracle_page_bytes(D, 0) - (int64_t)oracle_page_bytes(D, tgt);
+                }
+    }
+    return n;
+}
+
 /* Dense comparison cache: every token of the call, in index order, in tier-3
  * pages (K converted fp16 -> bf16 with round-to-nearest-even, V bf16). */
 int oracle_dense_pack(int D, int Hkv, int S, const int32_t *cu_tokens, const uint16_t *keys,

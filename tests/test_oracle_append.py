@@ -99,3 +99,83 @@ def test_append_capacity_status_bits():
     # arena for three fp16 pages (32 units each at D = 64)
     hc, _, st = _append_all(case, cfg, np.full(2, -np.inf, np.float32), 8, 3 * 4096)
     assert st == 2 and int(hc.num_pages.sum()) == 3 and hc.cursor[0] == 96
+
+
+def _packed(case, cfg, tiers, maxp=40):
+    r, c8, c4 = oracle.encode(case["keys"], case["cb8"], case["cb4"])
+    hc = oracle.HostCache(cfg.head_dim, cfg.num_kv_heads, len(case["lens"]), maxp, 1 << 22)
+    assert oracle.pack_tiers(hc, case["cu"], tiers, case["keys"], case["values"], r, c8, c4) == 0
+    return hc
+
+
+@pytest.mark.parametrize("tier", [1, 2])
+def test_retier_demotion_equals_packing_at_that_tier(tier):
+    """Demoting fp16 pages re-encodes their keys from the page itself: the
+    result is the page pack_tiers builds for the same tokens at that tier."""
+    cfg = small_workload(D=128, Hq=4, Hkv=2, S=2, T=70, seed=40 + tier)
+    case = make_case(cfg, lens=[70, 33])
+    fp16 = _packed(case, cfg, np.zeros((case["N"], 2), np.uint8))
+    coded = _packed(case, cfg, np.full((case["N"], 2), tier, np.uint8))
+    rows, pages = np.nonzero(np.arange(fp16.maxp)[None, :] < fp16.num_pages[:, None])
+    open_page = np.zeros((4, 3), np.int32)
+    st = oracle.retier(fp16, case["cb8"], case["cb4"], rows, pages, np.full(len(rows), tier), open_page)
+    assert st == 0
+    for row in range(4):
+        assert _row_pages(fp16, row) == _row_pages(coded, row)
+    assert np.array_equal(fp16.tier_tokens, coded.tier_tokens)
+    # demoting a page that is not fp16 is refused and changes nothing
+    before = (fp16.page_table.copy(), fp16.page_meta.copy(), fp16.cursor.copy())
+    assert oracle.retier(fp16, case["cb8"], case["cb4"], [0], [0], [2], open_page) == 4
+    assert np.array_equal(before[0], fp16.page_table) and before[2][0] == fp16.cursor[0]
+
+
+def test_retier_eviction_keeps_the_other_pages_and_remaps_open_pages():
+    cfg = small_workload(D=64, Hq=2, Hkv=2, S=1, T=120, seed=45)
+    case = make_case(cfg, lens=[120])
+    rng = np.random.default_rng(45)
+    tiers = rng.integers(0, 3, (120, 2)).astype(np.uint8)
+    hc = _packed(case, cfg, tiers)
+    before = [_row_pages(hc, row) for row in range(2)]
+    n0 = hc.num_pages.copy()
+    open_page = np.array([[n0[0], 0, 0], [0, 0, n0[1]]], np.int32)  # each row's last page is open
+    ev0 = [0, int(n0[0]) - 1, 2]
+    ev1 = [int(n0[1]) - 2]
+    st = oracle.retier(hc, case["cb8"], case["cb4"], [0, 1, 0, 0], [ev0[0], ev1[0], ev0[1], ev0[2]],
+                       [3, 3, 3, 3], open_page)
+    assert st == 0
+    for row, ev in ((0, ev0), (1, ev1)):
+        kept = [pg for i, pg in enumerate(before[row]) if i not in ev]
+        assert sorted(_row_pages(hc, row)) == sorted(kept)
+        assert hc.num_pages[row] == n0[row] - len(ev)
+        counts = np.zeros(3, np.int64)
+        for meta, _, _ in kept:
+            counts[meta & 3] += ((meta >> 2) & 15) + 1
+        assert np.array_equal(hc.tier_tokens[row], counts)
+    assert open_page[0, 0] == 0                     # row 0's open page was evicted
+    last1 = before[1][-1]
+    assert _row_pages(hc, 1)[open_page[1, 2] - 1] == last1   # row 1's open page moved, still open
+
+
+def test_retier_plan_brings_sequences_under_budget_oldest_first():
+    cfg = small_workload(D=128, Hq=4, Hkv=2, S=2, T=400, seed=46)
+    case = make_case(cfg, lens=[400, 250])
+    hc = _packed(case, cfg, np.zeros((case["N"], 2), np.uint8), maxp=32)
+    used = [sum(oracle.page_bytes(128, int(hc.page_meta[r, p]) & 3) for r in rows for p in range(hc.num_pages[r]))
+            for rows in ((0, 1), (2, 3))]
+    budgets = [int(used[0] * 0.7), int(used[1] * 0.2)]
+    rows, pages, tgt = oracle.retier_plan(hc, budgets, demote_to=2)
+    # sequence 0: only demotions of its oldest full fp16 pages, oldest first
+    s0 = rows < 2
+    assert (tgt[s0] == 2).all() and list(zip(pages[s0], rows[s0])) == sorted(zip(pages[s0], rows[s0]))
+    open_page = np.zeros((4, 3), np.int32)
+    assert oracle.retier(hc, case["cb8"], case["cb4"], rows, pages, tgt, open_page) == 0
+    now = [sum(oracle.page_bytes(128, int(hc.page_meta[r, p]) & 3) for r in rr for p in range(hc.num_pages[r]))
+           for rr in ((0, 1), (2, 3))]
+    assert now[0] <= budgets[0]
+    # sequence 1 needs evictions too: a second plan (now seeing coded pages) gets it there
+    rows2, pages2, tgt2 = oracle.retier_plan(hc, budgets, demote_to=2)
+    assert (rows2 >= 2).all() and (tgt2 == 3).any()
+    assert oracle.retier(hc, case["cb8"], case["cb4"], rows2, pages2, tgt2, open_page) == 0
+    now = sum(oracle.page_bytes(128, int(hc.page_meta[r, p]) & 3) for r in (2, 3) for p in range(hc.num_pages[r]))
+    assert now <= budgets[1]
+    assert len(oracle.retier_plan(hc, budgets)[0]) == 0
