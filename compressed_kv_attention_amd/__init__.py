@@ -92,6 +92,10 @@ def load():
         L.ada_append_state_bytes.restype = SZ
         L.ada_append.argtypes = [G, CV, P, P, P, P, P, P, P, P, P, P, P]
         L.ada_append.restype = C.c_int
+        L.ada_retier.argtypes = [G, CV, P, P, I32, P, P, P, P, P]
+        L.ada_retier.restype = C.c_int
+        L.ada_retier_plan.argtypes = [G, I32, P, P, P, I32, I32, I32, P, P, P, P]
+        L.ada_retier_plan.restype = C.c_int
         L.rdr_solve.restype = C.c_int
         L.rdr_tier_counts_workspace_size.argtypes = [G, I32]
         L.rdr_tier_counts_workspace_size.restype = SZ
@@ -354,6 +358,37 @@ def append(geom: Geom, cache: Cache, state: AppendState, cb8, cb4, keys, values,
                            _dev(pos, "pos", (torch.int64,)), _dev(tiers, "tiers", (torch.uint8,)),
                            _dev(state.buf, "state"), _stream(stream))
     _check(st, "ada_append")
+
+
+def retier(geom: Geom, cache: Cache, state: AppendState, cb8, cb4, rows, pages, target, stream=None):
+    """Demote (target 1 / 2) or evict (3) listed pages in place (ada_retier).
+    rows / pages int32 and target uint8 are device tensors of one length."""
+    n = int(rows.numel())
+    if pages.numel() != n or target.numel() != n:
+        raise ValueError("rows, pages and target must have one length")
+    view = cache.view()
+    st = load().ada_retier(C.byref(geom), C.byref(view), _dev(cb8, "cb8", (torch.float32,)),
+                           _dev(cb4, "cb4", (torch.float32,)), n, _dev(rows, "rows", (torch.int32,)),
+                           _dev(pages, "pages", (torch.int32,)), _dev(target, "target", (torch.uint8,)),
+                           _dev(state.buf, "state"), _stream(stream))
+    _check(st, "ada_retier")
+
+
+def retier_plan(geom: Geom, budget_bytes, num_pages_host, page_meta_host, demote_to: int = 2,
+                cap: int = 1 << 20):
+    """The age-ordered re-tiering policy (ada_retier_plan) on host copies of
+    the tables: (rows, pages, target) numpy arrays."""
+    bud, budp = _host(budget_bytes, np.int64, "budget_bytes")
+    npg, npgp = _host(num_pages_host, np.int32, "num_pages")
+    pm, pmp = _host(page_meta_host, np.uint8, "page_meta")
+    rows = np.zeros(cap, np.int32)
+    pages = np.zeros(cap, np.int32)
+    tgt = np.zeros(cap, np.uint8)
+    n = C.c_int32(0)
+    _check(load().ada_retier_plan(C.byref(geom), len(bud), budp, npgp, pmp, pm.shape[1], demote_to, cap,
+                                  rows.ctypes.data_as(C.c_void_p), pages.ctypes.data_as(C.c_void_p),
+                                  tgt.ctypes.data_as(C.c_void_p), C.byref(n)), "ada_retier_plan")
+    return rows[:n.value], pages[:n.value], tgt[:n.value]
 
 
 def tier_counts(geom: Geom, cu_tokens, tiers, stream=None) -> np.ndarray:

@@ -727,6 +727,103 @@ ada_status ada_append(const ada_geom *geom, const ada_cache *cache, const float 
     return launch_append(geom->head_dim, a, (int)rows, as_stream(stream)) == hipSuccess ? ADA_OK : ADA_EHIP;
 }
 
+ada_status ada_retier(const ada_geom *geom, const ada_cache *cache, const float *cb8, const float *cb4,
+                      int32_t n, const int32_t *rows, const int32_t *pages, const uint8_t *target, void *state,
+                      void *stream)
+{
+    if (!geom_ok(geom) || !cache_ok(cache) || cache->tier_tokens == nullptr || !cb8 || !cb4 || !state || n < 0)
+        return ADA_EINVAL;
+    if (n > 0 && (!rows || !pages || !target))
+        return ADA_EINVAL;
+    if ((reinterpret_cast<uintptr_t>(state) & 255) || (reinterpret_cast<uintptr_t>(cb8) & 15) ||
+        (reinterpret_cast<uintptr_t>(cb4) & 15) || (reinterpret_cast<uintptr_t>(cache->arena) & 15))
+        return ADA_EINVAL;
+    const int64_t nrows = (int64_t)cache->num_seqs * geom->num_kv_heads;
+    if (nrows > INT32_MAX)
+        return ADA_EINVAL;
+    uint8_t *st8 = static_cast<uint8_t *>(state);
+    RetierArgs a;
+    a.arena = cache->arena;
+    a.page_table = cache->page_table;
+    a.page_meta = cache->page_meta;
+    a.num_pages = cache->num_pages;
+    a.tier_tokens = cache->tier_tokens;
+    a.slot_token = cache->slot_token;
+    a.cb8 = cb8;
+    a.cb4 = cb4;
+    a.rows = rows;
+    a.pages = pages;
+    a.target = target;
+    a.cursor = reinterpret_cast<unsigned long long *>(st8);
+    a.status = reinterpret_cast<unsigned int *>(st8 + 8);
+    a.open = reinterpret_cast<int32_t *>(st8 + 256);
+    a.capacity = cache->arena_units;
+    a.n = n;
+    a.maxp = cache->max_pages_per_head;
+    a.Hkv = geom->num_kv_heads;
+    return launch_retier(geom->head_dim, a, (int)nrows, as_stream(stream)) == hipSuccess ? ADA_OK : ADA_EHIP;
+}
+
+ada_status ada_retier_plan(const ada_geom *geom, int32_t num_seqs, const int64_t *budget_bytes_host,
+                           const int32_t *num_pages_host, const uint8_t *page_meta_host,
+                           int32_t max_pages_per_head, int32_t demote_to, int32_t cap, int32_t *rows_out,
+                           int32_t *pages_out, uint8_t *target_out, int32_t *n_out)
+{
+    if (!geom_ok(geom) || num_seqs < 0 || !budget_bytes_host || !num_pages_host || !page_meta_host ||
+        max_pages_per_head < 0 || (demote_to != 1 && demote_to != 2) || cap < 0 || !n_out ||
+        (cap > 0 && (!rows_out || !pages_out || !target_out)))
+        return ADA_EINVAL;
+    const int H = geom->num_kv_heads, D = geom->head_dim;
+    int32_t n = 0;
+    for (int s = 0; s < num_seqs; s++) {
+        int64_t bytes = 0;
+        int32_t deepest = 0;
+        for (int h = 0; h < H; h++) {
+            const int64_t r = (int64_t)s * H + h;
+            const int32_t np = num_pages_host[r];
+            if (np < 0 || np > max_pages_per_head)
+                return ADA_EINVAL;
+            for (int32_t q = 0; q < np; q++)
+                bytes += page_bytes(D, page_meta_host[r * max_pages_per_head + q] & 3);
+            deepest = std::max(deepest, np);
+        }
+        // passes over (page index, head): demote full fp16 pages; evict coded
+        // pages; evict the remaining (partial) fp16 pages
+        for (int pass = 0; pass < 3 && bytes > budget_bytes_host[s]; pass++) {
+            for (int32_t q = 0; q < deepest && bytes > budget_bytes_host[s]; q++) {
+                for (int h = 0; h < H && bytes > budget_bytes_host[s]; h++) {
+                    const int64_t r = (int64_t)s * H + h;
+                    if (q >= num_pages_host[r])
+                        continue;
+                    const uint8_t m = page_meta_host[r * max_pages_per_head + q];
+                    const int tier = m & 3;
+                    const bool full = ((m >> 2) & 15) == 15;
+                    int tgt = 0;
+                    if (pass == 0 && tier == 0 && full)
+                        tgt = demote_to;
+                    else if (pass == 1 && (tier == 1 || tier == 2))
+                        tgt = 3;
+                    else if (pass == 2 && tier == 0 && !full)
+                        tgt = 3;
+                    if (tgt == 0)
+                        continue;
+                    if (n == cap) {
+                        *n_out = n;
+                        return ADA_OK;
+                    }
+                    rows_out[n] = (int32_t)r;
+                    pages_out[n] = q;
+                    target_out[n] = (uint8_t)tgt;
+                    n++;
+                    bytes -= tgt == 3 ? page_bytes(D, tier) : page_bytes(D, 0) - page_bytes(D, tgt);
+                }
+            }
+        }
+    }
+    *n_out = n;
+    return ADA_OK;
+}
+
 size_t ada_decode_sym_workspace_size(const ada_geom *geom, int32_t num_seqs, int32_t max_pages_per_head,
                                      int32_t num_splits)
 {

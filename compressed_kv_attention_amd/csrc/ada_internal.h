@@ -130,6 +130,24 @@ struct AppendArgs {
 };
 hipError_t launch_append(int D, const AppendArgs &a, int rows, hipStream_t st);
 
+struct RetierArgs {
+    uint8_t *arena;
+    uint32_t *page_table;
+    uint8_t *page_meta;
+    int32_t *num_pages;
+    int32_t *tier_tokens;
+    int32_t *slot_token;        // or null
+    const float *cb8, *cb4;
+    const int32_t *rows, *pages; // [n]
+    const uint8_t *target;       // [n]: 1, 2 demote to that tier; 3 evict
+    unsigned long long *cursor;
+    unsigned int *status;        // adds bit 4: a listed page could not be re-tiered
+    int32_t *open;
+    unsigned long long capacity;
+    int n, maxp, Hkv;
+};
+hipError_t launch_retier(int D, const RetierArgs &a, int rows, hipStream_t st);
+
 // ---- pack ----------------------------------------------------------------
 // Host-built plan of one pack call, copied into the workspace.
 struct PackSeq {

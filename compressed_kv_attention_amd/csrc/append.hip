@@ -272,6 +272,200 @@ __global__ __launch_bounds__(256) void append_kernel(AppendArgs a)
     }
 }
 
+// ---- re-tiering -----------------------------------------------------------------
+// Demotion: one block per list entry whose target is 1 or 2.  The page must
+// be fp16 and in use (else status bit 4).  Its slots' keys are encoded from
+// the page's own fp16 keys exactly as ada_encode does (norm summed
+// sequentially in double, nearest codeword in double, lowest index on ties),
+// the values kept (8-bit tier: the value section moves over unchanged) or
+// quantised (4-bit tier), the new page built in LDS, written to new arena
+// space, and the page-table entry pointed at it.
+template <int D>
+__global__ __launch_bounds__(256) void retier_demote_kernel(RetierArgs a)
+{
+    constexpr int G = D / 8;
+    __shared__ double u[kSlots][D];
+    __shared__ double rn[kSlots];
+    __shared__ int code[kSlots][G];
+    __shared__ uint4 img4[page_bytes(D, 1) / 16];
+    __shared__ int go_s, nv_s;
+    __shared__ uint32_t off_s;
+    const int i = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tier = a.target[i];
+    if (tier != 1 && tier != 2)
+        return;
+    const int row = a.rows[i], p = a.pages[i], h = row % a.Hkv;
+    if (tid == 0) {
+        int go = p >= 0 && p < a.num_pages[row] && (a.page_meta[(size_t)row * a.maxp + p] & 3) == 0;
+        if (!go)
+            atomicOr(a.status, 4u);
+        go_s = go;
+        nv_s = go ? ((a.page_meta[(size_t)row * a.maxp + p] >> 2) & 15) + 1 : 0;
+        off_s = go ? a.page_table[(size_t)row * a.maxp + p] : 0;
+    }
+    __syncthreads();
+    if (!go_s)
+        return;
+    const int nv = nv_s;
+    const uint8_t *old = a.arena + (size_t)off_s * kUnit;
+    if (tid < nv) {
+        double ss = 0.0;
+        for (int d = 0; d < D; d++) {
+            const double x = (double)f16_bits_to_f32(*reinterpret_cast<const uint16_t *>(old + row_off(tid, d)));
+            ss = ss + x * x;
+        }
+        rn[tid] = sqrt(ss);
+    }
+    __syncthreads();
+    for (int k = tid; k < nv * D; k += 256) {
+        const int t = k / D, d = k % D;
+        const double x = (double)f16_bits_to_f32(*reinterpret_cast<const uint16_t *>(old + row_off(t, d)));
+        u[t][d] = rn[t] > 0.0 ? x / rn[t] : 0.0;
+    }
+    for (int k = tid; k < page_bytes(D, tier) / 16; k += 256)
+        img4[k] = make_uint4(0, 0, 0, 0);
+    __syncthreads();
+    // nearest codeword of slot t, group g in the target tier's codebook
+    const int K = tier == 1 ? kCodes8 : kCodes4;
+    const float *cb = tier == 1 ? a.cb8 : a.cb4;
+    for (int k = tid; k < nv * G; k += 256) {
+        const int t = k / G, g = k % G;
+        const float *w = cb + ((size_t)h * G + g) * K * 8;
+        double bd = INFINITY;
+        int bc = 0;
+        for (int c = 0; c < K; c++) {
+            double d = 0.0;
+#pragma unroll
+            for (int j = 0; j < 8; j++) {
+                const double df = u[t][8 * g + j] - (double)w[c * 8 + j];
+                d = d + df * df;
+            }
+            if (d < bd) {
+                bd = d;
+                bc = c;
+            }
+        }
+        code[t][g] = bc;
+    }
+    __syncthreads();
+    uint8_t *img = reinterpret_cast<uint8_t *>(img4);
+    if (tier == 1) {
+        // the value section keeps its layout: copy it
+        const uint4 *v4 = reinterpret_cast<const uint4 *>(old + 32 * D);
+        for (int k = tid; k < 32 * D / 16; k += 256)
+            img4[k] = v4[k];
+        for (int k = tid; k < nv * G; k += 256)
+            img[codes_off(D, 1) + k] = (uint8_t)code[k / G][k % G];
+        if (tid < nv)
+            *reinterpret_cast<uint16_t *>(img + radius_off(D, 1) + 2 * tid) = f64_to_f16_sat(rn[tid]);
+    } else {
+        for (int t = wave; t < nv; t += 4) {
+            float amax = 0.f;
+            for (int d = lane; d < D; d += 64)
+                amax = fmaxf(amax, fabsf(bf16_bits_to_f32(*reinterpret_cast<const uint16_t *>(old + 32 * D + col_off(t, d)))));
+#pragma unroll
+            for (int o = 32; o >= 1; o >>= 1)
+                amax = fmaxf(amax, __shfl_xor(amax, o, 64));
+            const float s32 = amax / 127.0f;
+            const uint16_t sh = f64_to_f16_sat((double)s32);
+            const float sc = f16_bits_to_f32(sh);
+            for (int d = lane; d < D; d += 64) {
+                int q = 0;
+                if (sc != 0.f) {
+                    float y = rintf(bf16_bits_to_f32(*reinterpret_cast<const uint16_t *>(old + 32 * D + col_off(t, d))) / sc);
+                    y = fminf(fmaxf(y, -127.f), 127.f);
+                    q = (int)y;
+                }
+                img[col8_off(t, d)] = (uint8_t)(int8_t)q;
+            }
+            if (lane < G / 2)
+                img[codes_off(D, 2) + t * (G / 2) + lane] = (uint8_t)(code[t][2 * lane] | (code[t][2 * lane + 1] << 4));
+            if (lane == 0) {
+                *reinterpret_cast<uint16_t *>(img + radius_off(D, 2) + 2 * t) = f64_to_f16_sat(rn[t]);
+                *reinterpret_cast<uint16_t *>(img + vscale_off(D) + 2 * t) = sh;
+            }
+        }
+    }
+    if (tid == 0) {
+        const unsigned long long units = (unsigned long long)(page_bytes(D, tier) / kUnit);
+        unsigned long long cur = atomicAdd(a.cursor, 0ull);
+        bool ok = false;
+        while (cur + units <= a.capacity) {
+            const unsigned long long seen = atomicCAS(a.cursor, cur, cur + units);
+            if (seen == cur) {
+                ok = true;
+                break;
+            }
+            cur = seen;
+        }
+        if (!ok)
+            atomicOr(a.status, 2u);
+        go_s = ok;
+        off_s = (uint32_t)cur;
+    }
+    __syncthreads();
+    if (!go_s)
+        return;
+    uint4 *dst = reinterpret_cast<uint4 *>(a.arena + (size_t)off_s * kUnit);
+    for (int k = tid; k < page_bytes(D, tier) / 16; k += 256)
+        dst[k] = img4[k];
+    if (tid == 0) {
+        a.page_table[(size_t)row * a.maxp + p] = off_s;
+        a.page_meta[(size_t)row * a.maxp + p] = (uint8_t)(tier | ((nv - 1) << 2));
+        atomicSub(&a.tier_tokens[row * 3 + 0], nv);
+        atomicAdd(&a.tier_tokens[row * 3 + tier], nv);
+        if (a.open[row * 3 + 0] == p + 1)
+            a.open[row * 3 + 0] = 0;
+    }
+}
+
+// Eviction: one thread per row takes the row's listed pages in descending
+// page index; the row's last page moves into each evicted page's place.
+__global__ __launch_bounds__(256) void retier_evict_kernel(RetierArgs a, int rows)
+{
+    const int row = blockIdx.x * 256 + threadIdx.x;
+    if (row >= rows)
+        return;
+    int prev = 0x7fffffff;
+    for (;;) {
+        // the largest listed page of this row below the previous one
+        int p = -1;
+        bool any = false;
+        for (int i = 0; i < a.n; i++)
+            if (a.target[i] == 3 && a.rows[i] == row && a.pages[i] < prev) {
+                any = true;
+                p = a.pages[i] > p ? a.pages[i] : p;
+            }
+        if (!any)
+            break;
+        prev = p;
+        const int last = a.num_pages[row] - 1;
+        if (p < 0 || p > last) {
+            atomicOr(a.status, 4u);
+            if (p < 0)
+                break;
+            continue;
+        }
+        const size_t e = (size_t)row * a.maxp;
+        const uint8_t meta = a.page_meta[e + p];
+        a.tier_tokens[row * 3 + (meta & 3)] -= ((meta >> 2) & 15) + 1;
+        for (int t = 0; t < 3; t++)
+            if (a.open[row * 3 + t] == p + 1)
+                a.open[row * 3 + t] = 0;
+        if (p != last) {
+            a.page_table[e + p] = a.page_table[e + last];
+            a.page_meta[e + p] = a.page_meta[e + last];
+            if (a.slot_token != nullptr)
+                for (int t = 0; t < kSlots; t++)
+                    a.slot_token[(e + p) * kSlots + t] = a.slot_token[(e + last) * kSlots + t];
+            for (int t = 0; t < 3; t++)
+                if (a.open[row * 3 + t] == last + 1)
+                    a.open[row * 3 + t] = p + 1;
+        }
+        a.num_pages[row] = last;
+    }
+}
+
 } // namespace
 
 hipError_t launch_append(int D, const AppendArgs &a, int rows, hipStream_t st)
@@ -285,6 +479,25 @@ hipError_t launch_append(int D, const AppendArgs &a, int rows, hipStream_t st)
     else
         return hipErrorInvalidValue;
     return hipGetLastError();
+}
+
+hipError_t launch_retier(int D, const RetierArgs &a, int rows, hipStream_t st)
+{
+    if (a.n > 0) {
+        if (D == 128)
+            hipLaunchKernelGGL(retier_demote_kernel<128>, dim3(a.n), dim3(256), 0, st, a);
+        else if (D == 64)
+            hipLaunchKernelGGL(retier_demote_kernel<64>, dim3(a.n), dim3(256), 0, st, a);
+        else
+            return hipErrorInvalidValue;
+        if (hipError_t e = hipGetLastError(); e != hipSuccess)
+            return e;
+    }
+    if (a.n > 0 && rows > 0) {
+        hipLaunchKernelGGL(retier_evict_kernel, dim3((rows + 255) / 256), dim3(256), 0, st, a, rows);
+        return hipGetLastError();
+    }
+    return hipSuccess;
 }
 
 } // namespace ada

@@ -326,6 +326,51 @@ ada_status ada_append(const ada_geom *geom, const ada_cache *cache, const float 
                       const float *scores, const uint8_t *protect, const float *threshold,
                       const int64_t *pos, uint8_t *tiers_out, void *state, void *stream);
 
+/*
+ * ada_retier -- re-tiering as a sequence outgrows its budget: demote listed
+ * fp16 pages in place, evict listed pages.  [TS] 2.2 (states kept and
+ * tiered under a strict memory budget, in tier-homogeneous pages).
+ * Reading:
+ *   - target 1 or 2 demotes an fp16 page (full or not) to that tier. The
+ *     page's keys are encoded from its own fp16 keys, exactly as ada_encode
+ *     does. Its values are kept (8-bit tier) or quantised as in rdr_pack
+ *     (4-bit tier). The new page goes to arena space from the state's
+ *     cursor, and the page-table entry (same index, same slots) points at
+ *     it. The old bytes stay behind: the arena only grows.
+ *   - target 3 evicts a page: per row, in descending page index, the row's
+ *     last page moves into its place.
+ *   - Demotions run before evictions. Each page may be listed once.
+ *   - A page that cannot be demoted (not fp16) or is not in use adds status
+ *     bit 4. No arena space adds bit 2.
+ *   - tier_tokens, num_pages and the open pages in `state` are kept
+ *     current.
+ *   rows, pages [n] int32 and target [n] u8 are DEVICE arrays (the call can
+ *   be captured). state: as in ada_append.
+ */
+ada_status ada_retier(const ada_geom *geom, const ada_cache *cache, const float *cb8,
+                      const float *cb4, int32_t n, const int32_t *rows, const int32_t *pages,
+                      const uint8_t *target, void *state, void *stream);
+
+/*
+ * ada_retier_plan -- host-side policy for ada_retier. Stored pages keep no
+ * utility scores, so age stands in for utility (reading). For each
+ * sequence whose page bytes exceed budget_bytes_host[s], in three passes
+ * over (page index, then head), oldest first:
+ *   1. demote full fp16 pages to `demote_to` (1 or 2);
+ *   2. evict coded pages;
+ *   3. evict the remaining partial fp16 pages;
+ * each until the sequence fits. Pages demoted by a plan are not also
+ * evicted by it, so a second plan may be needed.
+ *   num_pages_host [S*Hkv], page_meta_host [S*Hkv][max_pages_per_head]:
+ *   host copies of the tables. Writes at most cap entries to rows_out /
+ *   pages_out / target_out (host) and their number to *n_out.
+ */
+ada_status ada_retier_plan(const ada_geom *geom, int32_t num_seqs, const int64_t *budget_bytes_host,
+                           const int32_t *num_pages_host, const uint8_t *page_meta_host,
+                           int32_t max_pages_per_head, int32_t demote_to, int32_t cap,
+                           int32_t *rows_out, int32_t *pages_out, uint8_t *target_out,
+                           int32_t *n_out);
+
 /* Workspace bytes of ada_decode_sym: ada_decode's plus every row's table. */
 size_t ada_decode_sym_workspace_size(const ada_geom *geom, int32_t num_seqs,
                                      int32_t max_pages_per_head, int32_t num_splits);

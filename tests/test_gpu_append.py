@@ -190,3 +190,54 @@ def test_append_step_in_a_graph_equals_eager():
         for p in range(int(eager.num_pages[row])):
             n = ada.page_bytes(128, int(pm[row, p]) & 3)
             assert np.array_equal(ag[int(pt_g[row, p]) * 128:][:n], ae[int(pt_e[row, p]) * 128:][:n])
+
+
+def _bytes_per_seq(hc, S, H):
+    return [sum(oracle.page_bytes(hc.D, int(hc.page_meta[r, p]) & 3)
+                for r in range(s * H, s * H + H) for p in range(hc.num_pages[r])) for s in range(S)]
+
+
+@pytest.mark.parametrize("D,demote_to", [(128, 2), (64, 1)])
+def test_decode_loop_with_retiering_under_a_fixed_budget(D, demote_to):
+    """Decode steps append one token per sequence; every 16 steps the pages
+    are re-tiered to the budget (plan on the host, demotion and eviction on
+    the device).  GPU and oracle run the same loop; rows, counters, open
+    pages and decode outputs match throughout."""
+    cfg = small_workload(D=D, Hq=8, Hkv=2, S=2, T=200, seed=240 + D)
+    lens = [200, 120]
+    case, hc, _, _ = _base(cfg, lens, 100, 8)
+    S, H = 2, 2
+    neg = np.full(S, -np.inf, np.float32)   # appends keep fp16; re-tiering does the rest
+    budgets = np.array(_bytes_per_seq(hc, S, H), np.int64) * 9 // 10
+    geom = geom_of(cfg)
+    dc = _upload(hc, geom)
+    state = ada.AppendState(geom, dc)
+    open_page = np.zeros((S * H, 3), np.int32)
+    cb8, cb4 = to_dev(case["cb8"]), to_dev(case["cb4"])
+    for step in range(64):
+        k, v, sc = _new_tokens(cfg, step, S)
+        pos = np.array(lens, np.int64) + step
+        ada.append(geom, dc, state, cb8, cb4, to_dev(k), to_dev(v), to_dev(sc), to_dev(neg), to_dev(pos))
+        _, st = oracle.append(hc, k, v, sc.numpy(), case["cb8"], case["cb4"], neg, pos, open_page)
+        assert st == 0
+        if step % 16 == 15:
+            assert state.pull() == 0
+            rows, pages, tgt = ada.retier_plan(geom, budgets, dc.num_pages_host,
+                                               dc.page_meta.cpu().numpy(), demote_to=demote_to)
+            o = oracle.retier_plan(hc, budgets, demote_to=demote_to)
+            assert all(np.array_equal(x, y) for x, y in zip((rows, pages, tgt), o))
+            flush(f"[retier] D={D} step {step}: {len(rows)} pages ({np.bincount(tgt, minlength=4)[1:]})")
+            ada.retier(geom, dc, state, cb8, cb4, to_dev(rows), to_dev(pages), to_dev(tgt))
+            assert oracle.retier(hc, case["cb8"], case["cb4"], rows, pages, tgt, open_page) == 0
+            assert state.pull() == 0
+            _compare(dc, hc, f"retier step {step}")
+            assert np.array_equal(state.buf[256:256 + 12 * 4].cpu().numpy().view(np.int32).reshape(4, 3),
+                                  open_page)
+    assert int(dc.cursor[0]) == int(hc.cursor[0])
+    now = _bytes_per_seq(hc, S, H)
+    ref = oracle.decode(hc, case["cb8"], case["cb4"], case["q"], cfg.sigma, nthreads=8)
+    out, lse, _ = decode_outputs(geom, dc, to_dev(case["q"]), with_logits=False)
+    ada.decode(geom, dc, cb8, cb4, to_dev(case["q"]), cfg.sigma, out, lse)
+    torch.cuda.synchronize()
+    assert np.abs(out.cpu().double().numpy() - ref["out"]).max() <= OUT_TOL
+    flush(f"[retier] final bytes {now} vs budgets {list(budgets)}")
