@@ -527,15 +527,18 @@ __global__ __launch_bounds__((Waves<D, NH>::THREADS)) void decode_main(DecodeArg
     const int last = n_mine - 1;
     const uint32_t *pt = a.page_table + (size_t)row * a.maxp;
     const uint8_t *pm = a.page_meta + (size_t)row * a.maxp;
-    // Prologue: every load is issued before any is waited for -- the wave's
-    // first page (straight from the table), the workgroup's table entries,
-    // the codewords and query slices of the LUT, the query operand -- so
-    // the prologue costs about one memory latency.  Then the entries go to
-    // LDS and the LUT is tabulated into LDS.
+    // Prologue: the wave's first table entry, the workgroup's table
+    // entries, the codewords and query slices of the LUT and the query
+    // operand are all loaded before any is waited for (one memory latency).
+    // The first page's loads go out only after that wait: vector-memory
+    // waits drain in issue order, so a page issued earlier would hold up
+    // the tabulation behind its own latency.  The tabulation then overlaps
+    // the page's loads.
     PageRegs<D> bufA, bufB;
+    uint2 first = make_uint2(0u, 0u);
     if (n_mine > 0) {
         const int p0 = split + wave * a.nsplit;
-        fetch_entry<D, DENSE>(bufA, make_uint2(pt[p0], pm[p0]), a.arena, L);
+        first = make_uint2(pt[p0], pm[p0]);
     }
     constexpr int TE = 2; // table entries per thread held in registers
     uint32_t te_off[TE], te_meta[TE];
@@ -575,13 +578,15 @@ __global__ __launch_bounds__((Waves<D, NH>::THREADS)) void decode_main(DecodeArg
     // Query operand of the key MFMA: lane h + 16 r takes dims 16 b + 4 r ..
     // +3 of head h (zero for h >= NH), as bf16 (bf16 keys) or as fp16
     // scaled by 2^-e_h with the head's largest |q| in [2^14, 2^15).
+    // (branch-free: lanes of unused heads read head NH - 1 and drop it)
     u32x2 qraw[D / 16];
+    const int hq_ld = L.hl < NH ? L.hl : NH - 1;
 #pragma unroll
-    for (int b = 0; b < D / 16; b++) {
-        qraw[b] = u32x2{0u, 0u};
-        if (L.hl < NH)
-            qraw[b] = *reinterpret_cast<const u32x2 *>(qrow + (size_t)L.hl * D + 16 * b + 4 * L.r);
-    }
+    for (int b = 0; b < D / 16; b++)
+        qraw[b] = *reinterpret_cast<const u32x2 *>(qrow + (size_t)hq_ld * D + 16 * b + 4 * L.r);
+#pragma unroll
+    for (int b = 0; b < D / 16; b++)
+        qraw[b] = L.hl < NH ? qraw[b] : u32x2{0u, 0u};
     // per-head max |q| (each wave on its own: in pass p lane j holds 8 dims
     // of head p HPP + j / (D/8))
     int eh = 0;
@@ -591,12 +596,16 @@ __global__ __launch_bounds__((Waves<D, NH>::THREADS)) void decode_main(DecodeArg
 #pragma unroll
         for (int h0 = 0; h0 < NH; h0 += HPP) {
             float mx = 0.f;
-            if (lane < (NH - h0 < HPP ? NH - h0 : HPP) * LPH) {
-                const uint4 v = *reinterpret_cast<const uint4 *>(qrow + (size_t)h0 * D + 8 * lane);
+            {
+                // (branch-free: lanes past the group's heads read its last
+                // slice and drop it)
+                const int nl = (NH - h0 < HPP ? NH - h0 : HPP) * LPH;
+                const uint4 v = *reinterpret_cast<const uint4 *>(qrow + (size_t)h0 * D + 8 * (lane < nl ? lane : nl - 1));
                 const uint32_t u[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
                 for (int e = 0; e < 4; e++)
                     mx = fmaxf(mx, fmaxf(fabsf(bf16_lo(u[e])), fabsf(bf16_hi(u[e]))));
+                mx = lane < nl ? mx : 0.f;
             }
 #pragma unroll
             for (int o = 1; o < LPH; o <<= 1)
@@ -628,6 +637,11 @@ __global__ __launch_bounds__((Waves<D, NH>::THREADS)) void decode_main(DecodeArg
         }
     }
     const float lsc = ldexpf(a.sigma, eh) * kLog2e;
+    // The wave's first page: its loads go out only now, after every other
+    // prologue load has been waited for, so the tabulation below overlaps
+    // them instead of waiting behind them.
+    if (n_mine > 0)
+        fetch_entry<D, DENSE>(bufA, first, a.arena, L);
 #pragma unroll
     for (int j = 0; j < TE; j++)
         if (tid + j * kThreads < n_wg)
