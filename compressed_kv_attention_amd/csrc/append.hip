@@ -13,13 +13,14 @@
 // passes the arena's end), zeroed before the slot is written.  Nothing goes
 // through the host, so a decode loop can capture the step in a graph.
 //
-// One 256-thread block per row:
+// One block of G waves per row:
 //   - the key's norm (double, summed sequentially over D, as in encode) and
 //     its unit direction;
-//   - per group, the nearest 8-bit codeword (16 lanes, 16 codewords each,
-//     then a (distance, index) reduction over the 16 lanes) and the nearest
-//     4-bit codeword (one per lane); the chosen distances, summed in group
-//     order, are the code errors of ada_code_error;
+//   - per group (one wave), the nearest 8-bit codeword (4 per lane, their
+//     loads issued together, then a (distance, index) reduction over the
+//     wave) and the nearest 4-bit codeword (one per lane); the chosen
+//     distances, summed in group order, are the code errors of
+//     ada_code_error;
 //   - the chain and the tier (binary32, as rdr_solve);
 //   - allocation if needed, then the slot's fields, metadata, counters.
 #include "ada_internal.h"
@@ -62,74 +63,108 @@ __device__ int chain_tier(int D, float w, uint16_t rbits, float e8, float e4, fl
 }
 
 template <int D>
-__global__ __launch_bounds__(256) void append_kernel(AppendArgs a)
+__global__ __launch_bounds__(D / 8 * 64) void append_kernel(AppendArgs a)
 {
     constexpr int G = D / 8;
+    constexpr int NT = G * 64; // one wave per code group
     __shared__ double u[D];
+    __shared__ float xk[D];
     __shared__ double rn;
     __shared__ double d8s[G], d4s[G];
     __shared__ int c8s[G], c4s[G];
     __shared__ int tier_s, pi_s, slot_s, fresh_s;
     __shared__ uint32_t off_s;
     __shared__ uint16_t rbits_s;
+    __shared__ int open_s[3], nvalid_s[3], npages_s;
+    __shared__ uint32_t open_off_s[3];
+    __shared__ unsigned long long cur_s;
     const int row = blockIdx.x, s = row / a.Hkv, h = row % a.Hkv;
     const int tid = threadIdx.x, lane = tid & 63;
     const uint16_t *k = a.keys + (size_t)row * D;
     const uint16_t *v = a.values + (size_t)row * D;
 
+    // the row's allocation state, read by one lane while the key is encoded
+    if (tid == 64) {
+        int op[3];
+        for (int t = 0; t < 3; t++)
+            op[t] = a.open[row * 3 + t] - 1;
+        npages_s = a.num_pages[row];
+        cur_s = atomicAdd(a.cursor, 0ull);
+        for (int t = 0; t < 3; t++) {
+            open_s[t] = op[t];
+            nvalid_s[t] = op[t] >= 0 ? ((a.page_meta[(size_t)row * a.maxp + op[t]] >> 2) & 15) + 1 : kSlots;
+            open_off_s[t] = op[t] >= 0 ? a.page_table[(size_t)row * a.maxp + op[t]] : 0u;
+        }
+    }
+    // this wave's codewords, loaded before they are needed
+    const int g_w = tid / 64, j_w = tid % 64;
+    float4 w[kCodes8 / 64 + 1][2];
+    {
+        const float *cb8 = a.cb8 + ((size_t)h * G + g_w) * kCodes8 * 8;
+        const float *cb4 = a.cb4 + ((size_t)h * G + g_w) * kCodes4 * 8;
+#pragma unroll
+        for (int i = 0; i < kCodes8 / 64; i++) {
+            w[i][0] = *reinterpret_cast<const float4 *>(cb8 + (j_w + 64 * i) * 8);
+            w[i][1] = *reinterpret_cast<const float4 *>(cb8 + (j_w + 64 * i) * 8 + 4);
+        }
+        w[kCodes8 / 64][0] = *reinterpret_cast<const float4 *>(cb4 + (j_w & 15) * 8);
+        w[kCodes8 / 64][1] = *reinterpret_cast<const float4 *>(cb4 + (j_w & 15) * 8 + 4);
+    }
+
+    // the key is staged in LDS by D threads; one thread then sums its
+    // squares in order (the encode's sequential norm)
+    if (tid < D)
+        xk[tid] = f16_bits_to_f32(k[tid]);
+    __syncthreads();
     if (tid == 0) {
         double ss = 0.0;
         for (int j = 0; j < D; j++) {
-            const double x = (double)f16_bits_to_f32(k[j]);
+            const double x = (double)xk[j];
             ss = ss + x * x;
         }
         rn = sqrt(ss);
     }
     __syncthreads();
     if (tid < D) {
-        const double x = (double)f16_bits_to_f32(k[tid]);
+        const double x = (double)xk[tid];
         u[tid] = rn > 0.0 ? x / rn : 0.0;
     }
     __syncthreads();
-    if (tid < G * 16) {
-        const int g = tid / 16, j16 = tid % 16;
+    {
+        // wave g scores group g: lane j the 8-bit codewords j + 64 i (all
+        // loads issued together) and, for j < 16, 4-bit codeword j; then a
+        // (distance, index) minimum over the wave
+        const int g = g_w, j = j_w;
         double uu[8];
 #pragma unroll
-        for (int j = 0; j < 8; j++)
-            uu[j] = u[8 * g + j];
-        const float *cb8 = a.cb8 + ((size_t)h * G + g) * kCodes8 * 8;
-        double bd = INFINITY;
-        int bc = 0;
-        for (int i = 0; i < kCodes8 / 16; i++) { // ascending codewords: strict < keeps the lowest
-            const int c = j16 + 16 * i;
-            const float4 w0 = *reinterpret_cast<const float4 *>(cb8 + c * 8);
-            const float4 w1 = *reinterpret_cast<const float4 *>(cb8 + c * 8 + 4);
-            const float w[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+        for (int q = 0; q < 8; q++)
+            uu[q] = u[8 * g + q];
+        double dist[kCodes8 / 64 + 1];
+#pragma unroll
+        for (int i = 0; i <= kCodes8 / 64; i++) {
+            const float ww[8] = {w[i][0].x, w[i][0].y, w[i][0].z, w[i][0].w,
+                                 w[i][1].x, w[i][1].y, w[i][1].z, w[i][1].w};
             double d = 0.0;
 #pragma unroll
-            for (int j = 0; j < 8; j++) {
-                const double df = uu[j] - (double)w[j];
+            for (int q = 0; q < 8; q++) {
+                const double df = uu[q] - (double)ww[q];
                 d = d + df * df;
             }
-            if (d < bd) {
-                bd = d;
-                bc = c;
+            dist[i] = d;
+        }
+        // ascending codewords: strict < keeps the lowest index
+        double bd = dist[0];
+        int bc = j;
+#pragma unroll
+        for (int i = 1; i < kCodes8 / 64; i++)
+            if (dist[i] < bd) {
+                bd = dist[i];
+                bc = j + 64 * i;
             }
-        }
-        const float *cb4 = a.cb4 + (((size_t)h * G + g) * kCodes4 + j16) * 8;
-        const float4 w0 = *reinterpret_cast<const float4 *>(cb4);
-        const float4 w1 = *reinterpret_cast<const float4 *>(cb4 + 4);
-        const float w[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
-        double b4 = 0.0;
+        double b4 = j < kCodes4 ? dist[kCodes8 / 64] : INFINITY;
+        int c4 = j < kCodes4 ? j : kCodes4;
 #pragma unroll
-        for (int j = 0; j < 8; j++) {
-            const double df = uu[j] - (double)w[j];
-            b4 = b4 + df * df;
-        }
-        int c4 = j16;
-        // (distance, index) minima over the group's 16 lanes
-#pragma unroll
-        for (int o = 8; o >= 1; o >>= 1) {
+        for (int o = 32; o >= 1; o >>= 1) {
             const double od = __shfl_xor(bd, o, 64);
             const int oc = __shfl_xor(bc, o, 64);
             if (od < bd || (od == bd && oc < bc)) {
@@ -143,7 +178,7 @@ __global__ __launch_bounds__(256) void append_kernel(AppendArgs a)
                 c4 = oc4;
             }
         }
-        if (j16 == 0) {
+        if (j == 0) {
             c8s[g] = bc;
             d8s[g] = bd;
             c4s[g] = c4;
@@ -167,17 +202,16 @@ __global__ __launch_bounds__(256) void append_kernel(AppendArgs a)
         int pi = -1, slot = kSlots, fresh = 0;
         uint32_t off = 0;
         if (tier < 3) {
-            pi = a.open[row * 3 + tier] - 1;
-            if (pi >= 0)
-                slot = ((a.page_meta[(size_t)row * a.maxp + pi] >> 2) & 15) + 1;
+            pi = open_s[tier];
+            slot = nvalid_s[tier];
             if (slot == kSlots) {
-                pi = a.num_pages[row];
+                pi = npages_s;
                 const unsigned long long units = (unsigned long long)(page_bytes(D, tier) / kUnit);
                 if (pi >= a.maxp) {
                     atomicOr(a.status, 1u);
                     tier = 3;
                 } else {
-                    unsigned long long cur = atomicAdd(a.cursor, 0ull);
+                    unsigned long long cur = cur_s; // (possibly stale: the CAS corrects it)
                     bool ok = false;
                     while (cur + units <= a.capacity) {
                         const unsigned long long seen = atomicCAS(a.cursor, cur, cur + units);
@@ -200,7 +234,7 @@ __global__ __launch_bounds__(256) void append_kernel(AppendArgs a)
                     }
                 }
             } else {
-                off = a.page_table[(size_t)row * a.maxp + pi];
+                off = open_off_s[tier];
             }
         }
         tier_s = tier;
@@ -217,21 +251,21 @@ __global__ __launch_bounds__(256) void append_kernel(AppendArgs a)
     uint8_t *page = a.arena + (size_t)off_s * kUnit;
     if (fresh_s) {
         uint4 *p4 = reinterpret_cast<uint4 *>(page);
-        for (int i = tid; i < page_bytes(D, tier) / 16; i += 256)
+        for (int i = tid; i < page_bytes(D, tier) / 16; i += NT)
             p4[i] = make_uint4(0, 0, 0, 0);
         if (a.slot_token != nullptr && tid < kSlots)
             a.slot_token[((size_t)row * a.maxp + pi) * kSlots + tid] = -1;
     }
     __syncthreads();
     if (tier == 0) {
-        for (int d = 2 * tid; d < D; d += 512) {
+        for (int d = 2 * tid; d < D; d += 2 * NT) {
             *reinterpret_cast<uint32_t *>(page + row_off(slot, d)) = *reinterpret_cast<const uint32_t *>(k + d);
             const uint32_t vv = *reinterpret_cast<const uint32_t *>(v + d);
             *reinterpret_cast<uint16_t *>(page + 32 * D + col_off(slot, d)) = (uint16_t)(vv & 0xffff);
             *reinterpret_cast<uint16_t *>(page + 32 * D + col_off(slot, d + 1)) = (uint16_t)(vv >> 16);
         }
     } else if (tier == 1) {
-        for (int d = tid; d < D; d += 256)
+        for (int d = tid; d < D; d += NT)
             *reinterpret_cast<uint16_t *>(page + col_off(slot, d)) = v[d];
         if (tid < G)
             page[codes_off(D, 1) + slot * G + tid] = (uint8_t)c8s[tid];
@@ -285,6 +319,7 @@ __global__ __launch_bounds__(256) void retier_demote_kernel(RetierArgs a)
 {
     constexpr int G = D / 8;
     __shared__ double u[kSlots][D];
+    __shared__ float xk[kSlots][D];
     __shared__ double rn[kSlots];
     __shared__ int code[kSlots][G];
     __shared__ uint4 img4[page_bytes(D, 1) / 16];
@@ -308,10 +343,15 @@ __global__ __launch_bounds__(256) void retier_demote_kernel(RetierArgs a)
         return;
     const int nv = nv_s;
     const uint8_t *old = a.arena + (size_t)off_s * kUnit;
+    for (int k = tid; k < nv * D; k += 256) {
+        const int t = k / D, d = k % D;
+        xk[t][d] = f16_bits_to_f32(*reinterpret_cast<const uint16_t *>(old + row_off(t, d)));
+    }
+    __syncthreads();
     if (tid < nv) {
         double ss = 0.0;
         for (int d = 0; d < D; d++) {
-            const double x = (double)f16_bits_to_f32(*reinterpret_cast<const uint16_t *>(old + row_off(tid, d)));
+            const double x = (double)xk[tid][d];
             ss = ss + x * x;
         }
         rn[tid] = sqrt(ss);
@@ -319,7 +359,7 @@ __global__ __launch_bounds__(256) void retier_demote_kernel(RetierArgs a)
     __syncthreads();
     for (int k = tid; k < nv * D; k += 256) {
         const int t = k / D, d = k % D;
-        const double x = (double)f16_bits_to_f32(*reinterpret_cast<const uint16_t *>(old + row_off(t, d)));
+        const double x = (double)xk[t][d];
         u[t][d] = rn[t] > 0.0 ? x / rn[t] : 0.0;
     }
     for (int k = tid; k < page_bytes(D, tier) / 16; k += 256)
@@ -473,9 +513,9 @@ hipError_t launch_append(int D, const AppendArgs &a, int rows, hipStream_t st)
     if (rows == 0)
         return hipSuccess;
     if (D == 128)
-        hipLaunchKernelGGL(append_kernel<128>, dim3(rows), dim3(256), 0, st, a);
+        hipLaunchKernelGGL(append_kernel<128>, dim3(rows), dim3(1024), 0, st, a);
     else if (D == 64)
-        hipLaunchKernelGGL(append_kernel<64>, dim3(rows), dim3(256), 0, st, a);
+        hipLaunchKernelGGL(append_kernel<64>, dim3(rows), dim3(512), 0, st, a);
     else
         return hipErrorInvalidValue;
     return hipGetLastError();

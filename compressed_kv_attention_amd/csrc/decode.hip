@@ -893,16 +893,20 @@ __global__ __launch_bounds__(256) void sym_lut_kernel(DecodeArgs a)
 {
     constexpr int G = D / 8, LUT_FLOATS = G * kLutCodes * NH;
     __shared__ double qn[NH], u[NH][8];
+    __shared__ float xq[NH][D];
     __shared__ double bd[4][NH];
     __shared__ int bc[4][NH];
     __shared__ int cq8[NH], cq4[NH];
     const int row = blockIdx.x, g = blockIdx.y, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int s = row / a.Hkv, hkv = row % a.Hkv;
     const uint16_t *qrow = a.q + ((size_t)s * a.Hq + (size_t)hkv * NH) * D;
+    for (int i = tid; i < NH * D; i += 256)
+        xq[i / D][i % D] = __uint_as_float((uint32_t)qrow[i] << 16);
+    __syncthreads();
     if (tid < NH) {
         double ss = 0.0;
         for (int j = 0; j < D; j++) {
-            const double x = (double)__uint_as_float((uint32_t)qrow[tid * D + j] << 16);
+            const double x = (double)xq[tid][j];
             ss = ss + x * x;
         }
         qn[tid] = sqrt(ss);

@@ -165,3 +165,20 @@ def test_rdr_entry_points_host_errors():
     # code error: nothing to do for no tokens; negative counts refused
     assert L.ada_code_error(C.byref(g), 0, None, None, None, None, None, None, None, None) == ada.OK
     assert L.ada_code_error(C.byref(g), -2, None, None, None, None, None, None, None, None) == ada.EINVAL
+
+
+def test_decode_refuses_a_split_count_whose_tables_overflow_lds():
+    """GQA 8 at D = 128 keeps a 136 KiB LUT in LDS: one split over 8192 pages
+    leaves no room for the page-table entries (refused on the host); the
+    default split count always fits."""
+    L = ada.load()
+    g = ada.Geom(128, 8, 1)
+    maxp = 8192
+    view = ada._CacheView(256, 1 << 20, 256, 256, 256, 256, 0, 1, maxp)
+    ws = ada.decode_workspace_size(g, 1, maxp, 1)
+    fake = C.c_void_p(256)
+    assert L.ada_decode(C.byref(g), C.byref(view), fake, fake, fake, 1.0, fake, None, None, 1,
+                        C.c_void_p(1 << 20), ws, None) == ada.EINVAL
+    ns = ada.decode_default_splits(g, 1, maxp)
+    lut = 16 * 272 * 8 * 4
+    assert lut + -(-maxp // ns) * 8 <= 160 * 1024 and ns <= 1024

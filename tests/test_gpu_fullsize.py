@@ -302,3 +302,26 @@ def test_workload4_ragged64_with_budget_solver():
 
 def test_workload2_budget_solver_60pct():
     _run_solver(2, 0, [0])
+
+
+def test_single_row_gqa8_d128_t128k_lds_bound_splits():
+    """One (sequence, kv-head) row of 131072 tokens with 8 query heads at
+    D = 128: the LUT fills most of LDS, so the default split count is set by
+    the page-table room; every head of the row against the oracle."""
+    from helpers import make_case, oracle_cache, small_workload
+    cfg = small_workload(D=128, Hq=8, Hkv=1, S=1, T=131072, mix=(1000, 5000, 8000), seed=300,
+                         samples=4096, iters=4)
+    case = make_case(cfg)
+    flush("[gqa8 t128k] oracle encode + pack")
+    hc, _ = oracle_cache(case, slot_tokens=False)
+    geom = ada.Geom(128, 8, 1)
+    from gpu_util import upload_cache, to_dev
+    dc = upload_cache(hc, geom)
+    ns = ada.decode_default_splits(geom, 1, hc.maxp)
+    flush(f"[gqa8 t128k] {int(hc.num_pages[0])} pages, {ns} splits")
+    out = torch.full((1, 8, 128), float("nan"), device="cuda")
+    lse = torch.full((1, 8), float("nan"), device="cuda")
+    ada.decode(geom, dc, to_dev(case["cb8"]), to_dev(case["cb4"]), to_dev(case["q"]), cfg.sigma, out, lse)
+    torch.cuda.synchronize()
+    ref = oracle.decode(hc, case["cb8"], case["cb4"], case["q"], cfg.sigma, nthreads=NTHREADS)
+    _check_outputs("gqa8 t128k", out, lse, ref, [0])
