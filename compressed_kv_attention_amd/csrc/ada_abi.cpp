@@ -363,9 +363,8 @@ ada_status ada_encode(const ada_geom *geom, int64_t n_tokens, const uint16_t *ke
         return ADA_OK;
     if (!keys || !cb8 || !cb4 || !radius || !codes8 || !codes4)
         return ADA_EINVAL;
-    if ((reinterpret_cast<uintptr_t>(keys) & 15) || (reinterpret_cast<uintptr_t>(codes8) & 1))
-        return ADA_EINVAL;
-    if ((n_tokens + 255) / 256 > INT32_MAX)
+    if ((reinterpret_cast<uintptr_t>(keys) & 15) || (reinterpret_cast<uintptr_t>(cb8) & 15) ||
+        (reinterpret_cast<uintptr_t>(cb4) & 15))
         return ADA_EINVAL;
     return launch_encode(geom->head_dim, geom->num_kv_heads, n_tokens, keys, cb8, cb4, radius, codes8,
                          codes4, as_stream(stream)) == hipSuccess

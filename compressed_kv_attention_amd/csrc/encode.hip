@@ -6,16 +6,25 @@
 // section 2.3 (dense keys are mapped to codes before tiering).  The angle
 // code is one codebook index per group of 8 direction coordinates.
 //
-// Precision: the norm, the direction and every candidate distance are
-// evaluated in double, in a fixed order with no fused multiply-add, so the
-// result is the exact argmin of the defined distances (ties -> lowest index).
-// The norm is summed sequentially over the D coordinates.
+// Definition kept exactly: the norm is summed in double, sequentially over
+// the D coordinates, with no fused multiply-add; the direction is u = k / r
+// in double (u = 0 for a zero key); the code is the argmin, lowest index on
+// ties, of the double distance sum_j (u_j - c_j)^2 summed in order.
 //
-// Grid: x = blocks of 256 tokens, y = (kv-head, pair of groups).  The block
-// stages the two groups' codebooks (2 x 272 codewords) in LDS; every thread
-// takes one token, so all lanes read the same codeword at a time (LDS
-// broadcast).  The thread writes both groups' 8-bit codes and the byte that
-// packs their two 4-bit codes; pair 0 also writes the radius.
+// The search is a dense contraction: for a tile of 16 tokens and 16
+// codewords the matrix cores form |c|^2 - 2 u.c in binary32 (three chained
+// 16x16x4 MFMAs: two over the 8 coordinates, one adding |c|^2), so the
+// codebook stays in registers as MFMA operands and the vector ALU only keeps
+// each token's best and second-best score.  A binary32 score is a filter:
+// where its best two are too close to be ordered for certain (see
+// kFilterRel), the wave rescans that token's codebook in double, so the codes
+// are still the exact double argmin.
+//
+// Grid: x = blocks of 64-token chunks (grid-stride), y = (kv-head, quarter
+// of the groups).  A block has one wave per group of its quarter (4 waves).
+// Per chunk it stages the 64 keys in LDS, sums the norms (one thread per
+// token), then every wave scores its group for the 4 tiles of 16 tokens and
+// leaves the codes in LDS for byte stores.
 #include "ada_internal.h"
 #include "numfmt.h"
 
@@ -24,93 +33,399 @@ namespace {
 
 #pragma clang fp contract(off)
 
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kChunk = 64;          // tokens per chunk
+constexpr float kCodeMax = 0x1p20f; // larger (or non-finite) codebooks skip the filter
+
+// Filter bound.  Let n = |u|^2 over the group, d the distance of codeword c
+// and s = fl(n' + |c|^2 - 2 u.c) the matrix-core score, where n' (a little
+// above n, see below) makes every score positive; s - n' estimates d - n.
+// With T = n' + |c|^2 + 2 sum_j |u_j c_j| (at most 7 (n + d), since |c| <= |u|
+// + sqrt(d)): rounding u to binary32 (through a double reciprocal of a norm
+// within 2^-45 of r) moves s by at most 3 2^-24 T; the binary32 |c|^2 by at most 2^-22 T; the
+// three MFMAs -- twelve products and twelve additions, each assumed within
+// one ulp (2^-23 relative) whatever the matrix core's order and rounding --
+// by at most 13 2^-23 T.  So |s - n' - (d - n)| <= 2^-16 (n + d).  The
+// tracked scores also carry a codeword index in their low 6 mantissa bits,
+// which moves them by at most 2^-17 s.  Together eps = 1.5 2^-16, and
+// codeword c is strictly farther in double than the best-scored one whenever
+// s_c - s_1 > eps (2 n + s_c + s_1); that holds for every c once the gap to
+// the second-best score s_2 exceeds eps (2 n + s_1 + s_2).  The test below
+// asks for 2^-14 (2 n + s_1 + s_2), over 2.6 times that, plus a tiny
+// absolute term for flushed subnormals (codewords are at most 2^20 in
+// magnitude on this path).
+constexpr float kFilterRel = 0x1p-14f;
+constexpr float kFilterAbs = 0x1p-90f;
+
+// Lowest codeword index of the smallest double distance (a NaN distance never
+// wins; all NaN or infinite -> 0): the defining scan, shared by the wave.
+// u is the group's direction slice in double (the same in every lane).
+template <int K>
+__device__ __forceinline__ int exact_nearest(const double (&u)[8], const float *cbg, int lane)
+{
+    constexpr int PER = (K + 63) / 64;
+    float4 cw[PER][2];
+#pragma unroll
+    for (int i = 0; i < PER; i++) { // (all loads first: one memory latency)
+        const int c = lane + 64 * i < K ? lane + 64 * i : K - 1;
+        cw[i][0] = *reinterpret_cast<const float4 *>(cbg + c * 8);
+        cw[i][1] = *reinterpret_cast<const float4 *>(cbg + c * 8 + 4);
+    }
+    double bd = INFINITY;
+    int bi = 0;
+#pragma unroll
+    for (int i = 0; i < PER; i++) {
+        const float cf[8] = {cw[i][0].x, cw[i][0].y, cw[i][0].z, cw[i][0].w,
+                             cw[i][1].x, cw[i][1].y, cw[i][1].z, cw[i][1].w};
+        double d = 0.0;
+#pragma unroll
+        for (int q = 0; q < 8; q++) {
+            const double df = u[q] - (double)cf[q];
+            d = d + df * df;
+        }
+        if (lane + 64 * i < K && d < bd) {
+            bd = d;
+            bi = lane + 64 * i;
+        }
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+        const double od = __shfl_xor(bd, off);
+        const int oi = __shfl_xor(bi, off);
+        if (od < bd || (od == bd && oi < bi)) {
+            bd = od;
+            bi = oi;
+        }
+    }
+    return bi;
+}
+
+// x of lane (l & ~16) and of lane (l | 16), in that order: the lanes of one
+// token column in rows 2r and 2r + 1 of the tile.
+__device__ __forceinline__ void pair16(uint32_t x, uint32_t &lo, uint32_t &hi)
+{
+    const auto r = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+    lo = r[0];
+    hi = r[1];
+}
+
+// x of lane (l & ~32) and of lane (l | 32).
+__device__ __forceinline__ void pair32(uint32_t x, uint32_t &lo, uint32_t &hi)
+{
+    const auto r = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+    lo = r[0];
+    hi = r[1];
+}
+
+// Sum over the four lanes of a token column (every lane gets the same value:
+// each pairwise sum has the same operands in the same order).
+__device__ __forceinline__ float column_sum(float x)
+{
+    uint32_t a, b;
+    pair16(__float_as_uint(x), a, b);
+    x = __uint_as_float(a) + __uint_as_float(b);
+    pair32(__float_as_uint(x), a, b);
+    return __uint_as_float(a) + __uint_as_float(b);
+}
+
+__device__ __forceinline__ double column_sum(double x)
+{
+#pragma unroll
+    for (int step = 0; step < 2; step++) {
+        const uint64_t v = (uint64_t)__double_as_longlong(x);
+        uint32_t al, bl, ah, bh;
+        if (step == 0) {
+            pair16((uint32_t)v, al, bl);
+            pair16((uint32_t)(v >> 32), ah, bh);
+        } else {
+            pair32((uint32_t)v, al, bl);
+            pair32((uint32_t)(v >> 32), ah, bh);
+        }
+        x = __longlong_as_double((long long)(((uint64_t)ah << 32) | al)) +
+            __longlong_as_double((long long)(((uint64_t)bh << 32) | bl));
+    }
+    return x;
+}
+
+// The defining norm of a staged key: squares summed in order, in double.
 template <int D>
-__global__ __launch_bounds__(256) void encode_kernel(int Hkv, int64_t n_tokens, const uint16_t *keys,
-                                                     const float *cb8, const float *cb4,
-                                                     uint16_t *radius, uint8_t *codes8,
-                                                     uint8_t *codes4)
+__device__ __forceinline__ double exact_norm(const uint32_t *row)
+{
+    double ss = 0.0;
+    for (int c = 0; c < D / 2; c++) {
+        const uint32_t kw = row[c];
+        const double lo = (double)f16_bits_to_f32((uint16_t)(kw & 0xffff));
+        const double hi = (double)f16_bits_to_f32((uint16_t)(kw >> 16));
+        ss = ss + lo * lo;
+        ss = ss + hi * hi;
+    }
+    return sqrt(ss);
+}
+
+// A lane's running best two packed scores (value bits | 6-bit slot): keys
+// are positive floats, so float and integer order agree.
+struct Best {
+    uint32_t k1;
+    float k2;
+};
+
+__device__ __forceinline__ void best_init(Best &s)
+{
+    s.k1 = 0x7f7fffffu;
+    s.k2 = __uint_as_float(0x7f7fffffu);
+}
+
+__device__ __forceinline__ void best_add(Best &s, float score, int slot)
+{
+    const uint32_t k = (__float_as_uint(score) & ~63u) | (uint32_t)slot;
+    s.k2 = __builtin_amdgcn_fmed3f(__uint_as_float(s.k1), s.k2, __uint_as_float(k));
+    s.k1 = min(s.k1, k);
+}
+
+// Best value, its codeword and the second-best value over a token column.
+// Equal best values leave v2 == v1, which the filter rejects.
+struct Column {
+    float v1, v2;
+    int i1;
+};
+
+__device__ __forceinline__ Column best_column(const Best &s, int cw)
+{
+    Column c{__uint_as_float(s.k1 & ~63u), __uint_as_float(__float_as_uint(s.k2) & ~63u), cw};
+#pragma unroll
+    for (int step = 0; step < 2; step++) {
+        uint32_t a1, b1, a2, b2, ai, bi;
+        if (step == 0) {
+            pair16(__float_as_uint(c.v1), a1, b1);
+            pair16(__float_as_uint(c.v2), a2, b2);
+            pair16((uint32_t)c.i1, ai, bi);
+        } else {
+            pair32(__float_as_uint(c.v1), a1, b1);
+            pair32(__float_as_uint(c.v2), a2, b2);
+            pair32((uint32_t)c.i1, ai, bi);
+        }
+        const float x1 = __uint_as_float(a1), y1 = __uint_as_float(b1);
+        c.v2 = __builtin_amdgcn_fmed3f(x1, y1, fminf(__uint_as_float(a2), __uint_as_float(b2)));
+        const bool lt = y1 < x1;
+        c.i1 = lt ? (int)bi : (int)ai;
+        c.v1 = lt ? y1 : x1;
+    }
+    return c;
+}
+
+// The defining codes of group g of one staged key row of norm r (the
+// defining one): direction, then the double scans; which: 1 = the 8-bit
+// code, 2 = the 4-bit code.  Returns code8 | code4 << 8.  Called by the
+// whole wave.
+__device__ __attribute__((noinline)) uint32_t rescan(const uint32_t *row, double r, int g,
+                                                     const float *c8g, const float *c4g, int lane,
+                                                     int which)
+{
+    const uint16_t *kg = reinterpret_cast<const uint16_t *>(row) + 8 * g;
+    double u[8];
+#pragma unroll
+    for (int p = 0; p < 8; p++)
+        u[p] = r > 0.0 ? (double)f16_bits_to_f32(kg[p]) / r : 0.0;
+    uint32_t e = 0;
+    if (which & 1)
+        e |= (uint32_t)exact_nearest<kCodes8>(u, c8g, lane);
+    if (which & 2)
+        e |= (uint32_t)exact_nearest<kCodes4>(u, c4g, lane) << 8;
+    return e;
+}
+
+template <int D>
+__global__ __launch_bounds__(256, 4) void encode_kernel(int Hkv, int64_t n_tokens, int64_t n_chunks,
+                                                        const uint16_t *__restrict__ keys,
+                                                        const float *__restrict__ cb8,
+                                                        const float *__restrict__ cb4,
+                                                        uint16_t *__restrict__ radius,
+                                                        uint8_t *__restrict__ codes8,
+                                                        uint8_t *__restrict__ codes4)
 {
     constexpr int G = D / 8;
-    __shared__ float c8[2][kCodes8][8];
-    __shared__ float c4[2][kCodes4][8];
-    const int h = blockIdx.y / (G / 2), gp = blockIdx.y % (G / 2);
-    for (int i = threadIdx.x; i < 2 * kCodes8 * 8; i += 256) {
-        const int g = i / (kCodes8 * 8), rest = i % (kCodes8 * 8);
-        (&c8[g][0][0])[rest] = cb8[(((size_t)h * G + 2 * gp + g) * kCodes8) * 8 + rest];
-    }
-    for (int i = threadIdx.x; i < 2 * kCodes4 * 8; i += 256) {
-        const int g = i / (kCodes4 * 8), rest = i % (kCodes4 * 8);
-        (&c4[g][0][0])[rest] = cb4[(((size_t)h * G + 2 * gp + g) * kCodes4) * 8 + rest];
+    constexpr int RW = D / 2 + 1; // LDS row stride in 32-bit words (odd: conflict-free norms)
+    // the block's four codebooks while the operands are loaded, then a
+    // chunk's keys
+    constexpr int kCbWords = 4 * (kCodes8 + kCodes4) * 8;
+    constexpr int kLdsWords = kCbWords > kChunk * RW ? kCbWords : kChunk * RW;
+    __shared__ __align__(16) uint32_t lds[kLdsWords];
+    uint32_t *xk = lds;
+    __shared__ double xri[kChunk]; // 1 / (norm in a fast order)
+    __shared__ double xr[kChunk];  // the defining norm
+    __shared__ uint8_t s8[kChunk][4];
+    __shared__ uint8_t s4[kChunk][4];
+    const int h = blockIdx.y / (G / 4), gq = blockIdx.y % (G / 4);
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = 4 * gq + w;
+    const int col = lane & 15, q = lane >> 4;
+    const float *c8g = cb8 + ((size_t)h * G + g) * kCodes8 * 8;
+    const float *c4g = cb4 + ((size_t)h * G + g) * kCodes4 * 8;
+    const uint16_t *xk16 = reinterpret_cast<const uint16_t *>(xk);
+
+    // The four groups' codebooks are contiguous: stage them with 16-byte loads.
+    {
+        const uint4 *src8 = reinterpret_cast<const uint4 *>(cb8 + ((size_t)h * G + 4 * gq) * kCodes8 * 8);
+        const uint4 *src4 = reinterpret_cast<const uint4 *>(cb4 + ((size_t)h * G + 4 * gq) * kCodes4 * 8);
+        uint4 *dst = reinterpret_cast<uint4 *>(lds);
+        constexpr int N8 = 4 * kCodes8 * 2, N4 = 4 * kCodes4 * 2;
+        for (int i = tid; i < N8 + N4; i += 256)
+            dst[i] = i < N8 ? src8[i] : src4[i - N8];
     }
     __syncthreads();
-    const int64_t n = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (n >= n_tokens)
-        return;
-    const size_t e = (size_t)n * Hkv + h;
-    const uint16_t *k = keys + e * D;
-
-    double ss = 0.0;
-    for (int c = 0; c < D / 8; c++) {
-        const uint4 w = *reinterpret_cast<const uint4 *>(k + 8 * c);
-        const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+    // A operands (rows = codewords): lane holds coordinates q and 4 + q of
+    // codeword 16 t + col of tile t (tile 16 = the 4-bit codebook); the third
+    // operand holds |c|^2 in the q == 0 lanes.
+    float a0[17], a1[17], an[17];
+    {
+        const float *s8w = reinterpret_cast<const float *>(lds) + w * kCodes8 * 8;
+        const float *s4w = reinterpret_cast<const float *>(lds) + 4 * kCodes8 * 8 + w * kCodes4 * 8;
 #pragma unroll
-        for (int q = 0; q < 4; q++) {
-            const double lo = (double)f16_bits_to_f32((uint16_t)(ws[q] & 0xffff));
-            const double hi = (double)f16_bits_to_f32((uint16_t)(ws[q] >> 16));
-            ss = ss + lo * lo;
-            ss = ss + hi * hi;
+        for (int t = 0; t < 17; t++) {
+            const float *cw = t < 16 ? s8w + (16 * t + col) * 8 : s4w + col * 8;
+            a0[t] = cw[q];
+            a1[t] = cw[4 + q];
         }
     }
-    const double r = sqrt(ss);
-    if (gp == 0)
-        radius[e] = f64_to_f16_sat(r);
-
-    int best8[2], best4[2];
+    bool fin = true;
 #pragma unroll
-    for (int g = 0; g < 2; g++) {
-        double u[8];
-        const uint4 w = *reinterpret_cast<const uint4 *>(k + 8 * (2 * gp + g));
-        const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
-#pragma unroll
-        for (int q = 0; q < 4; q++) {
-            const double lo = (double)f16_bits_to_f32((uint16_t)(ws[q] & 0xffff));
-            const double hi = (double)f16_bits_to_f32((uint16_t)(ws[q] >> 16));
-            u[2 * q] = r > 0.0 ? lo / r : 0.0;
-            u[2 * q + 1] = r > 0.0 ? hi / r : 0.0;
-        }
-        int b = 0;
-        double bd = INFINITY;
-        for (int c = 0; c < kCodes8; c++) {
-            double d = 0.0;
-#pragma unroll
-            for (int q = 0; q < 8; q++) {
-                const double df = u[q] - (double)c8[g][c][q];
-                d = d + df * df;
-            }
-            if (d < bd) {
-                bd = d;
-                b = c;
-            }
-        }
-        best8[g] = b;
-        b = 0;
-        bd = INFINITY;
-        for (int c = 0; c < kCodes4; c++) {
-            double d = 0.0;
-#pragma unroll
-            for (int q = 0; q < 8; q++) {
-                const double df = u[q] - (double)c4[g][c][q];
-                d = d + df * df;
-            }
-            if (d < bd) {
-                bd = d;
-                b = c;
-            }
-        }
-        best4[g] = b;
+    for (int t = 0; t < 17; t++) {
+        fin &= fabsf(a0[t]) <= kCodeMax;
+        fin &= fabsf(a1[t]) <= kCodeMax;
+        const float p = column_sum(fmaf(a1[t], a1[t], a0[t] * a0[t]));
+        an[t] = q == 0 ? p : 0.f;
     }
-    *reinterpret_cast<uint16_t *>(codes8 + e * G + 2 * gp) = (uint16_t)(best8[0] | (best8[1] << 8));
-    codes4[e * (G / 2) + gp] = (uint8_t)(best4[0] | (best4[1] << 4));
+    const bool filter = __ballot(!fin) == 0; // (wave-uniform)
+    const float bn = q == 0 ? 1.f : 0.f;
+    __syncthreads(); // (the keys reuse the codebooks' LDS)
+
+    for (int64_t chunk = blockIdx.x; chunk < n_chunks; chunk += gridDim.x) {
+        const int64_t n0 = chunk * kChunk;
+        // stage the chunk's keys (zeros past the end)
+        for (int i = tid; i < kChunk * (D / 8); i += 256) {
+            const int tk = i / (D / 8), c = i % (D / 8);
+            uint4 kw = make_uint4(0, 0, 0, 0);
+            if (n0 + tk < n_tokens)
+                kw = *reinterpret_cast<const uint4 *>(keys + ((size_t)(n0 + tk) * Hkv + h) * D + 8 * c);
+            uint32_t *dst = xk + tk * RW + 4 * c;
+            dst[0] = kw.x;
+            dst[1] = kw.y;
+            dst[2] = kw.z;
+            dst[3] = kw.w;
+        }
+        __syncthreads();
+        // Norms for the filter, wave w taking tokens 16 w + col: the four
+        // lanes of a column each sum a quarter of the squares (exact in
+        // double), then the quarters are added.  This order differs from the
+        // defining one by at most 2^-45 r, which the filter's bound absorbs.
+        {
+            const int tk = 16 * w + col;
+            const uint32_t *row = xk + tk * RW + (D / 8) * q;
+            double part = 0.0;
+#pragma unroll
+            for (int c = 0; c < D / 8; c++) {
+                const uint32_t kw = row[c];
+                const double lo = (double)f16_bits_to_f32((uint16_t)(kw & 0xffff));
+                const double hi = (double)f16_bits_to_f32((uint16_t)(kw >> 16));
+                part = part + lo * lo;
+                part = part + hi * hi;
+            }
+            const double r = sqrt(column_sum(part));
+            if (q == 0)
+                xri[tk] = r > 0.0 ? 1.0 / r : 0.0;
+        }
+        __syncthreads();
+        // The defining norms (a serial sum per token) for the radius and the
+        // rescans: the last wave, before its tiles; the others go on.
+        if (w == 3) {
+            const double r = exact_norm<D>(xk + lane * RW);
+            xr[lane] = r;
+            if (gq == 0 && n0 + lane < n_tokens)
+                radius[(size_t)(n0 + lane) * Hkv + h] = f64_to_f16_sat(r);
+        }
+
+        uint32_t redo[kChunk / 16]; // per tile: tokens to rescan (8-bit | 4-bit << 16)
+#pragma unroll
+        for (int tt = 0; tt < kChunk / 16; tt++) {
+            const int tk = 16 * tt + col; // this lane's token (B column)
+            const uint16_t *kg = xk16 + tk * (2 * RW) + 8 * g;
+            int code8 = 0, code4 = 0;
+            redo[tt] = 0xffffffffu; // (a codebook outside the filter's range: all)
+            if (filter) {
+                const double ri = xri[tk];
+                const float ua = (float)((double)f16_bits_to_f32(kg[q]) * ri);
+                const float ub = (float)((double)f16_bits_to_f32(kg[4 + q]) * ri);
+                const float b0 = -2.f * ua, b1 = -2.f * ub;
+                const float n32 = column_sum(fmaf(ub, ub, ua * ua));
+                const float np = fmaf(n32, 1.f + 0x1p-8f, 0x1p-100f);
+                Best s8b, s4b;
+                best_init(s8b);
+                best_init(s4b);
+#pragma unroll
+                for (int t = 0; t < 17; t++) {
+                    f32x4 acc = {np, np, np, np};
+                    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a0[t], b0, acc, 0, 0, 0);
+                    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a1[t], b1, acc, 0, 0, 0);
+                    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(an[t], bn, acc, 0, 0, 0);
+                    // element v: codeword (16 t +) 4 q + v of token tk; its
+                    // slot in the packed score is 4 t + v
+#pragma unroll
+                    for (int v = 0; v < 4; v++) {
+                        if (t < 16)
+                            best_add(s8b, acc[v], 4 * t + v);
+                        else
+                            best_add(s4b, acc[v], v);
+                    }
+                    if (t % 4 == 3)
+                        __builtin_amdgcn_sched_barrier(0);
+                }
+                const int j8 = (int)(s8b.k1 & 63u), j4 = (int)(s4b.k1 & 63u);
+                const Column c8 = best_column(s8b, 16 * (j8 >> 2) + 4 * q + (j8 & 3));
+                const Column c4 = best_column(s4b, 4 * q + j4);
+                const bool ok8 = c8.v2 - c8.v1 > fmaf(kFilterRel, 2.f * n32 + c8.v1 + c8.v2, kFilterAbs);
+                const bool ok4 = c4.v2 - c4.v1 > fmaf(kFilterRel, 2.f * n32 + c4.v1 + c4.v2, kFilterAbs);
+                code8 = c8.i1;
+                code4 = c4.i1;
+                // near ties: rescanned in double after the chunk's tiles
+                redo[tt] = (uint32_t)(__ballot(!ok8) & 0xffffull) | ((uint32_t)(__ballot(!ok4) & 0xffffull) << 16);
+            }
+            if (q == 0) {
+                s8[tk][w] = (uint8_t)code8;
+                s4[tk][w] = (uint8_t)code4;
+            }
+        }
+        __syncthreads(); // (the defining norms are in)
+        // the rescans, one token at a time by the whole wave (out of line:
+        // the filter loop keeps its registers)
+#pragma unroll
+        for (int tt = 0; tt < kChunk / 16; tt++) {
+            uint32_t m = (redo[tt] | (redo[tt] >> 16)) & 0xffffu;
+            while (m) {
+                const int j = __builtin_ctz(m);
+                m &= m - 1;
+                const int tk = 16 * tt + j;
+                const int which = (int)(((redo[tt] >> j) & 1u) | (((redo[tt] >> (16 + j)) & 1u) << 1));
+                const uint32_t e = rescan(xk + tk * RW, xr[tk], g, c8g, c4g, lane, which);
+                if (lane == 0) {
+                    if (which & 1)
+                        s8[tk][w] = (uint8_t)(e & 0xff);
+                    if (which & 2)
+                        s4[tk][w] = (uint8_t)(e >> 8);
+                }
+            }
+        }
+        __syncthreads();
+        {
+            const int tk = tid >> 2, k = tid & 3;
+            if (n0 + tk < n_tokens) {
+                const size_t e = (size_t)(n0 + tk) * Hkv + h;
+                codes8[e * G + 4 * gq + k] = s8[tk][k];
+                if (k < 2)
+                    codes4[e * (G / 2) + 2 * gq + k] = (uint8_t)(s4[tk][2 * k] | (s4[tk][2 * k + 1] << 4));
+            }
+        }
+        __syncthreads();
+    }
 }
 
 } // namespace
@@ -121,13 +436,17 @@ hipError_t launch_encode(int D, int Hkv, int64_t n_tokens, const uint16_t *keys,
 {
     if (n_tokens == 0)
         return hipSuccess;
-    const dim3 grid((unsigned)((n_tokens + 255) / 256), (unsigned)(Hkv * (D / 16)));
+    const int64_t n_chunks = (n_tokens + kChunk - 1) / kChunk;
+    // about four blocks per compute unit; each block walks its chunks
+    const int64_t by = (int64_t)Hkv * (D / 32);
+    const int64_t want = (1024 + by - 1) / by;
+    const dim3 grid((unsigned)(n_chunks < want ? n_chunks : want), (unsigned)by);
     if (D == 128)
-        hipLaunchKernelGGL(encode_kernel<128>, grid, dim3(256), 0, st, Hkv, n_tokens, keys, cb8,
-                           cb4, radius, codes8, codes4);
+        hipLaunchKernelGGL(encode_kernel<128>, grid, dim3(256), 0, st, Hkv, n_tokens, n_chunks, keys,
+                           cb8, cb4, radius, codes8, codes4);
     else if (D == 64)
-        hipLaunchKernelGGL(encode_kernel<64>, grid, dim3(256), 0, st, Hkv, n_tokens, keys, cb8, cb4,
-                           radius, codes8, codes4);
+        hipLaunchKernelGGL(encode_kernel<64>, grid, dim3(256), 0, st, Hkv, n_tokens, n_chunks, keys,
+                           cb8, cb4, radius, codes8, codes4);
     else
         return hipErrorInvalidValue;
     return hipGetLastError();

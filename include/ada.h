@@ -104,12 +104,15 @@ size_t ada_page_bytes(int32_t head_dim, int32_t tier);
  * group takes the index of its nearest codeword (squared Euclidean
  * distance, evaluated in double; lowest index on ties) among the 256
  * codewords of cb8 and, separately, the 16 codewords of cb4.
- *   keys    [n_tokens][Hkv][D] fp16
- *   cb8     [Hkv][G][256][8] f32,  cb4 [Hkv][G][16][8] f32 (one layer)
+ *   keys    [n_tokens][Hkv][D] fp16 (16-byte aligned)
+ *   cb8     [Hkv][G][256][8] f32,  cb4 [Hkv][G][16][8] f32 (one layer;
+ *           both 16-byte aligned)
  *   radius  [n_tokens][Hkv] fp16 out
  *   codes8  [n_tokens][Hkv][G] u8 out
  *   codes4  [n_tokens][Hkv][G/2] u8 out (two 4-bit codes per byte)
- * n_tokens may be 0 (no work).
+ * n_tokens may be 0 (no work).  Misaligned or null pointers -> ADA_EINVAL.
+ * The codes are the exact double-precision argmin (the kernel scores in
+ * binary32 and rescans near ties in double).
  */
 ada_status ada_encode(const ada_geom *geom, int64_t n_tokens, const uint16_t *keys,
                       const float *cb8, const float *cb4, uint16_t *radius, uint8_t *codes8,

@@ -83,6 +83,10 @@ def test_host_argument_errors():
     # encode with no tokens is a no-op; negative counts are refused
     assert L.ada_encode(C.byref(g), 0, None, None, None, None, None, None, None) == ada.OK
     assert L.ada_encode(C.byref(g), -1, None, None, None, None, None, None, None) == ada.EINVAL
+    # keys and both codebooks must be 16-byte aligned (staged with 16-byte loads)
+    p16, p4 = C.c_void_p(256), C.c_void_p(260)
+    for keys, cb8, cb4 in ((p4, p16, p16), (p16, p4, p16), (p16, p16, p4)):
+        assert L.ada_encode(C.byref(g), 1, keys, cb8, cb4, p16, p16, p16, None) == ada.EINVAL
 
 
 def test_pack_host_errors_leave_host_state_untouched():

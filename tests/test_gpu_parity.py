@@ -219,6 +219,30 @@ def test_encode_tiny_and_small():
     _check_encode(cfg, case, "D=128 with zero and extreme keys")
 
 
+def test_encode_near_ties_exact():
+    """Codebooks whose codewords come in pairs -- equal, or one binary32 ulp
+    apart in one coordinate -- make nearly every nearest codeword a near tie
+    that binary32 scores cannot separate; the codes must still equal the
+    double-precision argmin (lowest index on an exact tie) bit for bit."""
+    cfg = small_workload(D=64, Hq=4, Hkv=2, S=2, T=300, seed=61)
+    case = make_case(cfg)
+    for name in ("cb8", "cb4"):
+        cb = case[name].numpy().copy()
+        odd = cb[..., 0::2, :].copy()
+        odd[..., 0::2, 3] = np.nextafter(odd[..., 0::2, 3], np.float32(np.inf))
+        cb[..., 1::2, :] = odd
+        case[name] = torch.from_numpy(cb)
+    flush("[encode] paired codewords")
+    geom = geom_of(cfg)
+    d = _dev_case(case)
+    r, c8, c4 = gpu_encode(geom, d["keys"], d["cb8"], d["cb4"])
+    torch.cuda.synchronize()
+    rr, rc8, rc4 = oracle.encode(case["keys"], case["cb8"], case["cb4"], nthreads=8)
+    assert np.array_equal(u16(r), rr)
+    assert np.array_equal(c8.cpu().numpy(), rc8)
+    assert np.array_equal(c4.cpu().numpy(), rc4)
+
+
 def test_encode_llama_shape_t32k_full():
     cfg = synth.WORKLOADS[2]
     _check_encode(cfg, make_case(cfg), "Llama-3-8B shape T=32768")
