@@ -12,10 +12,10 @@
 // ties, of the double distance sum_j (u_j - c_j)^2 summed in order.
 //
 // The search is a dense contraction: for a tile of 16 tokens and 16
-// codewords the matrix cores form |c|^2 - 2 u.c in binary32 (three chained
-// 16x16x4 MFMAs: two over the 8 coordinates, one adding |c|^2), so the
-// codebook stays in registers as MFMA operands and the vector ALU only keeps
-// each token's best and second-best score.  A binary32 score is a filter:
+// codewords the matrix cores form |c|^2 - 2 u.c in binary32 (two chained
+// 16x16x4 MFMAs over the 8 coordinates, from an accumulator holding |c|^2),
+// so the codebook stays in registers as MFMA operands and the vector ALU
+// only keeps each token's best and second-best score.  A binary32 score is a filter:
 // where its best two are too close to be ordered for certain (see
 // kFilterRel), the wave rescans that token's codebook in double, so the codes
 // are still the exact double argmin.
@@ -39,14 +39,16 @@ constexpr int kChunk = 64;          // tokens per chunk
 constexpr float kCodeMax = 0x1p20f; // larger (or non-finite) codebooks skip the filter
 
 // Filter bound.  Let n = |u|^2 over the group, d the distance of codeword c
-// and s = fl(n' + |c|^2 - 2 u.c) the matrix-core score, where n' (a little
+// and s = fl(n' + |c|^2 - 2 u.c) the matrix-core score (the accumulator
+// starts at n' + |c|^2), where n' (a little
 // above n, see below) makes every score positive; s - n' estimates d - n.
 // With T = n' + |c|^2 + 2 sum_j |u_j c_j| (at most 7 (n + d), since |c| <= |u|
 // + sqrt(d)): rounding u to binary32 (through a double reciprocal of a norm
-// within 2^-45 of r) moves s by at most 3 2^-24 T; the binary32 |c|^2 by at most 2^-22 T; the
-// three MFMAs -- twelve products and twelve additions, each assumed within
-// one ulp (2^-23 relative) whatever the matrix core's order and rounding --
-// by at most 13 2^-23 T.  So |s - n' - (d - n)| <= 2^-16 (n + d).  The
+// within 2^-45 of r) moves s by at most 3 2^-24 T; the binary32 n' + |c|^2
+// by at most 2^-21 T; the two MFMAs -- eight products and eight additions,
+// each assumed within one ulp (2^-23 relative) whatever the matrix core's
+// order and rounding -- by at most 9 2^-23 T.  So |s - n' - (d - n)| <=
+// 2^-16 (n + d).  The
 // tracked scores also carry a codeword index in their low 6 mantissa bits,
 // which moves them by at most 2^-17 s.  Together eps = 1.5 2^-16, and
 // codeword c is strictly farther in double than the best-scored one whenever
@@ -57,6 +59,81 @@ constexpr float kCodeMax = 0x1p20f; // larger (or non-finite) codebooks skip the
 // magnitude on this path).
 constexpr float kFilterRel = 0x1p-14f;
 constexpr float kFilterAbs = 0x1p-90f;
+
+// x of lane (l & ~16) and of lane (l | 16), in that order: the lanes of one
+// token column in rows 2r and 2r + 1 of the tile.
+__device__ __forceinline__ void pair16(uint32_t x, uint32_t &lo, uint32_t &hi)
+{
+    const auto r = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+    lo = r[0];
+    hi = r[1];
+}
+
+// x of lane (l & ~32) and of lane (l | 32).
+__device__ __forceinline__ void pair32(uint32_t x, uint32_t &lo, uint32_t &hi)
+{
+    const auto r = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+    lo = r[0];
+    hi = r[1];
+}
+
+// (distance, index) of lane l ^ x, for the DPP permutes within a row
+template <int CTRL>
+__device__ __forceinline__ void dpp_pair(double d, int i, double &od, int &oi)
+{
+    const uint64_t v = (uint64_t)__double_as_longlong(d);
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_mov_dpp((int)(uint32_t)v, CTRL, 0xf, 0xf, false);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_mov_dpp((int)(uint32_t)(v >> 32), CTRL, 0xf, 0xf, false);
+    od = __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
+    oi = __builtin_amdgcn_mov_dpp(i, CTRL, 0xf, 0xf, false);
+}
+
+__device__ __forceinline__ void lexmin(double &d, int &i, double od, int oi)
+{
+    if (od < d || (od == d && oi < i)) {
+        d = od;
+        i = oi;
+    }
+}
+
+// The two lanes' (distance, index) of a permlane pair, merged.
+template <bool ROW32>
+__device__ __forceinline__ void perm_merge(double &d, int &i)
+{
+    const uint64_t v = (uint64_t)__double_as_longlong(d);
+    uint32_t al, bl, ah, bh, ai, bi;
+    if (ROW32) {
+        pair32((uint32_t)v, al, bl);
+        pair32((uint32_t)(v >> 32), ah, bh);
+        pair32((uint32_t)i, ai, bi);
+    } else {
+        pair16((uint32_t)v, al, bl);
+        pair16((uint32_t)(v >> 32), ah, bh);
+        pair16((uint32_t)i, ai, bi);
+    }
+    d = __longlong_as_double((long long)(((uint64_t)ah << 32) | al));
+    i = (int)ai;
+    lexmin(d, i, __longlong_as_double((long long)(((uint64_t)bh << 32) | bl)), (int)bi);
+}
+
+// Lexicographic (distance, index) minimum over the wave, in every lane:
+// lane pairs xor 1 and xor 2 (quad permutes), the 8-lane and 16-lane
+// mirrors, then rows 2r / 2r + 1 and the two halves.
+__device__ __forceinline__ void wave_argmin(double &d, int &i)
+{
+    double od;
+    int oi;
+    dpp_pair<0xB1>(d, i, od, oi); // quad_perm 1,0,3,2
+    lexmin(d, i, od, oi);
+    dpp_pair<0x4E>(d, i, od, oi); // quad_perm 2,3,0,1
+    lexmin(d, i, od, oi);
+    dpp_pair<0x141>(d, i, od, oi); // row_half_mirror
+    lexmin(d, i, od, oi);
+    dpp_pair<0x140>(d, i, od, oi); // row_mirror
+    lexmin(d, i, od, oi);
+    perm_merge<false>(d, i);
+    perm_merge<true>(d, i);
+}
 
 // Lowest codeword index of the smallest double distance (a NaN distance never
 // wins; all NaN or infinite -> 0): the defining scan, shared by the wave.
@@ -89,33 +166,8 @@ __device__ __forceinline__ int exact_nearest(const double (&u)[8], const float *
             bi = lane + 64 * i;
         }
     }
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-        const double od = __shfl_xor(bd, off);
-        const int oi = __shfl_xor(bi, off);
-        if (od < bd || (od == bd && oi < bi)) {
-            bd = od;
-            bi = oi;
-        }
-    }
+    wave_argmin(bd, bi);
     return bi;
-}
-
-// x of lane (l & ~16) and of lane (l | 16), in that order: the lanes of one
-// token column in rows 2r and 2r + 1 of the tile.
-__device__ __forceinline__ void pair16(uint32_t x, uint32_t &lo, uint32_t &hi)
-{
-    const auto r = __builtin_amdgcn_permlane16_swap(x, x, false, false);
-    lo = r[0];
-    hi = r[1];
-}
-
-// x of lane (l & ~32) and of lane (l | 32).
-__device__ __forceinline__ void pair32(uint32_t x, uint32_t &lo, uint32_t &hi)
-{
-    const auto r = __builtin_amdgcn_permlane32_swap(x, x, false, false);
-    lo = r[0];
-    hi = r[1];
 }
 
 // Sum over the four lanes of a token column (every lane gets the same value:
@@ -214,19 +266,20 @@ __device__ __forceinline__ Column best_column(const Best &s, int cw)
     return c;
 }
 
-// The defining codes of group g of one staged key row of norm r (the
-// defining one): direction, then the double scans; which: 1 = the 8-bit
-// code, 2 = the 4-bit code.  Returns code8 | code4 << 8.  Called by the
-// whole wave.
-__device__ __attribute__((noinline)) uint32_t rescan(const uint32_t *row, double r, int g,
-                                                     const float *c8g, const float *c4g, int lane,
-                                                     int which)
+// The defining codes of one group of a key (its 8 fp16 coordinates in kw)
+// of norm r (the defining one): direction, then the double scans; which:
+// 1 = the 8-bit code, 2 = the 4-bit code.  Returns code8 | code4 << 8.
+// Called by the whole wave.
+__device__ __attribute__((noinline)) uint32_t rescan(uint4 kw, double r, const float *c8g,
+                                                     const float *c4g, int lane, int which)
 {
-    const uint16_t *kg = reinterpret_cast<const uint16_t *>(row) + 8 * g;
+    const uint32_t ws[4] = {kw.x, kw.y, kw.z, kw.w};
     double u[8];
 #pragma unroll
-    for (int p = 0; p < 8; p++)
-        u[p] = r > 0.0 ? (double)f16_bits_to_f32(kg[p]) / r : 0.0;
+    for (int p = 0; p < 8; p++) {
+        const uint16_t hb = (uint16_t)(p & 1 ? ws[p / 2] >> 16 : ws[p / 2] & 0xffff);
+        u[p] = r > 0.0 ? (double)f16_bits_to_f32(hb) / r : 0.0;
+    }
     uint32_t e = 0;
     if (which & 1)
         e |= (uint32_t)exact_nearest<kCodes8>(u, c8g, lane);
@@ -249,13 +302,16 @@ __global__ __launch_bounds__(256, 4) void encode_kernel(int Hkv, int64_t n_token
     // the block's four codebooks while the operands are loaded, then a
     // chunk's keys
     constexpr int kCbWords = 4 * (kCodes8 + kCodes4) * 8;
-    constexpr int kLdsWords = kCbWords > kChunk * RW ? kCbWords : kChunk * RW;
+    constexpr int kKeyNormWords = kChunk * RW + 4 * 17 * 16;
+    constexpr int kLdsWords = kCbWords > kKeyNormWords ? kCbWords : kKeyNormWords;
     __shared__ __align__(16) uint32_t lds[kLdsWords];
     uint32_t *xk = lds;
     __shared__ double xri[kChunk]; // 1 / (norm in a fast order)
     __shared__ double xr[kChunk];  // the defining norm
     __shared__ uint8_t s8[kChunk][4];
     __shared__ uint8_t s4[kChunk][4];
+    __shared__ uint32_t rq[kChunk * 4]; // rescans: token | wave << 8 | which << 12
+    __shared__ int rqn;
     const int h = blockIdx.y / (G / 4), gq = blockIdx.y % (G / 4);
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = 4 * gq + w;
     const int col = lane & 15, q = lane >> 4;
@@ -274,9 +330,10 @@ __global__ __launch_bounds__(256, 4) void encode_kernel(int Hkv, int64_t n_token
     }
     __syncthreads();
     // A operands (rows = codewords): lane holds coordinates q and 4 + q of
-    // codeword 16 t + col of tile t (tile 16 = the 4-bit codebook); the third
-    // operand holds |c|^2 in the q == 0 lanes.
-    float a0[17], a1[17], an[17];
+    // codeword 16 t + col of tile t (tile 16 = the 4-bit codebook).  The
+    // norms |c|^2 go to LDS (after the codebooks, past the keys' rows), where
+    // lane (col, q) reads those of codewords 16 t + 4 q .. + 3.
+    float a0[17], a1[17], nrm[17];
     {
         const float *s8w = reinterpret_cast<const float *>(lds) + w * kCodes8 * 8;
         const float *s4w = reinterpret_cast<const float *>(lds) + 4 * kCodes8 * 8 + w * kCodes4 * 8;
@@ -293,14 +350,22 @@ __global__ __launch_bounds__(256, 4) void encode_kernel(int Hkv, int64_t n_token
         fin &= fabsf(a0[t]) <= kCodeMax;
         fin &= fabsf(a1[t]) <= kCodeMax;
         const float p = column_sum(fmaf(a1[t], a1[t], a0[t] * a0[t]));
-        an[t] = q == 0 ? p : 0.f;
+        nrm[t] = p;
     }
     const bool filter = __ballot(!fin) == 0; // (wave-uniform)
-    const float bn = q == 0 ? 1.f : 0.f;
-    __syncthreads(); // (the keys reuse the codebooks' LDS)
+    __syncthreads(); // (the codebooks have been read)
+    float *norms = reinterpret_cast<float *>(lds + kChunk * RW) + w * 17 * 16;
+    if (q == 0) {
+#pragma unroll
+        for (int t = 0; t < 17; t++)
+            norms[16 * t + col] = nrm[t];
+    }
+    __syncthreads(); // (the keys reuse the rest of the codebooks' LDS)
 
     for (int64_t chunk = blockIdx.x; chunk < n_chunks; chunk += gridDim.x) {
         const int64_t n0 = chunk * kChunk;
+        if (tid == 0)
+            rqn = 0;
         // stage the chunk's keys (zeros past the end)
         for (int i = tid; i < kChunk * (D / 8); i += 256) {
             const int tk = i / (D / 8), c = i % (D / 8);
@@ -344,13 +409,12 @@ __global__ __launch_bounds__(256, 4) void encode_kernel(int Hkv, int64_t n_token
                 radius[(size_t)(n0 + lane) * Hkv + h] = f64_to_f16_sat(r);
         }
 
-        uint32_t redo[kChunk / 16]; // per tile: tokens to rescan (8-bit | 4-bit << 16)
-#pragma unroll
         for (int tt = 0; tt < kChunk / 16; tt++) {
             const int tk = 16 * tt + col; // this lane's token (B column)
             const uint16_t *kg = xk16 + tk * (2 * RW) + 8 * g;
             int code8 = 0, code4 = 0;
-            redo[tt] = 0xffffffffu; // (a codebook outside the filter's range: all)
+            uint32_t redo = 0xffffffffu; // tokens to rescan: 8-bit | 4-bit << 16 (all
+                                         // for a codebook outside the filter's range)
             if (filter) {
                 const double ri = xri[tk];
                 const float ua = (float)((double)f16_bits_to_f32(kg[q]) * ri);
@@ -363,10 +427,10 @@ __global__ __launch_bounds__(256, 4) void encode_kernel(int Hkv, int64_t n_token
                 best_init(s4b);
 #pragma unroll
                 for (int t = 0; t < 17; t++) {
-                    f32x4 acc = {np, np, np, np};
+                    const float4 cn = *reinterpret_cast<const float4 *>(norms + 16 * t + 4 * q);
+                    f32x4 acc = {cn.x + np, cn.y + np, cn.z + np, cn.w + np};
                     acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a0[t], b0, acc, 0, 0, 0);
                     acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a1[t], b1, acc, 0, 0, 0);
-                    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(an[t], bn, acc, 0, 0, 0);
                     // element v: codeword (16 t +) 4 q + v of token tk; its
                     // slot in the packed score is 4 t + v
 #pragma unroll
@@ -387,31 +451,39 @@ __global__ __launch_bounds__(256, 4) void encode_kernel(int Hkv, int64_t n_token
                 code8 = c8.i1;
                 code4 = c4.i1;
                 // near ties: rescanned in double after the chunk's tiles
-                redo[tt] = (uint32_t)(__ballot(!ok8) & 0xffffull) | ((uint32_t)(__ballot(!ok4) & 0xffffull) << 16);
+                redo = (uint32_t)(__ballot(!ok8) & 0xffffull) | ((uint32_t)(__ballot(!ok4) & 0xffffull) << 16);
             }
             if (q == 0) {
                 s8[tk][w] = (uint8_t)code8;
                 s4[tk][w] = (uint8_t)code4;
             }
-        }
-        __syncthreads(); // (the defining norms are in)
-        // the rescans, one token at a time by the whole wave (out of line:
-        // the filter loop keeps its registers)
-#pragma unroll
-        for (int tt = 0; tt < kChunk / 16; tt++) {
-            uint32_t m = (redo[tt] | (redo[tt] >> 16)) & 0xffffu;
+            // queue the near ties for the whole block
+            uint32_t m = (redo | (redo >> 16)) & 0xffffu;
             while (m) {
                 const int j = __builtin_ctz(m);
                 m &= m - 1;
-                const int tk = 16 * tt + j;
-                const int which = (int)(((redo[tt] >> j) & 1u) | (((redo[tt] >> (16 + j)) & 1u) << 1));
-                const uint32_t e = rescan(xk + tk * RW, xr[tk], g, c8g, c4g, lane, which);
-                if (lane == 0) {
-                    if (which & 1)
-                        s8[tk][w] = (uint8_t)(e & 0xff);
-                    if (which & 2)
-                        s4[tk][w] = (uint8_t)(e >> 8);
-                }
+                const uint32_t which = ((redo >> j) & 1u) | (((redo >> (16 + j)) & 1u) << 1);
+                if (lane == 0)
+                    rq[atomicAdd(&rqn, 1)] = (uint32_t)(16 * tt + j) | ((uint32_t)w << 8) | (which << 12);
+            }
+        }
+        __syncthreads(); // (the queue and the defining norms are in)
+        // the rescans, dealt round-robin to the waves, one token-group at a
+        // time by a whole wave (out of line: the filter loop keeps its
+        // registers)
+        for (int i = w; i < rqn; i += 4) {
+            const uint32_t ent = rq[i];
+            const int tk = (int)(ent & 0xff), ew = (int)((ent >> 8) & 3), which = (int)(ent >> 12);
+            const int gg = 4 * gq + ew;
+            const uint32_t *kw = xk + tk * RW + 4 * gg;
+            const uint32_t e = rescan(make_uint4(kw[0], kw[1], kw[2], kw[3]), xr[tk],
+                                      cb8 + ((size_t)h * G + gg) * kCodes8 * 8,
+                                      cb4 + ((size_t)h * G + gg) * kCodes4 * 8, lane, which);
+            if (lane == 0) {
+                if (which & 1)
+                    s8[tk][ew] = (uint8_t)(e & 0xff);
+                if (which & 2)
+                    s4[tk][ew] = (uint8_t)(e >> 8);
             }
         }
         __syncthreads();
