@@ -25,6 +25,7 @@
 //   - allocation if needed, then the slot's fields, metadata, counters.
 #include "ada_internal.h"
 #include "numfmt.h"
+#include "wave_ops.h"
 
 namespace ada {
 namespace {
@@ -163,21 +164,8 @@ __global__ __launch_bounds__(D / 8 * 64) void append_kernel(AppendArgs a)
             }
         double b4 = j < kCodes4 ? dist[kCodes8 / 64] : INFINITY;
         int c4 = j < kCodes4 ? j : kCodes4;
-#pragma unroll
-        for (int o = 32; o >= 1; o >>= 1) {
-            const double od = __shfl_xor(bd, o, 64);
-            const int oc = __shfl_xor(bc, o, 64);
-            if (od < bd || (od == bd && oc < bc)) {
-                bd = od;
-                bc = oc;
-            }
-            const double o4 = __shfl_xor(b4, o, 64);
-            const int oc4 = __shfl_xor(c4, o, 64);
-            if (o4 < b4 || (o4 == b4 && oc4 < c4)) {
-                b4 = o4;
-                c4 = oc4;
-            }
-        }
+        wave_argmin(bd, bc);
+        wave_argmin(b4, c4);
         if (j == 0) {
             c8s[g] = bc;
             d8s[g] = bd;
