@@ -1,6 +1,6 @@
 """Benchmark of the ADA decode step on one MI355X.
 
-    python bench.py [--steps K] [--warmup W] [--workload 2|3] [--splits S]
+    python bench.py [--steps K] [--warmup W] [--workload 2|3|...] [--splits S] [--layers L]
 
 A step is one ada_decode call over the workload: the page stream (code
 tables, logits, online softmax, PV) and the split merge, for every
@@ -10,6 +10,8 @@ steps over rotated copies of the page arena, so repeated steps read HBM and
 not the 256 MiB Infinity Cache.  `value` is context tokens per second of
 whole steps.  The roofline entry is for the dominant kernel, the page
 stream, timed alone with events on its stream.  Prints one JSON line.
+With --layers L above 1 (the 32-layer workload), a step is L back-to-back
+ada_decode calls over L per-layer caches, and `value` counts layer-tokens.
 """
 from __future__ import annotations
 
@@ -412,6 +414,64 @@ def algorithmic_bytes(L, cfg):
     return cache.used_bytes() + cb + pages * 5 + qb + ob
 
 
+def multi_layer(cfg, layers, dev, steps, warmup, eager):
+    """A whole-model attention step: `layers` layers' caches built one after
+    another (per-layer codebooks, keys, values and queries), and one step =
+    back-to-back ada_decode calls over every layer on one stream.  The
+    layers' pages together far exceed the last-level cache, so no copies
+    are rotated."""
+    Ls = []
+    t0 = time.perf_counter()
+    for layer in range(layers):
+        Ls.append(build_layer(cfg, layer, dev))
+        if layer % 8 == 7 or layer == layers - 1:
+            log(f"built layer {layer + 1}/{layers} ({time.perf_counter() - t0:.1f} s)")
+    geom = Ls[0]["geom"]
+    S, Hq, D = cfg.num_seqs, cfg.num_q_heads, cfg.head_dim
+    maxp = max(L["cache"].maxp for L in Ls)
+    out = torch.empty((S, Hq, D), device=dev)
+    lse = torch.empty((S, Hq), device=dev)
+    ws = torch.zeros(ada.decode_workspace_size(geom, S, maxp, 0), dtype=torch.uint8, device=dev)
+
+    def step():
+        for L in Ls:
+            ada.decode(geom, L["cache"], L["cb8"], L["cb4"], L["q"], cfg.sigma, out, lse, ws=ws)
+
+    timer = time_eager if eager else time_graph
+    n, _, ms = timer([step], steps, warmup)
+    tokens = int(Ls[0]["lens"].sum()) * layers
+    used = sum(L["cache"].used_bytes() for L in Ls)
+    alg = sum(algorithmic_bytes(L, cfg) for L in Ls)
+    sfns = [(lambda L=L: ada.decode_stage("stream", geom, L["cache"], L["cb8"], L["cb4"], L["q"],
+                                          cfg.sigma, out, lse, ws=ws)) for L in Ls]
+    k_mean = batch_event_ms(sfns, 2 * layers)
+    sbytes = sum(stream_bytes(L) for L in Ls) / layers
+    achieved = sbytes / (k_mean / 1e3) / 1e9
+    log(f"{layers}-layer step {ms:.3f} ms (graph); page stream {k_mean * 1e3:.2f} us per layer, "
+        f"{achieved:.0f} GB/s")
+    return {
+        "metric": "ADA decode KV tokens/s per step",
+        "value": tokens / (ms / 1e3),
+        "unit": "KV layer-tokens/s",
+        "n_gpus": 1, "steps": n, "warmup": warmup, "ms_per_step": ms,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "fp32", "data": "synthetic",
+        "config": {"workload": cfg.name, "layers": layers, "num_seqs": S,
+                   "seq_len": int(Ls[0]["lens"].max()), "layer_tokens_per_step": tokens,
+                   "num_q_heads": Hq, "num_kv_heads": cfg.num_kv_heads, "head_dim": D,
+                   "tier_cum_bp": list(map(int, synth.tier_mix(cfg)[0])),
+                   "splits": ada.decode_default_splits(geom, S, maxp)},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "kernel": f"decode_main<{D},{Hq // cfg.num_kv_heads},false>",
+                     "kernel_us_mean": k_mean * 1e3, "bytes_per_launch": sbytes},
+        "step_roofline": {"bytes_per_step": alg, "achieved_GBs": alg / (ms / 1e3) / 1e9,
+                          "frac": alg / (ms / 1e3) / 1e9 / HBM_PEAK_GBS},
+        "stored_bytes": used,
+        "stored_fraction_of_dense": used / (tokens * cfg.num_kv_heads * 4 * D),
+    }
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -419,6 +479,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", type=int, default=2)
     ap.add_argument("--splits", type=int, default=0)
+    ap.add_argument("--layers", type=int, default=1,
+                    help="layers per step (each with its own cache); above 1 times the whole "
+                         "multi-layer step only")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--no-append", action="store_true", help="skip the append-path timing")
@@ -440,6 +503,12 @@ def main():
     ada.load()
     cfg = synth.WORKLOADS[args.workload]
     dev = torch.device("cuda:0")
+    if args.layers > 1:
+        if args.layers > cfg.num_layers:
+            print(f"workload {cfg.number} has {cfg.num_layers} layer(s)", file=sys.stderr)
+            sys.exit(2)
+        print(json.dumps(multi_layer(cfg, args.layers, dev, args.steps, args.warmup, args.eager)))
+        return
     if args.copy_probe_mib:
         src = torch.ones(args.copy_probe_mib << 20, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)
