@@ -264,10 +264,11 @@ int32_t default_splits(const ada_geom *g, int32_t S, int32_t maxp)
     const int64_t rows = (int64_t)S * g->num_kv_heads;
     if (rows <= 0)
         return 1;
-    // about one workgroup per compute unit and at least 16 pages per split,
-    // with few enough pages per split that their table entries fit in LDS
-    // beside the group's LUT
-    int64_t n = (256 + rows - 1) / rows;
+    // about one workgroup per compute unit (four splits once the rows alone
+    // fill the chip: ragged rows then still balance) and at least 16 pages
+    // per split, with few enough pages per split that their table entries
+    // fit in LDS beside the group's LUT
+    int64_t n = rows >= 256 ? 4 : (256 + rows - 1) / rows;
     n = std::min<int64_t>(n, std::max<int64_t>(1, maxp / 16));
     n = std::max<int64_t>(n, 1);
     const int NH = g->num_q_heads / g->num_kv_heads;
