@@ -5,8 +5,7 @@ pack into a (permuted) pool, decode with the default split count.  The
 oracle then builds its own cache from the same synthetic inputs for a sample
 of sequences -- a sequence's pages, and so its outputs, depend on no other
 sequence -- and the two are compared:
-  * radii bit-exact and codes bit-exact (a disagreement must be a near-tie,
-    distance gap < 1e-6 in the oracle's double arithmetic);
+  * radii and codes bit-exact;
   * every page of every sampled row bit-exact, with its metadata, page count
     and tier counts (pages are found through each side's own page table);
   * outputs max-abs <= 1e-2 and lse within 1e-3 * max(|lse|, 1).
@@ -52,25 +51,15 @@ def _gpu_encode(geom, keys, cb8, cb4):
 
 
 def _check_codes(label, g_r, g_c8, g_c4, keys_cpu, cb8, cb4):
-    """GPU encode outputs of a token sample against the oracle's."""
+    """GPU encode outputs of a token sample against the oracle's: bit-exact
+    (the kernel's binary32 filter only skips the double scan where its bound
+    proves the winner, so its codes are the defining argmin)."""
     rr, rc8, rc4 = oracle.encode(keys_cpu, cb8, cb4, nthreads=NTHREADS)
     assert np.array_equal(u16(g_r), rr), f"{label}: radius differs"
     g8, g4 = g_c8.cpu().numpy(), g_c4.cpu().numpy()
     bad = np.nonzero((g8 != rc8).any((1, 2)) | (g4 != rc4).any((1, 2)))[0]
-    if len(bad):
-        _, _, _, d8, d4 = oracle.encode(keys_cpu[bad], cb8, cb4, with_dist=True)
-        for i, t in enumerate(bad):
-            for h, g in zip(*np.nonzero(g8[t] != rc8[t])):
-                assert abs(d8[i, h, g, g8[t, h, g]] - d8[i, h, g, rc8[t, h, g]]) < 1e-6
-            lo, hi = g4[t] & 15, g4[t] >> 4
-            rlo, rhi = rc4[t] & 15, rc4[t] >> 4
-            for h, b in zip(*np.nonzero((lo != rlo) | (hi != rhi))):
-                for gg, a, c in ((2 * b, lo[h, b], rlo[h, b]), (2 * b + 1, hi[h, b], rhi[h, b])):
-                    if a != c:
-                        assert abs(d4[i, h, gg, a] - d4[i, h, gg, c]) < 1e-6
-    agree = 1.0 - len(bad) / max(1, len(g8))
-    assert agree >= 0.999
-    flush(f"[{label}] codes of {len(g8)} tokens: {len(bad)} tokens with near-tie differences")
+    assert len(bad) == 0, f"{label}: codes of {len(bad)} tokens differ (first {bad[:5].tolist()})"
+    flush(f"[{label}] codes of {len(g8)} tokens bit-exact")
     return rr, rc8, rc4
 
 
@@ -277,7 +266,7 @@ def _run_solver(number, layer, seqs):
     g_c4 = torch.cat([c4[x] for x in sl])
     flush(f"[{label}] oracle on {len(k_s)} tokens x {H} heads ({NTHREADS} threads)")
     _check_codes(label, g_r, g_c8, g_c4, k_s, cb8, cb4)
-    # downstream of the codes the oracle takes the GPU's (near-ties included)
+    # downstream of the codes the oracle takes the GPU's (equal, as checked)
     gr, gc8, gc4 = u16(g_r), g_c8.cpu().numpy(), g_c4.cpu().numpy()
     re8, re4 = oracle.code_error(k_s, cb8, cb4, gc8, gc4)
     assert np.array_equal(torch.cat([e8[x] for x in sl]).cpu().numpy(), re8), f"{label}: err8"

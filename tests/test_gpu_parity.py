@@ -2,8 +2,9 @@
 same seeded inputs.
 
 Bars (written here, from the method's targets): encode codes and radii
-bit-exact (both sides take the argmin in double; any disagreement must be a
-near-tie, |d_gpu - d_ref| < 1e-6); pages, page tables, metadata and tier
+bit-exact (both sides give the double-precision argmin: the kernel's
+binary32 filter decides only where its error bound proves the winner, and
+rescans in double otherwise); pages, page tables, metadata and tier
 counts bit-exact when both packs get the same encode outputs; logits within
 |d| <= 1e-3 * max(|l|, 1e-2); outputs max-abs <= 1e-2 (fp32 accumulation);
 lse within 1e-3 * max(|lse|, 1)."""
@@ -188,23 +189,7 @@ def _check_encode(cfg, case, label):
     agree8 = (g8 == rc8).mean()
     agree4 = (g4 == rc4).mean()
     flush(f"[encode] {label}: codes8 agree {agree8:.6f}, codes4 agree {agree4:.6f}")
-    if agree8 < 1.0 or agree4 < 1.0:
-        # every disagreement must be a near-tie under the oracle's distances
-        lo4, hi4 = g4 & 15, g4 >> 4
-        rlo4, rhi4 = rc4 & 15, rc4 >> 4
-        gg4 = np.stack([lo4, hi4], -1).reshape(g8.shape)
-        rr4 = np.stack([rlo4, rhi4], -1).reshape(g8.shape)
-        toks = np.unique(np.concatenate([np.nonzero((g8 != rc8).any((1, 2)))[0],
-                                         np.nonzero((gg4 != rr4).any((1, 2)))[0]]))
-        _, _, _, d8, d4 = oracle.encode(case["keys"][toks], case["cb8"], case["cb4"], with_dist=True)
-        for i, t in enumerate(toks):
-            for h, g in zip(*np.nonzero(g8[t] != rc8[t])):
-                gap = abs(d8[i, h, g, g8[t, h, g]] - d8[i, h, g, rc8[t, h, g]])
-                assert gap < 1e-6, f"8-bit code of token {t} head {h} group {g}: gap {gap}"
-            for h, g in zip(*np.nonzero(gg4[t] != rr4[t])):
-                gap = abs(d4[i, h, g, gg4[t, h, g]] - d4[i, h, g, rr4[t, h, g]])
-                assert gap < 1e-6, f"4-bit code of token {t} head {h} group {g}: gap {gap}"
-    assert agree8 >= 0.999 and agree4 >= 0.999
+    assert agree8 == 1.0 and agree4 == 1.0
     return r, c8, c4
 
 

@@ -172,8 +172,7 @@ def test_gpu_encode_error_solve_chain_matches_oracle():
     tiers = torch.empty(r.shape, dtype=torch.uint8, device="cuda")
     ada.rdr_solve(geom, case["cu"], budgets, r, e8, e4, to_dev(case["scores"]), tiers)
     counts = ada.tier_counts(geom, case["cu"], tiers)
-    # (the oracle takes the GPU's codes: encode parity, near-ties included,
-    # is tested on its own)
+    # (the oracle takes the GPU's codes: encode parity is tested on its own)
     rr, rc8, rc4 = u16(r), c8.cpu().numpy(), c4.cpu().numpy()
     re8, re4 = oracle.code_error(case["keys"], case["cb8"], case["cb4"], rc8, rc4)
     assert np.array_equal(e8.cpu().numpy(), re8) and np.array_equal(e4.cpu().numpy(), re4)
