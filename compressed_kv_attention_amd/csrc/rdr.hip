@@ -25,7 +25,7 @@
 // arithmetic that decides the chains is binary32 in a fixed order (IEEE
 // division and square root), so every decision is reproducible.
 //
-// Kernels: code_error (one thread per state), solve_zero (clears the digit
+// Kernels: code_error (64 states per block), solve_zero (clears the digit
 // histograms), solve_pass<P> (P = 0..3; one block per 1024 states of one
 // sequence), solve_assign (writes the tiers), tier_counts (one block per
 // row).
@@ -41,6 +41,12 @@ namespace {
 // err = sum_g || u_g - C_g[code_g] ||^2 with u = k / ||k|| in double: the norm
 // summed sequentially over the D coordinates, each group's distance summed
 // over its 8 coordinates, groups added in order, the total rounded to f32.
+// A block takes 64 consecutive states: their keys are staged in LDS with
+// coalesced 16-byte loads; one wave sums the 64 norms; every thread then
+// scores a quarter of one state's groups; 64 threads add each state's group
+// distances in order.
+constexpr int kErrItems = 64;
+
 template <int D>
 __global__ __launch_bounds__(256) void code_error_kernel(int Hkv, int64_t n_items, const uint16_t *keys,
                                                          const float *cb8, const float *cb4,
@@ -48,54 +54,84 @@ __global__ __launch_bounds__(256) void code_error_kernel(int Hkv, int64_t n_item
                                                          float *err8, float *err4)
 {
     constexpr int G = D / 8;
-    const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (e >= n_items)
-        return;
-    const int h = (int)(e % Hkv);
-    const uint16_t *k = keys + e * D;
-    double ss = 0.0;
-    for (int c = 0; c < G; c++) {
-        const uint4 w = *reinterpret_cast<const uint4 *>(k + 8 * c);
-        const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
-#pragma unroll
-        for (int q = 0; q < 4; q++) {
-            const double lo = (double)f16_bits_to_f32((uint16_t)(ws[q] & 0xffff));
-            const double hi = (double)f16_bits_to_f32((uint16_t)(ws[q] >> 16));
+    constexpr int RW = D / 2 + 1;  // LDS row stride in words (odd: the norm loop is conflict-free)
+    constexpr int GPT = G / 4;     // groups per thread
+    __shared__ uint32_t xk[kErrItems * RW];
+    __shared__ double rn[kErrItems];
+    __shared__ double d8s[kErrItems][G], d4s[kErrItems][G];
+    const int tid = threadIdx.x;
+    const int64_t e0 = (int64_t)blockIdx.x * kErrItems;
+    const int n_here = (int)(n_items - e0 < kErrItems ? n_items - e0 : kErrItems);
+    for (int i = tid; i < kErrItems * (D / 8); i += 256) {
+        const int it = i / (D / 8), c = i % (D / 8);
+        uint4 w = make_uint4(0, 0, 0, 0);
+        if (it < n_here)
+            w = *reinterpret_cast<const uint4 *>(keys + (e0 + it) * D + 8 * c);
+        uint32_t *dst = xk + it * RW + 4 * c;
+        dst[0] = w.x;
+        dst[1] = w.y;
+        dst[2] = w.z;
+        dst[3] = w.w;
+    }
+    __syncthreads();
+    if (tid < kErrItems) {
+        double ss = 0.0;
+        for (int c = 0; c < D / 2; c++) {
+            const uint32_t w = xk[tid * RW + c];
+            const double lo = (double)f16_bits_to_f32((uint16_t)(w & 0xffff));
+            const double hi = (double)f16_bits_to_f32((uint16_t)(w >> 16));
             ss = ss + lo * lo;
             ss = ss + hi * hi;
         }
+        rn[tid] = sqrt(ss);
     }
-    const double r = sqrt(ss);
-    double e8 = 0.0, e4 = 0.0;
-    for (int g = 0; g < G; g++) {
-        const uint4 w = *reinterpret_cast<const uint4 *>(k + 8 * g);
-        const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
-        const int c8 = codes8[e * G + g];
-        const int c4 = (codes4[e * (G / 2) + g / 2] >> (4 * (g & 1))) & 15;
-        const float4 *p8 = reinterpret_cast<const float4 *>(cb8 + (((size_t)h * G + g) * kCodes8 + c8) * 8);
-        const float4 *p4 = reinterpret_cast<const float4 *>(cb4 + (((size_t)h * G + g) * kCodes4 + c4) * 8);
-        const float4 a0 = p8[0], a1 = p8[1], b0 = p4[0], b1 = p4[1];
-        const float w8[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
-        const float w4[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
-        double d8 = 0.0, d4 = 0.0;
+    __syncthreads();
+    {
+        const int it = tid / 4, g0 = (tid % 4) * GPT;
+        if (it < n_here) {
+            const int64_t e = e0 + it;
+            const int h = (int)(e % Hkv);
+            const double r = rn[it];
 #pragma unroll
-        for (int q = 0; q < 4; q++) {
-            const double lo = (double)f16_bits_to_f32((uint16_t)(ws[q] & 0xffff));
-            const double hi = (double)f16_bits_to_f32((uint16_t)(ws[q] >> 16));
-            const double u0 = r > 0.0 ? lo / r : 0.0;
-            const double u1 = r > 0.0 ? hi / r : 0.0;
-            const double x0 = u0 - (double)w8[2 * q], y0 = u0 - (double)w4[2 * q];
-            d8 = d8 + x0 * x0;
-            d4 = d4 + y0 * y0;
-            const double x1 = u1 - (double)w8[2 * q + 1], y1 = u1 - (double)w4[2 * q + 1];
-            d8 = d8 + x1 * x1;
-            d4 = d4 + y1 * y1;
+            for (int gi = 0; gi < GPT; gi++) {
+                const int g = g0 + gi;
+                const int c8 = codes8[e * G + g];
+                const int c4 = (codes4[e * (G / 2) + g / 2] >> (4 * (g & 1))) & 15;
+                const float4 *p8 = reinterpret_cast<const float4 *>(cb8 + (((size_t)h * G + g) * kCodes8 + c8) * 8);
+                const float4 *p4 = reinterpret_cast<const float4 *>(cb4 + (((size_t)h * G + g) * kCodes4 + c4) * 8);
+                const float4 a0 = p8[0], a1 = p8[1], b0 = p4[0], b1 = p4[1];
+                const float w8[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+                const float w4[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
+                double d8 = 0.0, d4 = 0.0;
+#pragma unroll
+                for (int q = 0; q < 4; q++) {
+                    const uint32_t w = xk[it * RW + 4 * g + q];
+                    const double lo = (double)f16_bits_to_f32((uint16_t)(w & 0xffff));
+                    const double hi = (double)f16_bits_to_f32((uint16_t)(w >> 16));
+                    const double u0 = r > 0.0 ? lo / r : 0.0;
+                    const double u1 = r > 0.0 ? hi / r : 0.0;
+                    const double x0 = u0 - (double)w8[2 * q], y0 = u0 - (double)w4[2 * q];
+                    d8 = d8 + x0 * x0;
+                    d4 = d4 + y0 * y0;
+                    const double x1 = u1 - (double)w8[2 * q + 1], y1 = u1 - (double)w4[2 * q + 1];
+                    d8 = d8 + x1 * x1;
+                    d4 = d4 + y1 * y1;
+                }
+                d8s[it][g] = d8;
+                d4s[it][g] = d4;
+            }
         }
-        e8 = e8 + d8;
-        e4 = e4 + d4;
     }
-    err8[e] = (float)e8;
-    err4[e] = (float)e4;
+    __syncthreads();
+    if (tid < n_here) {
+        double e8 = 0.0, e4 = 0.0;
+        for (int g = 0; g < G; g++) {
+            e8 = e8 + d8s[tid][g];
+            e4 = e4 + d4s[tid][g];
+        }
+        err8[e0 + tid] = (float)e8;
+        err4[e0 + tid] = (float)e4;
+    }
 }
 
 // ---- budget solver ------------------------------------------------------------
@@ -336,7 +372,7 @@ hipError_t launch_code_error(int D, int Hkv, int64_t n_tokens, const uint16_t *k
     const int64_t n = n_tokens * Hkv;
     if (n == 0)
         return hipSuccess;
-    const dim3 grid((unsigned)((n + 255) / 256));
+    const dim3 grid((unsigned)((n + kErrItems - 1) / kErrItems));
     if (D == 128)
         hipLaunchKernelGGL(code_error_kernel<128>, grid, dim3(256), 0, st, Hkv, n, keys, cb8, cb4, codes8,
                            codes4, err8, err4);
