@@ -83,6 +83,15 @@ __global__ __launch_bounds__(1024) void pack_rank(PackPlan plan, PackData data)
             prefix[tid] = 0;
             mask[tid] = 0;
         }
+        // the first kKeyRegs keys of each thread stay in registers across
+        // the passes (all of them for rows of up to 4096 tokens)
+        constexpr int kKeyRegs = 4;
+        uint64_t kc[kKeyRegs];
+#pragma unroll
+        for (int v = 0; v < kKeyRegs; v++) {
+            const int i = tid + 1024 * v;
+            kc[v] = i < T ? rank_key(plan, data, ((size_t)sq.begin + i) * plan.Hkv + h, i) : 0ull;
+        }
         __syncthreads();
         for (int pass = 0; pass < 8; pass++) {
             const int shift = 56 - 8 * pass;
@@ -91,8 +100,7 @@ __global__ __launch_bounds__(1024) void pack_rank(PackPlan plan, PackData data)
             __syncthreads();
             const uint64_t p0 = prefix[0], p1 = prefix[1], p2 = prefix[2];
             const uint64_t m0 = mask[0], m1 = mask[1], m2 = mask[2];
-            for (int i = tid; i < T; i += 1024) {
-                const uint64_t K = rank_key(plan, data, ((size_t)sq.begin + i) * plan.Hkv + h, i);
+            auto count = [&](uint64_t K) {
                 const uint32_t dg = (uint32_t)(K >> shift) & 255u;
                 if (has[0] && (K & m0) == p0)
                     atomicAdd(&hist[0][dg], 1u);
@@ -100,19 +108,48 @@ __global__ __launch_bounds__(1024) void pack_rank(PackPlan plan, PackData data)
                     atomicAdd(&hist[1][dg], 1u);
                 if (has[2] && (K & m2) == p2)
                     atomicAdd(&hist[2][dg], 1u);
-            }
+            };
+#pragma unroll
+            for (int v = 0; v < kKeyRegs; v++)
+                if (tid + 1024 * v < T)
+                    count(kc[v]);
+            for (int i = tid + 1024 * kKeyRegs; i < T; i += 1024)
+                count(rank_key(plan, data, ((size_t)sq.begin + i) * plan.Hkv + h, i));
             __syncthreads();
-            if (tid < 3 && has[tid]) {
-                int64_t cum = 0;
-                for (int dg = 255; dg >= 0; dg--) {
-                    const int64_t c = hist[tid][dg];
-                    if (cum + c > krem[tid]) {
-                        prefix[tid] |= (uint64_t)dg << shift;
-                        mask[tid] |= 255ull << shift;
-                        krem[tid] -= cum;
-                        break;
+            // wave k finds select k's digit: lane j holds digits 255 - 4j ..
+            // 252 - 4j (descending), a wave scan gives the counts above each
+            // lane's digits, and the first lane whose running count passes
+            // krem holds the digit
+            if (wave < 3 && has[wave]) {
+                const int k = wave;
+                uint32_t c[4];
+                int sum = 0;
+#pragma unroll
+                for (int v = 0; v < 4; v++) {
+                    c[v] = hist[k][255 - 4 * lane - v];
+                    sum += (int)c[v];
+                }
+                int incl = sum;
+#pragma unroll
+                for (int off = 1; off < 64; off <<= 1) {
+                    const int t = __shfl_up(incl, off, 64);
+                    if (lane >= off)
+                        incl += t;
+                }
+                const int64_t kr = krem[k];
+                const uint64_t hit = __ballot((int64_t)incl > kr);
+                if (hit != 0 && lane == __builtin_ctzll(hit)) {
+                    int64_t cum = incl - sum;
+#pragma unroll
+                    for (int v = 0; v < 4; v++) {
+                        if (cum + (int64_t)c[v] > kr) {
+                            prefix[k] |= (uint64_t)(255 - 4 * lane - v) << shift;
+                            mask[k] |= 255ull << shift;
+                            krem[k] = kr - cum;
+                            break;
+                        }
+                        cum += c[v];
                     }
-                    cum += c;
                 }
             }
             __syncthreads();
