@@ -151,6 +151,11 @@ ada_status run_pack(const ada_geom *g, const ada_cache *c, int32_t S, const int3
 {
     const int H = g->num_kv_heads;
     const int64_t N = cu[S];
+    // (16-byte key and value loads, 4-byte code loads)
+    if ((reinterpret_cast<uintptr_t>(keys) & 15) || (reinterpret_cast<uintptr_t>(values) & 15) ||
+        (reinterpret_cast<uintptr_t>(codes8) & 3) || (reinterpret_cast<uintptr_t>(codes4) & 3) ||
+        (reinterpret_cast<uintptr_t>(radius) & 1))
+        return ADA_EINVAL;
     if (ws == nullptr || ws_bytes < pack_workspace(H, N, S) || (reinterpret_cast<uintptr_t>(ws) & 255))
         return ADA_EWORKSPACE;
     PlanBuf pb;

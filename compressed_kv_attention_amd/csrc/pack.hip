@@ -17,9 +17,11 @@
 //                given), then walk the row in index
 //                order with a block-wide scan to give every token its tier
 //                page and slot (src[page][slot] = the token-head it holds);
-//   pack_fill    one block per new page: assemble the page image in LDS in its
-//                final byte layout (fields copied, values of the 4-bit tier
-//                quantized, every other byte zero), write it with 16-byte
+//   pack_fill    one wave per new page (four per block): 16-byte loads of the
+//                slots' keys and values, all issued at once; the page image
+//                assembled in LDS in its final byte layout (fields copied,
+//                values transposed in registers, values of the 4-bit tier
+//                quantized, every other byte zero), written with 16-byte
 //                stores, then its page-table entry, metadata byte and
 //                slot_token entries.
 #include "ada_internal.h"
@@ -216,111 +218,200 @@ __global__ __launch_bounds__(1024) void pack_rank(PackPlan plan, PackData data)
     }
 }
 
-constexpr int kFillThreads = 256;
+constexpr int kFillWaves = 4;     // pages per block, one wave each
 constexpr int kMaxPageBytes = 8192; // the largest page (D = 128, tiers 0 and 3)
 
-__global__ __launch_bounds__(kFillThreads) void pack_fill(PackPlan plan, PackData data, PackCache cache)
+// Row-wise maximum of x over groups of N lanes (N = 8 or 16, aligned), in
+// every lane of the group: quad permutes, then the 8- and 16-lane mirrors.
+template <int N>
+__device__ __forceinline__ float group_max(float x)
 {
-    __shared__ uint4 img4[kMaxPageBytes / 16];
-    __shared__ int64_t src_s[kSlots];
-    const PackPage pg = plan.pages[blockIdx.x];
-    const int tier = pg.meta & 3, nv = ((pg.meta >> 2) & 15) + 1;
-    const int D = plan.D, G = D / 8, H = plan.Hkv;
-    const int n16 = page_bytes(D, tier) / 16;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    uint8_t *img = reinterpret_cast<uint8_t *>(img4);
-    for (int i = tid; i < n16; i += kFillThreads)
-        img4[i] = make_uint4(0, 0, 0, 0);
-    if (tid < kSlots)
-        src_s[tid] = tid < nv ? (int64_t)plan.src[(size_t)blockIdx.x * kSlots + tid] : -1;
-    __syncthreads();
+    x = fmaxf(x, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0xB1, 0xf, 0xf, false)));
+    x = fmaxf(x, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x4E, 0xf, 0xf, false)));
+    x = fmaxf(x, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x141, 0xf, 0xf, false)));
+    if (N == 16)
+        x = fmaxf(x, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x140, 0xf, 0xf, false)));
+    return x;
+}
 
-    if (tier == 0 || tier == 3) {
-        // keys: dims d, d+1 of a slot are adjacent in the row section
-        for (int i = tid; i < kSlots * D / 2; i += kFillThreads) {
-            const int t = i / (D / 2), d = 2 * (i % (D / 2));
-            const int64_t e = src_s[t];
-            if (e < 0)
-                continue;
-            uint32_t kk = *reinterpret_cast<const uint32_t *>(data.keys + e * D + d);
-            if (tier == 3)
-                kk = (uint32_t)f32_to_bf16(f16_bits_to_f32((uint16_t)(kk & 0xffff))) |
-                     ((uint32_t)f32_to_bf16(f16_bits_to_f32((uint16_t)(kk >> 16))) << 16);
-            *reinterpret_cast<uint32_t *>(img + row_off(t, d)) = kk;
-            const uint32_t vv = *reinterpret_cast<const uint32_t *>(data.values + e * D + d);
-            *reinterpret_cast<uint16_t *>(img + 32 * D + col_off(t, d)) = (uint16_t)(vv & 0xffff);
-            *reinterpret_cast<uint16_t *>(img + 32 * D + col_off(t, d + 1)) = (uint16_t)(vv >> 16);
-        }
-    } else if (tier == 1) {
-        for (int i = tid; i < kSlots * D / 2; i += kFillThreads) {
-            const int t = i / (D / 2), d = 2 * (i % (D / 2));
-            const int64_t e = src_s[t];
-            if (e < 0)
-                continue;
-            const uint32_t vv = *reinterpret_cast<const uint32_t *>(data.values + e * D + d);
-            *reinterpret_cast<uint16_t *>(img + col_off(t, d)) = (uint16_t)(vv & 0xffff);
-            *reinterpret_cast<uint16_t *>(img + col_off(t, d + 1)) = (uint16_t)(vv >> 16);
-        }
-        for (int i = tid; i < kSlots * G; i += kFillThreads) {
-            const int t = i / G, g = i % G;
-            if (src_s[t] >= 0)
-                img[codes_off(D, 1) + i] = data.codes8[src_s[t] * G + g];
-        }
-        if (tid < kSlots && src_s[tid] >= 0)
-            *reinterpret_cast<uint16_t *>(img + radius_off(D, 1) + 2 * tid) = data.radius[src_s[tid]];
-    } else {
-        // int8 values with one fp16 scale: scale = fp16(fp32(max|v| / 127)),
-        // q = clamp(rint(fp32(v / scale)), -127, 127), zero scale -> q = 0;
-        // wave w quantizes slots w, w + 4, w + 8, w + 12
-        for (int t = wave; t < kSlots; t += kFillThreads / 64) {
-            const int64_t e = src_s[t];
-            if (e < 0)
-                continue;
-            const uint16_t *vv = data.values + e * D;
-            float amax = 0.f;
-            for (int d = lane; d < D; d += 64)
-                amax = fmaxf(amax, fabsf(bf16_bits_to_f32(vv[d])));
+// One wave per page.  Lane (sg, dg) = (lane / DG, lane % DG), DG = D / 8,
+// takes dims 8 dg .. 8 dg + 7 of slots SPL sg .. SPL sg + SPL - 1 (SPL = 4
+// at D = 128, 2 at D = 64): one 16-byte load per slot for the keys and one
+// for the values, every load of the page issued before any is used.  The
+// key dims go to the row section as two 8-byte pieces; the values are
+// transposed in registers, the SPL slots of one dim being contiguous in the
+// column sections.
+template <int D>
+__device__ __forceinline__ void fill_page(const PackPlan &plan, const PackData &data, const PackCache &cache,
+                                          int64_t pidx, uint4 *img4, int lane)
+{
+    constexpr int G = D / 8, DG = D / 8, SG = 64 / DG, SPL = kSlots / SG;
+    const PackPage pg = plan.pages[pidx];
+    const int tier = pg.meta & 3, nv = ((pg.meta >> 2) & 15) + 1;
+    const int n16 = page_bytes(D, tier) / 16;
+    uint8_t *img = reinterpret_cast<uint8_t *>(img4);
+    const int sg = lane / DG, dg = lane % DG, t0 = SPL * sg, d0 = 8 * dg;
+    int64_t e[SPL];
 #pragma unroll
-            for (int o = 32; o >= 1; o >>= 1)
-                amax = fmaxf(amax, __shfl_xor(amax, o, 64));
-            const float s32 = amax / 127.0f;
-            const uint16_t sh = f64_to_f16_sat((double)s32);
-            const float sc = f16_bits_to_f32(sh);
-            for (int d = lane; d < D; d += 64) {
-                int q = 0;
-                if (sc != 0.f) {
-                    float y = rintf(bf16_bits_to_f32(vv[d]) / sc);
-                    y = fminf(fmaxf(y, -127.f), 127.f);
-                    q = (int)y;
-                }
-                img[col8_off(t, d)] = (uint8_t)(int8_t)q;
-            }
-            if (lane < G / 2)
-                img[codes_off(D, 2) + t * (G / 2) + lane] = data.codes4[e * (G / 2) + lane];
-            if (lane == 0) {
-                *reinterpret_cast<uint16_t *>(img + radius_off(D, 2) + 2 * t) = data.radius[e];
-                *reinterpret_cast<uint16_t *>(img + vscale_off(D) + 2 * t) = sh;
-            }
+    for (int j = 0; j < SPL; j++)
+        e[j] = t0 + j < nv ? (int64_t)plan.src[pidx * kSlots + t0 + j] : -1;
+    uint4 kv[SPL], vv[SPL];
+#pragma unroll
+    for (int j = 0; j < SPL; j++) {
+        kv[j] = make_uint4(0, 0, 0, 0);
+        vv[j] = make_uint4(0, 0, 0, 0);
+        if (e[j] >= 0) {
+            if (tier == 0 || tier == 3)
+                kv[j] = *reinterpret_cast<const uint4 *>(data.keys + e[j] * D + d0);
+            vv[j] = *reinterpret_cast<const uint4 *>(data.values + e[j] * D + d0);
         }
     }
-    __syncthreads();
+    for (int i = lane; i < n16; i += 64)
+        img4[i] = make_uint4(0, 0, 0, 0);
+    __builtin_amdgcn_wave_barrier();
+    if (tier == 0 || tier == 3) {
+#pragma unroll
+        for (int j = 0; j < SPL; j++) {
+            uint4 k = kv[j];
+            if (tier == 3) {
+                uint32_t w[4] = {k.x, k.y, k.z, k.w};
+#pragma unroll
+                for (int q = 0; q < 4; q++)
+                    w[q] = (uint32_t)f32_to_bf16(f16_bits_to_f32((uint16_t)(w[q] & 0xffff))) |
+                           ((uint32_t)f32_to_bf16(f16_bits_to_f32((uint16_t)(w[q] >> 16))) << 16);
+                k = make_uint4(w[0], w[1], w[2], w[3]);
+            }
+            *reinterpret_cast<uint2 *>(img + row_off(t0 + j, d0)) = make_uint2(k.x, k.y);
+            *reinterpret_cast<uint2 *>(img + row_off(t0 + j, d0 + 4)) = make_uint2(k.z, k.w);
+        }
+    }
+    if (tier != 2) {
+        // values: dim d0 + q of the SPL slots, contiguous in the column section
+        const int vbase = tier == 1 ? 0 : 32 * D;
+#pragma unroll
+        for (int q = 0; q < 8; q++) {
+            uint16_t h[SPL];
+#pragma unroll
+            for (int j = 0; j < SPL; j++) {
+                const uint32_t w = q < 2 ? (q & 1 ? vv[j].x >> 16 : vv[j].x)
+                                 : q < 4 ? (q & 1 ? vv[j].y >> 16 : vv[j].y)
+                                 : q < 6 ? (q & 1 ? vv[j].z >> 16 : vv[j].z)
+                                         : (q & 1 ? vv[j].w >> 16 : vv[j].w);
+                h[j] = (uint16_t)(w & 0xffff);
+            }
+            uint8_t *p = img + vbase + col_off(t0, d0 + q);
+            if (SPL == 4)
+                *reinterpret_cast<uint2 *>(p) = make_uint2((uint32_t)h[0] | ((uint32_t)h[1] << 16),
+                                                           (uint32_t)h[SPL > 2 ? 2 : 0] | ((uint32_t)h[SPL > 3 ? 3 : 0] << 16));
+            else
+                *reinterpret_cast<uint32_t *>(p) = (uint32_t)h[0] | ((uint32_t)h[SPL > 1 ? 1 : 0] << 16);
+        }
+    }
+    if (tier == 1) {
+        // 8-bit codes: slot t's G bytes; lane takes 4 of them
+        constexpr int PER = G / 4; // lanes per slot
+        if (lane < kSlots * PER) {
+            const int t = lane / PER, k = lane % PER;
+            const int64_t et = t < nv ? (int64_t)plan.src[pidx * kSlots + t] : -1;
+            if (et >= 0)
+                *reinterpret_cast<uint32_t *>(img + codes_off(D, 1) + t * G + 4 * k) =
+                    *reinterpret_cast<const uint32_t *>(data.codes8 + et * G + 4 * k);
+            if (k == 0 && et >= 0)
+                *reinterpret_cast<uint16_t *>(img + radius_off(D, 1) + 2 * t) = data.radius[et];
+        }
+    } else if (tier == 2) {
+        // int8 values with one fp16 scale per slot: scale = fp16(fp32(max|v| /
+        // 127)), q = clamp(rint(fp32(v / scale)), -127, 127), zero scale -> 0
+        float amax[SPL];
+#pragma unroll
+        for (int j = 0; j < SPL; j++) {
+            const uint32_t w[4] = {vv[j].x, vv[j].y, vv[j].z, vv[j].w};
+            float m = 0.f;
+#pragma unroll
+            for (int q = 0; q < 4; q++)
+                m = fmaxf(m, fmaxf(fabsf(bf16_bits_to_f32((uint16_t)(w[q] & 0xffff))),
+                                   fabsf(bf16_bits_to_f32((uint16_t)(w[q] >> 16)))));
+            amax[j] = group_max<DG>(m);
+        }
+        float sc[SPL];
+        uint16_t shs[SPL];
+#pragma unroll
+        for (int j = 0; j < SPL; j++) {
+            const float s32 = amax[j] / 127.0f;
+            shs[j] = f64_to_f16_sat((double)s32);
+            sc[j] = f16_bits_to_f32(shs[j]);
+        }
+#pragma unroll
+        for (int q = 0; q < 8; q++) {
+            uint32_t packed = 0;
+#pragma unroll
+            for (int j = 0; j < SPL; j++) {
+                const uint32_t w = q < 2 ? vv[j].x : q < 4 ? vv[j].y : q < 6 ? vv[j].z : vv[j].w;
+                const float v = bf16_bits_to_f32((uint16_t)(q & 1 ? w >> 16 : w & 0xffff));
+                int qi = 0;
+                if (sc[j] != 0.f) {
+                    float y = rintf(v / sc[j]);
+                    y = fminf(fmaxf(y, -127.f), 127.f);
+                    qi = (int)y;
+                }
+                packed |= (uint32_t)(uint8_t)(int8_t)qi << (8 * j);
+            }
+            uint8_t *p = img + col8_off(t0, d0 + q);
+            if (SPL == 4)
+                *reinterpret_cast<uint32_t *>(p) = packed;
+            else
+                *reinterpret_cast<uint16_t *>(p) = (uint16_t)packed;
+        }
+        if (dg == 0) {
+#pragma unroll
+            for (int j = 0; j < SPL; j++) {
+                if (e[j] >= 0) {
+                    *reinterpret_cast<uint16_t *>(img + radius_off(D, 2) + 2 * (t0 + j)) = data.radius[e[j]];
+                    *reinterpret_cast<uint16_t *>(img + vscale_off(D) + 2 * (t0 + j)) = shs[j];
+                }
+            }
+        }
+        // 4-bit codes: slot t's G / 2 bytes; lane takes 4 of them
+        constexpr int PER4 = G / 8;
+        if (lane < kSlots * PER4) {
+            const int t = lane / PER4, k = lane % PER4;
+            const int64_t et = t < nv ? (int64_t)plan.src[pidx * kSlots + t] : -1;
+            if (et >= 0)
+                *reinterpret_cast<uint32_t *>(img + codes_off(D, 2) + t * (G / 2) + 4 * k) =
+                    *reinterpret_cast<const uint32_t *>(data.codes4 + et * (G / 2) + 4 * k);
+        }
+    }
+    __builtin_amdgcn_wave_barrier();
     uint4 *dst = reinterpret_cast<uint4 *>(cache.arena + (size_t)pg.off * kUnit);
-    for (int i = tid; i < n16; i += kFillThreads)
+    for (int i = lane; i < n16; i += 64)
         dst[i] = img4[i];
     const size_t slot = (size_t)pg.row * plan.maxp + pg.pi;
-    if (tid == 0) {
+    if (lane == 0) {
         cache.page_table[slot] = pg.off;
         cache.page_meta[slot] = (uint8_t)pg.meta;
     }
-    if (cache.slot_token != nullptr && tid < kSlots) {
-        const int64_t e = src_s[tid];
+    if (cache.slot_token != nullptr && lane < kSlots) {
+        const int64_t et = lane < nv ? (int64_t)plan.src[pidx * kSlots + lane] : -1;
         int32_t pos = -1;
-        if (e >= 0) {
-            const PackSeq sq = plan.seqs[pg.row / H];
-            pos = (int32_t)(sq.pos_base + (e / H - sq.begin));
+        if (et >= 0) {
+            const PackSeq sq = plan.seqs[pg.row / plan.Hkv];
+            pos = (int32_t)(sq.pos_base + (et / plan.Hkv - sq.begin));
         }
-        cache.slot_token[slot * kSlots + tid] = pos;
+        cache.slot_token[slot * kSlots + lane] = pos;
     }
+}
+
+__global__ __launch_bounds__(64 * kFillWaves) void pack_fill(PackPlan plan, PackData data, PackCache cache)
+{
+    __shared__ uint4 img4[kFillWaves][kMaxPageBytes / 16];
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int64_t pidx = (int64_t)blockIdx.x * kFillWaves + wave;
+    if (pidx >= plan.n_pages)
+        return; // (no block barrier below: each wave has its own page)
+    if (plan.D == 128)
+        fill_page<128>(plan, data, cache, pidx, img4[wave], lane);
+    else
+        fill_page<64>(plan, data, cache, pidx, img4[wave], lane);
 }
 
 } // namespace
@@ -340,7 +431,8 @@ hipError_t launch_pack(const PackPlan &plan, const PackData &data, const PackCac
             return e;
     }
     if (plan.n_pages > 0) {
-        hipLaunchKernelGGL(pack_fill, dim3(plan.n_pages), dim3(kFillThreads), 0, st, plan, data, cache);
+        hipLaunchKernelGGL(pack_fill, dim3((plan.n_pages + kFillWaves - 1) / kFillWaves), dim3(64 * kFillWaves),
+                           0, st, plan, data, cache);
         if (hipError_t e = hipGetLastError(); e != hipSuccess)
             return e;
     }

@@ -150,8 +150,10 @@ size_t rdr_pack_workspace_size(const ada_geom *geom, int64_t n_tokens, int32_t n
  * scale per (token, head): scale = fp16(fp32(max|v| / 127)),
  * q = clamp(rint(fp32(v / scale)), -127, 127), q = 0 when scale = 0.
  *   num_seqs must equal cache->num_seqs (a sequence may bring 0 tokens).
- *   keys fp16 / values bf16 [N][Hkv][D]; radius [N][Hkv]; codes8 [N][Hkv][G];
- *   codes4 [N][Hkv][G/2] (from ada_encode); scores f32 [N][Hkv] (finite).
+ *   keys fp16 / values bf16 [N][Hkv][D] (both 16-byte aligned); radius
+ *   [N][Hkv] (2-byte aligned); codes8 [N][Hkv][G], codes4 [N][Hkv][G/2]
+ *   (from ada_encode; both 4-byte aligned); scores f32 [N][Hkv] (finite).
+ *   A misaligned pointer is ADA_EINVAL.
  *   protect_host [N][Hkv] u8 (nonzero = protected) or NULL; more protected
  *     tokens in a row than its tier-0 count is ADA_EINVAL.
  *   place_perm_host: permutation of [0, n_pages) or NULL.
