@@ -245,9 +245,11 @@ __device__ __forceinline__ void fetch_page(PageRegs<D> &pr, const uint8_t *page,
             t2 = L.sblk2;
         o[c] = (DENSE || tier == 0) ? dense : tier == 1 ? t1 : t2;
     }
+    // (non-temporal: every page byte is read once per step, so its lines
+    // are not worth keeping in the caches)
 #pragma unroll
     for (int c = 0; c < NL; c++)
-        pr.c[c] = *(gchunk)(page + o[c]);
+        pr.c[c] = __builtin_nontemporal_load((gchunk)(page + o[c]));
 }
 
 // The four fp16 values of slots 4r .. 4r+3 from a 16-byte block holding
