@@ -218,6 +218,20 @@ __global__ __launch_bounds__(1024) void pack_rank(PackPlan plan, PackData data)
     }
 }
 
+typedef unsigned int u32x4v __attribute__((ext_vector_type(4)));
+
+// 16-byte loads and stores that do not keep their lines in the caches (each
+// key, value and page byte is touched once by the pack)
+__device__ __forceinline__ uint4 nt_load16(const uint16_t *p)
+{
+    const u32x4v v = __builtin_nontemporal_load(reinterpret_cast<const u32x4v *>(p));
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ void nt_store16(uint4 *p, uint4 v)
+{
+    __builtin_nontemporal_store(u32x4v{v.x, v.y, v.z, v.w}, reinterpret_cast<u32x4v *>(p));
+}
+
 constexpr int kFillWaves = 4;     // pages per block, one wave each
 constexpr int kMaxPageBytes = 8192; // the largest page (D = 128, tiers 0 and 3)
 
@@ -262,8 +276,8 @@ __device__ __forceinline__ void fill_page(const PackPlan &plan, const PackData &
         vv[j] = make_uint4(0, 0, 0, 0);
         if (e[j] >= 0) {
             if (tier == 0 || tier == 3)
-                kv[j] = *reinterpret_cast<const uint4 *>(data.keys + e[j] * D + d0);
-            vv[j] = *reinterpret_cast<const uint4 *>(data.values + e[j] * D + d0);
+                kv[j] = nt_load16(data.keys + e[j] * D + d0);
+            vv[j] = nt_load16(data.values + e[j] * D + d0);
         }
     }
     for (int i = lane; i < n16; i += 64)
@@ -384,7 +398,7 @@ __device__ __forceinline__ void fill_page(const PackPlan &plan, const PackData &
     __builtin_amdgcn_wave_barrier();
     uint4 *dst = reinterpret_cast<uint4 *>(cache.arena + (size_t)pg.off * kUnit);
     for (int i = lane; i < n16; i += 64)
-        dst[i] = img4[i];
+        nt_store16(dst + i, img4[i]);
     const size_t slot = (size_t)pg.row * plan.maxp + pg.pi;
     if (lane == 0) {
         cache.page_table[slot] = pg.off;
