@@ -79,6 +79,9 @@ __global__ __launch_bounds__(D / 8 * 64) void append_kernel(AppendArgs a)
     __shared__ int open_s[3], nvalid_s[3], npages_s;
     __shared__ uint32_t open_off_s[3];
     __shared__ unsigned long long cur_s;
+    __shared__ float score_s, thr_s;
+    __shared__ int prot_s;
+    __shared__ int32_t pos_s;
     const int row = blockIdx.x, s = row / a.Hkv, h = row % a.Hkv;
     const int tid = threadIdx.x, lane = tid & 63;
     const uint16_t *k = a.keys + (size_t)row * D;
@@ -96,6 +99,14 @@ __global__ __launch_bounds__(D / 8 * 64) void append_kernel(AppendArgs a)
             nvalid_s[t] = op[t] >= 0 ? ((a.page_meta[(size_t)row * a.maxp + op[t]] >> 2) & 15) + 1 : kSlots;
             open_off_s[t] = op[t] >= 0 ? a.page_table[(size_t)row * a.maxp + op[t]] : 0u;
         }
+    }
+    // the row's score, protection, threshold and position, read by another
+    // wave's lane at the same time
+    if (tid == 128) {
+        prot_s = a.protect != nullptr ? (int)a.protect[row] : 0;
+        score_s = a.scores[row];
+        thr_s = a.threshold[s];
+        pos_s = a.slot_token != nullptr ? (int32_t)a.pos[s] : -1;
     }
     // this wave's codewords, loaded before they are needed
     const int g_w = tid / 64, j_w = tid % 64;
@@ -183,8 +194,8 @@ __global__ __launch_bounds__(D / 8 * 64) void append_kernel(AppendArgs a)
         const uint16_t rb = f64_to_f16_sat(rn);
         rbits_s = rb;
         int tier = 0;
-        if (a.protect == nullptr || a.protect[row] == 0)
-            tier = chain_tier(D, a.scores[row], rb, (float)e8, (float)e4, a.threshold[s]);
+        if (prot_s == 0)
+            tier = chain_tier(D, score_s, rb, (float)e8, (float)e4, thr_s);
         if (a.tiers_out != nullptr)
             a.tiers_out[row] = (uint8_t)tier;
         int pi = -1, slot = kSlots, fresh = 0;
@@ -290,7 +301,7 @@ __global__ __launch_bounds__(D / 8 * 64) void append_kernel(AppendArgs a)
         a.page_meta[(size_t)row * a.maxp + pi] = (uint8_t)(tier | (slot << 2));
         a.tier_tokens[row * 3 + tier] += 1;
         if (a.slot_token != nullptr)
-            a.slot_token[((size_t)row * a.maxp + pi) * kSlots + slot] = (int32_t)a.pos[s];
+            a.slot_token[((size_t)row * a.maxp + pi) * kSlots + slot] = pos_s;
     }
 }
 
