@@ -15,16 +15,18 @@
 // codewords the matrix cores form |c|^2 - 2 u.c in binary32 (two chained
 // 16x16x4 MFMAs over the 8 coordinates, from an accumulator holding |c|^2),
 // so the codebook stays in registers as MFMA operands and the vector ALU
-// only keeps each token's best and second-best score.  A binary32 score is a filter:
-// where its best two are too close to be ordered for certain (see
-// kFilterRel), the wave rescans that token's codebook in double, so the codes
-// are still the exact double argmin.
+// only keeps each token's best and second-best score.  A binary32 score is
+// a filter: where its best two are too close to be ordered for certain (see
+// kFilterRel), the token-group is rescanned in double, so the codes are
+// still the exact double argmin.
 //
 // Grid: x = blocks of 64-token chunks (grid-stride), y = (kv-head, quarter
 // of the groups).  A block has one wave per group of its quarter (4 waves).
-// Per chunk it stages the 64 keys in LDS, sums the norms (one thread per
-// token), then every wave scores its group for the 4 tiles of 16 tokens and
-// leaves the codes in LDS for byte stores.
+// Per chunk it stages the 64 keys in LDS and sums a fast-order norm per
+// token (four lanes a token); the last wave also sums the defining norms
+// (one lane a token) for the radius and the rescans; every wave scores its
+// group for the 4 tiles of 16 tokens, queues its near ties, and leaves the
+// codes in LDS; the queued rescans are dealt to the waves; byte stores.
 #include "ada_internal.h"
 #include "numfmt.h"
 #include "wave_ops.h"

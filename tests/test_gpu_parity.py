@@ -228,6 +228,31 @@ def test_encode_near_ties_exact():
     assert np.array_equal(c4.cpu().numpy(), rc4)
 
 
+def test_encode_codebooks_outside_the_filter_range():
+    """Codebooks the binary32 filter cannot bound -- a group with entries of
+    magnitude 2^30, a group with a NaN codeword, a group with an infinite
+    entry -- are scanned in double for every token (a NaN or infinite
+    distance never wins); the other groups keep the filter.  Codes equal the
+    oracle's bit for bit."""
+    cfg = small_workload(D=64, Hq=4, Hkv=2, S=1, T=200, seed=62)
+    case = make_case(cfg)
+    cb8 = case["cb8"].numpy().copy()
+    cb4 = case["cb4"].numpy().copy()
+    cb8[0, 1] *= np.float32(2.0 ** 30)        # head 0, group 1: far outside
+    cb8[1, 3, 7, :] = np.float32(np.nan)      # head 1, group 3: a NaN codeword
+    cb4[1, 5, 2, 0] = np.float32(np.inf)      # head 1, group 5: an infinite entry
+    case["cb8"], case["cb4"] = torch.from_numpy(cb8), torch.from_numpy(cb4)
+    flush("[encode] codebooks outside the filter range")
+    geom = geom_of(cfg)
+    d = _dev_case(case)
+    r, c8, c4 = gpu_encode(geom, d["keys"], d["cb8"], d["cb4"])
+    torch.cuda.synchronize()
+    rr, rc8, rc4 = oracle.encode(case["keys"], case["cb8"], case["cb4"], nthreads=8)
+    assert np.array_equal(u16(r), rr)
+    assert np.array_equal(c8.cpu().numpy(), rc8)
+    assert np.array_equal(c4.cpu().numpy(), rc4)
+
+
 def test_encode_llama_shape_t32k_full():
     cfg = synth.WORKLOADS[2]
     _check_encode(cfg, make_case(cfg), "Llama-3-8B shape T=32768")
