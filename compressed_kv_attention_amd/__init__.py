@@ -21,7 +21,10 @@ import torch
 __all__ = [
     "AdaError", "Geom", "Cache", "load", "lib_path", "page_bytes", "encode", "pack_num_pages",
     "pack_workspace_size", "rdr_pack", "dense_pack", "decode_default_splits",
-    "decode_workspace_size", "decode", "dense_decode",
+    "decode_workspace_size", "decode", "decode_stage", "dense_decode",
+    "code_error", "solve_workspace_size", "rdr_solve", "tier_counts", "pack_tiers_num_pages",
+    "rdr_pack_tiers", "AppendState", "append", "retier", "retier_plan",
+    "decode_sym_workspace_size", "decode_sym",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
