@@ -117,6 +117,15 @@ def test_pack_host_errors_leave_host_state_untouched():
     assert call(arena_units=1 << 20, maxp=64, protect=prot) == ada.EINVAL
     bad_perm = np.zeros(8, np.uint32)
     assert call(arena_units=1 << 20, maxp=64, perm=bad_perm) == ada.EINVAL
+    # misaligned keys / values (16-byte loads) or codes (4-byte loads)
+    view = ada._CacheView(256, 1 << 20, 256, 256, 256, 256, 0, 1, 64)
+    for k, v, c8, c4 in ((264, 256, 256, 256), (256, 264, 256, 256), (256, 256, 258, 256),
+                         (256, 256, 256, 257)):
+        assert L.rdr_pack(C.byref(g), C.byref(view), 1, cu.ctypes.data_as(C.c_void_p),
+                          bp.ctypes.data_as(C.c_void_p), C.c_void_p(k), C.c_void_p(v), fake,
+                          C.c_void_p(c8), C.c_void_p(c4), fake, None, None, None,
+                          cursor.ctypes.data_as(C.c_void_p), npages.ctypes.data_as(C.c_void_p),
+                          C.c_void_p(1 << 20), 1 << 30, None) == ada.EINVAL
     assert cursor[0] == 0 and not npages.any()
 
 
