@@ -49,6 +49,7 @@ struct PlanBuf {
     std::vector<uint8_t> blob; // [seqs][rows][pages] (each 256-byte aligned)
     size_t seq_off = 0, row_off = 0, page_off = 0;
     int n_pages = 0;
+    bool gen_pages = false; // the device writes the page list
     uint64_t cursor_after = 0;
     std::vector<int32_t> new_pages_per_row;
 };
@@ -67,6 +68,10 @@ size_t pack_workspace(int Hkv, int64_t n_tokens, int32_t num_seqs)
 // Plans one pack call on the host: counts, page numbering, placement.
 // counts[s][3] per-tier token counts of each sequence (the ranked path), and
 // row_counts[s * Hkv + h][3] those of each row; returns ADA_OK or the error.
+// Pages are numbered row by row, tiers 0, 1, 2 within a row.  In arena order
+// (perm null) a row's tier block is placed contiguously and the device
+// writes the page list from the rows' entries; for a given order the host
+// builds the list and places it.
 ada_status plan_pack(const ada_geom *g, const ada_cache *c, int32_t S, const int32_t *cu,
                      const std::vector<int64_t> &counts, const std::vector<int64_t> &row_counts,
                      bool dense, const uint32_t *perm,
@@ -77,8 +82,8 @@ ada_status plan_pack(const ada_geom *g, const ada_cache *c, int32_t S, const int
     const int64_t rows = (int64_t)S * H;
     std::vector<PackSeq> seqs(S);
     std::vector<PackRow> rowv(rows);
-    std::vector<PackPage> pages;
     pb.new_pages_per_row.assign(rows, 0);
+    int64_t n = 0;
     for (int s = 0; s < S; s++) {
         seqs[s].begin = cu[s];
         seqs[s].len = cu[s + 1] - cu[s];
@@ -91,53 +96,77 @@ ada_status plan_pack(const ada_geom *g, const ada_cache *c, int32_t S, const int
         seqs[s].pos_base = pos_base ? pos_base[s] : 0;
         for (int h = 0; h < H; h++) {
             const int64_t r = (int64_t)s * H + h;
-            int32_t pi = num_pages_host[r];
+            int64_t row_pages = 0;
             for (int k = 0; k < 3; k++) {
-                const int64_t n = row_counts[r * 3 + k];
-                rowv[r].lp_first[k] = (int32_t)pages.size();
-                rowv[r].count[k] = (int32_t)n;
-                for (int64_t f = 0; f < n; f += kSlots) {
+                const int64_t cnt = row_counts[r * 3 + k];
+                rowv[r].lp_first[k] = (int32_t)std::min<int64_t>(n + row_pages, INT32_MAX);
+                rowv[r].count[k] = (int32_t)cnt;
+                row_pages += (cnt + kSlots - 1) / kSlots;
+            }
+            rowv[r].pi0 = num_pages_host[r];
+            if ((int64_t)num_pages_host[r] + row_pages > c->max_pages_per_head)
+                return ADA_EINVAL;
+            pb.new_pages_per_row[r] = (int32_t)row_pages;
+            n += row_pages;
+        }
+    }
+    if (n > INT32_MAX)
+        return ADA_EINVAL;
+    const uint64_t unit[3] = {(uint64_t)page_bytes(D, dense ? 3 : 0) / kUnit,
+                              (uint64_t)page_bytes(D, dense ? 3 : 1) / kUnit,
+                              (uint64_t)page_bytes(D, dense ? 3 : 2) / kUnit};
+    uint64_t cur = cursor;
+    std::vector<PackPage> pages;
+    if (perm == nullptr) {
+        // arena order: each row's tier blocks back to back
+        for (int64_t r = 0; r < rows; r++)
+            for (int k = 0; k < 3; k++) {
+                rowv[r].off[k] = (uint32_t)std::min<uint64_t>(cur, UINT32_MAX);
+                cur += unit[k] * (uint64_t)((rowv[r].count[k] + kSlots - 1) / kSlots);
+                if (cur > c->arena_units)
+                    return ADA_ENOSPACE;
+            }
+    } else {
+        pages.reserve((size_t)n);
+        for (int64_t r = 0; r < rows; r++)
+            for (int k = 0; k < 3; k++) {
+                rowv[r].off[k] = 0;
+                const int64_t cnt = rowv[r].count[k];
+                for (int64_t f = 0; f < cnt; f += kSlots) {
                     PackPage p;
                     p.off = 0;
                     p.row = (int32_t)r;
-                    p.pi = pi++;
-                    const int nv = (int)std::min<int64_t>(kSlots, n - f);
+                    p.pi = rowv[r].pi0 + (int32_t)(pages.size() - rowv[r].lp_first[0]);
+                    const int nv = (int)std::min<int64_t>(kSlots, cnt - f);
                     p.meta = (dense ? 3 : k) | ((nv - 1) << 2);
                     pages.push_back(p);
                 }
             }
-            if (pi > c->max_pages_per_head)
-                return ADA_EINVAL;
-            pb.new_pages_per_row[r] = pi - num_pages_host[r];
-        }
-    }
-    const int64_t n = (int64_t)pages.size();
-    if (n > INT32_MAX)
-        return ADA_EINVAL;
-    // placement in the given order
-    uint64_t cur = cursor;
-    if (perm != nullptr) {
         std::vector<char> seen(n, 0);
         for (int64_t k = 0; k < n; k++)
             if (perm[k] >= (uint64_t)n || seen[perm[k]]++)
                 return ADA_EINVAL;
-    }
-    for (int64_t k = 0; k < n; k++) {
-        PackPage &p = pages[perm ? perm[k] : k];
-        p.off = (uint32_t)cur;
-        cur += (uint64_t)page_bytes(D, p.meta & 3) / kUnit;
-        if (cur > c->arena_units)
-            return ADA_ENOSPACE;
+        for (int64_t k = 0; k < n; k++) {
+            PackPage &p = pages[perm[k]];
+            p.off = (uint32_t)cur;
+            cur += (uint64_t)page_bytes(D, p.meta & 3) / kUnit;
+            if (cur > c->arena_units)
+                return ADA_ENOSPACE;
+        }
     }
     pb.n_pages = (int)n;
     pb.cursor_after = cur;
     pb.seq_off = 0;
     pb.row_off = align256(sizeof(PackSeq) * (size_t)std::max(S, 1));
     pb.page_off = pb.row_off + align256(sizeof(PackRow) * (size_t)std::max<int64_t>(rows, 1));
-    pb.blob.assign(pb.page_off + sizeof(PackPage) * (size_t)std::max<int64_t>(n, 1), 0);
+    pb.gen_pages = perm == nullptr;
+    pb.blob.assign(pb.gen_pages ? pb.row_off + sizeof(PackRow) * (size_t)std::max<int64_t>(rows, 1)
+                                : pb.page_off + sizeof(PackPage) * (size_t)std::max<int64_t>(n, 1),
+                   0);
     std::memcpy(pb.blob.data() + pb.seq_off, seqs.data(), sizeof(PackSeq) * seqs.size());
     std::memcpy(pb.blob.data() + pb.row_off, rowv.data(), sizeof(PackRow) * rowv.size());
-    std::memcpy(pb.blob.data() + pb.page_off, pages.data(), sizeof(PackPage) * pages.size());
+    if (!pb.gen_pages)
+        std::memcpy(pb.blob.data() + pb.page_off, pages.data(), sizeof(PackPage) * pages.size());
     return ADA_OK;
 }
 
@@ -182,7 +211,7 @@ ada_status run_pack(const ada_geom *g, const ada_cache *c, int32_t S, const int3
     PackPlan plan;
     plan.seqs = reinterpret_cast<const PackSeq *>(wsb + pb.seq_off);
     plan.rows = reinterpret_cast<const PackRow *>(wsb + pb.row_off);
-    plan.pages = reinterpret_cast<const PackPage *>(wsb + pb.page_off);
+    plan.pages = reinterpret_cast<PackPage *>(wsb + pb.page_off);
     plan.protect = protect_host != nullptr ? prot_dev : nullptr;
     plan.tiers = tiers;
     plan.src = src;
@@ -192,6 +221,7 @@ ada_status run_pack(const ada_geom *g, const ada_cache *c, int32_t S, const int3
     plan.maxp = c->max_pages_per_head;
     plan.n_pages = pb.n_pages;
     plan.dense = dense ? 1 : 0;
+    plan.gen_pages = pb.gen_pages ? 1 : 0;
     plan.n_tokens = N;
     PackData data{keys, values, radius, codes8, codes4, scores};
     PackCache cache{c->arena, c->page_table, c->page_meta, c->num_pages, c->tier_tokens, c->slot_token};

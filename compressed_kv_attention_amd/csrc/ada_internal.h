@@ -149,7 +149,9 @@ struct RetierArgs {
 hipError_t launch_retier(int D, const RetierArgs &a, int rows, hipStream_t st);
 
 // ---- pack ----------------------------------------------------------------
-// Host-built plan of one pack call, copied into the workspace.
+// Host-built plan of one pack call, copied into the workspace.  The page
+// list is built on the host only for a given placement order; in arena
+// order (the default) the row kernel writes it from the rows' entries.
 struct PackSeq {
     int32_t begin;     // first flat token of the sequence in this call
     int32_t len;       // T_s
@@ -160,6 +162,8 @@ struct PackSeq {
 struct PackRow {
     int32_t lp_first[3]; // logical index of the row's first page of each tier
     int32_t count[3];    // tokens per tier
+    int32_t pi0;         // the row's page count before this call
+    uint32_t off[3];     // arena offset of the row's first page of each tier (arena order)
 };
 struct PackPage {
     uint32_t off;        // arena offset, 128-byte units
@@ -170,11 +174,11 @@ struct PackPage {
 struct PackPlan {
     const PackSeq *seqs;
     const PackRow *rows;
-    const PackPage *pages;
+    PackPage *pages;        // written by pack_rows when gen_pages is set
     const uint8_t *protect; // [N][Hkv] or null
     const uint8_t *tiers;   // [N][Hkv] given tiers (0-2 kept, other values dropped) or null
     int32_t *src;           // [n_pages][16]: flat (token, head) index a slot holds, or -1
-    int S, Hkv, D, maxp, n_pages, dense;
+    int S, Hkv, D, maxp, n_pages, dense, gen_pages;
     int64_t n_tokens;
 };
 struct PackData {

@@ -10,7 +10,9 @@
 // is given (by the budget solver in rdr.hip).
 //
 // Kernels, in stream order:
-//   pack_rows    one thread per row: advance num_pages and tier_tokens;
+//   pack_rows    one block per row: advance num_pages and tier_tokens and,
+//                in arena order, write the row's page list (arena offset,
+//                page index, metadata of each new page);
 //   pack_rank    one 1024-thread block per row: radix-select the keys at the
 //                three tier boundaries (8 passes of 8 bits over 64-bit keys,
 //                exact because keys are unique; skipped when the tiers are
@@ -34,17 +36,36 @@ namespace {
 
 __global__ __launch_bounds__(256) void pack_rows(PackPlan plan, PackCache cache)
 {
-    const int row = blockIdx.x * 256 + threadIdx.x;
-    if (row >= plan.S * plan.Hkv)
-        return;
+    const int row = blockIdx.x;
     const PackRow rw = plan.rows[row];
-    int pages = 0;
-    for (int k = 0; k < 3; k++)
-        pages += (rw.count[k] + kSlots - 1) / kSlots;
-    cache.num_pages[row] += pages;
-    if (!plan.dense && cache.tier_tokens != nullptr)
-        for (int k = 0; k < 3; k++)
-            cache.tier_tokens[row * 3 + k] += rw.count[k];
+    int np[3], pages = 0;
+    for (int k = 0; k < 3; k++) {
+        np[k] = (rw.count[k] + kSlots - 1) / kSlots;
+        pages += np[k];
+    }
+    if (threadIdx.x == 0) {
+        cache.num_pages[row] += pages;
+        if (!plan.dense && cache.tier_tokens != nullptr)
+            for (int k = 0; k < 3; k++)
+                cache.tier_tokens[row * 3 + k] += rw.count[k];
+    }
+    if (!plan.gen_pages)
+        return;
+    // The row's pages in arena order: tier 0, then 1, then 2, each tier's
+    // pages back to back from the tier's first offset; all but a tier's last
+    // page are full.
+    for (int q = threadIdx.x; q < pages; q += 256) {
+        const int k = q < np[0] ? 0 : q < np[0] + np[1] ? 1 : 2;
+        const int f = q - (k == 0 ? 0 : k == 1 ? np[0] : np[0] + np[1]);
+        const int tier = plan.dense ? 3 : k;
+        const int nv = min(kSlots, rw.count[k] - f * kSlots);
+        PackPage pg;
+        pg.off = rw.off[k] + (uint32_t)f * (uint32_t)(page_bytes(plan.D, tier) / kUnit);
+        pg.row = row;
+        pg.pi = rw.pi0 + q;
+        pg.meta = tier | ((nv - 1) << 2);
+        plan.pages[rw.lp_first[k] + f] = pg;
+    }
 }
 
 // Order-preserving map of a finite float (with -0 == +0) to uint32.
@@ -435,7 +456,7 @@ hipError_t launch_pack(const PackPlan &plan, const PackData &data, const PackCac
 {
     const int rows = plan.S * plan.Hkv;
     if (rows > 0) {
-        hipLaunchKernelGGL(pack_rows, dim3((rows + 255) / 256), dim3(256), 0, st, plan, cache);
+        hipLaunchKernelGGL(pack_rows, dim3(rows), dim3(256), 0, st, plan, cache);
         if (hipError_t e = hipGetLastError(); e != hipSuccess)
             return e;
     }
