@@ -507,13 +507,25 @@ __global__ __launch_bounds__((Waves<D, NH>::THREADS)) void decode_main(DecodeArg
     float *lut = smem;
     uint2 *tbl = reinterpret_cast<uint2 *>(smem + LUT_FLOATS); // [n_wg] page-table entries
 
-    // Consecutive logical blocks share an XCD (blocks are dealt round-robin
-    // over the 8 XCDs), so one row's splits hit one L2.
-    const int nblk = gridDim.x;
-    int logical = blockIdx.x;
-    if (nblk % 8 == 0)
-        logical = (blockIdx.x % 8) * (nblk / 8) + blockIdx.x / 8;
-    const int row = logical / a.nsplit, split = logical % a.nsplit;
+    // Blocks are dealt round-robin over the 8 XCDs, each with its own L2.
+    // All splits of a row run on one XCD (one L2 holds the row's codebooks
+    // and table).  With a multiple of 8 rows, XCD x takes rows x, x + 8,
+    // x + 16, ...: with 8 kv-heads that is one head of every sequence, so
+    // ragged sequence lengths load the XCDs evenly.  Otherwise each XCD
+    // takes a contiguous range of rows.
+    const int nblk = gridDim.x, rows = a.S * a.Hkv;
+    int row, split;
+    if (rows % 8 == 0) {
+        const int i = blockIdx.x / 8;
+        row = 8 * (i / a.nsplit) + blockIdx.x % 8;
+        split = i % a.nsplit;
+    } else {
+        int logical = blockIdx.x;
+        if (nblk % 8 == 0)
+            logical = (blockIdx.x % 8) * (nblk / 8) + blockIdx.x / 8;
+        row = logical / a.nsplit;
+        split = logical % a.nsplit;
+    }
     const int s = row / a.Hkv, hkv = row % a.Hkv;
     // the wave index is wave-uniform; say so, so the page loop is scalar
     const int tid = threadIdx.x, lane = tid & 63;
