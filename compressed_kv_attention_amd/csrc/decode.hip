@@ -908,15 +908,43 @@ __global__ __launch_bounds__(256) void sym_lut_kernel(DecodeArgs a)
     constexpr int G = D / 8, LUT_FLOATS = G * kLutCodes * NH;
     __shared__ double qn[NH], u[NH][8];
     __shared__ float xq[NH][D];
+    __shared__ float4 cw[kLutCodes][2]; // group g's codewords: 256 8-bit, then 16 4-bit
     __shared__ double bd[4][NH];
     __shared__ int bc[4][NH];
     __shared__ int cq8[NH], cq4[NH];
     const int row = blockIdx.x, g = blockIdx.y, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int s = row / a.Hkv, hkv = row % a.Hkv;
     const uint16_t *qrow = a.q + ((size_t)s * a.Hq + (size_t)hkv * NH) * D;
-    for (int i = tid; i < NH * D; i += 256)
-        xq[i / D][i % D] = __uint_as_float((uint32_t)qrow[i] << 16);
+    const float *c8 = a.cb8 + ((size_t)hkv * G + g) * kCodes8 * 8;
+    const float *c4 = a.cb4 + ((size_t)hkv * G + g) * kCodes4 * 8;
+    // Every global load is issued before any is used (one memory latency):
+    // thread t's 8-bit codeword t, lanes 0..15 of wave 0 the 4-bit ones,
+    // and the query slices.
+    const float4 w0 = *reinterpret_cast<const float4 *>(c8 + tid * 8);
+    const float4 w1 = *reinterpret_cast<const float4 *>(c8 + tid * 8 + 4);
+    const int cc = lane & 15;
+    float4 v0 = make_float4(0.f, 0.f, 0.f, 0.f), v1 = v0;
+    if (wave == 0) {
+        v0 = *reinterpret_cast<const float4 *>(c4 + cc * 8);
+        v1 = *reinterpret_cast<const float4 *>(c4 + cc * 8 + 4);
+    }
+    constexpr int QPT = (NH * D + 255) / 256; // query elements per thread
+    uint16_t qv[QPT];
+#pragma unroll
+    for (int k = 0; k < QPT; k++)
+        qv[k] = tid + 256 * k < NH * D ? qrow[tid + 256 * k] : 0;
+    cw[tid][0] = w0;
+    cw[tid][1] = w1;
+    if (wave == 0 && lane < kCodes4) {
+        cw[kCodes8 + lane][0] = v0;
+        cw[kCodes8 + lane][1] = v1;
+    }
+#pragma unroll
+    for (int k = 0; k < QPT; k++)
+        if (tid + 256 * k < NH * D)
+            xq[(tid + 256 * k) / D][(tid + 256 * k) % D] = __uint_as_float((uint32_t)qv[k] << 16);
     __syncthreads();
+    // |q_h| summed sequentially in double, as the keys' norms are
     if (tid < NH) {
         double ss = 0.0;
         for (int j = 0; j < D; j++) {
@@ -928,16 +956,12 @@ __global__ __launch_bounds__(256) void sym_lut_kernel(DecodeArgs a)
     __syncthreads();
     if (tid < NH * 8) {
         const int h = tid / 8, j = tid % 8;
-        const double x = (double)__uint_as_float((uint32_t)qrow[h * D + 8 * g + j] << 16);
+        const double x = (double)xq[h][8 * g + j];
         u[h][j] = qn[h] > 0.0 ? x / qn[h] : 0.0;
     }
     __syncthreads();
-    const float *c8 = a.cb8 + ((size_t)hkv * G + g) * kCodes8 * 8;
-    const float *c4 = a.cb4 + ((size_t)hkv * G + g) * kCodes4 * 8;
     // nearest 8-bit codeword per head: thread t scores codeword t
     {
-        const float4 w0 = *reinterpret_cast<const float4 *>(c8 + tid * 8);
-        const float4 w1 = *reinterpret_cast<const float4 *>(c8 + tid * 8 + 4);
         const float w[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
 #pragma unroll
         for (int h = 0; h < NH; h++) {
@@ -965,10 +989,7 @@ __global__ __launch_bounds__(256) void sym_lut_kernel(DecodeArgs a)
     }
     // nearest 4-bit codeword per head: lanes 0..15 of wave 0
     if (wave == 0) {
-        const int cc = lane & 15;
-        const float4 w0 = *reinterpret_cast<const float4 *>(c4 + cc * 8);
-        const float4 w1 = *reinterpret_cast<const float4 *>(c4 + cc * 8 + 4);
-        const float w[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+        const float w[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
 #pragma unroll
         for (int h = 0; h < NH; h++) {
             double d = 0.0;
@@ -1005,11 +1026,14 @@ __global__ __launch_bounds__(256) void sym_lut_kernel(DecodeArgs a)
     __syncthreads();
     float *lut = a.glut + (size_t)row * LUT_FLOATS;
     for (int c = tid; c < kLutCodes; c += 256) {
-        const float *wc = c < kCodes8 ? c8 + c * 8 : c4 + (c - kCodes8) * 8;
+        const float4 c0 = cw[c][0], c1 = cw[c][1];
+        const float wc[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
         float o[NH];
 #pragma unroll
         for (int h = 0; h < NH; h++) {
-            const float *wq = c < kCodes8 ? c8 + cq8[h] * 8 : c4 + cq4[h] * 8;
+            const int iq = c < kCodes8 ? cq8[h] : kCodes8 + cq4[h];
+            const float4 q0 = cw[iq][0], q1 = cw[iq][1];
+            const float wq[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
             float acc = wq[0] * wc[0];
 #pragma unroll
             for (int j = 1; j < 8; j++)
