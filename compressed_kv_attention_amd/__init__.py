@@ -399,12 +399,14 @@ def tier_counts(geom: Geom, cu_tokens, tiers, stream=None) -> np.ndarray:
     (synchronizes the stream)."""
     cu, cup = _host(cu_tokens, np.int32, "cu_tokens")
     S = len(cu) - 1
-    out = np.zeros((max(1, S * geom.num_kv_heads), 3), dtype=np.int32)
+    # page-locked result buffer (from torch's caching host allocator): the
+    # device-to-host copy then needs no staging
+    out = torch.zeros((max(1, S * geom.num_kv_heads), 3), dtype=torch.int32, pin_memory=True)
     ws = _workspace(int(load().rdr_tier_counts_workspace_size(C.byref(geom), S)), tiers.device)
     st = load().rdr_tier_counts(C.byref(geom), S, cup, _dev(tiers, "tiers", (torch.uint8,)),
-                                out.ctypes.data_as(C.c_void_p), _dev(ws, "ws"), ws.numel(), _stream(stream))
+                                C.c_void_p(out.data_ptr()), _dev(ws, "ws"), ws.numel(), _stream(stream))
     _check(st, "rdr_tier_counts")
-    return out[: S * geom.num_kv_heads]
+    return out.numpy()[: S * geom.num_kv_heads].copy()
 
 
 def pack_tiers_num_pages(geom: Geom, row_counts) -> int:
