@@ -43,6 +43,7 @@
 // (m, l, acc) is written; the merge kernel combines a row's splits into the
 // outputs (with one split the stream writes them directly).
 #include "ada_internal.h"
+#include "wave_ops.h"
 
 #include <type_traits>
 
@@ -907,7 +908,7 @@ __global__ __launch_bounds__(256) void sym_lut_kernel(DecodeArgs a)
 {
     constexpr int G = D / 8, LUT_FLOATS = G * kLutCodes * NH;
     __shared__ double qn[NH], u[NH][8];
-    __shared__ float xq[NH][D];
+    __shared__ __align__(16) float xq[NH][D];
     __shared__ float4 cw[kLutCodes][2]; // group g's codewords: 256 8-bit, then 16 4-bit
     __shared__ double bd[4][NH];
     __shared__ int bc[4][NH];
@@ -944,12 +945,25 @@ __global__ __launch_bounds__(256) void sym_lut_kernel(DecodeArgs a)
         if (tid + 256 * k < NH * D)
             xq[(tid + 256 * k) / D][(tid + 256 * k) % D] = __uint_as_float((uint32_t)qv[k] << 16);
     __syncthreads();
-    // |q_h| summed sequentially in double, as the keys' norms are
+    // |q_h| summed sequentially in double, as the keys' norms are (each
+    // square is exact in double); the slices are read 32 dims ahead of the
+    // sum so that only the adds form the chain
     if (tid < NH) {
+        const float4 *xr = reinterpret_cast<const float4 *>(xq[tid]);
         double ss = 0.0;
-        for (int j = 0; j < D; j++) {
-            const double x = (double)xq[tid][j];
-            ss = ss + x * x;
+#pragma unroll
+        for (int j0 = 0; j0 < D / 4; j0 += 8) {
+            float4 xv[8];
+#pragma unroll
+            for (int j = 0; j < 8; j++)
+                xv[j] = xr[j0 + j];
+#pragma unroll
+            for (int j = 0; j < 8; j++) {
+                ss = ss + (double)xv[j].x * (double)xv[j].x;
+                ss = ss + (double)xv[j].y * (double)xv[j].y;
+                ss = ss + (double)xv[j].z * (double)xv[j].z;
+                ss = ss + (double)xv[j].w * (double)xv[j].w;
+            }
         }
         qn[tid] = sqrt(ss);
     }
@@ -972,15 +986,7 @@ __global__ __launch_bounds__(256) void sym_lut_kernel(DecodeArgs a)
                 d = d + df * df;
             }
             int c = tid;
-#pragma unroll
-            for (int o = 32; o >= 1; o >>= 1) {
-                const double d2 = __shfl_xor(d, o, 64);
-                const int c2 = __shfl_xor(c, o, 64);
-                if (d2 < d || (d2 == d && c2 < c)) {
-                    d = d2;
-                    c = c2;
-                }
-            }
+            wave_argmin(d, c);
             if (lane == 0) {
                 bd[wave][h] = d;
                 bc[wave][h] = c;
@@ -998,16 +1004,8 @@ __global__ __launch_bounds__(256) void sym_lut_kernel(DecodeArgs a)
                 const double df = u[h][j] - (double)w[j];
                 d = d + df * df;
             }
-            int c = cc;
-#pragma unroll
-            for (int o = 8; o >= 1; o >>= 1) {
-                const double d2 = __shfl_xor(d, o, 64);
-                const int c2 = __shfl_xor(c, o, 64);
-                if (d2 < d || (d2 == d && c2 < c)) {
-                    d = d2;
-                    c = c2;
-                }
-            }
+            int c = cc; // (lanes 16 .. 63 repeat lanes 0 .. 15)
+            wave_argmin(d, c);
             if (lane == 0)
                 cq4[h] = c;
         }
