@@ -30,6 +30,31 @@
 namespace ada {
 namespace {
 
+// The encode's sequential norm of a key staged in LDS as floats (16-byte
+// aligned): squares summed in order in double, the slices read 32 dims
+// ahead of the adds so that only the adds form the chain.
+template <int D>
+__device__ __forceinline__ double seq_norm(const float *x)
+{
+    const float4 *xr = reinterpret_cast<const float4 *>(x);
+    double ss = 0.0;
+#pragma unroll
+    for (int j0 = 0; j0 < D / 4; j0 += 8) {
+        float4 xv[8];
+#pragma unroll
+        for (int j = 0; j < 8; j++)
+            xv[j] = xr[j0 + j];
+#pragma unroll
+        for (int j = 0; j < 8; j++) {
+            ss = ss + (double)xv[j].x * (double)xv[j].x;
+            ss = ss + (double)xv[j].y * (double)xv[j].y;
+            ss = ss + (double)xv[j].z * (double)xv[j].z;
+            ss = ss + (double)xv[j].w * (double)xv[j].w;
+        }
+    }
+    return sqrt(ss);
+}
+
 #pragma clang fp contract(off)
 
 // The tier the chain rule gives a state for slope threshold th (binary32,
@@ -69,7 +94,7 @@ __global__ __launch_bounds__(D / 8 * 64) void append_kernel(AppendArgs a)
     constexpr int G = D / 8;
     constexpr int NT = G * 64; // one wave per code group
     __shared__ double u[D];
-    __shared__ float xk[D];
+    __shared__ __align__(16) float xk[D];
     __shared__ double rn;
     __shared__ double d8s[G], d4s[G];
     __shared__ int c8s[G], c4s[G];
@@ -128,14 +153,8 @@ __global__ __launch_bounds__(D / 8 * 64) void append_kernel(AppendArgs a)
     if (tid < D)
         xk[tid] = f16_bits_to_f32(k[tid]);
     __syncthreads();
-    if (tid == 0) {
-        double ss = 0.0;
-        for (int j = 0; j < D; j++) {
-            const double x = (double)xk[j];
-            ss = ss + x * x;
-        }
-        rn = sqrt(ss);
-    }
+    if (tid == 0)
+        rn = seq_norm<D>(xk);
     __syncthreads();
     if (tid < D) {
         const double x = (double)xk[tid];
@@ -318,7 +337,7 @@ __global__ __launch_bounds__(256) void retier_demote_kernel(RetierArgs a)
 {
     constexpr int G = D / 8;
     __shared__ double u[kSlots][D];
-    __shared__ float xk[kSlots][D];
+    __shared__ __align__(16) float xk[kSlots][D];
     __shared__ double rn[kSlots];
     __shared__ int code[kSlots][G];
     __shared__ uint4 img4[page_bytes(D, 1) / 16];
@@ -347,14 +366,8 @@ __global__ __launch_bounds__(256) void retier_demote_kernel(RetierArgs a)
         xk[t][d] = f16_bits_to_f32(*reinterpret_cast<const uint16_t *>(old + row_off(t, d)));
     }
     __syncthreads();
-    if (tid < nv) {
-        double ss = 0.0;
-        for (int d = 0; d < D; d++) {
-            const double x = (double)xk[tid][d];
-            ss = ss + x * x;
-        }
-        rn[tid] = sqrt(ss);
-    }
+    if (tid < nv)
+        rn[tid] = seq_norm<D>(xk[tid]);
     __syncthreads();
     for (int k = tid; k < nv * D; k += 256) {
         const int t = k / D, d = k % D;

@@ -129,16 +129,25 @@ __device__ __forceinline__ double column_sum(double x)
 }
 
 // The defining norm of a staged key: squares summed in order, in double.
+// (The words are read 16 ahead of the adds, so that only the adds form the
+// chain.)
 template <int D>
 __device__ __forceinline__ double exact_norm(const uint32_t *row)
 {
     double ss = 0.0;
-    for (int c = 0; c < D / 2; c++) {
-        const uint32_t kw = row[c];
-        const double lo = (double)f16_bits_to_f32((uint16_t)(kw & 0xffff));
-        const double hi = (double)f16_bits_to_f32((uint16_t)(kw >> 16));
-        ss = ss + lo * lo;
-        ss = ss + hi * hi;
+#pragma unroll
+    for (int c0 = 0; c0 < D / 2; c0 += 16) {
+        uint32_t kw[16];
+#pragma unroll
+        for (int c = 0; c < 16; c++)
+            kw[c] = row[c0 + c];
+#pragma unroll
+        for (int c = 0; c < 16; c++) {
+            const double lo = (double)f16_bits_to_f32((uint16_t)(kw[c] & 0xffff));
+            const double hi = (double)f16_bits_to_f32((uint16_t)(kw[c] >> 16));
+            ss = ss + lo * lo;
+            ss = ss + hi * hi;
+        }
     }
     return sqrt(ss);
 }
