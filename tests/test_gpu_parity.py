@@ -337,6 +337,37 @@ def test_pack_ragged_protect_permuted_two_calls(D):
     _compare_caches(dc, hc, f"ragged D={D}")
 
 
+@pytest.mark.parametrize("D", [64, 128])
+def test_pack_arena_order_page_list_equals_host_built_identity_order(D):
+    """In arena order the page list is written on the device from the rows'
+    entries; with the identity permutation the host builds it.  Both give
+    the oracle's cache, over two calls (the second appends to every row)."""
+    cfg = small_workload(D=D, Hq=16, Hkv=8, S=3, T=100, seed=90 + D)
+    lens = np.array([333, 17, 0, 45, 160, 1])
+    case = make_case(cfg, lens=lens, mixes=[(2000, 6000, 9000), (0, 10000, 10000), (5000, 5000, 5000),
+                                            (10000, 10000, 10000), (0, 0, 6000), (0, 3000, 10000)])
+    flush(f"[pack] arena-order page list D={D}")
+    r, c8, c4 = oracle.encode(case["keys"], case["cb8"], case["cb4"])
+    N1 = 350
+    cu1, cu2 = np.array([0, 333, 350, 350], np.int32), np.array([0, 45, 205, 206], np.int32)
+    calls = [dict(cu=cu1, bp=case["bp"][:3], keys=case["keys"][:N1], values=case["values"][:N1], radius=r[:N1],
+                  codes8=c8[:N1], codes4=c4[:N1], scores=case["scores"][:N1]),
+             dict(cu=cu2, bp=case["bp"][3:], keys=case["keys"][N1:], values=case["values"][N1:], radius=r[N1:],
+                  codes8=c8[N1:], codes4=c4[N1:], scores=case["scores"][N1:],
+                  pos_base=np.array([333, 17, 0], np.int64))]
+    hc = oracle.HostCache(D, 8, 3, 64, 4 << 20)
+    for c in calls:
+        assert oracle.pack(hc, c["cu"], c["bp"], c["keys"], c["values"], c["radius"], c["codes8"], c["codes4"],
+                           c["scores"], pos_base=c.get("pos_base")) == 0
+    geom = geom_of(cfg)
+    _compare_caches(_gpu_pack_like(hc, geom, calls), hc, f"device page list D={D}")
+    ident = []
+    for c in calls:
+        n = oracle.num_pages_of_call(D, 8, c["cu"], c["bp"])
+        ident.append(dict(c, perm=np.arange(n, dtype=np.uint32)))
+    _compare_caches(_gpu_pack_like(hc, geom, ident), hc, f"host page list D={D}")
+
+
 def test_pack_llama_shape_t32k_full():
     cfg = synth.WORKLOADS[2]
     case = make_case(cfg)
