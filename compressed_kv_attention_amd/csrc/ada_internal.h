@@ -174,7 +174,7 @@ struct PackPage {
 struct PackPlan {
     const PackSeq *seqs;
     const PackRow *rows;
-    PackPage *pages;        // written by pack_rows when gen_pages is set
+    PackPage *pages;        // written by pack_rank when gen_pages is set
     const uint8_t *protect; // [N][Hkv] or null
     const uint8_t *tiers;   // [N][Hkv] given tiers (0-2 kept, other values dropped) or null
     int32_t *src;           // [n_pages][16]: flat (token, head) index a slot holds, or -1

@@ -10,10 +10,10 @@
 // is given (by the budget solver in rdr.hip).
 //
 // Kernels, in stream order:
-//   pack_rows    one block per row: advance num_pages and tier_tokens and,
-//                in arena order, write the row's page list (arena offset,
-//                page index, metadata of each new page);
-//   pack_rank    one 1024-thread block per row: radix-select the keys at the
+//   pack_rank    one 1024-thread block per row: advance num_pages and
+//                tier_tokens and, in arena order, write the row's page list
+//                (arena offset, page index, metadata of each new page);
+//                radix-select the keys at the
 //                three tier boundaries (8 passes of 8 bits over 64-bit keys,
 //                exact because keys are unique; skipped when the tiers are
 //                given), then walk the row in index
@@ -34,16 +34,19 @@ namespace {
 
 #pragma clang fp contract(off)
 
-__global__ __launch_bounds__(256) void pack_rows(PackPlan plan, PackCache cache)
+// A row's bookkeeping, done by its pack_rank block before the ranking:
+// advance num_pages and tier_tokens and, in arena order, write the row's
+// page list (its pages: tier 0, then 1, then 2, each tier's pages back to
+// back from the tier's first offset; all but a tier's last page full).
+__device__ __forceinline__ void row_setup(const PackPlan &plan, const PackCache &cache, const PackRow &rw,
+                                          int row, int tid, int nthreads)
 {
-    const int row = blockIdx.x;
-    const PackRow rw = plan.rows[row];
     int np[3], pages = 0;
     for (int k = 0; k < 3; k++) {
         np[k] = (rw.count[k] + kSlots - 1) / kSlots;
         pages += np[k];
     }
-    if (threadIdx.x == 0) {
+    if (tid == 0) {
         cache.num_pages[row] += pages;
         if (!plan.dense && cache.tier_tokens != nullptr)
             for (int k = 0; k < 3; k++)
@@ -51,10 +54,7 @@ __global__ __launch_bounds__(256) void pack_rows(PackPlan plan, PackCache cache)
     }
     if (!plan.gen_pages)
         return;
-    // The row's pages in arena order: tier 0, then 1, then 2, each tier's
-    // pages back to back from the tier's first offset; all but a tier's last
-    // page are full.
-    for (int q = threadIdx.x; q < pages; q += 256) {
+    for (int q = tid; q < pages; q += nthreads) {
         const int k = q < np[0] ? 0 : q < np[0] + np[1] ? 1 : 2;
         const int f = q - (k == 0 ? 0 : k == 1 ? np[0] : np[0] + np[1]);
         const int tier = plan.dense ? 3 : k;
@@ -83,7 +83,7 @@ __device__ __forceinline__ uint64_t rank_key(const PackPlan &plan, const PackDat
            (uint64_t)(0x7fffffffu - (uint32_t)i);
 }
 
-__global__ __launch_bounds__(1024) void pack_rank(PackPlan plan, PackData data)
+__global__ __launch_bounds__(1024) void pack_rank(PackPlan plan, PackData data, PackCache cache)
 {
     __shared__ uint32_t hist[3][256];
     __shared__ uint64_t prefix[3], mask[3], thr[3];
@@ -98,6 +98,7 @@ __global__ __launch_bounds__(1024) void pack_rank(PackPlan plan, PackData data)
     const PackRow rw = plan.rows[row];
     const int T = sq.len;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    row_setup(plan, cache, rw, row, tid, 1024);
 
     if (!plan.dense && plan.tiers == nullptr) {
         if (tid < 3) {
@@ -455,13 +456,9 @@ hipError_t launch_pack(const PackPlan &plan, const PackData &data, const PackCac
                        hipStream_t st)
 {
     const int rows = plan.S * plan.Hkv;
-    if (rows > 0) {
-        hipLaunchKernelGGL(pack_rows, dim3(rows), dim3(256), 0, st, plan, cache);
-        if (hipError_t e = hipGetLastError(); e != hipSuccess)
-            return e;
-    }
+    // (with no tokens there are no pages, and the counters do not move)
     if (plan.n_tokens > 0 && rows > 0) {
-        hipLaunchKernelGGL(pack_rank, dim3(rows), dim3(1024), 0, st, plan, data);
+        hipLaunchKernelGGL(pack_rank, dim3(rows), dim3(1024), 0, st, plan, data, cache);
         if (hipError_t e = hipGetLastError(); e != hipSuccess)
             return e;
     }
