@@ -344,7 +344,22 @@ __global__ __launch_bounds__(256) void tier_counts_kernel(int Hkv, const int32_t
     const int row = blockIdx.x, s = row / Hkv, h = row % Hkv;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     int c[3] = {0, 0, 0};
-    for (int64_t t = (int64_t)cu[s] + tid; t < cu[s + 1]; t += 256) {
+    // eight tokens per thread per round, their loads issued together
+    const int64_t t0 = cu[s], t1 = cu[s + 1];
+    int64_t t = t0 + tid;
+    for (; t + 7 * 256 < t1; t += 8 * 256) {
+        int v[8];
+#pragma unroll
+        for (int j = 0; j < 8; j++)
+            v[j] = tiers[(t + j * 256) * Hkv + h];
+#pragma unroll
+        for (int j = 0; j < 8; j++) {
+            c[0] += v[j] == 0;
+            c[1] += v[j] == 1;
+            c[2] += v[j] == 2;
+        }
+    }
+    for (; t < t1; t += 256) {
         const int v = tiers[t * Hkv + h];
         c[0] += v == 0;
         c[1] += v == 1;
