@@ -58,7 +58,7 @@ def lib():
         L.oracle_pack_tiers.restype = I
         L.oracle_append.argtypes = [I, I, I, P, P, P, P, P, P, P, P, P, U64, P, P, P, P, P, P, I, P, P, P]
         L.oracle_append.restype = I
-        L.oracle_retier.argtypes = [I, I, I, P, P, P, P, P, P, U64, P, P, P, P, P, P, I, P, P]
+        L.oracle_retier.argtypes = [I, I, I, I, P, P, P, P, P, P, U64, P, P, P, P, P, P, I, P, P]
         L.oracle_retier.restype = I
         L.oracle_retier_plan.argtypes = [I, I, I, P, P, P, I, I, I, P, P, P]
         L.oracle_retier_plan.restype = I
@@ -303,7 +303,7 @@ def retier(cache: HostCache, cb8, cb4, rows, pages, target, open_page) -> int:
     t = np.ascontiguousarray(target, np.uint8)
     c8, c4 = _np(cb8, np.float32), _np(cb4, np.float32)
     status = np.zeros(1, np.int32)
-    rc = lib().oracle_retier(cache.D, cache.Hkv, len(r), _p(r), _p(p), _p(t), _p(c8), _p(c4), _p(cache.arena),
+    rc = lib().oracle_retier(cache.D, cache.Hkv, cache.S, len(r), _p(r), _p(p), _p(t), _p(c8), _p(c4), _p(cache.arena),
                              cache.arena_units, _p(cache.cursor), _p(cache.page_table), _p(cache.page_meta),
                              _p(cache.num_pages), _p(cache.tier_tokens), _p(cache.slot_token), cache.maxp,
                              _p(open_page), _p(status))

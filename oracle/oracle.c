@@ -1002,9 +1002,12 @@ int oracle_append(int D, int Hkv, int S, const uint16_t *keys, const uint16_t *v
 /*   the result written to new arena space and the page-table entry pointed  */
 /*   at it (same index, same slots, same slot positions); any page can be    */
 /*   evicted: per row, in descending page index, the row's last page moves   */
-/*   into the evicted page's place.  Demotions run before evictions.  A page */
-/*   that is not fp16 (demotion) or not in use sets status bit 4 and is       */
-/*   skipped; no arena space sets bit 2.                                      */
+/*   into the evicted page's place.  Demotions run before evictions.  An     */
+/*   entry that cannot apply -- a row outside the cache, a page not in use, a */
+/*   demotion of a page that is not fp16, an eviction of a tier-3 page (the   */
+/*   dense comparison format, which has no per-tier count), or a target      */
+/*   other than 1-3 -- sets status bit 4 and is skipped; no arena space sets */
+/*   bit 2.                                                                   */
 /*   policy -- stored pages keep no utility scores, so age stands in for     */
 /*   utility: while a sequence's page bytes exceed its budget, its oldest    */
 /*   full fp16 page (lowest page index, then lowest head) is demoted to the  */
@@ -1020,20 +1023,28 @@ static void read_key_value(int D, const uint8_t *page, int t, uint16_t *k, uint1
     }
 }
 
-int oracle_retier(int D, int Hkv, int n, const int32_t *rows, const int32_t *pages, const uint8_t *target,
-                  const float *cb8, const float *cb4, uint8_t *arena, uint64_t arena_units, uint64_t *cursor,
-                  uint32_t *page_table, uint8_t *page_meta, int32_t *num_pages, int32_t *tier_tokens,
-                  int32_t *slot_token, int maxp, int32_t *open_page, int32_t *status)
+int oracle_retier(int D, int Hkv, int S, int n, const int32_t *rows, const int32_t *pages,
+                  const uint8_t *target, const float *cb8, const float *cb4, uint8_t *arena,
+                  uint64_t arena_units, uint64_t *cursor, uint32_t *page_table, uint8_t *page_meta,
+                  int32_t *num_pages, int32_t *tier_tokens, int32_t *slot_token, int maxp,
+                  int32_t *open_page, int32_t *status)
 {
-    if ((D != 64 && D != 128) || Hkv <= 0 || n < 0)
+    if ((D != 64 && D != 128) || Hkv <= 0 || S < 0 || n < 0)
         return OR_EINVAL;
     int G = D / 8;
+    int64_t nrows = (int64_t)S * Hkv;
+    /* entries that can never apply */
+    for (int i = 0; i < n; i++)
+        if (target[i] < 1 || target[i] > 3 || rows[i] < 0 || rows[i] >= nrows)
+            *status |= 4;
     /* demotions, in list order */
     for (int i = 0; i < n; i++) {
         if (target[i] != 1 && target[i] != 2)
             continue;
         int32_t row = rows[i], p = pages[i];
         int tier = target[i], h = row % Hkv;
+        if (row < 0 || row >= nrows)
+            continue;
         if (p < 0 || p >= num_pages[row] || (page_meta[(int64_t)row * maxp + p] & 3) != 0) {
             *status |= 4;
             continue;
@@ -1070,6 +1081,8 @@ int oracle_retier(int D, int Hkv, int n, const int32_t *rows, const int32_t *pag
         if (target[i] != 3)
             continue;
         int32_t row = rows[i];
+        if (row < 0 || row >= nrows)
+            continue;
         int seen = 0;
         for (int j = 0; j < i; j++)
             seen |= target[j] == 3 && rows[j] == row;
@@ -1092,6 +1105,10 @@ int oracle_retier(int D, int Hkv, int n, const int32_t *rows, const int32_t *pag
                 continue;
             }
             uint8_t meta = page_meta[(int64_t)row * maxp + p];
+            if ((meta & 3) == 3) { /* a dense comparison page: no tier count */
+                *status |= 4;
+                continue;
+            }
             tier_tokens[row * 3 + (meta & 3)] -= ((meta >> 2) & 15) + 1;
             for (int t = 0; t < 3; t++)
                 if (open_page[row * 3 + t] == p + 1)

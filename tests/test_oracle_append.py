@@ -179,3 +179,35 @@ def test_retier_plan_brings_sequences_under_budget_oldest_first():
     now = sum(oracle.page_bytes(128, int(hc.page_meta[r, p]) & 3) for r in (2, 3) for p in range(hc.num_pages[r]))
     assert now <= budgets[1]
     assert len(oracle.retier_plan(hc, budgets)[0]) == 0
+
+
+def test_retier_entries_that_cannot_apply_set_bit4_and_change_nothing():
+    """A dense comparison page (tier 3) has no tier count, so it is not
+    evicted; rows outside the cache and unknown targets are skipped too.
+    Each sets status bit 4 and leaves every table, count and byte as it was."""
+    cfg = small_workload(D=64, Hq=2, Hkv=2, S=1, T=50, seed=47)
+    case = make_case(cfg, lens=[50])
+    hc = oracle.HostCache(64, 2, 1, 8, 1 << 20)
+    assert oracle.dense_pack(hc, case["cu"], case["keys"], case["values"]) == 0
+    tt0 = np.array([[50, 0, 0], [50, 0, 0]], np.int32)
+    hc.tier_tokens[:] = tt0  # (a dense cache keeps no counts; any values must stay)
+    snap = (hc.page_table.copy(), hc.page_meta.copy(), hc.num_pages.copy(), hc.arena.copy(),
+            hc.tier_tokens.copy(), hc.cursor.copy())
+    open_page = np.zeros((2, 3), np.int32)
+    for rows, pages, tgt in (([0], [1], [3]),        # evict a tier-3 page
+                             ([1], [0], [1]),        # demote a tier-3 page
+                             ([2], [0], [3]),        # row past the cache
+                             ([-1], [0], [2]),       # negative row
+                             ([0], [0], [0]),        # unknown target
+                             ([0], [0], [4])):
+        assert oracle.retier(hc, case["cb8"], case["cb4"], rows, pages, tgt, open_page) == 4
+        for a, b in zip(snap, (hc.page_table, hc.page_meta, hc.num_pages, hc.arena, hc.tier_tokens,
+                               hc.cursor)):
+            assert np.array_equal(a, b)
+    # a valid entry beside a bad one still applies
+    cfg2 = small_workload(D=64, Hq=2, Hkv=2, S=1, T=64, seed=48)
+    case2 = make_case(cfg2, lens=[64])
+    coded = _packed(case2, cfg2, np.full((64, 2), 1, np.uint8))
+    n0 = coded.num_pages.copy()
+    st = oracle.retier(coded, case2["cb8"], case2["cb4"], [5, 1], [0, 0], [3, 3], np.zeros((2, 3), np.int32))
+    assert st == 4 and coded.num_pages[1] == n0[1] - 1 and coded.num_pages[0] == n0[0]
