@@ -157,9 +157,19 @@ def kernel_event_ms(step_fns, n):
     return float(np.median(ts)), float(np.mean(ts))
 
 
+def cpu_threads():
+    """Threads the oracle runs on: the cores this process may use (its CPU
+    affinity), capped by OMP_NUM_THREADS where the machine sets it."""
+    n = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else (os.cpu_count() or 1)
+    cap = os.environ.get("OMP_NUM_THREADS", "")
+    return max(1, min(n, int(cap))) if cap.isdigit() and int(cap) > 0 else max(1, n)
+
+
 def cpu_baseline(cfg, layer, seconds_target=10.0):
     """The CPU oracle (test infrastructure) timed on this host on a bounded
-    sample: whole decode steps of the same workload on oracle-built pages."""
+    sample: whole decode steps of the same workload on oracle-built pages,
+    on every usable core and on one, plus oracle encode of the workload's
+    keys and of the 32-layer workload's 512-token append chunk (one layer)."""
     sys.path.insert(0, os.path.join(ROOT, "tests"))
     import oracle
     lens = synth.seq_lens(cfg)
@@ -172,29 +182,45 @@ def cpu_baseline(cfg, layer, seconds_target=10.0):
     scores = synth.scores(cfg, layer, N)
     q = synth.queries(cfg, layer)
     cb8, cb4 = synth.codebooks(cfg, layer)
-    threads = min(os.cpu_count() or 1, 16)
+    threads = cpu_threads()
+    t0 = time.perf_counter()
     r, c8, c4 = oracle.encode(keys, cb8, cb4, nthreads=threads)
+    t_enc = time.perf_counter() - t0
     hc = oracle.HostCache(cfg.head_dim, cfg.num_kv_heads, cfg.num_seqs, int(max(lens)) // 16 + 4,
                           N * cfg.num_kv_heads * 512 + (1 << 20), slot_tokens=False)
     assert oracle.pack(hc, cu, synth.tier_mix(cfg), keys, vals, r, c8, c4, scores) == 0
     units = cfg.num_seqs * cfg.num_q_heads
-    threads = min(threads, units)
+    dthreads = min(threads, units)
     reps, t = 0, 0.0
     res = None
     while t < seconds_target and reps < 50:
         t0 = time.perf_counter()
-        res = oracle.decode(hc, cb8, cb4, q, cfg.sigma, nthreads=threads)
+        res = oracle.decode(hc, cb8, cb4, q, cfg.sigma, nthreads=dthreads)
         t += time.perf_counter() - t0
         reps += 1
-    # one thread, on the first query head's share of the step
+    # one thread, one whole step
     t0 = time.perf_counter()
-    oracle.decode(hc, cb8, cb4, q, cfg.sigma, units=(0, 1), nthreads=1)
+    oracle.decode(hc, cb8, cb4, q, cfg.sigma, nthreads=1)
     t1 = time.perf_counter() - t0
+    # encode of one layer's append chunk of the 32-layer workload
+    c5 = synth.WORKLOADS[5]
+    na = c5.num_seqs * c5.append_tokens
+    ak = synth.keys(c5, 0, na, stream="k-append")
+    a8, a4 = synth.codebooks(c5, 0)
+    t0 = time.perf_counter()
+    oracle.encode(ak, a8, a4, nthreads=threads)
+    t_app = time.perf_counter() - t0
     tokens = int(lens.sum())
-    return dict(value=tokens * reps / t, unit="KV tokens/s", cores=threads, kind="oracle",
+    return dict(value=tokens * reps / t, unit="KV tokens/s", cores=dthreads, kind="oracle",
+                host_logical_cpus=os.cpu_count(), usable_cpus=threads,
                 sample=f"{reps} whole decode steps of the workload (all {units} query heads, "
-                       f"T={tokens}), double precision, {threads} threads",
-                single_thread_value=tokens / (t1 * units)), res
+                       f"T={tokens}), double precision, {dthreads} threads",
+                single_thread_value=tokens / t1,
+                encode_token_heads_per_s=N * cfg.num_kv_heads / t_enc,
+                encode_seconds=t_enc,
+                append_chunk_encode_seconds=t_app,
+                append_chunk=f"{c5.name}: {c5.append_tokens} tokens x {c5.num_seqs} sequences x "
+                             f"{c5.num_kv_heads} heads, one layer, {threads} threads"), res
 
 
 def append_path(dev, reps=20):
@@ -429,13 +455,14 @@ def multi_layer(cfg, layers, dev, steps, warmup, eager):
     geom = Ls[0]["geom"]
     S, Hq, D = cfg.num_seqs, cfg.num_q_heads, cfg.head_dim
     maxp = max(L["cache"].maxp for L in Ls)
-    out = torch.empty((S, Hq, D), device=dev)
-    lse = torch.empty((S, Hq), device=dev)
+    outs = [torch.empty((S, Hq, D), device=dev) for _ in Ls]
+    lses = [torch.empty((S, Hq), device=dev) for _ in Ls]
+    out, lse = outs[0], lses[0]
     ws = torch.zeros(ada.decode_workspace_size(geom, S, maxp, 0), dtype=torch.uint8, device=dev)
 
     def step():
-        for L in Ls:
-            ada.decode(geom, L["cache"], L["cb8"], L["cb4"], L["q"], cfg.sigma, out, lse, ws=ws)
+        for L, o, l in zip(Ls, outs, lses):
+            ada.decode(geom, L["cache"], L["cb8"], L["cb4"], L["q"], cfg.sigma, o, l, ws=ws)
 
     timer = time_eager if eager else time_graph
     n, _, ms = timer([step], steps, warmup)
@@ -472,6 +499,79 @@ def multi_layer(cfg, layers, dev, steps, warmup, eager):
     }
 
 
+def measure_step(cfg, L, args, out, lse, ws, timer):
+    """Times whole decode steps of one built layer (graph replays over rotated
+    arena copies) and the page-stream kernel alone (events around
+    back-to-back launches on its stream)."""
+    geom, cache = L["geom"], L["cache"]
+    S, Hq, D = cfg.num_seqs, cfg.num_q_heads, cfg.head_dim
+    used = cache.used_bytes()
+    n_copies = max(2, math.ceil(ROTATE_BYTES / max(used, 1)) + 1)
+    arenas = [cache.arena] + [cache.arena.clone() for _ in range(n_copies - 1)]
+    views = [cache.view(a) for a in arenas]
+    splits = args.splits or ada.decode_default_splits(geom, S, cache.maxp)
+
+    def make_step(v):
+        return lambda: ada.decode(geom, cache, L["cb8"], L["cb4"], L["q"], cfg.sigma, out, lse,
+                                  num_splits=args.splits, ws=ws, view=v)
+
+    fns = [make_step(v) for v in views]
+    log(f"{cfg.name}: stored {used / 1e6:.2f} MB in {int(cache.num_pages_host.sum())} pages; "
+        f"{n_copies} arena copies; {splits} splits per row")
+    steps, _, ms_graph = timer(fns, args.steps, args.warmup)
+    tokens = int(L["lens"].sum())
+    alg = algorithmic_bytes(L, cfg)
+
+    def make_stream(v):
+        return lambda: ada.decode_stage("stream", geom, cache, L["cb8"], L["cb4"], L["q"], cfg.sigma,
+                                        out, lse, num_splits=args.splits, ws=ws, view=v)
+
+    sfns = [make_stream(v) for v in views]
+    k_mean = batch_event_ms(sfns, max(200, 4 * n_copies))
+    k_med, _ = kernel_event_ms(sfns, max(50, 2 * n_copies))
+    sbytes = stream_bytes(L)
+    achieved = sbytes / (k_mean / 1e3) / 1e9
+    kernel_name = f"decode_main<{D},{Hq // cfg.num_kv_heads},false>"
+    traffic = profiled_traffic(kernel_name, cfg.name)
+    log(f"{cfg.name}: step {ms_graph * 1e3:.2f} us (graph); page stream {k_mean * 1e3:.2f} us mean of "
+        f"back-to-back launches, {k_med * 1e3:.2f} us median single launch (events), {achieved:.0f} GB/s")
+    return {
+        "value": tokens / (ms_graph / 1e3), "unit": "KV tokens/s", "steps": steps, "ms_per_step": ms_graph,
+        "config": {"workload": cfg.name, "num_seqs": S, "seq_len": int(L["lens"].max()),
+                   "tokens_per_step": tokens, "num_q_heads": Hq, "num_kv_heads": cfg.num_kv_heads,
+                   "head_dim": D, "tier_cum_bp": list(map(int, synth.tier_mix(cfg)[0])),
+                   "splits": splits, "arena_copies": n_copies},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
+                     "kernel": kernel_name, "kernel_us_mean": k_mean * 1e3,
+                     "kernel_us_median_single_launch": k_med * 1e3, "bytes_per_launch": sbytes},
+        "step_roofline": {"bytes_per_step": alg, "achieved_GBs": alg / (ms_graph / 1e3) / 1e9,
+                          "frac": alg / (ms_graph / 1e3) / 1e9 / HBM_PEAK_GBS},
+        "stored_bytes": used,
+        "stored_fraction_of_dense": used / (tokens * cfg.num_kv_heads * 4 * D),
+        "_views": views,
+    }
+
+
+def second_context_length(number, dev, args, timer):
+    """The same measurement on a second workload (the long-context batch by
+    default), reported beside the headline in the same line."""
+    cfg = synth.WORKLOADS[number]
+    log(f"workload {cfg.number} {cfg.name}: building cache on the GPU")
+    L = build_layer(cfg, 0, dev)
+    S, Hq, D = cfg.num_seqs, cfg.num_q_heads, cfg.head_dim
+    out = torch.empty((S, Hq, D), device=dev)
+    lse = torch.empty((S, Hq), device=dev)
+    ws = torch.zeros(ada.decode_workspace_size(L["geom"], S, L["cache"].maxp, args.splits),
+                     dtype=torch.uint8, device=dev)
+    m = measure_step(cfg, L, args, out, lse, ws, timer)
+    m.pop("_views")
+    del L
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return m
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -490,6 +590,10 @@ def main():
                     help="also time the budget solver over the whole workload")
     ap.add_argument("--eager", action="store_true",
                     help="time eager launches instead of graph replays (for profilers)")
+    ap.add_argument("--second-workload", type=int, default=3,
+                    help="workload measured beside the headline in the same line (0 = none): "
+                         "by default the 4 x 131072-token batch, the other context length the "
+                         "metric is quoted at")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="run one device-to-device copy of this size first (counter calibration)")
     args = ap.parse_args()
@@ -519,52 +623,22 @@ def main():
     log(f"workload {cfg.number} {cfg.name}: building cache on the GPU")
     L = build_layer(cfg, 0, dev, dense=not args.no_dense)
     geom, cache = L["geom"], L["cache"]
-    used = cache.used_bytes()
-    n_copies = max(2, math.ceil(ROTATE_BYTES / max(used, 1)) + 1)
-    arenas = [cache.arena] + [cache.arena.clone() for _ in range(n_copies - 1)]
-    views = [cache.view(a) for a in arenas]
     S, Hq, D = cfg.num_seqs, cfg.num_q_heads, cfg.head_dim
     out = torch.empty((S, Hq, D), device=dev)
     lse = torch.empty((S, Hq), device=dev)
     ws = torch.zeros(ada.decode_workspace_size(geom, S, cache.maxp, args.splits), dtype=torch.uint8,
                      device=dev)
-    splits = args.splits or ada.decode_default_splits(geom, S, cache.maxp)
-
-    def make_step(v):
-        return lambda: ada.decode(geom, cache, L["cb8"], L["cb4"], L["q"], cfg.sigma, out, lse,
-                                  num_splits=args.splits, ws=ws, view=v)
-
-    fns = [make_step(v) for v in views]
-    log(f"stored {used / 1e6:.2f} MB in {int(cache.num_pages_host.sum())} pages; "
-        f"{n_copies} arena copies; {splits} splits per row")
     timer = time_eager if args.eager else time_graph
-    steps, wall, ms_graph = timer(fns, args.steps, args.warmup)
-    tokens = int(L["lens"].sum())
-    value = tokens / (ms_graph / 1e3)
-    alg = algorithmic_bytes(L, cfg)
-
-    # dominant kernel: the page stream alone, events around back-to-back
-    # launches on the stream it is launched on
-    def make_stream(v):
-        return lambda: ada.decode_stage("stream", geom, cache, L["cb8"], L["cb4"], L["q"], cfg.sigma,
-                                        out, lse, num_splits=args.splits, ws=ws, view=v)
-
-    sfns = [make_stream(v) for v in views]
-    k_mean = batch_event_ms(sfns, max(200, 4 * n_copies))
-    k_med, _ = kernel_event_ms(sfns, max(50, 2 * n_copies))
-    sbytes = stream_bytes(L)
-    achieved = sbytes / (k_mean / 1e3) / 1e9
-    kernel_name = f"decode_main<{D},{Hq // cfg.num_kv_heads},false>"
-    traffic = profiled_traffic(kernel_name, cfg.name)
-    log(f"step {ms_graph * 1e3:.2f} us (graph); page stream {k_mean * 1e3:.2f} us mean of back-to-back "
-        f"launches, {k_med * 1e3:.2f} us median single launch (events), {achieved:.0f} GB/s")
-
+    m = measure_step(cfg, L, args, out, lse, ws, timer)
+    views, n_copies = m.pop("_views"), m["config"]["arena_copies"]
+    tokens = m["config"]["tokens_per_step"]
+    ms_graph = m["ms_per_step"]
     result = {
         "metric": "ADA decode KV tokens/s per step",
-        "value": value,
+        "value": m["value"],
         "unit": "KV tokens/s",
         "n_gpus": 1,
-        "steps": steps,
+        "steps": m["steps"],
         "warmup": args.warmup,
         "ms_per_step": ms_graph,
         "higher_is_better": True,
@@ -572,18 +646,11 @@ def main():
         "vs_baseline": None,
         "dtype": "fp32",
         "data": "synthetic",
-        "config": {"workload": cfg.name, "num_seqs": S, "seq_len": int(L["lens"].max()),
-                   "tokens_per_step": tokens, "num_q_heads": Hq, "num_kv_heads": cfg.num_kv_heads,
-                   "head_dim": D, "tier_cum_bp": list(map(int, synth.tier_mix(cfg)[0])),
-                   "splits": splits, "arena_copies": n_copies},
-        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
-                     "kernel": kernel_name, "kernel_us_mean": k_mean * 1e3,
-                     "kernel_us_median_single_launch": k_med * 1e3, "bytes_per_launch": sbytes},
-        "step_roofline": {"bytes_per_step": alg, "achieved_GBs": alg / (ms_graph / 1e3) / 1e9,
-                          "frac": alg / (ms_graph / 1e3) / 1e9 / HBM_PEAK_GBS},
-        "stored_bytes": used,
-        "stored_fraction_of_dense": used / (tokens * cfg.num_kv_heads * 4 * cfg.head_dim),
+        "config": m["config"],
+        "roofline": m["roofline"],
+        "step_roofline": m["step_roofline"],
+        "stored_bytes": m["stored_bytes"],
+        "stored_fraction_of_dense": m["stored_fraction_of_dense"],
     }
     if "dense" in L:
         dc = L["dense"]
@@ -629,6 +696,14 @@ def main():
         log(f"budget solver over the workload: code error {sf['code_error_us']:.1f} us, "
             f"solve {sf['solve_us']:.1f} us, counts {sf['tier_counts_us']:.1f} us, "
             f"pack {sf['pack_tiers_us']:.1f} us; mix {sf['tier_mix']}")
+    if args.second_workload and args.second_workload != args.workload:
+        del views
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+        m2 = second_context_length(args.second_workload, dev, args, timer)
+        result["second_workload"] = m2
+        log(f"{m2['config']['workload']}: {m2['value'] / 1e9:.3f} G tokens/s, stream "
+            f"{m2['roofline']['frac']:.3f} of peak, step {m2['step_roofline']['frac']:.3f}")
     # numerics check of the timed outputs against the oracle (CPU baseline leg)
     if not args.no_cpu_baseline:
         cb = cpu_baseline(cfg, 0)

@@ -61,13 +61,21 @@ def lib_path() -> str:
 
 
 def load():
-    """Loads libada.so once; raises if it is not built."""
+    """Loads libada.so once; raises if it is not built, or if it was built
+    from other sources than the ones beside it (a stale library)."""
     global _lib
     if _lib is None:
         if not os.path.exists(_LIB_PATH):
             raise ImportError(f"{_LIB_PATH} is missing: build it with "
                               "`python -m compressed_kv_attention_amd.build`")
         L = C.CDLL(_LIB_PATH)
+        L.ada_build_id.restype = C.c_char_p
+        from .build import source_digest
+        built, now = L.ada_build_id().decode(), source_digest()
+        if built != now:
+            raise ImportError(f"{_LIB_PATH} is stale: built from sources {built[:16]}, the sources "
+                              f"are now {now[:16]}; rebuild with "
+                              "`python -m compressed_kv_attention_amd.build`")
         P, I32, I64, U64, SZ, F = C.c_void_p, C.c_int32, C.c_int64, C.c_uint64, C.c_size_t, C.c_float
         G = C.POINTER(Geom)
         CV = C.POINTER(_CacheView)
@@ -239,10 +247,17 @@ def pack_workspace_size(geom: Geom, n_tokens: int, num_seqs: int) -> int:
     return int(load().rdr_pack_workspace_size(C.byref(geom), n_tokens, num_seqs))
 
 
-def _workspace(nbytes: int, device) -> torch.Tensor:
+def _workspace(nbytes: int, device, stream=None) -> torch.Tensor:
+    """A workspace for a call enqueued on `stream` (None = the current
+    stream).  It is allocated, and zero-filled, on that stream, so torch's
+    caching allocator orders any reuse of its memory after the call even if
+    the caller drops the tensor while the call still runs."""
     # (every entry point writes what it reads; zero-filled only so that a
     # workspace never holds stale data from elsewhere)
-    return torch.zeros(max(256, nbytes), dtype=torch.uint8, device=device)
+    if stream is None:
+        return torch.zeros(max(256, nbytes), dtype=torch.uint8, device=device)
+    with torch.cuda.stream(stream):
+        return torch.zeros(max(256, nbytes), dtype=torch.uint8, device=device)
 
 
 def rdr_pack(geom: Geom, cache: Cache, cu_tokens, tier_cum_bp, keys, values, radius, codes8, codes4,
@@ -256,7 +271,7 @@ def rdr_pack(geom: Geom, cache: Cache, cu_tokens, tier_cum_bp, keys, values, rad
     pp, ppp = _host(place_perm, np.uint32, "place_perm")
     pb, pbp = _host(pos_base, np.int64, "pos_base")
     if ws is None:
-        ws = _workspace(pack_workspace_size(geom, n, len(cu) - 1), cache.arena.device)
+        ws = _workspace(pack_workspace_size(geom, n, len(cu) - 1), cache.arena.device, stream)
     view = cache.view()
     st = load().rdr_pack(
         C.byref(geom), C.byref(view), len(cu) - 1, cup, bpp,
@@ -309,7 +324,7 @@ def rdr_solve(geom: Geom, cu_tokens, budget_bytes, radius, err8, err4, scores, t
         if tuple(t.shape) != (n, H):
             raise ValueError(f"{name} shape {tuple(t.shape)} != {(n, H)}")
     if ws is None:
-        ws = _workspace(solve_workspace_size(geom, len(cu) - 1, n), tiers.device)
+        ws = _workspace(solve_workspace_size(geom, len(cu) - 1, n), tiers.device, stream)
     st = load().rdr_solve(C.byref(geom), len(cu) - 1, cup, budp,
                           _dev(radius, "radius", (torch.float16, torch.int16)),
                           _dev(err8, "err8", (torch.float32,)), _dev(err4, "err4", (torch.float32,)),
@@ -330,17 +345,23 @@ class AppendState:
         self.cache = cache
         self.push_cursor()
 
-    def push_cursor(self):
-        """Host cursor -> device (before appending after host-planned packs)."""
-        self.buf[:8].copy_(torch.from_numpy(self.cache.cursor.view(np.uint8).copy()))
+    def push_cursor(self, stream=None):
+        """Host cursor -> device (before appending after host-planned packs),
+        ordered on `stream` (None = the current stream)."""
+        src = torch.from_numpy(self.cache.cursor.view(np.uint8).copy())
+        with torch.cuda.stream(torch.cuda.current_stream() if stream is None else stream):
+            self.buf[:8].copy_(src)
 
-    def pull(self) -> int:
+    def pull(self, stream=None) -> int:
         """Device cursor and page counts -> the cache's host copies (before a
-        host-planned pack); returns the status bits.  Synchronizes."""
-        c = self.buf[:16].cpu().numpy()
+        host-planned pack), after the work enqueued on `stream` (None = the
+        current stream); returns the status bits.  Synchronizes that stream."""
+        with torch.cuda.stream(torch.cuda.current_stream() if stream is None else stream):
+            c = self.buf[:16].cpu().numpy()
+            rows = self.cache.num_pages_host.shape[0]
+            npg = self.cache.num_pages[:rows].cpu().numpy()
         self.cache.cursor[:] = c[:8].view(np.uint64)
-        rows = self.cache.num_pages_host.shape[0]
-        self.cache.num_pages_host[:] = self.cache.num_pages[:rows].cpu().numpy()
+        self.cache.num_pages_host[:] = npg
         return int(c[8:12].view(np.uint32)[0])
 
 
@@ -402,7 +423,7 @@ def tier_counts(geom: Geom, cu_tokens, tiers, stream=None) -> np.ndarray:
     # page-locked result buffer (from torch's caching host allocator): the
     # device-to-host copy then needs no staging
     out = torch.zeros((max(1, S * geom.num_kv_heads), 3), dtype=torch.int32, pin_memory=True)
-    ws = _workspace(int(load().rdr_tier_counts_workspace_size(C.byref(geom), S)), tiers.device)
+    ws = _workspace(int(load().rdr_tier_counts_workspace_size(C.byref(geom), S)), tiers.device, stream)
     st = load().rdr_tier_counts(C.byref(geom), S, cup, _dev(tiers, "tiers", (torch.uint8,)),
                                 C.c_void_p(out.data_ptr()), _dev(ws, "ws"), ws.numel(), _stream(stream))
     _check(st, "rdr_tier_counts")
@@ -429,7 +450,7 @@ def rdr_pack_tiers(geom: Geom, cache: Cache, cu_tokens, row_counts, tiers, keys,
     pp, ppp = _host(place_perm, np.uint32, "place_perm")
     pb, pbp = _host(pos_base, np.int64, "pos_base")
     if ws is None:
-        ws = _workspace(pack_workspace_size(geom, n, len(cu) - 1), cache.arena.device)
+        ws = _workspace(pack_workspace_size(geom, n, len(cu) - 1), cache.arena.device, stream)
     view = cache.view()
     st = load().rdr_pack_tiers(
         C.byref(geom), C.byref(view), len(cu) - 1, cup, rcp, _dev(tiers, "tiers", (torch.uint8,)),
@@ -446,7 +467,7 @@ def dense_pack(geom: Geom, cache: Cache, cu_tokens, keys, values, place_perm=Non
     n = int(cu[-1])
     pp, ppp = _host(place_perm, np.uint32, "place_perm")
     if ws is None:
-        ws = _workspace(pack_workspace_size(geom, n, len(cu) - 1), cache.arena.device)
+        ws = _workspace(pack_workspace_size(geom, n, len(cu) - 1), cache.arena.device, stream)
     view = cache.view()
     st = load().dense_pack(C.byref(geom), C.byref(view), len(cu) - 1, cup,
                            _dev(keys, "keys", (torch.float16,)), _dev(values, "values", (torch.bfloat16,)),
@@ -465,7 +486,7 @@ def decode_workspace_size(geom: Geom, num_seqs: int, max_pages_per_head: int, nu
     return int(load().ada_decode_workspace_size(C.byref(geom), num_seqs, max_pages_per_head, num_splits))
 
 
-def _decode_args(geom, cache, q, out, lse, logits, ws, num_splits):
+def _decode_args(geom, cache, q, out, lse, logits, ws, num_splits, stream=None):
     S, Hq, D = cache.num_seqs, geom.num_q_heads, geom.head_dim
     if tuple(q.shape) != (S, Hq, D) or tuple(out.shape) != (S, Hq, D):
         raise ValueError("q and out must be [S][Hq][D]")
@@ -474,7 +495,7 @@ def _decode_args(geom, cache, q, out, lse, logits, ws, num_splits):
     if logits is not None and tuple(logits.shape) != (S, Hq, cache.maxp * 16):
         raise ValueError("logits must be [S][Hq][max_pages_per_head*16]")
     if ws is None:
-        ws = _workspace(decode_workspace_size(geom, S, cache.maxp, num_splits), q.device)
+        ws = _workspace(decode_workspace_size(geom, S, cache.maxp, num_splits), q.device, stream)
     return ws
 
 
@@ -482,7 +503,7 @@ def decode(geom: Geom, cache: Cache, cb8, cb4, q, softmax_scale: float, out, lse
            num_splits: int = 0, ws=None, stream=None, view=None):
     """One ADA decode step (ada_decode).  `view` may pass a prebuilt
     cache.view(...) (e.g. with a rotated arena)."""
-    ws = _decode_args(geom, cache, q, out, lse, logits, ws, num_splits)
+    ws = _decode_args(geom, cache, q, out, lse, logits, ws, num_splits, stream)
     v = cache.view() if view is None else view
     st = load().ada_decode(C.byref(geom), C.byref(v), _dev(cb8, "cb8", (torch.float32,)),
                            _dev(cb4, "cb4", (torch.float32,)), _dev(q, "q", (torch.bfloat16,)),
@@ -501,8 +522,9 @@ def decode_sym(geom: Geom, cache: Cache, cb8, cb4, q, softmax_scale: float, out,
                num_splits: int = 0, ws=None, stream=None, view=None):
     """One decode step with the symmetric angle-code logit (ada_decode_sym)."""
     if ws is None:
-        ws = _workspace(decode_sym_workspace_size(geom, cache.num_seqs, cache.maxp, num_splits), q.device)
-    ws = _decode_args(geom, cache, q, out, lse, logits, ws, num_splits)
+        ws = _workspace(decode_sym_workspace_size(geom, cache.num_seqs, cache.maxp, num_splits), q.device,
+                        stream)
+    ws = _decode_args(geom, cache, q, out, lse, logits, ws, num_splits, stream)
     v = cache.view() if view is None else view
     st = load().ada_decode_sym(C.byref(geom), C.byref(v), _dev(cb8, "cb8", (torch.float32,)),
                                _dev(cb4, "cb4", (torch.float32,)), _dev(q, "q", (torch.bfloat16,)),
@@ -517,7 +539,7 @@ def decode_stage(stage: str, geom: Geom, cache: Cache, cb8, cb4, q, softmax_scal
                  lse=None, logits=None, num_splits: int = 0, ws=None, stream=None, view=None):
     """One stage of ada_decode: "stream" or "merge" (ada_decode_stream /
     ada_decode_merge).  The stages share `ws`."""
-    ws = _decode_args(geom, cache, q, out, lse, logits, ws, num_splits)
+    ws = _decode_args(geom, cache, q, out, lse, logits, ws, num_splits, stream)
     v = cache.view() if view is None else view
     L = load()
     g, cv = C.byref(geom), C.byref(v)
@@ -539,7 +561,7 @@ def decode_stage(stage: str, geom: Geom, cache: Cache, cb8, cb4, q, softmax_scal
 
 def dense_decode(geom: Geom, cache: Cache, q, softmax_scale: float, out, lse=None, logits=None,
                  num_splits: int = 0, ws=None, stream=None, view=None):
-    ws = _decode_args(geom, cache, q, out, lse, logits, ws, num_splits)
+    ws = _decode_args(geom, cache, q, out, lse, logits, ws, num_splits, stream)
     v = cache.view() if view is None else view
     st = load().dense_decode(C.byref(geom), C.byref(v), _dev(q, "q", (torch.bfloat16,)),
                              float(softmax_scale), _dev(out, "out", (torch.float32,)),

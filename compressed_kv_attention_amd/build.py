@@ -4,6 +4,7 @@
 """
 from __future__ import annotations
 
+import hashlib
 import os
 import subprocess
 import sys
@@ -28,12 +29,29 @@ FLAGS = [
 ]
 
 
+def source_digest() -> str:
+    """SHA-256 over the library's sources (every file under csrc/ and the
+    public header), names and contents, in name order.  The build stamps it
+    into the library (ada_build_id) so that a stale libada.so is refused at
+    load time."""
+    h = hashlib.sha256()
+    files = sorted(f for f in os.listdir(CSRC) if f.endswith((".hip", ".cpp", ".h")))
+    paths = [os.path.join(CSRC, f) for f in files] + [os.path.join(ROOT, "include", "ada.h")]
+    for path in paths:
+        h.update(os.path.basename(path).encode() + b"\0")
+        with open(path, "rb") as f:
+            h.update(f.read())
+        h.update(b"\0")
+    return h.hexdigest()
+
+
 def build(verbose: bool = False) -> str:
     os.makedirs(BUILD, exist_ok=True)
+    digest = source_digest()
 
     def compile_one(src: str) -> str:
         obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-        cmd = ["hipcc", *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+        cmd = ["hipcc", *FLAGS, f'-DADA_BUILD_ID="{digest}"', "-c", os.path.join(CSRC, src), "-o", obj]
         r = subprocess.run(cmd, capture_output=True, text=True)
         if r.returncode != 0:
             raise RuntimeError(f"hipcc failed for {src}:\n{r.stderr}")

@@ -382,6 +382,11 @@ const char *ada_status_str(int status)
 
 int ada_version(void) { return kVersion; }
 
+#ifndef ADA_BUILD_ID
+#define ADA_BUILD_ID "unknown"
+#endif
+const char *ada_build_id(void) { return ADA_BUILD_ID; }
+
 size_t ada_page_bytes(int32_t head_dim, int32_t tier)
 {
     if ((head_dim != 64 && head_dim != 128) || tier < 0 || tier > 3)
@@ -796,6 +801,7 @@ ada_status ada_retier(const ada_geom *geom, const ada_cache *cache, const float 
     a.n = n;
     a.maxp = cache->max_pages_per_head;
     a.Hkv = geom->num_kv_heads;
+    a.nrows = (int)nrows;
     return launch_retier(geom->head_dim, a, (int)nrows, as_stream(stream)) == hipSuccess ? ADA_OK : ADA_EHIP;
 }
 

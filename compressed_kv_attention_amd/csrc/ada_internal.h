@@ -144,7 +144,7 @@ struct RetierArgs {
     unsigned int *status;        // adds bit 4: a listed page could not be re-tiered
     int32_t *open;
     unsigned long long capacity;
-    int n, maxp, Hkv;
+    int n, maxp, Hkv, nrows;
 };
 hipError_t launch_retier(int D, const RetierArgs &a, int rows, hipStream_t st);
 

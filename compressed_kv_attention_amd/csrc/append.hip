@@ -345,9 +345,16 @@ __global__ __launch_bounds__(256) void retier_demote_kernel(RetierArgs a)
     __shared__ uint32_t off_s;
     const int i = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int tier = a.target[i];
-    if (tier != 1 && tier != 2)
-        return;
     const int row = a.rows[i], p = a.pages[i], h = row % a.Hkv;
+    // an entry that can never apply (unknown target, row outside the cache)
+    // is reported here, once; evictions of valid rows are the next kernel's
+    if (tier < 1 || tier > 3 || row < 0 || row >= a.nrows) {
+        if (tid == 0)
+            atomicOr(a.status, 4u);
+        return;
+    }
+    if (tier == 3)
+        return;
     if (tid == 0) {
         int go = p >= 0 && p < a.num_pages[row] && (a.page_meta[(size_t)row * a.maxp + p] & 3) == 0;
         if (!go)
@@ -500,6 +507,10 @@ __global__ __launch_bounds__(256) void retier_evict_kernel(RetierArgs a, int row
         }
         const size_t e = (size_t)row * a.maxp;
         const uint8_t meta = a.page_meta[e + p];
+        if ((meta & 3) == 3) { // a dense comparison page: it has no tier count
+            atomicOr(a.status, 4u);
+            continue;
+        }
         a.tier_tokens[row * 3 + (meta & 3)] -= ((meta >> 2) & 15) + 1;
         for (int t = 0; t < 3; t++)
             if (a.open[row * 3 + t] == p + 1)

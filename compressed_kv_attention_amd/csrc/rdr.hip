@@ -407,6 +407,8 @@ hipError_t launch_solve(const SolveArgs &a, hipStream_t st)
     hipLaunchKernelGGL(solve_zero, dim3((unsigned)((nh + 255) / 256)), dim3(256), 0, st, a, nh);
     if (hipError_t e = hipGetLastError(); e != hipSuccess)
         return e;
+    if (a.n_blocks == 0) // no states: the thresholds are all the call computes
+        return hipSuccess;
     const dim3 grid((unsigned)a.n_blocks), blk(kSolveThreads);
     hipLaunchKernelGGL(solve_pass<0>, grid, blk, 0, st, a);
     hipLaunchKernelGGL(solve_pass<1>, grid, blk, 0, st, a);

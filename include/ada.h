@@ -71,6 +71,11 @@ const char *ada_status_str(int status);
 /* Library version, major * 10000 + minor * 100 + patch. */
 int ada_version(void);
 
+/* Identity of the sources the library was built from: the hex SHA-256 that
+ * the build computes over them ("unknown" for a build that gave none).  A
+ * binding compares it with its own sources to refuse a stale library. */
+const char *ada_build_id(void);
+
 typedef struct {
     int32_t head_dim;     /* D: 64 or 128 */
     int32_t num_q_heads;  /* Hq */
@@ -345,8 +350,11 @@ ada_status ada_append(const ada_geom *geom, const ada_cache *cache, const float 
  *   - target 3 evicts a page: per row, in descending page index, the row's
  *     last page moves into its place.
  *   - Demotions run before evictions. Each page may be listed once.
- *   - A page that cannot be demoted (not fp16) or is not in use adds status
- *     bit 4. No arena space adds bit 2.
+ *   - An entry that cannot apply adds status bit 4 and is skipped: a row
+ *     outside the cache, a page not in use, a target other than 1-3, a
+ *     demotion of a page that is not fp16, or an eviction of a tier-3
+ *     (dense comparison) page, which has no tier count. No arena space adds
+ *     bit 2.
  *   - tier_tokens, num_pages and the open pages in `state` are kept
  *     current.
  *   rows, pages [n] int32 and target [n] u8 are DEVICE arrays (the call can

@@ -195,3 +195,15 @@ def test_decode_refuses_a_split_count_whose_tables_overflow_lds():
     ns = ada.decode_default_splits(g, 1, maxp)
     lut = 16 * 272 * 8 * 4
     assert lut + -(-maxp // ns) * 8 <= 160 * 1024 and ns <= 1024
+
+
+def test_load_refuses_a_stale_library(monkeypatch):
+    """The library carries the digest of the sources it was built from; a
+    binding whose sources have changed since refuses to load it."""
+    import compressed_kv_attention_amd as ada
+    import compressed_kv_attention_amd.build as b
+    assert ada.load().ada_build_id().decode() == b.source_digest()
+    monkeypatch.setattr(ada, "_lib", None)
+    monkeypatch.setattr(b, "source_digest", lambda: "0" * 64)
+    with pytest.raises(ImportError, match="stale"):
+        ada.load()

@@ -314,3 +314,186 @@ def test_single_row_gqa8_d128_t128k_lds_bound_splits():
     torch.cuda.synchronize()
     ref = oracle.decode(hc, case["cb8"], case["cb4"], case["q"], cfg.sigma, nthreads=NTHREADS)
     _check_outputs("gqa8 t128k", out, lse, ref, [0])
+
+
+# ---- every sequence, with the GPU's encode outputs fed to the oracle ---------
+# Pages, tables and outputs are compared for every sequence of a workload.
+# The oracle's pack and decode take the GPU's radii and codes (checked bit
+# for bit against the oracle's own encode on a seeded token sample first), as
+# both packs must see the same encode outputs; oracle encode of every token
+# of the large workloads would take minutes of CPU time.
+
+def _host_tables(dc):
+    return dict(npg=dc.num_pages.cpu().numpy(), pt=dc.page_table.cpu().numpy().view(np.uint32),
+                pm=dc.page_meta.cpu().numpy(), tt=dc.tier_tokens.cpu().numpy())
+
+
+def _tier_pages(units, pt_row, pm_row, D):
+    """The row's pages of each tier in page order, as [n][bytes] arrays."""
+    out = []
+    for k in range(3):
+        sel = (pm_row & 3) == k
+        u = ada.page_bytes(D, k) // 128
+        idx = pt_row[sel].astype(np.int64)[:, None] + np.arange(u)[None, :]
+        out.append(units[idx].reshape(len(idx), -1))
+    return out
+
+
+def _compare_rows_all(label, arena_g, tab, hc, pairs, D):
+    """Bit-exact pages, metadata and counts for (GPU row, oracle row) pairs,
+    each side's pages found through its own page table."""
+    A = arena_g[: len(arena_g) // 128 * 128].reshape(-1, 128)
+    B = hc.arena[: len(hc.arena) // 128 * 128].reshape(-1, 128)
+    for rg, ro in pairs:
+        n = int(hc.num_pages[ro])
+        assert int(tab["npg"][rg]) == n, f"{label}: row {rg} page count"
+        assert np.array_equal(tab["pm"][rg, :n], hc.page_meta[ro, :n]), f"{label}: row {rg} metadata"
+        assert np.array_equal(tab["tt"][rg], hc.tier_tokens[ro]), f"{label}: row {rg} tier counts"
+        ga = _tier_pages(A, tab["pt"][rg, :n], tab["pm"][rg, :n], D)
+        oa = _tier_pages(B, hc.page_table[ro, :n], hc.page_meta[ro, :n], D)
+        for k in range(3):
+            assert np.array_equal(ga[k], oa[k]), f"{label}: row {rg} tier-{k} page bytes differ"
+
+
+def _sample_codes(label, keys, r, c8, c4, cb8, cb4, n, seed):
+    N = keys.shape[0]
+    idx = np.sort(np.random.default_rng(seed).choice(N, min(n, N), replace=False))
+    it = torch.from_numpy(idx).cuda()
+    _check_codes(label + " token sample", r[it], c8[it], c4[it], keys[it].cpu(), cb8, cb4)
+
+
+def _oracle_chunk(label, cfg, layer, seqs, lens, bp, cu, keys, vals, scores, g_r, g_c8, g_c4, maxp):
+    """Oracle pack of sequences seqs (contiguous) from the GPU's codes."""
+    H, D = cfg.num_kv_heads, cfg.head_dim
+    a, b = int(cu[seqs[0]]), int(cu[seqs[-1] + 1])
+    lens_s, bp_s = lens[seqs], bp[seqs]
+    hc = oracle.HostCache(D, H, len(seqs), maxp, _stored_bytes(cfg, lens_s, bp_s) + 4096, slot_tokens=False)
+    rc = oracle.pack(hc, synth.cu_tokens(lens_s), bp_s, keys[a:b].cpu(), vals[a:b].cpu(), g_r[a:b], g_c8[a:b],
+                     g_c4[a:b], scores[a:b])
+    assert rc == 0, f"{label}: oracle pack {rc}"
+    return hc
+
+
+def _run_all_seqs(number, layer, chunk, logits_seq=None):
+    cfg = synth.WORKLOADS[number]
+    label = f"workload {number} all sequences"
+    H, D, S, Hq = cfg.num_kv_heads, cfg.head_dim, cfg.num_seqs, cfg.num_q_heads
+    geom = ada.Geom(D, Hq, H)
+    lens = synth.seq_lens(cfg)
+    cu = synth.cu_tokens(lens)
+    N = int(cu[-1])
+    bp = synth.tier_mix(cfg)
+    flush(f"[{label}] GPU encode + pack of {N} tokens x {H} heads, decode")
+    keys = synth.keys(cfg, layer, N, "cuda")
+    vals = synth.values(cfg, layer, N, "cuda")
+    scores = synth.scores(cfg, layer, N)
+    q = synth.queries(cfg, layer, "cuda")
+    cb8, cb4 = synth.codebooks(cfg, layer)
+    cb8d, cb4d = cb8.cuda(), cb4.cuda()
+    r, c8, c4 = _gpu_encode(geom, keys, cb8d, cb4d)
+    maxp = int(max(lens)) // 16 + 4
+    dc = ada.Cache(geom, S, maxp, _stored_bytes(cfg, lens, bp))
+    n_pages = ada.pack_num_pages(geom, cu, bp)
+    ada.rdr_pack(geom, dc, cu, bp, keys, vals, r, c8, c4, scores.cuda(),
+                 place_perm=synth.place_perm(cfg, layer, n_pages))
+    out = torch.full((S, Hq, D), float("nan"), device="cuda")
+    lse = torch.full((S, Hq), float("nan"), device="cuda")
+    lg = torch.full((S, Hq, maxp * 16), float("nan"), device="cuda") if logits_seq is not None else None
+    ada.decode(geom, dc, cb8d, cb4d, q, cfg.sigma, out, lse, logits=lg)
+    torch.cuda.synchronize()
+    _check_pool_tiling(label, dc, geom)
+    _sample_codes(label, keys, r, c8, c4, cb8, cb4, 4096, 100 + number)
+    arena_g = dc.arena.cpu().numpy()
+    tab = _host_tables(dc)
+    g_r, g_c8, g_c4 = u16(r), c8.cpu().numpy(), c4.cpu().numpy()
+    del r, c8, c4
+    worst = 0.0
+    for s0 in range(0, S, chunk):
+        seqs = list(range(s0, min(S, s0 + chunk)))
+        hc = _oracle_chunk(label, cfg, layer, seqs, lens, bp, cu, keys, vals, scores, g_r, g_c8, g_c4, maxp)
+        _compare_rows_all(label, arena_g, tab, hc, [(s * H + h, i * H + h) for i, s in enumerate(seqs)
+                                                    for h in range(H)], D)
+        want_lg = logits_seq is not None and logits_seq in seqs
+        ref = oracle.decode(hc, cb8, cb4, q[seqs].cpu(), cfg.sigma, nthreads=NTHREADS, logits=want_lg)
+        o = out[seqs].cpu().double().numpy()
+        err = float(np.abs(o - ref["out"]).max())
+        assert err <= OUT_TOL, f"{label}: sequences {seqs[0]}..{seqs[-1]} out max-abs {err:.3g}"
+        ls = lse[seqs].cpu().double().numpy()
+        assert (np.abs(ls - ref["lse"]) <= 1e-3 * np.maximum(np.abs(ref["lse"]), 1.0)).all(), f"{label}: lse"
+        worst = max(worst, err)
+        if want_lg:
+            from gpu_util import logit_tol_ok
+            i = seqs.index(logits_seq)
+            ok, rel = logit_tol_ok(lg[logits_seq].cpu().double().numpy(), ref["logits"][i])
+            assert ok, f"{label}: sequence {logits_seq} logits rel err {rel:.3g}"
+            flush(f"[{label}] logits of sequence {logits_seq} (all {Hq} heads, every retained slot): "
+                  f"max rel {rel:.2e}")
+        flush(f"[{label}] sequences {seqs[0]}..{seqs[-1]}: pages of {len(seqs) * H} rows bit-exact, "
+              f"out max-abs {err:.2e}")
+    flush(f"[{label}] all {S} sequences: out max-abs {worst:.2e}")
+
+
+def test_workload3_all_sequences_and_full_logits():
+    """Every sequence of the 4 x 131072 permuted pool, and the logits of every
+    retained slot of one sequence at full size."""
+    _run_all_seqs(3, 0, chunk=2, logits_seq=1)
+
+
+def test_workload4_all_64_sequences():
+    """Every one of the 64 ragged sequences: pages bit-exact and outputs."""
+    _run_all_seqs(4, 0, chunk=16)
+
+
+def test_workload5_four_layers_back_to_back():
+    """Several layers of the 32-layer workload, each with its own keys,
+    values, queries, codebooks and cache, decoded back to back on one stream
+    into separate outputs (the order the benchmark times them in); each
+    layer's outputs for a sampled sequence against the oracle."""
+    cfg = synth.WORKLOADS[5]
+    H, D, S, Hq = cfg.num_kv_heads, cfg.head_dim, cfg.num_seqs, cfg.num_q_heads
+    geom = ada.Geom(D, Hq, H)
+    lens = synth.seq_lens(cfg)
+    cu = synth.cu_tokens(lens)
+    N = int(cu[-1])
+    bp = synth.tier_mix(cfg)
+    maxp = int(max(lens)) // 16 + 4
+    layers = [0, 11, 22, 31]
+    built = []
+    for layer in layers:
+        label = f"workload 5 layer {layer}"
+        flush(f"[{label}] GPU encode + pack of {N} tokens x {H} heads")
+        keys = synth.keys(cfg, layer, N, "cuda")
+        vals = synth.values(cfg, layer, N, "cuda")
+        scores = synth.scores(cfg, layer, N)
+        cb8, cb4 = synth.codebooks(cfg, layer)
+        cb8d, cb4d = cb8.cuda(), cb4.cuda()
+        r, c8, c4 = _gpu_encode(geom, keys, cb8d, cb4d)
+        dc = ada.Cache(geom, S, maxp, _stored_bytes(cfg, lens, bp))
+        ada.rdr_pack(geom, dc, cu, bp, keys, vals, r, c8, c4, scores.cuda(),
+                     place_perm=synth.place_perm(cfg, layer, ada.pack_num_pages(geom, cu, bp)))
+        s = (3 * layer + 1) % S  # the layer's sampled sequence
+        a, b = int(cu[s]), int(cu[s + 1])
+        _sample_codes(label, keys[a:b], r[a:b], c8[a:b], c4[a:b], cb8, cb4, 1024, layer)
+        torch.cuda.synchronize()
+        built.append(dict(layer=layer, s=s, dc=dc, cb8=cb8, cb4=cb4, cb8d=cb8d, cb4d=cb4d,
+                          q=synth.queries(cfg, layer, "cuda"), k=keys[a:b].cpu(), v=vals[a:b].cpu(),
+                          sc=scores[a:b], r=u16(r[a:b]), c8=c8[a:b].cpu().numpy(),
+                          c4=c4[a:b].cpu().numpy()))
+        del keys, vals, r, c8, c4
+    outs = [torch.full((S, Hq, D), float("nan"), device="cuda") for _ in layers]
+    lses = [torch.full((S, Hq), float("nan"), device="cuda") for _ in layers]
+    ws = torch.zeros(ada.decode_workspace_size(geom, S, maxp, 0), dtype=torch.uint8, device="cuda")
+    flush(f"[workload 5] {len(layers)} layers decoded back to back on one stream")
+    for B, o, l in zip(built, outs, lses):
+        ada.decode(geom, B["dc"], B["cb8d"], B["cb4d"], B["q"], cfg.sigma, o, l, ws=ws)
+    torch.cuda.synchronize()
+    for B, o, l in zip(built, outs, lses):
+        label = f"workload 5 layer {B['layer']}"
+        s = B["s"]
+        hc = oracle.HostCache(D, H, 1, maxp, _stored_bytes(cfg, lens[[s]], bp[[s]]) + 4096, slot_tokens=False)
+        assert oracle.pack(hc, synth.cu_tokens(lens[[s]]), bp[[s]], B["k"], B["v"], B["r"], B["c8"], B["c4"],
+                           B["sc"]) == 0
+        _compare_rows_all(label, B["dc"].arena.cpu().numpy(), _host_tables(B["dc"]), hc,
+                          [(s * H + h, h) for h in range(H)], D)
+        ref = oracle.decode(hc, B["cb8"], B["cb4"], B["q"][[s]].cpu(), cfg.sigma, nthreads=NTHREADS)
+        _check_outputs(label, o, l, ref, [s])
