@@ -630,6 +630,8 @@ def main():
                      device=dev)
     timer = time_eager if args.eager else time_graph
     m = measure_step(cfg, L, args, out, lse, ws, timer)
+    # (each view keeps its arena copy alive: the copies must outlive every
+    # call below that reads them, the symmetric variant's included)
     views, n_copies = m.pop("_views"), m["config"]["arena_copies"]
     tokens = m["config"]["tokens_per_step"]
     ms_graph = m["ms_per_step"]

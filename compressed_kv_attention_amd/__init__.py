@@ -207,11 +207,15 @@ class Cache:
         ar = self.arena if arena is None else arena
         if ar.numel() != self.arena.numel():
             raise ValueError("substitute arena must have the same size")
-        return _CacheView(ar.data_ptr(), ar.numel() // 128, self.page_table.data_ptr(),
-                          self.page_meta.data_ptr(), self.num_pages.data_ptr(),
-                          self.tier_tokens.data_ptr(),
-                          self.slot_token.data_ptr() if self.slot_token is not None else None,
-                          self.num_seqs, self.maxp)
+        v = _CacheView(ar.data_ptr(), ar.numel() // 128, self.page_table.data_ptr(),
+                       self.page_meta.data_ptr(), self.num_pages.data_ptr(),
+                       self.tier_tokens.data_ptr(),
+                       self.slot_token.data_ptr() if self.slot_token is not None else None,
+                       self.num_seqs, self.maxp)
+        # the view holds raw device addresses: it keeps the tensors behind
+        # them alive for as long as it exists
+        v._keep = (ar, self.page_table, self.page_meta, self.num_pages, self.tier_tokens, self.slot_token)
+        return v
 
 
 def encode(geom: Geom, keys, cb8, cb4, radius, codes8, codes4, stream=None):
@@ -486,7 +490,7 @@ def decode_workspace_size(geom: Geom, num_seqs: int, max_pages_per_head: int, nu
     return int(load().ada_decode_workspace_size(C.byref(geom), num_seqs, max_pages_per_head, num_splits))
 
 
-def _decode_args(geom, cache, q, out, lse, logits, ws, num_splits, stream=None):
+def _decode_shapes(geom, cache, q, out, lse, logits):
     S, Hq, D = cache.num_seqs, geom.num_q_heads, geom.head_dim
     if tuple(q.shape) != (S, Hq, D) or tuple(out.shape) != (S, Hq, D):
         raise ValueError("q and out must be [S][Hq][D]")
@@ -494,6 +498,11 @@ def _decode_args(geom, cache, q, out, lse, logits, ws, num_splits, stream=None):
         raise ValueError("lse must be [S][Hq]")
     if logits is not None and tuple(logits.shape) != (S, Hq, cache.maxp * 16):
         raise ValueError("logits must be [S][Hq][max_pages_per_head*16]")
+
+
+def _decode_args(geom, cache, q, out, lse, logits, ws, num_splits, stream=None):
+    _decode_shapes(geom, cache, q, out, lse, logits)
+    S = cache.num_seqs
     if ws is None:
         ws = _workspace(decode_workspace_size(geom, S, cache.maxp, num_splits), q.device, stream)
     return ws

@@ -207,3 +207,23 @@ def test_load_refuses_a_stale_library(monkeypatch):
     monkeypatch.setattr(b, "source_digest", lambda: "0" * 64)
     with pytest.raises(ImportError, match="stale"):
         ada.load()
+
+
+def test_cache_view_keeps_its_buffers_alive():
+    """A view holds raw addresses; it must keep the tensors behind them alive
+    (a freed arena copy read through a view would be a use after free)."""
+    import gc
+    import weakref
+
+    import torch
+    geom = ada.Geom(64, 4, 4)
+    c = ada.Cache(geom, 1, 4, 4096, device="cpu")
+    sub = torch.zeros_like(c.arena)
+    ref = weakref.ref(sub)
+    v = c.view(sub)
+    del sub
+    gc.collect()
+    assert ref() is not None and v.arena == ref().data_ptr()
+    del v
+    gc.collect()
+    assert ref() is None
