@@ -695,7 +695,9 @@ static int pack_impl(int D, int Hkv, int S, const int32_t *cu_tokens, const int3
                 order[i] = (int32_t)i;
             if (!dense && tiers) {
                 int64_t at = 0, cnt[4] = {0, 0, 0, 0};
-                /* a value above 3 counts as dropped */
+                /* Reading: a state carries a residency bit and, when it is
+                 * resident, a tier (technical summary, section 2.2); a value
+                 * other than the kept tiers 0-2 means not resident, like 3 */
                 for (int64_t i = 0; i < T; i++) {
                     int t = tiers[(b + i) * Hkv + h];
                     cnt[t < 3 ? t : 3]++;
