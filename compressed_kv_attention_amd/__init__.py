@@ -24,7 +24,7 @@ __all__ = [
     "decode_workspace_size", "decode", "decode_stage", "dense_decode",
     "code_error", "solve_workspace_size", "rdr_solve", "tier_counts", "pack_tiers_num_pages",
     "rdr_pack_tiers", "AppendState", "append", "retier", "retier_plan",
-    "decode_sym_workspace_size", "decode_sym",
+    "decode_sym_workspace_size", "decode_sym", "decode_noalloc",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -130,6 +130,8 @@ def load():
         L.ada_decode_sym.restype = C.c_int
         L.ada_decode_sym_workspace_size.argtypes = [G, I32, I32, I32]
         L.ada_decode_sym_workspace_size.restype = SZ
+        L.ada_decode_noalloc.argtypes = [G, CV, P, P, P, F, P, P, P, I32, P]
+        L.ada_decode_noalloc.restype = C.c_int
         L.ada_decode_merge.argtypes = [G, CV, P, P, P, F, P, P, I32, P, SZ, P]
         L.ada_decode_merge.restype = C.c_int
         _lib = L
@@ -521,6 +523,21 @@ def decode(geom: Geom, cache: Cache, cb8, cb4, q, softmax_scale: float, out, lse
                            num_splits, _dev(ws, "ws"), ws.numel(), _stream(stream))
     _check(st, "ada_decode")
     return ws
+
+
+def decode_noalloc(geom: Geom, cache: Cache, cb8, cb4, q, softmax_scale: float, out, lse=None, logits=None,
+                   num_splits: int = 0, stream=None, view=None):
+    """ada_decode_noalloc: one decode step that allocates nothing (the split
+    partials live in the library's own device array; overlapping calls on
+    one GPU race)."""
+    _decode_shapes(geom, cache, q, out, lse, logits)
+    v = cache.view() if view is None else view
+    st = load().ada_decode_noalloc(C.byref(geom), C.byref(v), _dev(cb8, "cb8", (torch.float32,)),
+                                   _dev(cb4, "cb4", (torch.float32,)), _dev(q, "q", (torch.bfloat16,)),
+                                   float(softmax_scale), _dev(out, "out", (torch.float32,)),
+                                   _dev(lse, "lse", (torch.float32,)), _dev(logits, "logits", (torch.float32,)),
+                                   num_splits, _stream(stream))
+    _check(st, "ada_decode_noalloc")
 
 
 def decode_sym_workspace_size(geom: Geom, num_seqs: int, max_pages_per_head: int, num_splits: int = 0) -> int:

@@ -703,6 +703,23 @@ ada_status ada_decode(const ada_geom *geom, const ada_cache *cache, const float 
                          ws_bytes, stream, false);
 }
 
+ada_status ada_decode_noalloc(const ada_geom *geom, const ada_cache *cache, const float *cb8,
+                              const float *cb4, const uint16_t *q, float softmax_scale, float *out,
+                              float *lse, float *logits_dbg, int32_t num_splits, void *stream)
+{
+    static_assert(ADA_NOALLOC_SCRATCH_BYTES == kNoAllocScratchBytes, "scratch size of the header");
+    if (!geom_ok(geom) || !cache_ok(cache) || num_splits < 0 || num_splits > kMaxSplits)
+        return ADA_EINVAL;
+    const int32_t ns = num_splits > 0 ? num_splits : default_splits(geom, cache->num_seqs, cache->max_pages_per_head);
+    if (ws_layout(geom, cache->num_seqs, ns).total > kNoAllocScratchBytes)
+        return ADA_EWORKSPACE; // the partials would not fit in the library's array
+    void *scr = nullptr;
+    if (noalloc_scratch(&scr) != hipSuccess)
+        return ADA_EHIP;
+    return decode_common(geom, cache, cb8, cb4, q, softmax_scale, out, lse, logits_dbg, num_splits, scr,
+                         kNoAllocScratchBytes, stream, false);
+}
+
 ada_status ada_decode_stream(const ada_geom *geom, const ada_cache *cache, const float *cb8,
                              const float *cb4, const uint16_t *q, float softmax_scale, float *out,
                              float *lse, float *logits_dbg, int32_t num_splits, void *ws,

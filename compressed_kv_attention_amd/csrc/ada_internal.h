@@ -66,6 +66,11 @@ hipError_t launch_decode(int D, int NH, bool dense, const DecodeArgs &a, hipStre
 // workspace).
 size_t decode_lut_floats(int D, int NH);
 
+// Device address, on the current device, of the library-owned array that
+// holds ada_decode_noalloc's split partials (kNoAllocScratchBytes).
+constexpr size_t kNoAllocScratchBytes = (size_t)8 << 20;
+hipError_t noalloc_scratch(void **ptr);
+
 // LDS bytes the page-stream workgroup needs; the device offers 160 KiB.
 size_t decode_shmem_bytes(int D, int NH, bool dense, int nsplit, int maxp);
 constexpr size_t kMaxLds = 160 * 1024;

@@ -45,7 +45,14 @@
 #include "ada_internal.h"
 #include "wave_ops.h"
 
+#include <mutex>
 #include <type_traits>
+
+// Split partials of ada_decode_noalloc: a library-owned device array, one
+// copy per GPU the library runs on, kept until the process ends.  Host code
+// never passes this name to a kernel (on the host it is only a stand-in):
+// noalloc_scratch() gives each device's address.
+static __device__ __align__(256) unsigned char scratch[ada::kNoAllocScratchBytes];
 
 namespace ada {
 namespace {
@@ -1090,6 +1097,30 @@ hipError_t launch_t(const DecodeArgs &a, hipStream_t st, unsigned stages)
 } // namespace
 
 size_t decode_lut_floats(int D, int NH) { return (size_t)(D / 8) * kLutCodes * NH; }
+
+hipError_t noalloc_scratch(void **ptr)
+{
+    // looked up once per device, with that device current (the caller's)
+    constexpr int kMaxDevices = 64;
+    static std::mutex mu;
+    static void *addr[kMaxDevices] = {};
+    int dev = 0;
+    if (hipError_t e = hipGetDevice(&dev); e != hipSuccess)
+        return e;
+    if (dev < 0 || dev >= kMaxDevices)
+        return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(mu);
+    if (addr[dev] == nullptr) {
+        void *p = nullptr;
+        if (hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)); e != hipSuccess)
+            return e;
+        if (p == nullptr)
+            return hipErrorInvalidSymbol;
+        addr[dev] = p;
+    }
+    *ptr = addr[dev];
+    return hipSuccess;
+}
 
 size_t decode_shmem_bytes(int D, int NH, bool dense, int nsplit, int maxp)
 {

@@ -455,6 +455,26 @@ ada_status ada_decode(const ada_geom *geom, const ada_cache *cache, const float 
                       size_t ws_bytes, void *stream);
 
 /*
+ * ada_decode_noalloc -- ada_decode for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid allocation).  It takes no workspace: the split partials live in a
+ * library-owned device array of ADA_NOALLOC_SCRATCH_BYTES, one per GPU the
+ * library runs on, held until the process ends (its address is looked up
+ * on the first call on each device, with that device current).  The call
+ * allocates and frees nothing.  Arguments, outputs and errors are those of
+ * ada_decode; a step whose partials (ada_decode_workspace_size) exceed the
+ * array gives ADA_EWORKSPACE before any device work.  The partials need no
+ * clearing: every call writes what it reads.  All calls on one GPU share
+ * the array, so calls that overlap in time on one GPU (on different
+ * streams, or from several host threads) race and must be serialised by
+ * the caller.
+ */
+#define ADA_NOALLOC_SCRATCH_BYTES ((size_t)8 << 20)
+ada_status ada_decode_noalloc(const ada_geom *geom, const ada_cache *cache, const float *cb8,
+                              const float *cb4, const uint16_t *q, float softmax_scale, float *out,
+                              float *lse, float *logits_dbg, int32_t num_splits, void *stream);
+
+/*
  * The two stages of ada_decode, for callers that time or schedule them
  * apart.  Each takes the arguments of ada_decode (unused ones may be NULL);
  * called in this order on one stream with the same arguments and workspace

@@ -227,3 +227,19 @@ def test_cache_view_keeps_its_buffers_alive():
     del v
     gc.collect()
     assert ref() is None
+
+
+def test_noalloc_decode_rejects_partials_beyond_its_array_on_the_host():
+    """ada_decode_noalloc checks the step's partials against its fixed array
+    before any device work: too many splits is ADA_EWORKSPACE."""
+    lib = ada.load()
+    geom = ada.Geom(128, 32, 8)
+    need = ada.decode_workspace_size(geom, 64, 4200, 64)
+    assert need > (8 << 20)
+    view = ada._CacheView(1 << 20, 1, 1 << 21, 1 << 22, 1 << 23, 1 << 24, None, 64, 4200)
+    st = lib.ada_decode_noalloc(C.byref(geom), C.byref(view), C.c_void_p(256), C.c_void_p(256),
+                                C.c_void_p(256), 0.1, C.c_void_p(256), None, None, 64, None)
+    assert st == ada.EWORKSPACE
+    st = lib.ada_decode_noalloc(C.byref(geom), C.byref(view), C.c_void_p(256), C.c_void_p(256),
+                                C.c_void_p(256), 0.1, C.c_void_p(256), None, None, 2000, None)
+    assert st == ada.EINVAL
