@@ -405,7 +405,7 @@ ada_status ada_encode(const ada_geom *geom, int64_t n_tokens, const uint16_t *ke
     if (!keys || !cb8 || !cb4 || !radius || !codes8 || !codes4)
         return ADA_EINVAL;
     if ((reinterpret_cast<uintptr_t>(keys) & 15) || (reinterpret_cast<uintptr_t>(cb8) & 15) ||
-        (reinterpret_cast<uintptr_t>(cb4) & 15))
+        (reinterpret_cast<uintptr_t>(cb4) & 15) || (reinterpret_cast<uintptr_t>(radius) & 1))
         return ADA_EINVAL;
     return launch_encode(geom->head_dim, geom->num_kv_heads, n_tokens, keys, cb8, cb4, radius, codes8,
                          codes4, as_stream(stream)) == hipSuccess
@@ -505,9 +505,10 @@ ada_status ada_code_error(const ada_geom *geom, int64_t n_tokens, const uint16_t
     if (!keys || !cb8 || !cb4 || !codes8 || !codes4 || !err8 || !err4)
         return ADA_EINVAL;
     if ((reinterpret_cast<uintptr_t>(keys) & 15) || (reinterpret_cast<uintptr_t>(cb8) & 15) ||
-        (reinterpret_cast<uintptr_t>(cb4) & 15))
+        (reinterpret_cast<uintptr_t>(cb4) & 15) || (reinterpret_cast<uintptr_t>(codes8) & 3) ||
+        (reinterpret_cast<uintptr_t>(codes4) & 3))
         return ADA_EINVAL;
-    if ((n_tokens * geom->num_kv_heads + 63) / 64 > INT32_MAX)
+    if ((n_tokens * geom->num_kv_heads + 255) / 256 > INT32_MAX)
         return ADA_EINVAL;
     return launch_code_error(geom->head_dim, geom->num_kv_heads, n_tokens, keys, cb8, cb4, codes8, codes4,
                              err8, err4, as_stream(stream)) == hipSuccess

@@ -212,8 +212,8 @@ __device__ __forceinline__ Lane make_lane(int lane)
 //   tiers 0/3: c[0 .. NV) value chunks, c[NV .. 2 NV) key chunks
 //   tier 1:    c[0 .. NV) value chunks; c[NV] the lane's code block;
 //              c[NV+1] the 16-byte block of radii holding slots 4r .. 4r+3
-//   tier 2:    c[0 .. NV/2) int8 value chunks; c[NV], c[NV+1] as in tier 1;
-//              c[NV+2] the value-scale block (as the radii)
+//   tier 2:    c[0 .. NV/2) int8 value chunks; c[NV/2] the value-scale
+//              block (as the radii); c[NV], c[NV+1] as in tier 1
 // Unused loads repeat chunk 0 (same cache lines, no extra HBM traffic).
 // Every tier issues the same loads with no branch, so the next page's loads
 // stay in flight while the current page is computed.  The value chunks sit
@@ -221,7 +221,7 @@ __device__ __forceinline__ Lane make_lane(int lane)
 template <int D>
 struct PageRegs {
     static constexpr int NV = D / 32;
-    static constexpr int NL = 2 * NV > NV + 3 ? 2 * NV : NV + 3;
+    static constexpr int NL = 2 * NV > NV + 2 ? 2 * NV : NV + 2;
     u32x4 c[NL];
     int tier, nvalid;
 };
@@ -249,7 +249,7 @@ __device__ __forceinline__ void fetch_page(PageRegs<D> &pr, const uint8_t *page,
             t1 = L.rblk1;
             t2 = L.rblk2;
         }
-        if (c == NV + 2)
+        if (c == NV / 2)
             t2 = L.sblk2;
         o[c] = (DENSE || tier == 0) ? dense : tier == 1 ? t1 : t2;
     }
@@ -445,7 +445,7 @@ __device__ __forceinline__ void process_page(PageRegs<D> &cur, int p, WaveState<
     const bool int8v = !DENSE && tier == 2;
     if (int8v) {
         float sc[4];
-        quad_f16(cur.c[NV + 2], L.r, sc);
+        quad_f16(cur.c[NV / 2], L.r, sc);
 #pragma unroll
         for (int e = 0; e < 4; e++)
             w[e] *= sc[e];

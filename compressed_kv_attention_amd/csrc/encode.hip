@@ -20,8 +20,9 @@
 // kFilterRel), the token-group is rescanned in double, so the codes are
 // still the exact double argmin.
 //
-// Grid: x = blocks of 64-token chunks (grid-stride), y = (kv-head, quarter
-// of the groups).  A block has one wave per group of its quarter (4 waves).
+// Grid: blocks of (64-token chunk range (grid-stride), kv-head, quarter of
+// the groups), XCD-aware (below).  A block has one wave per group of its
+// quarter (4 waves).
 // Per chunk it stages the 64 keys in LDS and sums a fast-order norm per
 // token (four lanes a token); the last wave also sums the defining norms
 // (one lane a token) for the radius and the rescans; every wave scores its
@@ -226,7 +227,7 @@ __device__ __attribute__((noinline)) uint32_t rescan(uint4 kw, double r, const f
 }
 
 template <int D>
-__global__ __launch_bounds__(256, 4) void encode_kernel(int Hkv, int64_t n_tokens, int64_t n_chunks,
+__global__ __launch_bounds__(256, 4) void encode_kernel(int Hkv, int gx, int64_t n_tokens, int64_t n_chunks,
                                                         const uint16_t *__restrict__ keys,
                                                         const float *__restrict__ cb8,
                                                         const float *__restrict__ cb4,
@@ -249,7 +250,32 @@ __global__ __launch_bounds__(256, 4) void encode_kernel(int Hkv, int64_t n_token
     __shared__ uint8_t s4[kChunk][4];
     __shared__ uint32_t rq[kChunk * 4]; // rescans: token | wave << 8 | which << 12
     __shared__ int rqn;
-    const int h = blockIdx.y / (G / 4), gq = blockIdx.y % (G / 4);
+    // Blocks are dealt round-robin over the 8 XCDs, each with its own L2:
+    // XCD x takes the blocks whose index is x mod 8.  With a multiple of 8
+    // kv-heads, XCD x serves heads x, x + 8, ... only, so each head's
+    // codebooks are fetched into one L2, not all eight.  The quarter blocks
+    // of one (chunk range, kv-head) are adjacent in their XCD's order, so
+    // they run at about the same time and the chunk's keys come from HBM
+    // once, then from that L2.  (Otherwise heads take the XCDs in turn.)
+    constexpr int NQ = G / 4;
+    const int bid = blockIdx.x, x = bid & 7, j = bid >> 3;
+    int h, bx, gq;
+    if (Hkv % 8 == 0) {
+        const int hpx = Hkv / 8; // heads per XCD
+        const int per_head = gx * NQ;
+        if (j >= hpx * per_head)
+            return;
+        h = x + 8 * (j / per_head);
+        bx = (j % per_head) / NQ;
+        gq = j % NQ;
+    } else {
+        gq = j % NQ;
+        const int item = (j / NQ) * 8 + x;
+        if (item >= gx * Hkv)
+            return;
+        h = item / gx;
+        bx = item % gx;
+    }
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = 4 * gq + w;
     const int col = lane & 15, q = lane >> 4;
     const float *c8g = cb8 + ((size_t)h * G + g) * kCodes8 * 8;
@@ -299,7 +325,7 @@ __global__ __launch_bounds__(256, 4) void encode_kernel(int Hkv, int64_t n_token
     }
     __syncthreads(); // (the keys reuse the rest of the codebooks' LDS)
 
-    for (int64_t chunk = blockIdx.x; chunk < n_chunks; chunk += gridDim.x) {
+    for (int64_t chunk = bx; chunk < n_chunks; chunk += gx) {
         const int64_t n0 = chunk * kChunk;
         if (tid == 0)
             rqn = 0;
@@ -449,12 +475,16 @@ hipError_t launch_encode(int D, int Hkv, int64_t n_tokens, const uint16_t *keys,
     // about four blocks per compute unit; each block walks its chunks
     const int64_t by = (int64_t)Hkv * (D / 32);
     const int64_t want = (1024 + by - 1) / by;
-    const dim3 grid((unsigned)(n_chunks < want ? n_chunks : want), (unsigned)by);
+    const int gx = (int)(n_chunks < want ? n_chunks : want);
+    // (chunk range, kv-head) items times quarters, in groups of 8 items
+    const int64_t nq = D / 32;
+    const int64_t items = (int64_t)gx * Hkv;
+    const dim3 grid((unsigned)(Hkv % 8 == 0 ? items * nq : (items + 7) / 8 * 8 * nq));
     if (D == 128)
-        hipLaunchKernelGGL(encode_kernel<128>, grid, dim3(256), 0, st, Hkv, n_tokens, n_chunks, keys,
+        hipLaunchKernelGGL(encode_kernel<128>, grid, dim3(256), 0, st, Hkv, gx, n_tokens, n_chunks, keys,
                            cb8, cb4, radius, codes8, codes4);
     else if (D == 64)
-        hipLaunchKernelGGL(encode_kernel<64>, grid, dim3(256), 0, st, Hkv, n_tokens, n_chunks, keys,
+        hipLaunchKernelGGL(encode_kernel<64>, grid, dim3(256), 0, st, Hkv, gx, n_tokens, n_chunks, keys,
                            cb8, cb4, radius, codes8, codes4);
     else
         return hipErrorInvalidValue;

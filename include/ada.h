@@ -112,7 +112,7 @@ size_t ada_page_bytes(int32_t head_dim, int32_t tier);
  *   keys    [n_tokens][Hkv][D] fp16 (16-byte aligned)
  *   cb8     [Hkv][G][256][8] f32,  cb4 [Hkv][G][16][8] f32 (one layer;
  *           both 16-byte aligned)
- *   radius  [n_tokens][Hkv] fp16 out
+ *   radius  [n_tokens][Hkv] fp16 out (2-byte aligned)
  *   codes8  [n_tokens][Hkv][G] u8 out
  *   codes4  [n_tokens][Hkv][G/2] u8 out (two 4-bit codes per byte)
  * n_tokens may be 0 (no work).  Misaligned or null pointers -> ADA_EINVAL.
@@ -205,7 +205,8 @@ ada_status dense_pack(const ada_geom *geom, const ada_cache *cache, int32_t num_
  * the total is rounded once to f32.
  *   keys [n_tokens][Hkv][D] fp16 (16-byte aligned); cb8 / cb4 as in
  *   ada_encode (16-byte aligned); codes8 / codes4 as ada_encode writes them
- *   (any codes are accepted); err8, err4 [n_tokens][Hkv] f32 out.
+ *   (any codes are accepted; both 4-byte aligned); err8, err4
+ *   [n_tokens][Hkv] f32 out.
  */
 ada_status ada_code_error(const ada_geom *geom, int64_t n_tokens, const uint16_t *keys,
                           const float *cb8, const float *cb4, const uint8_t *codes8,
