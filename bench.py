@@ -240,7 +240,7 @@ def append_path(dev, reps=20):
     c8 = torch.empty((S * n, H, D // 8), dtype=torch.uint8, device=dev)
     c4 = torch.empty((S * n, H, D // 16), dtype=torch.uint8, device=dev)
     per_call = S * H * (n // 16 + 3) * ada.page_bytes(D, 0)  # a bound: every page at the largest size
-    calls = 2 * reps + 2  # the ranked path, then the budget-solver path
+    calls = 3 * reps + 2  # the ranked path, then the budget-solver path (host plan, device plan)
     cache = ada.Cache(geom, S, calls * (n // 16 + 3), per_call * calls)
     ws = torch.zeros(ada.pack_workspace_size(geom, S * n, S), dtype=torch.uint8, device=dev)
     pos = np.zeros(S, np.int64)
@@ -292,6 +292,26 @@ def append_path(dev, reps=20):
                      "solve_us": t[2], "tier_counts_us": t[3], "pack_tiers_us": t[4],
                      "token_heads_per_s": th / (t.sum() / 1e6),
                      "note": "tier_counts includes its device-to-host copy and stream synchronization"}
+    # the same chain with the page plan made on the device: no host round
+    # trip, so the whole chain is enqueued at once and timed end to end
+    state = ada.AppendState(geom, cache)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(reps):
+        pos += n
+        ada.encode(geom, keys, cb8, cb4, r, c8, c4)
+        ada.code_error(geom, keys, cb8, cb4, c8, c4, e8, e4)
+        ada.rdr_solve(geom, cu, budgets, r, e8, e4, scores, tiers, ws=sws)
+        ada.rdr_pack_tiers_device(geom, cache, state, cu, tiers, keys, vals, r, c8, c4, pos_base=pos, ws=ws)
+    e1.record()
+    torch.cuda.synchronize()
+    status = state.pull()
+    chain_us = e0.elapsed_time(e1) / reps * 1e3
+    res["solver_device_plan"] = {"chain_us": chain_us, "token_heads_per_s": th / (chain_us / 1e6),
+                                 "status": status,
+                                 "note": "encode, code error, solve and rdr_pack_tiers_device per chunk, "
+                                         "enqueued back to back with no synchronization"}
     return res
 
 
@@ -687,7 +707,8 @@ def main():
         log(f"append path: encode {ap['encode_us']:.1f} us, pack {ap['pack_us']:.1f} us per layer; "
             f"with the budget solver: code error {ap['solver']['code_error_us']:.1f} us, "
             f"solve {ap['solver']['solve_us']:.1f} us, counts {ap['solver']['tier_counts_us']:.1f} us, "
-            f"pack {ap['solver']['pack_tiers_us']:.1f} us")
+            f"pack {ap['solver']['pack_tiers_us']:.1f} us; with the device page plan the chain takes "
+            f"{ap['solver_device_plan']['chain_us']:.1f} us")
     if not args.no_append:
         result["append_step"] = append_steps(dev)
         log(f"decode-step append: {result['append_step']['us_per_step']:.2f} us per step "

@@ -23,7 +23,7 @@ __all__ = [
     "pack_workspace_size", "rdr_pack", "dense_pack", "decode_default_splits",
     "decode_workspace_size", "decode", "decode_stage", "dense_decode",
     "code_error", "solve_workspace_size", "rdr_solve", "tier_counts", "pack_tiers_num_pages",
-    "rdr_pack_tiers", "AppendState", "append", "retier", "retier_plan",
+    "rdr_pack_tiers", "rdr_pack_tiers_device", "AppendState", "append", "retier", "retier_plan",
     "decode_sym_workspace_size", "decode_sym", "decode_noalloc",
 ]
 
@@ -116,6 +116,8 @@ def load():
         L.rdr_pack_tiers_num_pages.restype = C.c_int
         L.rdr_pack_tiers.argtypes = [G, CV, I32, P, P, P, P, P, P, P, P, P, P, P, P, P, SZ, P]
         L.rdr_pack_tiers.restype = C.c_int
+        L.rdr_pack_tiers_device.argtypes = [G, CV, I32, P, P, P, P, P, P, P, P, P, P, SZ, P]
+        L.rdr_pack_tiers_device.restype = C.c_int
         L.ada_decode_default_splits.argtypes = [G, I32, I32]
         L.ada_decode_default_splits.restype = I32
         L.ada_decode_workspace_size.argtypes = [G, I32, I32, I32]
@@ -465,6 +467,28 @@ def rdr_pack_tiers(geom: Geom, cache: Cache, cu_tokens, row_counts, tiers, keys,
         _dev(codes4, "codes4", (torch.uint8,)), ppp, pbp, cache.cursor.ctypes.data_as(C.c_void_p),
         cache.num_pages_host.ctypes.data_as(C.c_void_p), _dev(ws, "ws"), ws.numel(), _stream(stream))
     _check(st, "rdr_pack_tiers")
+    return ws
+
+
+def rdr_pack_tiers_device(geom: Geom, cache: Cache, state: "AppendState", cu_tokens, tiers, keys, values,
+                          radius, codes8, codes4, pos_base=None, ws=None, stream=None):
+    """rdr_pack_tiers with the page plan made on the device (see
+    rdr_pack_tiers_device in include/ada.h): no tier counts on the host and
+    no synchronization.  The arena space comes from `state`'s device cursor;
+    call state.pull() before the next host-planned pack."""
+    cu, cup = _host(cu_tokens, np.int32, "cu_tokens")
+    n = int(cu[-1])
+    pb, pbp = _host(pos_base, np.int64, "pos_base")
+    if ws is None:
+        ws = _workspace(pack_workspace_size(geom, n, len(cu) - 1), cache.arena.device, stream)
+    view = cache.view()
+    st = load().rdr_pack_tiers_device(
+        C.byref(geom), C.byref(view), len(cu) - 1, cup, _dev(tiers, "tiers", (torch.uint8,)),
+        _dev(keys, "keys", (torch.float16,)), _dev(values, "values", (torch.bfloat16,)),
+        _dev(radius, "radius", (torch.float16, torch.int16)), _dev(codes8, "codes8", (torch.uint8,)),
+        _dev(codes4, "codes4", (torch.uint8,)), pbp, _dev(state.buf, "state"), _dev(ws, "ws"), ws.numel(),
+        _stream(stream))
+    _check(st, "rdr_pack_tiers_device")
     return ws
 
 

@@ -223,6 +223,10 @@ ada_status run_pack(const ada_geom *g, const ada_cache *c, int32_t S, const int3
     plan.dense = dense ? 1 : 0;
     plan.gen_pages = pb.gen_pages ? 1 : 0;
     plan.n_tokens = N;
+    plan.dev_plan = 0;
+    plan.cursor = nullptr;
+    plan.status = nullptr;
+    plan.capacity = 0;
     PackData data{keys, values, radius, codes8, codes4, scores};
     PackCache cache{c->arena, c->page_table, c->page_meta, c->num_pages, c->tier_tokens, c->slot_token};
     if (launch_pack(plan, data, cache, st) != hipSuccess)
@@ -678,6 +682,88 @@ ada_status rdr_pack_tiers(const ada_geom *geom, const ada_cache *cache, int32_t 
     return run_pack(geom, cache, num_seqs, cu_tokens_host, counts, rc, tiers, false, keys, values, radius,
                     codes8, codes4, nullptr, nullptr, place_perm_host, pos_base_host, arena_cursor_host,
                     num_pages_host, ws, ws_bytes, stream);
+}
+
+ada_status rdr_pack_tiers_device(const ada_geom *geom, const ada_cache *cache, int32_t num_seqs,
+                                 const int32_t *cu_tokens_host, const uint8_t *tiers, const uint16_t *keys,
+                                 const uint16_t *values, const uint16_t *radius, const uint8_t *codes8,
+                                 const uint8_t *codes4, const int64_t *pos_base_host, void *state, void *ws,
+                                 size_t ws_bytes, void *stream)
+{
+    if (!geom_ok(geom) || !cache_ok(cache) || num_seqs != cache->num_seqs || num_seqs < 0 ||
+        !cu_ok(num_seqs, cu_tokens_host) || cache->tier_tokens == nullptr || state == nullptr ||
+        (reinterpret_cast<uintptr_t>(state) & 255))
+        return ADA_EINVAL;
+    const int H = geom->num_kv_heads;
+    const int64_t N = cu_tokens_host[num_seqs];
+    if (N > 0 && (!tiers || !keys || !values || !radius || !codes8 || !codes4))
+        return ADA_EINVAL;
+    if (N > 0 && ((reinterpret_cast<uintptr_t>(cache->arena) & 255) || (reinterpret_cast<uintptr_t>(keys) & 15) ||
+                  (reinterpret_cast<uintptr_t>(values) & 15) || (reinterpret_cast<uintptr_t>(codes8) & 3) ||
+                  (reinterpret_cast<uintptr_t>(codes4) & 3) || (reinterpret_cast<uintptr_t>(radius) & 1)))
+        return ADA_EINVAL;
+    if (ws == nullptr || ws_bytes < pack_workspace(H, N, num_seqs) || (reinterpret_cast<uintptr_t>(ws) & 255))
+        return ADA_EWORKSPACE;
+    if (N == 0)
+        return ADA_OK;
+    // the host plans only where each row's page list goes: a range sized
+    // for the row's tokens (at most one partial page per tier)
+    const int64_t rows = (int64_t)num_seqs * H;
+    std::vector<PackSeq> seqs(num_seqs);
+    std::vector<PackRow> rowv(rows);
+    int64_t n = 0;
+    for (int s = 0; s < num_seqs; s++) {
+        seqs[s].begin = cu_tokens_host[s];
+        seqs[s].len = cu_tokens_host[s + 1] - cu_tokens_host[s];
+        seqs[s].n_cum[0] = seqs[s].n_cum[1] = seqs[s].n_cum[2] = 0;
+        seqs[s].pad = 0;
+        seqs[s].pos_base = pos_base_host ? pos_base_host[s] : 0;
+        const int64_t cap = (seqs[s].len + kSlots - 1) / kSlots + 2;
+        for (int h = 0; h < H; h++) {
+            PackRow &r = rowv[(int64_t)s * H + h];
+            std::memset(&r, 0, sizeof(r));
+            r.lp_first[0] = (int32_t)n; // first entry of the row's range
+            r.lp_first[1] = (int32_t)cap; // its length
+            n += cap;
+        }
+    }
+    if (n > max_pack_pages(H, N, num_seqs) || n > INT32_MAX)
+        return ADA_EWORKSPACE;
+    uint8_t *wsb = static_cast<uint8_t *>(ws);
+    const size_t seq_off = 0, row_off = align256(sizeof(PackSeq) * (size_t)std::max(num_seqs, 1));
+    const size_t page_off = row_off + align256(sizeof(PackRow) * (size_t)std::max<int64_t>(rows, 1));
+    const size_t blob_cap = page_off + align256(sizeof(PackPage) * (size_t)max_pack_pages(H, N, num_seqs));
+    std::vector<uint8_t> blob(page_off, 0);
+    std::memcpy(blob.data() + seq_off, seqs.data(), sizeof(PackSeq) * seqs.size());
+    std::memcpy(blob.data() + row_off, rowv.data(), sizeof(PackRow) * rowv.size());
+    hipStream_t st = as_stream(stream);
+    // pageable host source: the runtime copies it before returning
+    if (hipMemcpyAsync(wsb, blob.data(), blob.size(), hipMemcpyHostToDevice, st) != hipSuccess)
+        return ADA_EHIP;
+    uint8_t *st8 = static_cast<uint8_t *>(state);
+    PackPlan plan;
+    plan.seqs = reinterpret_cast<const PackSeq *>(wsb + seq_off);
+    plan.rows = reinterpret_cast<const PackRow *>(wsb + row_off);
+    plan.pages = reinterpret_cast<PackPage *>(wsb + page_off);
+    plan.protect = nullptr;
+    plan.tiers = tiers;
+    plan.src = reinterpret_cast<int32_t *>(wsb + blob_cap + align256((size_t)N * H));
+    plan.S = num_seqs;
+    plan.Hkv = H;
+    plan.D = geom->head_dim;
+    plan.maxp = cache->max_pages_per_head;
+    plan.n_pages = (int)n;
+    plan.dense = 0;
+    plan.gen_pages = 1;
+    plan.n_tokens = N;
+    plan.dev_plan = 1;
+    plan.cursor = reinterpret_cast<unsigned long long *>(st8);
+    plan.status = reinterpret_cast<unsigned int *>(st8 + 8);
+    plan.capacity = cache->arena_units;
+    PackData data{keys, values, radius, codes8, codes4, nullptr};
+    PackCache pc{cache->arena, cache->page_table, cache->page_meta, cache->num_pages, cache->tier_tokens,
+                 cache->slot_token};
+    return launch_pack(plan, data, pc, st) == hipSuccess ? ADA_OK : ADA_EHIP;
 }
 
 int32_t ada_decode_default_splits(const ada_geom *geom, int32_t num_seqs, int32_t max_pages_per_head)

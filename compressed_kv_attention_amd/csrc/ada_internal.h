@@ -185,6 +185,15 @@ struct PackPlan {
     int32_t *src;           // [n_pages][16]: flat (token, head) index a slot holds, or -1
     int S, Hkv, D, maxp, n_pages, dense, gen_pages;
     int64_t n_tokens;
+    // Device-side page planning (dev_plan): each row counts its given tiers,
+    // takes its pages' arena space from the bump cursor and its page
+    // indices from num_pages itself.  Row r's pages then sit at plan.pages
+    // [rows[r].lp_first[0] ...), a range the host sized for the row's
+    // tokens; unused entries there get meta = -1.
+    int dev_plan;
+    unsigned long long *cursor; // arena cursor, 128-byte units
+    unsigned int *status;       // sticky bits: 1 a row's page table full, 2 arena full
+    unsigned long long capacity;
 };
 struct PackData {
     const uint16_t *keys, *values, *radius;

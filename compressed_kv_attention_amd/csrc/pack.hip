@@ -68,6 +68,91 @@ __device__ __forceinline__ void row_setup(const PackPlan &plan, const PackCache 
     }
 }
 
+// Device-side plan of one row (rdr_pack_tiers_device): count the row's
+// given tiers, then -- one thread -- check the row's page-table room, take
+// the arena space of all its new pages in one block from the bump cursor
+// (a compare-and-swap loop that never passes the capacity) and lay the
+// tiers out in it, tier 0 first.  A row that does not fit stores nothing
+// and sets its status bit.  Every entry of the row's page-list range past
+// its pages is marked unused.
+__device__ void plan_row_on_device(const PackPlan &plan, const PackCache &cache, int row, const PackSeq &sq,
+                                   int tid, int wave, int lane, PackRow &srw)
+{
+    __shared__ int cnt[16][3];
+    const int h = row % plan.Hkv;
+    int c[3] = {0, 0, 0};
+    for (int i = tid; i < sq.len; i += 1024) {
+        const int t = plan.tiers[((size_t)sq.begin + i) * plan.Hkv + h];
+        c[0] += t == 0;
+        c[1] += t == 1;
+        c[2] += t == 2;
+    }
+#pragma unroll
+    for (int k = 0; k < 3; k++) {
+#pragma unroll
+        for (int o = 32; o >= 1; o >>= 1)
+            c[k] += __shfl_xor(c[k], o, 64);
+        if (lane == 0)
+            cnt[wave][k] = c[k];
+    }
+    __syncthreads();
+    if (tid == 0) {
+        int n[3] = {0, 0, 0};
+        for (int w = 0; w < 16; w++)
+            for (int k = 0; k < 3; k++)
+                n[k] += cnt[w][k];
+        int np[3], pages = 0;
+        unsigned long long units = 0;
+        for (int k = 0; k < 3; k++) {
+            np[k] = (n[k] + kSlots - 1) / kSlots;
+            pages += np[k];
+            units += (unsigned long long)np[k] * (unsigned long long)(page_bytes(plan.D, k) / kUnit);
+        }
+        const int pi0 = cache.num_pages[row];
+        bool ok = pi0 + pages <= plan.maxp;
+        if (!ok)
+            atomicOr(plan.status, 1u);
+        unsigned long long base = 0;
+        if (ok && units > 0) {
+            unsigned long long cur = atomicAdd(plan.cursor, 0ull);
+            ok = false;
+            while (cur + units <= plan.capacity) {
+                const unsigned long long seen = atomicCAS(plan.cursor, cur, cur + units);
+                if (seen == cur) {
+                    ok = true;
+                    break;
+                }
+                cur = seen;
+            }
+            if (!ok)
+                atomicOr(plan.status, 2u);
+            base = cur;
+        }
+        const int first = plan.rows[row].lp_first[0];
+        PackRow r;
+        r.pi0 = pi0;
+        unsigned long long off = base;
+        int lp = first;
+        for (int k = 0; k < 3; k++) {
+            r.count[k] = ok ? n[k] : 0;
+            r.lp_first[k] = lp;
+            r.off[k] = (uint32_t)off;
+            if (ok) {
+                lp += np[k];
+                off += (unsigned long long)np[k] * (unsigned long long)(page_bytes(plan.D, k) / kUnit);
+            }
+        }
+        srw = r;
+    }
+    __syncthreads();
+    // unused entries of the row's page-list range
+    const int first = srw.lp_first[0];
+    const int used = srw.lp_first[2] + (srw.count[2] + kSlots - 1) / kSlots - first;
+    const int cap = plan.rows[row].lp_first[1]; // (the range's length, from the host)
+    for (int q = used + tid; q < cap; q += 1024)
+        plan.pages[first + q].meta = -1;
+}
+
 // Order-preserving map of a finite float (with -0 == +0) to uint32.
 __device__ __forceinline__ uint32_t ord_score(float f)
 {
@@ -92,12 +177,15 @@ __global__ __launch_bounds__(1024) void pack_rank(PackPlan plan, PackData data, 
     __shared__ int wave_tot[16][3];
     __shared__ int running[3];
 
+    __shared__ PackRow srw;
     const int row = blockIdx.x;
     const int s = row / plan.Hkv, h = row % plan.Hkv;
     const PackSeq sq = plan.seqs[s];
-    const PackRow rw = plan.rows[row];
     const int T = sq.len;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    if (plan.dev_plan)
+        plan_row_on_device(plan, cache, row, sq, tid, wave, lane, srw);
+    const PackRow rw = plan.dev_plan ? srw : plan.rows[row];
     row_setup(plan, cache, rw, row, tid, 1024);
 
     if (!plan.dense && plan.tiers == nullptr) {
@@ -283,6 +371,8 @@ __device__ __forceinline__ void fill_page(const PackPlan &plan, const PackData &
 {
     constexpr int G = D / 8, DG = D / 8, SG = 64 / DG, SPL = kSlots / SG;
     const PackPage pg = plan.pages[pidx];
+    if (pg.meta < 0)
+        return; // (an unused entry of a device-planned row)
     const int tier = pg.meta & 3, nv = ((pg.meta >> 2) & 15) + 1;
     const int n16 = page_bytes(D, tier) / 16;
     uint8_t *img = reinterpret_cast<uint8_t *>(img4);

@@ -297,6 +297,33 @@ ada_status rdr_pack_tiers(const ada_geom *geom, const ada_cache *cache, int32_t 
                           uint64_t *arena_cursor_host, int32_t *num_pages_host, void *ws,
                           size_t ws_bytes, void *stream);
 
+/*
+ * rdr_pack_tiers_device -- rdr_pack_tiers with the page plan made on the
+ * device, so the solver path (ada_code_error, rdr_solve, this call) needs
+ * no host round trip and no tier counts on the host.  [TS] 2.2 (retained
+ * states grouped into tier-homogeneous pages).  Each row counts its own
+ * tokens of tiers 0, 1 and 2 (other values are dropped, as in
+ * rdr_pack_tiers); its new pages are numbered after the row's num_pages on
+ * the device, and their arena space is one block per row taken from the
+ * device bump cursor of `state` (ada_append's state: u64 cursor at byte 0,
+ * sticky status at byte 8), tier 0's pages first.  Rows race for the
+ * cursor, so where a row's block lands is not fixed; what each row holds
+ * -- its pages' bytes, order, metadata, slot positions and counts -- is
+ * exactly what rdr_pack_tiers writes for the same tiers.  A row whose pages
+ * would pass max_pages_per_head stores nothing and sets status bit 1; a
+ * row whose block would pass arena_units stores nothing and sets bit 2.
+ * The host's cursor and page counts are not advanced: read them back from
+ * the device (state cursor, cache->num_pages) before a host-planned pack.
+ * Other arguments as rdr_pack_tiers (no row counts, no placement order);
+ * ws: rdr_pack_workspace_size bytes.  keys / values 16-byte, codes 4-byte,
+ * radius 2-byte aligned; state 256-byte aligned.
+ */
+ada_status rdr_pack_tiers_device(const ada_geom *geom, const ada_cache *cache, int32_t num_seqs,
+                                 const int32_t *cu_tokens_host, const uint8_t *tiers, const uint16_t *keys,
+                                 const uint16_t *values, const uint16_t *radius, const uint8_t *codes8,
+                                 const uint8_t *codes4, const int64_t *pos_base_host, void *state, void *ws,
+                                 size_t ws_bytes, void *stream);
+
 /* Bytes of the device state ada_append keeps between decode steps. */
 size_t ada_append_state_bytes(const ada_geom *geom, int32_t num_seqs);
 

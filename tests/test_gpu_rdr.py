@@ -179,3 +179,100 @@ def test_gpu_encode_error_solve_chain_matches_oracle():
     rt = oracle.rdr_solve(64, case["cu"], budgets, rr, re8, re4, case["scores"].numpy())
     assert np.array_equal(tiers.cpu().numpy(), rt)
     assert np.array_equal(counts, oracle.row_tier_counts(case["cu"], rt))
+
+
+def _row_contents(meta, pt, arena, npg, tt, slots, row, D):
+    """A row's pages (metadata, bytes, slot positions) and counts, found
+    through its own page table: placement-independent."""
+    out = []
+    for p in range(int(npg[row])):
+        m = int(meta[row, p])
+        off = int(pt[row, p]) * 128
+        out.append((m, arena[off:off + oracle.page_bytes(D, m & 3)].tobytes(),
+                    tuple(slots[row, p]) if slots is not None else None))
+    return out, tuple(int(x) for x in tt[row])
+
+
+@pytest.mark.parametrize("D,H", [(128, 2), (64, 4)])
+def test_pack_tiers_device_equals_the_host_planned_pack(D, H):
+    """The device-planned pack (rows take arena blocks from a device cursor)
+    holds, row by row, exactly the pages rdr_pack_tiers / the oracle's
+    pack_tiers build from the same tiers; two calls in a row append; the
+    pool is tiled by the rows' blocks; then decode matches the oracle."""
+    cfg = small_workload(D=D, Hq=2 * H, Hkv=H, S=3, T=900, seed=92 + D)
+    lens = [900, 250, 17]
+    case = make_case(cfg, lens=lens)
+    geom = geom_of(cfg)
+    r, c8, c4 = _codes(case)
+    e8, e4 = oracle.code_error(case["keys"], case["cb8"], case["cb4"], c8, c4)
+    budgets = synth.budget_bytes(cfg, lens) * 5 // 6
+    tiers = oracle.rdr_solve(D, case["cu"], budgets, r, e8, e4, case["scores"].numpy())
+    # two calls: the first 60% of each sequence's tokens, then the rest
+    cut = [int(0.6 * T) for T in lens]
+    parts = []
+    for lo, hi in (([0, 0, 0], cut), (cut, lens)):
+        idx = np.concatenate([np.arange(int(case["cu"][s]) + lo[s], int(case["cu"][s]) + hi[s]) for s in range(3)])
+        cu = synth.cu_tokens([hi[s] - lo[s] for s in range(3)])
+        parts.append((idx, cu, list(lo)))
+    maxp = max(lens) // 16 + 8
+    arena = int(sum(lens) * H * 512 + 3 * H * 6 * 8192)
+    hc = oracle.HostCache(D, H, 3, maxp, arena)
+    dc = ada.Cache(geom, 3, maxp, arena, slot_tokens=True)
+    state = ada.AppendState(geom, dc)
+    for idx, cu, pos in parts:
+        t = tiers[idx]
+        assert oracle.pack_tiers(hc, cu, t, case["keys"][idx], case["values"][idx], r[idx], c8[idx], c4[idx],
+                                 pos_base=np.array(pos, np.int64)) == 0
+        flush(f"[pack_tiers_device] D={D} H={H}: {len(idx)} tokens")
+        ada.rdr_pack_tiers_device(geom, dc, state, cu, to_dev(t), to_dev(case["keys"][idx]),
+                                  to_dev(case["values"][idx]), to_dev(r[idx]), to_dev(c8[idx]), to_dev(c4[idx]),
+                                  pos_base=np.array(pos, np.int64))
+    assert state.pull() == 0
+    assert int(dc.cursor[0]) == int(hc.cursor[0])
+    g_meta, g_pt = dc.page_meta.cpu().numpy(), dc.page_table.cpu().numpy().view(np.uint32)
+    g_ar, g_np = dc.arena.cpu().numpy(), dc.num_pages.cpu().numpy()
+    g_tt, g_sl = dc.tier_tokens.cpu().numpy(), dc.slot_token.cpu().numpy()
+    assert np.array_equal(g_np[:3 * H], hc.num_pages)
+    for row in range(3 * H):
+        assert _row_contents(g_meta, g_pt, g_ar, g_np, g_tt, g_sl, row, D) == \
+            _row_contents(hc.page_meta, hc.page_table, hc.arena, hc.num_pages, hc.tier_tokens, hc.slot_token, row, D)
+    # the rows' blocks tile the pool from 0 to the cursor
+    offs, ends = [], []
+    for row in range(3 * H):
+        for p in range(int(g_np[row])):
+            o = int(g_pt[row, p])
+            offs.append(o)
+            ends.append(o + oracle.page_bytes(D, int(g_meta[row, p]) & 3) // 128)
+    order = np.argsort(offs)
+    o, e = np.array(offs)[order], np.array(ends)[order]
+    assert o[0] == 0 and np.array_equal(o[1:], e[:-1]) and e[-1] == int(dc.cursor[0])
+    ref = oracle.decode(hc, case["cb8"], case["cb4"], case["q"], cfg.sigma, nthreads=8)
+    out, lse, _ = decode_outputs(geom, dc, to_dev(case["q"]), with_logits=False)
+    ada.decode(geom, dc, to_dev(case["cb8"]), to_dev(case["cb4"]), to_dev(case["q"]), cfg.sigma, out, lse)
+    torch.cuda.synchronize()
+    assert np.abs(out.cpu().double().numpy() - ref["out"]).max() <= OUT_TOL
+
+
+def test_pack_tiers_device_capacity_status_bits():
+    """A row whose pages pass max_pages_per_head, or whose block passes the
+    arena, stores nothing and sets its status bit; the other rows are
+    packed as usual."""
+    cfg = small_workload(D=64, Hq=2, Hkv=2, S=1, T=100, seed=95)
+    case = make_case(cfg, lens=[100])
+    geom = geom_of(cfg)
+    r, c8, c4 = _codes(case)
+    tiers = np.zeros((100, 2), np.uint8)
+    tiers[:, 1] = 3            # head 1 drops everything: no pages
+    args = (to_dev(tiers), to_dev(case["keys"]), to_dev(case["values"]), to_dev(r), to_dev(c8), to_dev(c4))
+    dc = ada.Cache(geom, 1, 4, 1 << 20)    # 7 fp16 pages needed, room for 4
+    st = ada.AppendState(geom, dc)
+    ada.rdr_pack_tiers_device(geom, dc, st, case["cu"], *args)
+    assert st.pull() == 1 and int(dc.num_pages[0]) == 0 and int(dc.cursor[0]) == 0
+    dc = ada.Cache(geom, 1, 16, 6 * 4096)  # room for 6 of the 7 fp16 pages
+    st = ada.AppendState(geom, dc)
+    ada.rdr_pack_tiers_device(geom, dc, st, case["cu"], *args)
+    assert st.pull() == 2 and int(dc.num_pages[0]) == 0 and int(dc.cursor[0]) == 0
+    dc = ada.Cache(geom, 1, 16, 7 * 4096)  # exactly enough
+    st = ada.AppendState(geom, dc)
+    ada.rdr_pack_tiers_device(geom, dc, st, case["cu"], *args)
+    assert st.pull() == 0 and int(dc.num_pages[0]) == 7 and int(dc.cursor[0]) == 7 * 32
