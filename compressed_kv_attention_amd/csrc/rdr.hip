@@ -25,7 +25,7 @@
 // arithmetic that decides the chains is binary32 in a fixed order (IEEE
 // division and square root), so every decision is reproducible.
 //
-// Kernels: code_error (64 states per block), solve_zero (clears the digit
+// Kernels: code_error (256 states per block), solve_zero (clears the digit
 // histograms), solve_pass<P> (P = 0..3; one block per 1024 states of one
 // sequence), solve_assign (writes the tiers), tier_counts (one block per
 // row).
