@@ -913,6 +913,9 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge(DecodeArgs a)
 template <int D, int NH>
 __global__ __launch_bounds__(256) void sym_lut_kernel(DecodeArgs a)
 {
+    // the query code is decided in double with every product rounded
+    // before it is added, as the definition does: no fused multiply-adds
+#pragma clang fp contract(off)
     constexpr int G = D / 8, LUT_FLOATS = G * kLutCodes * NH;
     __shared__ double qn[NH], u[NH][8];
     __shared__ __align__(16) float xq[NH][D];

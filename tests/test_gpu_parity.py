@@ -429,3 +429,82 @@ def test_dense_pack_and_decode(D, Hq, Hkv):
     err = np.abs(out.cpu().double().numpy() - ref["out"]).max()
     flush(f"[dense] out max-abs {err:.2e}")
     assert err <= OUT_TOL
+
+
+def _sym_tie_codebook(q_head, seed):
+    """Codewords A and B of group 0 at the same mathematical distance from the
+    query direction u (u_0 = u_1, B is A with coordinates 0 and 1 swapped),
+    such that the oracle's arithmetic (each square rounded, then added) ties
+    them while a fused multiply-add chain puts B strictly nearer.  Returns
+    (A, B) as float32 arrays; the oracle keeps the lower index on the tie."""
+    from fractions import Fraction
+    x = [float(v) for v in q_head]
+    ss = 0.0
+    for v in x:
+        ss = ss + v * v
+    qn = ss ** 0.5
+    u = [v / qn for v in x[:8]]
+    assert u[0] == u[1]
+
+    def unfused(w):
+        d = 0.0
+        for j in range(8):
+            df = u[j] - float(w[j])
+            d = d + df * df
+        return d
+
+    def fused(w):
+        d = 0.0
+        for j in range(8):
+            df = Fraction(u[j] - float(w[j]))
+            d = float(Fraction(d) + df * df)
+        return d
+
+    rng = np.random.default_rng(seed)
+    for _ in range(20000):
+        a = (np.array(u) + rng.uniform(-0.2, 0.2, 8) * np.array([1, 1, .01, .01, .01, .01, .01, .01]))
+        a = a.astype(np.float32)
+        b = a.copy()
+        b[0], b[1] = a[1], a[0]
+        if unfused(a) == unfused(b) and fused(b) < fused(a) and abs(float(a[0]) - float(a[1])) > 0.05:
+            return a, b
+    raise AssertionError("no near tie found")
+
+
+def test_decode_sym_query_code_tie_follows_the_oracles_rounding():
+    """The symmetric variant's query code is decided in double with each
+    square rounded before it is added, as the oracle does.  Two codewords
+    that tie under that arithmetic (the lower index wins) but not under a
+    fused multiply-add chain must still give the oracle's choice."""
+    cfg = small_workload(D=128, Hq=4, Hkv=1, S=1, T=64, seed=8)
+    case = make_case(cfg, lens=[64], mixes=[(0, 10000, 10000)])
+    q = case["q"].clone()
+    q[0, 0, 1] = q[0, 0, 0]
+    case["q"] = q
+    a, b = _sym_tie_codebook(q[0, 0].double().tolist(), seed=3)
+    cb8 = case["cb8"].clone()
+    far = -torch.from_numpy(a.astype(np.float32)) - 1.0
+    cb8[0, 0, :] = far
+    ia, ib = 3, 200
+    cb8[0, 0, ia] = torch.from_numpy(a)
+    cb8[0, 0, ib] = torch.from_numpy(b)
+    case["cb8"] = cb8
+    hc, _ = oracle_cache(case)
+    ref = oracle.decode(hc, case["cb8"], case["cb4"], case["q"], cfg.sigma, logits=True, sym=True)
+    # the other choice (B at the lower index) changes the logits far beyond
+    # the bar, so a wrong query code cannot pass
+    swapped = cb8.clone()
+    swapped[0, 0, ia], swapped[0, 0, ib] = cb8[0, 0, ib], cb8[0, 0, ia]
+    hc2, _ = oracle_cache(dict(case, cb8=swapped))
+    alt = oracle.decode(hc2, swapped, case["cb4"], case["q"], cfg.sigma, logits=True, sym=True)
+    m = ~np.isnan(ref["logits"][0, 0])
+    assert np.abs(alt["logits"][0, 0][m] - ref["logits"][0, 0][m]).max() > 1e-2 * np.abs(ref["logits"][0, 0][m]).max()
+    geom = geom_of(cfg)
+    dc = upload_cache(hc, geom)
+    d = _dev_case(case)
+    flush("[decode_sym] query-code tie")
+    out, lse, lg = decode_outputs(geom, dc, d["q"])
+    ada.decode_sym(geom, dc, d["cb8"], d["cb4"], d["q"], cfg.sigma, out, lse, lg, num_splits=1)
+    torch.cuda.synchronize()
+    ok, worst = logit_tol_ok(lg.cpu().double().numpy(), ref["logits"])
+    assert ok, f"logits off by {worst:.3g} (relative)"
