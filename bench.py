@@ -573,6 +573,49 @@ def measure_step(cfg, L, args, out, lse, ws, timer):
     }
 
 
+def phase_profile(cfg, dev, args):
+    """Per-wave phase timestamps of the page stream (the tracing build,
+    ada_phase_trace) for the last step of graph replays over rotated arena
+    copies, as the step is timed.  Durations in microseconds; percentiles
+    0/10/50/90/100 over all waves (or blocks) of the launch."""
+    log(f"workload {cfg.number} {cfg.name}: building cache on the GPU (tracing build)")
+    L = build_layer(cfg, 0, dev)
+    geom, cache = L["geom"], L["cache"]
+    S, Hq, D, H = cfg.num_seqs, cfg.num_q_heads, cfg.head_dim, cfg.num_kv_heads
+    out = torch.empty((S, Hq, D), device=dev)
+    lse = torch.empty((S, Hq), device=dev)
+    ws = torch.zeros(ada.decode_workspace_size(geom, S, cache.maxp, args.splits), dtype=torch.uint8, device=dev)
+    splits = args.splits or ada.decode_default_splits(geom, S, cache.maxp)
+    waves = 8 if (D == 128 and Hq // H > 4) else 12
+    nblk = S * H * splits
+    trace = torch.zeros(nblk * waves * 8, dtype=torch.int64, device=dev)
+    n_copies = max(2, math.ceil(ROTATE_BYTES / max(cache.used_bytes(), 1)) + 1)
+    views = [cache.view(a) for a in [cache.arena] + [cache.arena.clone() for _ in range(n_copies - 1)]]
+    fns = [(lambda v=v: ada.decode(geom, cache, L["cb8"], L["cb4"], L["q"], cfg.sigma, out, lse,
+                                   num_splits=args.splits, ws=ws, view=v)) for v in views]
+    ada.phase_trace(trace)
+    steps, _, ms = time_graph(fns, args.steps, args.warmup)
+    torch.cuda.synchronize()
+    ada.phase_trace(None)
+    t = trace.view(nblk, waves, 8).cpu().numpy()
+    ts = t[:, :, :6].astype(np.int64)
+    rel = (ts - ts[:, :, 0].min()) / 100.0  # 100 MHz ticks -> us
+
+    def pct(x):
+        return [round(float(np.percentile(x, q)), 2) for q in (0, 10, 50, 90, 100)]
+
+    names = ["prologue_loads", "table_build", "table_barrier_wait", "page_loop", "epilogue"]
+    res = {"workload": cfg.name, "splits": splits, "blocks": nblk, "waves_per_block": waves,
+           "arena_copies": n_copies, "step_us_tracing_build": ms * 1e3,
+           "per_wave_us": {n: pct(rel[:, :, k + 1] - rel[:, :, k]) for k, n in enumerate(names)},
+           "block_start_us": pct(rel[:, :, 0].min(1)),
+           "block_past_table_barrier_us": pct(rel[:, :, 3].max(1)),
+           "block_end_us": pct(rel[:, :, 5].max(1)),
+           "xcc_of_block0": int(t[0, 0, 7] & 7),
+           "xcc_round_robin_fraction": float(np.mean((t[:, 0, 7] & 7) == ((np.arange(nblk) + int(t[0, 0, 7] & 7)) % 8)))}
+    return res
+
+
 def second_context_length(number, dev, args, timer):
     """The same measurement on a second workload (the long-context batch by
     default), reported beside the headline in the same line."""
@@ -616,6 +659,10 @@ def main():
                          "metric is quoted at")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="run one device-to-device copy of this size first (counter calibration)")
+    ap.add_argument("--phase-trace", action="store_true",
+                    help="print the page stream's per-wave phase timestamps instead of the bench "
+                         "line (needs libada_trace.so: python -m compressed_kv_attention_amd.build "
+                         "--phase-trace)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: the ADA decode path has no multi-GPU mode "
@@ -624,9 +671,14 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
+    if args.phase_trace:
+        ada.use_tracing_build()
     ada.load()
     cfg = synth.WORKLOADS[args.workload]
     dev = torch.device("cuda:0")
+    if args.phase_trace:
+        print(json.dumps(phase_profile(cfg, dev, args)))
+        return
     if args.layers > 1:
         if args.layers > cfg.num_layers:
             print(f"workload {cfg.number} has {cfg.num_layers} layer(s)", file=sys.stderr)

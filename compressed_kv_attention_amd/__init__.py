@@ -60,6 +60,17 @@ def lib_path() -> str:
     return _LIB_PATH
 
 
+def use_tracing_build():
+    """Loads libada_trace.so instead of libada.so: the same sources built
+    with per-wave phase timestamps in the page stream (`python -m
+    compressed_kv_attention_amd.build --phase-trace`).  For profiling only;
+    call it before anything loads the library."""
+    global _LIB_PATH
+    if _lib is not None:
+        raise RuntimeError("the library is already loaded")
+    _LIB_PATH = os.path.join(_HERE, "libada_trace.so")
+
+
 def load():
     """Loads libada.so once; raises if it is not built, or if it was built
     from other sources than the ones beside it (a stale library)."""
@@ -134,6 +145,8 @@ def load():
         L.ada_decode_sym_workspace_size.restype = SZ
         L.ada_decode_noalloc.argtypes = [G, CV, P, P, P, F, P, P, P, I32, P]
         L.ada_decode_noalloc.restype = C.c_int
+        L.ada_phase_trace.argtypes = [P, SZ]
+        L.ada_phase_trace.restype = C.c_int
         L.ada_decode_merge.argtypes = [G, CV, P, P, P, F, P, P, I32, P, SZ, P]
         L.ada_decode_merge.restype = C.c_int
         _lib = L
@@ -547,6 +560,16 @@ def decode(geom: Geom, cache: Cache, cb8, cb4, q, softmax_scale: float, out, lse
                            num_splits, _dev(ws, "ws"), ws.numel(), _stream(stream))
     _check(st, "ada_decode")
     return ws
+
+
+def phase_trace(buf: torch.Tensor | None):
+    """ada_phase_trace: decode calls record per-wave phase timestamps into
+    buf (a device tensor the caller keeps alive; None stops).  Only the
+    tracing build records them; any other raises AdaError(EUNSUPPORTED)."""
+    if buf is None:
+        _check(load().ada_phase_trace(None, 0), "ada_phase_trace")
+        return
+    _check(load().ada_phase_trace(_dev(buf, "buf"), buf.numel() * buf.element_size()), "ada_phase_trace")
 
 
 def decode_noalloc(geom: Geom, cache: Cache, cb8, cb4, q, softmax_scale: float, out, lse=None, logits=None,

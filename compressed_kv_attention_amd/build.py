@@ -1,6 +1,11 @@
 """Builds libada.so (the gfx950 HIP library) in place with hipcc.
 
     python -m compressed_kv_attention_amd.build
+    python -m compressed_kv_attention_amd.build --phase-trace
+
+The second builds libada_trace.so instead: the same sources with
+ADA_PHASE_TRACE defined, whose page-stream kernel records per-wave phase
+timestamps (ada_phase_trace), for profiling only.
 """
 from __future__ import annotations
 
@@ -14,6 +19,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 OUT = os.path.join(PKG, "libada.so")
+OUT_TRACE = os.path.join(PKG, "libada_trace.so")
 BUILD = os.path.join(PKG, "_build")
 
 SOURCES = ["ada_abi.cpp", "decode.hip", "encode.hip", "pack.hip", "rdr.hip", "append.hip"]
@@ -45,13 +51,16 @@ def source_digest() -> str:
     return h.hexdigest()
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(BUILD, exist_ok=True)
+def build(verbose: bool = False, phase_trace: bool = False) -> str:
+    bdir = os.path.join(BUILD, "trace") if phase_trace else BUILD
+    out = OUT_TRACE if phase_trace else OUT
+    os.makedirs(bdir, exist_ok=True)
     digest = source_digest()
+    extra = ["-DADA_PHASE_TRACE"] if phase_trace else []
 
     def compile_one(src: str) -> str:
-        obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-        cmd = ["hipcc", *FLAGS, f'-DADA_BUILD_ID="{digest}"', "-c", os.path.join(CSRC, src), "-o", obj]
+        obj = os.path.join(bdir, os.path.splitext(src)[0] + ".o")
+        cmd = ["hipcc", *FLAGS, *extra, f'-DADA_BUILD_ID="{digest}"', "-c", os.path.join(CSRC, src), "-o", obj]
         r = subprocess.run(cmd, capture_output=True, text=True)
         if r.returncode != 0:
             raise RuntimeError(f"hipcc failed for {src}:\n{r.stderr}")
@@ -61,14 +70,14 @@ def build(verbose: bool = False) -> str:
 
     with ThreadPoolExecutor(max_workers=min(4, len(SOURCES))) as ex:
         objs = list(ex.map(compile_one, SOURCES))
-    tmp = OUT + ".tmp"
+    tmp = out + ".tmp"
     cmd = ["hipcc", "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr}")
-    os.replace(tmp, OUT)
-    return OUT
+    os.replace(tmp, out)
+    return out
 
 
 if __name__ == "__main__":
-    print(build(verbose="-v" in sys.argv))
+    print(build(verbose="-v" in sys.argv, phase_trace="--phase-trace" in sys.argv))

@@ -4,10 +4,28 @@
 #include "ada_internal.h"
 
 #include <algorithm>
+#include <atomic>
 #include <cstring>
 #include <vector>
 
 namespace {
+
+// Phase-timestamp buffer of tracing builds (ada_phase_trace): a decode call
+// passes it to the page stream only when its 64 bytes per wave fit.
+std::atomic<void *> g_trace_buf{nullptr};
+std::atomic<size_t> g_trace_bytes{0};
+
+unsigned long long *phase_trace_for(size_t waves)
+{
+#ifdef ADA_PHASE_TRACE
+    void *b = g_trace_buf.load();
+    if (b != nullptr && waves * 64 <= g_trace_bytes.load())
+        return static_cast<unsigned long long *>(b);
+#else
+    (void)waves;
+#endif
+    return nullptr;
+}
 
 using namespace ada;
 
@@ -340,6 +358,7 @@ ada_status decode_common(const ada_geom *g, const ada_cache *c, const float *cb8
     if (decode_shmem_bytes(g->head_dim, NH, dense, ns, c->max_pages_per_head) > kMaxLds)
         return ADA_EINVAL; // too many pages per split: use more splits
     DecodeArgs a;
+    a.trace = phase_trace_for((size_t)rows * ns * decode_waves(g->head_dim, NH));
     a.arena = c->arena;
     a.page_table = c->page_table;
     a.page_meta = c->page_meta;
@@ -390,6 +409,22 @@ int ada_version(void) { return kVersion; }
 #define ADA_BUILD_ID "unknown"
 #endif
 const char *ada_build_id(void) { return ADA_BUILD_ID; }
+
+ada_status ada_phase_trace(void *buf, size_t bytes)
+{
+#ifdef ADA_PHASE_TRACE
+    if (buf != nullptr && ((reinterpret_cast<uintptr_t>(buf) & 7) || bytes < 64))
+        return ADA_EINVAL;
+    g_trace_buf.store(nullptr);
+    g_trace_bytes.store(buf != nullptr ? bytes : 0);
+    g_trace_buf.store(buf);
+    return ADA_OK;
+#else
+    (void)buf;
+    (void)bytes;
+    return ADA_EUNSUPPORTED;
+#endif
+}
 
 size_t ada_page_bytes(int32_t head_dim, int32_t tier)
 {

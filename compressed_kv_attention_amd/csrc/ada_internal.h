@@ -53,6 +53,7 @@ struct DecodeArgs {
     float *part_ml;    // [rows][nsplit][NH][2]  (running max in log2 units, sum)
     float *part_acc;   // [rows][nsplit][NH][D]  (unnormalised output)
     float *glut;       // [rows][LUT floats]: symmetric variant's tabulated LUT, else null
+    unsigned long long *trace; // [blocks][waves][8] phase timestamps (tracing builds), else null
     float sigma;
     int S, Hq, Hkv, maxp, nsplit;
 };
@@ -65,6 +66,8 @@ hipError_t launch_decode(int D, int NH, bool dense, const DecodeArgs &a, hipStre
 // Floats of one row's LUT (the symmetric variant keeps every row's in the
 // workspace).
 size_t decode_lut_floats(int D, int NH);
+// Waves per workgroup of the page-stream kernel.
+int decode_waves(int D, int NH);
 
 // Device address, on the current device, of the library-owned array that
 // holds ada_decode_noalloc's split partials (kNoAllocScratchBytes).

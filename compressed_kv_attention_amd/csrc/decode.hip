@@ -501,6 +501,23 @@ __device__ __forceinline__ void fetch_entry(PageRegs<D> &pr, uint2 e, const uint
     fetch_page<D, DENSE>(pr, arena + (size_t)off * kUnit, meta & 3, ((meta >> 2) & 15) + 1, L);
 }
 
+// ---- phase timestamps (tracing builds only) ------------------------------------
+// With ADA_PHASE_TRACE defined, lane 0 of each wave writes the 100 MHz
+// real-time counter at the phase boundaries of the page stream to
+// a.trace[(block * waves + wave) * 8 + k]: k = 0 entry, 1 prologue loads in,
+// 2 table built, 3 past the table barrier, 4 page loop done, 5 end (every
+// load and store complete), then 6 HW_ID and 7 XCC_ID.  Other builds compile
+// none of it.
+#ifdef ADA_PHASE_TRACE
+#define ADA_PHASE(k)                                                                                   \
+    do {                                                                                               \
+        if (a.trace != nullptr && lane == 0)                                                           \
+            a.trace[((size_t)blockIdx.x * kWaves + wave) * 8 + (k)] = __builtin_amdgcn_s_memrealtime(); \
+    } while (0)
+#else
+#define ADA_PHASE(k) ((void)0)
+#endif
+
 // ---- page stream ------------------------------------------------------------
 // SYM: the symmetric variant; the row's LUT was tabulated by sym_lut_kernel
 // and is copied into LDS instead of being built from the query.
@@ -539,6 +556,7 @@ __global__ __launch_bounds__((Waves<D, NH>::THREADS)) void decode_main(DecodeArg
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const Lane L = make_lane<D, NH>(lane);
+    ADA_PHASE(0);
 
     // This workgroup's pages are p_k = split + k * nsplit, k < n_wg; wave w
     // takes k = w + kWaves * i, i < n_mine.  Their table entries are staged
@@ -659,6 +677,7 @@ __global__ __launch_bounds__((Waves<D, NH>::THREADS)) void decode_main(DecodeArg
         }
     }
     const float lsc = ldexpf(a.sigma, eh) * kLog2e;
+    ADA_PHASE(1);
     // The wave's first page: its loads go out only now, after every other
     // prologue load has been waited for, so the tabulation below overlaps
     // them instead of waiting behind them.
@@ -711,8 +730,10 @@ __global__ __launch_bounds__((Waves<D, NH>::THREADS)) void decode_main(DecodeArg
         }
     }
     const float sig2 = a.sigma * kLog2e;
+    ADA_PHASE(2);
 
     __syncthreads();
+    ADA_PHASE(3);
 
     WaveState<D, NH> st;
 #pragma unroll
@@ -749,6 +770,7 @@ __global__ __launch_bounds__((Waves<D, NH>::THREADS)) void decode_main(DecodeArg
         process_page<D, NH, DENSE>(bufA, split + (wave + kWaves * i) * a.nsplit, st, lut, qo, lsc, sig2,
                                    lgout, a.maxp, L);
     }
+    ADA_PHASE(4);
 
     // Waves -> LDS (the LUT space is free now): [wave][D][NHP] accumulators
     // (element h = head h) and [wave][h] (m, l).
@@ -798,6 +820,15 @@ __global__ __launch_bounds__((Waves<D, NH>::THREADS)) void decode_main(DecodeArg
             a.part_ml[(part * NH + h) * 2 + 1] = l;
         }
     }
+#ifdef ADA_PHASE_TRACE
+    __builtin_amdgcn_s_waitcnt(0);
+    ADA_PHASE(5);
+    if (a.trace != nullptr && lane == 0) {
+        unsigned long long *t = a.trace + ((size_t)blockIdx.x * kWaves + wave) * 8;
+        t[6] = __builtin_amdgcn_s_getreg((4 << 0) | (0 << 6) | (31 << 11));  // HW_ID
+        t[7] = __builtin_amdgcn_s_getreg((20 << 0) | (0 << 6) | (15 << 11)); // XCC_ID
+    }
+#endif
 }
 
 // ---- split merge --------------------------------------------------------------
@@ -1100,6 +1131,8 @@ hipError_t launch_t(const DecodeArgs &a, hipStream_t st, unsigned stages)
 } // namespace
 
 size_t decode_lut_floats(int D, int NH) { return (size_t)(D / 8) * kLutCodes * NH; }
+
+int decode_waves(int D, int NH) { return (D == 128 && NH > 4) ? Waves<128, 8>::W : Waves<64, 1>::W; }
 
 hipError_t noalloc_scratch(void **ptr)
 {

@@ -76,6 +76,25 @@ int ada_version(void);
  * binding compares it with its own sources to refuse a stale library. */
 const char *ada_build_id(void);
 
+/* Phase timestamps of the page-stream kernel, for profiling the decode
+ * step's fixed costs.  Only a library built with ADA_PHASE_TRACE
+ * (`python -m compressed_kv_attention_amd.build --phase-trace`, which makes
+ * libada_trace.so) records them; any other build returns ADA_EUNSUPPORTED
+ * and changes nothing.
+ *   buf    device memory the caller owns and keeps alive while it is set,
+ *          8-byte aligned; NULL stops tracing.
+ *   bytes  its size.
+ * While set, every decode call whose trace fits (64 bytes per wave: blocks
+ * = num_seqs x num_kv_heads x splits, each of 12 waves, or 8 at head_dim
+ * 128 with more than 4 query heads per kv-head) overwrites it: for block b
+ * and wave w, 8 u64 at (b x waves + w) x 8: the 100 MHz real-time counter at
+ * kernel entry, prologue loads in, table built, past the table barrier,
+ * page loop done, end (every load and store complete), then the wave's
+ * HW_ID and XCC_ID registers.  A call whose trace does not fit records
+ * nothing.  Not synchronised with calls in flight: set it between steps.
+ * Errors: ADA_EINVAL for a misaligned buffer or fewer than 64 bytes. */
+ada_status ada_phase_trace(void *buf, size_t bytes);
+
 typedef struct {
     int32_t head_dim;     /* D: 64 or 128 */
     int32_t num_q_heads;  /* Hq */

@@ -36,6 +36,14 @@ def test_status_strings_and_version():
     assert L.ada_version() >= 100
 
 
+def test_phase_trace_is_refused_by_the_product_build():
+    """Only the tracing build records phase timestamps; the product library
+    refuses the call and changes nothing (no device memory is touched)."""
+    L = ada.load()
+    assert L.ada_phase_trace(C.c_void_p(64), 4096) == ada.EUNSUPPORTED
+    assert L.ada_phase_trace(None, 0) == ada.EUNSUPPORTED
+
+
 def test_page_bytes_match_the_format():
     assert [ada.page_bytes(128, t) for t in range(4)] == [8192, 4480, 2304, 8192]
     assert [ada.page_bytes(64, t) for t in range(4)] == [4096, 2304, 1152, 4096]
