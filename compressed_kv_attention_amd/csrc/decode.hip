@@ -986,27 +986,40 @@ __global__ __launch_bounds__(256) void sym_lut_kernel(DecodeArgs a)
         if (tid + 256 * k < NH * D)
             xq[(tid + 256 * k) / D][(tid + 256 * k) % D] = __uint_as_float((uint32_t)qv[k] << 16);
     __syncthreads();
-    // |q_h| summed sequentially in double, as the keys' norms are (each
-    // square is exact in double); the slices are read 32 dims ahead of the
-    // sum so that only the adds form the chain
-    if (tid < NH) {
-        const float4 *xr = reinterpret_cast<const float4 *>(xq[tid]);
-        double ss = 0.0;
+    // |q_h| is the squares summed in order in double, as the keys' norms.
+    // That sum is the exact sum whenever no partial sum needs rounding:
+    // every square is a multiple of 2^e (e the smallest exponent of a
+    // square's last bit), so when the exact total is below 2^(52 + e) every
+    // partial sum, in any order, is exact.  The D/8 lanes of a head (8
+    // coordinates each) sum in a tree and test that; a head that fails it is
+    // summed in order by one lane.
+    if (tid < NH * (D / 8)) {
+        const int h = tid / (D / 8), j8 = tid % (D / 8);
+        const float4 *xr = reinterpret_cast<const float4 *>(xq[h]) + 2 * j8;
+        const float4 va = xr[0], vb = xr[1];
+        const float xs[8] = {va.x, va.y, va.z, va.w, vb.x, vb.y, vb.z, vb.w};
+        double part = 0.0;
+        int emin = 1 << 20;
 #pragma unroll
-        for (int j0 = 0; j0 < D / 4; j0 += 8) {
-            float4 xv[8];
-#pragma unroll
-            for (int j = 0; j < 8; j++)
-                xv[j] = xr[j0 + j];
-#pragma unroll
-            for (int j = 0; j < 8; j++) {
-                ss = ss + (double)xv[j].x * (double)xv[j].x;
-                ss = ss + (double)xv[j].y * (double)xv[j].y;
-                ss = ss + (double)xv[j].z * (double)xv[j].z;
-                ss = ss + (double)xv[j].w * (double)xv[j].w;
-            }
+        for (int j = 0; j < 8; j++) {
+            part = part + (double)xs[j] * (double)xs[j];
+            const uint32_t bits = __float_as_uint(xs[j]);
+            const int ex = (int)((bits >> 23) & 0xff);
+            // last bit of a bf16 value: 2^(E - 134); subnormals 2^-133
+            const int last = ex == 0 ? -133 : ex - 134;
+            emin = (bits & 0x7fffffffu) != 0 ? min(emin, 2 * last) : emin;
         }
-        qn[tid] = sqrt(ss);
+        const double tot = row_sum_f64<D == 64>(part);
+        emin = row_min_i32<D == 64>(emin);
+        if (j8 == 0) {
+            double ss = tot;
+            if (!(tot < ldexp(1.0, 52 + max(emin, -1000)))) {
+                ss = 0.0;
+                for (int j = 0; j < D; j++)
+                    ss = ss + (double)xq[h][j] * (double)xq[h][j];
+            }
+            qn[h] = sqrt(ss);
+        }
     }
     __syncthreads();
     if (tid < NH * 8) {

@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace ada {
 
 // x of lane (l & ~16) and of lane (l | 16), in that order (rows 2r and
@@ -80,6 +82,55 @@ __device__ __forceinline__ void wave_argmin(double &d, int &i)
     lexmin(d, i, od, oi);
     perm_merge<false>(d, i);
     perm_merge<true>(d, i);
+}
+
+// Minimum of an unsigned value over the wave, in every lane (the same
+// permutes as wave_argmin).
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v)
+{
+    v = min(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xf, 0xf, false));
+    v = min(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xf, 0xf, false));
+    v = min(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x141, 0xf, 0xf, false));
+    v = min(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x140, 0xf, 0xf, false));
+    uint32_t lo, hi;
+    pair16(v, lo, hi);
+    v = min(lo, hi);
+    pair32(v, lo, hi);
+    return min(lo, hi);
+}
+
+// Sum of a double over each row of 16 lanes (or each half row of 8 when
+// HALF), in every lane of it: quad, half-row and row butterflies.  The
+// additions' order differs between lanes, so the lanes agree only when the
+// sums are exact.
+template <bool HALF>
+__device__ __forceinline__ double row_sum_f64(double x)
+{
+    auto step = [](double y, auto ctrl) {
+        const uint64_t v = (uint64_t)__double_as_longlong(y);
+        constexpr int C = decltype(ctrl)::value;
+        const uint32_t lo = (uint32_t)__builtin_amdgcn_mov_dpp((int)(uint32_t)v, C, 0xf, 0xf, false);
+        const uint32_t hi = (uint32_t)__builtin_amdgcn_mov_dpp((int)(uint32_t)(v >> 32), C, 0xf, 0xf, false);
+        return y + __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
+    };
+    x = step(x, std::integral_constant<int, 0xB1>{});
+    x = step(x, std::integral_constant<int, 0x4E>{});
+    x = step(x, std::integral_constant<int, 0x141>{});
+    if (!HALF)
+        x = step(x, std::integral_constant<int, 0x140>{});
+    return x;
+}
+
+// Minimum of an int over each row of 16 lanes (or half row of 8).
+template <bool HALF>
+__device__ __forceinline__ int row_min_i32(int x)
+{
+    x = min(x, __builtin_amdgcn_mov_dpp(x, 0xB1, 0xf, 0xf, false));
+    x = min(x, __builtin_amdgcn_mov_dpp(x, 0x4E, 0xf, 0xf, false));
+    x = min(x, __builtin_amdgcn_mov_dpp(x, 0x141, 0xf, 0xf, false));
+    if (!HALF)
+        x = min(x, __builtin_amdgcn_mov_dpp(x, 0x140, 0xf, 0xf, false));
+    return x;
 }
 
 } // namespace ada

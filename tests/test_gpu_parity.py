@@ -508,3 +508,28 @@ def test_decode_sym_query_code_tie_follows_the_oracles_rounding():
     torch.cuda.synchronize()
     ok, worst = logit_tol_ok(lg.cpu().double().numpy(), ref["logits"])
     assert ok, f"logits off by {worst:.3g} (relative)"
+
+
+def test_decode_sym_query_norm_wide_range_and_exact_tree():
+    """The symmetric variant's |q| is the squares summed in order in double.
+    The kernel sums them in a tree when that sum is provably exact, else in
+    order: one head whose squares span far more than 53 bits takes the
+    ordered sum, the others the tree; both must give the oracle's codes."""
+    cfg = small_workload(D=128, Hq=4, Hkv=1, S=1, T=96, seed=12)
+    case = make_case(cfg, lens=[96], mixes=[(1000, 6000, 9000)])
+    q = case["q"].float().clone()
+    q[0, 0, 0::2] *= 2.0 ** 50
+    q[0, 0, 1::2] *= 2.0 ** -50
+    q[0, 1] *= 2.0 ** -100
+    case["q"] = q.to(torch.bfloat16)
+    hc, _ = oracle_cache(case)
+    ref = oracle.decode(hc, case["cb8"], case["cb4"], case["q"], cfg.sigma, logits=True, sym=True)
+    geom = geom_of(cfg)
+    dc = upload_cache(hc, geom)
+    d = _dev_case(case)
+    flush("[decode_sym] wide-range query norms")
+    out, lse, lg = decode_outputs(geom, dc, d["q"])
+    ada.decode_sym(geom, dc, d["cb8"], d["cb4"], d["q"], cfg.sigma, out, lse, lg, num_splits=1)
+    torch.cuda.synchronize()
+    ok, worst = logit_tol_ok(lg.cpu().double().numpy(), ref["logits"])
+    assert ok, f"logits off by {worst:.3g} (relative)"
