@@ -45,6 +45,8 @@
 #include "ada_internal.h"
 #include "wave_ops.h"
 
+#include <atomic>
+
 #include <mutex>
 #include <type_traits>
 
@@ -1113,13 +1115,22 @@ hipError_t launch_t(const DecodeArgs &a, hipStream_t st, unsigned stages)
     if (rows <= 0 || a.nsplit <= 0)
         return hipSuccess;
     const size_t shmem = shmem_bytes<D, NH, DENSE>((a.maxp + a.nsplit - 1) / a.nsplit);
-    static size_t attr_set = 0;
-    if (shmem > attr_set) {
+    // the kernel's dynamic-LDS limit, raised once per device as needed
+    constexpr int kMaxDevices = 64;
+    static std::atomic<size_t> attr_set[kMaxDevices];
+    int dev = 0;
+    if (hipError_t e = hipGetDevice(&dev); e != hipSuccess)
+        return e;
+    if (dev < 0 || dev >= kMaxDevices)
+        return hipErrorInvalidDevice;
+    if (shmem > attr_set[dev].load()) {
         hipError_t e = hipFuncSetAttribute((const void *)decode_main<D, NH, DENSE, SYM>,
                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)shmem);
         if (e != hipSuccess)
             return e;
-        attr_set = shmem;
+        size_t cur = attr_set[dev].load();
+        while (shmem > cur && !attr_set[dev].compare_exchange_weak(cur, shmem)) {
+        }
     }
     hipError_t e = hipSuccess;
     if constexpr (SYM) {
