@@ -24,7 +24,7 @@ __all__ = [
     "decode_workspace_size", "decode", "decode_stage", "dense_decode",
     "code_error", "solve_workspace_size", "rdr_solve", "tier_counts", "pack_tiers_num_pages",
     "rdr_pack_tiers", "rdr_pack_tiers_device", "AppendState", "append", "retier", "retier_plan",
-    "decode_sym_workspace_size", "decode_sym", "decode_noalloc",
+    "decode_sym_workspace_size", "decode_sym", "decode_noalloc", "phase_trace", "use_tracing_build",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
