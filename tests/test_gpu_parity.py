@@ -533,3 +533,58 @@ def test_decode_sym_query_norm_wide_range_and_exact_tree():
     torch.cuda.synchronize()
     ok, worst = logit_tol_ok(lg.cpu().double().numpy(), ref["logits"])
     assert ok, f"logits off by {worst:.3g} (relative)"
+
+
+def test_decode_sym_llama_shape_t32k_full():
+    """The symmetric variant at full size (one T=32768 sequence, 32/8 heads,
+    D=128) in the bench's launch configuration (default splits) and with 7
+    splits: every logit, output and lse against the oracle's."""
+    cfg = synth.WORKLOADS[2]
+    case = make_case(cfg)
+    hc, _ = oracle_cache(case, maxp=1760)
+    ref = oracle.decode(hc, case["cb8"], case["cb4"], case["q"], cfg.sigma, logits=True, nthreads=16, sym=True)
+    geom = geom_of(cfg)
+    dc = upload_cache(hc, geom)
+    d = _dev_case(case)
+    for sp in (0, 7):
+        flush(f"[decode_sym] Llama-3-8B shape T=32768 splits={sp}")
+        out, lse, lg = decode_outputs(geom, dc, d["q"])
+        ada.decode_sym(geom, dc, d["cb8"], d["cb4"], d["q"], cfg.sigma, out, lse, lg, num_splits=sp)
+        torch.cuda.synchronize()
+        ok, worst = logit_tol_ok(lg.cpu().double().numpy(), ref["logits"])
+        assert ok, f"logits off by {worst:.3g} (relative)"
+        err = np.abs(out.cpu().double().numpy() - ref["out"]).max()
+        assert err <= OUT_TOL, f"out max-abs {err:.3g}"
+        l = lse.cpu().double().numpy()
+        assert (np.abs(l - ref["lse"]) <= 1e-3 * np.maximum(np.abs(ref["lse"]), 1.0)).all()
+
+
+def test_dense_llama_shape_t32k_full():
+    """The dense bf16 comparison path at full size (one T=32768 sequence,
+    8 kv-heads, D=128): pages bit-exact, every logit and output against the
+    oracle's dense decode."""
+    cfg = synth.WORKLOADS[2]
+    case = make_case(cfg)
+    D, H, T = cfg.head_dim, cfg.num_kv_heads, int(case["lens"][0])
+    maxp = T // 16 + 4
+    nbytes = T * H * 4 * D + H * 8192
+    hc = oracle.HostCache(D, H, 1, maxp, nbytes, slot_tokens=False)
+    assert oracle.dense_pack(hc, case["cu"], case["keys"], case["values"]) == 0
+    geom = geom_of(cfg)
+    dc = ada.Cache(geom, 1, maxp, nbytes)
+    d = _dev_case(case)
+    flush("[dense] Llama-3-8B shape T=32768")
+    ada.dense_pack(geom, dc, case["cu"], d["keys"], d["values"])
+    torch.cuda.synchronize()
+    used = int(hc.cursor[0]) * 128
+    assert int(dc.cursor[0]) == int(hc.cursor[0])
+    assert np.array_equal(dc.arena[:used].cpu().numpy(), hc.arena[:used])
+    ref = oracle.decode(hc, None, None, case["q"], cfg.sigma, logits=True, nthreads=16)
+    out, lse, lg = decode_outputs(geom, dc, d["q"])
+    ada.dense_decode(geom, dc, d["q"], cfg.sigma, out, lse, lg)
+    torch.cuda.synchronize()
+    ok, worst = logit_tol_ok(lg.cpu().double().numpy(), ref["logits"])
+    assert ok, f"logits off by {worst:.3g} (relative)"
+    err = np.abs(out.cpu().double().numpy() - ref["out"]).max()
+    flush(f"[dense] full size out max-abs {err:.2e}")
+    assert err <= OUT_TOL
