@@ -288,8 +288,17 @@ __global__ __launch_bounds__(256, 4) void encode_kernel(int Hkv, int gx, int64_t
         const uint4 *src4 = reinterpret_cast<const uint4 *>(cb4 + ((size_t)h * G + 4 * gq) * kCodes4 * 8);
         uint4 *dst = reinterpret_cast<uint4 *>(lds);
         constexpr int N8 = 4 * kCodes8 * 2, N4 = 4 * kCodes4 * 2;
-        for (int i = tid; i < N8 + N4; i += 256)
-            dst[i] = i < N8 ? src8[i] : src4[i - N8];
+        constexpr int PER = (N8 + N4 + 255) / 256; // loads per thread, all issued first
+        uint4 v[PER];
+#pragma unroll
+        for (int k = 0; k < PER; k++) {
+            const int i = tid + 256 * k;
+            v[k] = i < N8 ? src8[i] : i < N8 + N4 ? src4[i - N8] : make_uint4(0, 0, 0, 0);
+        }
+#pragma unroll
+        for (int k = 0; k < PER; k++)
+            if (tid + 256 * k < N8 + N4)
+                dst[tid + 256 * k] = v[k];
     }
     __syncthreads();
     // A operands (rows = codewords): lane holds coordinates q and 4 + q of

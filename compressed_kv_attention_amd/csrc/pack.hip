@@ -81,11 +81,20 @@ __device__ void plan_row_on_device(const PackPlan &plan, const PackCache &cache,
     __shared__ int cnt[16][3];
     const int h = row % plan.Hkv;
     int c[3] = {0, 0, 0};
-    for (int i = tid; i < sq.len; i += 1024) {
-        const int t = plan.tiers[((size_t)sq.begin + i) * plan.Hkv + h];
-        c[0] += t == 0;
-        c[1] += t == 1;
-        c[2] += t == 2;
+    // (eight tier bytes in flight per thread per round)
+    for (int i0 = tid; i0 < sq.len; i0 += 8 * 1024) {
+        int t[8];
+#pragma unroll
+        for (int k = 0; k < 8; k++) {
+            const int i = i0 + 1024 * k;
+            t[k] = i < sq.len ? (int)plan.tiers[((size_t)sq.begin + i) * plan.Hkv + h] : 3;
+        }
+#pragma unroll
+        for (int k = 0; k < 8; k++) {
+            c[0] += t[k] == 0;
+            c[1] += t[k] == 1;
+            c[2] += t[k] == 2;
+        }
     }
 #pragma unroll
     for (int k = 0; k < 3; k++) {
@@ -225,8 +234,20 @@ __global__ __launch_bounds__(1024) void pack_rank(PackPlan plan, PackData data, 
             for (int v = 0; v < kKeyRegs; v++)
                 if (tid + 1024 * v < T)
                     count(kc[v]);
-            for (int i = tid + 1024 * kKeyRegs; i < T; i += 1024)
-                count(rank_key(plan, data, ((size_t)sq.begin + i) * plan.Hkv + h, i));
+            // (keys past those held in registers: four loads in flight per
+            // thread per round)
+            for (int i0 = tid + 1024 * kKeyRegs; i0 < T; i0 += 4 * 1024) {
+                uint64_t kk[4];
+#pragma unroll
+                for (int v = 0; v < 4; v++) {
+                    const int i = i0 + 1024 * v;
+                    kk[v] = i < T ? rank_key(plan, data, ((size_t)sq.begin + i) * plan.Hkv + h, i) : 0ull;
+                }
+#pragma unroll
+                for (int v = 0; v < 4; v++)
+                    if (i0 + 1024 * v < T)
+                        count(kk[v]);
+            }
             __syncthreads();
             // wave k finds select k's digit: lane j holds digits 255 - 4j ..
             // 252 - 4j (descending), a wave scan gives the counts above each

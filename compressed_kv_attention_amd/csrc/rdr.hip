@@ -60,16 +60,23 @@ __global__ __launch_bounds__(kErrItems) void code_error_kernel(int Hkv, int64_t 
     const int tid = threadIdx.x;
     const int64_t e0 = (int64_t)blockIdx.x * kErrItems;
     const int n_here = (int)(n_items - e0 < kErrItems ? n_items - e0 : kErrItems);
-    for (int i = tid; i < kErrItems * (D / 8); i += kErrItems) {
-        const int it = i / (D / 8), c = i % (D / 8);
-        uint4 w = make_uint4(0, 0, 0, 0);
-        if (it < n_here)
-            w = *reinterpret_cast<const uint4 *>(keys + (e0 + it) * D + 8 * c);
+    // (every load is issued before any is stored: one memory latency)
+    constexpr int KL = D / 8; // 16-byte loads per thread
+    uint4 kv[KL];
+#pragma unroll
+    for (int k = 0; k < KL; k++) {
+        const int i = tid + k * kErrItems, it = i / (D / 8), c = i % (D / 8);
+        kv[k] = it < n_here ? *reinterpret_cast<const uint4 *>(keys + (e0 + it) * D + 8 * c)
+                            : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int k = 0; k < KL; k++) {
+        const int i = tid + k * kErrItems, it = i / (D / 8), c = i % (D / 8);
         uint32_t *dst = xk + it * RW + 4 * c;
-        dst[0] = w.x;
-        dst[1] = w.y;
-        dst[2] = w.z;
-        dst[3] = w.w;
+        dst[0] = kv[k].x;
+        dst[1] = kv[k].y;
+        dst[2] = kv[k].z;
+        dst[3] = kv[k].w;
     }
     const int64_t e = e0 + tid;
     uint32_t c8w[G / 4], c4w[G / 8];
