@@ -234,20 +234,8 @@ __global__ __launch_bounds__(1024) void pack_rank(PackPlan plan, PackData data, 
             for (int v = 0; v < kKeyRegs; v++)
                 if (tid + 1024 * v < T)
                     count(kc[v]);
-            // (keys past those held in registers: four loads in flight per
-            // thread per round)
-            for (int i0 = tid + 1024 * kKeyRegs; i0 < T; i0 += 4 * 1024) {
-                uint64_t kk[4];
-#pragma unroll
-                for (int v = 0; v < 4; v++) {
-                    const int i = i0 + 1024 * v;
-                    kk[v] = i < T ? rank_key(plan, data, ((size_t)sq.begin + i) * plan.Hkv + h, i) : 0ull;
-                }
-#pragma unroll
-                for (int v = 0; v < 4; v++)
-                    if (i0 + 1024 * v < T)
-                        count(kk[v]);
-            }
+            for (int i = tid + 1024 * kKeyRegs; i < T; i += 1024)
+                count(rank_key(plan, data, ((size_t)sq.begin + i) * plan.Hkv + h, i));
             __syncthreads();
             // wave k finds select k's digit: lane j holds digits 255 - 4j ..
             // 252 - 4j (descending), a wave scan gives the counts above each
