@@ -30,6 +30,7 @@
 // sequence), solve_assign (writes the tiers), tier_counts (one block per
 // row).
 #include "ada_internal.h"
+#include "div_rn.h"
 #include "numfmt.h"
 
 namespace ada {
@@ -47,6 +48,21 @@ namespace {
 // summing a block's norms while the others waited, and four threads per
 // state for the distances, the kernel was 8% slower at 19.5 M states.)
 constexpr int kErrItems = 256; // states per block, one per thread
+constexpr int kErrAhead = 4;   // groups whose codewords are in flight
+
+// The 8-bit and 4-bit codewords of group g of one state (two float4 each).
+__device__ __forceinline__ void gather_codewords(const float *cb8, const float *cb4, int h, int G, int g,
+                                                 const uint32_t *c8w, const uint32_t *c4w, float4 (&w)[4])
+{
+    const int c8 = (c8w[g / 4] >> (8 * (g % 4))) & 255;
+    const int c4 = (c4w[g / 8] >> (4 * (g % 8))) & 15;
+    const float4 *p8 = reinterpret_cast<const float4 *>(cb8 + (((size_t)h * G + g) * kCodes8 + c8) * 8);
+    const float4 *p4 = reinterpret_cast<const float4 *>(cb4 + (((size_t)h * G + g) * kCodes4 + c4) * 8);
+    w[0] = p8[0];
+    w[1] = p8[1];
+    w[2] = p4[0];
+    w[3] = p4[1];
+}
 
 template <int D>
 __global__ __launch_bounds__(kErrItems) void code_error_kernel(int Hkv, int64_t n_items, const uint16_t *keys,
@@ -60,15 +76,32 @@ __global__ __launch_bounds__(kErrItems) void code_error_kernel(int Hkv, int64_t 
     const int tid = threadIdx.x;
     const int64_t e0 = (int64_t)blockIdx.x * kErrItems;
     const int n_here = (int)(n_items - e0 < kErrItems ? n_items - e0 : kErrItems);
-    // (every load is issued before any is stored: one memory latency)
-    constexpr int KL = D / 8; // 16-byte loads per thread
+    // Load order: this thread's codes, the block's keys, then (as soon as
+    // the codes are in) the codewords of the first groups, whose latency
+    // the staging and the norm then cover.  Threads past the block's end
+    // load the last state's codes and write nothing.
+    const int64_t e = e0 + (tid < n_here ? tid : n_here - 1);
+    uint32_t c8w[G / 4], c4w[G / 8];
+#pragma unroll
+    for (int k = 0; k < G / 4; k++)
+        c8w[k] = *reinterpret_cast<const uint32_t *>(codes8 + e * G + 4 * k);
+#pragma unroll
+    for (int k = 0; k < G / 8; k++)
+        c4w[k] = *reinterpret_cast<const uint32_t *>(codes4 + e * (G / 2) + 4 * k);
+    // (rows past the block's end repeat its last key: no branch, so the
+    // wait for the codes below leaves the key loads in flight)
+    constexpr int KL = D / 8; // 16-byte key loads per thread
     uint4 kv[KL];
 #pragma unroll
     for (int k = 0; k < KL; k++) {
         const int i = tid + k * kErrItems, it = i / (D / 8), c = i % (D / 8);
-        kv[k] = it < n_here ? *reinterpret_cast<const uint4 *>(keys + (e0 + it) * D + 8 * c)
-                            : make_uint4(0, 0, 0, 0);
+        kv[k] = *reinterpret_cast<const uint4 *>(keys + (e0 + (it < n_here ? it : n_here - 1)) * D + 8 * c);
     }
+    const int h = (int)(e % Hkv);
+    float4 cw[kErrAhead][4];
+#pragma unroll
+    for (int g = 0; g < kErrAhead; g++)
+        gather_codewords(cb8, cb4, h, G, g, c8w, c4w, cw[g]);
 #pragma unroll
     for (int k = 0; k < KL; k++) {
         const int i = tid + k * kErrItems, it = i / (D / 8), c = i % (D / 8);
@@ -77,16 +110,6 @@ __global__ __launch_bounds__(kErrItems) void code_error_kernel(int Hkv, int64_t 
         dst[1] = kv[k].y;
         dst[2] = kv[k].z;
         dst[3] = kv[k].w;
-    }
-    const int64_t e = e0 + tid;
-    uint32_t c8w[G / 4], c4w[G / 8];
-    if (tid < n_here) {
-#pragma unroll
-        for (int k = 0; k < G / 4; k++)
-            c8w[k] = *reinterpret_cast<const uint32_t *>(codes8 + e * G + 4 * k);
-#pragma unroll
-        for (int k = 0; k < G / 8; k++)
-            c4w[k] = *reinterpret_cast<const uint32_t *>(codes4 + e * (G / 2) + 4 * k);
     }
     __syncthreads();
     if (tid >= n_here)
@@ -108,30 +131,52 @@ __global__ __launch_bounds__(kErrItems) void code_error_kernel(int Hkv, int64_t 
         }
     }
     const double r = sqrt(ss);
-    const double inv = r > 0.0 ? 1.0 / r : 0.0;
-    const int h = (int)(e % Hkv);
     double e8 = 0.0, e4 = 0.0;
-#pragma unroll 2
-    for (int g = 0; g < G; g++) {
-        const int c8 = (c8w[g / 4] >> (8 * (g % 4))) & 255;
-        const int c4 = (c4w[g / 8] >> (4 * (g % 8))) & 15;
-        const float4 *p8 = reinterpret_cast<const float4 *>(cb8 + (((size_t)h * G + g) * kCodes8 + c8) * 8);
-        const float4 *p4 = reinterpret_cast<const float4 *>(cb4 + (((size_t)h * G + g) * kCodes4 + c4) * 8);
-        const float4 a0 = p8[0], a1 = p8[1], b0 = p4[0], b1 = p4[1];
-        const float w8[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
-        const float w4[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
-        const uint32_t w[4] = {row[4 * g], row[4 * g + 1], row[4 * g + 2], row[4 * g + 3]};
-        double d8 = 0.0, d4 = 0.0;
+    if (r > 0.0 && r < INFINITY) {
+        // u = x / r from y = RN(1 / r) (div_rn).  Each group's code is
+        // kept apart from the next (sched_barrier), so the codeword loads
+        // issued for group g + kErrAhead stay behind group g's arithmetic.
+        const double y = 1.0 / r;
 #pragma unroll
-        for (int j = 0; j < 8; j++) {
-            const double x = (double)f16_bits_to_f32((uint16_t)(j & 1 ? w[j / 2] >> 16 : w[j / 2] & 0xffff));
-            const double u = r > 0.0 ? (x / r) : 0.0;
-            const double xa = u - (double)w8[j], xb = u - (double)w4[j];
-            d8 = d8 + xa * xa;
-            d4 = d4 + xb * xb;
+        for (int g = 0; g < G; g++) {
+            float4 (&c)[4] = cw[g % kErrAhead];
+            const float w8[8] = {c[0].x, c[0].y, c[0].z, c[0].w, c[1].x, c[1].y, c[1].z, c[1].w};
+            const float w4[8] = {c[2].x, c[2].y, c[2].z, c[2].w, c[3].x, c[3].y, c[3].z, c[3].w};
+            const uint32_t w[4] = {row[4 * g], row[4 * g + 1], row[4 * g + 2], row[4 * g + 3]};
+            double d8 = 0.0, d4 = 0.0;
+#pragma unroll
+            for (int j = 0; j < 8; j++) {
+                const double x = (double)f16_bits_to_f32((uint16_t)(j & 1 ? w[j / 2] >> 16 : w[j / 2] & 0xffff));
+                const double u = div_rn(x, r, y);
+                const double xa = u - (double)w8[j], xb = u - (double)w4[j];
+                d8 = d8 + xa * xa;
+                d4 = d4 + xb * xb;
+            }
+            e8 = e8 + d8;
+            e4 = e4 + d4;
+            if (g + kErrAhead < G)
+                gather_codewords(cb8, cb4, h, G, g + kErrAhead, c8w, c4w, c);
+            __builtin_amdgcn_sched_barrier(0);
         }
-        e8 = e8 + d8;
-        e4 = e4 + d4;
+    } else {
+        // a zero key (u = 0) or a non-finite one: as the definition divides
+        for (int g = 0; g < G; g++) {
+            float4 c[4];
+            gather_codewords(cb8, cb4, h, G, g, c8w, c4w, c);
+            const float w8[8] = {c[0].x, c[0].y, c[0].z, c[0].w, c[1].x, c[1].y, c[1].z, c[1].w};
+            const float w4[8] = {c[2].x, c[2].y, c[2].z, c[2].w, c[3].x, c[3].y, c[3].z, c[3].w};
+            double d8 = 0.0, d4 = 0.0;
+            for (int j = 0; j < 8; j++) {
+                const uint32_t wd = row[4 * g + j / 2];
+                const double x = (double)f16_bits_to_f32((uint16_t)(j & 1 ? wd >> 16 : wd & 0xffff));
+                const double u = r > 0.0 ? x / r : 0.0;
+                const double xa = u - (double)w8[j], xb = u - (double)w4[j];
+                d8 = d8 + xa * xa;
+                d4 = d4 + xb * xb;
+            }
+            e8 = e8 + d8;
+            e4 = e4 + d4;
+        }
     }
     err8[e] = (float)e8;
     err4[e] = (float)e4;
@@ -261,6 +306,31 @@ __global__ __launch_bounds__(256) void solve_zero(SolveArgs a, int64_t n)
         a.threshold[i] = a.seqs[i].need <= 0 ? -INFINITY : INFINITY;
 }
 
+// A thread's four states' inputs, all loaded at kernel start (before the
+// digit search, which does not need them): one memory latency.
+struct SolveIn {
+    float w[4], e8[4], e4[4];
+    uint16_t r[4];
+    bool live[4];
+};
+
+__device__ __forceinline__ SolveIn solve_inputs(const SolveArgs &a, int64_t first, int64_t end, int tid)
+{
+    SolveIn in;
+#pragma unroll
+    for (int k = 0; k < 4; k++) {
+        const int64_t i = first + tid + k * kSolveThreads;
+        const bool ok = i < end;
+        const int64_t j = ok ? i : first; // (a valid index; its values are unused)
+        in.w[k] = a.scores[j];
+        in.r[k] = a.radius[j];
+        in.e8[k] = a.err8[j];
+        in.e4[k] = a.err4[j];
+        in.live[k] = ok && (a.protect == nullptr || a.protect[j] == 0);
+    }
+    return in;
+}
+
 template <int P>
 __global__ __launch_bounds__(kSolveThreads) void solve_pass(SolveArgs a)
 {
@@ -271,6 +341,8 @@ __global__ __launch_bounds__(kSolveThreads) void solve_pass(SolveArgs a)
     const int tid = threadIdx.x;
     if (sq.need <= 0)
         return;
+    const int64_t end = sq.begin + sq.n_items;
+    const SolveIn in = solve_inputs(a, blk.first, end, tid);
     h[tid] = 0ull;
     if (tid < 64) {
         const Sel r = select_prefix(a, blk.seq, P);
@@ -281,13 +353,11 @@ __global__ __launch_bounds__(kSolveThreads) void solve_pass(SolveArgs a)
     if (sel.state != 0)
         return;
     const uint32_t prefix = sel.prefix;
-    const int64_t end = sq.begin + sq.n_items;
 #pragma unroll
     for (int k = 0; k < 4; k++) {
-        const int64_t i = blk.first + tid + k * kSolveThreads;
-        if (i >= end || (a.protect != nullptr && a.protect[i] != 0))
+        if (!in.live[k])
             continue;
-        const Chain ch = make_chain(a.D, a.scores[i], a.radius[i], a.err8[i], a.err4[i]);
+        const Chain ch = make_chain(a.D, in.w[k], in.r[k], in.e8[k], in.e4[k]);
 #pragma unroll
         for (int n = 0; n < 3; n++) {
             const uint32_t key = ch.key[n];
@@ -306,6 +376,8 @@ __global__ __launch_bounds__(kSolveThreads) void solve_assign(SolveArgs a)
     const SolveBlock blk = a.blocks[blockIdx.x];
     const SolveSeq sq = a.seqs[blk.seq];
     const int tid = threadIdx.x;
+    const int64_t end = sq.begin + sq.n_items;
+    const SolveIn in = solve_inputs(a, blk.first, end, tid);
     if (tid < 64) {
         const Sel r = select_prefix(a, blk.seq, kSolvePasses);
         if (tid == 0)
@@ -319,15 +391,14 @@ __global__ __launch_bounds__(kSolveThreads) void solve_assign(SolveArgs a)
         const uint32_t bits = (kstar & 0x80000000u) ? (kstar & 0x7fffffffu) : ~kstar;
         a.threshold[blk.seq] = state == 1 ? -INFINITY : state == 2 ? INFINITY : __uint_as_float(bits);
     }
-    const int64_t end = sq.begin + sq.n_items;
 #pragma unroll
     for (int k = 0; k < 4; k++) {
         const int64_t i = blk.first + tid + k * kSolveThreads;
         if (i >= end)
             continue;
         int t = 0;
-        if (state != 1 && (a.protect == nullptr || a.protect[i] == 0)) {
-            const Chain ch = make_chain(a.D, a.scores[i], a.radius[i], a.err8[i], a.err4[i]);
+        if (state != 1 && in.live[k]) {
+            const Chain ch = make_chain(a.D, in.w[k], in.r[k], in.e8[k], in.e4[k]);
             bool go = true;
 #pragma unroll
             for (int n = 0; n < 3; n++) {

@@ -51,6 +51,64 @@ def test_code_error_bit_exact(D):
         assert np.array_equal(e8.cpu().numpy(), r8) and np.array_equal(e4.cpu().numpy(), r4)
 
 
+
+def _extreme_keys(T, H, D, seed):
+    """fp16 key bits [T][H][D] over the cases that stress u = k / |k|: zero
+    keys (u = 0), one nonzero coordinate (u = +-1), four equal powers of two
+    (|k| a power of two), exponents over the whole binary16 range,
+    subnormals only, +-65504 beside subnormals, and scaled normal keys."""
+    rng = np.random.default_rng(seed)
+    k = np.zeros((T, H, D), dtype=np.uint16)
+    for t in range(T):
+        for h in range(H):
+            kind = (t * H + h) % 8
+            if kind == 0:
+                continue
+            if kind == 1:
+                k[t, h, rng.integers(D)] = rng.integers(1, 0x7c00) | (rng.integers(2) << 15)
+            elif kind == 2:
+                e = rng.integers(0, 30)
+                k[t, h, rng.choice(D, 4, replace=False)] = (e << 10) if e else 1 << rng.integers(10)
+            elif kind == 3:
+                k[t, h] = (rng.integers(0, 31, D) << 10) | rng.integers(0, 1024, D) | (rng.integers(0, 2, D) << 15)
+            elif kind == 4:
+                k[t, h] = rng.integers(0, 1024, D) | (rng.integers(0, 2, D) << 15)
+            elif kind == 5:
+                v = rng.integers(0, 1024, D) | (rng.integers(0, 2, D) << 15)
+                v[rng.choice(D, 3, replace=False)] = 0x7bff | (rng.integers(2) << 15)
+                k[t, h] = v
+            else:
+                x = rng.standard_normal(D) * 2.0 ** rng.integers(-20, 13)
+                k[t, h] = np.clip(x, -65504, 65504).astype(np.float16).view(np.uint16)
+    return k
+
+
+@pytest.mark.parametrize("D", [64, 128])
+def test_code_error_bit_exact_extreme_keys(D):
+    """Key norms from zero to fp16 overflow range, over partial blocks: the
+    errors bit-exact with the oracle's division by the norm."""
+    cfg = small_workload(D=D, Hq=4, Hkv=2, S=1, T=600, seed=90 + D)
+    case = make_case(cfg, lens=[600])
+    keys = _extreme_keys(600, 2, D, seed=D)
+    assert np.isfinite(keys.view(np.float16)).all()
+    case["keys"] = torch.from_numpy(keys.view(np.float16))
+    r, c8, c4 = _codes(case)
+    rng = np.random.default_rng(D + 1)
+    rc8 = rng.integers(0, 256, c8.shape).astype(np.uint8)
+    rc4 = rng.integers(0, 256, c4.shape).astype(np.uint8)
+    geom = geom_of(cfg)
+    k = to_dev(case["keys"])
+    cb8, cb4 = to_dev(case["cb8"]), to_dev(case["cb4"])
+    for codes8, codes4, label in ((c8, c4, "nearest"), (rc8, rc4, "random")):
+        flush(f"[code_error extreme keys] D={D} {label}")
+        e8 = torch.full(c8.shape[:2], float("nan"), device="cuda")
+        e4 = torch.full(c8.shape[:2], float("nan"), device="cuda")
+        ada.code_error(geom, k, cb8, cb4, to_dev(codes8), to_dev(codes4), e8, e4)
+        torch.cuda.synchronize()
+        r8, r4 = oracle.code_error(case["keys"], case["cb8"], case["cb4"], codes8, codes4)
+        assert np.isfinite(r8).all() and np.isfinite(r4).all()
+        assert np.array_equal(e8.cpu().numpy(), r8) and np.array_equal(e4.cpu().numpy(), r4)
+
 def _solve_both(geom, D, cu, budgets, r, e8, e4, sc, prot=None):
     tiers = torch.full(r.shape, 77, dtype=torch.uint8, device="cuda")
     ada.rdr_solve(geom, cu, budgets, to_dev(r), to_dev(e8), to_dev(e4), to_dev(sc), tiers,
