@@ -938,164 +938,177 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge(DecodeArgs a)
 }
 
 // ---- symmetric variant: the LUT from the query's codes -------------------------
-// One block per (row, group g).  The query direction u_q = q / |q| (|q|
-// summed sequentially over D, in double) takes in each codebook the index
-// of its nearest codeword (squared distance in double, lowest index on
-// ties), as a key does in encode; then LUT_g[c][h] = |q_h| C_g[cq_h] .
-// C_g[c] (fp32 dot product), written in the page stream's LDS layout.
+// One wave per (row, group g, query head h), with no barrier and no LDS.
+// The query direction u_q = q / |q| (|q| summed sequentially over D, in
+// double) takes in each codebook the index of its nearest codeword (squared
+// distance in double, lowest index on ties), as a key does in encode; then
+// LUT_g[c][h] = |q_h| C_g[cq_h] . C_g[c] (fp32 dot product), written in the
+// page stream's LDS layout.
+template <int NH, int G>
+__device__ __forceinline__ float *lut_slot(float *lut, int idx, int h)
+{
+    constexpr int NQF = Heads<NH>::NQF, REM = Heads<NH>::REM;
+    constexpr int REGION = G * kLutCodes * 4;
+    return h < 4 * NQF ? lut + (h / 4) * REGION + idx * 4 + (h % 4)
+                       : lut + NQF * REGION + idx * REM + (h - 4 * NQF);
+}
+
+__device__ __forceinline__ double readlane_f64(double x, int l)
+{
+    const uint64_t v = (uint64_t)__double_as_longlong(x);
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, l);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), l);
+    return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
+}
+
+__device__ __forceinline__ float readlane_f32(float x, int l)
+{
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), l));
+}
+
 template <int D, int NH>
-__global__ __launch_bounds__(256) void sym_lut_kernel(DecodeArgs a)
+__global__ __launch_bounds__(64 * NH) void sym_lut_kernel(DecodeArgs a)
 {
     // the query code is decided in double with every product rounded
     // before it is added, as the definition does: no fused multiply-adds
 #pragma clang fp contract(off)
     constexpr int G = D / 8, LUT_FLOATS = G * kLutCodes * NH;
-    __shared__ double qn[NH], u[NH][8];
-    __shared__ __align__(16) float xq[NH][D];
-    __shared__ float4 cw[kLutCodes][2]; // group g's codewords: 256 8-bit, then 16 4-bit
-    __shared__ double bd[4][NH];
-    __shared__ int bc[4][NH];
-    __shared__ int cq8[NH], cq4[NH];
-    const int row = blockIdx.x, g = blockIdx.y, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int row = blockIdx.x, g = blockIdx.y, lane = threadIdx.x & 63;
+    const int h = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int s = row / a.Hkv, hkv = row % a.Hkv;
-    const uint16_t *qrow = a.q + ((size_t)s * a.Hq + (size_t)hkv * NH) * D;
+    const uint16_t *qh = a.q + ((size_t)s * a.Hq + (size_t)hkv * NH + h) * D;
     const float *c8 = a.cb8 + ((size_t)hkv * G + g) * kCodes8 * 8;
     const float *c4 = a.cb4 + ((size_t)hkv * G + g) * kCodes4 * 8;
     // Every global load is issued before any is used (one memory latency):
-    // thread t's 8-bit codeword t, lanes 0..15 of wave 0 the 4-bit ones,
-    // and the query slices.
-    const float4 w0 = *reinterpret_cast<const float4 *>(c8 + tid * 8);
-    const float4 w1 = *reinterpret_cast<const float4 *>(c8 + tid * 8 + 4);
-    const int cc = lane & 15;
-    float4 v0 = make_float4(0.f, 0.f, 0.f, 0.f), v1 = v0;
-    if (wave == 0) {
-        v0 = *reinterpret_cast<const float4 *>(c4 + cc * 8);
-        v1 = *reinterpret_cast<const float4 *>(c4 + cc * 8 + 4);
-    }
-    constexpr int QPT = (NH * D + 255) / 256; // query elements per thread
-    uint16_t qv[QPT];
+    // lane l's 8-bit codewords l + 64 k, its 4-bit codeword l % 16, and
+    // (lanes below G) query coordinates 8 l .. 8 l + 7.
+    float4 w0[4], w1[4];
 #pragma unroll
-    for (int k = 0; k < QPT; k++)
-        qv[k] = tid + 256 * k < NH * D ? qrow[tid + 256 * k] : 0;
-    cw[tid][0] = w0;
-    cw[tid][1] = w1;
-    if (wave == 0 && lane < kCodes4) {
-        cw[kCodes8 + lane][0] = v0;
-        cw[kCodes8 + lane][1] = v1;
+    for (int k = 0; k < 4; k++) {
+        w0[k] = *reinterpret_cast<const float4 *>(c8 + (lane + 64 * k) * 8);
+        w1[k] = *reinterpret_cast<const float4 *>(c8 + (lane + 64 * k) * 8 + 4);
     }
-#pragma unroll
-    for (int k = 0; k < QPT; k++)
-        if (tid + 256 * k < NH * D)
-            xq[(tid + 256 * k) / D][(tid + 256 * k) % D] = __uint_as_float((uint32_t)qv[k] << 16);
-    __syncthreads();
+    const int c4i = lane & 15; // (lanes 16 .. 63 repeat lanes 0 .. 15)
+    const float4 v0 = *reinterpret_cast<const float4 *>(c4 + c4i * 8);
+    const float4 v1 = *reinterpret_cast<const float4 *>(c4 + c4i * 8 + 4);
+    const uint4 qv = *reinterpret_cast<const uint4 *>(qh + 8 * (lane < G ? lane : 0));
+    const uint32_t qw[4] = {qv.x, qv.y, qv.z, qv.w};
+
     // |q_h| is the squares summed in order in double, as the keys' norms.
     // That sum is the exact sum whenever no partial sum needs rounding:
     // every square is a multiple of 2^e (e the smallest exponent of a
     // square's last bit), so when the exact total is below 2^(52 + e) every
-    // partial sum, in any order, is exact.  The D/8 lanes of a head (8
-    // coordinates each) sum in a tree and test that; a head that fails it is
-    // summed in order by one lane.
-    if (tid < NH * (D / 8)) {
-        const int h = tid / (D / 8), j8 = tid % (D / 8);
-        const float4 *xr = reinterpret_cast<const float4 *>(xq[h]) + 2 * j8;
-        const float4 va = xr[0], vb = xr[1];
-        const float xs[8] = {va.x, va.y, va.z, va.w, vb.x, vb.y, vb.z, vb.w};
-        double part = 0.0;
-        int emin = 1 << 20;
+    // partial sum, in any order, is exact.  The G lanes (8 coordinates
+    // each) sum in a tree and test that; otherwise the wave sums in order.
+    double part = 0.0;
+    int emin = 1 << 20;
+#pragma unroll
+    for (int j = 0; j < 8; j++) {
+        const float x = __uint_as_float((j & 1 ? qw[j / 2] >> 16 : qw[j / 2] & 0xffffu) << 16);
+        part = part + (double)x * (double)x;
+        const uint32_t bits = __float_as_uint(x);
+        const int ex = (int)((bits >> 23) & 0xff);
+        // last bit of a bf16 value: 2^(E - 134); subnormals 2^-133
+        const int last = ex == 0 ? -133 : ex - 134;
+        emin = (bits & 0x7fffffffu) != 0 ? min(emin, 2 * last) : emin;
+    }
+    const double tot = readlane_f64(row_sum_f64<D == 64>(part), 0);
+    const int emin0 = __builtin_amdgcn_readlane(row_min_i32<D == 64>(emin), 0);
+    double ss = tot;
+    if (!(tot < ldexp(1.0, 52 + max(emin0, -1000)))) {
+        ss = 0.0;
+        for (int j8 = 0; j8 < G; j8++) {
+#pragma unroll
+            for (int e = 0; e < 4; e++) {
+                const uint32_t wv = (uint32_t)__builtin_amdgcn_readlane((int)qw[e], j8);
+                const double lo = (double)__uint_as_float(wv << 16);
+                const double hi = (double)__uint_as_float(wv & 0xffff0000u);
+                ss = ss + lo * lo;
+                ss = ss + hi * hi;
+            }
+        }
+    }
+    const double qn = sqrt(ss);
+    // this group's direction slice, from lane g's coordinates
+    double u[8];
+#pragma unroll
+    for (int e = 0; e < 4; e++) {
+        const uint32_t wv = (uint32_t)__builtin_amdgcn_readlane((int)qw[e], g);
+        const double lo = (double)__uint_as_float(wv << 16);
+        const double hi = (double)__uint_as_float(wv & 0xffff0000u);
+        u[2 * e] = qn > 0.0 ? lo / qn : 0.0;
+        u[2 * e + 1] = qn > 0.0 ? hi / qn : 0.0;
+    }
+    // nearest 8-bit codeword: lane l scores l, l + 64, l + 128, l + 192
+    double bd = INFINITY;
+    int bc = 0;
+#pragma unroll
+    for (int k = 0; k < 4; k++) {
+        const float w[8] = {w0[k].x, w0[k].y, w0[k].z, w0[k].w, w1[k].x, w1[k].y, w1[k].z, w1[k].w};
+        double d = 0.0;
 #pragma unroll
         for (int j = 0; j < 8; j++) {
-            part = part + (double)xs[j] * (double)xs[j];
-            const uint32_t bits = __float_as_uint(xs[j]);
-            const int ex = (int)((bits >> 23) & 0xff);
-            // last bit of a bf16 value: 2^(E - 134); subnormals 2^-133
-            const int last = ex == 0 ? -133 : ex - 134;
-            emin = (bits & 0x7fffffffu) != 0 ? min(emin, 2 * last) : emin;
+            const double df = u[j] - (double)w[j];
+            d = d + df * df;
         }
-        const double tot = row_sum_f64<D == 64>(part);
-        emin = row_min_i32<D == 64>(emin);
-        if (j8 == 0) {
-            double ss = tot;
-            if (!(tot < ldexp(1.0, 52 + max(emin, -1000)))) {
-                ss = 0.0;
-                for (int j = 0; j < D; j++)
-                    ss = ss + (double)xq[h][j] * (double)xq[h][j];
-            }
-            qn[h] = sqrt(ss);
+        if (k == 0 || d < bd) {
+            bd = d;
+            bc = lane + 64 * k;
         }
     }
-    __syncthreads();
-    if (tid < NH * 8) {
-        const int h = tid / 8, j = tid % 8;
-        const double x = (double)xq[h][8 * g + j];
-        u[h][j] = qn[h] > 0.0 ? x / qn[h] : 0.0;
-    }
-    __syncthreads();
-    // nearest 8-bit codeword per head: thread t scores codeword t
+    wave_argmin(bd, bc);
+    const int cq8 = __builtin_amdgcn_readfirstlane(bc);
+    // nearest 4-bit codeword
     {
-        const float w[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
-#pragma unroll
-        for (int h = 0; h < NH; h++) {
-            double d = 0.0;
-#pragma unroll
-            for (int j = 0; j < 8; j++) {
-                const double df = u[h][j] - (double)w[j];
-                d = d + df * df;
-            }
-            int c = tid;
-            wave_argmin(d, c);
-            if (lane == 0) {
-                bd[wave][h] = d;
-                bc[wave][h] = c;
-            }
-        }
-    }
-    // nearest 4-bit codeword per head: lanes 0..15 of wave 0
-    if (wave == 0) {
         const float w[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+        double d = 0.0;
 #pragma unroll
-        for (int h = 0; h < NH; h++) {
-            double d = 0.0;
-#pragma unroll
-            for (int j = 0; j < 8; j++) {
-                const double df = u[h][j] - (double)w[j];
-                d = d + df * df;
-            }
-            int c = cc; // (lanes 16 .. 63 repeat lanes 0 .. 15)
-            wave_argmin(d, c);
-            if (lane == 0)
-                cq4[h] = c;
+        for (int j = 0; j < 8; j++) {
+            const double df = u[j] - (double)w[j];
+            d = d + df * df;
         }
+        bd = d;
+        bc = c4i;
     }
-    __syncthreads();
-    if (tid < NH) {
-        double d = bd[0][tid];
-        int c = bc[0][tid];
-        for (int w = 1; w < 4; w++)
-            if (bd[w][tid] < d || (bd[w][tid] == d && bc[w][tid] < c)) {
-                d = bd[w][tid];
-                c = bc[w][tid];
+    wave_argmin(bd, bc);
+    const int cq4 = __builtin_amdgcn_readfirstlane(bc);
+    // the two query codewords, read from the lanes that hold them (every
+    // candidate register is read and the uniform index picks one, so no
+    // register array is indexed at run time)
+    float wq8[8], wq4[8];
+    {
+        const int kq = cq8 >> 6, lq = cq8 & 63;
+#pragma unroll
+        for (int j = 0; j < 8; j++) {
+            float r[4];
+#pragma unroll
+            for (int k = 0; k < 4; k++) {
+                const float4 &c = j < 4 ? w0[k] : w1[k];
+                const float x = (j & 3) == 0 ? c.x : (j & 3) == 1 ? c.y : (j & 3) == 2 ? c.z : c.w;
+                r[k] = readlane_f32(x, lq);
             }
-        cq8[tid] = c;
+            wq8[j] = kq == 0 ? r[0] : kq == 1 ? r[1] : kq == 2 ? r[2] : r[3];
+        }
+        const float t4[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+#pragma unroll
+        for (int j = 0; j < 8; j++)
+            wq4[j] = readlane_f32(t4[j], cq4);
     }
-    __syncthreads();
     float *lut = a.glut + (size_t)row * LUT_FLOATS;
-    for (int c = tid; c < kLutCodes; c += 256) {
-        const float4 c0 = cw[c][0], c1 = cw[c][1];
+    const float qf = (float)qn;
+    auto entry = [&](const float4 &c0, const float4 &c1, const float (&wq)[8], int c) {
         const float wc[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
-        float o[NH];
+        float acc = wq[0] * wc[0];
 #pragma unroll
-        for (int h = 0; h < NH; h++) {
-            const int iq = c < kCodes8 ? cq8[h] : kCodes8 + cq4[h];
-            const float4 q0 = cw[iq][0], q1 = cw[iq][1];
-            const float wq[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
-            float acc = wq[0] * wc[0];
+        for (int j = 1; j < 8; j++)
+            acc = fmaf(wq[j], wc[j], acc);
+        *lut_slot<NH, G>(lut, g * kLutCodes + c, h) = acc * qf;
+    };
 #pragma unroll
-            for (int j = 1; j < 8; j++)
-                acc = fmaf(wq[j], wc[j], acc);
-            o[h] = acc * (float)qn[h];
-        }
-        lut_store<NH, G>(lut, g * kLutCodes + c, o);
-    }
+    for (int k = 0; k < 4; k++)
+        entry(w0[k], w1[k], wq8, lane + 64 * k);
+    if (lane < kCodes4)
+        entry(v0, v1, wq4, kCodes8 + lane);
 }
 
 template <int D, int NH, bool DENSE>
@@ -1135,7 +1148,7 @@ hipError_t launch_t(const DecodeArgs &a, hipStream_t st, unsigned stages)
     hipError_t e = hipSuccess;
     if constexpr (SYM) {
         if (stages & kStageStream) {
-            hipLaunchKernelGGL((sym_lut_kernel<D, NH>), dim3(rows, D / 8), dim3(256), 0, st, a);
+            hipLaunchKernelGGL((sym_lut_kernel<D, NH>), dim3(rows, D / 8), dim3(64 * NH), 0, st, a);
             e = hipGetLastError();
             if (e != hipSuccess)
                 return e;

@@ -204,6 +204,27 @@ def test_encode_tiny_and_small():
     _check_encode(cfg, case, "D=128 with zero and extreme keys")
 
 
+
+def test_encode_radius_at_fp16_rounding_boundaries():
+    """Keys whose norm is an fp16 rounding midpoint exactly, or just above
+    one: 2^k (1, 2^-5, 2^-11) has norm 2^k (1 + 2^-11), the midpoint between
+    2^k and its fp16 successor (a tie: rounds to even), and a fourth
+    coordinate of 2^(k-24) moves it above the midpoint by 2^-49 relative
+    (rounds up).  The radius must follow the defining norm bit for bit."""
+    cfg = small_workload(D=128, Hq=4, Hkv=2, S=1, T=96, seed=63)
+    case = make_case(cfg)
+    k = case["keys"]
+    for t in range(96):
+        for hh in range(2):
+            e = (t % 24) - 8 if hh == 0 else (t % 16)
+            row = torch.zeros(128, dtype=torch.float32)
+            row[[3, 40, 77]] = torch.tensor([2.0 ** e, 2.0 ** (e - 5), 2.0 ** (e - 11)])
+            if t % 2 and e - 24 >= -24:
+                row[120] = 2.0 ** (e - 24)
+            k[t, hh] = row.to(torch.float16)
+    assert torch.isfinite(k.float()).all()
+    _check_encode(cfg, case, "norms at fp16 rounding midpoints")
+
 def test_encode_near_ties_exact():
     """Codebooks whose codewords come in pairs -- equal, or one binary32 ulp
     apart in one coordinate -- make nearly every nearest codeword a near tie
