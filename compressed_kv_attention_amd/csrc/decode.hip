@@ -95,10 +95,13 @@ __device__ __forceinline__ uint32_t pack_bf16(float a, float b)
 __device__ __forceinline__ float bf16_lo(uint32_t u) { return __uint_as_float(u << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t u) { return __uint_as_float(u & 0xffff0000u); }
 
+// A lane permutation within rows (quad_perm, row_ror, row mirrors: every
+// source lane exists, so bound_ctrl changes nothing; with it set the
+// compiler folds the move into the consuming add).
 template <int CTRL>
 __device__ __forceinline__ float dpp(float x)
 {
-    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xf, 0xf, false));
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xf, 0xf, true));
 }
 
 // Max / sum over the four lanes h, h+16, h+32, h+48 (every lane receives it).
@@ -132,21 +135,23 @@ struct Heads {
     static constexpr int NQ = (NH + 3) / 4; // head quads of the output tile
 };
 
-template <int NH, int G>
+// sum[h] += LUT entry (idx, h), or sum[h] = the entry when FIRST
+template <int NH, int G, bool FIRST>
 __device__ __forceinline__ void lut_add(const float *lut, int idx, float (&sum)[NH])
 {
     constexpr int NQF = Heads<NH>::NQF, REM = Heads<NH>::REM;
     constexpr int REGION = G * kLutCodes * 4; // floats of one head-quad region
+    auto put = [&](int h, float v) { sum[h] = FIRST ? v : sum[h] + v; };
 #pragma unroll
     for (int j = 0; j < NQF; j++) {
         const float4 v = *reinterpret_cast<const float4 *>(lut + j * REGION + idx * 4);
-        sum[4 * j] += v.x; sum[4 * j + 1] += v.y; sum[4 * j + 2] += v.z; sum[4 * j + 3] += v.w;
+        put(4 * j, v.x); put(4 * j + 1, v.y); put(4 * j + 2, v.z); put(4 * j + 3, v.w);
     }
     if constexpr (REM == 2) {
         const float2 v = *reinterpret_cast<const float2 *>(lut + NQF * REGION + idx * 2);
-        sum[4 * NQF] += v.x; sum[4 * NQF + 1] += v.y;
+        put(4 * NQF, v.x); put(4 * NQF + 1, v.y);
     } else if constexpr (REM == 1) {
-        sum[4 * NQF] += lut[NQF * REGION + idx];
+        put(4 * NQF, lut[NQF * REGION + idx]);
     }
 }
 
@@ -326,12 +331,12 @@ __device__ __forceinline__ void coded_logits(const PageRegs<D> &cur, const float
     const int base = t8 ? 0 : kCodes8;
     float s[NH];
 #pragma unroll
-    for (int h = 0; h < NH; h++)
-        s[h] = 0.f;
-#pragma unroll
     for (int k = 0; k < GPL; k++) {
         const int code = base + (int)__builtin_amdgcn_ubfe(bits, k * width, width);
-        lut_add<NH, D / 8>(lut, (L.g0 + k) * kLutCodes + code, s);
+        if (k == 0)
+            lut_add<NH, D / 8, true>(lut, (L.g0 + k) * kLutCodes + code, s);
+        else
+            lut_add<NH, D / 8, false>(lut, (L.g0 + k) * kLutCodes + code, s);
     }
     // complete each slot's sum over its four lanes (a quad)
 #pragma unroll
