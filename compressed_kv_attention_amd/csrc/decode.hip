@@ -112,6 +112,24 @@ __device__ __forceinline__ float rows_max(float x)
     auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
     return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
+// max(a, b) for non-NaN operands in one instruction (the median of a, b
+// and +inf), with no canonicalising moves
+// (+inf is passed through an empty asm so that the median is not folded
+// back into a maxnum, which would canonicalise both operands first)
+__device__ __forceinline__ float max_nn(float a, float b)
+{
+    float inf;
+    asm("; +inf" : "=v"(inf) : "0"(INFINITY));
+    return __builtin_amdgcn_fmed3f(a, b, inf);
+}
+// rows_max for non-NaN values
+__device__ __forceinline__ float rows_max_nn(float x)
+{
+    auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = max_nn(__uint_as_float(a[0]), __uint_as_float(a[1]));
+    auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return max_nn(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
 __device__ __forceinline__ float rows_sum(float x)
 {
     auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
@@ -410,7 +428,8 @@ __device__ __forceinline__ void process_page(PageRegs<D> &cur, int p, WaveState<
     // online softmax: per-head page maxima; one wave-wide test whether any
     // of them runs ahead of its running maximum (lanes of unused heads have
     // pm = -inf and never do), the per-head rescale only then
-    const float pm = rows_max(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])));
+    // (logits are finite or -inf)
+    const float pm = rows_max_nn(max_nn(max_nn(x[0], x[1]), max_nn(x[2], x[3])));
     if (__builtin_amdgcn_ballot_w64(pm > st.mlane + kRescale) != 0) {
         // head h's outputs are element h % 4 of the C tiles in lanes
         // 16 (h / 4) .. 16 (h / 4) + 15
