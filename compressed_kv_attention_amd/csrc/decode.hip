@@ -193,10 +193,10 @@ __device__ __forceinline__ void lut_store(float *lut, int idx, const float (&o)[
 // registers.  A lane's code bytes never straddle an 8-byte boundary.
 __device__ __forceinline__ uint32_t bits_at(const u32x4 &v, int o)
 {
-    const uint64_t lo = ((uint64_t)v.y << 32) | v.x;
-    const uint64_t hi = ((uint64_t)v.w << 32) | v.z;
-    const uint64_t m = 0ull - (uint64_t)((o >> 3) & 1);
-    return (uint32_t)(((lo & ~m) | (hi & m)) >> (8 * (o & 7)));
+    // (32-bit masks, so each half is one bitfield insert)
+    const uint32_t m = 0u - (((uint32_t)o >> 3) & 1u);
+    const uint32_t lo = (v.z & m) | (v.x & ~m), hi = (v.w & m) | (v.y & ~m);
+    return (uint32_t)((((uint64_t)hi << 32) | lo) >> (8 * (o & 7)));
 }
 
 // Per-lane constants of the page walk.
