@@ -85,7 +85,8 @@ def test_decode_stages_equal_one_call(splits):
 
 
 @pytest.mark.parametrize("D,Hq,Hkv", [(128, 4, 2), (64, 8, 2), (128, 4, 4), (64, 2, 2),
-                                     (128, 10, 2), (64, 5, 1), (128, 16, 2), (64, 16, 2)])
+                                     (128, 10, 2), (64, 5, 1), (128, 16, 2), (64, 16, 2),
+                                     (64, 4, 2)])
 def test_decode_ragged_mixed_tiers(D, Hq, Hkv):
     cfg = small_workload(D=D, Hq=Hq, Hkv=Hkv, S=4, T=300, seed=40 + D + Hq)
     mixes = [(1500, 6000, 8500), (0, 0, 0), (10000, 10000, 10000), (0, 3000, 9000)]
@@ -112,7 +113,8 @@ def test_decode_growing_logits_rescale_per_head(D, ratio):
         _check_decode(geom_of(cfg), hc, case, sp, f"growing logits D={D} GQA {ratio}")
 
 
-@pytest.mark.parametrize("D,Hq,Hkv", [(128, 8, 2), (64, 4, 4), (128, 10, 2), (64, 16, 2)])
+@pytest.mark.parametrize("D,Hq,Hkv", [(128, 8, 2), (64, 4, 4), (128, 10, 2), (64, 16, 2),
+                                     (128, 4, 2), (64, 4, 2), (128, 16, 2), (64, 10, 2), (128, 3, 3)])
 def test_decode_sym_matches_oracle(D, Hq, Hkv):
     """The symmetric angle-code variant (query codes) against the oracle's:
     logits to the decode bar (so the query codes agree), outputs, lse."""
