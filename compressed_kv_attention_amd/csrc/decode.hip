@@ -641,6 +641,18 @@ __global__ __launch_bounds__((Waves<D, NH>::THREADS)) void decode_main(DecodeArg
         for (int h = 0; h < NH; h++)
             qv[h] = *reinterpret_cast<const uint4 *>(qrow + h * D + 8 * g);
     }
+    // SYM: the row's tabulated LUT (already in the LDS layout), loaded with
+    // the rest and written to LDS after the one wait
+    constexpr int LPT = SYM ? (LUT_FLOATS / 4 + kThreads - 1) / kThreads : 1;
+    f32x4 lv[LPT];
+    if constexpr (SYM) {
+        const f32x4 *src = reinterpret_cast<const f32x4 *>(a.glut + (size_t)row * LUT_FLOATS);
+#pragma unroll
+        for (int k = 0; k < LPT; k++) {
+            const int i = tid + k * kThreads;
+            lv[k] = src[i < LUT_FLOATS / 4 ? i : LUT_FLOATS / 4 - 1];
+        }
+    }
     // Query operand of the key MFMA: lane h + 16 r takes dims 16 b + 4 r ..
     // +3 of head h (zero for h >= NH), as bf16 (bf16 keys) or as fp16
     // scaled by 2^-e_h with the head's largest |q| in [2^14, 2^15).
@@ -688,6 +700,14 @@ __global__ __launch_bounds__((Waves<D, NH>::THREADS)) void decode_main(DecodeArg
             }
         }
     }
+    if constexpr (SYM) {
+        // (an empty asm that takes the table's registers: the compiler may
+        // not defer its loads to their LDS stores, which would wait for
+        // each in turn)
+#pragma unroll
+        for (int k = 0; k < LPT; k++)
+            asm volatile("" : "+v"(lv[k]));
+    }
     QOperand<D, DENSE> qo;
 #pragma unroll
     for (int b = 0; b < D / 16; b++) {
@@ -703,6 +723,15 @@ __global__ __launch_bounds__((Waves<D, NH>::THREADS)) void decode_main(DecodeArg
         }
     }
     const float lsc = ldexpf(a.sigma, eh) * kLog2e;
+    if constexpr (SYM) {
+        // (threads past the end rewrite the last entry with its own value,
+        // so no write is conditional and no load is deferred)
+#pragma unroll
+        for (int k = 0; k < LPT; k++) {
+            const int i = tid + k * kThreads;
+            reinterpret_cast<f32x4 *>(lut)[i < LUT_FLOATS / 4 ? i : LUT_FLOATS / 4 - 1] = lv[k];
+        }
+    }
     ADA_PHASE(1);
     // The wave's first page: its loads go out only now, after every other
     // prologue load has been waited for, so the tabulation below overlaps
@@ -718,10 +747,7 @@ __global__ __launch_bounds__((Waves<D, NH>::THREADS)) void decode_main(DecodeArg
         tbl[k] = make_uint2(pt[p], pm[p]);
     }
     if constexpr (SYM) {
-        // the row's tabulated LUT, already in the LDS layout
-        const float4 *src = reinterpret_cast<const float4 *>(a.glut + (size_t)row * LUT_FLOATS);
-        for (int i = tid; i < LUT_FLOATS / 4; i += kThreads)
-            reinterpret_cast<float4 *>(lut)[i] = src[i];
+        // (written to LDS before the first page was issued)
     } else if constexpr (!DENSE) {
         // LUT[g][c][h] = q_h[8g .. 8g+8) . C[g][c] (c < 256 from cb8, else cb4)
         float qq[NH][8];
