@@ -153,8 +153,33 @@ __global__ __launch_bounds__(D / 8 * 64) void append_kernel(AppendArgs a)
     if (tid < D)
         xk[tid] = f16_bits_to_f32(k[tid]);
     __syncthreads();
-    if (tid == 0)
-        rn = seq_norm<D>(xk);
+    // The ordered sum of the squares equals the exact sum whenever no
+    // partial sum needs rounding: every square of a binary16 value is a
+    // multiple of 2^e (e twice the smallest exponent of a coordinate's last
+    // bit), so when the exact total is below 2^(52 + e) every partial sum,
+    // in any order, is exact.  Wave 0's first D/8 lanes sum 8 squares each
+    // and then in a DPP tree, and test that; otherwise one lane sums in
+    // order.
+    if (tid < 64) {
+        double part = 0.0;
+        int emin = 1 << 20;
+        if (tid < D / 8) {
+#pragma unroll
+            for (int j = 0; j < 8; j++) {
+                const float x = xk[8 * tid + j];
+                part = part + (double)x * (double)x;
+                const uint32_t bits = __float_as_uint(x);
+                const int ex = (int)((bits >> 23) & 0xff);
+                // last bit of a binary16 value: 2^(E - 10), 2^-24 below 2^-14
+                const int last = ex - 137 > -24 ? ex - 137 : -24;
+                emin = (bits & 0x7fffffffu) != 0 ? min(emin, 2 * last) : emin;
+            }
+        }
+        const double tot = row_sum_f64<D == 64>(part);
+        emin = row_min_i32<D == 64>(emin);
+        if (tid == 0)
+            rn = tot < ldexp(1.0, 52 + max(emin, -1000)) ? sqrt(tot) : seq_norm<D>(xk);
+    }
     __syncthreads();
     if (tid < D) {
         const double x = (double)xk[tid];
