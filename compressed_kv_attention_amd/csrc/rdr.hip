@@ -25,11 +25,12 @@
 // arithmetic that decides the chains is binary32 in a fixed order (IEEE
 // division and square root), so every decision is reproducible.
 //
-// Kernels: code_error (256 states per block), solve_zero (clears the digit
+// Kernels: code_error (256 tokens of one kv-head per block), solve_zero (clears the digit
 // histograms), solve_pass<P> (P = 0..3; one block per 1024 states of one
 // sequence), solve_assign (writes the tiers), tier_counts (one block per
 // row).
 #include "ada_internal.h"
+#include "code_err.h"
 #include "div_rn.h"
 #include "numfmt.h"
 
@@ -42,13 +43,22 @@ namespace {
 // err = sum_g || u_g - C_g[code_g] ||^2 with u = k / ||k|| in double: the norm
 // summed sequentially over the D coordinates, each group's distance summed
 // over its 8 coordinates, groups added in order, the total rounded to f32.
-// A block takes 256 consecutive states, one per thread: their keys are
-// staged in LDS with coalesced 16-byte loads, then each thread sums its
-// key's norm in order and every group's two distances.  (With one wave
-// summing a block's norms while the others waited, and four threads per
-// state for the distances, the kernel was 8% slower at 19.5 M states.)
-constexpr int kErrItems = 256; // states per block, one per thread
-constexpr int kErrAhead = 4;   // groups whose codewords are in flight
+// A block takes 256 consecutive tokens of one kv-head, one state per
+// thread.  The keys are loaded with 16-byte loads (64 contiguous bytes per
+// key and load) and passed through LDS, 32 dimensions a round, so each
+// thread ends with its own key in registers.  The head's codebooks are
+// staged in LDS one group at a time (8-bit and 4-bit codewords, 8.5 KiB,
+// double-buffered; each group's loads are issued two groups ahead), so each
+// state's codewords are LDS reads rather than scattered global loads.  The
+// distances use the fast form of code_err.h; a state whose rounding test
+// fails is recomputed as defined, its codewords then read from global
+// memory.  (Gathering every state's codewords from global memory, 256
+// consecutive states of all heads per block, kept the kernel waiting on
+// its loads about two thirds of the time: 2.5 ms at 19.5 M states.)
+typedef float cbvec __attribute__((ext_vector_type(4))); // (a plain vector type stays in registers)
+constexpr int kErrItems = 256;                         // tokens per block, one per thread
+constexpr int kCbVec = (kCodes8 + kCodes4) * 8 / 4;    // float4 per group's codebooks (544)
+constexpr int kCbPer = (kCbVec + kErrItems - 1) / kErrItems;
 
 // The 8-bit and 4-bit codewords of group g of one state (two float4 each).
 __device__ __forceinline__ void gather_codewords(const float *cb8, const float *cb4, int h, int G, int g,
@@ -64,23 +74,48 @@ __device__ __forceinline__ void gather_codewords(const float *cb8, const float *
     w[3] = p4[1];
 }
 
+// Group g's codebooks of head h as kCbVec float4 (8-bit codewords, then
+// 4-bit): thread tid loads entries tid + kErrItems i (the last entry again
+// past the end).
+__device__ __forceinline__ void load_codebook(const float *cb8, const float *cb4, int h, int G, int g, int tid,
+                                              cbvec (&v)[kCbPer])
+{
+    const cbvec *p8 = reinterpret_cast<const cbvec *>(cb8 + ((size_t)h * G + g) * kCodes8 * 8);
+    const cbvec *p4 = reinterpret_cast<const cbvec *>(cb4 + ((size_t)h * G + g) * kCodes4 * 8);
+#pragma unroll
+    for (int i = 0; i < kCbPer; i++) {
+        const int k = min(tid + kErrItems * i, kCbVec - 1);
+        v[i] = k < kCodes8 * 2 ? p8[k] : p4[k - kCodes8 * 2];
+    }
+}
+__device__ __forceinline__ void store_codebook(cbvec *dst, int tid, const cbvec (&v)[kCbPer])
+{
+#pragma unroll
+    for (int i = 0; i < kCbPer; i++)
+        dst[min(tid + kErrItems * i, kCbVec - 1)] = v[i];
+}
+
 template <int D>
-__global__ __launch_bounds__(kErrItems) void code_error_kernel(int Hkv, int64_t n_items, const uint16_t *keys,
+// (four waves per SIMD: 128 registers; with three, a third group in flight
+// ran slower)
+__global__ __launch_bounds__(kErrItems) __attribute__((amdgpu_waves_per_eu(4))) void code_error_kernel(int Hkv, int64_t n_tokens, const uint16_t *keys,
                                                          const float *cb8, const float *cb4,
                                                          const uint8_t *codes8, const uint8_t *codes4,
                                                          float *err8, float *err4)
 {
     constexpr int G = D / 8;
-    constexpr int RW = D / 2 + 1; // row stride in words (odd: conflict-free)
-    __shared__ uint32_t xk[kErrItems * RW];
+    constexpr int RND = D / 32;  // staging rounds of 32 dimensions
+    constexpr int SW = 17;       // LDS row stride in words (odd: conflict-free reads)
+    __shared__ uint32_t xs[kErrItems * SW];
+    __shared__ cbvec cbs[2][kCbVec];
     const int tid = threadIdx.x;
-    const int64_t e0 = (int64_t)blockIdx.x * kErrItems;
-    const int n_here = (int)(n_items - e0 < kErrItems ? n_items - e0 : kErrItems);
-    // Load order: this thread's codes, the block's keys, then (as soon as
-    // the codes are in) the codewords of the first groups, whose latency
-    // the staging and the norm then cover.  Threads past the block's end
-    // load the last state's codes and write nothing.
-    const int64_t e = e0 + (tid < n_here ? tid : n_here - 1);
+    const int h = (int)(blockIdx.x % (unsigned)Hkv);
+    const int64_t t0 = (int64_t)(blockIdx.x / (unsigned)Hkv) * kErrItems;
+    const int n_here = (int)(n_tokens - t0 < kErrItems ? n_tokens - t0 : kErrItems);
+    // Load order: this thread's codes, the block's keys, the first group's
+    // codebooks.  Threads past the block's end take the last token's codes
+    // and key, and write nothing.
+    const int64_t e = (t0 + (tid < n_here ? tid : n_here - 1)) * Hkv + h;
     uint32_t c8w[G / 4], c4w[G / 8];
 #pragma unroll
     for (int k = 0; k < G / 4; k++)
@@ -88,78 +123,114 @@ __global__ __launch_bounds__(kErrItems) void code_error_kernel(int Hkv, int64_t 
 #pragma unroll
     for (int k = 0; k < G / 8; k++)
         c4w[k] = *reinterpret_cast<const uint32_t *>(codes4 + e * (G / 2) + 4 * k);
-    // (rows past the block's end repeat its last key: no branch, so the
-    // wait for the codes below leaves the key loads in flight)
-    constexpr int KL = D / 8; // 16-byte key loads per thread
-    uint4 kv[KL];
+    // round k, load j: chunk c = tid % 4 (8 dims) of token tid / 4 + 64 j
+    uint4 kv[RND][4];
 #pragma unroll
-    for (int k = 0; k < KL; k++) {
-        const int i = tid + k * kErrItems, it = i / (D / 8), c = i % (D / 8);
-        kv[k] = *reinterpret_cast<const uint4 *>(keys + (e0 + (it < n_here ? it : n_here - 1)) * D + 8 * c);
+    for (int k = 0; k < RND; k++) {
+#pragma unroll
+        for (int j = 0; j < 4; j++) {
+            const int it = tid / 4 + 64 * j, c = tid % 4;
+            const int64_t ek = (t0 + (it < n_here ? it : n_here - 1)) * Hkv + h;
+            kv[k][j] = *reinterpret_cast<const uint4 *>(keys + ek * D + 32 * k + 8 * c);
+        }
     }
-    const int h = (int)(e % Hkv);
-    float4 cw[kErrAhead][4];
+    // Group k's codebooks are loaded into registers two groups ahead and
+    // stored to LDS buffer k % 2 one group ahead: f1 and f2 hold groups
+    // g + 1 and g + 2 while group g is computed (named arrays, shifted each
+    // group, so they stay in registers).
+    cbvec f1[kCbPer], f2[kCbPer];
+    load_codebook(cb8, cb4, h, G, 0, tid, f2);
+    load_codebook(cb8, cb4, h, G, 1, tid, f1);
+    uint32_t kw[D / 2]; // this thread's key, two binary16 values a word
 #pragma unroll
-    for (int g = 0; g < kErrAhead; g++)
-        gather_codewords(cb8, cb4, h, G, g, c8w, c4w, cw[g]);
+    for (int k = 0; k < RND; k++) {
 #pragma unroll
-    for (int k = 0; k < KL; k++) {
-        const int i = tid + k * kErrItems, it = i / (D / 8), c = i % (D / 8);
-        uint32_t *dst = xk + it * RW + 4 * c;
-        dst[0] = kv[k].x;
-        dst[1] = kv[k].y;
-        dst[2] = kv[k].z;
-        dst[3] = kv[k].w;
-    }
-    __syncthreads();
-    if (tid >= n_here)
-        return;
-    const uint32_t *row = xk + tid * RW;
-    double ss = 0.0;
-#pragma unroll
-    for (int c0 = 0; c0 < D / 2; c0 += 16) {
-        uint32_t kw[16];
+        for (int j = 0; j < 4; j++) {
+            const int it = tid / 4 + 64 * j, c = tid % 4;
+            uint32_t *dst = xs + it * SW + 4 * c;
+            dst[0] = kv[k][j].x;
+            dst[1] = kv[k][j].y;
+            dst[2] = kv[k][j].z;
+            dst[3] = kv[k][j].w;
+        }
+        if (k == 0)
+            store_codebook(cbs[0], tid, f2);
+        __syncthreads();
 #pragma unroll
         for (int c = 0; c < 16; c++)
-            kw[c] = row[c0 + c];
+            kw[16 * k + c] = xs[tid * SW + c];
+        __syncthreads();
+    }
+    // (a binary16 value's square is exact in double, so the fused
+    // multiply-add rounds as the ordered sum of squares does)
+    double ss = 0.0;
 #pragma unroll
-        for (int c = 0; c < 16; c++) {
-            const double lo = (double)f16_bits_to_f32((uint16_t)(kw[c] & 0xffff));
-            const double hi = (double)f16_bits_to_f32((uint16_t)(kw[c] >> 16));
-            ss = ss + lo * lo;
-            ss = ss + hi * hi;
-        }
+    for (int c = 0; c < D / 2; c++) {
+        const double lo = (double)f16_bits_to_f32((uint16_t)(kw[c] & 0xffff));
+        const double hi = (double)f16_bits_to_f32((uint16_t)(kw[c] >> 16));
+        ss = __builtin_fma(lo, lo, ss);
+        ss = __builtin_fma(hi, hi, ss);
     }
     const double r = sqrt(ss);
+    const bool fin = r > 0.0 && r < INFINITY;
+    // (an empty asm that takes the key's registers: the conversions below
+    // are redone per group instead of being kept from the norm's, which
+    // would hold D doubles)
+#pragma unroll
+    for (int c = 0; c < D / 2; c++)
+        asm volatile("" : "+v"(kw[c]));
+    // The fast form (code_err.h): t = RN(x y - w) from y = RN(1 / r),
+    // squares added with fused multiply-adds, groups added in order; kept
+    // when its binary32 rounding cannot differ from the defined
+    // computation's.  Every thread runs the loop (it holds the block's
+    // barriers); a non-finite or zero norm takes the defined path below.
+    const double y = fin ? 1.0 / r : 0.0;
     double e8 = 0.0, e4 = 0.0;
-    if (r > 0.0 && r < INFINITY) {
-        // u = x / r from y = RN(1 / r) (div_rn).  Each group's code is
-        // kept apart from the next (sched_barrier), so the codeword loads
-        // issued for group g + kErrAhead stay behind group g's arithmetic.
-        const double y = 1.0 / r;
 #pragma unroll
-        for (int g = 0; g < G; g++) {
-            float4 (&c)[4] = cw[g % kErrAhead];
-            const float w8[8] = {c[0].x, c[0].y, c[0].z, c[0].w, c[1].x, c[1].y, c[1].z, c[1].w};
-            const float w4[8] = {c[2].x, c[2].y, c[2].z, c[2].w, c[3].x, c[3].y, c[3].z, c[3].w};
-            const uint32_t w[4] = {row[4 * g], row[4 * g + 1], row[4 * g + 2], row[4 * g + 3]};
-            double d8 = 0.0, d4 = 0.0;
+    for (int g = 0; g < G; g++) {
+        if (g + 2 < G)
+            load_codebook(cb8, cb4, h, G, g + 2, tid, f2);
+        const cbvec *cb = cbs[g & 1];
+        const int c8 = (c8w[g / 4] >> (8 * (g % 4))) & 255;
+        const int c4 = (c4w[g / 8] >> (4 * (g % 8))) & 15;
+        const cbvec a0 = cb[2 * c8], a1 = cb[2 * c8 + 1];
+        const cbvec b0 = cb[2 * kCodes8 + 2 * c4], b1 = cb[2 * kCodes8 + 2 * c4 + 1];
+        const float w8[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+        const float w4[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
+        double d8 = 0.0, d4 = 0.0;
 #pragma unroll
-            for (int j = 0; j < 8; j++) {
-                const double x = (double)f16_bits_to_f32((uint16_t)(j & 1 ? w[j / 2] >> 16 : w[j / 2] & 0xffff));
-                const double u = div_rn(x, r, y);
-                const double xa = u - (double)w8[j], xb = u - (double)w4[j];
-                d8 = d8 + xa * xa;
-                d4 = d4 + xb * xb;
-            }
-            e8 = e8 + d8;
-            e4 = e4 + d4;
-            if (g + kErrAhead < G)
-                gather_codewords(cb8, cb4, h, G, g + kErrAhead, c8w, c4w, c);
-            __builtin_amdgcn_sched_barrier(0);
+        for (int j = 0; j < 8; j++) {
+            const uint32_t wd = kw[4 * g + j / 2];
+            const double x = (double)f16_bits_to_f32((uint16_t)(j & 1 ? wd >> 16 : wd & 0xffff));
+            d8 = ce_term(d8, x, y, (double)w8[j]);
+            d4 = ce_term(d4, x, y, (double)w4[j]);
         }
-    } else {
-        // a zero key (u = 0) or a non-finite one: as the definition divides
+        e8 = e8 + d8;
+        e4 = e4 + d4;
+        // (an empty asm that takes the sums: the group's arithmetic stays
+        // ahead of the barrier instead of being deferred past the later
+        // groups' LDS reads, which would hold all their codewords)
+        asm volatile("" : "+v"(e8), "+v"(e4));
+        if (g + 1 < G) {
+            store_codebook(cbs[(g + 1) & 1], tid, f1);
+            __syncthreads();
+        }
+#pragma unroll
+        for (int i = 0; i < kCbPer; i++) {
+            f1[i] = f2[i];
+        }
+    }
+    if (tid >= n_here)
+        return;
+    if (!(fin && ce_rounds_alike(e8) && ce_rounds_alike(e4))) {
+        // As defined: u = x / r rounded (div_rn for a finite positive
+        // norm; a zero key gives u = 0, a non-finite norm divides), each
+        // difference squared and added with its own rounding.  (The key is
+        // read again from global memory: a rolled loop cannot index the
+        // key's registers.)
+        const uint32_t *kg = reinterpret_cast<const uint32_t *>(keys + e * D);
+        e8 = 0.0;
+        e4 = 0.0;
         for (int g = 0; g < G; g++) {
             float4 c[4];
             gather_codewords(cb8, cb4, h, G, g, c8w, c4w, c);
@@ -167,9 +238,9 @@ __global__ __launch_bounds__(kErrItems) void code_error_kernel(int Hkv, int64_t 
             const float w4[8] = {c[2].x, c[2].y, c[2].z, c[2].w, c[3].x, c[3].y, c[3].z, c[3].w};
             double d8 = 0.0, d4 = 0.0;
             for (int j = 0; j < 8; j++) {
-                const uint32_t wd = row[4 * g + j / 2];
+                const uint32_t wd = kg[4 * g + j / 2];
                 const double x = (double)f16_bits_to_f32((uint16_t)(j & 1 ? wd >> 16 : wd & 0xffff));
-                const double u = r > 0.0 ? x / r : 0.0;
+                const double u = fin ? div_rn(x, r, y) : r > 0.0 ? x / r : 0.0;
                 const double xa = u - (double)w8[j], xb = u - (double)w4[j];
                 d8 = d8 + xa * xa;
                 d4 = d4 + xb * xb;
@@ -458,16 +529,18 @@ hipError_t launch_code_error(int D, int Hkv, int64_t n_tokens, const uint16_t *k
                              const float *cb4, const uint8_t *codes8, const uint8_t *codes4,
                              float *err8, float *err4, hipStream_t st)
 {
-    const int64_t n = n_tokens * Hkv;
-    if (n == 0)
+    if (n_tokens == 0 || Hkv == 0)
         return hipSuccess;
-    const dim3 grid((unsigned)((n + kErrItems - 1) / kErrItems));
+    const int64_t blocks = (n_tokens + kErrItems - 1) / kErrItems * Hkv;
+    if (blocks > 0x7fffffff)
+        return hipErrorInvalidValue;
+    const dim3 grid((unsigned)blocks);
     if (D == 128)
-        hipLaunchKernelGGL(code_error_kernel<128>, grid, dim3(kErrItems), 0, st, Hkv, n, keys, cb8, cb4, codes8,
-                           codes4, err8, err4);
+        hipLaunchKernelGGL(code_error_kernel<128>, grid, dim3(kErrItems), 0, st, Hkv, n_tokens, keys, cb8, cb4,
+                           codes8, codes4, err8, err4);
     else if (D == 64)
-        hipLaunchKernelGGL(code_error_kernel<64>, grid, dim3(kErrItems), 0, st, Hkv, n, keys, cb8, cb4, codes8,
-                           codes4, err8, err4);
+        hipLaunchKernelGGL(code_error_kernel<64>, grid, dim3(kErrItems), 0, st, Hkv, n_tokens, keys, cb8, cb4,
+                           codes8, codes4, err8, err4);
     else
         return hipErrorInvalidValue;
     return hipGetLastError();
