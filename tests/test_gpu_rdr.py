@@ -109,6 +109,46 @@ def test_code_error_bit_exact_extreme_keys(D):
         assert np.isfinite(r8).all() and np.isfinite(r4).all()
         assert np.array_equal(e8.cpu().numpy(), r8) and np.array_equal(e4.cpu().numpy(), r4)
 
+@pytest.mark.parametrize("D", [64, 128])
+def test_code_error_bit_exact_codewords_on_the_key(D):
+    """Codewords equal to the key's direction rounded to binary32, or one
+    binary32 ulp from it: errors of about 1e-15 or exactly zero, which the
+    kernel's fast form cannot round with certainty, so these states take
+    the defined path (division rounded, each term rounded).  Bit-exact with
+    the oracle over partial blocks (600 tokens)."""
+    cfg = small_workload(D=D, Hq=4, Hkv=2, S=1, T=600, seed=95 + D)
+    case = make_case(cfg, lens=[600])
+    T, H, G = 600, 2, D // 8
+    x = case["keys"].double().numpy()                       # [T][H][D]
+    u = x / np.sqrt((x * x).sum(-1, keepdims=True))
+    cb8 = case["cb8"].numpy().copy()                         # [H][G][256][8]
+    cb4 = case["cb4"].numpy().copy()                         # [H][G][16][8]
+    rng = np.random.default_rng(D + 7)
+    for h in range(H):
+        for t in range(256):                                 # tokens 0..255: own 8-bit codeword
+            w = u[t, h].astype(np.float32).reshape(G, 8)
+            if t % 3 == 1:                                   # one ulp off in one coordinate
+                j = rng.integers(8)
+                w[:, j] = np.nextafter(w[:, j], np.float32(np.inf))
+            cb8[h, :, t] = w
+        for t in range(16):                                  # tokens 0..15: own 4-bit codeword
+            cb4[h, :, t] = u[t, h].astype(np.float32).reshape(G, 8)
+    tok = np.arange(T)
+    c8 = np.repeat((tok % 256).astype(np.uint8)[:, None, None], H, 1).repeat(G, 2)
+    nib = (tok % 16).astype(np.uint8)
+    c4 = np.repeat((nib | (nib << 4))[:, None, None], H, 1).repeat(G // 2, 2)
+    geom = geom_of(cfg)
+    flush(f"[code_error codewords on the key] D={D}")
+    e8 = torch.full((T, H), float("nan"), device="cuda")
+    e4 = torch.full((T, H), float("nan"), device="cuda")
+    ada.code_error(geom, to_dev(case["keys"]), to_dev(torch.from_numpy(cb8)), to_dev(torch.from_numpy(cb4)),
+                   to_dev(c8), to_dev(c4), e8, e4)
+    torch.cuda.synchronize()
+    r8, r4 = oracle.code_error(case["keys"], torch.from_numpy(cb8), torch.from_numpy(cb4), c8, c4)
+    assert (r8[:256] < 1e-12).all() and (r4[:16] < 1e-12).all()   # the cases are the tiny errors
+    assert np.array_equal(e8.cpu().numpy(), r8) and np.array_equal(e4.cpu().numpy(), r4)
+
+
 def _solve_both(geom, D, cu, budgets, r, e8, e4, sc, prot=None):
     tiers = torch.full(r.shape, 77, dtype=torch.uint8, device="cuda")
     ada.rdr_solve(geom, cu, budgets, to_dev(r), to_dev(e8), to_dev(e4), to_dev(sc), tiers,
