@@ -43,24 +43,23 @@ constexpr int kChunk = 64;          // tokens per chunk
 constexpr float kCodeMax = 0x1p20f; // larger (or non-finite) codebooks skip the filter
 
 // Filter bound.  Let n = |u|^2 over the group, d the distance of codeword c
-// and s = fl(n' + |c|^2 - 2 u.c) the matrix-core score (the accumulator
-// starts at n' + |c|^2), where n' (a little
-// above n, see below) makes every score positive; s - n' estimates d - n.
-// With T = n' + |c|^2 + 2 sum_j |u_j c_j| (at most 7 (n + d), since |c| <= |u|
-// + sqrt(d)): rounding u to binary32 (through a double reciprocal of a norm
-// within 2^-45 of r) moves s by at most 3 2^-24 T; the binary32 n' + |c|^2
-// by at most 2^-21 T; the two MFMAs -- eight products and eight additions,
-// each assumed within one ulp (2^-23 relative) whatever the matrix core's
-// order and rounding -- by at most 9 2^-23 T.  So |s - n' - (d - n)| <=
-// 2^-16 (n + d).  The
-// tracked scores also carry a codeword index in their low 6 mantissa bits,
-// which moves them by at most 2^-17 s.  Together eps = 1.5 2^-16, and
-// codeword c is strictly farther in double than the best-scored one whenever
-// s_c - s_1 > eps (2 n + s_c + s_1); that holds for every c once the gap to
-// the second-best score s_2 exceeds eps (2 n + s_1 + s_2).  The test below
-// asks for 2^-14 (2 n + s_1 + s_2), over 2.6 times that, plus a tiny
-// absolute term for flushed subnormals (codewords are at most 2^20 in
-// magnitude on this path).
+// and s = fl(|c|^2 - 2 u.c) the matrix-core score (the accumulator starts
+// at the binary32 |c|^2); s estimates d - n and may be negative.  With
+// T = |c|^2 + 2 sum_j |u_j c_j| (at most 7 (n + d), since |c| <= |u| +
+// sqrt(d)): rounding u to binary32 (through a double reciprocal of a norm
+// within 2^-45 of r) moves s by at most 3 2^-24 T; the binary32 |c|^2 by at
+// most 2^-21 T; the two MFMAs -- eight products and eight additions, each
+// assumed within one ulp (2^-23 relative) whatever the matrix core's order
+// and rounding -- by at most 9 2^-23 T.  So |s - (d - n)| <= 2^-16 (n + d).
+// The tracked scores also carry a codeword index in their low 6 mantissa
+// bits, which moves them by at most 2^-17 |s| <= 2^-17 (n + d).  Together
+// eps = 1.5 2^-16, and codeword c is strictly farther in double than the
+// best-scored one whenever s_c - s_1 > eps ((n + d_c) + (n + d_1)), i.e.
+// eps (4 n + s_c + s_1) up to those same errors; that holds for every c once
+// the gap to the second-best score s_2 exceeds eps (4 n + s_1 + s_2).  The
+// test below asks for 2^-14 (4 n + s_1 + s_2) with n in binary32, over 2.6
+// times that, plus a tiny absolute term for flushed subnormals (codewords
+// are at most 2^20 in magnitude on this path).
 constexpr float kFilterRel = 0x1p-14f;
 constexpr float kFilterAbs = 0x1p-90f;
 
@@ -153,24 +152,25 @@ __device__ __forceinline__ double exact_norm(const uint32_t *row)
     return sqrt(ss);
 }
 
-// A lane's running best two packed scores (value bits | 6-bit slot): keys
-// are positive floats, so float and integer order agree.
+// A lane's running best two packed scores (value bits | 6-bit slot),
+// compared as floats (the minimum is the median of a, b and -inf: no NaN
+// reaches this path, and the median needs no canonicalising moves).
 struct Best {
-    uint32_t k1;
-    float k2;
+    float k1, k2;
 };
 
 __device__ __forceinline__ void best_init(Best &s)
 {
-    s.k1 = 0x7f7fffffu;
+    s.k1 = __uint_as_float(0x7f7fffffu);
     s.k2 = __uint_as_float(0x7f7fffffu);
 }
 
-__device__ __forceinline__ void best_add(Best &s, float score, int slot)
+// ninf: -inf held in a register (the minimum is the median of a, b and -inf)
+__device__ __forceinline__ void best_add(Best &s, float score, int slot, float ninf)
 {
-    const uint32_t k = (__float_as_uint(score) & ~63u) | (uint32_t)slot;
-    s.k2 = __builtin_amdgcn_fmed3f(__uint_as_float(s.k1), s.k2, __uint_as_float(k));
-    s.k1 = min(s.k1, k);
+    const float k = __uint_as_float((__float_as_uint(score) & ~63u) | (uint32_t)slot);
+    s.k2 = __builtin_amdgcn_fmed3f(s.k1, s.k2, k);
+    s.k1 = __builtin_amdgcn_fmed3f(s.k1, k, ninf);
 }
 
 // Best value, its codeword and the second-best value over a token column.
@@ -182,7 +182,7 @@ struct Column {
 
 __device__ __forceinline__ Column best_column(const Best &s, int cw)
 {
-    Column c{__uint_as_float(s.k1 & ~63u), __uint_as_float(__float_as_uint(s.k2) & ~63u), cw};
+    Column c{__uint_as_float(__float_as_uint(s.k1) & ~63u), __uint_as_float(__float_as_uint(s.k2) & ~63u), cw};
 #pragma unroll
     for (int step = 0; step < 2; step++) {
         uint32_t a1, b1, a2, b2, ai, bi;
@@ -393,14 +393,15 @@ __global__ __launch_bounds__(256, 4) void encode_kernel(int Hkv, int gx, int64_t
                 const float ub = (float)((double)f16_bits_to_f32(kg[4 + q]) * ri);
                 const float b0 = -2.f * ua, b1 = -2.f * ub;
                 const float n32 = column_sum(fmaf(ub, ub, ua * ua));
-                const float np = fmaf(n32, 1.f + 0x1p-8f, 0x1p-100f);
+                float ninf;
+                asm("; -inf" : "=v"(ninf) : "0"(-INFINITY));
                 Best s8b, s4b;
                 best_init(s8b);
                 best_init(s4b);
 #pragma unroll
                 for (int t = 0; t < 17; t++) {
                     const float4 cn = *reinterpret_cast<const float4 *>(norms + 16 * t + 4 * q);
-                    f32x4 acc = {cn.x + np, cn.y + np, cn.z + np, cn.w + np};
+                    f32x4 acc = {cn.x, cn.y, cn.z, cn.w};
                     acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a0[t], b0, acc, 0, 0, 0);
                     acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a1[t], b1, acc, 0, 0, 0);
                     // element v: codeword (16 t +) 4 q + v of token tk; its
@@ -408,18 +409,18 @@ __global__ __launch_bounds__(256, 4) void encode_kernel(int Hkv, int gx, int64_t
 #pragma unroll
                     for (int v = 0; v < 4; v++) {
                         if (t < 16)
-                            best_add(s8b, acc[v], 4 * t + v);
+                            best_add(s8b, acc[v], 4 * t + v, ninf);
                         else
-                            best_add(s4b, acc[v], v);
+                            best_add(s4b, acc[v], v, ninf);
                     }
                     if (t % 4 == 3)
                         __builtin_amdgcn_sched_barrier(0);
                 }
-                const int j8 = (int)(s8b.k1 & 63u), j4 = (int)(s4b.k1 & 63u);
+                const int j8 = (int)(__float_as_uint(s8b.k1) & 63u), j4 = (int)(__float_as_uint(s4b.k1) & 63u);
                 const Column c8 = best_column(s8b, 16 * (j8 >> 2) + 4 * q + (j8 & 3));
                 const Column c4 = best_column(s4b, 4 * q + j4);
-                const bool ok8 = c8.v2 - c8.v1 > fmaf(kFilterRel, 2.f * n32 + c8.v1 + c8.v2, kFilterAbs);
-                const bool ok4 = c4.v2 - c4.v1 > fmaf(kFilterRel, 2.f * n32 + c4.v1 + c4.v2, kFilterAbs);
+                const bool ok8 = c8.v2 - c8.v1 > fmaf(kFilterRel, 4.f * n32 + c8.v1 + c8.v2, kFilterAbs);
+                const bool ok4 = c4.v2 - c4.v1 > fmaf(kFilterRel, 4.f * n32 + c4.v1 + c4.v2, kFilterAbs);
                 code8 = c8.i1;
                 code4 = c4.i1;
                 // near ties: rescanned in double after the chunk's tiles
