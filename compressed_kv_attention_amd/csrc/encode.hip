@@ -143,10 +143,12 @@ __device__ __forceinline__ double exact_norm(const uint32_t *row)
             kw[c] = row[c0 + c];
 #pragma unroll
         for (int c = 0; c < 16; c++) {
+            // (a binary16 value's square is exact in double: the fused
+            // multiply-add rounds as the sum of the square does)
             const double lo = (double)f16_bits_to_f32((uint16_t)(kw[c] & 0xffff));
             const double hi = (double)f16_bits_to_f32((uint16_t)(kw[c] >> 16));
-            ss = ss + lo * lo;
-            ss = ss + hi * hi;
+            ss = __builtin_fma(lo, lo, ss);
+            ss = __builtin_fma(hi, hi, ss);
         }
     }
     return sqrt(ss);
@@ -364,8 +366,8 @@ __global__ __launch_bounds__(256, 4) void encode_kernel(int Hkv, int gx, int64_t
                 const uint32_t kw = row[c];
                 const double lo = (double)f16_bits_to_f32((uint16_t)(kw & 0xffff));
                 const double hi = (double)f16_bits_to_f32((uint16_t)(kw >> 16));
-                part = part + lo * lo;
-                part = part + hi * hi;
+                part = __builtin_fma(lo, lo, part); // (exact squares)
+                part = __builtin_fma(hi, hi, part);
             }
             const double r = sqrt(column_sum(part));
             if (q == 0)
