@@ -611,6 +611,8 @@ def phase_profile(cfg, dev, args):
            "block_start_us": pct(rel[:, :, 0].min(1)),
            "block_past_table_barrier_us": pct(rel[:, :, 3].max(1)),
            "block_end_us": pct(rel[:, :, 5].max(1)),
+           "block_end_us_by_xcc": {int(x): pct(rel[:, :, 5].max(1)[(t[:, 0, 7] & 7) == x])
+                                   for x in range(8) if ((t[:, 0, 7] & 7) == x).any()},
            "xcc_of_block0": int(t[0, 0, 7] & 7),
            "xcc_round_robin_fraction": float(np.mean((t[:, 0, 7] & 7) == ((np.arange(nblk) + int(t[0, 0, 7] & 7)) % 8)))}
     return res
