@@ -95,13 +95,12 @@ __device__ __forceinline__ void store_codebook(cbvec *dst, int tid, const cbvec 
         dst[min(tid + kErrItems * i, kCbVec - 1)] = v[i];
 }
 
-template <int D>
 // (four waves per SIMD: 128 registers; with three, a third group in flight
 // ran slower)
-__global__ __launch_bounds__(kErrItems) __attribute__((amdgpu_waves_per_eu(4))) void code_error_kernel(int Hkv, int64_t n_tokens, const uint16_t *keys,
-                                                         const float *cb8, const float *cb4,
-                                                         const uint8_t *codes8, const uint8_t *codes4,
-                                                         float *err8, float *err4)
+template <int D>
+__global__ __launch_bounds__(kErrItems) __attribute__((amdgpu_waves_per_eu(4))) void
+code_error_kernel(int Hkv, int64_t n_tokens, const uint16_t *keys, const float *cb8, const float *cb4,
+                  const uint8_t *codes8, const uint8_t *codes4, float *err8, float *err4)
 {
     constexpr int G = D / 8;
     constexpr int RND = D / 32;  // staging rounds of 32 dimensions
