@@ -584,41 +584,10 @@ __global__ __launch_bounds__((Waves<D, NH>::THREADS)) void decode_main(DecodeArg
     const Lane L = make_lane<D, NH>(lane);
     ADA_PHASE(0);
 
-    // This workgroup's pages are p_k = split + k * nsplit, k < n_wg; wave w
-    // takes k = w + kWaves * i, i < n_mine.  Their table entries are staged
-    // in LDS.
-    const int np = a.num_pages[row];
-    const int n_wg = split < np ? (np - split + a.nsplit - 1) / a.nsplit : 0;
-    const int n_mine = wave < n_wg ? (n_wg - wave + kWaves - 1) / kWaves : 0;
-    const int last = n_mine - 1;
-    const uint32_t *pt = a.page_table + (size_t)row * a.maxp;
-    const uint8_t *pm = a.page_meta + (size_t)row * a.maxp;
-    // Prologue: the wave's first table entry, the workgroup's table
-    // entries, the codewords and query slices of the LUT and the query
-    // operand are all loaded before any is waited for (one memory latency).
-    // The first page's loads go out only after that wait: vector-memory
-    // waits drain in issue order, so a page issued earlier would hold up
-    // the tabulation behind its own latency.  The tabulation then overlaps
-    // the page's loads.
-    PageRegs<D> bufA, bufB;
-    uint2 first = make_uint2(0u, 0u);
-    if (n_mine > 0) {
-        const int p0 = split + wave * a.nsplit;
-        first = make_uint2(pt[p0], pm[p0]);
-    }
-    constexpr int TE = 2; // table entries per thread held in registers
-    uint32_t te_off[TE], te_meta[TE];
-#pragma unroll
-    for (int j = 0; j < TE; j++) {
-        const int k = tid + j * kThreads;
-        te_off[j] = 0u;
-        te_meta[j] = 0u;
-        if (k < n_wg) {
-            const int p = split + k * a.nsplit;
-            te_off[j] = pt[p];
-            te_meta[j] = pm[p];
-        }
-    }
+    // Prologue loads, all issued before any is waited for.  First those
+    // that need only the row: the codewords and query slices of the LUT and
+    // the query operand (ahead of the row's page count, a scalar load whose
+    // wait would otherwise hold them back by one memory latency).
     // Code tables: thread t serves group g = t / TPG and codes t % TPG +
     // TPG k; its codewords and the group's query slices load with the rest.
     constexpr int TPG = kThreads / G;
@@ -662,6 +631,42 @@ __global__ __launch_bounds__((Waves<D, NH>::THREADS)) void decode_main(DecodeArg
 #pragma unroll
     for (int b = 0; b < D / 16; b++)
         qraw[b] = *reinterpret_cast<const u32x2 *>(qrow + (size_t)hq_ld * D + 16 * b + 4 * L.r);
+    // This workgroup's pages are p_k = split + k * nsplit, k < n_wg; wave w
+    // takes k = w + kWaves * i, i < n_mine.  Their table entries are staged
+    // in LDS.
+    const int np = a.num_pages[row];
+    const int n_wg = split < np ? (np - split + a.nsplit - 1) / a.nsplit : 0;
+    const int n_mine = wave < n_wg ? (n_wg - wave + kWaves - 1) / kWaves : 0;
+    const int last = n_mine - 1;
+    const uint32_t *pt = a.page_table + (size_t)row * a.maxp;
+    const uint8_t *pm = a.page_meta + (size_t)row * a.maxp;
+    // Then, once the page count is in, the wave's first table entry and the
+    // workgroup's table entries.  The first page's loads go out only after
+    // the prologue's one wait: vector-memory
+    // waits drain in issue order, so a page issued earlier would hold up
+    // the tabulation behind its own latency.  The tabulation then overlaps
+    // the page's loads.
+    PageRegs<D> bufA, bufB;
+    uint2 first = make_uint2(0u, 0u);
+    if (n_mine > 0) {
+        const int p0 = split + wave * a.nsplit;
+        first = make_uint2(pt[p0], pm[p0]);
+    }
+    constexpr int TE = 2; // table entries per thread held in registers
+    uint32_t te_off[TE], te_meta[TE];
+#pragma unroll
+    for (int j = 0; j < TE; j++) {
+        const int k = tid + j * kThreads;
+        te_off[j] = 0u;
+        te_meta[j] = 0u;
+        if (k < n_wg) {
+            const int p = split + k * a.nsplit;
+            te_off[j] = pt[p];
+            te_meta[j] = pm[p];
+        }
+    }
+    // (lanes of unused heads zero their query slices only now: the select
+    // waits for the loads)
 #pragma unroll
     for (int b = 0; b < D / 16; b++)
         qraw[b] = L.hl < NH ? qraw[b] : u32x2{0u, 0u};
